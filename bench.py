@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed MoE layer (Step-5-Preview shape) on one MI355X.
+
+One step = one pass of the whole layer (router, grouping, routed expert
+gate/up + SwiGLU and down, shared expert, combine) over one batch of
+synthetic tokens already resident in HBM.  Prints one JSON line.
+
+  python bench.py [--workload decode_bf16|decode_fp8|prefill_fp8|ep8_share_fp8|small_bf16]
+                  [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+The default workload is the bf16 decode layer (T=64 tokens, hidden 4096,
+352 experts, top-8, intermediate 1536, one shared expert).  The dominant
+kernel's roofline figure comes from HIP events recorded around that kernel
+inside the timed steps (moe_timing.h); the CPU baseline is the fp64 oracle
+on a bounded sample of the same workload, on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + HBM GB/s (decode) / MFMA TFLOP/s % peak (prefill)"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # dense MFMA, TFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from router_gemm_amd import binding as B
+    from router_gemm_amd import workloads as W
+    from router_gemm_amd.build import LIB
+
+    if not os.path.exists(LIB):
+        from router_gemm_amd import build as hb
+        hb.build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(3)
+
+    cfg = W.get_config(args.workload)
+    dev = torch.device("cuda:0")
+    print(f"[bench] building {cfg.name} on {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+    lt = W.make_layer(cfg, dev)
+    x = W.make_x(cfg, dev)
+    T, H, E, I, Is = cfg.T, cfg.H, cfg.E, cfg.I, cfg.Is
+    fp8 = cfg.expert_dtype == "fp8"
+    layer = B.Layer.from_tensors(lt, top_k=cfg.k if not cfg.triples else 0)
+    N = cfg.N
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    if cfg.triples:
+        tok, exp, gate = W.make_triples(cfg)
+        tok_g, exp_g, gate_g = (torch.from_numpy(a).to(dev) for a in (tok, exp, gate))
+        shared = B.Layer.shared_view(lt)
+        ws = torch.empty(max(B.moe_workspace_bytes(layer, T, N), B.moe_workspace_bytes(shared, T, T)),
+                         dtype=torch.uint8, device=dev)
+        off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        src = torch.empty(N, dtype=torch.int32, device=dev)
+        pos = torch.empty(N, dtype=torch.int32, device=dev)
+        xp = torch.empty((N, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+        xs = torch.empty((N, H // 128), dtype=torch.float32, device=dev) if fp8 else None
+        yp = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+        s_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        sh_off = torch.tensor([0, T], dtype=torch.int32, device=dev)
+
+        def step():
+            B.moe_permute(layer, x, T, exp_g, tok_g, N, off, src, pos, xp, xs, ws=ws)
+            B.moe_expert_ffn(layer, off, xp, xs, N, yp, ws=ws)
+            B.moe_expert_ffn(shared, sh_off, x, None, T, s_out, ws=ws)
+            B.moe_combine(layer, yp, B.MOE_BF16, pos, tok_g, gate_g, N, s_out, B.MOE_BF16, T, y, B.MOE_BF16, ws=ws)
+
+        counts = np.bincount(exp, minlength=E)
+    else:
+        ws = B.workspace(layer, T, N, dev)
+        ids = torch.empty((T, cfg.k), dtype=torch.int32, device=dev)
+        gts = torch.empty((T, cfg.k), dtype=torch.float32, device=dev)
+
+        def step():
+            B.moe_forward(layer, x, T, y, topk_ids=ids, topk_gates=gts, ws=ws)
+
+        step()
+        torch.cuda.synchronize()
+        counts = np.bincount(ids.cpu().numpy().ravel(), minlength=E)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    site = 4   # MOE_SITE_GATE_UP: the routed grouped gate/up GEMM streams 2/3 of the expert weights
+    B.timing_arm(site, K)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record()
+    for _ in range(K):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    gu_ms_total, gu_launches = B.timing_read(site)
+    ms_per_step = ev0.elapsed_time(ev1) / K
+    tokens_per_s = T * K / (ms_per_step * K / 1e3)
+
+    # ---- algorithmic work (what the method must move / compute)
+    active = int((counts > 0).sum())
+    esz = 1 if fp8 else 2
+    w_gu_b = 2 * I * H * esz + ((2 * I // 128) * (H // 128) * 4 if fp8 else 0)
+    w_d_b = H * I * esz + ((H // 128) * (I // 128) * 4 if fp8 else 0)
+    shared_b = 3 * Is * H * 2
+    router_b = 0 if cfg.triples else E * H * 2
+    layer_bytes = active * (w_gu_b + w_d_b) + shared_b + router_b + T * H * 2 * 2
+    fl_routed = 2.0 * N * 3 * I * H
+    fl_bf16 = 2.0 * T * 3 * Is * H + (0 if cfg.triples else 2.0 * T * E * H)
+    if not fp8:
+        fl_bf16 += fl_routed
+        fl_routed_fp8 = 0.0
+    else:
+        fl_routed_fp8 = fl_routed
+    t_s = ms_per_step / 1e3
+    mfma_util = (fl_routed_fp8 / (PEAK_TFLOPS["fp8"] * 1e12) + fl_bf16 / (PEAK_TFLOPS["bf16"] * 1e12)) / t_s
+    # gate/up kernel per launch: active experts' [gate; up] weights (+ scales), its input rows, its h output
+    gu_bytes = active * w_gu_b + N * H * esz + N * I * esz + ((N * H // 128 + N * I // 128) * 4 if fp8 else 0)
+    gu_flops = 2.0 * N * 2 * I * H
+    gu_ms = gu_ms_total / max(gu_launches, 1)
+    decode_like = (N / max(active, 1)) < 64
+    if decode_like:
+        roof = {"bound": "hbm", "achieved": round(gu_bytes / (gu_ms / 1e3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    else:
+        pk = PEAK_TFLOPS["fp8" if fp8 else "bf16"]
+        roof = {"bound": "mfma", "achieved": round(gu_flops / (gu_ms / 1e3) / 1e12, 1), "peak": pk,
+                "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = "gate_up_kernel (routed experts)"
+    roof["kernel_ms"] = round(gu_ms, 4)
+    roof["algorithmic_bytes_per_launch"] = int(gu_bytes)
+    roof["algorithmic_flops_per_launch"] = gu_flops
+
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8" if fp8 else "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": T, "hidden": H, "experts": E, "top_k": cfg.k,
+                   "inter": I, "shared_inter": Is, "expert_dtype": cfg.expert_dtype,
+                   "assignments": N, "active_experts": active, "max_rows_per_expert": int(counts.max()),
+                   "parallelism": "1 GPU"},
+        "layer": {"algorithmic_bytes": int(layer_bytes), "hbm_GBps": round(layer_bytes / t_s / 1e9, 1),
+                  "hbm_frac": round(layer_bytes / t_s / 1e9 / PEAK_HBM_GBS, 4),
+                  "tflops": round((fl_routed + fl_bf16) / t_s / 1e12, 2),
+                  "mfma_util_blended": round(mfma_util, 4), "wall_s": round(wall, 4)},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, lt, x, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, lt, x, target_s):
+    """The fp64 oracle on a bounded sample of tokens of the same workload."""
+    import numpy as np
+
+    import oracle
+    from router_gemm_amd import workloads as W
+
+    print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+    h = W.host_layer_arrays(lt)
+    L = oracle.Layer(cfg.H, cfg.I, cfg.E, max(cfg.k, 1), cfg.expert_dtype == "fp8", h["w_router"],
+                     h["w_gate_up"], h["w_down"], s_gate_up=h["s_gate_up"], s_down=h["s_down"],
+                     router_bias=h["router_bias"], w_shared_gate_up=h["w_shared_gate_up"],
+                     w_shared_down=h["w_shared_down"])
+    xb = W.bf16_bits(x)
+    rng = np.random.default_rng(0)
+    n = min(cfg.T, 64)
+    sample = np.sort(rng.choice(cfg.T, n, replace=False))
+    if cfg.triples:
+        tok, exp, gate = W.make_triples(cfg)
+        run = lambda: oracle.forward_triples(L, xb, tok, exp, gate, token_list=sample)
+    else:
+        run = lambda: oracle.forward(L, xb, token_list=sample)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        run()
+        done += n
+        el = time.perf_counter() - t0
+        if el >= target_s or done >= 4 * n:
+            break
+    return {"value": round(done / el, 2), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} of the {cfg.T} tokens of {cfg.name} (seeded choice), full layer per token, "
+                      f"{done // n} pass(es) in {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

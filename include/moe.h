@@ -1,0 +1,200 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed Mixture-of-Experts layer.
+ *
+ * The layer is the MoE feed-forward block of Step-5-Preview
+ * ("Step-5-Preview", NeMo AutoModel model coverage, section "Model
+ * Architecture": hidden 4,096; 352 routed experts per MoE layer; top-8
+ * routing; one shared expert; intermediate size 1,536 for every expert; a
+ * learned router), with BF16 or block-scaled FP8 E4M3 expert weights
+ * ("Step-5 minimal inference", introduction and "Contents": block-scaled FP8
+ * expert GEMM and MoE primitives; section "Install": FP8 E4M3; expert dtype
+ * chosen per layer by the checkpoint configuration, section "Checkpoints and
+ * launch modes"):
+ *
+ *   y[t] = Shared(x[t]) + sum_{e in TopK(t)} g[t,e] * FFN_e(x[t])
+ *   FFN(a) = (silu(a Wg^T) * (a Wu^T)) Wd^T
+ *
+ * Conventions for every call
+ *   - Pointers are DEVICE pointers unless stated otherwise; tensors are
+ *     row-major and contiguous, 16-byte aligned.  `stream` is a hipStream_t
+ *     passed as void* (NULL = the null stream).
+ *   - The caller owns every buffer (inputs, outputs, workspace).  The library
+ *     allocates and frees nothing and keeps no device state between calls.
+ *     Calls on distinct streams with distinct workspaces may run concurrently.
+ *   - Every call validates its arguments on the host before launching
+ *     anything and returns a status; on error nothing is launched and no
+ *     output is written.  T == 0 or N == 0 is a valid no-op.
+ *   - Every call only enqueues work on `stream` and returns; none
+ *     synchronises with the host.
+ *   - Results are deterministic: the same inputs give the same bits on every
+ *     run (no floating-point atomics; all sums in a fixed order).
+ *
+ * Numerics
+ *   - Router: bf16 x and W_r, fp32 accumulation; bias (fp32, optional) added
+ *     to the logits; the k largest logits are chosen, an exact tie going to
+ *     the lower expert index; the k slots are returned in ascending expert id;
+ *     gates = softmax over the k chosen logits (= softmax over all experts
+ *     renormalised over the chosen ones), fp32.
+ *   - FP8 mode: OCP E4M3FN codes (max 448, no infinities).  Weights carry one
+ *     fp32 scale per 128x128 block of [out, in]; activations (x, and the
+ *     intermediate h) carry one fp32 scale per token per 128 consecutive
+ *     input columns: s = amax/448 (IEEE fp32 division; 1 when amax == 0),
+ *     code = round-to-nearest-even(v / s).  Dequantised value = code * s.
+ *   - Expert GEMMs accumulate in fp32; h = silu(z_gate) * z_up in fp32, then
+ *     stored as bf16 (bf16 experts) or E4M3 + 1x128 scales (fp8 experts).
+ *   - Combine: fp32 sum in a fixed order -- shared expert first, then the
+ *     token's assignments in increasing assignment index -- rounded once to
+ *     the output dtype (the partial sums of the pages' deployment are likewise
+ *     added in a fixed order in FP32: "Step-5 minimal inference", section
+ *     "Long-output stability").
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_dtype {
+  MOE_BF16 = 1,        /* bfloat16 */
+  MOE_FP8_E4M3FN = 2,  /* OCP E4M3FN with fp32 block/group scales */
+  MOE_F32 = 3          /* IEEE binary32 */
+} moe_dtype;
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,        /* NULL pointer where one is required, bad size or dimension,
+                            k outside [1, min(E, 32)], misaligned pointer */
+  MOE_EUNSUPPORTED = 2,  /* valid but not built: H % 128 != 0; bf16 experts with I % 64 != 0;
+                            fp8 experts with I % 128 != 0; E > 1024; H > 16384;
+                            unsupported dtype combination */
+  MOE_EWORKSPACE = 3,    /* ws_bytes smaller than the call needs */
+  MOE_EHIP = 4           /* a HIP launch failed; moe_last_error() has the detail */
+} moe_status;
+
+/* One MoE layer (host struct; the pointers in it are device pointers).
+ *   hidden H, inter I (routed expert intermediate), num_experts E (experts
+ *   held here: 352 for the whole layer, 44 for one of eight expert-parallel
+ *   shares), top_k k (0 allowed only for calls that take pre-routed
+ *   assignments), shared_inter Is (0 = no shared expert).
+ *   expert_dtype: MOE_BF16 or MOE_FP8_E4M3FN.
+ *   w_router        bf16 [E, H]            (moe_route / moe_forward only)
+ *   router_bias     f32  [E] or NULL       (added to the logits)
+ *   w_gate_up       [E, 2I, H]: rows 0..I-1 gate, rows I..2I-1 up  (bf16 or e4m3)
+ *   s_gate_up       f32 [E, 2I/128, H/128] (fp8 only, else NULL)
+ *   w_down          [E, H, I]              (bf16 or e4m3)
+ *   s_down          f32 [E, H/128, I/128]  (fp8 only, else NULL)
+ *   w_shared_gate_up bf16 [2Is, H], w_shared_down bf16 [H, Is] (NULL if Is == 0)
+ * Weights are read-only; they are the layout of a linear layer's weight
+ * ([out, in]; y = a W^T). */
+typedef struct moe_layer {
+  int32_t hidden;
+  int32_t inter;
+  int32_t num_experts;
+  int32_t top_k;
+  int32_t shared_inter;
+  int32_t expert_dtype;
+  const void *w_router;
+  const float *router_bias;
+  const void *w_gate_up;
+  const float *s_gate_up;
+  const void *w_down;
+  const float *s_down;
+  const void *w_shared_gate_up;
+  const void *w_shared_down;
+} moe_layer;
+
+/* Workspace bytes that suffice for every call below on this layer with up to
+ * T tokens and N assignments (N = T*k for routed calls).  Host-only; 0 on
+ * invalid arguments. */
+size_t moe_workspace_bytes(const moe_layer *layer, int64_t T, int64_t N);
+
+/* Router: logits, top-k selection and gates.
+ * ("Step-5-Preview", section "Model Architecture": learned router, top-8 of
+ * 352 routed experts.)
+ *   x           bf16 [T, H]
+ *   topk_ids    int32 [T, k] out: chosen experts, ascending per token
+ *   topk_gates  f32 [T, k] out: softmax over the chosen logits (same slots)
+ *   logits      f32 [T, E] out, or NULL: router logits including the bias */
+moe_status moe_route(const moe_layer *layer, const void *x, int64_t T,
+                     int32_t *topk_ids, float *topk_gates, float *logits,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/* Token-to-expert grouping: a stable counting sort of the N assignments by
+ * expert (histogram, exclusive scan, ordered scatter), then a row gather of
+ * x into expert order; in fp8 mode each gathered row is quantised per 1x128
+ * group.  ("Step-5 minimal inference", "Contents": the MoE primitives.)
+ *   x              bf16 [T, H]
+ *   assign_expert  int32 [N]: expert of assignment i (e.g. topk_ids viewed as [T*k])
+ *   assign_token   int32 [N] or NULL: token of assignment i (NULL: i / k)
+ *   expert_offsets int32 [E+1] out: rows of expert e are offsets[e]..offsets[e+1]-1
+ *   perm_src       int32 [N] out: assignment index placed at row p (rows in
+ *                  expert order; inside an expert, increasing assignment index)
+ *   perm_pos       int32 [N] out: row of assignment i (-1 if its expert or
+ *                  token is out of range: such assignments are dropped)
+ *   x_perm         [N, H] out: bf16 (bf16 experts) or e4m3 codes (fp8 experts);
+ *                  rows >= offsets[E] are left unwritten
+ *   x_scale        f32 [N, H/128] out (fp8 experts; NULL for bf16) */
+moe_status moe_permute(const moe_layer *layer, const void *x, int64_t T,
+                       const int32_t *assign_expert, const int32_t *assign_token, int64_t N,
+                       int32_t *expert_offsets, int32_t *perm_src, int32_t *perm_pos,
+                       void *x_perm, float *x_scale,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* Grouped expert FFN: for every expert e, rows offsets[e]..offsets[e+1]-1 of
+ * x_perm go through gate/up (one grouped GEMM with a fused SwiGLU epilogue),
+ * then down (a second grouped GEMM).  ("Step-5 minimal inference",
+ * introduction: block-scaled FP8 expert GEMM; "Step-5-Preview", "Model
+ * Architecture": intermediate 1,536 per expert.)
+ *   expert_offsets int32 [E+1] (device; offsets[E] <= N)
+ *   x_perm         [N, H] bf16 or e4m3 (the layer's expert dtype)
+ *   x_scale        f32 [N, H/128] (fp8 experts; NULL for bf16)
+ *   y_perm         [N, H] out, y_dtype MOE_BF16 or MOE_F32; rows >= offsets[E]
+ *                  are left unwritten
+ * The shared expert runs through this call as a one-expert bf16 layer
+ * (num_experts = 1, inter = Is, w_gate_up/w_down = the shared weights,
+ * offsets {0, T}, x_perm = x). */
+moe_status moe_expert_ffn(const moe_layer *layer, const int32_t *expert_offsets,
+                          const void *x_perm, const float *x_scale, int64_t N,
+                          void *y_perm, int32_t y_dtype,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/* Weighted un-permute and combine, adding the shared-expert output:
+ *   y[t] = shared[t] + sum_{i: token(i) = t} gates[i] * y_perm[perm_pos[i]]
+ * in fp32, shared first, then increasing i; rounded once to out_dtype.
+ *   y_perm       [N, H] (y_dtype MOE_BF16 or MOE_F32)
+ *   perm_pos     int32 [N]  (-1: assignment skipped)
+ *   assign_token int32 [N] or NULL (NULL: token(i) = i / k)
+ *   gates        f32 [N]
+ *   shared_out   [T, H] (shared_dtype MOE_BF16 or MOE_F32) or NULL
+ *   y            [T, H] out (out_dtype MOE_BF16 or MOE_F32); tokens with no
+ *                assignment get the shared output (or 0). */
+moe_status moe_combine(const moe_layer *layer, const void *y_perm, int32_t y_dtype,
+                       const int32_t *perm_pos, const int32_t *assign_token,
+                       const float *gates, int64_t N,
+                       const void *shared_out, int32_t shared_dtype, int64_t T,
+                       void *y, int32_t out_dtype,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* The whole layer: route -> permute -> routed expert FFN -> shared expert
+ * FFN -> combine, all on `stream`.
+ *   x          bf16 [T, H]
+ *   y          [T, H] out (MOE_BF16 or MOE_F32)
+ *   topk_ids   int32 [T, k] out or NULL;  topk_gates f32 [T, k] out or NULL */
+moe_status moe_forward(const moe_layer *layer, const void *x, int64_t T,
+                       void *y, int32_t out_dtype,
+                       int32_t *topk_ids, float *topk_gates,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* Static string naming a status. */
+const char *moe_status_string(moe_status s);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,357 @@
+// expert_gemm.hip -- grouped expert GEMMs on gfx950 MFMA:
+//   gate/up:  z = a W_gu[e]^T (one grouped GEMM over [gate; up] rows), fused
+//             SwiGLU epilogue h = silu(z_gate) * z_up, h stored as bf16 or as
+//             E4M3 with one fp32 scale per token per 128 columns;
+//   down:     o = h W_d[e]^T.
+// ("Step-5 minimal inference", introduction: block-scaled FP8 expert GEMM;
+// "Step-5-Preview", "Model Architecture": each expert is 4,096 -> 1,536 -> 4,096
+// and the parameter count gives three such matrices, a gated FFN.)
+//
+// Operand roles.  Weights are the MFMA A operand (rows n of [out, in]) and
+// token rows the B operand, so each lane's four accumulators are four
+// consecutive output columns of one token.  Both operands are K-contiguous in
+// memory: a lane reads 32 contiguous bytes of its row per 128-byte K chunk
+// (128 e4m3 codes or 64 bf16 values), so no transposes are needed.
+//
+// FP8 block scales.  A K chunk of 128 codes is exactly one weight block column
+// and one activation group, so one 16x16x128 MFMA yields the raw block
+// product, and acc += P * (s_w * s_a[token]) applies both scales in fp32.
+//
+// Work decomposition.  A device-built list holds one entry per (expert,
+// 16*MT-row tile of that expert's rows); blockIdx.y indexes it (entries past
+// the device-side count exit at once), blockIdx.x the output-column tile.
+// The host never reads the per-expert counts.
+
+#include "moe_common.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+struct TileEntry {
+  int32_t e;
+  int32_t m0;
+};
+
+// One workgroup (1024 threads, E <= 1024): tiles of 16*MT rows per expert, in
+// expert order.
+__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__restrict__ off, int E, int bm,
+                                                           int max_tiles, TileEntry *__restrict__ tiles,
+                                                           int32_t *__restrict__ ntiles) {
+  __shared__ int32_t buf[1024];
+  const int tid = threadIdx.x;
+  const int n = tid < E ? max(off[tid + 1] - off[tid], 0) : 0;
+  const int cnt = (n + bm - 1) / bm;
+  buf[tid] = cnt;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int32_t add = tid >= o ? buf[tid - o] : 0;
+    __syncthreads();
+    buf[tid] += add;
+    __syncthreads();
+  }
+  const int base = buf[tid] - cnt;
+  for (int j = 0; j < cnt; ++j)
+    if (base + j < max_tiles) tiles[base + j] = TileEntry{tid, j * bm};
+  if (tid == 1023) *ntiles = min(buf[1023], max_tiles);
+}
+
+// Operand fragment of one lane for one 128-byte K chunk: 32 bytes.
+struct Frag {
+  i32x4 lo, hi;
+};
+
+__device__ __forceinline__ Frag load_frag(const uint8_t *p) { return Frag{load16(p), load16(p + 16)}; }
+
+__device__ __forceinline__ i32x8 frag_fp8(const Frag &f) {
+  return i32x8{f.lo[0], f.lo[1], f.lo[2], f.lo[3], f.hi[0], f.hi[1], f.hi[2], f.hi[3]};
+}
+
+// acc += A(16 rows x chunk) * B(chunk x 16 tokens)
+template <bool FP8>
+__device__ __forceinline__ f32x4 chunk_mma(const Frag &a, const Frag &b, f32x4 acc, float scale) {
+  if constexpr (FP8) {
+    const f32x4 p = mfma_fp8(frag_fp8(a), frag_fp8(b), f32x4{0.f, 0.f, 0.f, 0.f});
+    acc[0] += p[0] * scale;
+    acc[1] += p[1] * scale;
+    acc[2] += p[2] * scale;
+    acc[3] += p[3] * scale;
+    return acc;
+  } else {
+    acc = mfma_bf16(__builtin_bit_cast(bf16x8, a.lo), __builtin_bit_cast(bf16x8, b.lo), acc);
+    return mfma_bf16(__builtin_bit_cast(bf16x8, a.hi), __builtin_bit_cast(bf16x8, b.hi), acc);
+  }
+}
+
+__device__ __forceinline__ float silu(float z) { return __fdiv_rn(z, 1.0f + expf(-z)); }
+
+struct GateUpArgs {
+  const uint8_t *x;        // [N, H] rows in expert order (e4m3 codes or bf16)
+  const float *xs;         // [N, H/128] (fp8)
+  const uint8_t *w;        // [E, 2I, H]
+  const float *ws;         // [E, 2I/128, H/128] (fp8)
+  const int32_t *off;      // [E+1]
+  const TileEntry *tiles;
+  const int32_t *ntiles;
+  uint8_t *h;              // [N, I] bf16 or e4m3
+  float *hs;               // [N, I/128] (fp8)
+  int H, I, nrows;         // rows at or beyond nrows are never read or written
+};
+
+// Workgroup: 4 waves x (GW gate + GW up 16-row weight tiles) = 64*GW h
+// columns, 16*MT token rows.
+template <bool FP8, int MT, int GW>
+__global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
+  constexpr int ESZ = FP8 ? 1 : 2;
+  if ((int)blockIdx.y >= a.ntiles[0]) return;
+  const TileEntry te = a.tiles[blockIdx.y];
+  const int lane = lane_id(), w = wave_id();
+  const int rend = min(max(a.off[te.e + 1], 0), a.nrows);
+  const int rbeg = min(max(a.off[te.e], 0) + te.m0, rend);
+  const int H = a.H, I = a.I;
+  const int64_t rowb = (int64_t)H * ESZ;
+  const int hc0 = blockIdx.x * (64 * GW) + w * (16 * GW);
+  const int koff = 32 * (lane >> 4);
+
+  const uint8_t *wbase = a.w + (int64_t)te.e * 2 * I * rowb;
+  const uint8_t *wg[GW], *wu[GW];
+#pragma unroll
+  for (int i = 0; i < GW; ++i) {
+    wg[i] = wbase + (int64_t)(hc0 + 16 * i + (lane & 15)) * rowb + koff;
+    wu[i] = wbase + (int64_t)(I + hc0 + 16 * i + (lane & 15)) * rowb + koff;
+  }
+  const uint8_t *xr[MT];
+  bool xv[MT];
+  int xrow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    xrow[m] = rbeg + 16 * m + (lane & 15);
+    xv[m] = xrow[m] < rend;
+    xr[m] = a.x + (int64_t)(xv[m] ? xrow[m] : rbeg) * rowb + koff;
+  }
+  f32x4 ag[GW][MT], au[GW][MT];
+#pragma unroll
+  for (int i = 0; i < GW; ++i)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) ag[i][m] = au[i][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nchunk = (int)(rowb / 128);
+  const int KB = H / 128;
+  const float *sg = FP8 ? a.ws + ((int64_t)te.e * (2 * I / 128) + hc0 / 128) * KB : nullptr;
+  const float *su = FP8 ? a.ws + ((int64_t)te.e * (2 * I / 128) + (I + hc0) / 128) * KB : nullptr;
+  const Frag zf = Frag{i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
+
+  for (int c = 0; c < nchunk; ++c) {
+    const int64_t kb = (int64_t)c * 128;
+    Frag fg[GW], fu[GW], fx[MT];
+#pragma unroll
+    for (int i = 0; i < GW; ++i) {
+      fg[i] = load_frag(wg[i] + kb);
+      fu[i] = load_frag(wu[i] + kb);
+    }
+    float sx[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      fx[m] = xv[m] ? load_frag(xr[m] + kb) : zf;
+      sx[m] = (FP8 && xv[m]) ? a.xs[(int64_t)xrow[m] * KB + c] : 0.f;
+    }
+    const float swg = FP8 ? sg[c] : 0.f;
+    const float swu = FP8 ? su[c] : 0.f;
+#pragma unroll
+    for (int i = 0; i < GW; ++i)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        ag[i][m] = chunk_mma<FP8>(fg[i], fx[m], ag[i][m], swg * sx[m]);
+        au[i][m] = chunk_mma<FP8>(fu[i], fx[m], au[i][m], swu * sx[m]);
+      }
+  }
+
+  // Epilogue: lane holds columns hc0 + 16i + 4*(lane/16) + r of token row xrow[m].
+  float hv[GW][MT][4];
+#pragma unroll
+  for (int i = 0; i < GW; ++i)
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hv[i][m][r] = silu(ag[i][m][r]) * au[i][m][r];
+
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int i = 0; i < GW; ++i) {
+      const int col = hc0 + 16 * i + 4 * (lane >> 4);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (!xv[m]) continue;
+        const uint32_t lo = f32_to_bf16(hv[i][m][0]) | (f32_to_bf16(hv[i][m][1]) << 16);
+        const uint32_t hi = f32_to_bf16(hv[i][m][2]) | (f32_to_bf16(hv[i][m][3]) << 16);
+        *reinterpret_cast<uint2 *>(a.h + ((int64_t)xrow[m] * I + col) * 2) = make_uint2(lo, hi);
+      }
+    }
+  } else {
+    // 1x128 group of h = the workgroup's 128 columns (GW == 2): amax over the
+    // lane's 8 values, the 4 lanes sharing the token, then the 4 waves.
+    __shared__ float red[4][16 * MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      float am = 0.f;
+#pragma unroll
+      for (int i = 0; i < GW; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) am = __builtin_fmaxf(am, __builtin_fabsf(hv[i][m][r]));
+      am = __builtin_fmaxf(am, __shfl_xor(am, 16, kWave));
+      am = __builtin_fmaxf(am, __shfl_xor(am, 32, kWave));
+      if (lane < 16) red[w][16 * m + lane] = am;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int tl = 16 * m + (lane & 15);
+      const float am = __builtin_fmaxf(__builtin_fmaxf(red[0][tl], red[1][tl]),
+                                       __builtin_fmaxf(red[2][tl], red[3][tl]));
+      const float s = group_scale(am);
+      if (!xv[m]) continue;
+#pragma unroll
+      for (int i = 0; i < GW; ++i) {
+        const int col = hc0 + 16 * i + 4 * (lane >> 4);
+        const uint32_t q = f32x4_to_e4m3(__fdiv_rn(hv[i][m][0], s), __fdiv_rn(hv[i][m][1], s),
+                                         __fdiv_rn(hv[i][m][2], s), __fdiv_rn(hv[i][m][3], s));
+        *reinterpret_cast<uint32_t *>(a.h + (int64_t)xrow[m] * I + col) = q;
+      }
+      if (w == 0 && lane < 16) a.hs[(int64_t)xrow[m] * (I / 128) + blockIdx.x] = s;
+    }
+  }
+}
+
+struct DownArgs {
+  const uint8_t *h;        // [N, I]
+  const float *hs;         // [N, I/128] (fp8)
+  const uint8_t *w;        // [E, H, I]
+  const float *ws;         // [E, H/128, I/128] (fp8)
+  const int32_t *off;
+  const TileEntry *tiles;
+  const int32_t *ntiles;
+  void *y;                 // [N, H] bf16 or f32
+  int H, I, y_f32, nrows;
+};
+
+// Workgroup: 4 waves x NW 16-column output tiles = 64*NW columns, 16*MT rows.
+template <bool FP8, int MT, int NW>
+__global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
+  constexpr int ESZ = FP8 ? 1 : 2;
+  if ((int)blockIdx.y >= a.ntiles[0]) return;
+  const TileEntry te = a.tiles[blockIdx.y];
+  const int lane = lane_id(), w = wave_id();
+  const int rend = min(max(a.off[te.e + 1], 0), a.nrows);
+  const int rbeg = min(max(a.off[te.e], 0) + te.m0, rend);
+  const int H = a.H, I = a.I;
+  const int64_t rowb = (int64_t)I * ESZ;
+  const int c0 = blockIdx.x * (64 * NW) + w * (16 * NW);
+  const int koff = 32 * (lane >> 4);
+  const uint8_t *wbase = a.w + (int64_t)te.e * H * rowb;
+  const uint8_t *wr[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) wr[i] = wbase + (int64_t)(c0 + 16 * i + (lane & 15)) * rowb + koff;
+  const uint8_t *hr[MT];
+  bool hv[MT];
+  int hrow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    hrow[m] = rbeg + 16 * m + (lane & 15);
+    hv[m] = hrow[m] < rend;
+    hr[m] = a.h + (int64_t)(hv[m] ? hrow[m] : rbeg) * rowb + koff;
+  }
+  f32x4 acc[NW][MT];
+#pragma unroll
+  for (int i = 0; i < NW; ++i)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[i][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nchunk = (int)(rowb / 128);
+  const int KB = I / 128;
+  const Frag zf = Frag{i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
+  for (int c = 0; c < nchunk; ++c) {
+    const int64_t kb = (int64_t)c * 128;
+    Frag fw[NW], fh[MT];
+    float sw[NW], sh[MT];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      fw[i] = load_frag(wr[i] + kb);
+      sw[i] = FP8 ? a.ws[((int64_t)te.e * (H / 128) + (c0 + 16 * i) / 128) * KB + c] : 0.f;
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      fh[m] = hv[m] ? load_frag(hr[m] + kb) : zf;
+      sh[m] = (FP8 && hv[m]) ? a.hs[(int64_t)hrow[m] * KB + c] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[i][m] = chunk_mma<FP8>(fw[i], fh[m], acc[i][m], sw[i] * sh[m]);
+  }
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int col = c0 + 16 * i + 4 * (lane >> 4);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (!hv[m]) continue;
+      const int64_t o = (int64_t)hrow[m] * H + col;
+      if (a.y_f32) {
+        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.y) + o) = acc[i][m];
+      } else {
+        const uint32_t lo = f32_to_bf16(acc[i][m][0]) | (f32_to_bf16(acc[i][m][1]) << 16);
+        const uint32_t hi = f32_to_bf16(acc[i][m][2]) | (f32_to_bf16(acc[i][m][3]) << 16);
+        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.y) + o) = make_uint2(lo, hi);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- host side
+
+FfnPlan ffn_plan(int64_t N, int E) {
+  FfnPlan p;
+  const double avg = E > 0 ? (double)N / E : 0.0;
+  p.mt = avg <= 16 ? 1 : (avg <= 32 ? 2 : 4);
+  p.max_tiles = (int)(cdiv(N, 16 * p.mt) + (N < E ? N : E) + 1);
+  return p;
+}
+
+size_t ffn_tiles_bytes(const FfnPlan &p) { return align_up(sizeof(TileEntry) * (size_t)p.max_tiles + 256, 256); }
+
+template <bool FP8, int MT>
+static hipError_t run_ffn(const GateUpArgs &gu, const DownArgs &dn, int E, int H, int I, const FfnPlan &plan,
+                          TileEntry *tiles, int32_t *ntiles, int site, hipStream_t st) {
+  build_tiles_kernel<<<1, 1024, 0, st>>>(gu.off, E, 16 * MT, plan.max_tiles, tiles, ntiles);
+  timing_before(site, st);
+  if (I % 128 == 0) {
+    dim3 g1((unsigned)(I / 128), (unsigned)plan.max_tiles);
+    gate_up_kernel<FP8, MT, 2><<<g1, 256, 0, st>>>(gu);
+  } else {
+    if constexpr (FP8) return hipErrorInvalidValue;
+    dim3 g1((unsigned)(I / 64), (unsigned)plan.max_tiles);
+    gate_up_kernel<FP8, MT, 1><<<g1, 256, 0, st>>>(gu);
+  }
+  timing_after(site, st);
+  dim3 g2((unsigned)(H / 128), (unsigned)plan.max_tiles);
+  timing_before(site + 1, st);
+  down_kernel<FP8, MT, 2><<<g2, 256, 0, st>>>(dn);
+  timing_after(site + 1, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_ffn(const uint8_t *x, const float *xs, const uint8_t *w_gu, const float *s_gu,
+                             const uint8_t *w_d, const float *s_d, const int32_t *offsets, int E, int H,
+                             int I, int64_t N, bool fp8, const FfnPlan &plan, int32_t *tiles_ws,
+                             uint8_t *h, float *hs, void *y, bool y_f32, bool shared_site, hipStream_t st) {
+  if (N == 0) return hipSuccess;
+  int32_t *ntiles = tiles_ws;
+  TileEntry *tiles = reinterpret_cast<TileEntry *>(tiles_ws + 64);
+  GateUpArgs gu{x, xs, w_gu, s_gu, offsets, tiles, ntiles, h, hs, H, I, (int)N};
+  DownArgs dn{h, hs, w_d, s_d, offsets, tiles, ntiles, y, H, I, y_f32 ? 1 : 0, (int)N};
+#define MOE_FFN_CASE(F, M) \
+  if (fp8 == F && plan.mt == M) return run_ffn<F, M>(gu, dn, E, H, I, plan, tiles, ntiles, shared_site ? 6 : 4, st);
+  MOE_FFN_CASE(true, 1) MOE_FFN_CASE(true, 2) MOE_FFN_CASE(true, 4)
+  MOE_FFN_CASE(false, 1) MOE_FFN_CASE(false, 2) MOE_FFN_CASE(false, 4)
+#undef MOE_FFN_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -1,0 +1,402 @@
+// moe_api.cpp -- the C ABI declared in include/moe.h: host-side argument
+// validation (everything is checked before anything is launched), workspace
+// carving, and the launch sequence of each call.  No allocation, no host
+// synchronisation, no device state kept between calls.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/moe.h"
+#include "moe_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+moe_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxK = 32;
+constexpr int kMaxE = 1024;
+constexpr int kMaxH = 65536;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool is_fp8(const moe_layer *L) { return L->expert_dtype == MOE_FP8_E4M3FN; }
+size_t esz(const moe_layer *L) { return is_fp8(L) ? 1 : 2; }
+
+// Sequential carving of the caller's workspace.
+struct Carve {
+  char *base;
+  size_t used = 0;
+  explicit Carve(void *b) : base(static_cast<char *>(b)) {}
+  template <class T>
+  T *take(size_t count) {
+    const size_t off = moe::align_up(used, kAlign);
+    used = off + moe::align_up(count * sizeof(T), kAlign);
+    return base ? reinterpret_cast<T *>(base + off) : nullptr;
+  }
+};
+
+// ---------------------------------------------------------------- validation
+
+moe_status check_layer_shape(const moe_layer *L, bool need_router) {
+  if (!L) return fail(MOE_EINVAL, "layer is NULL");
+  if (L->hidden <= 0 || L->inter <= 0 || L->num_experts <= 0 || L->shared_inter < 0)
+    return fail(MOE_EINVAL, "bad layer dimensions H=%d I=%d E=%d Is=%d", L->hidden, L->inter,
+                L->num_experts, L->shared_inter);
+  if (L->expert_dtype != MOE_BF16 && L->expert_dtype != MOE_FP8_E4M3FN)
+    return fail(MOE_EUNSUPPORTED, "expert_dtype %d is not MOE_BF16 or MOE_FP8_E4M3FN", L->expert_dtype);
+  if (L->hidden % 128 != 0 || L->hidden > kMaxH)
+    return fail(MOE_EUNSUPPORTED, "hidden %d must be a multiple of 128 and <= %d", L->hidden, kMaxH);
+  if (L->num_experts > kMaxE) return fail(MOE_EUNSUPPORTED, "num_experts %d > %d", L->num_experts, kMaxE);
+  if (is_fp8(L) && L->inter % 128 != 0)
+    return fail(MOE_EUNSUPPORTED, "fp8 experts need inter %% 128 == 0 (inter=%d)", L->inter);
+  if (!is_fp8(L) && L->inter % 64 != 0)
+    return fail(MOE_EUNSUPPORTED, "bf16 experts need inter %% 64 == 0 (inter=%d)", L->inter);
+  if (L->shared_inter % 64 != 0)
+    return fail(MOE_EUNSUPPORTED, "shared_inter %% 64 != 0 (%d)", L->shared_inter);
+  if (need_router && (L->top_k < 1 || L->top_k > kMaxK || L->top_k > L->num_experts))
+    return fail(MOE_EINVAL, "top_k %d outside [1, min(E=%d, %d)]", L->top_k, L->num_experts, kMaxK);
+  if (L->top_k < 0 || L->top_k > kMaxK) return fail(MOE_EINVAL, "top_k %d outside [0, %d]", L->top_k, kMaxK);
+  return MOE_OK;
+}
+
+moe_status check_expert_weights(const moe_layer *L) {
+  if (!L->w_gate_up || !L->w_down) return fail(MOE_EINVAL, "expert weights are NULL");
+  if (!aligned16(L->w_gate_up) || !aligned16(L->w_down)) return fail(MOE_EINVAL, "expert weights not 16-byte aligned");
+  if (is_fp8(L) && (!L->s_gate_up || !L->s_down)) return fail(MOE_EINVAL, "fp8 experts need s_gate_up and s_down");
+  return MOE_OK;
+}
+
+moe_status check_shared(const moe_layer *L) {
+  if (L->shared_inter == 0) return MOE_OK;
+  if (!L->w_shared_gate_up || !L->w_shared_down) return fail(MOE_EINVAL, "shared expert weights are NULL");
+  if (!aligned16(L->w_shared_gate_up) || !aligned16(L->w_shared_down))
+    return fail(MOE_EINVAL, "shared expert weights not 16-byte aligned");
+  return MOE_OK;
+}
+
+moe_status check_rows(int64_t T, int64_t N) {
+  if (T < 0 || N < 0) return fail(MOE_EINVAL, "negative size T=%lld N=%lld", (long long)T, (long long)N);
+  if (T > (int64_t)INT32_MAX / 2 || N > (int64_t)INT32_MAX / 2)
+    return fail(MOE_EINVAL, "size too large T=%lld N=%lld", (long long)T, (long long)N);
+  return MOE_OK;
+}
+
+moe_status check_ws(const void *ws, size_t ws_bytes, size_t need) {
+  if (need > ws_bytes)
+    return fail(MOE_EWORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
+  if (need > 0 && !ws) return fail(MOE_EINVAL, "workspace is NULL");
+  if (((uintptr_t)ws & (kAlign - 1)) != 0) return fail(MOE_EINVAL, "workspace not %zu-byte aligned", kAlign);
+  return MOE_OK;
+}
+
+bool out_dtype_ok(int32_t d) { return d == MOE_BF16 || d == MOE_F32; }
+
+// ---------------------------------------------------------------- workspace plans
+
+struct RouteWs {
+  float *partial;
+  int S;
+};
+RouteWs carve_route(Carve &c, const moe_layer *L, int64_t T) {
+  RouteWs r;
+  r.S = moe::router_ksplit(T, L->num_experts, L->hidden);
+  r.partial = c.take<float>((size_t)r.S * T * L->num_experts + 1);
+  return r;
+}
+
+int32_t *carve_sort(Carve &c, int64_t N, int64_t nbins) { return c.take<int32_t>(moe::sort_ws_words(N, nbins) + 1); }
+
+struct FfnWs {
+  moe::FfnPlan plan;
+  int32_t *tiles;
+  uint8_t *h;
+  float *hs;
+};
+FfnWs carve_ffn(Carve &c, int64_t N, int E, int I, bool fp8) {
+  FfnWs f;
+  f.plan = moe::ffn_plan(N, E);
+  f.tiles = c.take<int32_t>(moe::ffn_tiles_bytes(f.plan) / 4);
+  f.h = c.take<uint8_t>((size_t)N * I * (fp8 ? 1 : 2) + 16);
+  f.hs = fp8 ? c.take<float>((size_t)N * (I / 128) + 1) : nullptr;
+  return f;
+}
+
+struct CombineWs {
+  int32_t *tok_off, *tok_list, *sort;
+};
+CombineWs carve_combine(Carve &c, int64_t T, int64_t N) {
+  CombineWs w;
+  w.tok_off = c.take<int32_t>((size_t)T + 1);
+  w.tok_list = c.take<int32_t>((size_t)N + 1);
+  w.sort = carve_sort(c, N, T);
+  return w;
+}
+
+struct ForwardWs {
+  int32_t *ids;
+  float *gates;
+  RouteWs route;
+  int32_t *offsets, *perm_src, *perm_pos, *sort;
+  uint8_t *x_perm;
+  float *x_scale;
+  FfnWs ffn;
+  uint16_t *y_perm;
+  int32_t *sh_off;
+  FfnWs sh_ffn;
+  void *sh_out;
+};
+ForwardWs carve_forward(Carve &c, const moe_layer *L, int64_t T, bool out_f32) {
+  ForwardWs f;
+  const int64_t N = T * L->top_k;
+  const int H = L->hidden, E = L->num_experts;
+  f.ids = c.take<int32_t>((size_t)N + 1);
+  f.gates = c.take<float>((size_t)N + 1);
+  f.route = carve_route(c, L, T);
+  f.offsets = c.take<int32_t>((size_t)E + 1);
+  f.perm_src = c.take<int32_t>((size_t)N + 1);
+  f.perm_pos = c.take<int32_t>((size_t)N + 1);
+  f.sort = carve_sort(c, N, E);
+  f.x_perm = c.take<uint8_t>((size_t)N * H * esz(L) + 16);
+  f.x_scale = is_fp8(L) ? c.take<float>((size_t)N * (H / 128) + 1) : nullptr;
+  f.ffn = carve_ffn(c, N, E, L->inter, is_fp8(L));
+  f.y_perm = c.take<uint16_t>((size_t)N * H + 8);
+  if (L->shared_inter > 0) {
+    f.sh_off = c.take<int32_t>(2);
+    f.sh_ffn = carve_ffn(c, T, 1, L->shared_inter, false);
+    f.sh_out = c.take<uint8_t>((size_t)T * H * (out_f32 ? 4 : 2) + 16);
+  } else {
+    f.sh_off = nullptr;
+    f.sh_out = nullptr;
+  }
+  return f;
+}
+
+size_t need_route(const moe_layer *L, int64_t T) { Carve c(nullptr); carve_route(c, L, T); return c.used; }
+size_t need_permute(const moe_layer *L, int64_t N) { Carve c(nullptr); carve_sort(c, N, L->num_experts); return c.used; }
+size_t need_ffn(int64_t N, int E, int I, bool fp8) { Carve c(nullptr); carve_ffn(c, N, E, I, fp8); return c.used; }
+size_t need_combine(int64_t T, int64_t N, bool tokens) {
+  if (!tokens) return 0;
+  Carve c(nullptr);
+  carve_combine(c, T, N);
+  return c.used;
+}
+size_t need_forward(const moe_layer *L, int64_t T) {
+  Carve c(nullptr);
+  carve_forward(c, L, T, true);
+  return c.used;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: configuration not built";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace too small";
+    case MOE_EHIP: return "MOE_EHIP: HIP launch failed";
+  }
+  return "unknown moe_status";
+}
+
+const char *moe_last_error(void) { return g_last_error.c_str(); }
+
+size_t moe_workspace_bytes(const moe_layer *L, int64_t T, int64_t N) {
+  if (check_layer_shape(L, false) != MOE_OK || check_rows(T, N) != MOE_OK) return 0;
+  size_t need = 0;
+  auto upd = [&](size_t v) { need = v > need ? v : need; };
+  upd(need_permute(L, N));
+  upd(need_ffn(N, L->num_experts, L->inter, is_fp8(L)));
+  upd(need_combine(T, N, true));
+  if (L->shared_inter > 0) upd(need_ffn(T, 1, L->shared_inter, false));
+  if (L->top_k >= 1) {
+    upd(need_route(L, T));
+    upd(need_forward(L, T));
+  }
+  return need;
+}
+
+moe_status moe_route(const moe_layer *L, const void *x, int64_t T, int32_t *topk_ids, float *topk_gates,
+                     float *logits, void *ws, size_t ws_bytes, void *stream) {
+  moe_status s;
+  if ((s = check_layer_shape(L, true)) != MOE_OK) return s;
+  if ((s = check_rows(T, 0)) != MOE_OK) return s;
+  if (T > 0) {
+    if (!L->w_router || !x || !topk_ids || !topk_gates) return fail(MOE_EINVAL, "NULL router argument");
+    if (!aligned16(x) || !aligned16(L->w_router)) return fail(MOE_EINVAL, "x or w_router not 16-byte aligned");
+  }
+  if (T == 0) return MOE_OK;
+  if ((s = check_ws(ws, ws_bytes, need_route(L, T))) != MOE_OK) return s;
+  Carve c(ws);
+  RouteWs r = carve_route(c, L, T);
+  return hip_status(moe::launch_router(static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(L->w_router),
+                                       L->router_bias, T, L->num_experts, L->hidden, L->top_k, r.partial, r.S,
+                                       topk_ids, topk_gates, logits, (hipStream_t)stream),
+                    "moe_route");
+}
+
+moe_status moe_permute(const moe_layer *L, const void *x, int64_t T, const int32_t *assign_expert,
+                       const int32_t *assign_token, int64_t N, int32_t *expert_offsets, int32_t *perm_src,
+                       int32_t *perm_pos, void *x_perm, float *x_scale, void *ws, size_t ws_bytes,
+                       void *stream) {
+  moe_status s;
+  if ((s = check_layer_shape(L, false)) != MOE_OK) return s;
+  if ((s = check_rows(T, N)) != MOE_OK) return s;
+  if (!assign_token) {
+    if (L->top_k < 1) return fail(MOE_EINVAL, "assign_token is NULL but top_k < 1");
+    if (N != T * L->top_k) return fail(MOE_EINVAL, "N=%lld != T*k=%lld without assign_token", (long long)N,
+                                       (long long)(T * L->top_k));
+  }
+  if (!expert_offsets) return fail(MOE_EINVAL, "expert_offsets is NULL");
+  if (N > 0) {
+    if (!x || !assign_expert || !perm_src || !perm_pos || !x_perm) return fail(MOE_EINVAL, "NULL permute argument");
+    if (is_fp8(L) && !x_scale) return fail(MOE_EINVAL, "fp8 experts need x_scale");
+    if (!aligned16(x) || !aligned16(x_perm)) return fail(MOE_EINVAL, "x or x_perm not 16-byte aligned");
+  }
+  if ((s = check_ws(ws, ws_bytes, need_permute(L, N))) != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;  // N == 0 still writes expert_offsets (all zero)
+  Carve c(ws);
+  int32_t *sort = carve_sort(c, N, L->num_experts);
+  hipError_t e = moe::launch_counting_sort(assign_expert, assign_token, T, N, L->num_experts, expert_offsets,
+                                           perm_src, perm_pos, sort, st);
+  if (e != hipSuccess) return hip_status(e, "moe_permute: sort");
+  e = moe::launch_gather_rows(static_cast<const uint16_t *>(x), L->hidden, perm_src, assign_token, L->top_k, N,
+                              expert_offsets + L->num_experts, is_fp8(L), x_perm, x_scale, st);
+  return hip_status(e, "moe_permute: gather");
+}
+
+moe_status moe_expert_ffn(const moe_layer *L, const int32_t *expert_offsets, const void *x_perm,
+                          const float *x_scale, int64_t N, void *y_perm, int32_t y_dtype, void *ws,
+                          size_t ws_bytes, void *stream) {
+  moe_status s;
+  if ((s = check_layer_shape(L, false)) != MOE_OK) return s;
+  if ((s = check_rows(0, N)) != MOE_OK) return s;
+  if (!out_dtype_ok(y_dtype)) return fail(MOE_EUNSUPPORTED, "y_dtype %d is not MOE_BF16 or MOE_F32", y_dtype);
+  if (N > 0) {
+    if ((s = check_expert_weights(L)) != MOE_OK) return s;
+    if (!expert_offsets || !x_perm || !y_perm) return fail(MOE_EINVAL, "NULL expert_ffn argument");
+    if (is_fp8(L) && !x_scale) return fail(MOE_EINVAL, "fp8 experts need x_scale");
+    if (!aligned16(x_perm) || !aligned16(y_perm)) return fail(MOE_EINVAL, "x_perm or y_perm not 16-byte aligned");
+  }
+  if (N == 0) return MOE_OK;
+  if ((s = check_ws(ws, ws_bytes, need_ffn(N, L->num_experts, L->inter, is_fp8(L)))) != MOE_OK) return s;
+  Carve c(ws);
+  FfnWs f = carve_ffn(c, N, L->num_experts, L->inter, is_fp8(L));
+  return hip_status(
+      moe::launch_expert_ffn(static_cast<const uint8_t *>(x_perm), x_scale, static_cast<const uint8_t *>(L->w_gate_up),
+                             L->s_gate_up, static_cast<const uint8_t *>(L->w_down), L->s_down, expert_offsets,
+                             L->num_experts, L->hidden, L->inter, N, is_fp8(L), f.plan, f.tiles, f.h, f.hs, y_perm,
+                             y_dtype == MOE_F32, false, (hipStream_t)stream),
+      "moe_expert_ffn");
+}
+
+moe_status moe_combine(const moe_layer *L, const void *y_perm, int32_t y_dtype, const int32_t *perm_pos,
+                       const int32_t *assign_token, const float *gates, int64_t N, const void *shared_out,
+                       int32_t shared_dtype, int64_t T, void *y, int32_t out_dtype, void *ws, size_t ws_bytes,
+                       void *stream) {
+  moe_status s;
+  if ((s = check_layer_shape(L, false)) != MOE_OK) return s;
+  if ((s = check_rows(T, N)) != MOE_OK) return s;
+  if (!out_dtype_ok(y_dtype) || !out_dtype_ok(out_dtype) || (shared_out && !out_dtype_ok(shared_dtype)))
+    return fail(MOE_EUNSUPPORTED, "dtypes must be MOE_BF16 or MOE_F32");
+  if (!assign_token) {
+    if (L->top_k < 1) return fail(MOE_EINVAL, "assign_token is NULL but top_k < 1");
+    if (N != T * L->top_k) return fail(MOE_EINVAL, "N=%lld != T*k without assign_token", (long long)N);
+  }
+  if (T > 0) {
+    if (!y || !aligned16(y)) return fail(MOE_EINVAL, "y NULL or not 16-byte aligned");
+    if (shared_out && !aligned16(shared_out)) return fail(MOE_EINVAL, "shared_out not 16-byte aligned");
+  }
+  if (N > 0 && (!y_perm || !perm_pos || !gates || !aligned16(y_perm)))
+    return fail(MOE_EINVAL, "NULL or misaligned combine argument");
+  if (T == 0) return MOE_OK;
+  if ((s = check_ws(ws, ws_bytes, need_combine(T, N, assign_token != nullptr))) != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const int32_t *tok_off = nullptr, *tok_list = nullptr;
+  if (assign_token) {
+    Carve c(ws);
+    CombineWs w = carve_combine(c, T, N);
+    hipError_t e = moe::launch_counting_sort(assign_token, nullptr, 0, N, T, w.tok_off, w.tok_list, nullptr,
+                                             w.sort, st);
+    if (e != hipSuccess) return hip_status(e, "moe_combine: token sort");
+    tok_off = w.tok_off;
+    tok_list = w.tok_list;
+  }
+  return hip_status(moe::launch_combine(y_perm, y_dtype == MOE_F32, perm_pos, tok_off, tok_list, L->top_k, gates,
+                                        shared_out, shared_dtype == MOE_F32, T, L->hidden, N, y, out_dtype == MOE_F32, st),
+                    "moe_combine");
+}
+
+moe_status moe_forward(const moe_layer *L, const void *x, int64_t T, void *y, int32_t out_dtype, int32_t *topk_ids,
+                       float *topk_gates, void *ws, size_t ws_bytes, void *stream) {
+  moe_status s;
+  if ((s = check_layer_shape(L, true)) != MOE_OK) return s;
+  if ((s = check_rows(T, T * (int64_t)L->top_k)) != MOE_OK) return s;
+  if (!out_dtype_ok(out_dtype)) return fail(MOE_EUNSUPPORTED, "out_dtype %d is not MOE_BF16 or MOE_F32", out_dtype);
+  if (T > 0) {
+    if (!x || !y || !L->w_router) return fail(MOE_EINVAL, "NULL forward argument");
+    if (!aligned16(x) || !aligned16(y) || !aligned16(L->w_router)) return fail(MOE_EINVAL, "x, y or w_router not 16-byte aligned");
+    if ((s = check_expert_weights(L)) != MOE_OK) return s;
+    if ((s = check_shared(L)) != MOE_OK) return s;
+  }
+  if (T == 0) return MOE_OK;
+  if ((s = check_ws(ws, ws_bytes, need_forward(L, T))) != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const bool out_f32 = out_dtype == MOE_F32;
+  const int64_t N = T * L->top_k;
+  const int H = L->hidden, E = L->num_experts;
+  Carve c(ws);
+  ForwardWs f = carve_forward(c, L, T, out_f32);
+  int32_t *ids = topk_ids ? topk_ids : f.ids;
+  float *gates = topk_gates ? topk_gates : f.gates;
+  hipError_t e;
+  e = moe::launch_router(static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(L->w_router), L->router_bias,
+                         T, E, H, L->top_k, f.route.partial, f.route.S, ids, gates, nullptr, st);
+  if (e != hipSuccess) return hip_status(e, "moe_forward: route");
+  e = moe::launch_counting_sort(ids, nullptr, 0, N, E, f.offsets, f.perm_src, f.perm_pos, f.sort, st);
+  if (e != hipSuccess) return hip_status(e, "moe_forward: sort");
+  e = moe::launch_gather_rows(static_cast<const uint16_t *>(x), H, f.perm_src, nullptr, L->top_k, N, f.offsets + E,
+                              is_fp8(L), f.x_perm, f.x_scale, st);
+  if (e != hipSuccess) return hip_status(e, "moe_forward: gather");
+  e = moe::launch_expert_ffn(f.x_perm, f.x_scale, static_cast<const uint8_t *>(L->w_gate_up), L->s_gate_up,
+                             static_cast<const uint8_t *>(L->w_down), L->s_down, f.offsets, E, H, L->inter, N,
+                             is_fp8(L), f.ffn.plan, f.ffn.tiles, f.ffn.h, f.ffn.hs, f.y_perm, false, false, st);
+  if (e != hipSuccess) return hip_status(e, "moe_forward: routed experts");
+  if (L->shared_inter > 0) {
+    e = moe::launch_fill_offsets2(f.sh_off, (int32_t)T, st);
+    if (e != hipSuccess) return hip_status(e, "moe_forward: shared offsets");
+    e = moe::launch_expert_ffn(static_cast<const uint8_t *>(x), nullptr,
+                               static_cast<const uint8_t *>(L->w_shared_gate_up), nullptr,
+                               static_cast<const uint8_t *>(L->w_shared_down), nullptr, f.sh_off, 1, H,
+                               L->shared_inter, T, false, f.sh_ffn.plan, f.sh_ffn.tiles, f.sh_ffn.h, nullptr,
+                               f.sh_out, out_f32, true, st);
+    if (e != hipSuccess) return hip_status(e, "moe_forward: shared expert");
+  }
+  e = moe::launch_combine(f.y_perm, false, f.perm_pos, nullptr, nullptr, L->top_k, gates, f.sh_out, out_f32, T, H, N, y,
+                          out_f32, st);
+  return hip_status(e, "moe_forward: combine");
+}
+
+}  // extern "C"

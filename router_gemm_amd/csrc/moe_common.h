@@ -1,0 +1,89 @@
+// moe_common.h -- device helpers shared by the gfx950 kernels of the MoE layer:
+// number formats, MFMA wrappers, wave reductions, launch-side structs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+constexpr int kWave = 64;
+constexpr float kFp8Max = 448.0f;  // largest finite OCP E4M3FN value
+
+// ---------------------------------------------------------------- formats
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// binary32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two binary32 values -> two E4M3FN codes in the low 16 bits.  The hardware
+// conversion rounds to nearest even; values are clamped to +-448 first so that
+// out-of-range magnitudes saturate instead of becoming NaN.
+__device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b) {
+  a = __builtin_fminf(__builtin_fmaxf(a, -kFp8Max), kFp8Max);
+  b = __builtin_fminf(__builtin_fmaxf(b, -kFp8Max), kFp8Max);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// Four binary32 values -> four E4M3FN codes packed little-endian.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, float d) {
+  return f32x2_to_e4m3(a, b) | (f32x2_to_e4m3(c, d) << 16);
+}
+
+// Scale of a 1x128 group: amax / 448 with an IEEE binary32 division; 1 for an
+// all-zero group.
+__device__ __forceinline__ float group_scale(float amax) {
+  return amax == 0.0f ? 1.0f : __fdiv_rn(amax, kFp8Max);
+}
+
+// ---------------------------------------------------------------- MFMA
+
+// D(16x16, f32) += A(16x32 bf16) * B(32x16 bf16).  Lane l supplies row (A) /
+// column (B) l%16 and 8 consecutive k; lane l receives D[4*(l/16)+r][l%16].
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(16x16, f32) = A(16x128 e4m3) * B(128x16 e4m3) + C, unscaled (OCP E4M3 for
+// both operands).  Lane l supplies row/column l%16 and 32 codes of k.
+__device__ __forceinline__ f32x4 mfma_fp8(const i32x8 &a, const i32x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- waves
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+__device__ __forceinline__ int wave_id() { return (int)(threadIdx.x / kWave); }
+
+__device__ __forceinline__ float wave_xor_max(float v, int width) {
+  for (int o = 1; o < width; o <<= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// ---------------------------------------------------------------- memory
+
+__device__ __forceinline__ i32x4 load16(const void *p) { return *reinterpret_cast<const i32x4 *>(p); }
+__device__ __forceinline__ void store16(void *p, const i32x4 &v) { *reinterpret_cast<i32x4 *>(p) = v; }
+
+
+}  // namespace moe

@@ -1,0 +1,163 @@
+// router.hip -- router logits (bf16 MFMA, fp32 accumulation) and the
+// wavefront top-k selection with renormalised softmax gates.
+//
+// Layer definition: "Step-5-Preview" (NeMo AutoModel model coverage), section
+// "Model Architecture": a learned router picks the top 8 of 352 routed
+// experts per token.  Gates are the softmax over the chosen logits, which is
+// the softmax over all experts renormalised over the chosen ones.
+
+#include "moe_common.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+// logits partial sums: partial[s][t][e] = sum_{h in chunk s} x[t,h] * Wr[e,h].
+// Grid (ceil(E/64), ceil(T/64), S); 4 waves, wave w owns tokens
+// [64*by + 16w, +16) x experts [64*bx, +64) as four 16x16 MFMA tiles.
+__global__ __launch_bounds__(256) void router_logits_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, float *__restrict__ partial,
+    int T, int E, int H, int kchunk) {
+  const int lane = lane_id(), w = wave_id();
+  const int e0 = blockIdx.x * 64;
+  const int t0 = blockIdx.y * 64 + 16 * w;
+  const int s = blockIdx.z;
+  const int kbeg = s * kchunk + 8 * (lane >> 4);
+  const int trow = t0 + (lane & 15);
+  const bool tvalid = trow < T;
+  const uint16_t *xp = x + (int64_t)(tvalid ? trow : 0) * H + kbeg;
+  const uint16_t *wp[4];
+  bool ev[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int er = e0 + 16 * j + (lane & 15);
+    ev[j] = er < E;
+    wp[j] = wr + (int64_t)(ev[j] ? er : 0) * H + kbeg;
+  }
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const i32x4 zero = {0, 0, 0, 0};
+#pragma unroll 4
+  for (int k = 0; k < kchunk; k += 32) {
+    const i32x4 a = tvalid ? load16(xp + k) : zero;
+    i32x4 b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = ev[j] ? load16(wp[j] + k) : zero;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[j] = mfma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b[j]), acc[j]);
+  }
+  // lane holds D[token 4*(lane/16)+r][expert lane%16] of each tile
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = e0 + 16 * j + (lane & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + 4 * (lane >> 4) + r;
+      if (t < T && e < E) partial[((int64_t)s * T + t) * E + e] = acc[j][r];
+    }
+  }
+}
+
+// One wave per token: logits = sum of the S partials (in order s = 0..S-1)
+// + bias; k rounds of a wave-wide arg-max under the order (value desc, index
+// asc); slots sorted by expert id; gates = exp(l - l_max) / sum, fp32.
+template <int NJ>
+__global__ __launch_bounds__(256) void router_topk_kernel(
+    const float *__restrict__ partial, int S, const float *__restrict__ bias, int T, int E, int k,
+    int32_t *__restrict__ ids, float *__restrict__ gates, float *__restrict__ logits_out) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + wave_id();
+  if (t >= T) return;
+  float v[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + 64 * j;
+    float a = 0.f;
+    if (e < E) {
+      for (int s = 0; s < S; ++s) a += partial[((int64_t)s * T + t) * E + e];
+      if (bias) a += bias[e];
+      if (logits_out) logits_out[(int64_t)t * E + e] = a;
+    }
+    v[j] = a;
+  }
+  uint32_t taken = 0;
+  float my_v = 0.f;
+  int my_e = 0;
+  for (int it = 0; it < k; ++it) {
+    float bv = -__builtin_huge_valf();
+    int be = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E && !((taken >> j) & 1u) && (v[j] > bv || (v[j] == bv && e < be))) {
+        bv = v[j];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oe = __shfl_xor(be, o, kWave);
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if (be < E && (be & 63) == lane) taken |= 1u << (be >> 6);
+    if (lane == it) {
+      my_v = bv;
+      my_e = be;
+    }
+  }
+  // slot of the j-th winner = number of winners with a smaller expert id
+  int rank = 0;
+  for (int j = 0; j < k; ++j) {
+    const int ej = __shfl(my_e, j, kWave);
+    rank += (ej < my_e) ? 1 : 0;
+  }
+  const float vmax = __shfl(my_v, 0, kWave);
+  const float ex = lane < k ? expf(my_v - vmax) : 0.f;
+  const float den = __shfl(wave_sum(ex), 0, kWave);
+  if (lane < k) {
+    ids[(int64_t)t * k + rank] = my_e;
+    gates[(int64_t)t * k + rank] = __fdiv_rn(ex, den);
+  }
+}
+
+int router_ksplit(int64_t T, int E, int H) {
+  const int64_t tiles = cdiv(E, 64) * cdiv(T, 64);
+  int S = 1;
+  // split K until there are enough workgroups, keeping chunks of >= 128 (multiples of 32)
+  while (tiles * S < 512 && (H / (2 * S)) % 32 == 0 && H / (2 * S) >= 128 && H % (2 * S) == 0) S *= 2;
+  return S;
+}
+
+hipError_t launch_router(const uint16_t *x, const uint16_t *wr, const float *bias, int64_t T, int E,
+                         int H, int k, float *partial, int S, int32_t *ids, float *gates,
+                         float *logits, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  dim3 g1((unsigned)cdiv(E, 64), (unsigned)cdiv(T, 64), (unsigned)S);
+  timing_before(0, st);
+  router_logits_kernel<<<g1, 256, 0, st>>>(x, wr, partial, (int)T, E, H, H / S);
+  timing_after(0, st);
+  const unsigned g2 = (unsigned)cdiv(T, 4);
+  const int nj = (int)cdiv(E, 64);
+  timing_before(1, st);
+#define MOE_TOPK_CASE(NJ)                                                                      \
+  case NJ:                                                                                     \
+    router_topk_kernel<NJ><<<g2, 256, 0, st>>>(partial, S, bias, (int)T, E, k, ids, gates, logits); \
+    break;
+  switch (nj) {
+    MOE_TOPK_CASE(1) MOE_TOPK_CASE(2) MOE_TOPK_CASE(3) MOE_TOPK_CASE(4)
+    MOE_TOPK_CASE(5) MOE_TOPK_CASE(6) MOE_TOPK_CASE(7) MOE_TOPK_CASE(8)
+    MOE_TOPK_CASE(9) MOE_TOPK_CASE(10) MOE_TOPK_CASE(11) MOE_TOPK_CASE(12)
+    MOE_TOPK_CASE(13) MOE_TOPK_CASE(14) MOE_TOPK_CASE(15) MOE_TOPK_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_TOPK_CASE
+  timing_after(1, st);
+  return hipGetLastError();
+}
+
+}  // namespace moe

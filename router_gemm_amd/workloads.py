@@ -63,6 +63,10 @@ CONFIGS = {
         "small_bf16", T=128, H=512, E=32, k=4, I=192, Is=192, expert_dtype="bf16",
         router_std=1.0 / math.sqrt(512),
         description="scaled-down MoE layer, bf16, T=128, H=512, 32 experts top-4, I=192"),
+    "small_fp8": MoEConfig(
+        "small_fp8", T=200, H=512, E=16, k=4, I=256, Is=128, expert_dtype="fp8",
+        router_std=1.0 / math.sqrt(512),
+        description="scaled-down MoE layer, FP8 experts, T=200 (ragged), H=512, 16 experts top-4, I=256"),
     "decode_bf16": MoEConfig(
         "decode_bf16", T=64, H=4096, E=352, k=8, I=1536, Is=1536, expert_dtype="bf16",
         router_std=1.0 / 64,

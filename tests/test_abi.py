@@ -1,0 +1,114 @@
+"""The C-ABI library loads, exports every entry point include/moe.h declares,
+and refuses bad arguments on the host before launching anything (so these run
+without a GPU: every call below fails validation, or is a T == 0 no-op)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from router_gemm_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000  # never dereferenced: validation fails first
+
+
+def header_functions():
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", text, re.M))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert set(names) == set(B.EXPORTS), names
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def layer(H=4096, I=1536, E=352, k=8, dtype=B.MOE_FP8_E4M3FN, Is=1536):
+    return B.MoELayerC(H, I, E, k, Is, dtype, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+
+
+def route(L, T=64, ws=FAKE, nb=1 << 40, x=FAKE):
+    return B.lib().moe_route(C.byref(L), x, T, FAKE, FAKE, None, ws, nb, None)
+
+
+def test_status_strings():
+    lib = B.lib()
+    for s in range(5):
+        assert lib.moe_status_string(s).startswith(b"MOE_")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), B.MOE_EINVAL), (dict(k=33), B.MOE_EINVAL), (dict(E=4, k=5), B.MOE_EINVAL),
+    (dict(H=4000), B.MOE_EUNSUPPORTED), (dict(E=1025), B.MOE_EUNSUPPORTED),
+    (dict(I=1600), B.MOE_EUNSUPPORTED),                              # fp8 needs I % 128 == 0
+    (dict(I=1600, dtype=B.MOE_BF16), B.MOE_OK),                       # bf16 allows I % 64 == 0 (T=0 below)
+    (dict(I=1568, dtype=B.MOE_BF16), B.MOE_EUNSUPPORTED),
+    (dict(dtype=7), B.MOE_EUNSUPPORTED), (dict(Is=100), B.MOE_EUNSUPPORTED),
+    (dict(H=0), B.MOE_EINVAL), (dict(E=-1), B.MOE_EINVAL),
+])
+def test_layer_validation(kw, status):
+    L = layer(**kw)
+    assert route(L, T=0) == status, B.lib().moe_last_error()
+
+
+def test_null_layer_and_pointers():
+    lib = B.lib()
+    assert lib.moe_route(None, FAKE, 4, FAKE, FAKE, None, FAKE, 1 << 30, None) == B.MOE_EINVAL
+    assert route(layer(), x=None) == B.MOE_EINVAL
+    assert route(layer(), x=FAKE + 2) == B.MOE_EINVAL          # misaligned
+    assert route(layer(), T=-1) == B.MOE_EINVAL
+
+
+def test_workspace_refusal():
+    L = layer()
+    need = B.lib().moe_workspace_bytes(C.byref(L), 64, 512)
+    assert need > 0
+    assert route(L, nb=0) == B.MOE_EWORKSPACE
+    assert route(L, ws=None, nb=1 << 40) == B.MOE_EINVAL
+    assert route(L, ws=FAKE + 64) == B.MOE_EINVAL              # workspace must be 256-byte aligned
+    assert b"workspace" in B.lib().moe_last_error()
+    bad = layer(k=0)
+    assert B.lib().moe_workspace_bytes(C.byref(bad), 64, 512) > 0   # k = 0 allowed for pre-routed calls
+    assert B.lib().moe_workspace_bytes(C.byref(layer(H=100)), 64, 512) == 0
+
+
+def test_permute_combine_ffn_refusals():
+    lib, L = B.lib(), layer()
+    r = lib.moe_permute(C.byref(L), FAKE, 64, FAKE, None, 500, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert r == B.MOE_EINVAL and b"T*k" in lib.moe_last_error()
+    r = lib.moe_permute(C.byref(L), FAKE, 64, FAKE, None, 512, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None)
+    assert r == B.MOE_EINVAL and b"x_scale" in lib.moe_last_error()
+    r = lib.moe_expert_ffn(C.byref(L), FAKE, FAKE, FAKE, 100, FAKE, 9, FAKE, 1 << 40, None)
+    assert r == B.MOE_EUNSUPPORTED
+    r = lib.moe_expert_ffn(C.byref(L), FAKE, FAKE, FAKE, 100, FAKE, B.MOE_F32, FAKE, 16, None)
+    assert r == B.MOE_EWORKSPACE
+    r = lib.moe_expert_ffn(C.byref(L), FAKE, FAKE, FAKE, 0, FAKE, B.MOE_F32, None, 0, None)
+    assert r == B.MOE_OK                                       # N == 0: no-op
+    Lk0 = layer(k=0)
+    r = lib.moe_combine(C.byref(Lk0), FAKE, B.MOE_BF16, FAKE, None, FAKE, 10, None, 0, 10, FAKE, B.MOE_BF16,
+                        FAKE, 1 << 40, None)
+    assert r == B.MOE_EINVAL
+    r = lib.moe_combine(C.byref(L), FAKE, B.MOE_BF16, FAKE, FAKE, FAKE, 10, None, 0, 10, FAKE, B.MOE_FP8_E4M3FN,
+                        FAKE, 1 << 40, None)
+    assert r == B.MOE_EUNSUPPORTED
+    r = lib.moe_forward(C.byref(L), FAKE, 0, FAKE, B.MOE_BF16, None, None, None, 0, None)
+    assert r == B.MOE_OK                                       # T == 0: no-op
+    r = lib.moe_forward(C.byref(L), FAKE, 8, FAKE, B.MOE_F32, None, None, FAKE, 1024, None)
+    assert r == B.MOE_EWORKSPACE
+
+
+def test_timing_sites_validate_without_gpu():
+    lib = B.lib()
+    assert lib.moe_timing_arm(-1, 4) == B.MOE_EINVAL
+    assert lib.moe_timing_arm(9, 4) == B.MOE_EINVAL
+    assert lib.moe_timing_arm(4, 0) == B.MOE_EINVAL
+    ms, n = C.c_double(1.0), C.c_int32(7)
+    assert lib.moe_timing_read(5, C.byref(ms), C.byref(n)) == B.MOE_OK
+    assert ms.value == 0.0 and n.value == 0

@@ -1,0 +1,337 @@
+"""GPU parity: every primitive and the fused forward through the C ABI against
+the fp64 oracle on the same seeded inputs.
+
+Bars: expert ids, offsets and permutation indices and the fp8 x_perm bytes and
+scales bit-exact (ids up to the near-tie exemption); gates within 2e-6;
+outputs within the per-token max relative error 2e-2 (bf16) / 4e-2 (fp8).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from router_gemm_amd import binding as B
+from router_gemm_amd import workloads as W
+
+from conftest import gpu_available
+from gpu_util import TOL, check_forward, check_ids, dev, oracle_layer, rel_err_rows, run_forward, to_np
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------ router
+
+@pytest.mark.parametrize("name", ["c0", "small_fp8"])
+def test_route_matches_oracle(name):
+    cfg = W.get_config(name)
+    lt = W.make_layer(cfg, dev())
+    x = W.make_x(cfg, dev())
+    layer = B.Layer.from_tensors(lt)
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev())
+    gates = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev())
+    logits = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev())
+    B.moe_route(layer, x, cfg.T, ids, gates, logits, ws=B.workspace(layer, cfg.T, cfg.N, dev()))
+    torch.cuda.synchronize()
+    OL = oracle_layer(lt)
+    ids_ref, g_ref, gap, l_ref = oracle.route(OL, W.bf16_bits(x), want_logits=True)
+    same = check_ids(ids.cpu().numpy(), ids_ref, gap)
+    np.testing.assert_allclose(logits.cpu().numpy(), l_ref, rtol=0, atol=2e-5)
+    assert np.abs(gates.cpu().numpy()[same] - g_ref[same]).max() < 2e-6
+
+
+def _route_with(wr, x, k, bias=None):
+    E, H = wr.shape
+    I = 64
+    wgu = torch.zeros((E, 2 * I, H), dtype=torch.bfloat16, device=dev())
+    wd = torch.zeros((E, H, I), dtype=torch.bfloat16, device=dev())
+    layer = B.Layer(H, I, E, k, B.MOE_BF16, wgu, wd, w_router=wr, router_bias=bias)
+    T = x.shape[0]
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev())
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev())
+    B.moe_route(layer, x, T, ids, gates, ws=B.workspace(layer, T, T * k, dev()))
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), gates.cpu().numpy()
+
+
+def test_route_exact_ties_lowest_index():
+    # duplicated router rows give bit-identical logits in any arithmetic
+    E, H, T, k = 40, 256, 70, 4
+    g = torch.Generator(device="cpu").manual_seed(5)
+    wr = (torch.randn(E, H, generator=g) / 16).to(torch.bfloat16)
+    for a, b in [(3, 17), (5, 6), (20, 39), (0, 1)]:
+        wr[b] = wr[a]
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    ids, gates = _route_with(wr.to(dev()), x.to(dev()), k)
+    for t in range(T):
+        s = set(ids[t].tolist())
+        for a, b in [(3, 17), (5, 6), (20, 39), (0, 1)]:
+            assert not (b in s and a not in s), (t, a, b, ids[t])
+        if 3 in s and 17 in s:
+            j3, j17 = list(ids[t]).index(3), list(ids[t]).index(17)
+            assert gates[t, j3] == gates[t, j17]
+    # all-equal logits: x = 0 -> every logit 0 -> experts 0..k-1, gates 1/k
+    ids0, g0 = _route_with(wr.to(dev()), torch.zeros((3, H), dtype=torch.bfloat16, device=dev()), k)
+    assert (ids0 == np.arange(k)).all() and np.allclose(g0, 1.0 / k, atol=1e-7)
+
+
+def test_route_k_equals_E_and_k1():
+    cfg = W.get_config("c0", k=32, T=37)
+    lt = W.make_layer(cfg, dev())
+    x = W.make_x(cfg, dev())
+    OL = oracle_layer(lt)
+    ids, gates = _route_with(lt.w_router, x, 32)
+    assert (ids == np.arange(32)).all()
+    _, g_ref, _, _ = oracle.route(OL, W.bf16_bits(x))
+    assert np.abs(gates - g_ref).max() < 2e-6
+    ids1, g1 = _route_with(lt.w_router, x, 1)
+    OL1 = oracle_layer(W.make_layer(W.get_config("c0", k=1), "cpu"))
+    ids1_ref, _, gap1, _ = oracle.route(OL1, W.bf16_bits(x))
+    check_ids(ids1, ids1_ref, gap1)
+    assert (g1 == 1.0).all()
+
+
+# ------------------------------------------------------------------ permute
+
+def _permute(cfg_name, N, T, k, E, with_tokens, invalid, fp8, seed=0):
+    rng = np.random.default_rng(seed)
+    H = 512
+    keys = rng.integers(0, E, size=N).astype(np.int32)
+    tok = rng.integers(0, T, size=N).astype(np.int32) if with_tokens else None
+    if invalid:
+        keys[rng.choice(N, size=max(1, N // 50), replace=False)] = rng.choice([-1, E, E + 7])
+        if with_tokens:
+            tok[rng.choice(N, size=max(1, N // 60), replace=False)] = T + 3
+    x = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32) * 3).to(torch.bfloat16)
+    lt_dtype = B.MOE_FP8_E4M3FN if fp8 else B.MOE_BF16
+    layer = B.Layer(H, 128, E, k if not with_tokens else 0, lt_dtype, None, None)
+    d = dev()
+    xg = x.to(d)
+    off = torch.empty(E + 1, dtype=torch.int32, device=d)
+    src = torch.full((N,), -7, dtype=torch.int32, device=d)
+    pos = torch.empty(N, dtype=torch.int32, device=d)
+    xp = torch.zeros((N, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=d)
+    xs = torch.zeros((N, H // 128), dtype=torch.float32, device=d) if fp8 else None
+    kg = torch.from_numpy(keys).to(d)
+    tg = torch.from_numpy(tok).to(d) if with_tokens else None
+    B.moe_permute(layer, xg, T, kg, tg, N, off, src, pos, xp, xs, ws=B.workspace(layer, T, N, d))
+    torch.cuda.synchronize()
+    okeys = keys.copy()
+    if with_tokens:
+        okeys[(tok < 0) | (tok >= T)] = -1
+    off_r, src_r, pos_r, dropped = oracle.permute(okeys, E)
+    assert np.array_equal(off.cpu().numpy(), off_r)
+    nv = off_r[E]
+    assert np.array_equal(src.cpu().numpy()[:nv], src_r[:nv])
+    assert np.array_equal(pos.cpu().numpy(), pos_r)
+    # gathered rows
+    toks = (tok[src_r[:nv]] if with_tokens else src_r[:nv] // k)
+    xb = W.bf16_bits(x)
+    if fp8:
+        q_r, s_r = oracle.quant_bf16_rows(xb[toks])
+        assert np.array_equal(xp.cpu().numpy()[:nv], q_r)
+        assert np.array_equal(xs.cpu().numpy()[:nv], s_r)
+    else:
+        assert np.array_equal(W.bf16_bits(xp)[:nv], xb[toks])
+    return dropped
+
+
+@pytest.mark.parametrize("N,T,k,E,tokens,invalid,fp8", [
+    (1000, 250, 4, 32, False, False, False),
+    (1000, 250, 4, 32, False, False, True),
+    (513, 400, 0, 44, True, True, True),        # ragged, pre-routed, dropped entries
+    (65536, 8192, 8, 352, False, False, True),  # prefill size
+    (1, 1, 1, 5, False, False, True),
+    (7, 9, 0, 1000, True, False, False),
+])
+def test_permute_bit_exact(N, T, k, E, tokens, invalid, fp8):
+    if not tokens:
+        N = T * k
+    _permute("p", N, T, k, E, tokens, invalid, fp8)
+
+
+def test_permute_empty():
+    d = dev()
+    layer = B.Layer(512, 128, 8, 2, B.MOE_BF16, None, None)
+    off = torch.full((9,), 5, dtype=torch.int32, device=d)
+    z = torch.empty(0, dtype=torch.int32, device=d)
+    B.moe_permute(layer, torch.empty((0, 512), dtype=torch.bfloat16, device=d), 0, z, None, 0, off, z, z,
+                  torch.empty((0, 512), dtype=torch.bfloat16, device=d), ws=B.workspace(layer, 1, 1, d))
+    torch.cuda.synchronize()
+    assert (off.cpu().numpy() == 0).all()
+
+
+# ------------------------------------------------------------------ expert FFN
+
+def _grouped_rows(E, N, H, fp8, rng, empty_frac=0.3):
+    counts = rng.multinomial(N, rng.dirichlet(np.ones(E) * 0.5))
+    counts[rng.random(E) < empty_frac] = 0
+    counts[0] += N - counts.sum()
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    if fp8:
+        codes = rng.integers(0, 0x7E, size=(N, H)).astype(np.uint8) | (rng.integers(0, 2, (N, H)) << 7).astype(np.uint8)
+        scales = (rng.random((N, H // 128)) * 0.01 + 1e-3).astype(np.float32)
+        return off, codes, scales
+    xb = torch.from_numpy(rng.standard_normal((N, H)).astype(np.float32)).to(torch.bfloat16)
+    return off, W.bf16_bits(xb), None
+
+
+@pytest.mark.parametrize("fp8,E,N,H,I,ydt", [
+    (False, 32, 300, 512, 192, torch.float32),
+    (False, 5, 1000, 512, 128, torch.bfloat16),
+    (True, 16, 777, 512, 256, torch.float32),
+    (True, 3, 2000, 1024, 384, torch.bfloat16),
+])
+def test_expert_ffn_matches_oracle(fp8, E, N, H, I, ydt):
+    rng = np.random.default_rng(E * N)
+    cfg = W.MoEConfig("t", T=N, H=H, E=E, k=1, I=I, Is=0, expert_dtype="fp8" if fp8 else "bf16",
+                      router_std=0.05, seed=3)
+    lt = W.make_layer(cfg, dev())
+    off, a, s = _grouped_rows(E, N, H, fp8, rng)
+    d = dev()
+    layer = B.Layer.from_tensors(lt)
+    a_t = torch.from_numpy(a).to(d) if fp8 else torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(d)
+    s_t = torch.from_numpy(s).to(d) if fp8 else None
+    y = torch.full((N, H), float("nan"), dtype=ydt, device=d)
+    B.moe_expert_ffn(layer, torch.from_numpy(off).to(d), a_t, s_t, N, y, ws=B.workspace(layer, N, N, d))
+    torch.cuda.synchronize()
+    y_ref = oracle.expert_ffn(oracle_layer(lt), off, a, s)
+    err = rel_err_rows(to_np(y), y_ref)
+    _print(f"expert_ffn fp8={fp8} E={E} N={N}: max rel err {err.max():.3e}")
+    assert err.max() < TOL["fp8" if fp8 else "bf16"]
+
+
+def test_shared_expert_view_matches_oracle():
+    cfg = W.get_config("c0")
+    lt = W.make_layer(cfg, dev())
+    x = W.make_x(cfg, dev())
+    layer = B.Layer.shared_view(lt)
+    off = torch.tensor([0, cfg.T], dtype=torch.int32, device=dev())
+    y = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=dev())
+    B.moe_expert_ffn(layer, off, x, None, cfg.T, y, ws=B.workspace(layer, cfg.T, cfg.T, dev()))
+    torch.cuda.synchronize()
+    OL = oracle_layer(lt)
+    xb = W.bf16_bits(x)
+    y_ref = np.stack([oracle.shared_row(OL, xb[t]) for t in range(cfg.T)])
+    assert rel_err_rows(to_np(y), y_ref).max() < TOL["bf16"]
+
+
+# ------------------------------------------------------------------ combine
+
+@pytest.mark.parametrize("tokens,ydt,sdt,odt", [
+    (False, torch.float32, torch.float32, torch.float32),
+    (False, torch.bfloat16, torch.bfloat16, torch.bfloat16),
+    (True, torch.bfloat16, torch.float32, torch.float32),
+    (True, torch.float32, None, torch.bfloat16),
+])
+def test_combine_matches_oracle(tokens, ydt, sdt, odt):
+    rng = np.random.default_rng(11)
+    T, H, k = 300, 512, 4
+    N = 777 if tokens else T * k
+    d = dev()
+    yp = torch.from_numpy(rng.standard_normal((N, H)).astype(np.float32)).to(ydt)
+    pos = rng.permutation(N).astype(np.int32)
+    pos[rng.choice(N, 5, replace=False)] = -1
+    tok = rng.integers(0, T, size=N).astype(np.int32) if tokens else None
+    if tokens:
+        tok[:3] = [T + 5, -2, T]           # out of range: skipped
+    gates = rng.random(N).astype(np.float32)
+    sh = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(sdt) if sdt else None
+    layer = B.Layer(H, 128, 8, 0 if tokens else k, B.MOE_BF16, None, None)
+    y = torch.empty((T, H), dtype=odt, device=d)
+    B.moe_combine(layer, yp.to(d), B.dtype_code(yp), torch.from_numpy(pos).to(d),
+                  torch.from_numpy(tok).to(d) if tokens else None, torch.from_numpy(gates).to(d), N,
+                  sh.to(d) if sh is not None else None, B.dtype_code(sh) if sh is not None else 0, T, y,
+                  B.dtype_code(y), ws=B.workspace(layer, T, N, d))
+    torch.cuda.synchronize()
+    y_ref = oracle.combine(to_np(yp), pos, gates, T, k=k, tok=tok, shared=None if sh is None else to_np(sh))
+    err = rel_err_rows(to_np(y), y_ref)       # rows with nothing to add are exactly zero
+    assert err.max() < (1e-6 if odt == torch.float32 else 2 ** -8)
+
+
+def test_combine_of_permute_is_identity():
+    """y_perm := x_perm (identity expert, bf16): k = 1 with gate 1 gives y == x
+    bit for bit; k = 4 with all gates 1 gives y == 4x bit for bit."""
+    rng = np.random.default_rng(12)
+    T, H, E = 333, 512, 24
+    d = dev()
+    x = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16).to(d)
+    for k in (1, 4):
+        N = T * k
+        ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+        layer = B.Layer(H, 128, E, k, B.MOE_BF16, None, None)
+        ws = B.workspace(layer, T, N, d)
+        off = torch.empty(E + 1, dtype=torch.int32, device=d)
+        src = torch.empty(N, dtype=torch.int32, device=d)
+        pos = torch.empty(N, dtype=torch.int32, device=d)
+        xp = torch.empty((N, H), dtype=torch.bfloat16, device=d)
+        B.moe_permute(layer, x, T, torch.from_numpy(ids).to(d), None, N, off, src, pos, xp, ws=ws)
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=d)
+        B.moe_combine(layer, xp, B.MOE_BF16, pos, None, torch.ones(N, device=d), N, None, 0, T, y, B.MOE_BF16,
+                      ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y.float(), x.float() * k)
+
+
+# ------------------------------------------------------------------ whole layer
+
+@pytest.mark.parametrize("name", ["c0", "small_fp8"])
+def test_forward_small_full_parity(name):
+    cfg = W.get_config(name)
+    lt = W.make_layer(cfg, dev())
+    x = W.make_x(cfg, dev())
+    st = check_forward(lt, x)
+    _print(f"forward {name}: {st}")
+
+
+def test_forward_ragged_and_single_token():
+    cfg = W.get_config("small_fp8")
+    lt = W.make_layer(cfg, dev())
+    OL = oracle_layer(lt)
+    for T in (1, 17, 63):
+        x = W.make_x(cfg, dev(), T=T)
+        check_forward(lt, x, OL=OL)
+
+
+def test_forward_bf16_output_and_k1_E1():
+    cfg = W.get_config("c0", E=1, k=1)
+    lt = W.make_layer(cfg, dev())
+    x = W.make_x(cfg, dev())
+    check_forward(lt, x, out_dtype=torch.bfloat16)
+
+
+def test_forward_zero_tokens():
+    cfg = W.get_config("c0")
+    lt = W.make_layer(cfg, dev())
+    layer = B.Layer.from_tensors(lt)
+    y = torch.empty((0, cfg.H), dtype=torch.float32, device=dev())
+    B.moe_forward(layer, torch.empty((0, cfg.H), dtype=torch.bfloat16, device=dev()), 0, y)
+
+
+def test_forward_deterministic_and_workspace_independent():
+    cfg = W.get_config("small_fp8")
+    lt = W.make_layer(cfg, dev())
+    x = W.make_x(cfg, dev())
+    layer = B.Layer.from_tensors(lt)
+    ws = B.workspace(layer, cfg.T, cfg.N, dev())
+    ws.fill_(0xFF)                              # NaN patterns everywhere
+    y1, i1, g1 = run_forward(lt, x, ws=ws)
+    ws.fill_(0x7F)
+    y2, i2, g2 = run_forward(lt, x, ws=ws)
+    for _ in range(3):
+        y3, _, _ = run_forward(lt, x)
+        assert torch.equal(y1, y3)
+    assert torch.equal(y1, y2) and torch.equal(i1, i2) and torch.equal(g1, g2)
+
+
+def test_forward_token_order_equivariance():
+    cfg = W.get_config("small_fp8")
+    lt = W.make_layer(cfg, dev())
+    x = W.make_x(cfg, dev())
+    perm = torch.randperm(cfg.T, generator=torch.Generator().manual_seed(3)).to(dev())
+    y, ids, _ = run_forward(lt, x)
+    yp, idsp, _ = run_forward(lt, x[perm].contiguous())
+    assert torch.equal(yp, y[perm]) and torch.equal(idsp, ids[perm])
