@@ -112,8 +112,8 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    site = 4   # MOE_SITE_GATE_UP: the routed grouped gate/up GEMM streams 2/3 of the expert weights
-    B.timing_arm(site, K)
+    site = 4   # MOE_SITE_GATE_UP: grouped gate/up GEMM, which streams 2/3 of the expert weights
+    B.timing_arm(site, 4 * K)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -144,24 +144,45 @@ def main():
         fl_routed_fp8 = fl_routed
     t_s = ms_per_step / 1e3
     mfma_util = (fl_routed_fp8 / (PEAK_TFLOPS["fp8"] * 1e12) + fl_bf16 / (PEAK_TFLOPS["bf16"] * 1e12)) / t_s
-    # gate/up kernel per launch: active experts' [gate; up] weights (+ scales), its input rows, its h output
+    # gate/up launch(es) of one step: the routed experts' [gate; up] weights (+ scales), their
+    # input rows and h output, plus the shared expert's (same launch inside moe_forward; a second
+    # moe_expert_ffn launch at the same timing site for the pre-routed workload)
     gu_bytes = active * w_gu_b + N * H * esz + N * I * esz + ((N * H // 128 + N * I // 128) * 4 if fp8 else 0)
-    gu_flops = 2.0 * N * 2 * I * H
-    gu_ms = gu_ms_total / max(gu_launches, 1)
+    gu_bytes += 2 * Is * H * 2 + T * H * 2 + T * Is * 2
+    gu_f_routed = 2.0 * N * 2 * I * H
+    gu_f_shared = 2.0 * T * 2 * Is * H
+    gu_ms = gu_ms_total / K                      # per step (all gate/up launches of the step)
     decode_like = (N / max(active, 1)) < 64
     if decode_like:
         roof = {"bound": "hbm", "achieved": round(gu_bytes / (gu_ms / 1e3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     else:
-        pk = PEAK_TFLOPS["fp8" if fp8 else "bf16"]
-        roof = {"bound": "mfma", "achieved": round(gu_flops / (gu_ms / 1e3) / 1e12, 1), "peak": pk,
+        f8 = gu_f_routed if fp8 else 0.0
+        f16 = gu_f_shared + (0.0 if fp8 else gu_f_routed)
+        # mixed fp8/bf16 contraction: peak = total flops / ideal time at each dtype's dense peak
+        peak = (f8 + f16) / (f8 / PEAK_TFLOPS["fp8"] + f16 / PEAK_TFLOPS["bf16"])
+        roof = {"bound": "mfma", "achieved": round((f8 + f16) / (gu_ms / 1e3) / 1e12, 1), "peak": round(peak, 1),
                 "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = None
-    roof["kernel"] = "gate_up_kernel (routed experts)"
-    roof["kernel_ms"] = round(gu_ms, 4)
-    roof["algorithmic_bytes_per_launch"] = int(gu_bytes)
-    roof["algorithmic_flops_per_launch"] = gu_flops
+    roof["kernel"] = "grouped gate/up + SwiGLU (routed and shared experts)"
+    roof["kernel_ms_per_step"] = round(gu_ms, 4)
+    roof["launches_per_step"] = gu_launches // K
+    roof["algorithmic_bytes_per_step"] = int(gu_bytes)
+    roof["algorithmic_flops_per_step"] = gu_f_routed + gu_f_shared
+
+    # per-kernel breakdown: a separate pass of K steps with every launch site timed
+    sites = {0: "router_logits", 1: "router_topk", 2: "sort", 3: "gather", 4: "gate_up", 5: "down", 8: "combine"}
+    for sidx in sites:
+        B.timing_arm(sidx, 4 * K)
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    breakdown = {}
+    for sidx, nm in sites.items():
+        ms, n = B.timing_read(sidx)
+        if n:
+            breakdown[nm] = round(1e3 * ms / K, 1)   # microseconds per step
 
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
@@ -176,6 +197,7 @@ def main():
                   "tflops": round((fl_routed + fl_bf16) / t_s / 1e12, 2),
                   "mfma_util_blended": round(mfma_util, 4), "wall_s": round(wall, 4)},
         "roofline": roof,
+        "breakdown_us_per_step": breakdown,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

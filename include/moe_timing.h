@@ -24,10 +24,11 @@ typedef enum moe_site {
   MOE_SITE_ROUTER_TOPK = 1,     /* top-k selection and gates */
   MOE_SITE_SORT = 2,            /* stable counting sort (3 kernels, timed together) */
   MOE_SITE_GATHER = 3,          /* row gather (+ fp8 quantisation) */
-  MOE_SITE_GATE_UP = 4,         /* routed experts: grouped gate/up GEMM + SwiGLU */
-  MOE_SITE_DOWN = 5,            /* routed experts: grouped down GEMM */
-  MOE_SITE_SHARED_GATE_UP = 6,  /* shared expert inside moe_forward: gate/up + SwiGLU */
-  MOE_SITE_SHARED_DOWN = 7,     /* shared expert inside moe_forward: down */
+  MOE_SITE_GATE_UP = 4,         /* grouped gate/up GEMM + SwiGLU: the routed experts, and inside
+                                   moe_forward also the shared expert's tiles (one launch) */
+  MOE_SITE_DOWN = 5,            /* grouped down GEMM (same groups as MOE_SITE_GATE_UP) */
+  MOE_SITE_SHARED_GATE_UP = 6,  /* reserved (no launch records here at present) */
+  MOE_SITE_SHARED_DOWN = 7,     /* reserved (no launch records here at present) */
   MOE_SITE_COMBINE = 8,         /* weighted combine */
   MOE_SITE_COUNT = 9
 } moe_site;

@@ -22,37 +22,49 @@
 // the device-side count exit at once), blockIdx.x the output-column tile.
 // The host never reads the per-expert counts.
 
+#include <algorithm>
+
 #include "moe_common.h"
 #include "moe_kernels.h"
 
 namespace moe {
 
-struct TileEntry {
-  int32_t e;
-  int32_t m0;
-};
+__device__ __forceinline__ FfnGroup pick_group(const FfnGroup &g0, const FfnGroup &g1, int g) {
+  return g ? g1 : g0;
+}
 
-// One workgroup (1024 threads, E <= 1024): tiles of 16*MT rows per expert, in
-// expert order.
-__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__restrict__ off, int E, int bm,
+// One workgroup (1024 threads, E <= 1024 per group): for each group in turn,
+// tiles of bm rows per expert, in expert order.
+__global__ __launch_bounds__(1024) void build_tiles_kernel(FfnGroup g0, FfnGroup g1, int ngroups, int bm,
                                                            int max_tiles, TileEntry *__restrict__ tiles,
                                                            int32_t *__restrict__ ntiles) {
   __shared__ int32_t buf[1024];
   const int tid = threadIdx.x;
-  const int n = tid < E ? max(off[tid + 1] - off[tid], 0) : 0;
-  const int cnt = (n + bm - 1) / bm;
-  buf[tid] = cnt;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int32_t add = tid >= o ? buf[tid - o] : 0;
+  int base0 = 0;
+  for (int g = 0; g < ngroups; ++g) {
+    const FfnGroup G = pick_group(g0, g1, g);
+    int n = 0;
+    if (tid < G.E) {
+      const int b = min(max(G.off[tid], 0), G.nrows);
+      const int e = min(max(G.off[tid + 1], b), G.nrows);
+      n = e - b;
+    }
+    const int cnt = (n + bm - 1) / bm;
     __syncthreads();
-    buf[tid] += add;
+    buf[tid] = cnt;
     __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+      const int32_t add = tid >= o ? buf[tid - o] : 0;
+      __syncthreads();
+      buf[tid] += add;
+      __syncthreads();
+    }
+    const int base = base0 + buf[tid] - cnt;
+    for (int j = 0; j < cnt; ++j)
+      if (base + j < max_tiles) tiles[base + j] = TileEntry{(g << 24) | tid, j * bm};
+    base0 += buf[1023];
   }
-  const int base = buf[tid] - cnt;
-  for (int j = 0; j < cnt; ++j)
-    if (base + j < max_tiles) tiles[base + j] = TileEntry{tid, j * bm};
-  if (tid == 1023) *ntiles = min(buf[1023], max_tiles);
+  if (tid == 0) *ntiles = min(base0, max_tiles);
 }
 
 // Operand fragment of one lane for one 128-byte K chunk: 32 bytes.
@@ -66,7 +78,8 @@ __device__ __forceinline__ i32x8 frag_fp8(const Frag &f) {
   return i32x8{f.lo[0], f.lo[1], f.lo[2], f.lo[3], f.hi[0], f.hi[1], f.hi[2], f.hi[3]};
 }
 
-// acc += A(16 rows x chunk) * B(chunk x 16 tokens)
+// acc += A(16 rows x chunk) * B(chunk x 16 tokens); fp8 chunks are one
+// 128-wide scale block, so the block product is scaled once.
 template <bool FP8>
 __device__ __forceinline__ f32x4 chunk_mma(const Frag &a, const Frag &b, f32x4 acc, float scale) {
   if constexpr (FP8) {
@@ -84,35 +97,37 @@ __device__ __forceinline__ f32x4 chunk_mma(const Frag &a, const Frag &b, f32x4 a
 
 __device__ __forceinline__ float silu(float z) { return __fdiv_rn(z, 1.0f + expf(-z)); }
 
-struct GateUpArgs {
-  const uint8_t *x;        // [N, H] rows in expert order (e4m3 codes or bf16)
-  const float *xs;         // [N, H/128] (fp8)
-  const uint8_t *w;        // [E, 2I, H]
-  const float *ws;         // [E, 2I/128, H/128] (fp8)
-  const int32_t *off;      // [E+1]
+struct StreamArgs {
+  FfnGroup g0, g1;
   const TileEntry *tiles;
   const int32_t *ntiles;
-  uint8_t *h;              // [N, I] bf16 or e4m3
-  float *hs;               // [N, I/128] (fp8)
-  int H, I, nrows;         // rows at or beyond nrows are never read or written
+  int H;
 };
 
+// Rows [rbeg, rend) of the tile, clamped to the group's row count.
+__device__ __forceinline__ void tile_rows(const FfnGroup &G, const TileEntry &te, int &rbeg, int &rend) {
+  const int e = te.ge & 0xFFFFFF;
+  rend = min(max(G.off[e + 1], 0), G.nrows);
+  rbeg = min(max(G.off[e], 0) + te.m0, rend);
+}
+
+// ---------------------------------------------------------------- gate/up (streaming)
 // Workgroup: 4 waves x (GW gate + GW up 16-row weight tiles) = 64*GW h
-// columns, 16*MT token rows.
+// columns x 16*MT token rows.  Each wave streams its own weight rows straight
+// from HBM into MFMA operand registers (no reuse across waves, so no LDS).
 template <bool FP8, int MT, int GW>
-__global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
+__device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry &te, int H) {
   constexpr int ESZ = FP8 ? 1 : 2;
-  if ((int)blockIdx.y >= a.ntiles[0]) return;
-  const TileEntry te = a.tiles[blockIdx.y];
   const int lane = lane_id(), w = wave_id();
-  const int rend = min(max(a.off[te.e + 1], 0), a.nrows);
-  const int rbeg = min(max(a.off[te.e], 0) + te.m0, rend);
-  const int H = a.H, I = a.I;
+  int rbeg, rend;
+  tile_rows(G, te, rbeg, rend);
+  const int e = te.ge & 0xFFFFFF;
+  const int I = G.I;
   const int64_t rowb = (int64_t)H * ESZ;
   const int hc0 = blockIdx.x * (64 * GW) + w * (16 * GW);
   const int koff = 32 * (lane >> 4);
 
-  const uint8_t *wbase = a.w + (int64_t)te.e * 2 * I * rowb;
+  const uint8_t *wbase = G.wgu + (int64_t)e * 2 * I * rowb;
   const uint8_t *wg[GW], *wu[GW];
 #pragma unroll
   for (int i = 0; i < GW; ++i) {
@@ -126,7 +141,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
   for (int m = 0; m < MT; ++m) {
     xrow[m] = rbeg + 16 * m + (lane & 15);
     xv[m] = xrow[m] < rend;
-    xr[m] = a.x + (int64_t)(xv[m] ? xrow[m] : rbeg) * rowb + koff;
+    xr[m] = G.x + (int64_t)(xv[m] ? xrow[m] : 0) * rowb + koff;
   }
   f32x4 ag[GW][MT], au[GW][MT];
 #pragma unroll
@@ -136,8 +151,8 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
 
   const int nchunk = (int)(rowb / 128);
   const int KB = H / 128;
-  const float *sg = FP8 ? a.ws + ((int64_t)te.e * (2 * I / 128) + hc0 / 128) * KB : nullptr;
-  const float *su = FP8 ? a.ws + ((int64_t)te.e * (2 * I / 128) + (I + hc0) / 128) * KB : nullptr;
+  const float *sg = FP8 ? G.sgu + ((int64_t)e * (2 * I / 128) + hc0 / 128) * KB : nullptr;
+  const float *su = FP8 ? G.sgu + ((int64_t)e * (2 * I / 128) + (I + hc0) / 128) * KB : nullptr;
   const Frag zf = Frag{i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
 
   for (int c = 0; c < nchunk; ++c) {
@@ -152,7 +167,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       fx[m] = xv[m] ? load_frag(xr[m] + kb) : zf;
-      sx[m] = (FP8 && xv[m]) ? a.xs[(int64_t)xrow[m] * KB + c] : 0.f;
+      sx[m] = (FP8 && xv[m]) ? G.xs[(int64_t)xrow[m] * KB + c] : 0.f;
     }
     const float swg = FP8 ? sg[c] : 0.f;
     const float swu = FP8 ? su[c] : 0.f;
@@ -183,7 +198,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
         if (!xv[m]) continue;
         const uint32_t lo = f32_to_bf16(hv[i][m][0]) | (f32_to_bf16(hv[i][m][1]) << 16);
         const uint32_t hi = f32_to_bf16(hv[i][m][2]) | (f32_to_bf16(hv[i][m][3]) << 16);
-        *reinterpret_cast<uint2 *>(a.h + ((int64_t)xrow[m] * I + col) * 2) = make_uint2(lo, hi);
+        *reinterpret_cast<uint2 *>(G.h + ((int64_t)xrow[m] * I + col) * 2) = make_uint2(lo, hi);
       }
     }
   } else {
@@ -214,39 +229,40 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a) {
         const int col = hc0 + 16 * i + 4 * (lane >> 4);
         const uint32_t q = f32x4_to_e4m3(__fdiv_rn(hv[i][m][0], s), __fdiv_rn(hv[i][m][1], s),
                                          __fdiv_rn(hv[i][m][2], s), __fdiv_rn(hv[i][m][3], s));
-        *reinterpret_cast<uint32_t *>(a.h + (int64_t)xrow[m] * I + col) = q;
+        *reinterpret_cast<uint32_t *>(G.h + (int64_t)xrow[m] * I + col) = q;
       }
-      if (w == 0 && lane < 16) a.hs[(int64_t)xrow[m] * (I / 128) + blockIdx.x] = s;
+      if (w == 0 && lane < 16) G.hs[(int64_t)xrow[m] * (I / 128) + blockIdx.x] = s;
     }
   }
 }
 
-struct DownArgs {
-  const uint8_t *h;        // [N, I]
-  const float *hs;         // [N, I/128] (fp8)
-  const uint8_t *w;        // [E, H, I]
-  const float *ws;         // [E, H/128, I/128] (fp8)
-  const int32_t *off;
-  const TileEntry *tiles;
-  const int32_t *ntiles;
-  void *y;                 // [N, H] bf16 or f32
-  int H, I, y_f32, nrows;
-};
-
-// Workgroup: 4 waves x NW 16-column output tiles = 64*NW columns, 16*MT rows.
-template <bool FP8, int MT, int NW>
-__global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
-  constexpr int ESZ = FP8 ? 1 : 2;
+template <int MT, int GW>
+__global__ __launch_bounds__(256) void gate_up_stream_kernel(StreamArgs a) {
   if ((int)blockIdx.y >= a.ntiles[0]) return;
   const TileEntry te = a.tiles[blockIdx.y];
+  const FfnGroup G = pick_group(a.g0, a.g1, te.ge >> 24);
+  if ((int)blockIdx.x * 64 * GW >= G.I) return;     // group narrower than the grid
+  if (G.fp8) {
+    if constexpr (GW == 2) gate_up_body<true, MT, GW>(G, te, a.H);
+  } else {
+    gate_up_body<false, MT, GW>(G, te, a.H);
+  }
+}
+
+// ---------------------------------------------------------------- down (streaming)
+// Workgroup: 4 waves x NW 16-column output tiles = 64*NW columns, 16*MT rows.
+template <bool FP8, int MT, int NW>
+__device__ __forceinline__ void down_body(const FfnGroup &G, const TileEntry &te, int H) {
+  constexpr int ESZ = FP8 ? 1 : 2;
   const int lane = lane_id(), w = wave_id();
-  const int rend = min(max(a.off[te.e + 1], 0), a.nrows);
-  const int rbeg = min(max(a.off[te.e], 0) + te.m0, rend);
-  const int H = a.H, I = a.I;
+  int rbeg, rend;
+  tile_rows(G, te, rbeg, rend);
+  const int e = te.ge & 0xFFFFFF;
+  const int I = G.I;
   const int64_t rowb = (int64_t)I * ESZ;
   const int c0 = blockIdx.x * (64 * NW) + w * (16 * NW);
   const int koff = 32 * (lane >> 4);
-  const uint8_t *wbase = a.w + (int64_t)te.e * H * rowb;
+  const uint8_t *wbase = G.wd + (int64_t)e * H * rowb;
   const uint8_t *wr[NW];
 #pragma unroll
   for (int i = 0; i < NW; ++i) wr[i] = wbase + (int64_t)(c0 + 16 * i + (lane & 15)) * rowb + koff;
@@ -257,7 +273,7 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
   for (int m = 0; m < MT; ++m) {
     hrow[m] = rbeg + 16 * m + (lane & 15);
     hv[m] = hrow[m] < rend;
-    hr[m] = a.h + (int64_t)(hv[m] ? hrow[m] : rbeg) * rowb + koff;
+    hr[m] = G.h + (int64_t)(hv[m] ? hrow[m] : 0) * rowb + koff;
   }
   f32x4 acc[NW][MT];
 #pragma unroll
@@ -274,12 +290,12 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       fw[i] = load_frag(wr[i] + kb);
-      sw[i] = FP8 ? a.ws[((int64_t)te.e * (H / 128) + (c0 + 16 * i) / 128) * KB + c] : 0.f;
+      sw[i] = FP8 ? G.sd[((int64_t)e * (H / 128) + (c0 + 16 * i) / 128) * KB + c] : 0.f;
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       fh[m] = hv[m] ? load_frag(hr[m] + kb) : zf;
-      sh[m] = (FP8 && hv[m]) ? a.hs[(int64_t)hrow[m] * KB + c] : 0.f;
+      sh[m] = (FP8 && hv[m]) ? G.hs[(int64_t)hrow[m] * KB + c] : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < NW; ++i)
@@ -293,65 +309,103 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
     for (int m = 0; m < MT; ++m) {
       if (!hv[m]) continue;
       const int64_t o = (int64_t)hrow[m] * H + col;
-      if (a.y_f32) {
-        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.y) + o) = acc[i][m];
+      if (G.y_f32) {
+        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(G.y) + o) = acc[i][m];
       } else {
         const uint32_t lo = f32_to_bf16(acc[i][m][0]) | (f32_to_bf16(acc[i][m][1]) << 16);
         const uint32_t hi = f32_to_bf16(acc[i][m][2]) | (f32_to_bf16(acc[i][m][3]) << 16);
-        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.y) + o) = make_uint2(lo, hi);
+        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(G.y) + o) = make_uint2(lo, hi);
       }
     }
   }
 }
 
+template <int MT, int NW>
+__global__ __launch_bounds__(256) void down_stream_kernel(StreamArgs a) {
+  if ((int)blockIdx.y >= a.ntiles[0]) return;
+  const TileEntry te = a.tiles[blockIdx.y];
+  const FfnGroup G = pick_group(a.g0, a.g1, te.ge >> 24);
+  if (G.fp8)
+    down_body<true, MT, NW>(G, te, a.H);
+  else
+    down_body<false, MT, NW>(G, te, a.H);
+}
+
 // ---------------------------------------------------------------- host side
 
-FfnPlan ffn_plan(int64_t N, int E) {
+FfnPlan ffn_plan(const FfnGroup *g, int ngroups) {
   FfnPlan p;
-  const double avg = E > 0 ? (double)N / E : 0.0;
+  int64_t rows = 0, experts = 0;
+  bool all128 = true;
+  for (int i = 0; i < ngroups; ++i) {
+    rows += g[i].nrows;
+    experts += g[i].E;
+    all128 = all128 && (g[i].I % 128 == 0);
+  }
+  // token-tile height from the mean rows per expert of the group with the most
+  // experts (the routed experts when the shared expert rides along)
+  int big = 0;
+  for (int i = 1; i < ngroups; ++i)
+    if (g[i].E > g[big].E) big = i;
+  const double avg = g[big].E > 0 ? (double)g[big].nrows / g[big].E : 0.0;
   p.mt = avg <= 16 ? 1 : (avg <= 32 ? 2 : 4);
-  p.max_tiles = (int)(cdiv(N, 16 * p.mt) + (N < E ? N : E) + 1);
+  p.gw = all128 ? 2 : 1;
+  // many rows per expert: the LDS-tiled kernels (weights reused across 128 tokens)
+  p.tiled = (all128 && g[0].nrows > 0 && avg >= 48.0) ? 1 : 0;
+  p.bm = p.tiled ? 128 : 16 * p.mt;
+  int64_t cap = 1;
+  for (int i = 0; i < ngroups; ++i) cap += cdiv(g[i].nrows, p.bm) + std::min<int64_t>(g[i].nrows, g[i].E);
+  p.max_tiles = (int)cap;
+  (void)rows;
+  (void)experts;
   return p;
 }
 
 size_t ffn_tiles_bytes(const FfnPlan &p) { return align_up(sizeof(TileEntry) * (size_t)p.max_tiles + 256, 256); }
 
-template <bool FP8, int MT>
-static hipError_t run_ffn(const GateUpArgs &gu, const DownArgs &dn, int E, int H, int I, const FfnPlan &plan,
-                          TileEntry *tiles, int32_t *ntiles, int site, hipStream_t st) {
-  build_tiles_kernel<<<1, 1024, 0, st>>>(gu.off, E, 16 * MT, plan.max_tiles, tiles, ntiles);
+template <int MT>
+static void run_stream(const StreamArgs &a, const FfnPlan &plan, int maxI, int site, hipStream_t st) {
   timing_before(site, st);
-  if (I % 128 == 0) {
-    dim3 g1((unsigned)(I / 128), (unsigned)plan.max_tiles);
-    gate_up_kernel<FP8, MT, 2><<<g1, 256, 0, st>>>(gu);
+  if (plan.gw == 2) {
+    dim3 g1((unsigned)cdiv(maxI, 128), (unsigned)plan.max_tiles);
+    gate_up_stream_kernel<MT, 2><<<g1, 256, 0, st>>>(a);
   } else {
-    if constexpr (FP8) return hipErrorInvalidValue;
-    dim3 g1((unsigned)(I / 64), (unsigned)plan.max_tiles);
-    gate_up_kernel<FP8, MT, 1><<<g1, 256, 0, st>>>(gu);
+    dim3 g1((unsigned)cdiv(maxI, 64), (unsigned)plan.max_tiles);
+    gate_up_stream_kernel<MT, 1><<<g1, 256, 0, st>>>(a);
   }
   timing_after(site, st);
-  dim3 g2((unsigned)(H / 128), (unsigned)plan.max_tiles);
+  dim3 g2((unsigned)(a.H / 128), (unsigned)plan.max_tiles);
   timing_before(site + 1, st);
-  down_kernel<FP8, MT, 2><<<g2, 256, 0, st>>>(dn);
+  down_stream_kernel<MT, 2><<<g2, 256, 0, st>>>(a);
   timing_after(site + 1, st);
-  return hipGetLastError();
 }
 
-hipError_t launch_expert_ffn(const uint8_t *x, const float *xs, const uint8_t *w_gu, const float *s_gu,
-                             const uint8_t *w_d, const float *s_d, const int32_t *offsets, int E, int H,
-                             int I, int64_t N, bool fp8, const FfnPlan &plan, int32_t *tiles_ws,
-                             uint8_t *h, float *hs, void *y, bool y_f32, bool shared_site, hipStream_t st) {
-  if (N == 0) return hipSuccess;
+hipError_t launch_expert_ffn(const FfnGroup *g, int ngroups, int H, const FfnPlan &plan, int32_t *tiles_ws,
+                             int site, hipStream_t st) {
+  if (ngroups < 1 || ngroups > kMaxGroups) return hipErrorInvalidValue;
+  int64_t rows = 0;
+  int maxI = 0;
+  for (int i = 0; i < ngroups; ++i) {
+    rows += g[i].nrows;
+    maxI = std::max(maxI, (int)g[i].I);
+    if (g[i].fp8 && plan.gw != 2) return hipErrorInvalidValue;
+  }
+  if (rows == 0) return hipSuccess;
   int32_t *ntiles = tiles_ws;
   TileEntry *tiles = reinterpret_cast<TileEntry *>(tiles_ws + 64);
-  GateUpArgs gu{x, xs, w_gu, s_gu, offsets, tiles, ntiles, h, hs, H, I, (int)N};
-  DownArgs dn{h, hs, w_d, s_d, offsets, tiles, ntiles, y, H, I, y_f32 ? 1 : 0, (int)N};
-#define MOE_FFN_CASE(F, M) \
-  if (fp8 == F && plan.mt == M) return run_ffn<F, M>(gu, dn, E, H, I, plan, tiles, ntiles, shared_site ? 6 : 4, st);
-  MOE_FFN_CASE(true, 1) MOE_FFN_CASE(true, 2) MOE_FFN_CASE(true, 4)
-  MOE_FFN_CASE(false, 1) MOE_FFN_CASE(false, 2) MOE_FFN_CASE(false, 4)
-#undef MOE_FFN_CASE
-  return hipErrorInvalidValue;
+  StreamArgs a{g[0], ngroups > 1 ? g[1] : g[0], tiles, ntiles, H};
+  build_tiles_kernel<<<1, 1024, 0, st>>>(a.g0, a.g1, ngroups, plan.bm, plan.max_tiles, tiles, ntiles);
+  if (plan.tiled) {
+    if (H % 256 != 0) return hipErrorInvalidValue;
+    return launch_tiled_ffn(g, ngroups, H, tiles, ntiles, num_compute_units(), site, st);
+  }
+  switch (plan.mt) {
+    case 1: run_stream<1>(a, plan, maxI, site, st); break;
+    case 2: run_stream<2>(a, plan, maxI, site, st); break;
+    case 4: run_stream<4>(a, plan, maxI, site, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -1,0 +1,476 @@
+// expert_gemm_tiled.hip -- the grouped expert GEMMs for experts with many
+// rows (prefill): LDS-tiled, double-buffered, persistent and XCD-aware.
+//
+// Same operation as the streaming kernels in expert_gemm.hip (gate/up with a
+// fused SwiGLU epilogue, then down; "Step-5 minimal inference", introduction:
+// block-scaled FP8 expert GEMM), organised for reuse:
+//   - a workgroup tile is 256 weight rows x 128 token rows; each 128-byte K
+//     chunk of both (one fp8 scale block, or 64 bf16 values) is copied straight
+//     from HBM into LDS by direct-to-LDS loads (48 KB per stage, a ring of
+//     three stages, two in flight while the third is consumed), so a weight
+//     byte fetched once feeds 128 tokens and a token byte feeds 256 weight rows;
+//   - 4 waves = 2 (weight halves of 128 rows) x 2 (token halves); a wave owns
+//     8 x 4 MFMA tiles of 16x16 (128 rows x 64 tokens, 128 fp32 accumulators
+//     per lane), with its token sub-tiles interleaved (16-row slices
+//     wm, wm+2, wm+4, wm+6) so that a partly filled tile idles both waves
+//     equally and slices beyond the last row skip their MFMAs;
+//   - LDS rows are 128 bytes with the 16-byte column XOR-swizzled by row % 8,
+//     so the MFMA operand reads (8 lanes = 8 consecutive rows) hit distinct banks;
+//   - the grid is one workgroup per CU; work items (tile-list slot x column
+//     tile) are split into 8 contiguous ranges, one per XCD (workgroup i runs
+//     on XCD i % 8), so the column tiles of one token tile share that XCD's L2.
+
+#include <algorithm>
+
+#include "moe_common.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+namespace {
+constexpr int TBN = 256;                    // weight rows per workgroup tile
+constexpr int TBM = 128;                    // token rows per workgroup tile
+constexpr int TW = TBN * 128;               // weight bytes per stage
+constexpr int TX = TBM * 128;               // token bytes per stage
+constexpr int TSX = 1024;                   // token scales per stage (4 waves x 256 B)
+constexpr int TSTAGE = TW + TX + TSX;       // bytes per LDS stage
+constexpr int NSTAGE = 3;
+constexpr int TTHREADS = 256;
+
+struct TiledArgs {
+  FfnGroup g0, g1;
+  const TileEntry *tiles;
+  const int32_t *ntiles;
+  int H;
+  int nt;        // column tiles per tile-list slot (largest over the groups)
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
+
+// Copy 16 bytes per lane from global memory to LDS at base + 16 * lane.
+__device__ __forceinline__ void dma16(const void *g, uint8_t *lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void *)g, (lds_void *)lds_base, 16, 0, 0);
+}
+// Copy 4 bytes per lane to LDS at base + 4 * lane.
+__device__ __forceinline__ void dma4(const void *g, uint8_t *lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void *)g, (lds_void *)lds_base, 4, 0, 0);
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0], [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+// Workgroup barrier without a memory fence (the direct-to-LDS copies are
+// waited for explicitly with vmcnt); the empty asm keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ int swz_f(int row) { return row & 7; }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ swz_f(row)) << 4); }
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+}  // namespace
+
+// One work item: a 256 x 128 output tile (gate/up: 128 gate + the matching 128
+// up rows = 128 h columns; down: 256 output columns) of one expert.
+template <bool FP8, bool GATEUP>
+struct TiledItem {
+  // ---- set up by the constructor
+  const FfnGroup &G;
+  int e, rbeg, rend, nvalid, I, K, KB, nchunk, col0, ntile, H;
+  int64_t rowb;
+  const uint8_t *wsrc, *asrc;
+  const float *ascale;
+  int lane, w, wn, wm;
+  uint32_t woff[8], xoff[4], soff;   // per-lane byte offsets of this lane's copies
+
+  __device__ TiledItem(const FfnGroup &g, const TileEntry &te, int nt_, int H_) : G(g), ntile(nt_), H(H_) {
+    lane = threadIdx.x & 63;
+    w = uniform(threadIdx.x >> 6);
+    wn = w & 1;
+    wm = w >> 1;
+    e = te.ge & 0xFFFFFF;
+    rend = min(max(G.off[e + 1], 0), G.nrows);
+    rbeg = min(max(G.off[e], 0) + te.m0, rend);
+    nvalid = min(rend - rbeg, TBM);
+    I = G.I;
+    K = GATEUP ? H : I;
+    rowb = (int64_t)K * (FP8 ? 1 : 2);
+    nchunk = (int)(rowb / 128);
+    KB = K / 128;
+    col0 = GATEUP ? ntile * 128 : ntile * TBN;
+    wsrc = GATEUP ? G.wgu + (int64_t)e * 2 * I * rowb : G.wd + (int64_t)e * H * rowb;
+    asrc = (GATEUP ? G.x : G.h) + (int64_t)rbeg * rowb;
+    ascale = (GATEUP ? G.xs : G.hs) + (FP8 ? (int64_t)rbeg * KB : 0);
+    const int sub = lane >> 3;   // row within an 8-row group
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int r = 8 * (w + 4 * q) + sub;
+      const int c = (lane & 7) ^ swz_f(r);   // logical 16-byte column landing in this lane's slot
+      const int grow = GATEUP ? (r < 128 ? col0 + r : I + col0 + r - 128) : col0 + r;
+      woff[q] = (uint32_t)(grow * rowb + c * 16);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 8 * (w + 4 * q) + sub;
+      const int c = (lane & 7) ^ swz_f(r);
+      xoff[q] = (uint32_t)(min(r, nvalid - 1) * rowb + c * 16);   // rows past the end repeat a valid row
+    }
+    soff = (uint32_t)(min(32 * w + (lane & 31), nvalid - 1) * KB * 4);
+  }
+
+  // Issue the direct-to-LDS copies of K chunk kc into stage buffer sb:
+  // 8 (weights) + 4 (tokens) [+ 1 (token scales, fp8)] instructions per wave.
+  __device__ __forceinline__ void issue(int kc, uint8_t *sb) const {
+    const uint8_t *wb = wsrc + (int64_t)kc * 128;   // uniform bases, per-lane 32-bit offsets
+    const uint8_t *xb = asrc + (int64_t)kc * 128;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dma16(wb + woff[q], sb + (w + 4 * q) * 1024);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dma16(xb + xoff[q], sb + TW + (w + 4 * q) * 1024);
+    if constexpr (FP8) dma4(reinterpret_cast<const uint8_t *>(ascale + kc) + soff, sb + TW + TX + 256 * w);
+  }
+
+  // Operands of one K chunk for this wave, read from LDS into registers.
+  // A (weight) fragments: one set, refilled in place with the next chunk's
+  // tile i right after tile i's MFMAs are issued.  B (token) fragments and
+  // scales: two sets, the next chunk's read at the start of a step.
+  struct AFrags {
+    i32x4 al[8], ah[8];
+  };
+  template <int NJ>
+  struct BFrags {
+    i32x4 bl[NJ], bh[NJ];
+    float sx[NJ];
+    float sa, sb;
+  };
+
+  __device__ __forceinline__ int arow(int i) const {
+    return (GATEUP ? (i < 4 ? 64 * wn + 16 * i : 128 + 64 * wn + 16 * (i - 4)) : 128 * wn + 16 * i) + (lane & 15);
+  }
+
+  __device__ __forceinline__ void read_a(const uint8_t *sb, int i, AFrags &A) const {
+    const int ck = 2 * (lane >> 4);
+    A.al[i] = *reinterpret_cast<const i32x4 *>(sb + swz(arow(i), ck));
+    A.ah[i] = *reinterpret_cast<const i32x4 *>(sb + swz(arow(i), ck + 1));
+  }
+
+  template <int NJ>
+  __device__ __forceinline__ void read_b(const uint8_t *sb, const float *wsc, int kc, BFrags<NJ> &F) const {
+    const int ck = 2 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int r = 16 * (wm + 2 * j) + (lane & 15);
+      F.bl[j] = *reinterpret_cast<const i32x4 *>(sb + TW + swz(r, ck));
+      F.bh[j] = *reinterpret_cast<const i32x4 *>(sb + TW + swz(r, ck + 1));
+      // token r's scale sits in wave (r / 32)'s slot, lane r % 32
+      if constexpr (FP8) F.sx[j] = *reinterpret_cast<const float *>(sb + TW + TX + 256 * (r >> 5) + 4 * (r & 31));
+    }
+    if constexpr (FP8) {
+      F.sa = GATEUP ? wsc[kc] : wsc[wn * KB + kc];
+      F.sb = GATEUP ? wsc[KB + kc] : F.sa;
+    }
+  }
+
+  // Chunk MFMAs from (A, F); A is refilled tile by tile from buffer `next`.
+  template <int NJ>
+  __device__ __forceinline__ void mma(AFrags &A, const BFrags<NJ> &F, const uint8_t *next, f32x4 (&acc)[8][4]) const {
+    if constexpr (FP8) {
+      // Raw block products are folded into the accumulators one weight tile
+      // behind, so tile i's MFMAs are in flight while tile i-1's products are
+      // scaled in by FMAs.
+      float sc[2][NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        sc[0][j] = F.sa * F.sx[j];
+        sc[1][j] = F.sb * F.sx[j];
+      }
+      constexpr int NT = 8 * NJ;
+      f32x4 prev = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t <= NT; ++t) {
+        f32x4 cur = {0.f, 0.f, 0.f, 0.f};
+        if (t < NT) {
+          const int i = t / NJ, j = t % NJ;
+          const i32x8 a8 = {A.al[i][0], A.al[i][1], A.al[i][2], A.al[i][3],
+                            A.ah[i][0], A.ah[i][1], A.ah[i][2], A.ah[i][3]};
+          const i32x8 b8 = {F.bl[j][0], F.bl[j][1], F.bl[j][2], F.bl[j][3],
+                            F.bh[j][0], F.bh[j][1], F.bh[j][2], F.bh[j][3]};
+          cur = mfma_fp8(a8, b8, f32x4{0.f, 0.f, 0.f, 0.f});
+          if (j == NJ - 1) read_a(next, i, A);
+        }
+        if (t > 0) {
+          const int i = (t - 1) / NJ, j = (t - 1) % NJ;
+          const float s = sc[(GATEUP && i >= 4) ? 1 : 0][j];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(prev[r], s, acc[i][j][r]);
+        }
+        prev = cur;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          acc[i][j] = mfma_bf16(__builtin_bit_cast(bf16x8, A.al[i]), __builtin_bit_cast(bf16x8, F.bl[j]), acc[i][j]);
+          acc[i][j] = mfma_bf16(__builtin_bit_cast(bf16x8, A.ah[i]), __builtin_bit_cast(bf16x8, F.bh[j]), acc[i][j]);
+        }
+        read_a(next, i, A);
+      }
+    }
+  }
+
+  // The item's weight-block scales, staged once in LDS (wsc[0][kb], wsc[1][kb]):
+  // gate/up: the gate block and the up block of the tile; down: the block of
+  // each weight half.  Loaded before the copy ring starts, so the only vector
+  // memory operations inside the K loop are the counted direct-to-LDS copies.
+  __device__ __forceinline__ void load_wscales(float *wsc) const {
+    if constexpr (FP8) {
+      const float *s0, *s1;
+      if (GATEUP) {
+        s0 = G.sgu + ((int64_t)e * (2 * I / 128) + col0 / 128) * KB;
+        s1 = G.sgu + ((int64_t)e * (2 * I / 128) + (I + col0) / 128) * KB;
+      } else {
+        s0 = G.sd + ((int64_t)e * (H / 128) + col0 / 128) * KB;
+        s1 = G.sd + ((int64_t)e * (H / 128) + (col0 + 128) / 128) * KB;
+      }
+      for (int i = threadIdx.x; i < 2 * KB; i += TTHREADS) wsc[i] = i < KB ? s0[i] : s1[i - KB];
+    }
+  }
+
+  // One pipeline step: chunk kc's operands are already in Fcur.  Wait until
+  // chunk kc+1 has landed in LDS (chunk kc+2 may still be in flight) and this
+  // wave's reads of chunk kc have completed, sync the workgroup (chunk kc's
+  // buffer is then free and is refilled with chunk kc+3), read chunk kc+1 into
+  // Fnext, and run chunk kc's MFMAs while those reads are in flight.
+  template <int NJ>
+  __device__ __forceinline__ void step(int kc, uint8_t *lds, const float *wsc, AFrags &A, BFrags<NJ> &Fcur,
+                                       BFrags<NJ> &Fnext, f32x4 (&acc)[8][4]) const {
+    constexpr int PS = FP8 ? 13 : 12;    // vector memory instructions per wave per stage
+    if (kc + 2 < nchunk)
+      wait_vm_lgkm0<PS>();
+    else
+      wait_vm_lgkm0<0>();
+    wg_barrier();
+    if (kc + 3 < nchunk) issue(kc + 3, lds + ((kc + 3) % NSTAGE) * TSTAGE);
+    // The last step reads its own buffer again (nothing is copied into it any
+    // more), which keeps the refills unconditional.
+    const int kn = kc + 1 < nchunk ? kc + 1 : kc;
+    const uint8_t *next = lds + (kn % NSTAGE) * TSTAGE;
+    read_b<NJ>(next, wsc, kn, Fnext);
+    mma<NJ>(A, Fcur, next, acc);
+  }
+
+  template <int NJ>
+  __device__ __forceinline__ void mainloop(uint8_t *lds, const float *wsc, f32x4 (&acc)[8][4]) const {
+    constexpr int PS = FP8 ? 13 : 12;
+    issue(0, lds);
+    if (nchunk > 1) issue(1, lds + TSTAGE);
+    if (nchunk > 2) issue(2, lds + 2 * TSTAGE);
+    if (nchunk > 2)
+      wait_vm<2 * PS>();
+    else if (nchunk > 1)
+      wait_vm<PS>();
+    else
+      wait_vm<0>();
+    wg_barrier();
+    AFrags A;
+    BFrags<NJ> F0, F1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) read_a(lds, i, A);
+    read_b<NJ>(lds, wsc, 0, F0);
+    for (int kc = 0; kc < nchunk; kc += 2) {
+      step<NJ>(kc, lds, wsc, A, F0, F1, acc);
+      if (kc + 1 < nchunk) step<NJ>(kc + 1, lds, wsc, A, F1, F0, acc);
+    }
+  }
+};
+
+template <bool FP8, bool GATEUP>
+__device__ __forceinline__ void tiled_item(const FfnGroup &G, const TileEntry &te, int ntile, int H, uint8_t *lds,
+                                           float *red, float *wsc) {
+  TiledItem<FP8, GATEUP> it(G, te, ntile, H);
+  it.load_wscales(wsc);
+  __syncthreads();
+  const int lane = it.lane, wn = it.wn, wm = it.wm;
+  // active 16-row token slices of this wave: slice j covers rows 16*(wm + 2j)
+  const int nact = uniform(it.nvalid <= 16 * wm ? 0 : min(4, (it.nvalid - 16 * wm + 31) / 32));
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  switch (nact) {
+    case 4: it.template mainloop<4>(lds, wsc, acc); break;
+    case 3: it.template mainloop<3>(lds, wsc, acc); break;
+    case 2: it.template mainloop<2>(lds, wsc, acc); break;
+    case 1: it.template mainloop<1>(lds, wsc, acc); break;
+    default: it.template mainloop<1>(lds, wsc, acc); break;   // keeps the barrier count equal across waves
+  }
+  const int rbeg = it.rbeg, nvalid = it.nvalid, I = it.I, col0 = it.col0;
+  int brow[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) brow[j] = 16 * (wm + 2 * j);
+
+  // ---- epilogue.  Lane holds rows 4*(lane/16)+r of weight tile i for token
+  // slice j, token row = rbeg + brow[j] + lane%16.
+  if constexpr (GATEUP) {
+    float hv[4][4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float g = acc[i][j][r], u = acc[i + 4][j][r];
+          hv[i][j][r] = __fdiv_rn(g, 1.0f + expf(-g)) * u;
+        }
+    if constexpr (!FP8) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tr = brow[j] + (lane & 15);
+        if (tr >= nvalid) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int col = col0 + 64 * wn + 16 * i + 4 * (lane >> 4);
+          const uint32_t lo = f32_to_bf16(hv[i][j][0]) | (f32_to_bf16(hv[i][j][1]) << 16);
+          const uint32_t hi = f32_to_bf16(hv[i][j][2]) | (f32_to_bf16(hv[i][j][3]) << 16);
+          *reinterpret_cast<uint2 *>(G.h + ((int64_t)(rbeg + tr) * I + col) * 2) = make_uint2(lo, hi);
+        }
+      }
+    } else {
+      // amax over the tile's 128 h columns per token: lane (16 values), the 4
+      // lanes of the token (xor 16, 32), then the two weight-half waves (LDS).
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float am = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) am = __builtin_fmaxf(am, __builtin_fabsf(hv[i][j][r]));
+        am = __builtin_fmaxf(am, __shfl_xor(am, 16, kWave));
+        am = __builtin_fmaxf(am, __shfl_xor(am, 32, kWave));
+        if (lane < 16) red[wn * TBM + brow[j] + lane] = am;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tr = brow[j] + (lane & 15);
+        const float s = group_scale(__builtin_fmaxf(red[tr], red[TBM + tr]));
+        if (tr >= nvalid) continue;
+        const int64_t row = rbeg + tr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int col = col0 + 64 * wn + 16 * i + 4 * (lane >> 4);
+          *reinterpret_cast<uint32_t *>(G.h + row * I + col) =
+              f32x4_to_e4m3(__fdiv_rn(hv[i][j][0], s), __fdiv_rn(hv[i][j][1], s), __fdiv_rn(hv[i][j][2], s),
+                            __fdiv_rn(hv[i][j][3], s));
+        }
+        if (wn == 0 && lane < 16) G.hs[row * (I / 128) + ntile] = s;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tr = brow[j] + (lane & 15);
+      if (tr >= nvalid) continue;
+      const int64_t row = rbeg + tr;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int col = col0 + 128 * wn + 16 * i + 4 * (lane >> 4);
+        const int64_t o = row * H + col;
+        if (G.y_f32) {
+          *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(G.y) + o) = acc[i][j];
+        } else {
+          const uint32_t lo = f32_to_bf16(acc[i][j][0]) | (f32_to_bf16(acc[i][j][1]) << 16);
+          const uint32_t hi = f32_to_bf16(acc[i][j][2]) | (f32_to_bf16(acc[i][j][3]) << 16);
+          *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(G.y) + o) = make_uint2(lo, hi);
+        }
+      }
+    }
+  }
+  __syncthreads();   // the next work item reuses the LDS ring and the reduction area
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(TTHREADS, 1) void tiled_ffn_kernel(TiledArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  float *red = reinterpret_cast<float *>(lds + NSTAGE * TSTAGE);
+  float *wsc = red + 2 * TBM;
+  const int count = a.ntiles[0] * a.nt;
+  const int xcd = blockIdx.x & 7, per = gridDim.x >> 3, slot0 = blockIdx.x >> 3;
+  const int span = (count + 7) / 8;
+  const int beg = xcd * span, end = min(beg + span, count);
+  for (int L = beg + slot0; L < end; L += per) {
+    const int slot = L / a.nt, ntile = L % a.nt;
+    const TileEntry te = a.tiles[slot];
+    const FfnGroup G = (te.ge >> 24) ? a.g1 : a.g0;
+    if (GATEUP && ntile * 128 >= G.I) continue;
+    if (G.fp8)
+      tiled_item<true, GATEUP>(G, te, ntile, a.H, lds, red, wsc);
+    else
+      tiled_item<false, GATEUP>(G, te, ntile, a.H, lds, red, wsc);
+  }
+}
+
+// LDS: the copy ring, the h-scale reduction area, the weight-scale staging (H, I <= 16384)
+size_t tiled_lds_bytes() { return NSTAGE * TSTAGE + 2 * TBM * sizeof(float) + 2 * 128 * sizeof(float); }
+
+int num_compute_units() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+hipError_t launch_tiled_ffn(const FfnGroup *g, int ngroups, int H, const void *tiles, const int32_t *ntiles,
+                            int num_cus, int site, hipStream_t st) {
+  TiledArgs a{g[0], ngroups > 1 ? g[1] : g[0], static_cast<const TileEntry *>(tiles), ntiles, H, 0};
+  int maxI = 0;
+  for (int i = 0; i < ngroups; ++i) maxI = std::max(maxI, (int)g[i].I);
+  const unsigned grid = (unsigned)(std::max(num_cus, 8) / 8 * 8);
+  const size_t lds = tiled_lds_bytes();
+  static bool attr_set[64] = {};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (dev >= 0 && dev < 64 && !attr_set[dev]) {
+    hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void *>(&tiled_ffn_kernel<true>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void *>(&tiled_ffn_kernel<false>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e1 != hipSuccess) return e1;
+    if (e2 != hipSuccess) return e2;
+    attr_set[dev] = true;
+  }
+  a.nt = maxI / 128;
+  timing_before(site, st);
+  tiled_ffn_kernel<true><<<grid, TTHREADS, lds, st>>>(a);
+  timing_after(site, st);
+  a.nt = H / TBN;
+  timing_before(site + 1, st);
+  tiled_ffn_kernel<false><<<grid, TTHREADS, lds, st>>>(a);
+  timing_after(site + 1, st);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -11,6 +11,7 @@
 #include <string>
 
 #include "../../include/moe.h"
+#include "../../include/moe_timing.h"
 #include "moe_kernels.h"
 
 namespace {
@@ -126,19 +127,58 @@ RouteWs carve_route(Carve &c, const moe_layer *L, int64_t T) {
 
 int32_t *carve_sort(Carve &c, int64_t N, int64_t nbins) { return c.take<int32_t>(moe::sort_ws_words(N, nbins) + 1); }
 
+// Expert-FFN workspace: the tile list plus each group's intermediate h.
 struct FfnWs {
   moe::FfnPlan plan;
   int32_t *tiles;
-  uint8_t *h;
-  float *hs;
+  uint8_t *h[moe::kMaxGroups];
+  float *hs[moe::kMaxGroups];
 };
-FfnWs carve_ffn(Carve &c, int64_t N, int E, int I, bool fp8) {
+FfnWs carve_ffn(Carve &c, moe::FfnGroup *g, int ngroups) {
   FfnWs f;
-  f.plan = moe::ffn_plan(N, E);
+  f.plan = moe::ffn_plan(g, ngroups);
   f.tiles = c.take<int32_t>(moe::ffn_tiles_bytes(f.plan) / 4);
-  f.h = c.take<uint8_t>((size_t)N * I * (fp8 ? 1 : 2) + 16);
-  f.hs = fp8 ? c.take<float>((size_t)N * (I / 128) + 1) : nullptr;
+  for (int i = 0; i < ngroups; ++i) {
+    f.h[i] = c.take<uint8_t>((size_t)g[i].nrows * g[i].I * (g[i].fp8 ? 1 : 2) + 16);
+    f.hs[i] = g[i].fp8 ? c.take<float>((size_t)g[i].nrows * (g[i].I / 128) + 1) : nullptr;
+    g[i].h = f.h[i];
+    g[i].hs = f.hs[i];
+  }
   return f;
+}
+
+moe::FfnGroup routed_group(const moe_layer *L, const void *x_perm, const float *x_scale, const int32_t *off,
+                           int64_t N, void *y, bool y_f32) {
+  moe::FfnGroup g{};
+  g.x = static_cast<const uint8_t *>(x_perm);
+  g.xs = x_scale;
+  g.wgu = static_cast<const uint8_t *>(L->w_gate_up);
+  g.sgu = L->s_gate_up;
+  g.wd = static_cast<const uint8_t *>(L->w_down);
+  g.sd = L->s_down;
+  g.off = off;
+  g.y = y;
+  g.E = L->num_experts;
+  g.I = L->inter;
+  g.nrows = (int32_t)N;
+  g.fp8 = is_fp8(L) ? 1 : 0;
+  g.y_f32 = y_f32 ? 1 : 0;
+  return g;
+}
+
+moe::FfnGroup shared_group(const moe_layer *L, const void *x, const int32_t *off2, int64_t T, void *y, bool y_f32) {
+  moe::FfnGroup g{};
+  g.x = static_cast<const uint8_t *>(x);
+  g.wgu = static_cast<const uint8_t *>(L->w_shared_gate_up);
+  g.wd = static_cast<const uint8_t *>(L->w_shared_down);
+  g.off = off2;
+  g.y = y;
+  g.E = 1;
+  g.I = L->shared_inter;
+  g.nrows = (int32_t)T;
+  g.fp8 = 0;
+  g.y_f32 = y_f32 ? 1 : 0;
+  return g;
 }
 
 struct CombineWs {
@@ -159,13 +199,14 @@ struct ForwardWs {
   int32_t *offsets, *perm_src, *perm_pos, *sort;
   uint8_t *x_perm;
   float *x_scale;
-  FfnWs ffn;
+  FfnWs ffn;                       // routed (+ shared) experts in one launch
+  moe::FfnGroup groups[moe::kMaxGroups];
+  int ngroups;
   uint16_t *y_perm;
   int32_t *sh_off;
-  FfnWs sh_ffn;
   void *sh_out;
 };
-ForwardWs carve_forward(Carve &c, const moe_layer *L, int64_t T, bool out_f32) {
+ForwardWs carve_forward(Carve &c, const moe_layer *L, const void *x, int64_t T, bool out_f32) {
   ForwardWs f;
   const int64_t N = T * L->top_k;
   const int H = L->hidden, E = L->num_experts;
@@ -178,22 +219,30 @@ ForwardWs carve_forward(Carve &c, const moe_layer *L, int64_t T, bool out_f32) {
   f.sort = carve_sort(c, N, E);
   f.x_perm = c.take<uint8_t>((size_t)N * H * esz(L) + 16);
   f.x_scale = is_fp8(L) ? c.take<float>((size_t)N * (H / 128) + 1) : nullptr;
-  f.ffn = carve_ffn(c, N, E, L->inter, is_fp8(L));
   f.y_perm = c.take<uint16_t>((size_t)N * H + 8);
+  f.ngroups = 0;
   if (L->shared_inter > 0) {
     f.sh_off = c.take<int32_t>(2);
-    f.sh_ffn = carve_ffn(c, T, 1, L->shared_inter, false);
     f.sh_out = c.take<uint8_t>((size_t)T * H * (out_f32 ? 4 : 2) + 16);
+    // the shared expert's tiles go first in the list: they carry twice the bytes (bf16)
+    f.groups[f.ngroups++] = shared_group(L, x, f.sh_off, T, f.sh_out, out_f32);
   } else {
     f.sh_off = nullptr;
     f.sh_out = nullptr;
   }
+  f.groups[f.ngroups++] = routed_group(L, f.x_perm, f.x_scale, f.offsets, N, f.y_perm, false);
+  f.ffn = carve_ffn(c, f.groups, f.ngroups);
   return f;
 }
 
 size_t need_route(const moe_layer *L, int64_t T) { Carve c(nullptr); carve_route(c, L, T); return c.used; }
 size_t need_permute(const moe_layer *L, int64_t N) { Carve c(nullptr); carve_sort(c, N, L->num_experts); return c.used; }
-size_t need_ffn(int64_t N, int E, int I, bool fp8) { Carve c(nullptr); carve_ffn(c, N, E, I, fp8); return c.used; }
+size_t need_ffn(const moe_layer *L, int64_t N) {
+  Carve c(nullptr);
+  moe::FfnGroup g = routed_group(L, nullptr, nullptr, nullptr, N, nullptr, false);
+  carve_ffn(c, &g, 1);
+  return c.used;
+}
 size_t need_combine(int64_t T, int64_t N, bool tokens) {
   if (!tokens) return 0;
   Carve c(nullptr);
@@ -202,7 +251,7 @@ size_t need_combine(int64_t T, int64_t N, bool tokens) {
 }
 size_t need_forward(const moe_layer *L, int64_t T) {
   Carve c(nullptr);
-  carve_forward(c, L, T, true);
+  carve_forward(c, L, nullptr, T, true);
   return c.used;
 }
 
@@ -228,9 +277,8 @@ size_t moe_workspace_bytes(const moe_layer *L, int64_t T, int64_t N) {
   size_t need = 0;
   auto upd = [&](size_t v) { need = v > need ? v : need; };
   upd(need_permute(L, N));
-  upd(need_ffn(N, L->num_experts, L->inter, is_fp8(L)));
+  upd(need_ffn(L, N));
   upd(need_combine(T, N, true));
-  if (L->shared_inter > 0) upd(need_ffn(T, 1, L->shared_inter, false));
   if (L->top_k >= 1) {
     upd(need_route(L, T));
     upd(need_forward(L, T));
@@ -301,15 +349,12 @@ moe_status moe_expert_ffn(const moe_layer *L, const int32_t *expert_offsets, con
     if (!aligned16(x_perm) || !aligned16(y_perm)) return fail(MOE_EINVAL, "x_perm or y_perm not 16-byte aligned");
   }
   if (N == 0) return MOE_OK;
-  if ((s = check_ws(ws, ws_bytes, need_ffn(N, L->num_experts, L->inter, is_fp8(L)))) != MOE_OK) return s;
+  if ((s = check_ws(ws, ws_bytes, need_ffn(L, N))) != MOE_OK) return s;
   Carve c(ws);
-  FfnWs f = carve_ffn(c, N, L->num_experts, L->inter, is_fp8(L));
-  return hip_status(
-      moe::launch_expert_ffn(static_cast<const uint8_t *>(x_perm), x_scale, static_cast<const uint8_t *>(L->w_gate_up),
-                             L->s_gate_up, static_cast<const uint8_t *>(L->w_down), L->s_down, expert_offsets,
-                             L->num_experts, L->hidden, L->inter, N, is_fp8(L), f.plan, f.tiles, f.h, f.hs, y_perm,
-                             y_dtype == MOE_F32, false, (hipStream_t)stream),
-      "moe_expert_ffn");
+  moe::FfnGroup g = routed_group(L, x_perm, x_scale, expert_offsets, N, y_perm, y_dtype == MOE_F32);
+  FfnWs f = carve_ffn(c, &g, 1);
+  return hip_status(moe::launch_expert_ffn(&g, 1, L->hidden, f.plan, f.tiles, MOE_SITE_GATE_UP, (hipStream_t)stream),
+                    "moe_expert_ffn");
 }
 
 moe_status moe_combine(const moe_layer *L, const void *y_perm, int32_t y_dtype, const int32_t *perm_pos,
@@ -368,7 +413,7 @@ moe_status moe_forward(const moe_layer *L, const void *x, int64_t T, void *y, in
   const int64_t N = T * L->top_k;
   const int H = L->hidden, E = L->num_experts;
   Carve c(ws);
-  ForwardWs f = carve_forward(c, L, T, out_f32);
+  ForwardWs f = carve_forward(c, L, x, T, out_f32);
   int32_t *ids = topk_ids ? topk_ids : f.ids;
   float *gates = topk_gates ? topk_gates : f.gates;
   hipError_t e;
@@ -380,20 +425,12 @@ moe_status moe_forward(const moe_layer *L, const void *x, int64_t T, void *y, in
   e = moe::launch_gather_rows(static_cast<const uint16_t *>(x), H, f.perm_src, nullptr, L->top_k, N, f.offsets + E,
                               is_fp8(L), f.x_perm, f.x_scale, st);
   if (e != hipSuccess) return hip_status(e, "moe_forward: gather");
-  e = moe::launch_expert_ffn(f.x_perm, f.x_scale, static_cast<const uint8_t *>(L->w_gate_up), L->s_gate_up,
-                             static_cast<const uint8_t *>(L->w_down), L->s_down, f.offsets, E, H, L->inter, N,
-                             is_fp8(L), f.ffn.plan, f.ffn.tiles, f.ffn.h, f.ffn.hs, f.y_perm, false, false, st);
-  if (e != hipSuccess) return hip_status(e, "moe_forward: routed experts");
   if (L->shared_inter > 0) {
     e = moe::launch_fill_offsets2(f.sh_off, (int32_t)T, st);
     if (e != hipSuccess) return hip_status(e, "moe_forward: shared offsets");
-    e = moe::launch_expert_ffn(static_cast<const uint8_t *>(x), nullptr,
-                               static_cast<const uint8_t *>(L->w_shared_gate_up), nullptr,
-                               static_cast<const uint8_t *>(L->w_shared_down), nullptr, f.sh_off, 1, H,
-                               L->shared_inter, T, false, f.sh_ffn.plan, f.sh_ffn.tiles, f.sh_ffn.h, nullptr,
-                               f.sh_out, out_f32, true, st);
-    if (e != hipSuccess) return hip_status(e, "moe_forward: shared expert");
   }
+  e = moe::launch_expert_ffn(f.groups, f.ngroups, H, f.ffn.plan, f.ffn.tiles, MOE_SITE_GATE_UP, st);
+  if (e != hipSuccess) return hip_status(e, "moe_forward: experts");
   e = moe::launch_combine(f.y_perm, false, f.perm_pos, nullptr, nullptr, L->top_k, gates, f.sh_out, out_f32, T, H, N, y,
                           out_f32, st);
   return hip_status(e, "moe_forward: combine");

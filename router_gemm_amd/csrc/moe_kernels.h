@@ -39,17 +39,46 @@ hipError_t launch_gather_rows(const uint16_t *x, int64_t H, const int32_t *perm_
 hipError_t launch_fill_offsets2(int32_t *dst, int32_t n, hipStream_t st);
 
 // ---- grouped expert GEMMs (expert_gemm.hip)
+// One group = one set of experts with its own weights, rows and outputs.  A
+// launch covers up to two groups (the routed experts and the shared expert),
+// so the shared expert's tiles run inside the routed experts' launch.
+struct FfnGroup {
+  const uint8_t *x;    // [nrows, H] rows in expert order: e4m3 codes (fp8) or bf16
+  const float *xs;     // [nrows, H/128] (fp8)
+  const uint8_t *wgu;  // [E, 2I, H]: rows 0..I-1 gate, I..2I-1 up
+  const float *sgu;    // [E, 2I/128, H/128] (fp8)
+  const uint8_t *wd;   // [E, H, I]
+  const float *sd;     // [E, H/128, I/128] (fp8)
+  const int32_t *off;  // [E+1] device offsets of each expert's rows
+  uint8_t *h;          // [nrows, I] intermediate: e4m3 (fp8) or bf16
+  float *hs;           // [nrows, I/128] (fp8)
+  void *y;             // [nrows, H] output, bf16 or f32
+  int32_t E, I, nrows, fp8, y_f32;
+};
+constexpr int kMaxGroups = 2;
+// Tile list entry: group (0 or 1), expert of that group, first row (relative
+// to the expert's offset).
+struct TileEntry {
+  int32_t ge;   // group << 24 | expert
+  int32_t m0;
+};
 struct FfnPlan {
-  int mt;          // 16-row token subtiles per workgroup
+  int tiled;       // 1: LDS-tiled persistent kernels (128-row token tiles), 0: streaming kernels
+  int mt;          // streaming: 16-row token subtiles per workgroup
+  int gw;          // streaming: gate (and up) 16-row weight tiles per wave (2 -> 128 h columns)
+  int bm;          // token rows per tile-list entry
   int max_tiles;   // capacity of the tile list
 };
-FfnPlan ffn_plan(int64_t N, int E);
+FfnPlan ffn_plan(const FfnGroup *g, int ngroups);
 size_t ffn_tiles_bytes(const FfnPlan &p);
-// h: [N, I] bf16 or e4m3 (+ hs [N, I/128]).
-hipError_t launch_expert_ffn(const uint8_t *x, const float *xs, const uint8_t *w_gu, const float *s_gu,
-                             const uint8_t *w_d, const float *s_d, const int32_t *offsets, int E, int H,
-                             int I, int64_t N, bool fp8, const FfnPlan &plan, int32_t *tiles,
-                             uint8_t *h, float *hs, void *y, bool y_f32, bool shared_site, hipStream_t st);
+// LDS-tiled variant (expert_gemm_tiled.hip); tiles built with 128-row entries.
+hipError_t launch_tiled_ffn(const FfnGroup *g, int ngroups, int H, const void *tiles, const int32_t *ntiles,
+                            int num_cus, int site, hipStream_t st);
+// Compute units of the current device (cached per device).
+int num_compute_units();
+// site: timing site of the gate/up launch (the down launch uses site + 1).
+hipError_t launch_expert_ffn(const FfnGroup *g, int ngroups, int H, const FfnPlan &plan, int32_t *tiles_ws,
+                             int site, hipStream_t st);
 
 // ---- combine (combine.hip)
 // y[t] = shared[t] + sum over the token's assignments (fixed order) of g * y_perm[perm_pos]

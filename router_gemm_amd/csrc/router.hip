@@ -71,15 +71,23 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
   if (t >= T) return;
   float v[NJ];
 #pragma unroll
+  for (int j = 0; j < NJ; ++j) v[j] = 0.f;
+  // partial sums added in split order s = 0..S-1 (loads of one split are independent)
+  for (int s = 0; s < S; ++s) {
+    const float *p = partial + ((int64_t)s * T + t) * E;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E) v[j] += p[e];
+    }
+  }
+#pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int e = lane + 64 * j;
-    float a = 0.f;
     if (e < E) {
-      for (int s = 0; s < S; ++s) a += partial[((int64_t)s * T + t) * E + e];
-      if (bias) a += bias[e];
-      if (logits_out) logits_out[(int64_t)t * E + e] = a;
+      if (bias) v[j] += bias[e];
+      if (logits_out) logits_out[(int64_t)t * E + e] = v[j];
     }
-    v[j] = a;
   }
   uint32_t taken = 0;
   float my_v = 0.f;
@@ -128,8 +136,9 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
 int router_ksplit(int64_t T, int E, int H) {
   const int64_t tiles = cdiv(E, 64) * cdiv(T, 64);
   int S = 1;
-  // split K until there are enough workgroups, keeping chunks of >= 128 (multiples of 32)
-  while (tiles * S < 512 && (H / (2 * S)) % 32 == 0 && H / (2 * S) >= 128 && H % (2 * S) == 0) S *= 2;
+  // split K (at most 8 ways) until there are enough workgroups, keeping chunks
+  // of >= 256 that are multiples of 32
+  while (S < 8 && tiles * S < 256 && H % (2 * S) == 0 && (H / (2 * S)) % 32 == 0 && H / (2 * S) >= 256) S *= 2;
   return S;
 }
 
