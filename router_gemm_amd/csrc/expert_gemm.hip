@@ -95,8 +95,6 @@ __device__ __forceinline__ f32x4 chunk_mma(const Frag &a, const Frag &b, f32x4 a
   }
 }
 
-__device__ __forceinline__ float silu(float z) { return __fdiv_rn(z, 1.0f + expf(-z)); }
-
 struct StreamArgs {
   FfnGroup g0, g1;
   const TileEntry *tiles;
@@ -187,7 +185,7 @@ __device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry 
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) hv[i][m][r] = silu(ag[i][m][r]) * au[i][m][r];
+      for (int r = 0; r < 4; ++r) hv[i][m][r] = swiglu(ag[i][m][r], au[i][m][r]);
 
   if constexpr (!FP8) {
 #pragma unroll
@@ -223,12 +221,12 @@ __device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry 
       const float am = __builtin_fmaxf(__builtin_fmaxf(red[0][tl], red[1][tl]),
                                        __builtin_fmaxf(red[2][tl], red[3][tl]));
       const float s = group_scale(am);
+      const float inv = __builtin_amdgcn_rcpf(s);
       if (!xv[m]) continue;
 #pragma unroll
       for (int i = 0; i < GW; ++i) {
         const int col = hc0 + 16 * i + 4 * (lane >> 4);
-        const uint32_t q = f32x4_to_e4m3(__fdiv_rn(hv[i][m][0], s), __fdiv_rn(hv[i][m][1], s),
-                                         __fdiv_rn(hv[i][m][2], s), __fdiv_rn(hv[i][m][3], s));
+        const uint32_t q = f32x4_to_e4m3(hv[i][m][0] * inv, hv[i][m][1] * inv, hv[i][m][2] * inv, hv[i][m][3] * inv);
         *reinterpret_cast<uint32_t *>(G.h + (int64_t)xrow[m] * I + col) = q;
       }
       if (w == 0 && lane < 16) G.hs[(int64_t)xrow[m] * (I / 128) + blockIdx.x] = s;

@@ -337,8 +337,7 @@ __device__ __forceinline__ void tiled_item(const FfnGroup &G, const TileEntry &t
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float g = acc[i][j][r], u = acc[i + 4][j][r];
-          hv[i][j][r] = __fdiv_rn(g, 1.0f + expf(-g)) * u;
+          hv[i][j][r] = swiglu(acc[i][j][r], acc[i + 4][j][r]);
         }
     if constexpr (!FP8) {
 #pragma unroll
@@ -372,14 +371,14 @@ __device__ __forceinline__ void tiled_item(const FfnGroup &G, const TileEntry &t
       for (int j = 0; j < 4; ++j) {
         const int tr = brow[j] + (lane & 15);
         const float s = group_scale(__builtin_fmaxf(red[tr], red[TBM + tr]));
+        const float inv = __builtin_amdgcn_rcpf(s);
         if (tr >= nvalid) continue;
         const int64_t row = rbeg + tr;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int col = col0 + 64 * wn + 16 * i + 4 * (lane >> 4);
           *reinterpret_cast<uint32_t *>(G.h + row * I + col) =
-              f32x4_to_e4m3(__fdiv_rn(hv[i][j][0], s), __fdiv_rn(hv[i][j][1], s), __fdiv_rn(hv[i][j][2], s),
-                            __fdiv_rn(hv[i][j][3], s));
+              f32x4_to_e4m3(hv[i][j][0] * inv, hv[i][j][1] * inv, hv[i][j][2] * inv, hv[i][j][3] * inv);
         }
         if (wn == 0 && lane < 16) G.hs[row * (I / 128) + ntile] = s;
       }

@@ -51,6 +51,12 @@ __device__ __forceinline__ float group_scale(float amax) {
   return amax == 0.0f ? 1.0f : __fdiv_rn(amax, kFp8Max);
 }
 
+// silu(z) * u for the SwiGLU epilogue, with the hardware exp and reciprocal
+// (h is not compared bit for bit; its rounding error is ~1e-7 relative).
+__device__ __forceinline__ float swiglu(float z, float u) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) * u;
+}
+
 // ---------------------------------------------------------------- MFMA
 
 // D(16x16, f32) += A(16x32 bf16) * B(32x16 bf16).  Lane l supplies row (A) /

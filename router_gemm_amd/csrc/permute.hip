@@ -25,10 +25,14 @@ constexpr int CH = kSortChunk;   // elements per chunk
 constexpr int SORT_THREADS = 256;
 }
 
+constexpr int SCAN_BLOCK = 256;         // bins per workgroup of the multi-workgroup scan
+constexpr int64_t SINGLE_SCAN_BINS = 4096;
+
 size_t sort_ws_words(int64_t N, int64_t nbins) {
   const int64_t nchunk = cdiv(N, CH);
-  // chunk counts [nchunk][nbins+1], sorted keys/indices/ranks [nchunk*CH] x 3
-  return (size_t)(nchunk * (nbins + 1) + 3 * nchunk * CH);
+  // chunk counts [nchunk][nbins+1], sorted keys/indices/ranks [nchunk*CH] x 3,
+  // per-block totals of the multi-workgroup scan
+  return (size_t)(nchunk * (nbins + 1) + 3 * nchunk * CH + cdiv(nbins, SCAN_BLOCK) + 1);
 }
 
 __global__ __launch_bounds__(SORT_THREADS) void sort_chunks_kernel(
@@ -147,6 +151,84 @@ __global__ __launch_bounds__(1024) void scan_counts_kernel(int32_t *__restrict__
   }
 }
 
+// Multi-workgroup variant for many bins (e.g. one bin per token).
+// Pass 1: per bin, exclusive scan over chunks in place; bin totals to offsets[b]
+// and per-block sums of the totals to bsum[block].
+__global__ __launch_bounds__(SCAN_BLOCK) void scan_bins_pass1(int32_t *__restrict__ cc, int nchunk, int nbins,
+                                                              int32_t *__restrict__ offsets, int32_t *__restrict__ bsum) {
+  __shared__ int32_t red[SCAN_BLOCK];
+  const int b = blockIdx.x * SCAN_BLOCK + threadIdx.x;
+  const int64_t ld = nbins + 1;
+  int32_t run = 0;
+  if (b < nbins) {
+    for (int c = 0; c < nchunk; ++c) {
+      const int32_t x = cc[c * ld + b];
+      cc[c * ld + b] = run;
+      run += x;
+    }
+    offsets[b] = run;
+  }
+  red[threadIdx.x] = run;
+  __syncthreads();
+  for (int o = SCAN_BLOCK / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) bsum[blockIdx.x] = red[0];
+}
+
+// Pass 2 (one workgroup): exclusive scan of the block sums; total to offsets[nbins].
+__global__ __launch_bounds__(1024) void scan_bins_pass2(int32_t *__restrict__ bsum, int nblocks, int nbins,
+                                                        int32_t *__restrict__ offsets) {
+  __shared__ int32_t buf[1024];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int b0 = 0; b0 < nblocks; b0 += 1024) {
+    const int b = b0 + tid;
+    const int32_t own = b < nblocks ? bsum[b] : 0;
+    buf[tid] = own;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int32_t add = tid >= off ? buf[tid - off] : 0;
+      __syncthreads();
+      buf[tid] += add;
+      __syncthreads();
+    }
+    const int32_t excl = carry + buf[tid] - own;
+    if (b < nblocks) bsum[b] = excl;
+    __syncthreads();
+    if (tid == 1023) carry = excl + own;
+    __syncthreads();
+  }
+  if (tid == 0) offsets[nbins] = carry;
+}
+
+// Pass 3: exclusive scan of the bin totals inside each block plus the block's
+// base gives offsets[b]; every chunk's base for the bin adds it.
+__global__ __launch_bounds__(SCAN_BLOCK) void scan_bins_pass3(int32_t *__restrict__ cc, int nchunk, int nbins,
+                                                              int32_t *__restrict__ offsets,
+                                                              const int32_t *__restrict__ bsum) {
+  __shared__ int32_t buf[SCAN_BLOCK];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x * SCAN_BLOCK + tid;
+  const int32_t own = b < nbins ? offsets[b] : 0;
+  buf[tid] = own;
+  __syncthreads();
+  for (int off = 1; off < SCAN_BLOCK; off <<= 1) {
+    const int32_t add = tid >= off ? buf[tid - off] : 0;
+    __syncthreads();
+    buf[tid] += add;
+    __syncthreads();
+  }
+  if (b >= nbins) return;
+  const int32_t o = bsum[blockIdx.x] + buf[tid] - own;
+  offsets[b] = o;
+  const int64_t ld = nbins + 1;
+  for (int c = 0; c < nchunk; ++c) cc[c * ld + b] += o;
+}
+
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *__restrict__ cc, int nbins, int64_t N,
                                                       const int32_t *__restrict__ s_key,
                                                       const int32_t *__restrict__ s_idx,
@@ -179,7 +261,15 @@ hipError_t launch_counting_sort(const int32_t *keys, const int32_t *aux, int64_t
   if (N > 0)
     sort_chunks_kernel<<<(unsigned)nchunk, SORT_THREADS, 0, st>>>(keys, aux, aux_bound, N, (int)nbins, cc,
                                                                   s_key, s_idx, s_rank);
-  scan_counts_kernel<<<1, 1024, 0, st>>>(cc, (int)nchunk, (int)nbins, offsets);
+  if (nbins <= SINGLE_SCAN_BINS) {
+    scan_counts_kernel<<<1, 1024, 0, st>>>(cc, (int)nchunk, (int)nbins, offsets);
+  } else {
+    int32_t *bsum = s_rank + nchunk * CH;
+    const unsigned nb = (unsigned)cdiv(nbins, SCAN_BLOCK);
+    scan_bins_pass1<<<nb, SCAN_BLOCK, 0, st>>>(cc, (int)nchunk, (int)nbins, offsets, bsum);
+    scan_bins_pass2<<<1, 1024, 0, st>>>(bsum, (int)nb, (int)nbins, offsets);
+    scan_bins_pass3<<<nb, SCAN_BLOCK, 0, st>>>(cc, (int)nchunk, (int)nbins, offsets, bsum);
+  }
   if (N > 0)
     scatter_kernel<<<(unsigned)cdiv(N, 256), 256, 0, st>>>(cc, (int)nbins, N, s_key, s_idx, s_rank, perm_src,
                                                           perm_pos);

@@ -335,3 +335,23 @@ def test_forward_token_order_equivariance():
     y, ids, _ = run_forward(lt, x)
     yp, idsp, _ = run_forward(lt, x[perm].contiguous())
     assert torch.equal(yp, y[perm]) and torch.equal(idsp, ids[perm])
+
+
+def test_combine_many_tokens_uses_multiblock_scan():
+    """More token bins than one workgroup scans (T > 4096): per-token order and sums."""
+    rng = np.random.default_rng(21)
+    T, H, N = 6000, 128, 9001
+    d = dev()
+    yp = rng.standard_normal((N, H)).astype(np.float32)
+    pos = rng.permutation(N).astype(np.int32)
+    tok = rng.integers(0, T, size=N).astype(np.int32)
+    tok[rng.choice(N, 7, replace=False)] = T + 1
+    gates = rng.random(N).astype(np.float32)
+    layer = B.Layer(H, 128, 8, 0, B.MOE_BF16, None, None)
+    y = torch.empty((T, H), dtype=torch.float32, device=d)
+    B.moe_combine(layer, torch.from_numpy(yp).to(d), B.MOE_F32, torch.from_numpy(pos).to(d),
+                  torch.from_numpy(tok).to(d), torch.from_numpy(gates).to(d), N, None, 0, T, y, B.MOE_F32,
+                  ws=B.workspace(layer, T, N, d))
+    torch.cuda.synchronize()
+    y_ref = oracle.combine(yp.astype(np.float64), pos, gates, T, tok=tok)
+    assert rel_err_rows(to_np(y), y_ref).max() < 1e-6
