@@ -39,7 +39,52 @@ def parse():
     ap.add_argument("--workload", default="decode_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run plain 1 GiB device copies only (reference dispatches for the HBM byte counters)")
     return ap.parse_args()
+
+
+# HBM traffic of the dominant kernel, from two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE,
+# KiB per dispatch) over this command, each scaled by what the same counter reads for a plain
+# 1 GiB device copy (bench.py --copy-calibration).  Valid only for the kernel sources they were
+# taken on: a different hash of the library sources reports null.
+TRAFFIC = {
+    "decode_bf16": {"src_hash": "8758114636e1f920", "fetch_kib": 3309000.0, "write_kib": 1886.0, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_fp8": {"src_hash": "8758114636e1f920", "fetch_kib": 1667000.0, "write_kib": 1193.0, "fetch_scale": 2.0, "write_scale": 1.0},
+    "prefill_fp8": {"src_hash": "8758114636e1f920", "fetch_kib": 4177000.0, "write_kib": 132100.0, "fetch_scale": 2.0, "write_scale": 1.0},
+}
+
+
+def library_source_hash():
+    import hashlib
+    d = os.path.join(ROOT, "router_gemm_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration():
+    """Plain device copies of a known size: 3 x copy_ and 3 x neg over 1 GiB."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(3):
+        dst.copy_(src)
+    ev1.record()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / 3
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                      "launches": {"copy_": 3, "neg": 3}, "copy_ms": round(ms, 4),
+                      "copy_GBps": round(2 * n / (ms / 1e3) / 1e9, 1)}), flush=True)
 
 
 def main():
@@ -48,6 +93,9 @@ def main():
         print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import numpy as np
     import torch
 
@@ -164,10 +212,21 @@ def main():
         roof = {"bound": "mfma", "achieved": round((f8 + f16) / (gu_ms / 1e3) / 1e12, 1), "peak": round(peak, 1),
                 "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    tr = TRAFFIC.get(cfg.name)
+    src_hash = library_source_hash()
+    launches = max(gu_launches // K, 1)
+    if tr and tr["src_hash"] == src_hash:
+        roof["traffic"] = int((tr["fetch_kib"] * tr["fetch_scale"] + tr["write_kib"] * tr["write_scale"]) * 1024)
+        roof["traffic_per"] = "launch"
+    else:
+        roof["traffic"] = None
+        roof["traffic_note"] = ("no counters taken on these kernel sources" if not tr
+                                else "kernel sources changed since the counters were taken")
+    roof["library_source_hash"] = src_hash
     roof["kernel"] = "grouped gate/up + SwiGLU (routed and shared experts)"
     roof["kernel_ms_per_step"] = round(gu_ms, 4)
-    roof["launches_per_step"] = gu_launches // K
+    roof["launches_per_step"] = launches
+    roof["avg_launch_us"] = round(1e3 * gu_ms / launches, 2)
     roof["algorithmic_bytes_per_step"] = int(gu_bytes)
     roof["algorithmic_flops_per_step"] = gu_f_routed + gu_f_shared
 
