@@ -37,7 +37,7 @@ __device__ __forceinline__ FfnGroup pick_group(const FfnGroup &g0, const FfnGrou
 // tiles of bm rows per expert, in expert order.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(FfnGroup g0, FfnGroup g1, int ngroups, int bm,
                                                            int max_tiles, TileEntry *__restrict__ tiles,
-                                                           int32_t *__restrict__ ntiles) {
+                                                           int32_t *__restrict__ hdr) {
   __shared__ int32_t buf[1024];
   const int tid = threadIdx.x;
   int base0 = 0;
@@ -63,8 +63,9 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(FfnGroup g0, FfnGroup
     for (int j = 0; j < cnt; ++j)
       if (base + j < max_tiles) tiles[base + j] = TileEntry{(g << 24) | tid, j * bm};
     base0 += buf[1023];
+    if (g == 0 && tid == 0) hdr[1] = min(base0, max_tiles);
   }
-  if (tid == 0) *ntiles = min(base0, max_tiles);
+  if (tid == 0) hdr[0] = min(base0, max_tiles);
 }
 
 // Operand fragment of one lane for one 128-byte K chunk: 32 bytes.
@@ -359,7 +360,9 @@ FfnPlan ffn_plan(const FfnGroup *g, int ngroups) {
   return p;
 }
 
-size_t ffn_tiles_bytes(const FfnPlan &p) { return align_up(sizeof(TileEntry) * (size_t)p.max_tiles + 256, 256); }
+size_t ffn_tiles_bytes(const FfnPlan &p) {
+  return align_up(sizeof(TileEntry) * (size_t)p.max_tiles + kTileHdrWords * sizeof(int32_t), 256);
+}
 
 template <int MT>
 static void run_stream(const StreamArgs &a, const FfnPlan &plan, int maxI, int site, hipStream_t st) {
@@ -389,13 +392,13 @@ hipError_t launch_expert_ffn(const FfnGroup *g, int ngroups, int H, const FfnPla
     if (g[i].fp8 && plan.gw != 2) return hipErrorInvalidValue;
   }
   if (rows == 0) return hipSuccess;
-  int32_t *ntiles = tiles_ws;
-  TileEntry *tiles = reinterpret_cast<TileEntry *>(tiles_ws + 64);
-  StreamArgs a{g[0], ngroups > 1 ? g[1] : g[0], tiles, ntiles, H};
-  build_tiles_kernel<<<1, 1024, 0, st>>>(a.g0, a.g1, ngroups, plan.bm, plan.max_tiles, tiles, ntiles);
+  int32_t *hdr = tiles_ws;
+  TileEntry *tiles = reinterpret_cast<TileEntry *>(tiles_ws + kTileHdrWords);
+  StreamArgs a{g[0], ngroups > 1 ? g[1] : g[0], tiles, hdr, H};
+  build_tiles_kernel<<<1, 1024, 0, st>>>(a.g0, a.g1, ngroups, plan.bm, plan.max_tiles, tiles, hdr);
   if (plan.tiled) {
     if (H % 256 != 0) return hipErrorInvalidValue;
-    return launch_tiled_ffn(g, ngroups, H, tiles, ntiles, num_compute_units(), site, st);
+    return launch_tiled_ffn(g, ngroups, H, tiles, hdr, num_compute_units(), site, st);
   }
   switch (plan.mt) {
     case 1: run_stream<1>(a, plan, maxI, site, st); break;

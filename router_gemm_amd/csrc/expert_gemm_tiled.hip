@@ -17,8 +17,11 @@
 //   - LDS rows are 128 bytes with the 16-byte column XOR-swizzled by row % 8,
 //     so the MFMA operand reads (8 lanes = 8 consecutive rows) hit distinct banks;
 //   - the grid is one workgroup per CU; work items (tile-list slot x column
-//     tile) are split into 8 contiguous ranges, one per XCD (workgroup i runs
-//     on XCD i % 8), so the column tiles of one token tile share that XCD's L2.
+//     tile) are split into 8 contiguous ranges of equal cost, one per XCD
+//     (workgroup i runs on XCD i % 8); inside a range, items come in bands of
+//     up to 8 token tiles of one expert, column-tile-major, so that the
+//     workgroups of an XCD that run at the same time share weight and token
+//     tiles in its L2.
 
 #include <algorithm>
 
@@ -37,12 +40,15 @@ constexpr int TSTAGE = TW + TX + TSX;       // bytes per LDS stage
 constexpr int NSTAGE = 3;
 constexpr int TTHREADS = 256;
 
+constexpr int TBAND = 8;      // token tiles of one expert whose items are interleaved
+
 struct TiledArgs {
   FfnGroup g0, g1;
   const TileEntry *tiles;
-  const int32_t *ntiles;
+  const int32_t *hdr;     // [0] tile count, [1] tiles of group 0
   int H;
-  int nt;        // column tiles per tile-list slot (largest over the groups)
+  int nt;                 // column tiles per tile-list slot (largest over the groups)
+  int c0, c1;             // K chunks of one item of group 0 / group 1 (its cost)
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -406,24 +412,58 @@ __device__ __forceinline__ void tiled_item(const FfnGroup &G, const TileEntry &t
   __syncthreads();   // the next work item reuses the LDS ring and the reduction area
 }
 
+// Work item L -> (tile-list slot, column tile).  The slots of one expert are
+// taken in bands of up to TBAND token tiles, and the items of a band are
+// ordered column-tile-major: the 32 workgroups of an XCD that start
+// consecutive items share about four weight tiles and eight token tiles,
+// instead of one token tile's twelve weight tiles.
+__device__ __forceinline__ void map_item(const TiledArgs &a, int L, int &slot, int &ntile) {
+  const int s = L / a.nt;
+  const TileEntry te = a.tiles[s];
+  const FfnGroup &G = (te.ge >> 24) ? a.g1 : a.g0;
+  const int e = te.ge & 0xFFFFFF;
+  const int r0 = min(max(G.off[e], 0), G.nrows);
+  const int r1 = min(max(G.off[e + 1], r0), G.nrows);
+  const int t = te.m0 / TBM, p = t % TBAND;
+  const int band = min(TBAND, (r1 - r0 + TBM - 1) / TBM - (t - p));
+  const int s0 = s - p, q = L - a.nt * s0;
+  slot = s0 + q % max(band, 1);
+  ntile = q / max(band, 1);
+}
+
+// First item of XCD range x: the ranges split the summed K-chunk cost of the
+// items evenly (a bf16 item of the shared expert streams twice the bytes of
+// an fp8 item), group 0's items first.
+__device__ __forceinline__ int range_start(int x, int64_t n0, int count, int c0, int c1) {
+  const int64_t total = n0 * c0 + (int64_t)(count - n0) * c1;
+  const int64_t C = total * x / 8;
+  const int64_t idx = C <= n0 * c0 ? (C + c0 - 1) / c0 : n0 + (C - n0 * c0 + c1 - 1) / c1;
+  return (int)min<int64_t>(idx, count);
+}
+
 template <bool GATEUP>
 __global__ __launch_bounds__(TTHREADS, 1) void tiled_ffn_kernel(TiledArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   float *red = reinterpret_cast<float *>(lds + NSTAGE * TSTAGE);
   float *wsc = red + 2 * TBM;
-  const int count = a.ntiles[0] * a.nt;
+  const int nslots = a.hdr[0];
+  const int count = nslots * a.nt;
+  const int64_t n0 = (int64_t)min(a.hdr[1], nslots) * a.nt;
   const int xcd = blockIdx.x & 7, per = gridDim.x >> 3, slot0 = blockIdx.x >> 3;
-  const int span = (count + 7) / 8;
-  const int beg = xcd * span, end = min(beg + span, count);
+  const int beg = range_start(xcd, n0, count, a.c0, a.c1), end = range_start(xcd + 1, n0, count, a.c0, a.c1);
   for (int L = beg + slot0; L < end; L += per) {
-    const int slot = L / a.nt, ntile = L % a.nt;
-    const TileEntry te = a.tiles[slot];
-    const FfnGroup G = (te.ge >> 24) ? a.g1 : a.g0;
-    if (GATEUP && ntile * 128 >= G.I) continue;
-    if (G.fp8)
-      tiled_item<true, GATEUP>(G, te, ntile, a.H, lds, red, wsc);
-    else
-      tiled_item<false, GATEUP>(G, te, ntile, a.H, lds, red, wsc);
+    int slot, ntile;
+    map_item(a, L, slot, ntile);
+    if (slot < nslots) {
+      const TileEntry te = a.tiles[slot];
+      const FfnGroup G = (te.ge >> 24) ? a.g1 : a.g0;
+      if (!(GATEUP && ntile * 128 >= G.I)) {
+        if (G.fp8)
+          tiled_item<true, GATEUP>(G, te, ntile, a.H, lds, red, wsc);
+        else
+          tiled_item<false, GATEUP>(G, te, ntile, a.H, lds, red, wsc);
+      }
+    }
   }
 }
 
@@ -442,9 +482,10 @@ int num_compute_units() {
   return cached[dev];
 }
 
-hipError_t launch_tiled_ffn(const FfnGroup *g, int ngroups, int H, const void *tiles, const int32_t *ntiles,
-                            int num_cus, int site, hipStream_t st) {
-  TiledArgs a{g[0], ngroups > 1 ? g[1] : g[0], static_cast<const TileEntry *>(tiles), ntiles, H, 0};
+hipError_t launch_tiled_ffn(const FfnGroup *g, int ngroups, int H, const void *tiles, int32_t *hdr, int num_cus,
+                            int site, hipStream_t st) {
+  TiledArgs a{g[0], ngroups > 1 ? g[1] : g[0], static_cast<const TileEntry *>(tiles), hdr, H, 0, 0, 0};
+  auto chunks = [](const FfnGroup &G, int K) { return std::max(1, K * (G.fp8 ? 1 : 2) / 128); };
   int maxI = 0;
   for (int i = 0; i < ngroups; ++i) maxI = std::max(maxI, (int)g[i].I);
   const unsigned grid = (unsigned)(std::max(num_cus, 8) / 8 * 8);
@@ -462,10 +503,14 @@ hipError_t launch_tiled_ffn(const FfnGroup *g, int ngroups, int H, const void *t
     attr_set[dev] = true;
   }
   a.nt = maxI / 128;
+  a.c0 = chunks(a.g0, H);
+  a.c1 = chunks(a.g1, H);
   timing_before(site, st);
   tiled_ffn_kernel<true><<<grid, TTHREADS, lds, st>>>(a);
   timing_after(site, st);
   a.nt = H / TBN;
+  a.c0 = chunks(a.g0, a.g0.I);
+  a.c1 = chunks(a.g1, a.g1.I);
   timing_before(site + 1, st);
   tiled_ffn_kernel<false><<<grid, TTHREADS, lds, st>>>(a);
   timing_after(site + 1, st);

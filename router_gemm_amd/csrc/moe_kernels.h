@@ -69,11 +69,14 @@ struct FfnPlan {
   int bm;          // token rows per tile-list entry
   int max_tiles;   // capacity of the tile list
 };
+// Tile-list workspace header (int32 words): [0] tile count, [1] tiles of
+// group 0; the tile list follows.
+constexpr int kTileHdrWords = 64;
 FfnPlan ffn_plan(const FfnGroup *g, int ngroups);
 size_t ffn_tiles_bytes(const FfnPlan &p);
 // LDS-tiled variant (expert_gemm_tiled.hip); tiles built with 128-row entries.
-hipError_t launch_tiled_ffn(const FfnGroup *g, int ngroups, int H, const void *tiles, const int32_t *ntiles,
-                            int num_cus, int site, hipStream_t st);
+hipError_t launch_tiled_ffn(const FfnGroup *g, int ngroups, int H, const void *tiles, int32_t *hdr, int num_cus,
+                            int site, hipStream_t st);
 // Compute units of the current device (cached per device).
 int num_compute_units();
 // site: timing site of the gate/up launch (the down launch uses site + 1).
