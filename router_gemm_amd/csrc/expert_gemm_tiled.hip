@@ -51,45 +51,6 @@ struct TiledArgs {
   int c0, c1;             // K chunks of one item of group 0 / group 1 (its cost)
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef const __attribute__((address_space(1))) void gbl_void;
-
-// Copy 16 bytes per lane from global memory to LDS at base + 16 * lane.
-__device__ __forceinline__ void dma16(const void *g, uint8_t *lds_base) {
-  __builtin_amdgcn_global_load_lds((gbl_void *)g, (lds_void *)lds_base, 16, 0, 0);
-}
-// Copy 4 bytes per lane to LDS at base + 4 * lane.
-__device__ __forceinline__ void dma4(const void *g, uint8_t *lds_base) {
-  __builtin_amdgcn_global_load_lds((gbl_void *)g, (lds_void *)lds_base, 4, 0, 0);
-}
-
-// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0], [15:14]).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// s_waitcnt vmcnt(N) lgkmcnt(0).
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
-}
-
-// Workgroup barrier without a memory fence (the direct-to-LDS copies are
-// waited for explicitly with vmcnt); the empty asm keeps the compiler from
-// moving LDS accesses across it.
-__device__ __forceinline__ void wg_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ int swz_f(int row) { return row & 7; }
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ swz_f(row)) << 4); }
-
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 }  // namespace
 
 // One work item: a 256 x 128 output tile (gate/up: 128 gate + the matching 128

@@ -91,5 +91,50 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ i32x4 load16(const void *p) { return *reinterpret_cast<const i32x4 *>(p); }
 __device__ __forceinline__ void store16(void *p, const i32x4 &v) { *reinterpret_cast<i32x4 *>(p) = v; }
 
+// ---------------------------------------------------------------- LDS staging
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
+
+// Copy 16 bytes per lane from global memory to LDS at base + 16 * lane.
+__device__ __forceinline__ void dma16(const void *g, uint8_t *lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void *)g, (lds_void *)lds_base, 16, 0, 0);
+}
+// Copy 4 bytes per lane to LDS at base + 4 * lane.
+__device__ __forceinline__ void dma4(const void *g, uint8_t *lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void *)g, (lds_void *)lds_base, 4, 0, 0);
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0], [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+// Workgroup barrier without a memory fence (the direct-to-LDS copies are
+// waited for explicitly with vmcnt); the empty asm keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// LDS rows of 128 bytes with the 16-byte column XOR-swizzled by row % 8, so
+// that MFMA operand reads of 8 consecutive rows hit distinct banks.
+__device__ __forceinline__ int swz_f(int row) { return row & 7; }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ swz_f(row)) << 4); }
+
+// A value the compiler may keep in a scalar register (uniform across the wave).
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 
 }  // namespace moe

@@ -43,6 +43,26 @@ def test_route_matches_oracle(name):
     assert np.abs(gates.cpu().numpy()[same] - g_ref[same]).max() < 2e-6
 
 
+def test_route_many_tokens_tiled_path():
+    """T >= 2048 takes the LDS-tiled logits kernel: ragged T (not a multiple of
+    the 64-token tile) and E = 352 (not a multiple of the 192-expert tile);
+    every token's ids, gates and logits against the oracle."""
+    cfg = W.get_config("c0", T=2085, E=352, k=8, I=64, Is=0)
+    lt = W.make_layer(cfg, dev())
+    x = W.make_x(cfg, dev())
+    layer = B.Layer.from_tensors(lt)
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev())
+    gates = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev())
+    logits = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev())
+    B.moe_route(layer, x, cfg.T, ids, gates, logits, ws=B.workspace(layer, cfg.T, cfg.N, dev()))
+    torch.cuda.synchronize()
+    OL = oracle_layer(lt)
+    ids_ref, g_ref, gap, l_ref = oracle.route(OL, W.bf16_bits(x), want_logits=True)
+    same = check_ids(ids.cpu().numpy(), ids_ref, gap)
+    np.testing.assert_allclose(logits.cpu().numpy(), l_ref, rtol=0, atol=2e-5)
+    assert np.abs(gates.cpu().numpy()[same] - g_ref[same]).max() < 2e-6
+
+
 def _route_with(wr, x, k, bias=None):
     E, H = wr.shape
     I = 64
