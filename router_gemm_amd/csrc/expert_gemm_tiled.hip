@@ -82,8 +82,9 @@ struct TiledItem {
     KB = K / 128;
     col0 = GATEUP ? ntile * 128 : ntile * TBN;
     wsrc = GATEUP ? G.wgu + (int64_t)e * 2 * I * rowb : G.wd + (int64_t)e * H * rowb;
-    asrc = (GATEUP ? G.x : G.h) + (int64_t)rbeg * rowb;
-    ascale = (GATEUP ? G.xs : G.hs) + (FP8 ? (int64_t)rbeg * KB : 0);
+    const bool indirect = GATEUP && G.xsrc != nullptr;
+    asrc = (GATEUP ? G.x : G.h) + (indirect ? 0 : (int64_t)rbeg * rowb);
+    ascale = (GATEUP ? G.xs : G.hs) + (FP8 && !indirect ? (int64_t)rbeg * KB : 0);
     const int sub = lane >> 3;   // row within an 8-row group
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -96,9 +97,16 @@ struct TiledItem {
     for (int q = 0; q < 4; ++q) {
       const int r = 8 * (w + 4 * q) + sub;
       const int c = (lane & 7) ^ swz_f(r);
-      xoff[q] = (uint32_t)(min(r, nvalid - 1) * rowb + c * 16);   // rows past the end repeat a valid row
+      // rows past the end repeat a valid row; indirect rows come from x row xsrc[row] / xdiv
+      const int rr = min(r, nvalid - 1);
+      const int64_t src = indirect ? G.xsrc[rbeg + rr] / G.xdiv : rr;
+      xoff[q] = (uint32_t)(src * rowb + c * 16);
     }
-    soff = (uint32_t)(min(32 * w + (lane & 31), nvalid - 1) * KB * 4);
+    {
+      const int rr = min(32 * w + (lane & 31), nvalid - 1);
+      const int64_t src = indirect ? G.xsrc[rbeg + rr] / G.xdiv : rr;
+      soff = (uint32_t)(src * KB * 4);
+    }
   }
 
   // Issue the direct-to-LDS copies of K chunk kc into stage buffer sb:

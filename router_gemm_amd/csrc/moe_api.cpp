@@ -422,9 +422,24 @@ moe_status moe_forward(const moe_layer *L, const void *x, int64_t T, void *y, in
   if (e != hipSuccess) return hip_status(e, "moe_forward: route");
   e = moe::launch_counting_sort(ids, nullptr, 0, N, E, f.offsets, f.perm_src, f.perm_pos, f.sort, st);
   if (e != hipSuccess) return hip_status(e, "moe_forward: sort");
-  e = moe::launch_gather_rows(static_cast<const uint16_t *>(x), H, f.perm_src, nullptr, L->top_k, N, f.offsets + E,
-                              is_fp8(L), f.x_perm, f.x_scale, st);
-  if (e != hipSuccess) return hip_status(e, "moe_forward: gather");
+  // LDS-tiled expert kernels read the routed rows through the sort permutation
+  // (x quantised once per token for fp8 experts) instead of a gathered copy;
+  // their per-lane row offsets are 32-bit.
+  moe::FfnGroup &R = f.groups[f.ngroups - 1];
+  if (f.ffn.plan.tiled && T * H * (int64_t)esz(L) < (int64_t(1) << 31)) {
+    R.xsrc = f.perm_src;
+    R.xdiv = L->top_k;
+    if (is_fp8(L)) {
+      e = moe::launch_quantize_rows(static_cast<const uint16_t *>(x), H, T, f.x_perm, f.x_scale, st);
+      if (e != hipSuccess) return hip_status(e, "moe_forward: quantise");
+    } else {
+      R.x = static_cast<const uint8_t *>(x);
+    }
+  } else {
+    e = moe::launch_gather_rows(static_cast<const uint16_t *>(x), H, f.perm_src, nullptr, L->top_k, N, f.offsets + E,
+                                is_fp8(L), f.x_perm, f.x_scale, st);
+    if (e != hipSuccess) return hip_status(e, "moe_forward: gather");
+  }
   if (L->shared_inter > 0) {
     e = moe::launch_fill_offsets2(f.sh_off, (int32_t)T, st);
     if (e != hipSuccess) return hip_status(e, "moe_forward: shared offsets");

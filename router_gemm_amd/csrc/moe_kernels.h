@@ -35,6 +35,10 @@ hipError_t launch_counting_sort(const int32_t *keys, const int32_t *aux, int64_t
 hipError_t launch_gather_rows(const uint16_t *x, int64_t H, const int32_t *perm_src, const int32_t *tok,
                               int k, int64_t N, const int32_t *offsets_end, bool fp8, void *x_perm,
                               float *x_scale, hipStream_t st);
+// Per-token 1x128 quantisation of x into e4m3 codes and scales (the same
+// arithmetic as the fp8 gather, without the permutation).
+hipError_t launch_quantize_rows(const uint16_t *x, int64_t H, int64_t T, uint8_t *xq, float *x_scale,
+                                hipStream_t st);
 // Writes {0, n} into dst[0..1] (device).
 hipError_t launch_fill_offsets2(int32_t *dst, int32_t n, hipStream_t st);
 
@@ -54,6 +58,10 @@ struct FfnGroup {
   float *hs;           // [nrows, I/128] (fp8)
   void *y;             // [nrows, H] output, bf16 or f32
   int32_t E, I, nrows, fp8, y_f32;
+  // Optional (tiled kernels only): row r of the GEMM input is row
+  // xsrc[r] / xdiv of x (and xs), so the rows need not be gathered first.
+  const int32_t *xsrc;
+  int32_t xdiv;
 };
 constexpr int kMaxGroups = 2;
 // Tile list entry: group (0 or 1), expert of that group, first row (relative

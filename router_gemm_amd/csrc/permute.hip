@@ -106,6 +106,36 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_chunks_kernel(
   }
 }
 
+// Column c of bin b: exclusive scan over the chunks in place, returning the
+// bin's total.  Loads go out in batches of 16 so that their latencies overlap
+// (a load of the next chunk may not pass the store of the previous one).
+constexpr int SCAN_BATCH = 16;
+__device__ __forceinline__ int32_t column_exclusive_scan(int32_t *__restrict__ cc, int64_t ld, int b, int nchunk) {
+  int32_t run = 0;
+  for (int c0 = 0; c0 < nchunk; c0 += SCAN_BATCH) {
+    int32_t v[SCAN_BATCH];
+#pragma unroll
+    for (int u = 0; u < SCAN_BATCH; ++u) v[u] = c0 + u < nchunk ? cc[(c0 + u) * ld + b] : 0;
+#pragma unroll
+    for (int u = 0; u < SCAN_BATCH; ++u) {
+      if (c0 + u < nchunk) cc[(c0 + u) * ld + b] = run;
+      run += v[u];
+    }
+  }
+  return run;
+}
+// cc[c][b] += o for every chunk c, in batches of 16 loads.
+__device__ __forceinline__ void column_add(int32_t *__restrict__ cc, int64_t ld, int b, int nchunk, int32_t o) {
+  for (int c0 = 0; c0 < nchunk; c0 += SCAN_BATCH) {
+    int32_t v[SCAN_BATCH];
+#pragma unroll
+    for (int u = 0; u < SCAN_BATCH; ++u) v[u] = c0 + u < nchunk ? cc[(c0 + u) * ld + b] : 0;
+#pragma unroll
+    for (int u = 0; u < SCAN_BATCH; ++u)
+      if (c0 + u < nchunk) cc[(c0 + u) * ld + b] = v[u] + o;
+  }
+}
+
 // One workgroup: bases[c][b] = offsets[b] + sum_{c' < c} counts[c'][b].
 __global__ __launch_bounds__(1024) void scan_counts_kernel(int32_t *__restrict__ cc, int nchunk, int nbins,
                                                            int32_t *__restrict__ offsets) {
@@ -114,15 +144,7 @@ __global__ __launch_bounds__(1024) void scan_counts_kernel(int32_t *__restrict__
   const int tid = threadIdx.x;
   const int64_t ld = nbins + 1;
   // per bin: exclusive scan over chunks; the total goes to offsets[b] for now
-  for (int b = tid; b < nbins; b += 1024) {
-    int32_t run = 0;
-    for (int c = 0; c < nchunk; ++c) {
-      const int32_t x = cc[c * ld + b];
-      cc[c * ld + b] = run;
-      run += x;
-    }
-    offsets[b] = run;
-  }
+  for (int b = tid; b < nbins; b += 1024) offsets[b] = column_exclusive_scan(cc, ld, b, nchunk);
   if (tid == 0) carry = 0;
   __syncthreads();
   // exclusive scan of the totals over bins, 1024 at a time
@@ -145,10 +167,7 @@ __global__ __launch_bounds__(1024) void scan_counts_kernel(int32_t *__restrict__
   }
   if (tid == 0) offsets[nbins] = carry;
   __syncthreads();
-  for (int b = tid; b < nbins; b += 1024) {
-    const int32_t o = offsets[b];
-    for (int c = 0; c < nchunk; ++c) cc[c * ld + b] += o;
-  }
+  for (int b = tid; b < nbins; b += 1024) column_add(cc, ld, b, nchunk, offsets[b]);
 }
 
 // Multi-workgroup variant for many bins (e.g. one bin per token).
@@ -161,11 +180,7 @@ __global__ __launch_bounds__(SCAN_BLOCK) void scan_bins_pass1(int32_t *__restric
   const int64_t ld = nbins + 1;
   int32_t run = 0;
   if (b < nbins) {
-    for (int c = 0; c < nchunk; ++c) {
-      const int32_t x = cc[c * ld + b];
-      cc[c * ld + b] = run;
-      run += x;
-    }
+    run = column_exclusive_scan(cc, ld, b, nchunk);
     offsets[b] = run;
   }
   red[threadIdx.x] = run;
@@ -225,8 +240,7 @@ __global__ __launch_bounds__(SCAN_BLOCK) void scan_bins_pass3(int32_t *__restric
   if (b >= nbins) return;
   const int32_t o = bsum[blockIdx.x] + buf[tid] - own;
   offsets[b] = o;
-  const int64_t ld = nbins + 1;
-  for (int c = 0; c < nchunk; ++c) cc[c * ld + b] += o;
+  column_add(cc, nbins + 1, b, nchunk, o);
 }
 
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *__restrict__ cc, int nbins, int64_t N,
@@ -291,8 +305,8 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t *__rest
                                                           float *__restrict__ x_scale) {
   const int lane = lane_id();
   const int64_t p = (int64_t)blockIdx.x * 4 + wave_id();
-  if (p >= N || p >= offsets_end[0]) return;
-  const int32_t i = perm_src[p];
+  if (p >= N || (offsets_end && p >= offsets_end[0])) return;
+  const int64_t i = perm_src ? perm_src[p] : p;   // no permutation: quantise rows in place order
   const int64_t t = tok ? tok[i] : i / k;
   const uint16_t *src = x + t * H;
   if constexpr (!FP8) {
@@ -332,6 +346,16 @@ hipError_t launch_gather_rows(const uint16_t *x, int64_t H, const int32_t *perm_
     gather_rows_kernel<true><<<g, 256, 0, st>>>(x, (int)H, perm_src, tok, k, N, offsets_end, x_perm, x_scale);
   else
     gather_rows_kernel<false><<<g, 256, 0, st>>>(x, (int)H, perm_src, tok, k, N, offsets_end, x_perm, x_scale);
+  timing_after(3, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows(const uint16_t *x, int64_t H, int64_t T, uint8_t *xq, float *x_scale,
+                                hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  const unsigned g = (unsigned)cdiv(T, 4);
+  timing_before(3, st);
+  gather_rows_kernel<true><<<g, 256, 0, st>>>(x, (int)H, nullptr, nullptr, 1, T, nullptr, xq, x_scale);
   timing_after(3, st);
   return hipGetLastError();
 }

@@ -307,6 +307,19 @@ def test_forward_small_full_parity(name):
     _print(f"forward {name}: {st}")
 
 
+@pytest.mark.parametrize("name,over", [("c0", dict(T=517, I=128, Is=128)), ("small_fp8", dict(T=389))])
+def test_forward_tiled_path_reads_rows_through_permutation(name, over):
+    """Enough rows per expert (mean >= 48) for the LDS-tiled kernels, which read
+    the routed rows through the sort permutation (bf16 x directly, fp8 x
+    quantised once per token) instead of a gathered copy; ragged T."""
+    cfg = W.get_config(name, **over)
+    assert cfg.N / cfg.E >= 48 and cfg.I % 128 == 0 and cfg.Is % 128 == 0
+    lt = W.make_layer(cfg, dev())
+    x = W.make_x(cfg, dev())
+    st = check_forward(lt, x)
+    _print(f"forward tiled {name} {over}: {st}")
+
+
 def test_forward_ragged_and_single_token():
     cfg = W.get_config("small_fp8")
     lt = W.make_layer(cfg, dev())
