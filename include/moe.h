@@ -69,7 +69,8 @@ typedef enum moe_status {
   MOE_EINVAL = 1,        /* NULL pointer where one is required, bad size or dimension,
                             k outside [1, min(E, 32)], misaligned pointer */
   MOE_EUNSUPPORTED = 2,  /* valid but not built: H % 128 != 0; bf16 experts with I % 64 != 0;
-                            fp8 experts with I % 128 != 0; E > 1024; H > 16384;
+                            fp8 experts with I % 128 != 0; E > 1024; H, I or the
+                            shared expert's I > 16384;
                             unsupported dtype combination */
   MOE_EWORKSPACE = 3,    /* ws_bytes smaller than the call needs */
   MOE_EHIP = 4           /* a HIP launch failed; moe_last_error() has the detail */

@@ -36,7 +36,10 @@ moe_status hip_status(hipError_t e, const char *what) {
 constexpr size_t kAlign = 256;
 constexpr int kMaxK = 32;
 constexpr int kMaxE = 1024;
-constexpr int kMaxH = 65536;
+// The expert kernels stage 2 x K/128 weight-block scales per work item in
+// LDS, sized for K <= 16384 (K = H for gate/up, I or shared I for down).
+constexpr int kMaxH = 16384;
+constexpr int kMaxI = 16384;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -68,6 +71,8 @@ moe_status check_layer_shape(const moe_layer *L, bool need_router) {
   if (L->hidden % 128 != 0 || L->hidden > kMaxH)
     return fail(MOE_EUNSUPPORTED, "hidden %d must be a multiple of 128 and <= %d", L->hidden, kMaxH);
   if (L->num_experts > kMaxE) return fail(MOE_EUNSUPPORTED, "num_experts %d > %d", L->num_experts, kMaxE);
+  if (L->inter > kMaxI || L->shared_inter > kMaxI)
+    return fail(MOE_EUNSUPPORTED, "inter %d / shared_inter %d > %d", L->inter, L->shared_inter, kMaxI);
   if (is_fp8(L) && L->inter % 128 != 0)
     return fail(MOE_EUNSUPPORTED, "fp8 experts need inter %% 128 == 0 (inter=%d)", L->inter);
   if (!is_fp8(L) && L->inter % 64 != 0)

@@ -52,6 +52,8 @@ def test_status_strings():
     (dict(I=1568, dtype=B.MOE_BF16), B.MOE_EUNSUPPORTED),
     (dict(dtype=7), B.MOE_EUNSUPPORTED), (dict(Is=100), B.MOE_EUNSUPPORTED),
     (dict(H=0), B.MOE_EINVAL), (dict(E=-1), B.MOE_EINVAL),
+    (dict(H=16384 + 128), B.MOE_EUNSUPPORTED), (dict(I=16384 + 128), B.MOE_EUNSUPPORTED),
+    (dict(Is=16384 + 64), B.MOE_EUNSUPPORTED), (dict(H=16384, I=16384, Is=16384), B.MOE_OK),
 ])
 def test_layer_validation(kw, status):
     L = layer(**kw)
