@@ -35,14 +35,13 @@ size_t sort_ws_words(int64_t N, int64_t nbins) {
   return (size_t)(nchunk * (nbins + 1) + 3 * nchunk * CH + cdiv(nbins, SCAN_BLOCK) + 1);
 }
 
-__global__ __launch_bounds__(SORT_THREADS) void sort_chunks_kernel(
-    const int32_t *__restrict__ keys, const int32_t *__restrict__ aux, int64_t aux_bound, int64_t N,
-    int nbins, int32_t *__restrict__ chunk_counts, int32_t *__restrict__ s_key,
-    int32_t *__restrict__ s_idx, int32_t *__restrict__ s_rank) {
-  __shared__ uint64_t sk[CH];
-  __shared__ int32_t start[CH];
+// Sort chunk `chunk` of the keys in LDS: sk[j] = (bin << 32 | i) ascending
+// (bin nbins = dropped), start[j] = first position of sk[j]'s bin in the chunk.
+__device__ __forceinline__ void sort_chunk_lds(const int32_t *__restrict__ keys, const int32_t *__restrict__ aux,
+                                               int64_t aux_bound, int64_t N, int nbins, int64_t chunk,
+                                               uint64_t *sk, int32_t *start) {
   const int tid = threadIdx.x;
-  const int64_t base = (int64_t)blockIdx.x * CH;
+  const int64_t base = chunk * CH;
   for (int j = tid; j < CH; j += SORT_THREADS) {
     const int64_t i = base + j;
     uint64_t v = ~0ull;  // padding sorts last
@@ -58,8 +57,6 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_chunks_kernel(
     }
     sk[j] = v;
   }
-  int32_t *row = chunk_counts + (int64_t)blockIdx.x * (nbins + 1);
-  for (int b = tid; b <= nbins; b += SORT_THREADS) row[b] = 0;
   __syncthreads();
   // bitonic sort, ascending
   for (int size = 2; size <= CH; size <<= 1) {
@@ -93,6 +90,19 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_chunks_kernel(
     for (int q = 0; q < CH / SORT_THREADS; ++q) start[tid + q * SORT_THREADS] = vals[q];
     __syncthreads();
   }
+}
+
+__global__ __launch_bounds__(SORT_THREADS) void sort_chunks_kernel(
+    const int32_t *__restrict__ keys, const int32_t *__restrict__ aux, int64_t aux_bound, int64_t N,
+    int nbins, int32_t *__restrict__ chunk_counts, int32_t *__restrict__ s_key,
+    int32_t *__restrict__ s_idx, int32_t *__restrict__ s_rank) {
+  __shared__ uint64_t sk[CH];
+  __shared__ int32_t start[CH];
+  const int tid = threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * CH;
+  int32_t *row = chunk_counts + (int64_t)blockIdx.x * (nbins + 1);
+  for (int b = tid; b <= nbins; b += SORT_THREADS) row[b] = 0;
+  sort_chunk_lds(keys, aux, aux_bound, N, nbins, blockIdx.x, sk, start);
   const int64_t nreal = min((int64_t)CH, N - base);
   for (int j = tid; j < nreal; j += SORT_THREADS) {
     const uint64_t v = sk[j];
@@ -263,6 +273,63 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *__restrict_
   if (perm_pos) perm_pos[i] = pos;
 }
 
+// The whole sort in one workgroup when every key fits one chunk (N <= 512,
+// e.g. a decode step) and the bins fit LDS: chunk sort, bin counts, their
+// exclusive scan and the scatter, with the same results as the general path.
+constexpr int ONE_CHUNK_BINS = 4096;
+__global__ __launch_bounds__(SORT_THREADS) void sort_one_chunk_kernel(
+    const int32_t *__restrict__ keys, const int32_t *__restrict__ aux, int64_t aux_bound, int64_t N, int nbins,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ perm_src, int32_t *__restrict__ perm_pos) {
+  __shared__ uint64_t sk[CH];
+  __shared__ int32_t start[CH];
+  __shared__ int32_t off[ONE_CHUNK_BINS + 1];
+  __shared__ int32_t part[SORT_THREADS];
+  const int tid = threadIdx.x;
+  for (int b = tid; b <= nbins; b += SORT_THREADS) off[b] = 0;
+  sort_chunk_lds(keys, aux, aux_bound, N, nbins, 0, sk, start);
+  const int nreal = (int)min((int64_t)CH, N);
+  for (int j = tid; j < nreal; j += SORT_THREADS) {
+    const uint32_t key = (uint32_t)(sk[j] >> 32);
+    const bool last = (j == nreal - 1) || ((uint32_t)(sk[j + 1] >> 32) != key);
+    if (last) off[key] = j - start[j] + 1;   // count of the bin (the dropped bin nbins included)
+  }
+  __syncthreads();
+  // exclusive scan of off[0 .. nbins-1]: thread t sums bins [per*t, per*t + per)
+  const int per = (nbins + SORT_THREADS - 1) / SORT_THREADS;
+  const int b0 = min(tid * per, nbins), b1 = min(b0 + per, nbins);
+  int32_t sum = 0;
+  for (int b = b0; b < b1; ++b) sum += off[b];
+  part[tid] = sum;
+  __syncthreads();
+  for (int o = 1; o < SORT_THREADS; o <<= 1) {
+    const int32_t add = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  int32_t run = part[tid] - sum;
+  for (int b = b0; b < b1; ++b) {
+    const int32_t c = off[b];
+    off[b] = run;
+    offsets[b] = run;
+    run += c;
+  }
+  if (tid == SORT_THREADS - 1) offsets[nbins] = part[SORT_THREADS - 1];
+  __syncthreads();
+  for (int j = tid; j < nreal; j += SORT_THREADS) {
+    const uint64_t v = sk[j];
+    const int32_t key = (int32_t)(v >> 32);
+    const int32_t i = (int32_t)(uint32_t)v;
+    if (key >= nbins) {
+      if (perm_pos) perm_pos[i] = -1;
+      continue;
+    }
+    const int32_t pos = off[key] + (j - start[j]);
+    if (perm_src) perm_src[pos] = i;
+    if (perm_pos) perm_pos[i] = pos;
+  }
+}
+
 hipError_t launch_counting_sort(const int32_t *keys, const int32_t *aux, int64_t aux_bound, int64_t N,
                                 int64_t nbins, int32_t *offsets, int32_t *perm_src, int32_t *perm_pos,
                                 int32_t *ws, hipStream_t st) {
@@ -272,6 +339,12 @@ hipError_t launch_counting_sort(const int32_t *keys, const int32_t *aux, int64_t
   int32_t *s_idx = s_key + nchunk * CH;
   int32_t *s_rank = s_idx + nchunk * CH;
   timing_before(2, st);
+  if (N <= CH && nbins <= ONE_CHUNK_BINS) {
+    sort_one_chunk_kernel<<<1, SORT_THREADS, 0, st>>>(keys, aux, aux_bound, N, (int)nbins, offsets, perm_src,
+                                                     perm_pos);
+    timing_after(2, st);
+    return hipGetLastError();
+  }
   if (N > 0)
     sort_chunks_kernel<<<(unsigned)nchunk, SORT_THREADS, 0, st>>>(keys, aux, aux_bound, N, (int)nbins, cc,
                                                                   s_key, s_idx, s_rank);

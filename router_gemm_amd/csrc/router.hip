@@ -164,15 +164,23 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
   float v[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) v[j] = 0.f;
-  // partial sums added in split order s = 0..S-1 (loads of one split are independent)
-  for (int s = 0; s < S; ++s) {
-    const float *p = partial + ((int64_t)s * T + t) * E;
+  // partial sums added in split order s = 0..S-1 (S <= 8); every split's
+  // values are loaded before the first add, so the loads overlap
+  float pv[8][NJ];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const float *p = partial + ((int64_t)(s < S ? s : 0) * T + t) * E;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int e = lane + 64 * j;
-      if (e < E) v[j] += p[e];
+      pv[s][j] = (s < S && e < E) ? p[e] : 0.f;
     }
   }
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      if (s < S) v[j] += pv[s][j];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int e = lane + 64 * j;

@@ -163,6 +163,7 @@ def _permute(cfg_name, N, T, k, E, with_tokens, invalid, fp8, seed=0):
     (1000, 250, 4, 32, False, False, False),
     (1000, 250, 4, 32, False, False, True),
     (513, 400, 0, 44, True, True, True),        # ragged, pre-routed, dropped entries
+    (512, 300, 0, 44, True, True, True),        # one chunk exactly (one-workgroup sort), dropped entries
     (65536, 8192, 8, 352, False, False, True),  # prefill size
     (1, 1, 1, 5, False, False, True),
     (7, 9, 0, 1000, True, False, False),
