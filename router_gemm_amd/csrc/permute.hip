@@ -382,29 +382,49 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t *__rest
   const int64_t i = perm_src ? perm_src[p] : p;   // no permutation: quantise rows in place order
   const int64_t t = tok ? tok[i] : i / k;
   const uint16_t *src = x + t * H;
+  // row segments of 512 values (8 per lane), four at a time: the loads of a
+  // batch are issued before any of them is used
+  constexpr int BATCH = 4;
   if constexpr (!FP8) {
     uint16_t *dst = reinterpret_cast<uint16_t *>(x_perm) + p * H;
-    for (int c = lane * 8; c < H; c += 512) store16(dst + c, load16(src + c));
+    for (int c0 = lane * 8; c0 < H; c0 += 512 * BATCH) {
+      i32x4 raw[BATCH];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u)
+        if (c0 + 512 * u < H) raw[u] = load16(src + c0 + 512 * u);
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u)
+        if (c0 + 512 * u < H) store16(dst + c0 + 512 * u, raw[u]);
+    }
   } else {
     uint8_t *dst = reinterpret_cast<uint8_t *>(x_perm) + p * H;
-    for (int c = lane * 8; c < H; c += 512) {
-      const i32x4 raw = load16(src + c);
-      float v[8];
+    for (int c0 = lane * 8; c0 < H; c0 += 512 * BATCH) {
+      i32x4 rawb[BATCH];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t wv = (uint32_t)raw[q];
-        v[2 * q] = bf16_to_f32(wv & 0xFFFFu);
-        v[2 * q + 1] = bf16_to_f32(wv >> 16);
+      for (int u = 0; u < BATCH; ++u)
+        if (c0 + 512 * u < H) rawb[u] = load16(src + c0 + 512 * u);
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int c = c0 + 512 * u;
+        if (c >= H) break;
+        const i32x4 raw = rawb[u];
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t wv = (uint32_t)raw[q];
+          v[2 * q] = bf16_to_f32(wv & 0xFFFFu);
+          v[2 * q + 1] = bf16_to_f32(wv >> 16);
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[q]));
+        amax = wave_xor_max(amax, 16);
+        const float s = group_scale(amax);
+        uint32_t lo = f32x4_to_e4m3(__fdiv_rn(v[0], s), __fdiv_rn(v[1], s), __fdiv_rn(v[2], s), __fdiv_rn(v[3], s));
+        uint32_t hi = f32x4_to_e4m3(__fdiv_rn(v[4], s), __fdiv_rn(v[5], s), __fdiv_rn(v[6], s), __fdiv_rn(v[7], s));
+        *reinterpret_cast<uint2 *>(dst + c) = make_uint2(lo, hi);
+        if ((lane & 15) == 0) x_scale[p * (H / 128) + c / 128] = s;
       }
-      float amax = 0.f;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[q]));
-      amax = wave_xor_max(amax, 16);
-      const float s = group_scale(amax);
-      uint32_t lo = f32x4_to_e4m3(__fdiv_rn(v[0], s), __fdiv_rn(v[1], s), __fdiv_rn(v[2], s), __fdiv_rn(v[3], s));
-      uint32_t hi = f32x4_to_e4m3(__fdiv_rn(v[4], s), __fdiv_rn(v[5], s), __fdiv_rn(v[6], s), __fdiv_rn(v[7], s));
-      *reinterpret_cast<uint2 *>(dst + c) = make_uint2(lo, hi);
-      if ((lane & 15) == 0) x_scale[p * (H / 128) + c / 128] = s;
     }
   }
 }
