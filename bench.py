@@ -5,7 +5,7 @@ One step = one pass of the whole layer (router, grouping, routed expert
 gate/up + SwiGLU and down, shared expert, combine) over one batch of
 synthetic tokens already resident in HBM.  Prints one JSON line.
 
-  python bench.py [--workload decode_bf16|decode_fp8|prefill_fp8|ep8_share_fp8|small_bf16]
+  python bench.py [--workload decode_bf16|decode_fp8|prefill_fp8|ep8_share_fp8|dense_ff_bf16|small_bf16]
                   [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 
 The default workload is the bf16 decode layer (T=64 tokens, hidden 4096,
@@ -121,7 +121,16 @@ def main():
     N = cfg.N
     y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
-    if cfg.triples:
+    if cfg.dense:
+        # the dense FF layer: one expert holding every token, rows in token order
+        ws = B.workspace(layer, T, T, dev)
+        off = torch.tensor([0, T], dtype=torch.int32, device=dev)
+
+        def step():
+            B.moe_expert_ffn(layer, off, x, None, T, y, ws=ws)
+
+        counts = np.array([T])
+    elif cfg.triples:
         tok, exp, gate = W.make_triples(cfg)
         tok_g, exp_g, gate_g = (torch.from_numpy(a).to(dev) for a in (tok, exp, gate))
         shared = B.Layer.shared_view(lt)
@@ -181,10 +190,10 @@ def main():
     w_gu_b = 2 * I * H * esz + ((2 * I // 128) * (H // 128) * 4 if fp8 else 0)
     w_d_b = H * I * esz + ((H // 128) * (I // 128) * 4 if fp8 else 0)
     shared_b = 3 * Is * H * 2
-    router_b = 0 if cfg.triples else E * H * 2
+    router_b = 0 if (cfg.triples or cfg.dense) else E * H * 2
     layer_bytes = active * (w_gu_b + w_d_b) + shared_b + router_b + T * H * 2 * 2
     fl_routed = 2.0 * N * 3 * I * H
-    fl_bf16 = 2.0 * T * 3 * Is * H + (0 if cfg.triples else 2.0 * T * E * H)
+    fl_bf16 = 2.0 * T * 3 * Is * H + (0 if (cfg.triples or cfg.dense) else 2.0 * T * E * H)
     if not fp8:
         fl_bf16 += fl_routed
         fl_routed_fp8 = 0.0
@@ -196,7 +205,8 @@ def main():
     # input rows and h output, plus the shared expert's (same launch inside moe_forward; a second
     # moe_expert_ffn launch at the same timing site for the pre-routed workload)
     gu_bytes = active * w_gu_b + N * H * esz + N * I * esz + ((N * H // 128 + N * I // 128) * 4 if fp8 else 0)
-    gu_bytes += 2 * Is * H * 2 + T * H * 2 + T * Is * 2
+    if Is > 0:
+        gu_bytes += 2 * Is * H * 2 + T * H * 2 + T * Is * 2
     gu_f_routed = 2.0 * N * 2 * I * H
     gu_f_shared = 2.0 * T * 2 * Is * H
     gu_ms = gu_ms_total / K                      # per step (all gate/up launches of the step)
@@ -223,7 +233,8 @@ def main():
         roof["traffic_note"] = ("no counters taken on these kernel sources" if not tr
                                 else "kernel sources changed since the counters were taken")
     roof["library_source_hash"] = src_hash
-    roof["kernel"] = "grouped gate/up + SwiGLU (routed and shared experts)"
+    roof["kernel"] = ("gate/up + SwiGLU of the dense FF layer (one expert)" if cfg.dense
+                      else "grouped gate/up + SwiGLU (routed and shared experts)")
     roof["kernel_ms_per_step"] = round(gu_ms, 4)
     roof["launches_per_step"] = launches
     roof["avg_launch_us"] = round(1e3 * gu_ms / launches, 2)

@@ -45,6 +45,7 @@ class MoEConfig:
     zipf_s: float = 0.0    # > 0: router bias skews loads by Zipf(s) ranks
     zipf_beta: float = 0.0 # strength of that bias (see zipf_bias)
     triples: int = 0       # > 0: number of pre-routed (token, expert, gate) triples
+    dense: bool = False    # a dense SwiGLU FF layer: one "expert" applied to every token
     seed: int = 0
     description: str = ""
 
@@ -84,6 +85,11 @@ CONFIGS = {
         router_std=1.0 / 64, zipf_s=1.1, triples=16384,
         description="one rank's EP=8 share: 44 FP8 experts, 16384 pre-routed Zipf(1.1) "
                     "triples, bf16 shared expert on 16384 tokens"),
+    "dense_ff_bf16": MoEConfig(
+        "dense_ff_bf16", T=8192, H=4096, E=1, k=1, I=13824, Is=0, expert_dtype="bf16",
+        router_std=1.0 / 64, dense=True,
+        description="the model's dense SwiGLU FF layers (0-2 and 91): intermediate 13824, bf16, "
+                    "8192 tokens, as one expert through moe_expert_ffn"),
 }
 # Short aliases by position in the workload list.
 ALIASES = {"c0": "small_bf16", "c1": "decode_bf16", "c2": "decode_fp8",
