@@ -284,7 +284,7 @@ def cpu_baseline(cfg, lt, x, target_s):
 
     print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
     h = W.host_layer_arrays(lt)
-    L = oracle.Layer(cfg.H, cfg.I, cfg.E, max(cfg.k, 1), cfg.expert_dtype == "fp8", h["w_router"],
+    L = oracle.Layer(cfg.H, cfg.I, cfg.E, max(cfg.k, 1), cfg.expert_dtype, h["w_router"],
                      h["w_gate_up"], h["w_down"], s_gate_up=h["s_gate_up"], s_down=h["s_down"],
                      router_bias=h["router_bias"], w_shared_gate_up=h["w_shared_gate_up"],
                      w_shared_down=h["w_shared_down"])

@@ -41,7 +41,7 @@ def build() -> str:
 
 class _Layer(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("inter", C.c_int32), ("num_experts", C.c_int32),
-                ("top_k", C.c_int32), ("shared_inter", C.c_int32), ("expert_fp8", C.c_int32),
+                ("top_k", C.c_int32), ("shared_inter", C.c_int32), ("expert_format", C.c_int32),
                 ("w_router", C.c_void_p), ("router_bias", C.c_void_p),
                 ("w_gate_up", C.c_void_p), ("s_gate_up", C.c_void_p),
                 ("w_down", C.c_void_p), ("s_down", C.c_void_p),
@@ -66,6 +66,10 @@ def lib():
         L.oref_e4m3_decode.argtypes = [C.c_uint8]
         L.oref_e4m3_encode.restype = C.c_uint8
         L.oref_e4m3_encode.argtypes = [C.c_float]
+        L.oref_e2m1_decode.restype = C.c_double
+        L.oref_e2m1_decode.argtypes = [C.c_uint8]
+        L.oref_e8m0_decode.restype = C.c_double
+        L.oref_e8m0_decode.argtypes = [C.c_uint8]
         for name, args in {
             "oref_quant_row": [vp, i64, vp, vp],
             "oref_e4m3_encode_array": [vp, i64, vp],
@@ -76,6 +80,7 @@ def lib():
             "oref_expert_row": [vp, i32, vp, vp, vp, vp],
             "oref_expert_gate_up_factored": [vp, i32, vp, vp, vp, vp],
             "oref_expert_gate_up_dequant": [vp, i32, vp, vp, vp, vp],
+            "oref_expert_gate_up_mx_factored": [vp, i32, vp, vp, vp, vp],
             "oref_shared_row": [vp, vp, vp],
             "oref_expert_ffn": [vp, vp, vp, vp, i64, vp],
             "oref_forward": [vp, vp, i64, vp, i64, vp, vp, vp, vp],
@@ -102,27 +107,41 @@ def _c(a, dtype):
     return None if a is None else np.ascontiguousarray(a, dtype=dtype)
 
 
+BF16, FP8, MXFP4 = 0, 1, 2
+_FORMATS = {"bf16": BF16, "fp8": FP8, "mxfp4": MXFP4}
+
+
 class Layer:
     """Host copy of one MoE layer for the oracle (numpy arrays).
 
     w_router uint16 (bf16 bits) [E,H]; router_bias float32 [E] or None;
-    w_gate_up [E,2I,H] and w_down [E,H,I]: uint16 (bf16) or uint8 (e4m3fn);
-    s_gate_up float32 [E,2I/128,H/128], s_down float32 [E,H/128,I/128] (fp8);
+    expert_format: "bf16" / "fp8" / "mxfp4" (or False / True / 2):
+      bf16:  w_gate_up uint16 [E,2I,H], w_down uint16 [E,H,I];
+      fp8:   w_gate_up uint8 (e4m3fn) [E,2I,H], w_down [E,H,I],
+             s_gate_up float32 [E,2I/128,H/128], s_down float32 [E,H/128,I/128];
+      mxfp4: w_gate_up uint8 [E,2I,H/2], w_down uint8 [E,H,I/2] (two E2M1
+             codes per byte, even input in the low nibble),
+             s_gate_up uint8 (E8M0) [E,2I,H/32], s_down uint8 [E,H,I/32];
     w_shared_gate_up uint16 [2Is,H], w_shared_down uint16 [H,Is] or None.
     """
 
-    def __init__(self, hidden, inter, num_experts, top_k, expert_fp8, w_router, w_gate_up,
+    def __init__(self, hidden, inter, num_experts, top_k, expert_format, w_router, w_gate_up,
                  w_down, s_gate_up=None, s_down=None, router_bias=None,
                  w_shared_gate_up=None, w_shared_down=None, shared_inter=None):
         self.H, self.I, self.E, self.k = int(hidden), int(inter), int(num_experts), int(top_k)
-        self.fp8 = bool(expert_fp8)
-        wdt = np.uint8 if self.fp8 else np.uint16
+        fmt = _FORMATS[expert_format] if isinstance(expert_format, str) else int(expert_format)
+        assert fmt in (BF16, FP8, MXFP4)
+        self.format = fmt
+        self.mx = fmt == MXFP4
+        self.fp8 = fmt != BF16          # activations and h stored as e4m3 + 1x128 scales
+        wdt = np.uint16 if fmt == BF16 else np.uint8
+        sdt = np.uint8 if self.mx else np.float32
         self.w_router = _c(w_router, np.uint16)
         self.router_bias = _c(router_bias, np.float32)
         self.w_gate_up = _c(w_gate_up, wdt)
         self.w_down = _c(w_down, wdt)
-        self.s_gate_up = _c(s_gate_up, np.float32)
-        self.s_down = _c(s_down, np.float32)
+        self.s_gate_up = _c(s_gate_up, sdt)
+        self.s_down = _c(s_down, sdt)
         self.w_shared_gate_up = _c(w_shared_gate_up, np.uint16)
         self.w_shared_down = _c(w_shared_down, np.uint16)
         if shared_inter is None:
@@ -131,7 +150,11 @@ class Layer:
         if self.fp8:
             assert self.s_gate_up is not None and self.s_down is not None
             assert self.H % 128 == 0 and self.I % 128 == 0
-        self._s = _Layer(self.H, self.I, self.E, self.k, self.Is, int(self.fp8),
+        if self.mx:
+            E, H, I = self.E, self.H, self.I
+            assert self.w_gate_up.shape == (E, 2 * I, H // 2) and self.w_down.shape == (E, H, I // 2)
+            assert self.s_gate_up.shape == (E, 2 * I, H // 32) and self.s_down.shape == (E, H, I // 32)
+        self._s = _Layer(self.H, self.I, self.E, self.k, self.Is, fmt,
                          _p(self.w_router), _p(self.router_bias), _p(self.w_gate_up),
                          _p(self.s_gate_up), _p(self.w_down), _p(self.s_down),
                          _p(self.w_shared_gate_up), _p(self.w_shared_down))
@@ -166,6 +189,19 @@ def e4m3_encode(v) -> np.ndarray:
     out = np.empty(v.shape, dtype=np.uint8)
     lib().oref_e4m3_encode_array(_p(v), v.size, _p(out))
     return out
+
+
+def e2m1_decode(c) -> np.ndarray:
+    """E2M1 value of the low nibble of each code."""
+    c = np.asarray(c, dtype=np.uint8)
+    table = np.array([lib().oref_e2m1_decode(i) for i in range(16)])
+    return table[c & 0x0F]
+
+
+def e8m0_decode(c) -> np.ndarray:
+    c = np.asarray(c, dtype=np.uint8)
+    table = np.array([lib().oref_e8m0_decode(i) for i in range(256)])
+    return table[c]
 
 
 def quant_row(v):
@@ -247,11 +283,15 @@ def expert_row(layer: Layer, e, a, a_scale=None):
 
 
 def expert_gate_up(layer: Layer, e, a, a_scale, factored: bool):
+    """Gate/up pre-activations (fp8 or mxfp4 layer) -> zg [I], zu [I]."""
     a = np.ascontiguousarray(a, dtype=np.uint8)
     sc = np.ascontiguousarray(a_scale, dtype=np.float32)
     zg = np.empty(layer.I)
     zu = np.empty(layer.I)
-    f = lib().oref_expert_gate_up_factored if factored else lib().oref_expert_gate_up_dequant
+    if factored:
+        f = lib().oref_expert_gate_up_mx_factored if layer.mx else lib().oref_expert_gate_up_factored
+    else:
+        f = lib().oref_expert_gate_up_dequant
     f(layer.ref, int(e), _p(a), _p(sc), _p(zg), _p(zu))
     return zg, zu
 

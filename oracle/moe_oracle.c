@@ -78,6 +78,19 @@ static inline const double *e4m3_tab(void) { return e4m3_table; }
 
 double oref_e4m3_decode(uint8_t c) { return e4m3_tab()[c]; }
 
+/* OCP 4-bit E2M1 (the element type of MX FP4): sign, 2 exponent bits (bias
+ * 1), 1 mantissa bit; exponent field 0 is subnormal (m * 2^-1); no NaN or
+ * infinity; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.  Only the low nibble of c
+ * is read. */
+double oref_e2m1_decode(uint8_t c) {
+  int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+  double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return s ? -v : v;
+}
+
+/* OCP E8M0 scale: an unsigned biased exponent, 2^(e - 127); 0xFF is NaN. */
+double oref_e8m0_decode(uint8_t e) { return e == 0xFF ? NAN : ldexp(1.0, (int)e - 127); }
+
 /* Round a binary32 value to E4M3: nearest representable value, ties to the
  * even mantissa; magnitudes beyond 448 saturate to 448.  Arithmetic in double
  * is exact here (a power-of-two rescale of a binary32). */
@@ -268,16 +281,40 @@ int64_t oref_permute(const int32_t *key, int64_t N, int32_t E,
 /* Expert FFN                                                                */
 /* ------------------------------------------------------------------------ */
 
-/* Dequantised weight element (row n, column c) of a [R, C] matrix of expert
- * e; fp8: code * scale[n/128][c/128]. */
-static inline double w_elem(int fp8, const void *w, const float *s, int64_t base,
+/* Dequantised weight element (row n, column c) of the [R, C] matrix of one
+ * expert whose weights start at element (fp8: byte) base and whose scales
+ * start at scale index sbase:
+ *   bf16:  the bf16 value;
+ *   fp8:   code * scale[n/128][c/128];
+ *   mxfp4: e2m1(nibble c of row n) * 2^(scale[n][c/32] - 127), row n being
+ *          C/2 bytes with input c in the low nibble of byte c/2 when c is even. */
+static inline double w_elem(int fmt, const void *w, const void *s, int64_t base,
                             int64_t sbase, int64_t C, int64_t n, int64_t c) {
-  if (fp8) {
+  if (fmt == OREF_FP8) {
     const uint8_t *q = (const uint8_t *)w;
-    return e4m3_tab()[q[base + n * C + c]] * (double)s[sbase + (n / 128) * (C / 128) + c / 128];
+    const float *sf = (const float *)s;
+    return e4m3_tab()[q[base + n * C + c]] * (double)sf[sbase + (n / 128) * (C / 128) + c / 128];
+  }
+  if (fmt == OREF_MXFP4) {
+    const uint8_t *q = (const uint8_t *)w;
+    const uint8_t *se = (const uint8_t *)s;
+    const uint8_t byte = q[base + n * (C / 2) + c / 2];
+    const uint8_t code = (c % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+    return oref_e2m1_decode(code) * oref_e8m0_decode(se[sbase + n * (C / 32) + c / 32]);
   }
   const uint16_t *b = (const uint16_t *)w;
   return oref_bf16_decode(b[base + n * C + c]);
+}
+
+/* Start of expert e's weights (elements; bytes for the byte formats) and of
+ * its scales (scale entries) in an [E, R, C] weight tensor. */
+static inline int64_t w_base(int fmt, int64_t e, int64_t R, int64_t C) {
+  return fmt == OREF_MXFP4 ? e * R * (C / 2) : e * R * C;
+}
+static inline int64_t s_base(int fmt, int64_t e, int64_t R, int64_t C) {
+  if (fmt == OREF_FP8) return e * (R / 128) * (C / 128);
+  if (fmt == OREF_MXFP4) return e * R * (C / 32);
+  return 0;
 }
 
 static inline double silu(double z) { return z / (1.0 + exp(-z)); }
@@ -286,16 +323,16 @@ static inline double silu(double z) { return z / (1.0 + exp(-z)); }
  *   zg[n] = sum_h a[h] Wg[n,h],  zu[n] = sum_h a[h] Wu[n,h]
  *   h = silu(zg) * zu, stored as h_fp8 ? e4m3 + 1x128 scales : bf16
  *   out[c] = sum_i h[i] Wd[c,i]                                           */
-static void gated_ffn(int H, int I, int w_fp8, int h_fp8,
-                      const void *wgu, const float *sgu, int64_t gu_base, int64_t sgu_base,
-                      const void *wd, const float *sd, int64_t d_base, int64_t sd_base,
+static void gated_ffn(int H, int I, int w_fmt, int h_fp8,
+                      const void *wgu, const void *sgu, int64_t gu_base, int64_t sgu_base,
+                      const void *wd, const void *sd, int64_t d_base, int64_t sd_base,
                       const double *a, double *out, double *out_h) {
   double *hs = (double *)malloc(sizeof(double) * (size_t)I);
   float *hf = (float *)calloc((size_t)I + 1, sizeof(float));
   for (int n = 0; n < I; ++n) {
     double zg = 0.0, zu = 0.0;
-    for (int h = 0; h < H; ++h) zg += a[h] * w_elem(w_fp8, wgu, sgu, gu_base, sgu_base, H, n, h);
-    for (int h = 0; h < H; ++h) zu += a[h] * w_elem(w_fp8, wgu, sgu, gu_base, sgu_base, H, (int64_t)I + n, h);
+    for (int h = 0; h < H; ++h) zg += a[h] * w_elem(w_fmt, wgu, sgu, gu_base, sgu_base, H, n, h);
+    for (int h = 0; h < H; ++h) zu += a[h] * w_elem(w_fmt, wgu, sgu, gu_base, sgu_base, H, (int64_t)I + n, h);
     hf[n] = (float)(silu(zg) * zu);   /* the value the layer holds before storing h */
   }
   if (h_fp8) {
@@ -310,7 +347,7 @@ static void gated_ffn(int H, int I, int w_fp8, int h_fp8,
   if (out_h) memcpy(out_h, hs, sizeof(double) * (size_t)I);
   for (int c = 0; c < H; ++c) {
     double acc = 0.0;
-    for (int i = 0; i < I; ++i) acc += hs[i] * w_elem(w_fp8, wd, sd, d_base, sd_base, I, c, i);
+    for (int i = 0; i < I; ++i) acc += hs[i] * w_elem(w_fmt, wd, sd, d_base, sd_base, I, c, i);
     out[c] = acc;
   }
   free(hs); free(hf);
@@ -318,7 +355,7 @@ static void gated_ffn(int H, int I, int w_fp8, int h_fp8,
 
 static void dequant_input(const oref_layer *L, const void *a, const float *a_scale, double *ad) {
   const int H = L->hidden;
-  if (L->expert_fp8) {
+  if (L->expert_format != OREF_BF16) {
     const uint8_t *q = (const uint8_t *)a;
     for (int h = 0; h < H; ++h) ad[h] = e4m3_tab()[q[h]] * (double)a_scale[h / 128];
   } else {
@@ -332,10 +369,10 @@ void oref_expert_row(const oref_layer *L, int32_t e, const void *a, const float 
   const int64_t H = L->hidden, I = L->inter;
   double *ad = (double *)malloc(sizeof(double) * (size_t)H);
   dequant_input(L, a, a_scale, ad);
-  int fp8 = L->expert_fp8;
-  gated_ffn((int)H, (int)I, fp8, fp8,
-            L->w_gate_up, L->s_gate_up, (int64_t)e * 2 * I * H, (int64_t)e * (2 * I / 128) * (H / 128),
-            L->w_down, L->s_down, (int64_t)e * H * I, (int64_t)e * (H / 128) * (I / 128),
+  const int fmt = L->expert_format;
+  gated_ffn((int)H, (int)I, fmt, fmt != OREF_BF16,
+            L->w_gate_up, L->s_gate_up, w_base(fmt, e, 2 * I, H), s_base(fmt, e, 2 * I, H),
+            L->w_down, L->s_down, w_base(fmt, e, H, I), s_base(fmt, e, H, I),
             ad, out, out_h);
   free(ad);
 }
@@ -344,7 +381,7 @@ void oref_expert_gate_up_factored(const oref_layer *L, int32_t e, const uint8_t 
                                   const float *a_scale, double *zg, double *zu) {
   const int64_t H = L->hidden, I = L->inter, KB = H / 128;
   const uint8_t *w = (const uint8_t *)L->w_gate_up + (int64_t)e * 2 * I * H;
-  const float *s = L->s_gate_up + (int64_t)e * (2 * I / 128) * KB;
+  const float *s = (const float *)L->s_gate_up + (int64_t)e * (2 * I / 128) * KB;
   for (int64_t r = 0; r < 2 * I; ++r) {
     double acc = 0.0;
     for (int64_t kb = 0; kb < KB; ++kb) {
@@ -357,16 +394,41 @@ void oref_expert_gate_up_factored(const oref_layer *L, int32_t e, const uint8_t 
   }
 }
 
+void oref_expert_gate_up_mx_factored(const oref_layer *L, int32_t e, const uint8_t *a,
+                                     const float *a_scale, double *zg, double *zu) {
+  const int64_t H = L->hidden, I = L->inter;
+  const uint8_t *w = (const uint8_t *)L->w_gate_up + (int64_t)e * 2 * I * (H / 2);
+  const uint8_t *s = (const uint8_t *)L->s_gate_up + (int64_t)e * 2 * I * (H / 32);
+  for (int64_t r = 0; r < 2 * I; ++r) {
+    double acc = 0.0;
+    for (int64_t kg = 0; kg < H / 128; ++kg) {
+      double group = 0.0;
+      for (int64_t kb = 4 * kg; kb < 4 * kg + 4; ++kb) {
+        double part = 0.0;
+        for (int64_t k = 32 * kb; k < 32 * kb + 32; k += 2) {
+          const uint8_t byte = w[r * (H / 2) + k / 2];
+          part += e4m3_tab()[a[k]] * oref_e2m1_decode(byte & 0x0F);
+          part += e4m3_tab()[a[k + 1]] * oref_e2m1_decode(byte >> 4);
+        }
+        group += oref_e8m0_decode(s[r * (H / 32) + kb]) * part;
+      }
+      acc += (double)a_scale[kg] * group;
+    }
+    if (r < I) zg[r] = acc; else zu[r - I] = acc;
+  }
+}
+
 void oref_expert_gate_up_dequant(const oref_layer *L, int32_t e, const uint8_t *a,
                                  const float *a_scale, double *zg, double *zu) {
   const int64_t H = L->hidden, I = L->inter;
+  const int fmt = L->expert_format;
   double *ad = (double *)malloc(sizeof(double) * (size_t)H);
   for (int64_t h = 0; h < H; ++h) ad[h] = e4m3_tab()[a[h]] * (double)a_scale[h / 128];
   for (int64_t r = 0; r < 2 * I; ++r) {
     double acc = 0.0;
     for (int64_t h = 0; h < H; ++h)
-      acc += ad[h] * w_elem(1, L->w_gate_up, L->s_gate_up, (int64_t)e * 2 * I * H,
-                            (int64_t)e * (2 * I / 128) * (H / 128), H, r, h);
+      acc += ad[h] * w_elem(fmt, L->w_gate_up, L->s_gate_up, w_base(fmt, e, 2 * I, H),
+                            s_base(fmt, e, 2 * I, H), H, r, h);
     if (r < I) zg[r] = acc; else zu[r - I] = acc;
   }
   free(ad);
@@ -384,7 +446,7 @@ void oref_shared_row(const oref_layer *L, const uint16_t *x_row, double *out) {
 void oref_expert_ffn(const oref_layer *L, const int32_t *offsets, const void *a_rows,
                      const float *a_scale, int64_t N, double *out) {
   const int64_t H = L->hidden, E = L->num_experts, G = H / 128;
-  const int fp8 = L->expert_fp8;
+  const int fp8 = L->expert_format != OREF_BF16;
 #ifdef _OPENMP
 #pragma omp parallel for schedule(dynamic, 1)
 #endif
@@ -411,7 +473,7 @@ static void token_output(const oref_layer *L, const uint16_t *xr, const int32_t 
   oref_shared_row(L, xr, y);
   uint8_t *q = NULL;
   float *sc = NULL;
-  if (L->expert_fp8) {
+  if (L->expert_format != OREF_BF16) {
     float *xf = (float *)malloc(sizeof(float) * (size_t)H);
     for (int h = 0; h < H; ++h) xf[h] = (float)oref_bf16_decode(xr[h]);
     q = (uint8_t *)malloc((size_t)H);
@@ -421,7 +483,7 @@ static void token_output(const oref_layer *L, const uint16_t *xr, const int32_t 
   }
   for (int j = 0; j < nsel; ++j) {
     if (ids[j] < 0 || ids[j] >= L->num_experts) continue;
-    oref_expert_row(L, ids[j], L->expert_fp8 ? (const void *)q : (const void *)xr, sc, o, NULL);
+    oref_expert_row(L, ids[j], q ? (const void *)q : (const void *)xr, sc, o, NULL);
     for (int c = 0; c < H; ++c) y[c] += g[j] * o[c];
   }
   free(o); free(q); free(sc);

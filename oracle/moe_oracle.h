@@ -19,7 +19,8 @@
  *
  * in fp64, with the quantisation points of the FP8 mode (1x128 per-token
  * activation groups, 128x128 weight blocks) applied where the layer stores a
- * value in a narrow format.  Quantisation decisions (which fp8 code a value
+ * value in a narrow format.  A third weight format, MX FP4 (E2M1 codes with
+ * one power-of-two scale per 32 inputs), keeps the FP8 mode's activations.  Quantisation decisions (which fp8 code a value
  * gets) are taken in fp32, the precision the GPU takes them in.
  *
  * Parity status of each function is listed beside it; every function here is
@@ -39,21 +40,34 @@ extern "C" {
  *   w_router        bf16 [E, H]
  *   router_bias     f32  [E] or NULL (added to the logits before selection)
  *   w_gate_up       [E, 2I, H]  rows 0..I-1 gate, rows I..2I-1 up
- *   s_gate_up       f32 [E, 2I/128, H/128]  (fp8 only; dequant = code * scale)
+ *   s_gate_up       scales of w_gate_up (see below)
  *   w_down          [E, H, I]
- *   s_down          f32 [E, H/128, I/128]   (fp8 only)
+ *   s_down          scales of w_down
  *   w_shared_gate_up bf16 [2Is, H], w_shared_down bf16 [H, Is]  (Is = 0: none)
- * expert_fp8 = 0: expert weights are bf16 (uint16 bit patterns);
- * expert_fp8 = 1: expert weights are OCP E4M3FN bytes with the fp32 scales. */
+ * expert_format:
+ *   OREF_BF16  (0): expert weights are bf16 (uint16 bit patterns), no scales;
+ *   OREF_FP8   (1): OCP E4M3FN bytes; s_gate_up f32 [E, 2I/128, H/128],
+ *                   s_down f32 [E, H/128, I/128]; dequant = code * scale;
+ *   OREF_MXFP4 (2): OCP MX FP4: E2M1 codes two to a byte, input 2j in the
+ *                   low nibble of byte j ("TensorFold" pull-request page,
+ *                   nvfp4 format notes: the same packing), so w_gate_up is
+ *                   [E, 2I, H/2] and w_down [E, H, I/2] bytes; one E8M0
+ *                   scale byte per 32 consecutive inputs of a row (OCP
+ *                   Microscaling Formats specification v1.0): s_gate_up
+ *                   uint8 [E, 2I, H/32], s_down uint8 [E, H, I/32];
+ *                   dequant = e2m1(code) * 2^(scale - 127).
+ * Activations and h are stored as E4M3 with 1x128 scales in both scaled
+ * formats, as bf16 in bf16 mode. */
+enum { OREF_BF16 = 0, OREF_FP8 = 1, OREF_MXFP4 = 2 };
 typedef struct oref_layer {
   int32_t hidden, inter, num_experts, top_k, shared_inter;
-  int32_t expert_fp8;
+  int32_t expert_format;
   const uint16_t *w_router;
   const float *router_bias;
   const void *w_gate_up;
-  const float *s_gate_up;
+  const void *s_gate_up;
   const void *w_down;
-  const float *s_down;
+  const void *s_down;
   const uint16_t *w_shared_gate_up;
   const uint16_t *w_shared_down;
 } oref_layer;
@@ -63,6 +77,8 @@ double oref_bf16_decode(uint16_t b);
 uint16_t oref_bf16_encode(double v);          /* v -> binary32 -> bf16, each round to nearest even */
 double oref_e4m3_decode(uint8_t c);           /* NaN for S.1111.111 */
 uint8_t oref_e4m3_encode(float v);            /* RNE, saturate to +-448, NaN -> 0x7F|sign */
+double oref_e2m1_decode(uint8_t c);           /* low 4 bits: S.EE.M, bias 1, max 6 */
+double oref_e8m0_decode(uint8_t e);           /* 2^(e-127); NaN for 0xFF */
 
 /* Per-token 1x128 activation quantisation of one row of n values (n % 128 == 0):
  * for each group, a = max|v|, s = a / 448 in fp32 (s = 1 when a == 0),
@@ -100,7 +116,7 @@ int64_t oref_permute(const int32_t *key, int64_t N, int32_t E,
 /* ---- expert FFN -------------------------------------------------------- */
 /* Routed expert e applied to rows of an already-stored input:
  *   bf16 mode: a = bf16 row of length H;
- *   fp8  mode: a = e4m3 codes (H bytes) with H/128 fp32 group scales.
+ *   fp8 and mxfp4 modes: a = e4m3 codes (H bytes) with H/128 fp32 group scales.
  * h is stored as the GPU stores it (bf16, or e4m3 + 1x128 scales, each
  * decided from the fp32 value of h); out[H] in fp64.
  * out_h (optional, [I]) receives the dequantised stored h. */
@@ -112,7 +128,14 @@ void oref_expert_row(const oref_layer *L, int32_t e, const void *a, const float 
  * for the gate/up pre-activations: zg[I], zu[I]. */
 void oref_expert_gate_up_factored(const oref_layer *L, int32_t e, const uint8_t *a,
                                   const float *a_scale, double *zg, double *zu);
-/* Same pre-activations from dequantised operands (dequant then matmul). */
+/* The same pre-activations for mxfp4 weights in the factored form of the
+ * scaled MFMA: for each 128-input group kg of the activation and each
+ * 32-input block kb inside it,
+ *   sum_kg s_a[kg] sum_{kb in kg} 2^(s_w[n,kb]-127) sum_{k in kb} q_a[k] e2m1(q_w[n,k]). */
+void oref_expert_gate_up_mx_factored(const oref_layer *L, int32_t e, const uint8_t *a,
+                                     const float *a_scale, double *zg, double *zu);
+/* Same pre-activations from dequantised operands (dequant then matmul;
+ * fp8 and mxfp4 modes). */
 void oref_expert_gate_up_dequant(const oref_layer *L, int32_t e, const uint8_t *a,
                                  const float *a_scale, double *zg, double *zu);
 
@@ -121,13 +144,13 @@ void oref_shared_row(const oref_layer *L, const uint16_t *x_row, double *out);
 
 /* moe_expert_ffn equivalent over expert-grouped rows:
  * rows offsets[e]..offsets[e+1]-1 of a_rows go through expert e.
- * a_rows: bf16 [N,H] or e4m3 [N,H] with a_scale [N,H/128].  out [N,H]. */
+ * a_rows: bf16 [N,H] or (fp8, mxfp4) e4m3 [N,H] with a_scale [N,H/128].  out [N,H]. */
 void oref_expert_ffn(const oref_layer *L, const int32_t *offsets, const void *a_rows,
                      const float *a_scale, int64_t N, double *out);
 
 /* ---- whole layer ------------------------------------------------------- */
 /* y[n_list, H] for the listed tokens (NULL = all T).  Routes with oref_route,
- * quantises x per token (fp8 mode), sums shared + gated experts in fp64.
+ * quantises x per token (fp8 and mxfp4 modes), sums shared + gated experts in fp64.
  * ids/gates/gap outputs optional ([n_list,k], [n_list,k], [n_list]). */
 void oref_forward(const oref_layer *L, const uint16_t *x, int64_t T,
                   const int64_t *token_list, int64_t n_list, double *y,

@@ -18,7 +18,9 @@ Recipe (all draws seeded):
   * routed expert weights (up to 13 GB) come from torch's generator on the
     target device, one generator per (expert, matrix) keyed by the seed;
   * every value is drawn in fp32 and rounded to bf16 (nearest even), or, for
-    fp8 experts, scaled per 128x128 block by s = amax/448 and rounded to E4M3.
+    fp8 experts, scaled per 128x128 block by s = amax/448 and rounded to E4M3,
+    or, for MX FP4 experts, given one power-of-two scale per 32 inputs of a
+    row and rounded to E2M1 (see quantize_mxfp4).
 """
 from __future__ import annotations
 
@@ -39,7 +41,7 @@ class MoEConfig:
     k: int                 # top-k (0 for pre-routed triples)
     I: int                 # routed expert intermediate
     Is: int                # shared expert intermediate (0 = none)
-    expert_dtype: str      # "bf16" | "fp8"
+    expert_dtype: str      # "bf16" | "fp8" | "mxfp4"
     router_std: float      # std of the router weights
     expert_std: float = 0.02
     zipf_s: float = 0.0    # > 0: router bias skews loads by Zipf(s) ranks
@@ -85,6 +87,14 @@ CONFIGS = {
         router_std=1.0 / 64, zipf_s=1.1, triples=16384,
         description="one rank's EP=8 share: 44 FP8 experts, 16384 pre-routed Zipf(1.1) "
                     "triples, bf16 shared expert on 16384 tokens"),
+    "small_mxfp4": MoEConfig(
+        "small_mxfp4", T=136, H=512, E=16, k=4, I=256, Is=128, expert_dtype="mxfp4",
+        router_std=1.0 / math.sqrt(512),
+        description="scaled-down MoE layer, MX FP4 experts, T=136, H=512, 16 experts top-4, I=256"),
+    "decode_mxfp4": MoEConfig(
+        "decode_mxfp4", T=64, H=4096, E=352, k=8, I=1536, Is=1536, expert_dtype="mxfp4",
+        router_std=1.0 / 64,
+        description="Step-5 MoE shape with MX FP4 expert weights (E2M1, E8M0 per 32), decode T=64"),
     "dense_ff_bf16": MoEConfig(
         "dense_ff_bf16", T=8192, H=4096, E=1, k=1, I=13824, Is=0, expert_dtype="bf16",
         router_std=1.0 / 64, dense=True,
@@ -128,6 +138,43 @@ def quantize_blocks_e4m3(w: torch.Tensor):
     return q.to(torch.float8_e4m3fn).view(torch.uint8), s.contiguous()
 
 
+# E2M1 magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6 (codes 0..7).  Rounding to
+# nearest: a magnitude goes to code i when it lies between the midpoints
+# around value i; at a midpoint the even code wins (ties to even).
+_E2M1_MID = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+_E2M1_TIE_UP = (0.75, 1.75, 3.5)   # midpoints whose even neighbour is the upper code
+
+
+def quantize_mxfp4(w: torch.Tensor):
+    """Input-side weight quantiser to OCP MX FP4: [R, C] fp32 ->
+    (uint8 [R, C/2]: two E2M1 codes per byte, input 2j in the low nibble of
+    byte j; uint8 [R, C/32]: E8M0 scale bytes).
+
+    Per 32 inputs of a row: the scale is 2^(floor(log2 amax) - 2) (E2M1's
+    largest exponent is 2), byte = exponent + 127 clamped to [0, 254] (127
+    for an all-zero block); code = E2M1(w / scale), nearest with ties to
+    even, magnitudes above 6 saturated to 6.  This prepares stored weights
+    the way an MX checkpoint holds them; it is not part of the layer.
+    """
+    R, Cc = w.shape
+    assert Cc % 32 == 0
+    blk = w.float().reshape(R, Cc // 32, 32)
+    amax = blk.abs().amax(dim=2)
+    _, ex = torch.frexp(amax)                  # amax = m * 2^ex, m in [0.5, 1)
+    e = ex.to(torch.int32) - 1 - 2             # floor(log2 amax) - 2
+    sbyte = torch.where(amax > 0, (e + 127).clamp(0, 254), torch.full_like(e, 127))
+    scale = torch.exp2((sbyte - 127).float())
+    v = (blk / scale[..., None]).abs().clamp(max=6.0)
+    mid = torch.tensor(_E2M1_MID, dtype=torch.float32, device=w.device)
+    code = torch.bucketize(v, mid, right=False)
+    for t in _E2M1_TIE_UP:
+        code = code + (v == t).to(code.dtype)
+    code = code | (((blk < 0) & (code > 0)).to(code.dtype) << 3)
+    code = code.to(torch.uint8).reshape(R, Cc)
+    packed = code[:, 0::2] | (code[:, 1::2] << 4)
+    return packed.contiguous(), sbyte.to(torch.uint8).contiguous()
+
+
 def zipf_bias(cfg: MoEConfig) -> Optional[np.ndarray]:
     """Per-expert router bias: b_e = -beta * s * ln(r_e), r = seeded permutation of 1..E."""
     if cfg.zipf_s <= 0 or cfg.triples:
@@ -141,16 +188,21 @@ class LayerTensors:
     cfg: MoEConfig
     w_router: torch.Tensor                 # bf16 [E,H]
     router_bias: Optional[torch.Tensor]    # f32 [E]
-    w_gate_up: torch.Tensor                # bf16 or uint8(e4m3) [E,2I,H]
-    w_down: torch.Tensor                   # bf16 or uint8(e4m3) [E,H,I]
-    s_gate_up: Optional[torch.Tensor]      # f32 [E,2I/128,H/128]
-    s_down: Optional[torch.Tensor]         # f32 [E,H/128,I/128]
+    w_gate_up: torch.Tensor                # bf16 or uint8(e4m3) [E,2I,H]; mxfp4: uint8 [E,2I,H/2]
+    w_down: torch.Tensor                   # bf16 or uint8(e4m3) [E,H,I]; mxfp4: uint8 [E,H,I/2]
+    s_gate_up: Optional[torch.Tensor]      # f32 [E,2I/128,H/128]; mxfp4: uint8 (E8M0) [E,2I,H/32]
+    s_down: Optional[torch.Tensor]         # f32 [E,H/128,I/128]; mxfp4: uint8 (E8M0) [E,H,I/32]
     w_shared_gate_up: Optional[torch.Tensor]  # bf16 [2Is,H]
     w_shared_down: Optional[torch.Tensor]     # bf16 [H,Is]
 
     @property
     def fp8(self) -> bool:
-        return self.cfg.expert_dtype == "fp8"
+        """Activations and h are stored as e4m3 + 1x128 scales (fp8 and mxfp4 experts)."""
+        return self.cfg.expert_dtype != "bf16"
+
+    @property
+    def mx(self) -> bool:
+        return self.cfg.expert_dtype == "mxfp4"
 
 
 def _expert_gen(device, seed: int, e: int, which: int) -> torch.Generator:
@@ -164,23 +216,30 @@ def make_layer(cfg: MoEConfig, device="cpu") -> LayerTensors:
     dev = torch.device(device)
     E, H, I, Is = cfg.E, cfg.H, cfg.I, cfg.Is
     fp8 = cfg.expert_dtype == "fp8"
-    if fp8:
-        assert H % 128 == 0 and I % 128 == 0, "fp8 experts need H and I multiples of 128"
+    mx = cfg.expert_dtype == "mxfp4"
+    if fp8 or mx:
+        assert H % 128 == 0 and I % 128 == 0, "fp8 and mxfp4 experts need H and I multiples of 128"
     w_router = _bf16_bits(_rng(cfg.seed, 2).standard_normal((E, H), dtype=np.float32)
                           * np.float32(cfg.router_std)).to(dev)
     b = zipf_bias(cfg)
     router_bias = None if b is None else torch.from_numpy(b).to(dev)
-    wdt = torch.uint8 if fp8 else torch.bfloat16
-    w_gu = torch.empty((E, 2 * I, H), dtype=wdt, device=dev)
-    w_d = torch.empty((E, H, I), dtype=wdt, device=dev)
-    s_gu = torch.empty((E, 2 * I // 128, H // 128), dtype=torch.float32, device=dev) if fp8 else None
-    s_d = torch.empty((E, H // 128, I // 128), dtype=torch.float32, device=dev) if fp8 else None
+    wdt = torch.bfloat16 if not (fp8 or mx) else torch.uint8
+    pk = 2 if mx else 1
+    w_gu = torch.empty((E, 2 * I, H // pk), dtype=wdt, device=dev)
+    w_d = torch.empty((E, H, I // pk), dtype=wdt, device=dev)
+    s_gu = s_d = None
+    if fp8:
+        s_gu = torch.empty((E, 2 * I // 128, H // 128), dtype=torch.float32, device=dev)
+        s_d = torch.empty((E, H // 128, I // 128), dtype=torch.float32, device=dev)
+    elif mx:
+        s_gu = torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device=dev)
+        s_d = torch.empty((E, H, I // 32), dtype=torch.uint8, device=dev)
     for e in range(E):
         for which, (shape, dst) in enumerate((((2 * I, H), w_gu), ((H, I), w_d))):
             w = torch.randn(shape, generator=_expert_gen(dev, cfg.seed, e, which), device=dev,
                             dtype=torch.float32) * cfg.expert_std
-            if fp8:
-                q, s = quantize_blocks_e4m3(w)
+            if fp8 or mx:
+                q, s = quantize_mxfp4(w) if mx else quantize_blocks_e4m3(w)
                 dst[e].copy_(q)
                 (s_gu if which == 0 else s_d)[e].copy_(s)
             else:

@@ -21,7 +21,7 @@ def dev():
 def oracle_layer(lt: W.LayerTensors) -> oracle.Layer:
     cfg = lt.cfg
     h = W.host_layer_arrays(lt)
-    return oracle.Layer(cfg.H, cfg.I, cfg.E, max(cfg.k, 1), cfg.expert_dtype == "fp8", h["w_router"],
+    return oracle.Layer(cfg.H, cfg.I, cfg.E, max(cfg.k, 1), cfg.expert_dtype, h["w_router"],
                         h["w_gate_up"], h["w_down"], s_gate_up=h["s_gate_up"], s_down=h["s_down"],
                         router_bias=h["router_bias"], w_shared_gate_up=h["w_shared_gate_up"],
                         w_shared_down=h["w_shared_down"])
