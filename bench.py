@@ -5,7 +5,7 @@ One step = one pass of the whole layer (router, grouping, routed expert
 gate/up + SwiGLU and down, shared expert, combine) over one batch of
 synthetic tokens already resident in HBM.  Prints one JSON line.
 
-  python bench.py [--workload decode_bf16|decode_fp8|prefill_fp8|ep8_share_fp8|dense_ff_bf16|small_bf16]
+  python bench.py [--workload decode_bf16|decode_fp8|decode_mxfp4|prefill_fp8|ep8_share_fp8|dense_ff_bf16|small_bf16]
                   [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 
 The default workload is the bf16 decode layer (T=64 tokens, hidden 4096,
@@ -28,7 +28,7 @@ if ROOT not in sys.path:
 
 METRIC = "MoE-layer tokens/s + HBM GB/s (decode) / MFMA TFLOP/s % peak (prefill)"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # dense MFMA, TFLOP/s
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # dense MFMA, TFLOP/s (e2m1 x e4m3 runs at the fp8 rate)
 
 
 def parse():
@@ -116,7 +116,8 @@ def main():
     lt = W.make_layer(cfg, dev)
     x = W.make_x(cfg, dev)
     T, H, E, I, Is = cfg.T, cfg.H, cfg.E, cfg.I, cfg.Is
-    fp8 = cfg.expert_dtype == "fp8"
+    fp8 = cfg.expert_dtype != "bf16"     # activations and h stored as e4m3 + 1x128 scales
+    mx = cfg.expert_dtype == "mxfp4"
     layer = B.Layer.from_tensors(lt, top_k=cfg.k if not cfg.triples else 0)
     N = cfg.N
     y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
@@ -187,8 +188,12 @@ def main():
     # ---- algorithmic work (what the method must move / compute)
     active = int((counts > 0).sum())
     esz = 1 if fp8 else 2
-    w_gu_b = 2 * I * H * esz + ((2 * I // 128) * (H // 128) * 4 if fp8 else 0)
-    w_d_b = H * I * esz + ((H // 128) * (I // 128) * 4 if fp8 else 0)
+    if mx:   # half a byte per weight plus one E8M0 byte per 32 weights
+        w_gu_b = 2 * I * H // 2 + 2 * I * H // 32
+        w_d_b = H * I // 2 + H * I // 32
+    else:
+        w_gu_b = 2 * I * H * esz + ((2 * I // 128) * (H // 128) * 4 if fp8 else 0)
+        w_d_b = H * I * esz + ((H // 128) * (I // 128) * 4 if fp8 else 0)
     shared_b = 3 * Is * H * 2
     router_b = 0 if (cfg.triples or cfg.dense) else E * H * 2
     layer_bytes = active * (w_gu_b + w_d_b) + shared_b + router_b + T * H * 2 * 2
@@ -257,7 +262,7 @@ def main():
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp8" if fp8 else "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.expert_dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": T, "hidden": H, "experts": E, "top_k": cfg.k,
                    "inter": I, "shared_inter": Is, "expert_dtype": cfg.expert_dtype,
                    "assignments": N, "active_experts": active, "max_rows_per_expert": int(counts.max()),

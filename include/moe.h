@@ -40,8 +40,16 @@
  *     intermediate h) carry one fp32 scale per token per 128 consecutive
  *     input columns: s = amax/448 (IEEE fp32 division; 1 when amax == 0),
  *     code = round-to-nearest-even(v / s).  Dequantised value = code * s.
+ *   - MX FP4 mode (a low-bit weight format beside the two above): weights
+ *     are OCP MX FP4, E2M1 codes two to a byte with input 2j in the low
+ *     nibble of byte j (the packing of the NVFP4 linears described on the
+ *     "TensorFold" pull-request page) and one E8M0 scale byte per 32
+ *     consecutive inputs of a row (OCP Microscaling Formats specification
+ *     v1.0); dequantised weight = e2m1(code) * 2^(scale - 127).  Activations
+ *     and h are E4M3 with 1x128 scales exactly as in FP8 mode.
  *   - Expert GEMMs accumulate in fp32; h = silu(z_gate) * z_up in fp32, then
- *     stored as bf16 (bf16 experts) or E4M3 + 1x128 scales (fp8 experts).
+ *     stored as bf16 (bf16 experts) or E4M3 + 1x128 scales (fp8 and mxfp4
+ *     experts).
  *   - Combine: fp32 sum in a fixed order -- shared expert first, then the
  *     token's assignments in increasing assignment index -- rounded once to
  *     the output dtype (the partial sums of the pages' deployment are likewise
@@ -61,7 +69,8 @@ extern "C" {
 typedef enum moe_dtype {
   MOE_BF16 = 1,        /* bfloat16 */
   MOE_FP8_E4M3FN = 2,  /* OCP E4M3FN with fp32 block/group scales */
-  MOE_F32 = 3          /* IEEE binary32 */
+  MOE_F32 = 3,         /* IEEE binary32 */
+  MOE_MXFP4_E2M1 = 4   /* OCP MX FP4: E2M1 codes, two per byte, E8M0 scale per 32 */
 } moe_dtype;
 
 typedef enum moe_status {
@@ -69,7 +78,7 @@ typedef enum moe_status {
   MOE_EINVAL = 1,        /* NULL pointer where one is required, bad size or dimension,
                             k outside [1, min(E, 32)], misaligned pointer */
   MOE_EUNSUPPORTED = 2,  /* valid but not built: H % 128 != 0; bf16 experts with I % 64 != 0;
-                            fp8 experts with I % 128 != 0; E > 1024; H, I or the
+                            fp8 or mxfp4 experts with I % 128 != 0; E > 1024; H, I or the
                             shared expert's I > 16384;
                             unsupported dtype combination */
   MOE_EWORKSPACE = 3,    /* ws_bytes smaller than the call needs */
@@ -81,13 +90,16 @@ typedef enum moe_status {
  *   held here: 352 for the whole layer, 44 for one of eight expert-parallel
  *   shares), top_k k (0 allowed only for calls that take pre-routed
  *   assignments), shared_inter Is (0 = no shared expert).
- *   expert_dtype: MOE_BF16 or MOE_FP8_E4M3FN.
+ *   expert_dtype: MOE_BF16, MOE_FP8_E4M3FN or MOE_MXFP4_E2M1.
  *   w_router        bf16 [E, H]            (moe_route / moe_forward only)
  *   router_bias     f32  [E] or NULL       (added to the logits)
- *   w_gate_up       [E, 2I, H]: rows 0..I-1 gate, rows I..2I-1 up  (bf16 or e4m3)
- *   s_gate_up       f32 [E, 2I/128, H/128] (fp8 only, else NULL)
- *   w_down          [E, H, I]              (bf16 or e4m3)
- *   s_down          f32 [E, H/128, I/128]  (fp8 only, else NULL)
+ *   w_gate_up       [E, 2I, H]: rows 0..I-1 gate, rows I..2I-1 up  (bf16 or e4m3;
+ *                   mxfp4: bytes [E, 2I, H/2], two codes per byte)
+ *   s_gate_up       fp8: f32 [E, 2I/128, H/128]; mxfp4: E8M0 bytes [E, 2I, H/32];
+ *                   bf16: NULL
+ *   w_down          [E, H, I]              (bf16 or e4m3; mxfp4: bytes [E, H, I/2])
+ *   s_down          fp8: f32 [E, H/128, I/128]; mxfp4: E8M0 bytes [E, H, I/32];
+ *                   bf16: NULL
  *   w_shared_gate_up bf16 [2Is, H], w_shared_down bf16 [H, Is] (NULL if Is == 0)
  * Weights are read-only; they are the layout of a linear layer's weight
  * ([out, in]; y = a W^T). */
@@ -101,9 +113,9 @@ typedef struct moe_layer {
   const void *w_router;
   const float *router_bias;
   const void *w_gate_up;
-  const float *s_gate_up;
+  const void *s_gate_up;
   const void *w_down;
-  const float *s_down;
+  const void *s_down;
   const void *w_shared_gate_up;
   const void *w_shared_down;
 } moe_layer;
@@ -136,9 +148,9 @@ moe_status moe_route(const moe_layer *layer, const void *x, int64_t T,
  *                  expert order; inside an expert, increasing assignment index)
  *   perm_pos       int32 [N] out: row of assignment i (-1 if its expert or
  *                  token is out of range: such assignments are dropped)
- *   x_perm         [N, H] out: bf16 (bf16 experts) or e4m3 codes (fp8 experts);
- *                  rows >= offsets[E] are left unwritten
- *   x_scale        f32 [N, H/128] out (fp8 experts; NULL for bf16) */
+ *   x_perm         [N, H] out: bf16 (bf16 experts) or e4m3 codes (fp8 and
+ *                  mxfp4 experts); rows >= offsets[E] are left unwritten
+ *   x_scale        f32 [N, H/128] out (fp8 and mxfp4 experts; NULL for bf16) */
 moe_status moe_permute(const moe_layer *layer, const void *x, int64_t T,
                        const int32_t *assign_expert, const int32_t *assign_token, int64_t N,
                        int32_t *expert_offsets, int32_t *perm_src, int32_t *perm_pos,
@@ -151,8 +163,8 @@ moe_status moe_permute(const moe_layer *layer, const void *x, int64_t T,
  * introduction: block-scaled FP8 expert GEMM; "Step-5-Preview", "Model
  * Architecture": intermediate 1,536 per expert.)
  *   expert_offsets int32 [E+1] (device; offsets[E] <= N)
- *   x_perm         [N, H] bf16 or e4m3 (the layer's expert dtype)
- *   x_scale        f32 [N, H/128] (fp8 experts; NULL for bf16)
+ *   x_perm         [N, H] bf16 (bf16 experts) or e4m3 (fp8 and mxfp4 experts)
+ *   x_scale        f32 [N, H/128] (fp8 and mxfp4 experts; NULL for bf16)
  *   y_perm         [N, H] out, y_dtype MOE_BF16 or MOE_F32; rows >= offsets[E]
  *                  are left unwritten
  * The shared expert runs through this call as a one-expert bf16 layer

@@ -19,6 +19,9 @@ from .build import LIB
 MOE_BF16 = 1
 MOE_FP8_E4M3FN = 2
 MOE_F32 = 3
+MOE_MXFP4_E2M1 = 4
+
+EXPERT_DTYPE = {"bf16": MOE_BF16, "fp8": MOE_FP8_E4M3FN, "mxfp4": MOE_MXFP4_E2M1}
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
 
@@ -122,9 +125,8 @@ class Layer:
     def from_tensors(cls, lt, top_k: Optional[int] = None) -> "Layer":
         """Routed layer from workloads.LayerTensors."""
         cfg = lt.cfg
-        fp8 = cfg.expert_dtype == "fp8"
         return cls(cfg.H, cfg.I, cfg.E, cfg.k if top_k is None else top_k,
-                   MOE_FP8_E4M3FN if fp8 else MOE_BF16, lt.w_gate_up, lt.w_down,
+                   EXPERT_DTYPE[cfg.expert_dtype], lt.w_gate_up, lt.w_down,
                    lt.s_gate_up, lt.s_down, lt.w_router, lt.router_bias,
                    lt.w_shared_gate_up, lt.w_shared_down, cfg.Is if lt.w_shared_gate_up is not None else 0)
 

@@ -17,17 +17,34 @@
 // and one activation group, so one 16x16x128 MFMA yields the raw block
 // product, and acc += P * (s_w * s_a[token]) applies both scales in fp32.
 //
+// MX FP4 weights.  The scaled MFMA takes an E2M1 A operand (16 bytes per lane:
+// lane group g = lane/16 holds inputs 32g..32g+31 of the 128-input chunk,
+// even input in the low nibble, exactly the stored packing) with one E8M0
+// scale byte per lane (its row, its 32-input block), so the weight scales
+// are applied inside the instruction; the E4M3 B operand is read in the
+// instruction's own K order (lane group g: inputs 16g..16g+15 and
+// 64+16g..64+16g+15), and the token's fp32 group scale multiplies the chunk
+// product afterwards as in fp8 mode.
+//
 // Work decomposition.  A device-built list holds one entry per (expert,
 // 16*MT-row tile of that expert's rows); blockIdx.y indexes it (entries past
 // the device-side count exit at once), blockIdx.x the output-column tile.
 // The host never reads the per-expert counts.
 
 #include <algorithm>
+#include <type_traits>
 
 #include "moe_common.h"
 #include "moe_kernels.h"
 
 namespace moe {
+
+#ifndef MX_NC4
+#define MX_NC4 1   // MX loops: four-chunk steps where K allows (else two-chunk steps)
+#endif
+#ifndef MX_PIPE
+#define MX_PIPE 1  // MX loops: software-pipelined two-chunk steps where K allows
+#endif
 
 __device__ __forceinline__ FfnGroup pick_group(const FfnGroup &g0, const FfnGroup &g1, int g) {
   return g ? g1 : g0;
@@ -96,6 +113,23 @@ __device__ __forceinline__ f32x4 chunk_mma(const Frag &a, const Frag &b, f32x4 a
   }
 }
 
+// acc += (E2M1 A with per-lane E8M0 scale sa) * (E4M3 B) * sx for one chunk.
+__device__ __forceinline__ f32x4 chunk_mma_mx(const i32x4 &a, const Frag &b, int sa, f32x4 acc, float sx) {
+  const i32x8 a8 = i32x8{a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, frag_fp8(b), f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                   4, 0, 0, sa, 0, 127);
+  acc[0] += p[0] * sx;
+  acc[1] += p[1] * sx;
+  acc[2] += p[2] * sx;
+  acc[3] += p[3] * sx;
+  return acc;
+}
+
+// E4M3 B fragment of one chunk in the scaled MFMA's K order: inputs
+// 16g..16g+15 and 64+16g..64+16g+15 of the chunk for lane group g
+// (p points at the chunk start + 16g).
+__device__ __forceinline__ Frag load_frag_k64(const uint8_t *p) { return Frag{load16(p), load16(p + 64)}; }
+
 struct StreamArgs {
   FfnGroup g0, g1;
   const TileEntry *tiles;
@@ -114,33 +148,43 @@ __device__ __forceinline__ void tile_rows(const FfnGroup &G, const TileEntry &te
 // Workgroup: 4 waves x (GW gate + GW up 16-row weight tiles) = 64*GW h
 // columns x 16*MT token rows.  Each wave streams its own weight rows straight
 // from HBM into MFMA operand registers (no reuse across waves, so no LDS).
-template <bool FP8, int MT, int GW>
+template <bool FP8, bool MX, int MT, int GW>
 __device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry &te, int H) {
+  static_assert(FP8 || !MX, "MX weights take e4m3 activations");
   constexpr int ESZ = FP8 ? 1 : 2;
   const int lane = lane_id(), w = wave_id();
   int rbeg, rend;
   tile_rows(G, te, rbeg, rend);
   const int e = te.ge & 0xFFFFFF;
   const int I = G.I;
-  const int64_t rowb = (int64_t)H * ESZ;
+  const int64_t xrowb = (int64_t)H * ESZ;             // activation row bytes
+  const int64_t wrowb = MX ? (int64_t)H / 2 : xrowb;  // weight row bytes
   const int hc0 = blockIdx.x * (64 * GW) + w * (16 * GW);
-  const int koff = 32 * (lane >> 4);
+  const int g4 = lane >> 4;
+  const int koff = MX ? 16 * g4 : 32 * g4;
 
-  const uint8_t *wbase = G.wgu + (int64_t)e * 2 * I * rowb;
+  const uint8_t *wbase = G.wgu + (int64_t)e * 2 * I * wrowb;
   const uint8_t *wg[GW], *wu[GW];
+  const uint8_t *mg[GW], *mu[GW];   // MX: the lane's row of E8M0 scale bytes
 #pragma unroll
   for (int i = 0; i < GW; ++i) {
-    wg[i] = wbase + (int64_t)(hc0 + 16 * i + (lane & 15)) * rowb + koff;
-    wu[i] = wbase + (int64_t)(I + hc0 + 16 * i + (lane & 15)) * rowb + koff;
+    const int64_t rg = hc0 + 16 * i + (lane & 15), ru = I + rg;
+    wg[i] = wbase + rg * wrowb + koff;
+    wu[i] = wbase + ru * wrowb + koff;
+    if constexpr (MX) {
+      mg[i] = G.mgu + ((int64_t)e * 2 * I + rg) * (H / 32);
+      mu[i] = G.mgu + ((int64_t)e * 2 * I + ru) * (H / 32);
+    }
   }
   const uint8_t *xr[MT];
   bool xv[MT];
-  int xrow[MT];
+  int xrow[MT], xsrow[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     xrow[m] = rbeg + 16 * m + (lane & 15);
     xv[m] = xrow[m] < rend;
-    xr[m] = G.x + (int64_t)(xv[m] ? xrow[m] : 0) * rowb + koff;
+    xsrow[m] = xv[m] ? xrow[m] : (rbeg < rend ? rbeg : 0);   // a row that exists
+    xr[m] = G.x + (int64_t)xsrow[m] * xrowb + koff;
   }
   f32x4 ag[GW][MT], au[GW][MT];
 #pragma unroll
@@ -148,35 +192,179 @@ __device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry 
 #pragma unroll
     for (int m = 0; m < MT; ++m) ag[i][m] = au[i][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nchunk = (int)(rowb / 128);
+  const int nchunk = (int)(xrowb / 128);
   const int KB = H / 128;
-  const float *sg = FP8 ? G.sgu + ((int64_t)e * (2 * I / 128) + hc0 / 128) * KB : nullptr;
-  const float *su = FP8 ? G.sgu + ((int64_t)e * (2 * I / 128) + (I + hc0) / 128) * KB : nullptr;
+  const float *sg = (FP8 && !MX) ? G.sgu + ((int64_t)e * (2 * I / 128) + hc0 / 128) * KB : nullptr;
+  const float *su = (FP8 && !MX) ? G.sgu + ((int64_t)e * (2 * I / 128) + (I + hc0) / 128) * KB : nullptr;
   const Frag zf = Frag{i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
 
-  for (int c = 0; c < nchunk; ++c) {
-    const int64_t kb = (int64_t)c * 128;
-    Frag fg[GW], fu[GW], fx[MT];
+  if constexpr (MX) {
+    // NC chunks per step, every load of a step issued before its first MFMA.
+    // With NC == 4 (K a multiple of 512) one 16-byte load per row brings the
+    // scale words of all four chunks.
+    auto steps = [&](auto nc_tag) {
+      constexpr int NC = decltype(nc_tag)::value;
+      for (int c = 0; c < nchunk; c += NC) {
+        const int nv = min(NC, nchunk - c);
+        i32x4 fg[NC][GW], fu[NC][GW];
+        uint32_t sgw[NC][GW], suw[NC][GW];
+        Frag fx[NC][MT];
+        float sx[NC][MT];
+        if constexpr (NC == 4) {
 #pragma unroll
-    for (int i = 0; i < GW; ++i) {
-      fg[i] = load_frag(wg[i] + kb);
-      fu[i] = load_frag(wu[i] + kb);
+          for (int i = 0; i < GW; ++i) {
+            const i32x4 a = load16(mg[i] + 4 * c), b = load16(mu[i] + 4 * c);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              sgw[j][i] = (uint32_t)a[j];
+              suw[j][i] = (uint32_t)b[j];
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+          const int cj = j < nv ? c + j : c;   // a short last step reloads its first chunk, counted once
+#pragma unroll
+          for (int i = 0; i < GW; ++i) {
+            fg[j][i] = load16(wg[i] + (int64_t)cj * 64);
+            fu[j][i] = load16(wu[i] + (int64_t)cj * 64);
+            if constexpr (NC != 4) {
+              sgw[j][i] = *reinterpret_cast<const uint32_t *>(mg[i] + 4 * cj);
+              suw[j][i] = *reinterpret_cast<const uint32_t *>(mu[i] + 4 * cj);
+            }
+          }
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            // branch-free: rows past the tile read a valid row and are zeroed after
+            const Frag f = load_frag_k64(xr[m] + (int64_t)cj * 128);
+            const float sv = G.xs[(int64_t)xsrow[m] * KB + cj];
+            fx[j][m] = xv[m] ? f : zf;
+            sx[j][m] = xv[m] ? sv : 0.f;
+          }
+        }
+        // keep every load of the step ahead of the first MFMA (the scheduler
+        // otherwise interleaves load, wait, MFMA and loses the overlap)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+          if (j >= nv) break;
+#pragma unroll
+          for (int i = 0; i < GW; ++i) {
+            const int sag = (int)((sgw[j][i] >> (8 * g4)) & 0xFFu);
+            const int sau = (int)((suw[j][i] >> (8 * g4)) & 0xFFu);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+              ag[i][m] = chunk_mma_mx(fg[j][i], fx[j][m], sag, ag[i][m], sx[j][m]);
+              au[i][m] = chunk_mma_mx(fu[j][i], fx[j][m], sau, au[i][m], sx[j][m]);
+            }
+          }
+        }
+      }
+    };
+    // Software-pipelined two-chunk steps: the next step's loads are in flight
+    // while this step's MFMAs run.  Needs an even chunk count, so that one
+    // 8-byte load per row brings a step's scale words.
+    struct Buf {
+      i32x4 g[2][GW], u[2][GW];
+      uint2 sg[GW], su[GW];
+      Frag x[2][MT];
+      float sx[2][MT];
+    };
+    auto load = [&](Buf &b, int c) {
+#pragma unroll
+      for (int i = 0; i < GW; ++i) {
+        b.sg[i] = *reinterpret_cast<const uint2 *>(mg[i] + 4 * c);
+        b.su[i] = *reinterpret_cast<const uint2 *>(mu[i] + 4 * c);
+      }
+      // the two chunks of a row share one 128-byte line: load them back to back
+#pragma unroll
+      for (int i = 0; i < GW; ++i) {
+        b.g[0][i] = load16(wg[i] + (int64_t)c * 64);
+        b.g[1][i] = load16(wg[i] + (int64_t)c * 64 + 64);
+      }
+#pragma unroll
+      for (int i = 0; i < GW; ++i) {
+        b.u[0][i] = load16(wu[i] + (int64_t)c * 64);
+        b.u[1][i] = load16(wu[i] + (int64_t)c * 64 + 64);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          // rows past the tile read a valid row; their scale is zeroed at use,
+          // so that nothing here waits for a load
+          b.x[j][m] = load_frag_k64(xr[m] + (int64_t)(c + j) * 128);
+          b.sx[j][m] = G.xs[(int64_t)xsrow[m] * KB + c + j];
+        }
+      }
+    };
+    auto compute = [&](const Buf &b) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < GW; ++i) {
+          const int sag = (int)(((j ? b.sg[i].y : b.sg[i].x) >> (8 * g4)) & 0xFFu);
+          const int sau = (int)(((j ? b.su[i].y : b.su[i].x) >> (8 * g4)) & 0xFFu);
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            const float sxm = xv[m] ? b.sx[j][m] : 0.f;
+            ag[i][m] = chunk_mma_mx(b.g[j][i], b.x[j][m], sag, ag[i][m], sxm);
+            au[i][m] = chunk_mma_mx(b.u[j][i], b.x[j][m], sau, au[i][m], sxm);
+          }
+        }
+    };
+    if (MX_PIPE && MT <= 2 && (nchunk & 1) == 0) {
+      Buf A, B;
+      load(A, 0);
+      int c = 0;
+      for (; c + 4 < nchunk; c += 4) {
+        load(B, c + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(A);
+        __builtin_amdgcn_sched_barrier(0);
+        load(A, c + 4);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(B);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (c + 2 < nchunk) {
+        load(B, c + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(A);
+        compute(B);
+      } else {
+        compute(A);
+      }
+    } else if (MX_NC4 && MT <= 2 && (nchunk & 3) == 0) {
+      steps(std::integral_constant<int, 4>{});
+    } else {
+      steps(std::integral_constant<int, 2>{});
     }
-    float sx[MT];
+  } else {
+    for (int c = 0; c < nchunk; ++c) {
+      const int64_t kb = (int64_t)c * 128;
+      Frag fg[GW], fu[GW], fx[MT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      fx[m] = xv[m] ? load_frag(xr[m] + kb) : zf;
-      sx[m] = (FP8 && xv[m]) ? G.xs[(int64_t)xrow[m] * KB + c] : 0.f;
-    }
-    const float swg = FP8 ? sg[c] : 0.f;
-    const float swu = FP8 ? su[c] : 0.f;
-#pragma unroll
-    for (int i = 0; i < GW; ++i)
+      for (int i = 0; i < GW; ++i) {
+        fg[i] = load_frag(wg[i] + kb);
+        fu[i] = load_frag(wu[i] + kb);
+      }
+      float sx[MT];
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        ag[i][m] = chunk_mma<FP8>(fg[i], fx[m], ag[i][m], swg * sx[m]);
-        au[i][m] = chunk_mma<FP8>(fu[i], fx[m], au[i][m], swu * sx[m]);
+        fx[m] = xv[m] ? load_frag(xr[m] + kb) : zf;
+        sx[m] = (FP8 && xv[m]) ? G.xs[(int64_t)xrow[m] * KB + c] : 0.f;
       }
+      const float swg = FP8 ? sg[c] : 0.f;
+      const float swu = FP8 ? su[c] : 0.f;
+#pragma unroll
+      for (int i = 0; i < GW; ++i)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          ag[i][m] = chunk_mma<FP8>(fg[i], fx[m], ag[i][m], swg * sx[m]);
+          au[i][m] = chunk_mma<FP8>(fu[i], fx[m], au[i][m], swu * sx[m]);
+        }
+    }
   }
 
   // Epilogue: lane holds columns hc0 + 16i + 4*(lane/16) + r of token row xrow[m].
@@ -235,71 +423,194 @@ __device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry 
   }
 }
 
-template <int MT, int GW>
+// MXK: the launch's e4m3 group carries MX FP4 weights.  The MX bodies are
+// instantiated only there, so the bf16/fp8 kernels keep their register budget.
+template <int MT, int GW, bool MXK>
 __global__ __launch_bounds__(256) void gate_up_stream_kernel(StreamArgs a) {
   if ((int)blockIdx.y >= a.ntiles[0]) return;
   const TileEntry te = a.tiles[blockIdx.y];
   const FfnGroup G = pick_group(a.g0, a.g1, te.ge >> 24);
   if ((int)blockIdx.x * 64 * GW >= G.I) return;     // group narrower than the grid
   if (G.fp8) {
-    if constexpr (GW == 2) gate_up_body<true, MT, GW>(G, te, a.H);
+    if constexpr (GW == 2) gate_up_body<true, MXK, MT, GW>(G, te, a.H);
   } else {
-    gate_up_body<false, MT, GW>(G, te, a.H);
+    gate_up_body<false, false, MT, GW>(G, te, a.H);
   }
 }
 
 // ---------------------------------------------------------------- down (streaming)
 // Workgroup: 4 waves x NW 16-column output tiles = 64*NW columns, 16*MT rows.
-template <bool FP8, int MT, int NW>
+template <bool FP8, bool MX, int MT, int NW>
 __device__ __forceinline__ void down_body(const FfnGroup &G, const TileEntry &te, int H) {
+  static_assert(FP8 || !MX, "MX weights take e4m3 activations");
   constexpr int ESZ = FP8 ? 1 : 2;
   const int lane = lane_id(), w = wave_id();
   int rbeg, rend;
   tile_rows(G, te, rbeg, rend);
   const int e = te.ge & 0xFFFFFF;
   const int I = G.I;
-  const int64_t rowb = (int64_t)I * ESZ;
+  const int64_t hrowb = (int64_t)I * ESZ;             // h row bytes
+  const int64_t wrowb = MX ? (int64_t)I / 2 : hrowb;  // weight row bytes
   const int c0 = blockIdx.x * (64 * NW) + w * (16 * NW);
-  const int koff = 32 * (lane >> 4);
-  const uint8_t *wbase = G.wd + (int64_t)e * H * rowb;
+  const int g4 = lane >> 4;
+  const int koff = MX ? 16 * g4 : 32 * g4;
+  const uint8_t *wbase = G.wd + (int64_t)e * H * wrowb;
   const uint8_t *wr[NW];
+  const uint8_t *mr[NW];   // MX: the lane's row of E8M0 scale bytes
 #pragma unroll
-  for (int i = 0; i < NW; ++i) wr[i] = wbase + (int64_t)(c0 + 16 * i + (lane & 15)) * rowb + koff;
+  for (int i = 0; i < NW; ++i) {
+    const int64_t r = c0 + 16 * i + (lane & 15);
+    wr[i] = wbase + r * wrowb + koff;
+    if constexpr (MX) mr[i] = G.md + ((int64_t)e * H + r) * (I / 32);
+  }
   const uint8_t *hr[MT];
   bool hv[MT];
-  int hrow[MT];
+  int hrow[MT], hsrow[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     hrow[m] = rbeg + 16 * m + (lane & 15);
     hv[m] = hrow[m] < rend;
-    hr[m] = G.h + (int64_t)(hv[m] ? hrow[m] : 0) * rowb + koff;
+    hsrow[m] = hv[m] ? hrow[m] : (rbeg < rend ? rbeg : 0);   // a row that exists
+    hr[m] = G.h + (int64_t)hsrow[m] * hrowb + koff;
   }
   f32x4 acc[NW][MT];
 #pragma unroll
   for (int i = 0; i < NW; ++i)
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[i][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nchunk = (int)(rowb / 128);
+  const int nchunk = (int)(hrowb / 128);
   const int KB = I / 128;
   const Frag zf = Frag{i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
-  for (int c = 0; c < nchunk; ++c) {
-    const int64_t kb = (int64_t)c * 128;
-    Frag fw[NW], fh[MT];
-    float sw[NW], sh[MT];
+  if constexpr (MX) {
+    auto steps = [&](auto nc_tag) {
+      constexpr int NC = decltype(nc_tag)::value;
+      for (int c = 0; c < nchunk; c += NC) {
+        const int nv = min(NC, nchunk - c);
+        i32x4 fw[NC][NW];
+        uint32_t sww[NC][NW];
+        Frag fh[NC][MT];
+        float sh[NC][MT];
+        if constexpr (NC == 4) {
 #pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      fw[i] = load_frag(wr[i] + kb);
-      sw[i] = FP8 ? G.sd[((int64_t)e * (H / 128) + (c0 + 16 * i) / 128) * KB + c] : 0.f;
+          for (int i = 0; i < NW; ++i) {
+            const i32x4 a = load16(mr[i] + 4 * c);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sww[j][i] = (uint32_t)a[j];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+          const int cj = j < nv ? c + j : c;   // a short last step reloads its first chunk, counted once
+#pragma unroll
+          for (int i = 0; i < NW; ++i) {
+            fw[j][i] = load16(wr[i] + (int64_t)cj * 64);
+            if constexpr (NC != 4) sww[j][i] = *reinterpret_cast<const uint32_t *>(mr[i] + 4 * cj);
+          }
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            // branch-free: rows past the tile read a valid row and are zeroed after
+            const Frag f = load_frag_k64(hr[m] + (int64_t)cj * 128);
+            const float sv = G.hs[(int64_t)hsrow[m] * KB + cj];
+            fh[j][m] = hv[m] ? f : zf;
+            sh[j][m] = hv[m] ? sv : 0.f;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+          if (j >= nv) break;
+#pragma unroll
+          for (int i = 0; i < NW; ++i) {
+            const int sa = (int)((sww[j][i] >> (8 * g4)) & 0xFFu);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[i][m] = chunk_mma_mx(fw[j][i], fh[j][m], sa, acc[i][m], sh[j][m]);
+          }
+        }
+      }
+    };
+    struct Buf {
+      i32x4 w[2][NW];
+      uint2 s[NW];
+      Frag h[2][MT];
+      float sh[2][MT];
+    };
+    auto load = [&](Buf &b, int c) {
+#pragma unroll
+      for (int i = 0; i < NW; ++i) b.s[i] = *reinterpret_cast<const uint2 *>(mr[i] + 4 * c);
+      // the two chunks of a row share one 128-byte line: load them back to back
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        b.w[0][i] = load16(wr[i] + (int64_t)c * 64);
+        b.w[1][i] = load16(wr[i] + (int64_t)c * 64 + 64);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          // rows past the tile read a valid row; their scale is zeroed at use
+          b.h[j][m] = load_frag_k64(hr[m] + (int64_t)(c + j) * 128);
+          b.sh[j][m] = G.hs[(int64_t)hsrow[m] * KB + c + j];
+        }
+      }
+    };
+    auto compute = [&](const Buf &b) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+          const int sa = (int)(((j ? b.s[i].y : b.s[i].x) >> (8 * g4)) & 0xFFu);
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+            acc[i][m] = chunk_mma_mx(b.w[j][i], b.h[j][m], sa, acc[i][m], hv[m] ? b.sh[j][m] : 0.f);
+        }
+    };
+    if (MX_PIPE && MT <= 2 && (nchunk & 1) == 0) {
+      Buf A, B;
+      load(A, 0);
+      int c = 0;
+      for (; c + 4 < nchunk; c += 4) {
+        load(B, c + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(A);
+        __builtin_amdgcn_sched_barrier(0);
+        load(A, c + 4);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(B);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (c + 2 < nchunk) {
+        load(B, c + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(A);
+        compute(B);
+      } else {
+        compute(A);
+      }
+    } else if (MX_NC4 && MT <= 2 && (nchunk & 3) == 0) {
+      steps(std::integral_constant<int, 4>{});
+    } else {
+      steps(std::integral_constant<int, 2>{});
     }
+  } else {
+    for (int c = 0; c < nchunk; ++c) {
+      const int64_t kb = (int64_t)c * 128;
+      Frag fw[NW], fh[MT];
+      float sw[NW], sh[MT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      fh[m] = hv[m] ? load_frag(hr[m] + kb) : zf;
-      sh[m] = (FP8 && hv[m]) ? G.hs[(int64_t)hrow[m] * KB + c] : 0.f;
+      for (int i = 0; i < NW; ++i) {
+        fw[i] = load_frag(wr[i] + kb);
+        sw[i] = FP8 ? G.sd[((int64_t)e * (H / 128) + (c0 + 16 * i) / 128) * KB + c] : 0.f;
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        fh[m] = hv[m] ? load_frag(hr[m] + kb) : zf;
+        sh[m] = (FP8 && hv[m]) ? G.hs[(int64_t)hrow[m] * KB + c] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < NW; ++i)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[i][m] = chunk_mma<FP8>(fw[i], fh[m], acc[i][m], sw[i] * sh[m]);
     }
-#pragma unroll
-    for (int i = 0; i < NW; ++i)
-#pragma unroll
-      for (int m = 0; m < MT; ++m) acc[i][m] = chunk_mma<FP8>(fw[i], fh[m], acc[i][m], sw[i] * sh[m]);
   }
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
@@ -319,15 +630,15 @@ __device__ __forceinline__ void down_body(const FfnGroup &G, const TileEntry &te
   }
 }
 
-template <int MT, int NW>
+template <int MT, int NW, bool MXK>
 __global__ __launch_bounds__(256) void down_stream_kernel(StreamArgs a) {
   if ((int)blockIdx.y >= a.ntiles[0]) return;
   const TileEntry te = a.tiles[blockIdx.y];
   const FfnGroup G = pick_group(a.g0, a.g1, te.ge >> 24);
   if (G.fp8)
-    down_body<true, MT, NW>(G, te, a.H);
+    down_body<true, MXK, MT, NW>(G, te, a.H);
   else
-    down_body<false, MT, NW>(G, te, a.H);
+    down_body<false, false, MT, NW>(G, te, a.H);
 }
 
 // ---------------------------------------------------------------- host side
@@ -350,7 +661,10 @@ FfnPlan ffn_plan(const FfnGroup *g, int ngroups) {
   p.mt = avg <= 16 ? 1 : (avg <= 32 ? 2 : 4);
   p.gw = all128 ? 2 : 1;
   // many rows per expert: the LDS-tiled kernels (weights reused across 128 tokens)
-  p.tiled = (all128 && g[0].nrows > 0 && avg >= 48.0) ? 1 : 0;
+  // (MX weights run on the streaming kernels only)
+  bool any_mx = false;
+  for (int i = 0; i < ngroups; ++i) any_mx = any_mx || g[i].mx;
+  p.tiled = (all128 && !any_mx && g[0].nrows > 0 && avg >= 48.0) ? 1 : 0;
   p.bm = p.tiled ? 128 : 16 * p.mt;
   int64_t cap = 1;
   for (int i = 0; i < ngroups; ++i) cap += cdiv(g[i].nrows, p.bm) + std::min<int64_t>(g[i].nrows, g[i].E);
@@ -364,20 +678,20 @@ size_t ffn_tiles_bytes(const FfnPlan &p) {
   return align_up(sizeof(TileEntry) * (size_t)p.max_tiles + kTileHdrWords * sizeof(int32_t), 256);
 }
 
-template <int MT>
+template <int MT, bool MXK>
 static void run_stream(const StreamArgs &a, const FfnPlan &plan, int maxI, int site, hipStream_t st) {
   timing_before(site, st);
   if (plan.gw == 2) {
     dim3 g1((unsigned)cdiv(maxI, 128), (unsigned)plan.max_tiles);
-    gate_up_stream_kernel<MT, 2><<<g1, 256, 0, st>>>(a);
+    gate_up_stream_kernel<MT, 2, MXK><<<g1, 256, 0, st>>>(a);
   } else {
     dim3 g1((unsigned)cdiv(maxI, 64), (unsigned)plan.max_tiles);
-    gate_up_stream_kernel<MT, 1><<<g1, 256, 0, st>>>(a);
+    gate_up_stream_kernel<MT, 1, false><<<g1, 256, 0, st>>>(a);
   }
   timing_after(site, st);
   dim3 g2((unsigned)(a.H / 128), (unsigned)plan.max_tiles);
   timing_before(site + 1, st);
-  down_stream_kernel<MT, 2><<<g2, 256, 0, st>>>(a);
+  down_stream_kernel<MT, 2, MXK><<<g2, 256, 0, st>>>(a);
   timing_after(site + 1, st);
 }
 
@@ -386,11 +700,17 @@ hipError_t launch_expert_ffn(const FfnGroup *g, int ngroups, int H, const FfnPla
   if (ngroups < 1 || ngroups > kMaxGroups) return hipErrorInvalidValue;
   int64_t rows = 0;
   int maxI = 0;
+  bool mx = false, fp8_plain = false;
   for (int i = 0; i < ngroups; ++i) {
     rows += g[i].nrows;
     maxI = std::max(maxI, (int)g[i].I);
     if (g[i].fp8 && plan.gw != 2) return hipErrorInvalidValue;
+    if (g[i].mx && !g[i].fp8) return hipErrorInvalidValue;
+    mx = mx || g[i].mx;
+    fp8_plain = fp8_plain || (g[i].fp8 && !g[i].mx);
   }
+  // one launch holds either MX or block-scaled fp8 weights (plus bf16 groups)
+  if (mx && (fp8_plain || plan.tiled)) return hipErrorInvalidValue;
   if (rows == 0) return hipSuccess;
   int32_t *hdr = tiles_ws;
   TileEntry *tiles = reinterpret_cast<TileEntry *>(tiles_ws + kTileHdrWords);
@@ -400,10 +720,13 @@ hipError_t launch_expert_ffn(const FfnGroup *g, int ngroups, int H, const FfnPla
     if (H % 256 != 0) return hipErrorInvalidValue;
     return launch_tiled_ffn(g, ngroups, H, tiles, hdr, num_compute_units(), site, st);
   }
-  switch (plan.mt) {
-    case 1: run_stream<1>(a, plan, maxI, site, st); break;
-    case 2: run_stream<2>(a, plan, maxI, site, st); break;
-    case 4: run_stream<4>(a, plan, maxI, site, st); break;
+  switch (plan.mt * 2 + (mx ? 1 : 0)) {
+    case 2: run_stream<1, false>(a, plan, maxI, site, st); break;
+    case 4: run_stream<2, false>(a, plan, maxI, site, st); break;
+    case 8: run_stream<4, false>(a, plan, maxI, site, st); break;
+    case 3: run_stream<1, true>(a, plan, maxI, site, st); break;
+    case 5: run_stream<2, true>(a, plan, maxI, site, st); break;
+    case 9: run_stream<4, true>(a, plan, maxI, site, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

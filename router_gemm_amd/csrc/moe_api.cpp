@@ -43,7 +43,9 @@ constexpr int kMaxI = 16384;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-bool is_fp8(const moe_layer *L) { return L->expert_dtype == MOE_FP8_E4M3FN; }
+// Activations and h are e4m3 + 1x128 scales for fp8 and MX FP4 experts.
+bool is_fp8(const moe_layer *L) { return L->expert_dtype == MOE_FP8_E4M3FN || L->expert_dtype == MOE_MXFP4_E2M1; }
+bool is_mx(const moe_layer *L) { return L->expert_dtype == MOE_MXFP4_E2M1; }
 size_t esz(const moe_layer *L) { return is_fp8(L) ? 1 : 2; }
 
 // Sequential carving of the caller's workspace.
@@ -66,15 +68,16 @@ moe_status check_layer_shape(const moe_layer *L, bool need_router) {
   if (L->hidden <= 0 || L->inter <= 0 || L->num_experts <= 0 || L->shared_inter < 0)
     return fail(MOE_EINVAL, "bad layer dimensions H=%d I=%d E=%d Is=%d", L->hidden, L->inter,
                 L->num_experts, L->shared_inter);
-  if (L->expert_dtype != MOE_BF16 && L->expert_dtype != MOE_FP8_E4M3FN)
-    return fail(MOE_EUNSUPPORTED, "expert_dtype %d is not MOE_BF16 or MOE_FP8_E4M3FN", L->expert_dtype);
+  if (L->expert_dtype != MOE_BF16 && L->expert_dtype != MOE_FP8_E4M3FN && L->expert_dtype != MOE_MXFP4_E2M1)
+    return fail(MOE_EUNSUPPORTED, "expert_dtype %d is not MOE_BF16, MOE_FP8_E4M3FN or MOE_MXFP4_E2M1",
+                L->expert_dtype);
   if (L->hidden % 128 != 0 || L->hidden > kMaxH)
     return fail(MOE_EUNSUPPORTED, "hidden %d must be a multiple of 128 and <= %d", L->hidden, kMaxH);
   if (L->num_experts > kMaxE) return fail(MOE_EUNSUPPORTED, "num_experts %d > %d", L->num_experts, kMaxE);
   if (L->inter > kMaxI || L->shared_inter > kMaxI)
     return fail(MOE_EUNSUPPORTED, "inter %d / shared_inter %d > %d", L->inter, L->shared_inter, kMaxI);
   if (is_fp8(L) && L->inter % 128 != 0)
-    return fail(MOE_EUNSUPPORTED, "fp8 experts need inter %% 128 == 0 (inter=%d)", L->inter);
+    return fail(MOE_EUNSUPPORTED, "fp8 and mxfp4 experts need inter %% 128 == 0 (inter=%d)", L->inter);
   if (!is_fp8(L) && L->inter % 64 != 0)
     return fail(MOE_EUNSUPPORTED, "bf16 experts need inter %% 64 == 0 (inter=%d)", L->inter);
   if (L->shared_inter % 64 != 0)
@@ -88,7 +91,10 @@ moe_status check_layer_shape(const moe_layer *L, bool need_router) {
 moe_status check_expert_weights(const moe_layer *L) {
   if (!L->w_gate_up || !L->w_down) return fail(MOE_EINVAL, "expert weights are NULL");
   if (!aligned16(L->w_gate_up) || !aligned16(L->w_down)) return fail(MOE_EINVAL, "expert weights not 16-byte aligned");
-  if (is_fp8(L) && (!L->s_gate_up || !L->s_down)) return fail(MOE_EINVAL, "fp8 experts need s_gate_up and s_down");
+  if (is_fp8(L) && (!L->s_gate_up || !L->s_down))
+    return fail(MOE_EINVAL, "fp8 and mxfp4 experts need s_gate_up and s_down");
+  if (is_mx(L) && (!aligned16(L->s_gate_up) || !aligned16(L->s_down)))
+    return fail(MOE_EINVAL, "mxfp4 scale tensors not 16-byte aligned");
   return MOE_OK;
 }
 
@@ -158,15 +164,21 @@ moe::FfnGroup routed_group(const moe_layer *L, const void *x_perm, const float *
   g.x = static_cast<const uint8_t *>(x_perm);
   g.xs = x_scale;
   g.wgu = static_cast<const uint8_t *>(L->w_gate_up);
-  g.sgu = L->s_gate_up;
   g.wd = static_cast<const uint8_t *>(L->w_down);
-  g.sd = L->s_down;
+  if (is_mx(L)) {
+    g.mgu = static_cast<const uint8_t *>(L->s_gate_up);
+    g.md = static_cast<const uint8_t *>(L->s_down);
+  } else {
+    g.sgu = static_cast<const float *>(L->s_gate_up);
+    g.sd = static_cast<const float *>(L->s_down);
+  }
   g.off = off;
   g.y = y;
   g.E = L->num_experts;
   g.I = L->inter;
   g.nrows = (int32_t)N;
   g.fp8 = is_fp8(L) ? 1 : 0;
+  g.mx = is_mx(L) ? 1 : 0;
   g.y_f32 = y_f32 ? 1 : 0;
   return g;
 }

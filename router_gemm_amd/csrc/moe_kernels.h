@@ -47,7 +47,7 @@ hipError_t launch_fill_offsets2(int32_t *dst, int32_t n, hipStream_t st);
 // launch covers up to two groups (the routed experts and the shared expert),
 // so the shared expert's tiles run inside the routed experts' launch.
 struct FfnGroup {
-  const uint8_t *x;    // [nrows, H] rows in expert order: e4m3 codes (fp8) or bf16
+  const uint8_t *x;    // [nrows, H] rows in expert order: e4m3 codes (fp8, mx) or bf16
   const float *xs;     // [nrows, H/128] (fp8)
   const uint8_t *wgu;  // [E, 2I, H]: rows 0..I-1 gate, I..2I-1 up
   const float *sgu;    // [E, 2I/128, H/128] (fp8)
@@ -57,7 +57,12 @@ struct FfnGroup {
   uint8_t *h;          // [nrows, I] intermediate: e4m3 (fp8) or bf16
   float *hs;           // [nrows, I/128] (fp8)
   void *y;             // [nrows, H] output, bf16 or f32
-  int32_t E, I, nrows, fp8, y_f32;
+  // MX FP4 weights (mx = 1): wgu [E, 2I, H/2] and wd [E, H, I/2] hold two
+  // E2M1 codes per byte, mgu [E, 2I, H/32] and md [E, H, I/32] one E8M0
+  // scale byte per 32 inputs of a row; x and h are e4m3 as in fp8 mode.
+  const uint8_t *mgu;
+  const uint8_t *md;
+  int32_t E, I, nrows, fp8, y_f32, mx;
   // Optional (tiled kernels only): row r of the GEMM input is row
   // xsrc[r] / xdiv of x (and xs), so the rows need not be gathered first.
   const int32_t *xsrc;

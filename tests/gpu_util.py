@@ -10,7 +10,7 @@ import oracle
 from router_gemm_amd import binding as B
 from router_gemm_amd import workloads as W
 
-TOL = {"bf16": 2e-2, "fp8": 4e-2}   # max relative error (per-token inf-norm) vs the fp64 oracle
+TOL = {"bf16": 2e-2, "fp8": 4e-2, "mxfp4": 4e-2}   # max relative error (per-token inf-norm) vs the fp64 oracle
 TIE_GAP = 1e-4                       # exemption: k-th and (k+1)-th oracle logits closer than this
 
 

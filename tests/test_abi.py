@@ -54,6 +54,9 @@ def test_status_strings():
     (dict(H=0), B.MOE_EINVAL), (dict(E=-1), B.MOE_EINVAL),
     (dict(H=16384 + 128), B.MOE_EUNSUPPORTED), (dict(I=16384 + 128), B.MOE_EUNSUPPORTED),
     (dict(Is=16384 + 64), B.MOE_EUNSUPPORTED), (dict(H=16384, I=16384, Is=16384), B.MOE_OK),
+    (dict(dtype=B.MOE_MXFP4_E2M1), B.MOE_OK),
+    (dict(dtype=B.MOE_MXFP4_E2M1, I=1600), B.MOE_EUNSUPPORTED),      # mxfp4 needs I % 128 == 0
+    (dict(dtype=B.MOE_MXFP4_E2M1, H=4000), B.MOE_EUNSUPPORTED),
 ])
 def test_layer_validation(kw, status):
     L = layer(**kw)
@@ -114,3 +117,17 @@ def test_timing_sites_validate_without_gpu():
     ms, n = C.c_double(1.0), C.c_int32(7)
     assert lib.moe_timing_read(5, C.byref(ms), C.byref(n)) == B.MOE_OK
     assert ms.value == 0.0 and n.value == 0
+
+
+def test_mxfp4_scale_refusals():
+    """MX FP4 layers need both E8M0 scale tensors, 16-byte aligned."""
+    lib = B.lib()
+    for sgu, sd, what in ((None, FAKE, b"s_gate_up"), (FAKE, None, b"s_gate_up"), (FAKE + 4, FAKE, b"aligned"),
+                          (FAKE, FAKE + 8, b"aligned")):
+        L = B.MoELayerC(4096, 1536, 352, 8, 0, B.MOE_MXFP4_E2M1, FAKE, None, FAKE, sgu, FAKE, sd, None, None)
+        r = lib.moe_expert_ffn(C.byref(L), FAKE, FAKE, FAKE, 100, FAKE, B.MOE_F32, FAKE, 1 << 40, None)
+        assert r == B.MOE_EINVAL and what in lib.moe_last_error(), lib.moe_last_error()
+    # activations of an mxfp4 layer are e4m3 with 1x128 scales: x_scale is required
+    L = layer(dtype=B.MOE_MXFP4_E2M1)
+    r = lib.moe_permute(C.byref(L), FAKE, 64, FAKE, None, 512, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None)
+    assert r == B.MOE_EINVAL and b"x_scale" in lib.moe_last_error()

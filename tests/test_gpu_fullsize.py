@@ -1,5 +1,5 @@
 """GPU parity at the full Step-5 layer sizes, in the launch configuration the
-benchmark times: decode T=64 (bf16 and FP8 experts), prefill T=8192 with the
+benchmark times: decode T=64 (bf16, FP8 and MX FP4 experts), prefill T=8192 with the
 Zipf-biased router (FP8), and one expert-parallel share driven through the four
 primitives with pre-routed triples.  Routing, grouping and the fp8 x_perm bytes
 are checked for every token; outputs on every token where the oracle is quick
@@ -18,7 +18,7 @@ from gpu_util import TOL, check_forward, check_ids, dev, oracle_layer, rel_err_r
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
 
-@pytest.mark.parametrize("name", ["c1", "c2"])
+@pytest.mark.parametrize("name", ["c1", "c2", "decode_mxfp4"])
 def test_decode_full_parity(name):
     cfg = W.get_config(name)
     print(f"[{cfg.name}] building layer", flush=True)
