@@ -45,6 +45,9 @@ namespace moe {
 #ifndef MX_PIPE
 #define MX_PIPE 1  // MX loops: software-pipelined two-chunk steps where K allows
 #endif
+#ifndef MX_LDS
+#define MX_LDS 1   // MX loops: weight codes staged through LDS by whole-line copies
+#endif
 
 __device__ __forceinline__ FfnGroup pick_group(const FfnGroup &g0, const FfnGroup &g1, int g) {
   return g ? g1 : g0;
@@ -129,6 +132,41 @@ __device__ __forceinline__ f32x4 chunk_mma_mx(const i32x4 &a, const Frag &b, int
 // 16g..16g+15 and 64+16g..64+16g+15 of the chunk for lane group g
 // (p points at the chunk start + 16g).
 __device__ __forceinline__ Frag load_frag_k64(const uint8_t *p) { return Frag{load16(p), load16(p + 64)}; }
+
+// LDS reads of staged MX weight fragments, written as one asm block that
+// waits for its own results.  The compiler cannot tell these buffers apart
+// from the ones the direct-to-LDS copies are still filling, so LDS reads it
+// can see make it wait for every copy in flight; the callers instead wait
+// with vmcnt for exactly the copies into the buffer they read.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
+}
+// r[4j + t] = 16 bytes at a_j + 2048 t (t = 0..3, j = 0..1).
+__device__ __forceinline__ void lds_read_2x4(uint32_t a0, uint32_t a1, i32x4 (&r)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:2048\n\t"
+      "ds_read_b128 %2, %8 offset:4096\n\t"
+      "ds_read_b128 %3, %8 offset:6144\n\t"
+      "ds_read_b128 %4, %9\n\t"
+      "ds_read_b128 %5, %9 offset:2048\n\t"
+      "ds_read_b128 %6, %9 offset:4096\n\t"
+      "ds_read_b128 %7, %9 offset:6144\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a0), "v"(a1));
+}
+// r[2j + t] = 16 bytes at a_j + 2048 t (t = 0..1, j = 0..1).
+__device__ __forceinline__ void lds_read_2x2(uint32_t a0, uint32_t a1, i32x4 (&r)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:2048\n\t"
+      "ds_read_b128 %2, %5\n\t"
+      "ds_read_b128 %3, %5 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(a0), "v"(a1));
+}
 
 struct StreamArgs {
   FfnGroup g0, g1;
@@ -313,7 +351,119 @@ __device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry 
           }
         }
     };
-    if (MX_PIPE && MT <= 2 && (nchunk & 1) == 0) {
+    if (MX_LDS && MT <= 2 && (nchunk & 1) == 0) {
+      // Weight codes go through LDS.  A 16x16x128 fp4 fragment gives a row
+      // only 64 bytes per load instruction (half a 128-byte line, so every L1
+      // miss moves half a line); a direct-to-LDS copy instead moves 8 rows x
+      // one whole line (two chunks) per instruction.  Each wave owns two 8 KB
+      // buffers (its 2*GW tiles x 16 rows x 128 bytes), 16-byte columns
+      // XOR-swizzled by row % 8; no other wave touches them, so no barriers.
+      // (two separate arrays, so that alias analysis sees that reading one
+      // buffer never waits for the copies into the other)
+      __shared__ __attribute__((aligned(16))) uint8_t wlds0[4][2 * GW][2048];
+      __shared__ __attribute__((aligned(16))) uint8_t wlds1[4][2 * GW][2048];
+      const uint8_t *tb[2 * GW];
+#pragma unroll
+      for (int i = 0; i < GW; ++i) {
+        tb[i] = wbase + (int64_t)(hc0 + 16 * i) * wrowb;
+        tb[GW + i] = wbase + (int64_t)(I + hc0 + 16 * i) * wrowb;
+      }
+      const int sr = lane >> 3;
+      const uint32_t coff0 = (uint32_t)(sr * wrowb + 16 * ((lane & 7) ^ sr));
+      const uint32_t coff1 = coff0 + (uint32_t)(8 * wrowb);
+      auto copy = [&](uint8_t *buf, int c) {
+#pragma unroll
+        for (int t = 0; t < 2 * GW; ++t) {
+          const uint8_t *src = tb[t] + (int64_t)c * 64;
+          dma16(src + coff0, buf + t * 2048);
+          dma16(src + coff1, buf + t * 2048 + 1024);
+        }
+      };
+      struct XB {
+        uint2 sg[GW], su[GW];
+        Frag x[2][MT];
+        float sx[2][MT];
+      };
+      auto loadx = [&](XB &b, int c) {
+#pragma unroll
+        for (int i = 0; i < GW; ++i) {
+          b.sg[i] = *reinterpret_cast<const uint2 *>(mg[i] + 4 * c);
+          b.su[i] = *reinterpret_cast<const uint2 *>(mu[i] + 4 * c);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            b.x[j][m] = load_frag_k64(xr[m] + (int64_t)(c + j) * 128);
+            b.sx[j][m] = G.xs[(int64_t)xsrow[m] * KB + c + j];
+          }
+      };
+      const int rho = lane & 15;
+      static_assert(GW == 2, "the staged MX gate/up path reads 2 x 4 tiles");
+      auto compute = [&](const uint8_t *buf, const XB &b) {
+        i32x4 fr[8];
+        lds_read_2x4(lds_addr(buf + rho * 128 + 16 * ((0 + g4) ^ (rho & 7))),
+                     lds_addr(buf + rho * 128 + 16 * ((4 + g4) ^ (rho & 7))), fr);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < GW; ++i) {
+            const i32x4 fgv = fr[4 * j + i];
+            const i32x4 fuv = fr[4 * j + GW + i];
+            const int sag = (int)(((j ? b.sg[i].y : b.sg[i].x) >> (8 * g4)) & 0xFFu);
+            const int sau = (int)(((j ? b.su[i].y : b.su[i].x) >> (8 * g4)) & 0xFFu);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+              const float sxm = xv[m] ? b.sx[j][m] : 0.f;
+              ag[i][m] = chunk_mma_mx(fgv, b.x[j][m], sag, ag[i][m], sxm);
+              au[i][m] = chunk_mma_mx(fuv, b.x[j][m], sau, au[i][m], sxm);
+            }
+          }
+      };
+      // Each step issues its token loads first and its 4*GW copies last, so
+      // "all but the last 4*GW vector-memory instructions done" means the
+      // previous step's copies have landed.
+      uint8_t *const B0 = &wlds0[w][0][0];
+      uint8_t *const B1 = &wlds1[w][0][0];
+      constexpr int COPIES = 4 * GW;
+      XB X0, X1;
+      loadx(X0, 0);
+      copy(B0, 0);
+      // the token loads of the first step done before the loop, as they are
+      // on the way round it (a loop-carried load still in flight on one path
+      // makes the compiler wait for everything at the top of the loop)
+      wait_vm<COPIES>();
+      int c = 0;
+      for (; c + 4 < nchunk; c += 4) {
+        loadx(X1, c + 2);
+        copy(B1, c + 2);
+        wait_vm<COPIES>();
+        __builtin_amdgcn_sched_barrier(0);
+        compute(B0, X0);
+        __builtin_amdgcn_sched_barrier(0);
+        loadx(X0, c + 4);
+        copy(B0, c + 4);
+        wait_vm<COPIES>();
+        __builtin_amdgcn_sched_barrier(0);
+        compute(B1, X1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (c + 2 < nchunk) {
+        loadx(X1, c + 2);
+        copy(B1, c + 2);
+        wait_vm<COPIES>();
+        __builtin_amdgcn_sched_barrier(0);
+        compute(B0, X0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<0>();
+        __builtin_amdgcn_sched_barrier(0);
+        compute(B1, X1);
+      } else {
+        wait_vm<0>();
+        __builtin_amdgcn_sched_barrier(0);
+        compute(B0, X0);
+      }
+    } else if (MX_PIPE && MT <= 2 && (nchunk & 1) == 0) {
       Buf A, B;
       load(A, 0);
       int c = 0;
@@ -564,7 +714,100 @@ __device__ __forceinline__ void down_body(const FfnGroup &G, const TileEntry &te
             acc[i][m] = chunk_mma_mx(b.w[j][i], b.h[j][m], sa, acc[i][m], hv[m] ? b.sh[j][m] : 0.f);
         }
     };
-    if (MX_PIPE && MT <= 2 && (nchunk & 1) == 0) {
+    if (MX_LDS && MT <= 2 && (nchunk & 1) == 0) {
+      // Weight codes through LDS, as in the gate/up kernel: each copy
+      // instruction moves 8 rows x one whole 128-byte line; two 4 KB buffers
+      // per wave, private to it.
+      __shared__ __attribute__((aligned(16))) uint8_t wlds0[4][NW][2048];
+      __shared__ __attribute__((aligned(16))) uint8_t wlds1[4][NW][2048];
+      const uint8_t *tb[NW];
+#pragma unroll
+      for (int i = 0; i < NW; ++i) tb[i] = wbase + (int64_t)(c0 + 16 * i) * wrowb;
+      const int sr = lane >> 3;
+      const uint32_t coff0 = (uint32_t)(sr * wrowb + 16 * ((lane & 7) ^ sr));
+      const uint32_t coff1 = coff0 + (uint32_t)(8 * wrowb);
+      auto copy = [&](uint8_t *buf, int c) {
+#pragma unroll
+        for (int t = 0; t < NW; ++t) {
+          const uint8_t *src = tb[t] + (int64_t)c * 64;
+          dma16(src + coff0, buf + t * 2048);
+          dma16(src + coff1, buf + t * 2048 + 1024);
+        }
+      };
+      struct XB {
+        uint2 s[NW];
+        Frag h[2][MT];
+        float sh[2][MT];
+      };
+      auto loadx = [&](XB &b, int c) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) b.s[i] = *reinterpret_cast<const uint2 *>(mr[i] + 4 * c);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            b.h[j][m] = load_frag_k64(hr[m] + (int64_t)(c + j) * 128);
+            b.sh[j][m] = G.hs[(int64_t)hsrow[m] * KB + c + j];
+          }
+      };
+      const int rho = lane & 15;
+      static_assert(NW == 2, "the staged MX down path reads 2 x 2 tiles");
+      auto compute = [&](const uint8_t *buf, const XB &b) {
+        i32x4 fr[4];
+        lds_read_2x2(lds_addr(buf + rho * 128 + 16 * ((0 + g4) ^ (rho & 7))),
+                     lds_addr(buf + rho * 128 + 16 * ((4 + g4) ^ (rho & 7))), fr);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < NW; ++i) {
+            const i32x4 fw = fr[2 * j + i];
+            const int sa = (int)(((j ? b.s[i].y : b.s[i].x) >> (8 * g4)) & 0xFFu);
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+              acc[i][m] = chunk_mma_mx(fw, b.h[j][m], sa, acc[i][m], hv[m] ? b.sh[j][m] : 0.f);
+          }
+      };
+      uint8_t *const B0 = &wlds0[w][0][0];
+      uint8_t *const B1 = &wlds1[w][0][0];
+      constexpr int COPIES = 2 * NW;
+      XB X0, X1;
+      loadx(X0, 0);
+      copy(B0, 0);
+      // the token loads of the first step done before the loop, as they are
+      // on the way round it (a loop-carried load still in flight on one path
+      // makes the compiler wait for everything at the top of the loop)
+      wait_vm<COPIES>();
+      int c = 0;
+      for (; c + 4 < nchunk; c += 4) {
+        loadx(X1, c + 2);
+        copy(B1, c + 2);
+        wait_vm<COPIES>();
+        __builtin_amdgcn_sched_barrier(0);
+        compute(B0, X0);
+        __builtin_amdgcn_sched_barrier(0);
+        loadx(X0, c + 4);
+        copy(B0, c + 4);
+        wait_vm<COPIES>();
+        __builtin_amdgcn_sched_barrier(0);
+        compute(B1, X1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (c + 2 < nchunk) {
+        loadx(X1, c + 2);
+        copy(B1, c + 2);
+        wait_vm<COPIES>();
+        __builtin_amdgcn_sched_barrier(0);
+        compute(B0, X0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<0>();
+        __builtin_amdgcn_sched_barrier(0);
+        compute(B1, X1);
+      } else {
+        wait_vm<0>();
+        __builtin_amdgcn_sched_barrier(0);
+        compute(B0, X0);
+      }
+    } else if (MX_PIPE && MT <= 2 && (nchunk & 1) == 0) {
       Buf A, B;
       load(A, 0);
       int c = 0;

@@ -38,6 +38,8 @@ def _grouped_e4m3_rows(E, N, H, rng, empty_frac=0.3):
     (3, 2000, 384, 128, torch.bfloat16),    # ~667: 64-row tiles; 3 and 1 chunks of 128 inputs (odd)
     (8, 517, 640, 384, torch.bfloat16),     # 5 and 3 chunks
     (1, 100, 512, 1536, torch.float32),     # one expert, the routed width
+    (32, 150, 768, 640, torch.float32),     # 16-row tiles: 6 gate/up chunks (pipelined steps + a lone last step), 5 down chunks
+    (8, 200, 1024, 512, torch.bfloat16),    # 32-row tiles: 8 and 4 chunks
 ])
 def test_mx_expert_ffn_matches_oracle(E, N, H, I, ydt):
     rng = np.random.default_rng(E * N + H)
