@@ -24,7 +24,10 @@
 // are applied inside the instruction; the E4M3 B operand is read in the
 // instruction's own K order (lane group g: inputs 16g..16g+15 and
 // 64+16g..64+16g+15), and the token's fp32 group scale multiplies the chunk
-// product afterwards as in fp8 mode.
+// product afterwards as in fp8 mode.  Such a fragment is only 64 bytes of a
+// row per load instruction (half a 128-byte line), so for 16- and 32-row
+// token tiles the codes are staged through LDS by direct-to-LDS copies that
+// move 8 rows x a whole line per instruction (see the gate/up body).
 //
 // Work decomposition.  A device-built list holds one entry per (expert,
 // 16*MT-row tile of that expert's rows); blockIdx.y indexes it (entries past
@@ -32,22 +35,11 @@
 // The host never reads the per-expert counts.
 
 #include <algorithm>
-#include <type_traits>
 
 #include "moe_common.h"
 #include "moe_kernels.h"
 
 namespace moe {
-
-#ifndef MX_NC4
-#define MX_NC4 1   // MX loops: four-chunk steps where K allows (else two-chunk steps)
-#endif
-#ifndef MX_PIPE
-#define MX_PIPE 1  // MX loops: software-pipelined two-chunk steps where K allows
-#endif
-#ifndef MX_LDS
-#define MX_LDS 1   // MX loops: weight codes staged through LDS by whole-line copies
-#endif
 
 __device__ __forceinline__ FfnGroup pick_group(const FfnGroup &g0, const FfnGroup &g1, int g) {
   return g ? g1 : g0;
@@ -237,39 +229,26 @@ __device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry 
   const Frag zf = Frag{i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
 
   if constexpr (MX) {
-    // NC chunks per step, every load of a step issued before its first MFMA.
-    // With NC == 4 (K a multiple of 512) one 16-byte load per row brings the
-    // scale words of all four chunks.
-    auto steps = [&](auto nc_tag) {
-      constexpr int NC = decltype(nc_tag)::value;
-      for (int c = 0; c < nchunk; c += NC) {
-        const int nv = min(NC, nchunk - c);
-        i32x4 fg[NC][GW], fu[NC][GW];
-        uint32_t sgw[NC][GW], suw[NC][GW];
-        Frag fx[NC][MT];
-        float sx[NC][MT];
-        if constexpr (NC == 4) {
+    // Fallback for shapes the staged loop below does not take (64-row token
+    // tiles, an odd chunk count): two-chunk steps with fragments loaded
+    // straight into registers, every load of a step issued before its first
+    // MFMA.
+    auto plain_steps = [&]() {
+      for (int c = 0; c < nchunk; c += 2) {
+        const int nv = min(2, nchunk - c);
+        i32x4 fg[2][GW], fu[2][GW];
+        uint32_t sgw[2][GW], suw[2][GW];
+        Frag fx[2][MT];
+        float sx[2][MT];
 #pragma unroll
-          for (int i = 0; i < GW; ++i) {
-            const i32x4 a = load16(mg[i] + 4 * c), b = load16(mu[i] + 4 * c);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              sgw[j][i] = (uint32_t)a[j];
-              suw[j][i] = (uint32_t)b[j];
-            }
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < NC; ++j) {
-          const int cj = j < nv ? c + j : c;   // a short last step reloads its first chunk, counted once
+        for (int j = 0; j < 2; ++j) {
+          const int cj = j < nv ? c + j : c;   // a lone last chunk is loaded twice, counted once
 #pragma unroll
           for (int i = 0; i < GW; ++i) {
             fg[j][i] = load16(wg[i] + (int64_t)cj * 64);
             fu[j][i] = load16(wu[i] + (int64_t)cj * 64);
-            if constexpr (NC != 4) {
-              sgw[j][i] = *reinterpret_cast<const uint32_t *>(mg[i] + 4 * cj);
-              suw[j][i] = *reinterpret_cast<const uint32_t *>(mu[i] + 4 * cj);
-            }
+            sgw[j][i] = *reinterpret_cast<const uint32_t *>(mg[i] + 4 * cj);
+            suw[j][i] = *reinterpret_cast<const uint32_t *>(mu[i] + 4 * cj);
           }
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
@@ -284,7 +263,7 @@ __device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry 
         // otherwise interleaves load, wait, MFMA and loses the overlap)
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < NC; ++j) {
+        for (int j = 0; j < 2; ++j) {
           if (j >= nv) break;
 #pragma unroll
           for (int i = 0; i < GW; ++i) {
@@ -299,59 +278,7 @@ __device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry 
         }
       }
     };
-    // Software-pipelined two-chunk steps: the next step's loads are in flight
-    // while this step's MFMAs run.  Needs an even chunk count, so that one
-    // 8-byte load per row brings a step's scale words.
-    struct Buf {
-      i32x4 g[2][GW], u[2][GW];
-      uint2 sg[GW], su[GW];
-      Frag x[2][MT];
-      float sx[2][MT];
-    };
-    auto load = [&](Buf &b, int c) {
-#pragma unroll
-      for (int i = 0; i < GW; ++i) {
-        b.sg[i] = *reinterpret_cast<const uint2 *>(mg[i] + 4 * c);
-        b.su[i] = *reinterpret_cast<const uint2 *>(mu[i] + 4 * c);
-      }
-      // the two chunks of a row share one 128-byte line: load them back to back
-#pragma unroll
-      for (int i = 0; i < GW; ++i) {
-        b.g[0][i] = load16(wg[i] + (int64_t)c * 64);
-        b.g[1][i] = load16(wg[i] + (int64_t)c * 64 + 64);
-      }
-#pragma unroll
-      for (int i = 0; i < GW; ++i) {
-        b.u[0][i] = load16(wu[i] + (int64_t)c * 64);
-        b.u[1][i] = load16(wu[i] + (int64_t)c * 64 + 64);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          // rows past the tile read a valid row; their scale is zeroed at use,
-          // so that nothing here waits for a load
-          b.x[j][m] = load_frag_k64(xr[m] + (int64_t)(c + j) * 128);
-          b.sx[j][m] = G.xs[(int64_t)xsrow[m] * KB + c + j];
-        }
-      }
-    };
-    auto compute = [&](const Buf &b) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < GW; ++i) {
-          const int sag = (int)(((j ? b.sg[i].y : b.sg[i].x) >> (8 * g4)) & 0xFFu);
-          const int sau = (int)(((j ? b.su[i].y : b.su[i].x) >> (8 * g4)) & 0xFFu);
-#pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            const float sxm = xv[m] ? b.sx[j][m] : 0.f;
-            ag[i][m] = chunk_mma_mx(b.g[j][i], b.x[j][m], sag, ag[i][m], sxm);
-            au[i][m] = chunk_mma_mx(b.u[j][i], b.x[j][m], sau, au[i][m], sxm);
-          }
-        }
-    };
-    if (MX_LDS && MT <= 2 && (nchunk & 1) == 0) {
+    if (MT <= 2 && (nchunk & 1) == 0) {
       // Weight codes go through LDS.  A 16x16x128 fp4 fragment gives a row
       // only 64 bytes per load instruction (half a 128-byte line, so every L1
       // miss moves half a line); a direct-to-LDS copy instead moves 8 rows x
@@ -463,32 +390,8 @@ __device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry 
         __builtin_amdgcn_sched_barrier(0);
         compute(B0, X0);
       }
-    } else if (MX_PIPE && MT <= 2 && (nchunk & 1) == 0) {
-      Buf A, B;
-      load(A, 0);
-      int c = 0;
-      for (; c + 4 < nchunk; c += 4) {
-        load(B, c + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(A);
-        __builtin_amdgcn_sched_barrier(0);
-        load(A, c + 4);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(B);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (c + 2 < nchunk) {
-        load(B, c + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(A);
-        compute(B);
-      } else {
-        compute(A);
-      }
-    } else if (MX_NC4 && MT <= 2 && (nchunk & 3) == 0) {
-      steps(std::integral_constant<int, 4>{});
     } else {
-      steps(std::integral_constant<int, 2>{});
+      plain_steps();
     }
   } else {
     for (int c = 0; c < nchunk; ++c) {
@@ -632,29 +535,21 @@ __device__ __forceinline__ void down_body(const FfnGroup &G, const TileEntry &te
   const int KB = I / 128;
   const Frag zf = Frag{i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
   if constexpr (MX) {
-    auto steps = [&](auto nc_tag) {
-      constexpr int NC = decltype(nc_tag)::value;
-      for (int c = 0; c < nchunk; c += NC) {
-        const int nv = min(NC, nchunk - c);
-        i32x4 fw[NC][NW];
-        uint32_t sww[NC][NW];
-        Frag fh[NC][MT];
-        float sh[NC][MT];
-        if constexpr (NC == 4) {
+    // Fallback for shapes the staged loop below does not take (see gate/up).
+    auto plain_steps = [&]() {
+      for (int c = 0; c < nchunk; c += 2) {
+        const int nv = min(2, nchunk - c);
+        i32x4 fw[2][NW];
+        uint32_t sww[2][NW];
+        Frag fh[2][MT];
+        float sh[2][MT];
 #pragma unroll
-          for (int i = 0; i < NW; ++i) {
-            const i32x4 a = load16(mr[i] + 4 * c);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sww[j][i] = (uint32_t)a[j];
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < NC; ++j) {
-          const int cj = j < nv ? c + j : c;   // a short last step reloads its first chunk, counted once
+        for (int j = 0; j < 2; ++j) {
+          const int cj = j < nv ? c + j : c;   // a lone last chunk is loaded twice, counted once
 #pragma unroll
           for (int i = 0; i < NW; ++i) {
             fw[j][i] = load16(wr[i] + (int64_t)cj * 64);
-            if constexpr (NC != 4) sww[j][i] = *reinterpret_cast<const uint32_t *>(mr[i] + 4 * cj);
+            sww[j][i] = *reinterpret_cast<const uint32_t *>(mr[i] + 4 * cj);
           }
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
@@ -667,7 +562,7 @@ __device__ __forceinline__ void down_body(const FfnGroup &G, const TileEntry &te
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < NC; ++j) {
+        for (int j = 0; j < 2; ++j) {
           if (j >= nv) break;
 #pragma unroll
           for (int i = 0; i < NW; ++i) {
@@ -678,43 +573,7 @@ __device__ __forceinline__ void down_body(const FfnGroup &G, const TileEntry &te
         }
       }
     };
-    struct Buf {
-      i32x4 w[2][NW];
-      uint2 s[NW];
-      Frag h[2][MT];
-      float sh[2][MT];
-    };
-    auto load = [&](Buf &b, int c) {
-#pragma unroll
-      for (int i = 0; i < NW; ++i) b.s[i] = *reinterpret_cast<const uint2 *>(mr[i] + 4 * c);
-      // the two chunks of a row share one 128-byte line: load them back to back
-#pragma unroll
-      for (int i = 0; i < NW; ++i) {
-        b.w[0][i] = load16(wr[i] + (int64_t)c * 64);
-        b.w[1][i] = load16(wr[i] + (int64_t)c * 64 + 64);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          // rows past the tile read a valid row; their scale is zeroed at use
-          b.h[j][m] = load_frag_k64(hr[m] + (int64_t)(c + j) * 128);
-          b.sh[j][m] = G.hs[(int64_t)hsrow[m] * KB + c + j];
-        }
-      }
-    };
-    auto compute = [&](const Buf &b) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < NW; ++i) {
-          const int sa = (int)(((j ? b.s[i].y : b.s[i].x) >> (8 * g4)) & 0xFFu);
-#pragma unroll
-          for (int m = 0; m < MT; ++m)
-            acc[i][m] = chunk_mma_mx(b.w[j][i], b.h[j][m], sa, acc[i][m], hv[m] ? b.sh[j][m] : 0.f);
-        }
-    };
-    if (MX_LDS && MT <= 2 && (nchunk & 1) == 0) {
+    if (MT <= 2 && (nchunk & 1) == 0) {
       // Weight codes through LDS, as in the gate/up kernel: each copy
       // instruction moves 8 rows x one whole 128-byte line; two 4 KB buffers
       // per wave, private to it.
@@ -807,32 +666,8 @@ __device__ __forceinline__ void down_body(const FfnGroup &G, const TileEntry &te
         __builtin_amdgcn_sched_barrier(0);
         compute(B0, X0);
       }
-    } else if (MX_PIPE && MT <= 2 && (nchunk & 1) == 0) {
-      Buf A, B;
-      load(A, 0);
-      int c = 0;
-      for (; c + 4 < nchunk; c += 4) {
-        load(B, c + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(A);
-        __builtin_amdgcn_sched_barrier(0);
-        load(A, c + 4);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(B);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (c + 2 < nchunk) {
-        load(B, c + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(A);
-        compute(B);
-      } else {
-        compute(A);
-      }
-    } else if (MX_NC4 && MT <= 2 && (nchunk & 3) == 0) {
-      steps(std::integral_constant<int, 4>{});
     } else {
-      steps(std::integral_constant<int, 2>{});
+      plain_steps();
     }
   } else {
     for (int c = 0; c < nchunk; ++c) {
