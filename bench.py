@@ -49,9 +49,11 @@ def parse():
 # 1 GiB device copy (bench.py --copy-calibration).  Valid only for the kernel sources they were
 # taken on: a different hash of the library sources reports null.
 TRAFFIC = {
-    "decode_bf16": {"src_hash": "75b4fbebfedccb3a", "fetch_kib": 3309119.1, "write_kib": 1885.5586, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_fp8": {"src_hash": "75b4fbebfedccb3a", "fetch_kib": 1666807.0, "write_kib": 1193.457, "fetch_scale": 2.0, "write_scale": 1.0},
-    "prefill_fp8": {"src_hash": "75b4fbebfedccb3a", "fetch_kib": 4430257.2, "write_kib": 140290.45, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_bf16": {"src_hash": "a87c18d4e41a8ac1", "fetch_kib": 3309815.9, "write_kib": 1884.8555, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_fp8": {"src_hash": "a87c18d4e41a8ac1", "fetch_kib": 1666956.0, "write_kib": 1191.5312, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_mxfp4": {"src_hash": "a87c18d4e41a8ac1", "fetch_kib": 1008328.0, "write_kib": 1199.4414, "fetch_scale": 2.0, "write_scale": 1.0},
+    "dense_ff_bf16": {"src_hash": "a87c18d4e41a8ac1", "fetch_kib": 1781697.4, "write_kib": 221184.0, "fetch_scale": 2.0, "write_scale": 1.0},
+    "prefill_fp8": {"src_hash": "a87c18d4e41a8ac1", "fetch_kib": 4420431.4, "write_kib": 140277.27, "fetch_scale": 2.0, "write_scale": 1.0},
 }
 
 
