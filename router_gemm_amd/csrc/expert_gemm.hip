@@ -285,6 +285,9 @@ __device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry 
       // one whole line (two chunks) per instruction.  Each wave owns two 8 KB
       // buffers (its 2*GW tiles x 16 rows x 128 bytes), 16-byte columns
       // XOR-swizzled by row % 8; no other wave touches them, so no barriers.
+      // Every code line is read once, so the copies are non-temporal: cached
+      // normally they evicted the rows' scale words between steps (16% more
+      // bytes fetched, 8% slower).
       // (two separate arrays, so that alias analysis sees that reading one
       // buffer never waits for the copies into the other)
       __shared__ __attribute__((aligned(16))) uint8_t wlds0[4][2 * GW][2048];
@@ -302,8 +305,8 @@ __device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry 
 #pragma unroll
         for (int t = 0; t < 2 * GW; ++t) {
           const uint8_t *src = tb[t] + (int64_t)c * 64;
-          dma16(src + coff0, buf + t * 2048);
-          dma16(src + coff1, buf + t * 2048 + 1024);
+          dma16_stream(src + coff0, buf + t * 2048);
+          dma16_stream(src + coff1, buf + t * 2048 + 1024);
         }
       };
       struct XB {
@@ -589,8 +592,8 @@ __device__ __forceinline__ void down_body(const FfnGroup &G, const TileEntry &te
 #pragma unroll
         for (int t = 0; t < NW; ++t) {
           const uint8_t *src = tb[t] + (int64_t)c * 64;
-          dma16(src + coff0, buf + t * 2048);
-          dma16(src + coff1, buf + t * 2048 + 1024);
+          dma16_stream(src + coff0, buf + t * 2048);
+          dma16_stream(src + coff1, buf + t * 2048 + 1024);
         }
       };
       struct XB {

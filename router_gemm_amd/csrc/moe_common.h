@@ -100,6 +100,12 @@ typedef const __attribute__((address_space(1))) void gbl_void;
 __device__ __forceinline__ void dma16(const void *g, uint8_t *lds_base) {
   __builtin_amdgcn_global_load_lds((gbl_void *)g, (lds_void *)lds_base, 16, 0, 0);
 }
+// As dma16, with the non-temporal cache policy (the "nt" bit, aux = 2): for
+// data read exactly once per line, so that streaming it does not evict lines
+// that are still being reused (scale words, token rows).
+__device__ __forceinline__ void dma16_stream(const void *g, uint8_t *lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void *)g, (lds_void *)lds_base, 16, 0, 2);
+}
 // Copy 4 bytes per lane to LDS at base + 4 * lane.
 __device__ __forceinline__ void dma4(const void *g, uint8_t *lds_base) {
   __builtin_amdgcn_global_load_lds((gbl_void *)g, (lds_void *)lds_base, 4, 0, 0);
