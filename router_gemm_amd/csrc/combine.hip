@@ -26,8 +26,13 @@ __device__ __forceinline__ void load8(const void *base, bool f32, int64_t idx, f
   }
 }
 
-// One workgroup (256 threads) per token; each thread owns 8 consecutive columns
-// per 2048-column stride.
+// Grid: one workgroup (256 threads) per (token, 2048-column block); each
+// thread owns 8 consecutive columns.  The token's assignments are taken in
+// batches of up to 32: their rows and gates are staged in LDS, then every
+// thread issues its row loads 8 at a time before summing them in order, so
+// the memory latency is paid once per 8 rows rather than twice per row.
+constexpr int kCombBatch = 32;
+
 __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y_perm, int yp_f32,
                                                       const int32_t *__restrict__ perm_pos,
                                                       const int32_t *__restrict__ tok_off,
@@ -35,7 +40,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y
                                                       const float *__restrict__ gates,
                                                       const void *__restrict__ shared, int sh_f32, int64_t H, int64_t nrows,
                                                       void *__restrict__ y, int out_f32) {
+  __shared__ int32_t srow[kCombBatch];
+  __shared__ float sgate[kCombBatch];
   const int64_t t = blockIdx.x;
+  const int64_t c = (int64_t)blockIdx.y * 2048 + (int64_t)threadIdx.x * 8;
+  const bool active = c < H;
   int jbeg, jend;
   if (tok_off) {
     jbeg = tok_off[t];
@@ -44,34 +53,53 @@ __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y
     jbeg = (int)(t * k);
     jend = jbeg + k;
   }
-  for (int64_t c = (int64_t)threadIdx.x * 8; c < H; c += 2048) {
-    float acc[8];
-    if (shared) {
-      load8(shared, sh_f32 != 0, t * H + c, acc);
-    } else {
+  float acc[8];
+  if (shared && active) {
+    load8(shared, sh_f32 != 0, t * H + c, acc);
+  } else {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-    }
-    for (int j = jbeg; j < jend; ++j) {
-      const int32_t i = tok_list ? tok_list[j] : j;
+    for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+  }
+  for (int jb = jbeg; jb < jend; jb += kCombBatch) {
+    const int n = min(kCombBatch, jend - jb);
+    if ((int)threadIdx.x < n) {
+      const int32_t i = tok_list ? tok_list[jb + threadIdx.x] : jb + (int)threadIdx.x;
       const int32_t p = perm_pos[i];
-      if (p < 0 || p >= nrows) continue;
-      const float g = gates[i];
-      float v[8];
-      load8(y_perm, yp_f32 != 0, (int64_t)p * H + c, v);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(g, v[q], acc[q]);
+      srow[threadIdx.x] = (p < 0 || p >= nrows) ? -1 : p;   // -1: assignment skipped
+      sgate[threadIdx.x] = gates[i];
     }
-    if (out_f32) {
-      f32x4 *o = reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(y) + t * H + c);
-      o[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
-      o[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
-    } else {
-      i32x4 r;
+    __syncthreads();
+    if (active && nrows > 0) {   // nrows == 0: every slot is skipped
+      for (int q0 = 0; q0 < n; q0 += 8) {
+        float v[8][8];
+        int32_t pr[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) r[q] = (int)(f32_to_bf16(acc[2 * q]) | (f32_to_bf16(acc[2 * q + 1]) << 16));
-      store16(reinterpret_cast<uint16_t *>(y) + t * H + c, r);
+        for (int u = 0; u < 8; ++u) {
+          pr[u] = q0 + u < n ? srow[q0 + u] : -1;
+          // a skipped slot reads row 0 and is left out of the sum below
+          load8(y_perm, yp_f32 != 0, (int64_t)(pr[u] >= 0 ? pr[u] : 0) * H + c, v[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (pr[u] < 0) continue;
+          const float g = sgate[q0 + u];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(g, v[u][q], acc[q]);
+        }
+      }
     }
+    __syncthreads();
+  }
+  if (!active) return;
+  if (out_f32) {
+    f32x4 *o = reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(y) + t * H + c);
+    o[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    o[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  } else {
+    i32x4 r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = (int)(f32_to_bf16(acc[2 * q]) | (f32_to_bf16(acc[2 * q + 1]) << 16));
+    store16(reinterpret_cast<uint16_t *>(y) + t * H + c, r);
   }
 }
 
@@ -80,7 +108,8 @@ hipError_t launch_combine(const void *y_perm, bool yp_f32, const int32_t *perm_p
                           bool sh_f32, int64_t T, int64_t H, int64_t nrows, void *y, bool out_f32, hipStream_t st) {
   if (T == 0) return hipSuccess;
   timing_before(8, st);
-  combine_kernel<<<(unsigned)T, 256, 0, st>>>(y_perm, yp_f32 ? 1 : 0, perm_pos, tok_off, tok_list, k, gates,
+  const dim3 grid((unsigned)T, (unsigned)cdiv(H, 2048));
+  combine_kernel<<<grid, 256, 0, st>>>(y_perm, yp_f32 ? 1 : 0, perm_pos, tok_off, tok_list, k, gates,
                                               shared, sh_f32 ? 1 : 0, H, nrows, y, out_f32 ? 1 : 0);
   timing_after(8, st);
   return hipGetLastError();

@@ -57,8 +57,8 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(FfnGroup g0, FfnGroup
     const FfnGroup G = pick_group(g0, g1, g);
     int n = 0;
     if (tid < G.E) {
-      const int b = min(max(G.off[tid], 0), G.nrows);
-      const int e = min(max(G.off[tid + 1], b), G.nrows);
+      const int b = min(max(group_off(G, tid), 0), G.nrows);
+      const int e = min(max(group_off(G, tid + 1), b), G.nrows);
       n = e - b;
     }
     const int cnt = (n + bm - 1) / bm;
@@ -170,8 +170,8 @@ struct StreamArgs {
 // Rows [rbeg, rend) of the tile, clamped to the group's row count.
 __device__ __forceinline__ void tile_rows(const FfnGroup &G, const TileEntry &te, int &rbeg, int &rend) {
   const int e = te.ge & 0xFFFFFF;
-  rend = min(max(G.off[e + 1], 0), G.nrows);
-  rbeg = min(max(G.off[e], 0) + te.m0, rend);
+  rend = min(max(group_off(G, e + 1), 0), G.nrows);
+  rbeg = min(max(group_off(G, e), 0) + te.m0, rend);
 }
 
 // ---------------------------------------------------------------- gate/up (streaming)

@@ -72,8 +72,8 @@ struct TiledItem {
     wn = w & 1;
     wm = w >> 1;
     e = te.ge & 0xFFFFFF;
-    rend = min(max(G.off[e + 1], 0), G.nrows);
-    rbeg = min(max(G.off[e], 0) + te.m0, rend);
+    rend = min(max(group_off(G, e + 1), 0), G.nrows);
+    rbeg = min(max(group_off(G, e), 0) + te.m0, rend);
     nvalid = min(rend - rbeg, TBM);
     I = G.I;
     K = GATEUP ? H : I;
@@ -391,8 +391,8 @@ __device__ __forceinline__ void map_item(const TiledArgs &a, int L, int &slot, i
   const TileEntry te = a.tiles[s];
   const FfnGroup &G = (te.ge >> 24) ? a.g1 : a.g0;
   const int e = te.ge & 0xFFFFFF;
-  const int r0 = min(max(G.off[e], 0), G.nrows);
-  const int r1 = min(max(G.off[e + 1], r0), G.nrows);
+  const int r0 = min(max(group_off(G, e), 0), G.nrows);
+  const int r1 = min(max(group_off(G, e + 1), r0), G.nrows);
   const int t = te.m0 / TBM, p = t % TBAND;
   const int band = min(TBAND, (r1 - r0 + TBM - 1) / TBM - (t - p));
   const int s0 = s - p, q = L - a.nt * s0;

@@ -220,7 +220,6 @@ struct ForwardWs {
   moe::FfnGroup groups[moe::kMaxGroups];
   int ngroups;
   uint16_t *y_perm;
-  int32_t *sh_off;
   void *sh_out;
 };
 ForwardWs carve_forward(Carve &c, const moe_layer *L, const void *x, int64_t T, bool out_f32) {
@@ -239,12 +238,11 @@ ForwardWs carve_forward(Carve &c, const moe_layer *L, const void *x, int64_t T, 
   f.y_perm = c.take<uint16_t>((size_t)N * H + 8);
   f.ngroups = 0;
   if (L->shared_inter > 0) {
-    f.sh_off = c.take<int32_t>(2);
     f.sh_out = c.take<uint8_t>((size_t)T * H * (out_f32 ? 4 : 2) + 16);
-    // the shared expert's tiles go first in the list: they carry twice the bytes (bf16)
-    f.groups[f.ngroups++] = shared_group(L, x, f.sh_off, T, f.sh_out, out_f32);
+    // the shared expert's tiles go first in the list: they carry twice the bytes
+    // (bf16); no offsets array: one expert holding all T rows
+    f.groups[f.ngroups++] = shared_group(L, x, nullptr, T, f.sh_out, out_f32);
   } else {
-    f.sh_off = nullptr;
     f.sh_out = nullptr;
   }
   f.groups[f.ngroups++] = routed_group(L, f.x_perm, f.x_scale, f.offsets, N, f.y_perm, false);
@@ -456,10 +454,6 @@ moe_status moe_forward(const moe_layer *L, const void *x, int64_t T, void *y, in
     e = moe::launch_gather_rows(static_cast<const uint16_t *>(x), H, f.perm_src, nullptr, L->top_k, N, f.offsets + E,
                                 is_fp8(L), f.x_perm, f.x_scale, st);
     if (e != hipSuccess) return hip_status(e, "moe_forward: gather");
-  }
-  if (L->shared_inter > 0) {
-    e = moe::launch_fill_offsets2(f.sh_off, (int32_t)T, st);
-    if (e != hipSuccess) return hip_status(e, "moe_forward: shared offsets");
   }
   e = moe::launch_expert_ffn(f.groups, f.ngroups, H, f.ffn.plan, f.ffn.tiles, MOE_SITE_GATE_UP, st);
   if (e != hipSuccess) return hip_status(e, "moe_forward: experts");

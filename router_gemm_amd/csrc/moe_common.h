@@ -139,6 +139,12 @@ __device__ __forceinline__ void wg_barrier() {
 __device__ __forceinline__ int swz_f(int row) { return row & 7; }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ swz_f(row)) << 4); }
 
+// Row offset e of an expert group: G.off[e], or, for a group given without an
+// offsets array (one expert holding every row), 0 / nrows.
+__device__ __forceinline__ int group_off(const FfnGroup &G, int e) {
+  return G.off ? G.off[e] : (e == 0 ? 0 : G.nrows);
+}
+
 // A value the compiler may keep in a scalar register (uniform across the wave).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

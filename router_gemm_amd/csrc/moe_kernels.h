@@ -39,8 +39,6 @@ hipError_t launch_gather_rows(const uint16_t *x, int64_t H, const int32_t *perm_
 // arithmetic as the fp8 gather, without the permutation).
 hipError_t launch_quantize_rows(const uint16_t *x, int64_t H, int64_t T, uint8_t *xq, float *x_scale,
                                 hipStream_t st);
-// Writes {0, n} into dst[0..1] (device).
-hipError_t launch_fill_offsets2(int32_t *dst, int32_t n, hipStream_t st);
 
 // ---- grouped expert GEMMs (expert_gemm.hip)
 // One group = one set of experts with its own weights, rows and outputs.  A
@@ -53,7 +51,7 @@ struct FfnGroup {
   const float *sgu;    // [E, 2I/128, H/128] (fp8)
   const uint8_t *wd;   // [E, H, I]
   const float *sd;     // [E, H/128, I/128] (fp8)
-  const int32_t *off;  // [E+1] device offsets of each expert's rows
+  const int32_t *off;  // [E+1] device offsets of each expert's rows; NULL: E == 1, rows [0, nrows)
   uint8_t *h;          // [nrows, I] intermediate: e4m3 (fp8) or bf16
   float *hs;           // [nrows, I/128] (fp8)
   void *y;             // [nrows, H] output, bf16 or f32

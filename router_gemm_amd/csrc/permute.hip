@@ -453,16 +453,4 @@ hipError_t launch_quantize_rows(const uint16_t *x, int64_t H, int64_t T, uint8_t
   return hipGetLastError();
 }
 
-__global__ void fill_offsets2_kernel(int32_t *dst, int32_t n) {
-  if (threadIdx.x == 0) {
-    dst[0] = 0;
-    dst[1] = n;
-  }
-}
-
-hipError_t launch_fill_offsets2(int32_t *dst, int32_t n, hipStream_t st) {
-  fill_offsets2_kernel<<<1, 64, 0, st>>>(dst, n);
-  return hipGetLastError();
-}
-
 }  // namespace moe

@@ -276,6 +276,38 @@ def test_combine_matches_oracle(tokens, ydt, sdt, odt):
     assert err.max() < (1e-6 if odt == torch.float32 else 2 ** -8)
 
 
+@pytest.mark.parametrize("tokens", [True, False])
+def test_combine_long_assignment_lists_and_partial_column_block(tokens):
+    """Tokens with 70, 33, 32, 9 and 0 assignments (several 32-slot batches,
+    8-row load groups cut short), k = 32 slots per token, and H = 2176: a
+    second 2048-column block only partly covered."""
+    rng = np.random.default_rng(13)
+    H = 2176
+    d = dev()
+    if tokens:
+        T, k = 5, 0
+        counts = [70, 33, 32, 9, 0]
+        tok = np.repeat(np.arange(T), counts).astype(np.int32)
+        rng.shuffle(tok)
+        N = tok.size
+    else:
+        T, k = 7, 32
+        N, tok = T * k, None
+    yp = rng.standard_normal((N, H)).astype(np.float32)
+    pos = rng.permutation(N).astype(np.int32)
+    pos[rng.choice(N, 6, replace=False)] = -1
+    gates = rng.random(N).astype(np.float32)
+    sh = rng.standard_normal((T, H)).astype(np.float32)
+    layer = B.Layer(H, 128, 8, k, B.MOE_BF16, None, None)
+    y = torch.empty((T, H), dtype=torch.float32, device=d)
+    B.moe_combine(layer, torch.from_numpy(yp).to(d), B.MOE_F32, torch.from_numpy(pos).to(d),
+                  torch.from_numpy(tok).to(d) if tokens else None, torch.from_numpy(gates).to(d), N,
+                  torch.from_numpy(sh).to(d), B.MOE_F32, T, y, B.MOE_F32, ws=B.workspace(layer, T, N, d))
+    torch.cuda.synchronize()
+    y_ref = oracle.combine(yp.astype(np.float64), pos, gates, T, k=max(k, 1), tok=tok, shared=sh.astype(np.float64))
+    assert rel_err_rows(to_np(y), y_ref).max() < 1e-6
+
+
 def test_combine_of_permute_is_identity():
     """y_perm := x_perm (identity expert, bf16): k = 1 with gate 1 gives y == x
     bit for bit; k = 4 with all gates 1 gives y == 4x bit for bit."""
