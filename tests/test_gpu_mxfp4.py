@@ -89,3 +89,49 @@ def test_mx_weights_are_read_as_stored():
     lt2 = W.LayerTensors(cfg, lt.w_router, lt.router_bias, sw(lt.w_gate_up), sw(lt.w_down), lt.s_gate_up,
                          lt.s_down, None, None)
     check_forward(lt2, x)
+
+
+def test_mx_primitives_with_pre_routed_triples():
+    """An expert-parallel share with MX FP4 experts driven through the four
+    primitives: permute (e4m3 rows + 1x128 scales), the MX expert FFN, the
+    shared expert as a one-expert bf16 layer, combine; against the oracle's
+    pre-routed-triples form of the layer."""
+    cfg = W.MoEConfig("mx_triples", T=300, H=512, E=12, k=0, I=256, Is=128, expert_dtype="mxfp4",
+                      router_std=0.05, zipf_s=1.1, triples=700, seed=5)
+    _print("[mx triples]")
+    lt = W.make_layer(cfg, dev())
+    x = W.make_x(cfg, dev())
+    tok, exp, gate = W.make_triples(cfg)
+    exp[:3] = [cfg.E, -1, cfg.E + 7]          # out of range: dropped
+    d = dev()
+    T, N, E, H = cfg.T, cfg.N, cfg.E, cfg.H
+    layer = B.Layer.from_tensors(lt, top_k=0)
+    shared = B.Layer.shared_view(lt)
+    ws = torch.empty(max(B.moe_workspace_bytes(layer, T, N), B.moe_workspace_bytes(shared, T, T)),
+                     dtype=torch.uint8, device=d)
+    off = torch.empty(E + 1, dtype=torch.int32, device=d)
+    src = torch.empty(N, dtype=torch.int32, device=d)
+    pos = torch.empty(N, dtype=torch.int32, device=d)
+    xp = torch.empty((N, H), dtype=torch.uint8, device=d)
+    xs = torch.empty((N, H // 128), dtype=torch.float32, device=d)
+    tok_g, exp_g, gate_g = (torch.from_numpy(a).to(d) for a in (tok, exp, gate))
+    B.moe_permute(layer, x, T, exp_g, tok_g, N, off, src, pos, xp, xs, ws=ws)
+    yp = torch.empty((N, H), dtype=torch.bfloat16, device=d)
+    B.moe_expert_ffn(layer, off, xp, xs, N, yp, ws=ws)
+    s_out = torch.empty((T, H), dtype=torch.float32, device=d)
+    B.moe_expert_ffn(shared, torch.tensor([0, T], dtype=torch.int32, device=d), x, None, T, s_out, ws=ws)
+    y = torch.empty((T, H), dtype=torch.float32, device=d)
+    B.moe_combine(layer, yp, B.MOE_BF16, pos, tok_g, gate_g, N, s_out, B.MOE_F32, T, y, B.MOE_F32, ws=ws)
+    torch.cuda.synchronize()
+    off_r, src_r, pos_r, dropped = oracle.permute(exp, E)
+    assert dropped == 3
+    assert np.array_equal(off.cpu().numpy(), off_r) and np.array_equal(pos.cpu().numpy(), pos_r)
+    # the e4m3 rows and scales are bit-exact: quantisation decisions in fp32 on both sides
+    q_tok, s_tok = oracle.quant_bf16_rows(W.bf16_bits(x))
+    nv = int(off_r[-1])
+    assert np.array_equal(xp.cpu().numpy()[:nv], q_tok[tok[src_r[:nv]]])
+    assert np.array_equal(xs.cpu().numpy()[:nv], s_tok[tok[src_r[:nv]]])
+    y_ref = oracle.forward_triples(oracle_layer(lt), W.bf16_bits(x), tok, exp, gate)
+    err = rel_err_rows(to_np(y), y_ref)
+    _print(f"  max rel err {err.max():.3e} over {T} tokens")
+    assert err.max() < TOL["mxfp4"]
