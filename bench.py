@@ -248,6 +248,17 @@ def main():
     roof["algorithmic_bytes_per_step"] = int(gu_bytes)
     roof["algorithmic_flops_per_step"] = gu_f_routed + gu_f_shared
 
+    # per-step spread: a separate pass of K steps with an event between steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(K):
+        step()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(K)])
+    spread = {q: round(float(np.percentile(per_step, v)), 4) for q, v in (("p10", 10), ("p50", 50), ("p90", 90))}
+
     # per-kernel breakdown: a separate pass of K steps with every launch site timed
     sites = {0: "router_logits", 1: "router_topk", 2: "sort", 3: "gather", 4: "gate_up", 5: "down", 8: "combine"}
     for sidx in sites:
@@ -275,6 +286,7 @@ def main():
                   "mfma_util_blended": round(mfma_util, 4), "wall_s": round(wall, 4)},
         "roofline": roof,
         "breakdown_us_per_step": breakdown,
+        "step_ms_percentiles": spread,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -302,8 +314,11 @@ def cpu_baseline(cfg, lt, x, target_s):
     if cfg.triples:
         tok, exp, gate = W.make_triples(cfg)
         run = lambda: oracle.forward_triples(L, xb, tok, exp, gate, token_list=sample)
+        n_assign = int(np.isin(tok, sample).sum())
+        pass_flops = 2.0 * (n_assign * 3 * cfg.I * cfg.H + n * 3 * cfg.Is * cfg.H)
     else:
         run = lambda: oracle.forward(L, xb, token_list=sample)
+        pass_flops = 2.0 * n * (cfg.k * 3 * cfg.I * cfg.H + 3 * cfg.Is * cfg.H + cfg.E * cfg.H)
     done, t0 = 0, time.perf_counter()
     while True:
         run()
@@ -312,6 +327,7 @@ def cpu_baseline(cfg, lt, x, target_s):
         if el >= target_s or done >= 16 * n:
             break
     return {"value": round(done / el, 2), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "fp64_gflops": round(pass_flops * (done // n) / el / 1e9, 2),
             "sample": f"{n} of the {cfg.T} tokens of {cfg.name} (seeded choice), full layer per token, "
                       f"{done // n} pass(es) in {el:.1f} s"}
 

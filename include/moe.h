@@ -143,7 +143,8 @@ moe_status moe_route(const moe_layer *layer, const void *x, int64_t T,
  *   x              bf16 [T, H]
  *   assign_expert  int32 [N]: expert of assignment i (e.g. topk_ids viewed as [T*k])
  *   assign_token   int32 [N] or NULL: token of assignment i (NULL: i / k)
- *   expert_offsets int32 [E+1] out: rows of expert e are offsets[e]..offsets[e+1]-1
+ *   expert_offsets int32 [E+1] out: rows of expert e are offsets[e]..offsets[e+1]-1;
+ *                  offsets[E] = assignments kept, so N - offsets[E] were dropped
  *   perm_src       int32 [N] out: assignment index placed at row p (rows in
  *                  expert order; inside an expert, increasing assignment index)
  *   perm_pos       int32 [N] out: row of assignment i (-1 if its expert or
