@@ -724,7 +724,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(StreamArgs a) {
 
 // ---------------------------------------------------------------- host side
 
-FfnPlan ffn_plan(const FfnGroup *g, int ngroups) {
+FfnPlan ffn_plan(const FfnGroup *g, int ngroups, int H) {
   FfnPlan p;
   int64_t rows = 0, experts = 0;
   bool all128 = true;
@@ -742,11 +742,15 @@ FfnPlan ffn_plan(const FfnGroup *g, int ngroups) {
   p.mt = avg <= 16 ? 1 : (avg <= 32 ? 2 : 4);
   p.gw = all128 ? 2 : 1;
   // many rows per expert: the LDS-tiled kernels (weights reused across 128 tokens)
-  // (MX weights run on the streaming kernels only)
-  bool any_mx = false;
-  for (int i = 0; i < ngroups; ++i) any_mx = any_mx || g[i].mx;
-  p.tiled = (all128 && !any_mx && g[0].nrows > 0 && avg >= 48.0) ? 1 : 0;
-  p.bm = p.tiled ? 128 : 16 * p.mt;
+  // MX weights: their own tiled kernels (64-row token tiles, H and I multiples of 256)
+  bool any_mx = false, mx_ok = true;
+  for (int i = 0; i < ngroups; ++i)
+    if (g[i].mx) {
+      any_mx = true;
+      mx_ok = mx_ok && tiled_mx_supported(g[i], H);
+    }
+  p.tiled = (all128 && H % 256 == 0 && mx_ok && g[0].nrows > 0 && avg >= 48.0) ? 1 : 0;
+  p.bm = p.tiled ? (any_mx ? 64 : 128) : 16 * p.mt;
   int64_t cap = 1;
   for (int i = 0; i < ngroups; ++i) cap += cdiv(g[i].nrows, p.bm) + std::min<int64_t>(g[i].nrows, g[i].E);
   p.max_tiles = (int)cap;
@@ -791,11 +795,23 @@ hipError_t launch_expert_ffn(const FfnGroup *g, int ngroups, int H, const FfnPla
     fp8_plain = fp8_plain || (g[i].fp8 && !g[i].mx);
   }
   // one launch holds either MX or block-scaled fp8 weights (plus bf16 groups)
-  if (mx && (fp8_plain || plan.tiled)) return hipErrorInvalidValue;
+  if (mx && fp8_plain) return hipErrorInvalidValue;
   if (rows == 0) return hipSuccess;
   int32_t *hdr = tiles_ws;
   TileEntry *tiles = reinterpret_cast<TileEntry *>(tiles_ws + kTileHdrWords);
   StreamArgs a{g[0], ngroups > 1 ? g[1] : g[0], tiles, hdr, H};
+  if (plan.tiled && mx) {
+    // MX tiles are 64 token rows, the other groups' 128: each group gets its
+    // own tile list and launches, one after the other on the stream.
+    for (int i = 0; i < ngroups; ++i) {
+      if (g[i].nrows == 0) continue;
+      build_tiles_kernel<<<1, 1024, 0, st>>>(g[i], g[i], 1, g[i].mx ? 64 : 128, plan.max_tiles, tiles, hdr);
+      const hipError_t e = g[i].mx ? launch_tiled_mx_ffn(g[i], H, tiles, hdr, num_compute_units(), site, st)
+                                   : launch_tiled_ffn(&g[i], 1, H, tiles, hdr, num_compute_units(), site, st);
+      if (e != hipSuccess) return e;
+    }
+    return hipGetLastError();
+  }
   build_tiles_kernel<<<1, 1024, 0, st>>>(a.g0, a.g1, ngroups, plan.bm, plan.max_tiles, tiles, hdr);
   if (plan.tiled) {
     if (H % 256 != 0) return hipErrorInvalidValue;

@@ -145,9 +145,9 @@ struct FfnWs {
   uint8_t *h[moe::kMaxGroups];
   float *hs[moe::kMaxGroups];
 };
-FfnWs carve_ffn(Carve &c, moe::FfnGroup *g, int ngroups) {
+FfnWs carve_ffn(Carve &c, moe::FfnGroup *g, int ngroups, int H) {
   FfnWs f;
-  f.plan = moe::ffn_plan(g, ngroups);
+  f.plan = moe::ffn_plan(g, ngroups, H);
   f.tiles = c.take<int32_t>(moe::ffn_tiles_bytes(f.plan) / 4);
   for (int i = 0; i < ngroups; ++i) {
     f.h[i] = c.take<uint8_t>((size_t)g[i].nrows * g[i].I * (g[i].fp8 ? 1 : 2) + 16);
@@ -246,7 +246,7 @@ ForwardWs carve_forward(Carve &c, const moe_layer *L, const void *x, int64_t T, 
     f.sh_out = nullptr;
   }
   f.groups[f.ngroups++] = routed_group(L, f.x_perm, f.x_scale, f.offsets, N, f.y_perm, false);
-  f.ffn = carve_ffn(c, f.groups, f.ngroups);
+  f.ffn = carve_ffn(c, f.groups, f.ngroups, H);
   return f;
 }
 
@@ -255,7 +255,7 @@ size_t need_permute(const moe_layer *L, int64_t N) { Carve c(nullptr); carve_sor
 size_t need_ffn(const moe_layer *L, int64_t N) {
   Carve c(nullptr);
   moe::FfnGroup g = routed_group(L, nullptr, nullptr, nullptr, N, nullptr, false);
-  carve_ffn(c, &g, 1);
+  carve_ffn(c, &g, 1, L->hidden);
   return c.used;
 }
 size_t need_combine(int64_t T, int64_t N, bool tokens) {
@@ -367,7 +367,7 @@ moe_status moe_expert_ffn(const moe_layer *L, const int32_t *expert_offsets, con
   if ((s = check_ws(ws, ws_bytes, need_ffn(L, N))) != MOE_OK) return s;
   Carve c(ws);
   moe::FfnGroup g = routed_group(L, x_perm, x_scale, expert_offsets, N, y_perm, y_dtype == MOE_F32);
-  FfnWs f = carve_ffn(c, &g, 1);
+  FfnWs f = carve_ffn(c, &g, 1, L->hidden);
   return hip_status(moe::launch_expert_ffn(&g, 1, L->hidden, f.plan, f.tiles, MOE_SITE_GATE_UP, (hipStream_t)stream),
                     "moe_expert_ffn");
 }

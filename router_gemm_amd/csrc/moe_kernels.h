@@ -74,7 +74,7 @@ struct TileEntry {
   int32_t m0;
 };
 struct FfnPlan {
-  int tiled;       // 1: LDS-tiled persistent kernels (128-row token tiles), 0: streaming kernels
+  int tiled;       // 1: LDS-tiled persistent kernels (128-row token tiles; 64 for MX FP4), 0: streaming
   int mt;          // streaming: 16-row token subtiles per workgroup
   int gw;          // streaming: gate (and up) 16-row weight tiles per wave (2 -> 128 h columns)
   int bm;          // token rows per tile-list entry
@@ -83,11 +83,16 @@ struct FfnPlan {
 // Tile-list workspace header (int32 words): [0] tile count, [1] tiles of
 // group 0; the tile list follows.
 constexpr int kTileHdrWords = 64;
-FfnPlan ffn_plan(const FfnGroup *g, int ngroups);
+FfnPlan ffn_plan(const FfnGroup *g, int ngroups, int H);
 size_t ffn_tiles_bytes(const FfnPlan &p);
 // LDS-tiled variant (expert_gemm_tiled.hip); tiles built with 128-row entries.
 hipError_t launch_tiled_ffn(const FfnGroup *g, int ngroups, int H, const void *tiles, int32_t *hdr, int num_cus,
                             int site, hipStream_t st);
+// LDS-tiled variant for MX FP4 weights (expert_gemm_tiled_mx.hip): one group,
+// tiles built with 64-row entries; needs H and I multiples of 256.
+bool tiled_mx_supported(const FfnGroup &g, int H);
+hipError_t launch_tiled_mx_ffn(const FfnGroup &g, int H, const void *tiles, int32_t *hdr, int num_cus, int site,
+                               hipStream_t st);
 // Compute units of the current device (cached per device).
 int num_compute_units();
 // site: timing site of the gate/up launch (the down launch uses site + 1).

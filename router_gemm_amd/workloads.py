@@ -95,6 +95,10 @@ CONFIGS = {
         "decode_mxfp4", T=64, H=4096, E=352, k=8, I=1536, Is=1536, expert_dtype="mxfp4",
         router_std=1.0 / 64,
         description="Step-5 MoE shape with MX FP4 expert weights (E2M1, E8M0 per 32), decode T=64"),
+    "prefill_mxfp4": MoEConfig(
+        "prefill_mxfp4", T=8192, H=4096, E=352, k=8, I=1536, Is=1536, expert_dtype="mxfp4",
+        router_std=1.0 / 64, zipf_s=1.1, zipf_beta=_ZIPF_BETA_PREFILL,
+        description="the prefill layer with MX FP4 experts, T=8192, Zipf(1.1)-biased router"),
     "dense_ff_bf16": MoEConfig(
         "dense_ff_bf16", T=8192, H=4096, E=1, k=1, I=13824, Is=0, expert_dtype="bf16",
         router_std=1.0 / 64, dense=True,

@@ -62,6 +62,24 @@ def test_prefill_routing_grouping_and_sampled_outputs():
     assert np.array_equal(xs.cpu().numpy(), s_tok[toks])
 
 
+def test_prefill_mxfp4_sampled_outputs():
+    """The prefill layer with MX FP4 experts (LDS-tiled MX kernels, 64-row token
+    tiles; the bf16 shared expert on its own tiled launch): routing of every
+    token, outputs of a seeded sample of tokens plus the tokens routed to the
+    most loaded expert."""
+    cfg = W.get_config("prefill_mxfp4")
+    print("[prefill_mxfp4] building layer", flush=True)
+    lt = W.make_layer(cfg, dev())
+    x = W.make_x(cfg, dev())
+    OL = oracle_layer(lt)
+    ids_all, _, _, _ = oracle.route(OL, W.bf16_bits(x))
+    hot = np.bincount(ids_all.ravel(), minlength=cfg.E).argmax()
+    hot_tokens = np.nonzero((ids_all == hot).any(1))[0][:4]
+    sample = np.concatenate([np.random.default_rng(2).choice(cfg.T, 20, replace=False), hot_tokens])
+    st = check_forward(lt, x, OL=OL, sample=np.unique(sample))
+    print(f"[prefill_mxfp4] {st}", flush=True)
+
+
 def test_ep_share_primitives_with_triples():
     cfg = W.get_config("c4")
     print("[ep8_share_fp8] building layer", flush=True)

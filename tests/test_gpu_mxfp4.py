@@ -37,9 +37,12 @@ def _grouped_e4m3_rows(E, N, H, rng, empty_frac=0.3):
     (16, 300, 512, 256, torch.float32),     # ~19: 32-row tiles
     (3, 2000, 384, 128, torch.bfloat16),    # ~667: 64-row tiles; 3 and 1 chunks of 128 inputs (odd)
     (8, 517, 640, 384, torch.bfloat16),     # 5 and 3 chunks
-    (1, 100, 512, 1536, torch.float32),     # one expert, the routed width
+    (1, 100, 512, 1536, torch.float32),     # one expert, the routed width (tiled: 100 rows)
     (32, 150, 768, 640, torch.float32),     # 16-row tiles: 6 gate/up chunks (pipelined steps + a lone last step), 5 down chunks
     (8, 200, 1024, 512, torch.bfloat16),    # 32-row tiles: 8 and 4 chunks
+    # LDS-tiled MX kernels (>= 48 rows per expert, H and I multiples of 256):
+    (6, 1500, 1024, 768, torch.bfloat16),   # several 64-row token tiles per expert; 4 and 3 (odd) stages
+    (3, 700, 512, 256, torch.float32),      # 2 and 1 stages; ragged last token tile
 ])
 def test_mx_expert_ffn_matches_oracle(E, N, H, I, ydt):
     rng = np.random.default_rng(E * N + H)

@@ -205,6 +205,8 @@ def _grouped_rows(E, N, H, fp8, rng, empty_frac=0.3):
     (False, 5, 1000, 512, 128, torch.bfloat16),
     (True, 16, 777, 512, 256, torch.float32),
     (True, 3, 2000, 1024, 384, torch.bfloat16),
+    # many rows per expert but H % 256 != 0: the streaming kernels (64-row token tiles)
+    (True, 3, 600, 384, 256, torch.float32),
     # the dense FF layers' width (intermediate 13824) as one expert holding every row
     (False, 1, 300, 512, 13824, torch.float32),
     (True, 1, 300, 512, 13824, torch.bfloat16),
