@@ -33,7 +33,7 @@ _i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
 def build() -> str:
     """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
-           "-Wall", SRC_PATH, "-o", LIB_PATH + ".tmp", "-lm"]
+           "-Wall", "-Wpointer-arith", SRC_PATH, "-o", LIB_PATH + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(LIB_PATH + ".tmp", LIB_PATH)
     return LIB_PATH
@@ -87,6 +87,7 @@ def lib():
             "oref_forward_with_ids": [vp, vp, i64, vp, i64, vp, vp],
             "oref_forward_triples": [vp, vp, i64, vp, vp, vp, i64, vp, i64, vp],
             "oref_combine": [vp, vp, vp, i32, vp, i64, vp, i64, i64, vp],
+            "oref_backward": [vp, vp, i64, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp],
         }.items():
             f = getattr(L, name)
             f.restype = None
@@ -364,6 +365,27 @@ def combine(y_perm, perm_pos, gates, T, k=1, tok=None, shared=None):
     lib().oref_combine(_p(y_perm), _p(perm_pos), _p(tok), int(k), _p(gates), perm_pos.size,
                        _p(shared), T, H, _p(y))
     return y
+
+
+def backward(layer: Layer, x, ids, dy, token_list=None):
+    """Backward of the layer (bf16 experts) with experts fixed to ids -> dict of fp64 gradients:
+    dx [n,H], dw_gate_up [E,2I,H], dw_down [E,H,I], dw_shared_gate_up [2Is,H], dw_shared_down [H,Is],
+    dw_router [E,H], dbias [E] (weight gradients summed over the listed tokens)."""
+    assert layer.format == BF16, "the backward oracle covers bf16 experts"
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    dy = np.ascontiguousarray(dy, dtype=np.uint16)
+    T = x.shape[0]
+    tl, n = _tokens(token_list, T)
+    ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(T, layer.k)
+    E, H, I, Is = layer.E, layer.H, layer.I, layer.Is
+    out = dict(dx=np.empty((n, H)), dw_gate_up=np.empty((E, 2 * I, H)), dw_down=np.empty((E, H, I)),
+               dw_shared_gate_up=np.empty((2 * Is, H)) if Is else None,
+               dw_shared_down=np.empty((H, Is)) if Is else None,
+               dw_router=np.empty((E, H)), dbias=np.empty(E))
+    lib().oref_backward(layer.ref, _p(x), T, _p(ids), _p(dy), _p(tl), n, _p(out["dx"]), _p(out["dw_gate_up"]),
+                        _p(out["dw_down"]), _p(out["dw_shared_gate_up"]), _p(out["dw_shared_down"]),
+                        _p(out["dw_router"]), _p(out["dbias"]))
+    return out
 
 
 def num_threads() -> int:

@@ -557,6 +557,121 @@ void oref_combine(const double *y_perm, const int32_t *perm_pos, const int32_t *
   }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Backward (bf16 experts)                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* One expert's forward and backward for one token a[H] with output gradient
+ * d_o[H] (already multiplied by the gate):
+ *   zg = a Wg^T, zu = a Wu^T, h = silu(zg) zu, o = h Wd^T       (returned: o)
+ *   dh = d_o Wd, dzu = dh silu(zg), dzg = dh zu silu'(zg),
+ *   silu'(z) = s (1 + z (1 - s)), s = sigmoid(z)
+ *   da += dzg Wg + dzu Wu;  dWd += d_o (x) h;  dWg += dzg (x) a;  dWu += dzu (x) a.
+ * Weight gradients accumulate into dwgu [2I, H] and dwd [H, I] (may be NULL). */
+static void expert_backward(int H, int I, const uint16_t *wgu, const uint16_t *wd, const double *a,
+                            const double *d_o, double *o, double *da, double *dwgu, double *dwd) {
+  double *zg = (double *)malloc(sizeof(double) * (size_t)I * 5);
+  double *zu = zg + I, *hh = zu + I, *dzg = hh + I, *dzu = dzg + I;
+  for (int n = 0; n < I; ++n) {
+    double g = 0.0, u = 0.0;
+    for (int h = 0; h < H; ++h) {
+      g += a[h] * oref_bf16_decode(wgu[(int64_t)n * H + h]);
+      u += a[h] * oref_bf16_decode(wgu[(int64_t)(I + n) * H + h]);
+    }
+    zg[n] = g; zu[n] = u; hh[n] = silu(g) * u;
+  }
+  if (o)
+    for (int c = 0; c < H; ++c) {
+      double acc = 0.0;
+      for (int n = 0; n < I; ++n) acc += hh[n] * oref_bf16_decode(wd[(int64_t)c * I + n]);
+      o[c] = acc;
+    }
+  for (int n = 0; n < I; ++n) {
+    double dh = 0.0;
+    for (int c = 0; c < H; ++c) dh += d_o[c] * oref_bf16_decode(wd[(int64_t)c * I + n]);
+    const double sg = 1.0 / (1.0 + exp(-zg[n]));
+    dzu[n] = dh * zg[n] * sg;
+    dzg[n] = dh * zu[n] * sg * (1.0 + zg[n] * (1.0 - sg));
+  }
+  for (int h = 0; h < H; ++h) {
+    double acc = 0.0;
+    for (int n = 0; n < I; ++n)
+      acc += dzg[n] * oref_bf16_decode(wgu[(int64_t)n * H + h]) + dzu[n] * oref_bf16_decode(wgu[(int64_t)(I + n) * H + h]);
+    da[h] += acc;
+  }
+  if (dwd)
+    for (int c = 0; c < H; ++c)
+      for (int n = 0; n < I; ++n) dwd[(int64_t)c * I + n] += d_o[c] * hh[n];
+  if (dwgu)
+    for (int n = 0; n < I; ++n)
+      for (int h = 0; h < H; ++h) {
+        dwgu[(int64_t)n * H + h] += dzg[n] * a[h];
+        dwgu[(int64_t)(I + n) * H + h] += dzu[n] * a[h];
+      }
+  free(zg);
+}
+
+void oref_backward(const oref_layer *L, const uint16_t *x, int64_t T, const int32_t *ids,
+                   const uint16_t *dy, const int64_t *token_list, int64_t n_list,
+                   double *dx, double *dwgu, double *dwd, double *dwsgu, double *dwsd,
+                   double *dwr, double *dbias) {
+  const int H = L->hidden, I = L->inter, E = L->num_experts, k = L->top_k, Is = L->shared_inter;
+  if (!token_list) n_list = T;
+  if (dwgu) memset(dwgu, 0, sizeof(double) * (size_t)E * 2 * I * H);
+  if (dwd) memset(dwd, 0, sizeof(double) * (size_t)E * H * I);
+  if (dwsgu && Is > 0) memset(dwsgu, 0, sizeof(double) * (size_t)2 * Is * H);
+  if (dwsd && Is > 0) memset(dwsd, 0, sizeof(double) * (size_t)H * Is);
+  if (dwr) memset(dwr, 0, sizeof(double) * (size_t)E * H);
+  if (dbias) memset(dbias, 0, sizeof(double) * (size_t)E);
+  double *a = (double *)malloc(sizeof(double) * (size_t)H * 3);
+  double *g_dy = a + H, *o = g_dy + H;
+  double *l = (double *)malloc(sizeof(double) * (size_t)(E + 3 * k + 1));
+  double *g = l + E, *dg = g + k, *dl = dg + k;
+  /* tokens one after another: the weight gradients are sums over tokens */
+  for (int64_t li = 0; li < n_list; ++li) {
+    const int64_t t = tok_of(token_list, li);
+    const uint16_t *xr = x + t * H;
+    const int32_t *id = ids + t * k;
+    double *dxt = dx + li * H;
+    for (int h = 0; h < H; ++h) { a[h] = oref_bf16_decode(xr[h]); dxt[h] = 0.0; }
+    /* gates: softmax over the chosen logits */
+    token_logits(L, xr, l);
+    double lmax = -INFINITY;
+    for (int j = 0; j < k; ++j) if (l[id[j]] > lmax) lmax = l[id[j]];
+    double den = 0.0;
+    for (int j = 0; j < k; ++j) { g[j] = exp(l[id[j]] - lmax); den += g[j]; }
+    for (int j = 0; j < k; ++j) g[j] /= den;
+    /* routed experts: d_o = g_j dy_t; dg_j = <dy_t, o_j> */
+    for (int j = 0; j < k; ++j) {
+      const int e = id[j];
+      for (int c = 0; c < H; ++c) g_dy[c] = g[j] * oref_bf16_decode(dy[t * H + c]);
+      expert_backward(H, I, (const uint16_t *)L->w_gate_up + (int64_t)e * 2 * I * H,
+                      (const uint16_t *)L->w_down + (int64_t)e * H * I, a, g_dy,
+                      o, dxt, dwgu ? dwgu + (int64_t)e * 2 * I * H : NULL, dwd ? dwd + (int64_t)e * H * I : NULL);
+      double acc = 0.0;
+      for (int c = 0; c < H; ++c) acc += oref_bf16_decode(dy[t * H + c]) * o[c];
+      dg[j] = acc;
+    }
+    /* softmax backward over the chosen logits, then the router */
+    double sdg = 0.0;
+    for (int j = 0; j < k; ++j) sdg += g[j] * dg[j];
+    for (int j = 0; j < k; ++j) {
+      dl[j] = g[j] * (dg[j] - sdg);
+      const int e = id[j];
+      const uint16_t *wr = L->w_router + (int64_t)e * H;
+      for (int h = 0; h < H; ++h) dxt[h] += dl[j] * oref_bf16_decode(wr[h]);
+      if (dwr) for (int h = 0; h < H; ++h) dwr[(int64_t)e * H + h] += dl[j] * a[h];
+      if (dbias) dbias[e] += dl[j];
+    }
+    /* shared expert, unweighted */
+    if (Is > 0 && L->w_shared_gate_up) {
+      for (int c = 0; c < H; ++c) g_dy[c] = oref_bf16_decode(dy[t * H + c]);
+      expert_backward(H, Is, L->w_shared_gate_up, L->w_shared_down, a, g_dy, NULL, dxt, dwsgu, dwsd);
+    }
+  }
+  free(a); free(l);
+}
+
 int oref_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

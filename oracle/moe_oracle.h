@@ -176,6 +176,24 @@ void oref_combine(const double *y_perm, const int32_t *perm_pos, const int32_t *
                   int32_t k, const float *gate, int64_t N, const double *shared,
                   int64_t T, int64_t H, double *y);
 
+/* ---- backward (bf16 experts) ------------------------------------------ */
+/* Gradients of the layer with its routed experts fixed to ids [T, k] (the
+ * forward's choice), for an output gradient dy (bf16 [T, H]), in fp64:
+ *   gates g = softmax over the chosen logits; y[t] = Shared(x_t) + sum_j g_j FFN_j(x_t);
+ *   dg_j = <dy_t, FFN_j(x_t)>, dl_j = g_j (dg_j - sum_m g_m dg_m);
+ *   dx_t = Shared'(x_t)^T dy_t + sum_j [ FFN_j'(x_t)^T (g_j dy_t) + dl_j W_r[e_j] ];
+ *   dW_gu[e], dW_d[e]: sums over the (token, slot) pairs routed to e of the
+ *   FFN's weight gradients for output gradient g_j dy_t; the shared expert's
+ *   likewise with gradient dy_t; dW_r[e] = sum dl_j x_t, dbias[e] = sum dl_j.
+ * The gradient of the layer as a function (no storage rounding of h).
+ * token_list restricts the sums to the listed tokens (NULL = all T);
+ * dx [n_list, H]; weight gradients over the listed tokens only.  Any
+ * gradient pointer except dx may be NULL. */
+void oref_backward(const oref_layer *L, const uint16_t *x, int64_t T, const int32_t *ids,
+                   const uint16_t *dy, const int64_t *token_list, int64_t n_list,
+                   double *dx, double *dwgu, double *dwd, double *dwsgu, double *dwsd,
+                   double *dwr, double *dbias);
+
 int oref_num_threads(void);
 
 #ifdef __cplusplus
