@@ -5,7 +5,8 @@ One step = one pass of the whole layer (router, grouping, routed expert
 gate/up + SwiGLU and down, shared expert, combine) over one batch of
 synthetic tokens already resident in HBM.  Prints one JSON line.
 
-  python bench.py [--workload decode_bf16|decode_fp8|decode_mxfp4|prefill_fp8|ep8_share_fp8|dense_ff_bf16|small_bf16]
+  python bench.py [--workload decode_bf16|decode_fp8|decode_mxfp4|prefill_fp8|ep8_share_fp8|dense_ff_bf16|
+                              train_bf16|small_bf16]
                   [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 
 The default workload is the bf16 decode layer (T=64 tokens, hidden 4096,
@@ -117,6 +118,9 @@ def main():
     print(f"[bench] building {cfg.name} on {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
     lt = W.make_layer(cfg, dev)
     x = W.make_x(cfg, dev)
+    if cfg.name.startswith("train"):
+        bench_train(args, cfg, lt, x, dev)
+        return
     T, H, E, I, Is = cfg.T, cfg.H, cfg.E, cfg.I, cfg.Is
     fp8 = cfg.expert_dtype != "bf16"     # activations and h stored as e4m3 + 1x128 scales
     mx = cfg.expert_dtype == "mxfp4"
@@ -292,6 +296,147 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, lt, x, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def bench_train(args, cfg, lt, x, dev):
+    """Training step of the layer: moe_forward then moe_backward (all weight,
+    router and input gradients) on one batch of tokens."""
+    import numpy as np
+    import torch
+
+    from router_gemm_amd import binding as B
+    from router_gemm_amd import workloads as W
+
+    T, H, E, I, Is, k = cfg.T, cfg.H, cfg.E, cfg.I, cfg.Is, cfg.k
+    N = T * k
+    dy = W.make_dy(cfg, dev)
+    layer = B.Layer.from_tensors(lt)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gts = torch.empty((T, k), dtype=torch.float32, device=dev)
+    ws_f = B.workspace(layer, T, N, dev)
+    ws_b = B.backward_workspace(layer, T, dev)
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+    grads = dict(dx=f32(T, H), dw_gate_up=f32(E, 2 * I, H), dw_down=f32(E, H, I),
+                 dw_shared_gate_up=f32(2 * Is, H) if Is else None, dw_shared_down=f32(H, Is) if Is else None,
+                 dw_router=f32(E, H), dbias=f32(E) if lt.router_bias is not None else None)
+
+    def step():
+        B.moe_forward(layer, x, T, y, topk_ids=ids, topk_gates=gts, ws=ws_f)
+        B.moe_backward(layer, x, T, ids, gts, dy, ws=ws_b, **grads)
+
+    step()
+    torch.cuda.synchronize()
+    counts = np.bincount(ids.cpu().numpy().ravel(), minlength=E)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    gemm_sites = {9: "bwd_dgrad_gemm", 10: "bwd_wgrad_gemm"}
+    for sidx in gemm_sites:
+        B.timing_arm(sidx, 8 * K)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record()
+    for _ in range(K):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    gemm = {nm: B.timing_read(sidx) for sidx, nm in gemm_sites.items()}
+    ms_per_step = ev0.elapsed_time(ev1) / K
+    t_s = ms_per_step / 1e3
+
+    # ---- algorithmic work.  Expert rows: N routed assignments + T shared-expert rows.
+    ih = N * I * H + T * Is * H
+    fwd_flops = 2.0 * 3 * ih + 2.0 * T * E * H
+    # model flops of a training step: forward, plus twice the expert GEMM flops for the
+    # data and weight gradients, plus the router's two gradient products
+    model_flops = fwd_flops + 2.0 * 6 * ih + 2.0 * 2 * N * H
+    # the backward's grouped GEMM launches: recompute of z (2IH), dy W_down (IH), dz W_gate_up
+    # (2IH) per row = dgrad site; dW_down (IH) and dW_gate_up (2IH) per row = wgrad site
+    dgrad_flops, wgrad_flops = 2.0 * 5 * ih, 2.0 * 3 * ih
+    g_ms = {nm: ms / K for nm, (ms, n) in gemm.items()}
+    g_launch = {nm: max(n // K, 1) for nm, (ms, n) in gemm.items()}
+    gemm_ms = sum(g_ms.values())
+    peak = PEAK_TFLOPS["bf16"]
+    achieved = (dgrad_flops + wgrad_flops) / (gemm_ms / 1e3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": None,
+            "traffic_note": "no counters taken on these kernel sources",
+            "library_source_hash": library_source_hash(),
+            "kernel": "grouped bf16 GEMM of the backward (all its launches in a step: recompute, dgrad, wgrad)",
+            "kernel_ms_per_step": round(gemm_ms, 4),
+            "launches_per_step": sum(g_launch.values()),
+            "algorithmic_flops_per_step": dgrad_flops + wgrad_flops,
+            "per_site": {nm: {"ms_per_step": round(g_ms[nm], 4), "launches_per_step": g_launch[nm],
+                              "tflops": round(f / (g_ms[nm] / 1e3) / 1e12, 1) if g_ms[nm] > 0 else None}
+                         for nm, f in (("bwd_dgrad_gemm", dgrad_flops), ("bwd_wgrad_gemm", wgrad_flops))}}
+
+    # per-kernel breakdown: a separate pass with every launch site timed
+    sites = {0: "router_logits", 1: "router_topk", 2: "sort", 3: "gather", 4: "gate_up", 5: "down", 8: "combine",
+             9: "bwd_dgrad_gemm", 10: "bwd_wgrad_gemm"}
+    for sidx in sites:
+        B.timing_arm(sidx, 8 * K)
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    breakdown = {}
+    for sidx, nm in sites.items():
+        ms, n = B.timing_read(sidx)
+        if n:
+            breakdown[nm] = round(1e3 * ms / K, 1)
+    out = {
+        "metric": METRIC, "value": round(T / t_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "step": "moe_forward + moe_backward (all gradients)", "tokens": T,
+                   "hidden": H, "experts": E, "top_k": k, "inter": I, "shared_inter": Is, "expert_dtype": "bf16",
+                   "assignments": N, "active_experts": int((counts > 0).sum()),
+                   "min_rows_per_expert": int(counts.min()), "max_rows_per_expert": int(counts.max()),
+                   "parallelism": "1 GPU"},
+        "layer": {"model_tflops": round(model_flops / t_s / 1e12, 2), "mfma_util": round(model_flops / t_s / 1e12 / peak, 4),
+                  "model_flops_per_step": model_flops, "wall_s": round(wall, 4)},
+        "roofline": roof,
+        "breakdown_us_per_step": breakdown,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_train(cfg, lt, x, dy, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_train(cfg, lt, x, dy, target_s):
+    """The fp64 oracle's forward and backward (input gradient only: its weight
+    gradients would be 53 GB of fp64 at this shape) on a sample of tokens."""
+    import numpy as np
+
+    import oracle
+    from router_gemm_amd import workloads as W
+
+    print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+    h = W.host_layer_arrays(lt)
+    L = oracle.Layer(cfg.H, cfg.I, cfg.E, cfg.k, "bf16", h["w_router"], h["w_gate_up"], h["w_down"],
+                     router_bias=h["router_bias"], w_shared_gate_up=h["w_shared_gate_up"],
+                     w_shared_down=h["w_shared_down"])
+    xb, dyb = W.bf16_bits(x), W.bf16_bits(dy)
+    n = 8
+    sample = np.sort(np.random.default_rng(0).choice(cfg.T, n, replace=False))
+    ids = np.zeros((cfg.T, cfg.k), dtype=np.int32)        # rows outside the sample are never read
+    ids[sample] = oracle.route(L, xb, token_list=sample)[0]
+    done, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(L, xb, token_list=sample)
+        oracle.backward(L, xb, ids, dyb, token_list=sample, weights=False)
+        done += n
+        el = time.perf_counter() - t0
+        if el >= target_s or done >= 8 * n:
+            break
+    return {"value": round(done / el, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} of the {cfg.T} tokens of {cfg.name} (seeded choice): forward of the layer, then "
+                      f"the backward's input gradient (no weight gradients), {done // n} pass(es) in {el:.1f} s; "
+                      f"the sample's routing is done once beforehand, untimed"}
 
 
 def cpu_baseline(cfg, lt, x, target_s):

@@ -120,9 +120,9 @@ typedef struct moe_layer {
   const void *w_shared_down;
 } moe_layer;
 
-/* Workspace bytes that suffice for every call below on this layer with up to
- * T tokens and N assignments (N = T*k for routed calls).  Host-only; 0 on
- * invalid arguments. */
+/* Workspace bytes that suffice for every call below except moe_backward on
+ * this layer with up to T tokens and N assignments (N = T*k for routed
+ * calls).  Host-only; 0 on invalid arguments. */
 size_t moe_workspace_bytes(const moe_layer *layer, int64_t T, int64_t N);
 
 /* Router: logits, top-k selection and gates.
@@ -202,6 +202,42 @@ moe_status moe_forward(const moe_layer *layer, const void *x, int64_t T,
                        void *y, int32_t out_dtype,
                        int32_t *topk_ids, float *topk_gates,
                        void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes moe_backward needs for up to T tokens (moe_workspace_bytes
+ * does not cover moe_backward).  Host-only; 0 on invalid arguments. */
+size_t moe_backward_workspace_bytes(const moe_layer *layer, int64_t T);
+
+/* Backward of the whole layer with bf16 experts, for training: the gradients
+ * of L = sum_t <y[t], dy[t]> for the forward above with the routed experts
+ * held fixed at topk_ids ("Step-5-Preview", section "Full-Depth H100
+ * Benchmark": the layer is trained in BF16; section "Model Architecture":
+ * learned router, top-8, one shared expert).  With g = softmax over the chosen
+ * logits l_j and o_j = FFN_{e_j}(x):
+ *   dg_j = <dy, o_j>;  dl_j = g_j (dg_j - sum_m g_m dg_m)    (softmax backward)
+ *   each expert's SwiGLU FFN is differentiated with output gradient g_j dy
+ *   (shared expert: dy); dW_router[e] += dl_j x, dbias[e] += dl_j,
+ *   dx += dl_j W_router[e_j].
+ * Recomputes the expert pre-activations from x (nothing is kept from the
+ * forward but topk_ids and topk_gates).  GEMM inputs are bf16 (x, dy, the
+ * weights, g * h and the gradient of the pre-activations, rounded to bf16),
+ * accumulation fp32; per-row and per-token reductions in a fixed order.
+ *   x            bf16 [T, H]  (the forward's input)
+ *   topk_ids     int32 [T, k] (the forward's choice; an id outside [0, E) is skipped)
+ *   topk_gates   f32 [T, k]   (the forward's gates: softmax over the chosen logits)
+ *   dy           bf16 [T, H]  (gradient of the layer output)
+ *   dx           f32 [T, H] out
+ *   dw_gate_up   f32 [E, 2I, H] out;  dw_down f32 [E, H, I] out
+ *   dw_shared_gate_up f32 [2Is, H] out, dw_shared_down f32 [H, Is] out (NULL if Is == 0)
+ *   dw_router    f32 [E, H] out;  dbias f32 [E] out or NULL
+ * Gradients are written, not accumulated; experts that receive no token get
+ * zero gradients.  MOE_EUNSUPPORTED unless expert_dtype == MOE_BF16; top_k >= 1
+ * and w_router are required.  T == 0 is a no-op (nothing written). */
+moe_status moe_backward(const moe_layer *layer, const void *x, int64_t T,
+                        const int32_t *topk_ids, const float *topk_gates, const void *dy,
+                        float *dx, float *dw_gate_up, float *dw_down,
+                        float *dw_shared_gate_up, float *dw_shared_down,
+                        float *dw_router, float *dbias,
+                        void *ws, size_t ws_bytes, void *stream);
 
 /* Static string naming a status. */
 const char *moe_status_string(moe_status s);

@@ -30,7 +30,9 @@ typedef enum moe_site {
   MOE_SITE_SHARED_GATE_UP = 6,  /* reserved (no launch records here at present) */
   MOE_SITE_SHARED_DOWN = 7,     /* reserved (no launch records here at present) */
   MOE_SITE_COMBINE = 8,         /* weighted combine */
-  MOE_SITE_COUNT = 9
+  MOE_SITE_BWD_DGRAD = 9,       /* backward: row-grouped GEMMs (z recompute, dy W_down, dz W_gate_up) */
+  MOE_SITE_BWD_WGRAD = 10,      /* backward: token-grouped weight-gradient GEMMs */
+  MOE_SITE_COUNT = 11
 } moe_site;
 
 /* Arm `site` for its next `capacity` launches (capacity in [1, 100000]).

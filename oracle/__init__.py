@@ -367,10 +367,11 @@ def combine(y_perm, perm_pos, gates, T, k=1, tok=None, shared=None):
     return y
 
 
-def backward(layer: Layer, x, ids, dy, token_list=None):
+def backward(layer: Layer, x, ids, dy, token_list=None, weights=True):
     """Backward of the layer (bf16 experts) with experts fixed to ids -> dict of fp64 gradients:
     dx [n,H], dw_gate_up [E,2I,H], dw_down [E,H,I], dw_shared_gate_up [2Is,H], dw_shared_down [H,Is],
-    dw_router [E,H], dbias [E] (weight gradients summed over the listed tokens)."""
+    dw_router [E,H], dbias [E] (weight gradients summed over the listed tokens).
+    weights=False: dx only (the weight gradients are not formed; they are None)."""
     assert layer.format == BF16, "the backward oracle covers bf16 experts"
     x = np.ascontiguousarray(x, dtype=np.uint16)
     dy = np.ascontiguousarray(dy, dtype=np.uint16)
@@ -378,14 +379,53 @@ def backward(layer: Layer, x, ids, dy, token_list=None):
     tl, n = _tokens(token_list, T)
     ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(T, layer.k)
     E, H, I, Is = layer.E, layer.H, layer.I, layer.Is
-    out = dict(dx=np.empty((n, H)), dw_gate_up=np.empty((E, 2 * I, H)), dw_down=np.empty((E, H, I)),
-               dw_shared_gate_up=np.empty((2 * Is, H)) if Is else None,
-               dw_shared_down=np.empty((H, Is)) if Is else None,
-               dw_router=np.empty((E, H)), dbias=np.empty(E))
+    w = weights
+    out = dict(dx=np.empty((n, H)), dw_gate_up=np.empty((E, 2 * I, H)) if w else None,
+               dw_down=np.empty((E, H, I)) if w else None,
+               dw_shared_gate_up=np.empty((2 * Is, H)) if Is and w else None,
+               dw_shared_down=np.empty((H, Is)) if Is and w else None,
+               dw_router=np.empty((E, H)) if w else None, dbias=np.empty(E) if w else None)
     lib().oref_backward(layer.ref, _p(x), T, _p(ids), _p(dy), _p(tl), n, _p(out["dx"]), _p(out["dw_gate_up"]),
                         _p(out["dw_down"]), _p(out["dw_shared_gate_up"]), _p(out["dw_shared_down"]),
                         _p(out["dw_router"]), _p(out["dbias"]))
     return out
+
+
+def _bf16_f64(b) -> np.ndarray:
+    """bf16 bits -> fp64: a bf16 value is the binary32 value with the same top 16 bits."""
+    b = np.asarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def expert_weight_grads(layer: Layer, x, ids, dy, e):
+    """dW_gate_up[e] [2I,H] and dW_down[e] [H,I] (fp64) of the layer's backward
+    (bf16 experts, experts fixed to ids), summed over every token routed to e.
+
+    Only expert e's slots enter these two gradients: with g the slot's gate
+    (softmax over the token's chosen logits) the expert sees output gradient
+    g dy, so dW_down = sum (g dy) h^T and dW_gate_up = sum dz x^T with the
+    SwiGLU backward dz.  numpy matmuls serve as the products, one batch of
+    the expert's tokens (for sizes where the whole backward is out of reach)."""
+    assert layer.format == BF16
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    T = x.shape[0]
+    ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(T, layer.k)
+    H, I = layer.H, layer.I
+    ts, js = np.nonzero(ids == e)
+    if ts.size == 0:
+        return np.zeros((2 * I, H)), np.zeros((H, I))
+    g = gates_for_ids(layer, x, ids[ts], token_list=ts)[np.arange(ts.size), js]
+    X = _bf16_f64(x[ts])
+    dO = g[:, None] * _bf16_f64(np.asarray(dy, dtype=np.uint16)[ts])
+    wgu = _bf16_f64(layer.w_gate_up[e])
+    wd = _bf16_f64(layer.w_down[e])
+    z = X @ wgu.T
+    zg, zu = z[:, :I], z[:, I:]
+    sg = 1.0 / (1.0 + np.exp(-zg))
+    h = zg * sg * zu
+    dh = dO @ wd
+    dz = np.concatenate([dh * zu * sg * (1.0 + zg * (1.0 - sg)), dh * zg * sg], axis=1)
+    return dz.T @ X, dO.T @ h
 
 
 def num_threads() -> int:

@@ -45,7 +45,8 @@ class MoELayerC(C.Structure):
 
 
 EXPORTS = ["moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_forward", "moe_status_string", "moe_last_error", "moe_timing_arm", "moe_timing_read"]
+           "moe_forward", "moe_backward_workspace_bytes", "moe_backward", "moe_status_string",
+           "moe_last_error", "moe_timing_arm", "moe_timing_read"]
 
 _lib = None
 
@@ -70,6 +71,10 @@ def lib() -> C.CDLL:
         L.moe_combine.argtypes = [vp, vp, i32, vp, vp, vp, i64, vp, i32, i64, vp, i32, vp, sz, vp]
         L.moe_forward.restype = C.c_int
         L.moe_forward.argtypes = [vp, vp, i64, vp, i32, vp, vp, vp, sz, vp]
+        L.moe_backward_workspace_bytes.restype = sz
+        L.moe_backward_workspace_bytes.argtypes = [vp, i64]
+        L.moe_backward.restype = C.c_int
+        L.moe_backward.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_status_string.restype = C.c_char_p
         L.moe_status_string.argtypes = [C.c_int]
         L.moe_last_error.restype = C.c_char_p
@@ -185,6 +190,23 @@ def moe_forward(layer: Layer, x, T, y, out_dtype=None, topk_ids=None, topk_gates
     od = dtype_code(y) if out_dtype is None else out_dtype
     _check(lib().moe_forward(layer.ref, _ptr(x), T, _ptr(y), od, _ptr(topk_ids), _ptr(topk_gates),
                              w, nb, _stream(stream)))
+
+
+def moe_backward_workspace_bytes(layer: Layer, T: int) -> int:
+    return int(lib().moe_backward_workspace_bytes(layer.ref, T))
+
+
+def backward_workspace(layer: Layer, T: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(moe_backward_workspace_bytes(layer, T), 256), dtype=torch.uint8, device=device)
+
+
+def moe_backward(layer: Layer, x, T, topk_ids, topk_gates, dy, dx, dw_gate_up, dw_down,
+                 dw_shared_gate_up, dw_shared_down, dw_router, dbias=None, ws=None, stream=None):
+    w, nb = _ws(ws)
+    _check(lib().moe_backward(layer.ref, _ptr(x), T, _ptr(topk_ids), _ptr(topk_gates), _ptr(dy),
+                              _ptr(dx), _ptr(dw_gate_up), _ptr(dw_down), _ptr(dw_shared_gate_up),
+                              _ptr(dw_shared_down), _ptr(dw_router), _ptr(dbias), w, nb,
+                              _stream(stream)))
 
 
 def timing_arm(site: int, capacity: int):

@@ -1,0 +1,428 @@
+// backward.hip -- backward of the routed MoE layer with bf16 experts:
+// recompute of the expert pre-activations, the SwiGLU and softmax-gate
+// backward, data and weight gradients of the routed and shared experts, and
+// the router gradients.  The gradients are those of the layer
+//   y[t] = Shared(x[t]) + sum_j g[t,j] FFN_{e_j}(x[t]),  g = softmax over the chosen logits
+// ("Step-5-Preview", "Model Architecture": learned top-8 router, one shared
+// expert, SwiGLU experts; "Full-Depth H100 Benchmark": the layer is trained
+// in BF16).
+//
+// Every GEMM of the backward is one grouped bf16 kernel, C_g = A_g B_g^T
+// over K, whose operands are each stored either K-contiguous ("N" layout:
+// element (r, k) at r*rs + k) or row-contiguous ("T" layout: at k*ks + r).
+// Groups are experts: either they own token rows (the M dimension: forward
+// recompute and data gradients) or a token range (the K dimension: weight
+// gradients).  128x128 output tiles, 64-wide K steps staged in LDS through
+// registers (the next step's global loads are in flight during the current
+// step's MFMAs), T-layout operands transposed on the way into LDS, fp32
+// accumulation and output.
+
+#include <algorithm>
+
+#include "../../include/moe_timing.h"
+#include "moe_common.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+namespace {
+constexpr int BT = 128;          // output tile rows and columns
+constexpr int BK = 64;           // K step
+constexpr int TILE = BT * BK;    // bf16 elements of one staged operand tile
+constexpr int kGemmThreads = 256;
+}  // namespace
+
+// Operand element (r, k) of group g: base + g * gstride + r * rs + k * ks (bf16).
+struct GemmOp {
+  const uint16_t *base;
+  int64_t gstride, rs, ks;
+};
+
+struct GemmArgs {
+  GemmOp a, b;
+  float *c;            // fp32 output, C_g at c + g * cgstride, row pitch ldc
+  int64_t ldc, cgstride;
+  const int32_t *off;  // [G+1] segment offsets, or NULL: one group owning [0, rows) / [0, K)
+  int G, M, N, K;      // M: rows (row-segmented: all rows); K: reduction length (K-segmented: all of it)
+  int ntm, ntn;        // tiles along M (K-segmented) and N
+  const TileEntry *tiles;  // row-segmented: 128-row tile list and its header
+  const int32_t *hdr;
+};
+
+// LDS position (in bf16 elements) of operand element (r, k) of a staged tile:
+// rows of 64 k, 16-byte units permuted per row so that both the staging
+// writes and the fragment reads spread over the banks.  N-layout tiles are
+// written 8 k of one row at a time, T-layout tiles 4 k of one row per lane
+// with 8 consecutive rows per lane, hence the two permutations.
+template <bool T>
+__device__ __forceinline__ int lds_pos(int r, int k) {
+  const int sw = T ? ((r >> 3) & 7) : (r & 7);
+  return r * BK + (((k >> 3) ^ sw) << 3) + (k & 7);
+}
+
+// Global loads of one operand's 128 x 64 tile into registers: 4 x 16 bytes
+// per thread.  N layout: chunk q = tid + 256 j holds row q / 8, k 8 (q % 8)
+// .. +7.  T layout: the thread's rows are 8 (tid % 16) .. +7 and its k are
+// 4 (tid / 16) + j.  Rows >= nr and k >= nk read as zero (rows come in whole
+// chunks: every row count and pitch here is a multiple of 8).
+template <bool T>
+__device__ __forceinline__ void tile_load(const uint16_t *base, int64_t rs, int64_t ks, int r0, int nr, int k0,
+                                          int nk, i32x4 (&v)[4]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int r, k;
+    int64_t o;
+    if (!T) {
+      const int q = tid + kGemmThreads * j;
+      r = r0 + (q >> 3);
+      k = k0 + ((q & 7) << 3);
+      o = (int64_t)r * rs + k;
+    } else {
+      r = r0 + ((tid & 15) << 3);
+      k = k0 + ((tid >> 4) << 2) + j;
+      o = (int64_t)k * ks + r;
+    }
+    v[j] = (r < nr && k < nk) ? load16(base + o) : i32x4{0, 0, 0, 0};
+  }
+}
+
+template <bool T>
+__device__ __forceinline__ void tile_store(uint16_t *s, const i32x4 (&v)[4]) {
+  const int tid = threadIdx.x;
+  if (!T) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = tid + kGemmThreads * j;
+      *reinterpret_cast<i32x4 *>(s + lds_pos<false>(q >> 3, (q & 7) << 3)) = v[j];
+    }
+  } else {
+    // transpose 4 k x 8 rows: row u of the thread gets k .. k+3 as 8 bytes
+    const int r = (tid & 15) << 3, k = (tid >> 4) << 2;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int w = u >> 1;
+      uint32_t lo, hi;
+      if (u & 1) {
+        lo = ((uint32_t)v[0][w] >> 16) | ((uint32_t)v[1][w] & 0xFFFF0000u);
+        hi = ((uint32_t)v[2][w] >> 16) | ((uint32_t)v[3][w] & 0xFFFF0000u);
+      } else {
+        lo = ((uint32_t)v[0][w] & 0xFFFFu) | ((uint32_t)v[1][w] << 16);
+        hi = ((uint32_t)v[2][w] & 0xFFFFu) | ((uint32_t)v[3][w] << 16);
+      }
+      *reinterpret_cast<uint2 *>(s + lds_pos<true>(r + u, k)) = uint2{lo, hi};
+    }
+  }
+}
+
+template <bool AT, bool BTL>
+__global__ __launch_bounds__(kGemmThreads) void grouped_gemm_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sa[2][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sb[2][TILE];
+  const bool kseg = a.tiles == nullptr;
+  int g, m0, mend, n0, kbeg, kend;
+  if (kseg) {
+    const int per = a.ntm * a.ntn;
+    g = blockIdx.x / per;
+    const int r = blockIdx.x - g * per;
+    m0 = (r / a.ntn) * BT;
+    n0 = (r % a.ntn) * BT;
+    mend = a.M;
+    kbeg = a.off ? a.off[g] : 0;
+    kend = a.off ? a.off[g + 1] : a.K;
+  } else {
+    const int tile = blockIdx.x / a.ntn;
+    if (tile >= a.hdr[0]) return;
+    n0 = (blockIdx.x - tile * a.ntn) * BT;
+    const TileEntry te = a.tiles[tile];
+    g = te.ge & 0xFFFFFF;
+    const int rb = a.off ? a.off[g] : 0;
+    m0 = rb + te.m0;
+    mend = a.off ? a.off[g + 1] : a.M;
+    kbeg = 0;
+    kend = a.K;
+  }
+  // Row-segmented: A rows are global rows (gstride 0) and B is the group's
+  // weight; K-segmented: both operands are indexed by the global K (token)
+  // index and only the output is per group.
+  const uint16_t *abase = a.a.base + (int64_t)g * a.a.gstride;
+  const uint16_t *bbase = a.b.base + (int64_t)g * a.b.gstride;
+  const int lane = lane_id(), w = wave_id();
+  const int wm = (w & 1) * 64, wn = (w >> 1) * 64;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nsteps = (int)cdiv(kend - kbeg, BK);
+  i32x4 va[4], vb[4];
+  if (nsteps > 0) {
+    tile_load<AT>(abase, a.a.rs, a.a.ks, m0, mend, kbeg, kend, va);
+    tile_load<BTL>(bbase, a.b.rs, a.b.ks, n0, a.N, kbeg, kend, vb);
+    tile_store<AT>(sa[0], va);
+    tile_store<BTL>(sb[0], vb);
+    __syncthreads();
+  }
+  for (int s = 0; s < nsteps; ++s) {
+    const int buf = s & 1;
+    const bool more = s + 1 < nsteps;
+    if (more) {
+      const int k1 = kbeg + (s + 1) * BK;
+      tile_load<AT>(abase, a.a.rs, a.a.ks, m0, mend, k1, kend, va);
+      tile_load<BTL>(bbase, a.b.rs, a.b.ks, n0, a.N, k1, kend, vb);
+    }
+#pragma unroll
+    for (int kk = 0; kk < BK / 32; ++kk) {
+      bf16x8 fa[4], fb[4];
+      const int kf = kk * 32 + 8 * (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fa[i] = *reinterpret_cast<const bf16x8 *>(sa[buf] + lds_pos<AT>(wm + 16 * i + (lane & 15), kf));
+        fb[i] = *reinterpret_cast<const bf16x8 *>(sb[buf] + lds_pos<BTL>(wn + 16 * i + (lane & 15), kf));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(fa[i], fb[j], acc[i][j]);
+    }
+    if (more) {
+      tile_store<AT>(sa[buf ^ 1], va);
+      tile_store<BTL>(sb[buf ^ 1], vb);
+    }
+    __syncthreads();
+  }
+  // lane holds C[4 (lane / 16) + r][lane % 16] of each 16 x 16 tile
+  float *cbase = a.c + (int64_t)g * a.cgstride;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn + 16 * j + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm + 16 * i + 4 * (lane >> 4) + r;
+        if (m < mend && n < a.N) cbase[(int64_t)m * a.ldc + n] = acc[i][j][r];
+      }
+    }
+}
+
+// ---------------------------------------------------------------- element-wise steps
+
+// Gate of row p: gates[perm_src[p]] (routed rows), 1 for the shared expert.
+__device__ __forceinline__ float row_gate(const float *gates, const int32_t *perm_src, int64_t p) {
+  return gates ? gates[perm_src[p]] : 1.0f;
+}
+
+// One wave per row p: h = silu(z_gate) * z_up; hg[p] = g h (bf16, the down
+// layer's input as seen by dW_down); dg[p] = <u[p], h> with u = dy W_down, so
+// that dg is the gate's gradient <dy, FFN(x)> (lane partial sums, then the
+// wave tree: a fixed order).
+__global__ __launch_bounds__(256) void bwd_h_dg_kernel(const float *__restrict__ z, const float *__restrict__ u,
+                                                       const float *__restrict__ gates,
+                                                       const int32_t *__restrict__ perm_src,
+                                                       const int32_t *__restrict__ kept, int64_t N, int I,
+                                                       uint16_t *__restrict__ hg, float *__restrict__ dg) {
+  const int64_t p = (int64_t)blockIdx.x * 4 + wave_id();
+  if (p >= (kept ? *kept : N)) return;
+  const int lane = lane_id();
+  const float g = row_gate(gates, perm_src, p);
+  const float *zr = z + p * 2 * I, *ur = u + p * I;
+  float acc = 0.f;
+  for (int i = lane; i < I; i += kWave) {
+    const float hv = swiglu(zr[i], zr[I + i]);
+    hg[p * I + i] = (uint16_t)f32_to_bf16(g * hv);
+    acc = __builtin_fmaf(ur[i], hv, acc);
+  }
+  acc = wave_sum(acc);
+  if (dg && lane == 0) dg[p] = acc;
+}
+
+// One thread per token: softmax backward over its k chosen logits,
+// dl_j = g_j (dg_j - sum_m g_m dg_m), written at the slots' rows.
+__global__ void bwd_dl_kernel(const float *__restrict__ dg, const float *__restrict__ gates,
+                              const int32_t *__restrict__ perm_pos, int64_t T, int k, float *__restrict__ dl) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  float s = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int32_t p = perm_pos[t * k + j];
+    if (p >= 0) s = __builtin_fmaf(gates[t * k + j], dg[p], s);
+  }
+  for (int j = 0; j < k; ++j) {
+    const int32_t p = perm_pos[t * k + j];
+    if (p >= 0) dl[p] = gates[t * k + j] * (dg[p] - s);
+  }
+}
+
+// One block per row p: with dh = g u, the SwiGLU backward
+//   dz_up = dh silu(z_gate),  dz_gate = dh z_up sigma(z_gate) (1 + z_gate (1 - sigma(z_gate)))
+// stored bf16 as [gate half | up half], the layout of z.
+__global__ __launch_bounds__(256) void bwd_dz_kernel(const float *__restrict__ z, const float *__restrict__ u,
+                                                     const float *__restrict__ gates,
+                                                     const int32_t *__restrict__ perm_src,
+                                                     const int32_t *__restrict__ kept, int64_t N, int I,
+                                                     uint16_t *__restrict__ dz) {
+  const int64_t p = blockIdx.x;
+  if (p >= (kept ? *kept : N)) return;
+  const float g = row_gate(gates, perm_src, p);
+  const float *zr = z + p * 2 * I, *ur = u + p * I;
+  uint16_t *dr = dz + p * 2 * I;
+  for (int i = threadIdx.x; i < I; i += blockDim.x) {
+    const float zg = zr[i], zu = zr[I + i];
+    const float dh = g * ur[i];
+    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-zg));
+    dr[I + i] = (uint16_t)f32_to_bf16(dh * zg * sg);
+    dr[i] = (uint16_t)f32_to_bf16(dh * zu * sg * (1.0f + zg * (1.0f - sg)));
+  }
+}
+
+// Router weight gradient: dW_r[e][h] = sum over e's rows p (in order) of
+// dl[p] x_perm[p][h]; dbias[e] = sum of dl[p].  Grid (E, ceil(H / 256)).
+__global__ __launch_bounds__(256) void bwd_router_w_kernel(const float *__restrict__ dl,
+                                                           const uint16_t *__restrict__ x_perm,
+                                                           const int32_t *__restrict__ off, int H,
+                                                           float *__restrict__ dwr, float *__restrict__ dbias) {
+  const int e = blockIdx.x;
+  const int h = blockIdx.y * 256 + threadIdx.x;
+  const int p0 = off[e], p1 = off[e + 1];
+  if (h < H) {
+    float acc = 0.f;
+    for (int p = p0; p < p1; ++p) acc = __builtin_fmaf(dl[p], bf16_to_f32(x_perm[(int64_t)p * H + h]), acc);
+    dwr[(int64_t)e * H + h] = acc;
+  }
+  if (dbias && blockIdx.y == 0 && threadIdx.x == 0) {
+    float s = 0.f;
+    for (int p = p0; p < p1; ++p) s += dl[p];
+    dbias[e] = s;
+  }
+}
+
+// dx[t] = dx_shared[t] + sum_j dx_rows[row of (t, j)] + sum_j dl_j W_r[e_j],
+// fp32, in that order (slots in increasing j).  Grid (T, ceil(H / 256)).
+__global__ __launch_bounds__(256) void bwd_dx_kernel(const float *__restrict__ dx_shared,
+                                                     const float *__restrict__ dx_rows,
+                                                     const int32_t *__restrict__ perm_pos,
+                                                     const int32_t *__restrict__ ids, const float *__restrict__ dl,
+                                                     const uint16_t *__restrict__ wr, int k, int H,
+                                                     float *__restrict__ dx) {
+  const int64_t t = blockIdx.x;
+  const int h = blockIdx.y * 256 + threadIdx.x;
+  if (h >= H) return;
+  float acc = dx_shared ? dx_shared[t * H + h] : 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int32_t p = perm_pos[t * k + j];
+    if (p >= 0) acc += dx_rows[(int64_t)p * H + h];
+  }
+  for (int j = 0; j < k; ++j) {
+    const int32_t p = perm_pos[t * k + j];
+    if (p >= 0) acc = __builtin_fmaf(dl[p], bf16_to_f32(wr[(int64_t)ids[t * k + j] * H + h]), acc);
+  }
+  dx[t * H + h] = acc;
+}
+
+// ---------------------------------------------------------------- host side
+
+namespace {
+
+hipError_t launch_gemm(const GemmArgs &a, bool at, bool bt, unsigned blocks, hipStream_t st) {
+  if (blocks == 0) return hipSuccess;
+  if (!at && !bt)
+    grouped_gemm_kernel<false, false><<<blocks, kGemmThreads, 0, st>>>(a);
+  else if (!at && bt)
+    grouped_gemm_kernel<false, true><<<blocks, kGemmThreads, 0, st>>>(a);
+  else if (at && bt)
+    grouped_gemm_kernel<true, true><<<blocks, kGemmThreads, 0, st>>>(a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+bool op_t(const GemmOp &o) { return o.ks != 1; }
+
+// Row-segmented GEMM: rows of group g are [off[g], off[g+1]) (or [0, rows)
+// when off is NULL), walked through the 128-row tile list in tiles_ws;
+// C[row, n] = sum_k A(row, k) B_g(n, k).  A must be N-layout and K a
+// multiple of the K step.
+hipError_t gemm_rows(const GemmOp &A, const GemmOp &B, float *c, int64_t ldc, const int32_t *off, int G, int64_t rows,
+                     int N, int K, const int32_t *tiles_ws, int max_tiles, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  if (op_t(A) || K % BK != 0) return hipErrorInvalidValue;
+  const TileEntry *tiles = reinterpret_cast<const TileEntry *>(tiles_ws + kTileHdrWords);
+  GemmArgs a{A, B, c, ldc, 0, off, G, (int)rows, N, K, 0, (int)cdiv(N, BT), tiles, tiles_ws};
+  timing_before(MOE_SITE_BWD_DGRAD, st);
+  const hipError_t e = launch_gemm(a, false, op_t(B), (unsigned)((int64_t)max_tiles * a.ntn), st);
+  timing_after(MOE_SITE_BWD_DGRAD, st);
+  return e;
+}
+
+// K-segmented GEMM: C_g [M, N] = sum over k in group g's range of A(m, k) B(n, k),
+// for every group (a group with an empty range gets zeros).  Both operands
+// T-layout.
+hipError_t gemm_kseg(const GemmOp &A, const GemmOp &B, float *c, int64_t ldc, int64_t cgstride, const int32_t *off,
+                     int G, int M, int N, int K, hipStream_t st) {
+  if (!op_t(A) || !op_t(B)) return hipErrorInvalidValue;
+  GemmArgs a{A, B, c, ldc, cgstride, off, G, M, N, K, (int)cdiv(M, BT), (int)cdiv(N, BT), nullptr, nullptr};
+  timing_before(MOE_SITE_BWD_WGRAD, st);
+  const hipError_t e = launch_gemm(a, true, true, (unsigned)((int64_t)G * a.ntm * a.ntn), st);
+  timing_after(MOE_SITE_BWD_WGRAD, st);
+  return e;
+}
+
+}  // namespace
+
+int bwd_max_tiles(int64_t rows, int G) { return (int)(cdiv(rows, BT) + std::min<int64_t>(rows, G) + 1); }
+
+hipError_t launch_expert_backward(const BwdExpert &X, hipStream_t st) {
+  const int H = X.H, I = X.I, G = X.G;
+  const int64_t N = X.rows;
+  hipError_t e;
+  if (N > 0) {
+    FfnGroup fg{};
+    fg.off = X.off;
+    fg.E = G;
+    fg.nrows = (int32_t)N;
+    e = launch_build_tiles(fg, BT, X.max_tiles, reinterpret_cast<TileEntry *>(X.tiles + kTileHdrWords), X.tiles, st);
+    if (e != hipSuccess) return e;
+    // z = x W_gu^T: B(n = j, k = h) = W_gu[g][j][h]
+    e = gemm_rows(GemmOp{X.x, 0, H, 1}, GemmOp{X.wgu, (int64_t)2 * I * H, H, 1}, X.z, 2 * I, X.off, G, N, 2 * I, H,
+                  X.tiles, X.max_tiles, st);
+    if (e != hipSuccess) return e;
+    // u = dy W_d: B(n = i, k = c) = W_d[g][c][i]
+    e = gemm_rows(GemmOp{X.dy, 0, H, 1}, GemmOp{X.wd, (int64_t)H * I, 1, I}, X.u, I, X.off, G, N, I, H, X.tiles,
+                  X.max_tiles, st);
+    if (e != hipSuccess) return e;
+    // rows past off[G] (assignments the sort dropped) belong to no expert
+    const int32_t *kept = X.off ? X.off + G : nullptr;
+    bwd_h_dg_kernel<<<(unsigned)cdiv(N, 4), 256, 0, st>>>(X.z, X.u, X.gates, X.perm_src, kept, N, I, X.hg, X.dg);
+    if (X.dl) bwd_dl_kernel<<<(unsigned)cdiv(X.T, 256), 256, 0, st>>>(X.dg, X.gates, X.perm_pos, X.T, X.k, X.dl);
+    bwd_dz_kernel<<<(unsigned)N, 256, 0, st>>>(X.z, X.u, X.gates, X.perm_src, kept, N, I, X.dz);
+    // dx rows = dz W_gu: B(n = h, k = j) = W_gu[g][j][h]
+    e = gemm_rows(GemmOp{X.dz, 0, 2 * I, 1}, GemmOp{X.wgu, (int64_t)2 * I * H, 1, H}, X.dx_rows, H, X.off, G, N, H,
+                  2 * I, X.tiles, X.max_tiles, st);
+    if (e != hipSuccess) return e;
+  }
+  // dW_d[g] = dy^T hg over g's rows: A(m = c, k = p) = dy[p][c], B(n = i, k = p) = hg[p][i]
+  e = gemm_kseg(GemmOp{X.dy, 0, 1, H}, GemmOp{X.hg, 0, 1, I}, X.dwd, I, (int64_t)H * I, X.off, G, H, I, (int)N, st);
+  if (e != hipSuccess) return e;
+  // dW_gu[g] = dz^T x over g's rows: A(m = j, k = p) = dz[p][j], B(n = h, k = p) = x[p][h]
+  return gemm_kseg(GemmOp{X.dz, 0, 1, 2 * I}, GemmOp{X.x, 0, 1, H}, X.dwgu, H, (int64_t)2 * I * H, X.off, G, 2 * I,
+                   H, (int)N, st);
+}
+
+hipError_t launch_router_backward(const float *dl, const uint16_t *x_perm, const int32_t *off, int E, int H,
+                                  float *dwr, float *dbias, hipStream_t st) {
+  bwd_router_w_kernel<<<dim3((unsigned)E, (unsigned)cdiv(H, 256)), 256, 0, st>>>(dl, x_perm, off, H, dwr, dbias);
+  return hipGetLastError();
+}
+
+hipError_t launch_dx_backward(const float *dx_shared, const float *dx_rows, const int32_t *perm_pos,
+                              const int32_t *ids, const float *dl, const uint16_t *wr, int64_t T, int k, int H,
+                              float *dx, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  bwd_dx_kernel<<<dim3((unsigned)T, (unsigned)cdiv(H, 256)), 256, 0, st>>>(dx_shared, dx_rows, perm_pos, ids, dl, wr,
+                                                                          k, H, dx);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -80,6 +80,12 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(FfnGroup g0, FfnGroup
   if (tid == 0) hdr[0] = min(base0, max_tiles);
 }
 
+hipError_t launch_build_tiles(const FfnGroup &g, int bm, int max_tiles, TileEntry *tiles, int32_t *hdr,
+                              hipStream_t st) {
+  build_tiles_kernel<<<1, 1024, 0, st>>>(g, g, 1, bm, max_tiles, tiles, hdr);
+  return hipGetLastError();
+}
+
 // Operand fragment of one lane for one 128-byte K chunk: 32 bytes.
 struct Frag {
   i32x4 lo, hi;

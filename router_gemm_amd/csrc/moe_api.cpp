@@ -250,6 +250,50 @@ ForwardWs carve_forward(Carve &c, const moe_layer *L, const void *x, int64_t T, 
   return f;
 }
 
+// Backward: the sort, rows gathered into expert order, and each expert set's
+// scratch (routed experts; shared expert).
+struct BackwardWs {
+  int32_t *offsets, *perm_src, *perm_pos, *sort;
+  uint16_t *x_perm, *dy_perm;
+  float *dl;
+  moe::BwdExpert routed, shared;
+};
+void carve_bwd_expert(Carve &c, moe::BwdExpert &X, int H, int I, int G, int64_t rows, bool with_dg) {
+  X = moe::BwdExpert{};
+  X.H = H;
+  X.I = I;
+  X.G = G;
+  X.rows = rows;
+  X.z = c.take<float>((size_t)rows * 2 * I + 1);
+  X.u = c.take<float>((size_t)rows * I + 1);
+  X.hg = c.take<uint16_t>((size_t)rows * I + 8);
+  X.dz = c.take<uint16_t>((size_t)rows * 2 * I + 8);
+  X.dg = with_dg ? c.take<float>((size_t)rows + 1) : nullptr;
+  X.dx_rows = c.take<float>((size_t)rows * H + 1);
+  X.max_tiles = moe::bwd_max_tiles(rows, G);
+  X.tiles = c.take<int32_t>((size_t)moe::kTileHdrWords + 2 * (size_t)X.max_tiles);
+}
+BackwardWs carve_backward(Carve &c, const moe_layer *L, int64_t T) {
+  BackwardWs b;
+  const int64_t N = T * L->top_k;
+  const int H = L->hidden, E = L->num_experts;
+  b.offsets = c.take<int32_t>((size_t)E + 1);
+  b.perm_src = c.take<int32_t>((size_t)N + 1);
+  b.perm_pos = c.take<int32_t>((size_t)N + 1);
+  b.sort = carve_sort(c, N, E);
+  b.x_perm = c.take<uint16_t>((size_t)N * H + 8);
+  b.dy_perm = c.take<uint16_t>((size_t)N * H + 8);
+  b.dl = c.take<float>((size_t)N + 1);
+  carve_bwd_expert(c, b.routed, H, L->inter, E, N, true);
+  if (L->shared_inter > 0) carve_bwd_expert(c, b.shared, H, L->shared_inter, 1, T, false);
+  return b;
+}
+size_t need_backward(const moe_layer *L, int64_t T) {
+  Carve c(nullptr);
+  carve_backward(c, L, T);
+  return c.used;
+}
+
 size_t need_route(const moe_layer *L, int64_t T) { Carve c(nullptr); carve_route(c, L, T); return c.used; }
 size_t need_permute(const moe_layer *L, int64_t N) { Carve c(nullptr); carve_sort(c, N, L->num_experts); return c.used; }
 size_t need_ffn(const moe_layer *L, int64_t N) {
@@ -460,6 +504,83 @@ moe_status moe_forward(const moe_layer *L, const void *x, int64_t T, void *y, in
   e = moe::launch_combine(f.y_perm, false, f.perm_pos, nullptr, nullptr, L->top_k, gates, f.sh_out, out_f32, T, H, N, y,
                           out_f32, st);
   return hip_status(e, "moe_forward: combine");
+}
+
+size_t moe_backward_workspace_bytes(const moe_layer *L, int64_t T) {
+  if (check_layer_shape(L, true) != MOE_OK || check_rows(T, T * (int64_t)L->top_k) != MOE_OK) return 0;
+  return need_backward(L, T);
+}
+
+moe_status moe_backward(const moe_layer *L, const void *x, int64_t T, const int32_t *topk_ids,
+                        const float *topk_gates, const void *dy, float *dx, float *dw_gate_up, float *dw_down,
+                        float *dw_shared_gate_up, float *dw_shared_down, float *dw_router, float *dbias, void *ws,
+                        size_t ws_bytes, void *stream) {
+  moe_status s;
+  if ((s = check_layer_shape(L, true)) != MOE_OK) return s;
+  if (L->expert_dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "moe_backward needs bf16 experts");
+  if ((s = check_rows(T, T * (int64_t)L->top_k)) != MOE_OK) return s;
+  if (T > 0) {
+    if (!x || !dy || !topk_ids || !topk_gates || !L->w_router) return fail(MOE_EINVAL, "NULL backward input");
+    if (!dx || !dw_gate_up || !dw_down || !dw_router) return fail(MOE_EINVAL, "NULL backward output");
+    if (L->shared_inter > 0 && (!dw_shared_gate_up || !dw_shared_down))
+      return fail(MOE_EINVAL, "shared expert gradients are NULL");
+    if (!aligned16(x) || !aligned16(dy) || !aligned16(L->w_router)) return fail(MOE_EINVAL, "x, dy or w_router not 16-byte aligned");
+    if ((s = check_expert_weights(L)) != MOE_OK) return s;
+    if ((s = check_shared(L)) != MOE_OK) return s;
+  }
+  if (T == 0) return MOE_OK;
+  if ((s = check_ws(ws, ws_bytes, need_backward(L, T))) != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t N = T * L->top_k;
+  const int H = L->hidden, E = L->num_experts, k = L->top_k;
+  Carve c(ws);
+  BackwardWs b = carve_backward(c, L, T);
+  hipError_t e = moe::launch_counting_sort(topk_ids, nullptr, 0, N, E, b.offsets, b.perm_src, b.perm_pos, b.sort, st);
+  if (e != hipSuccess) return hip_status(e, "moe_backward: sort");
+  e = moe::launch_gather_rows(static_cast<const uint16_t *>(x), H, b.perm_src, nullptr, k, N, b.offsets + E, false,
+                              b.x_perm, nullptr, st);
+  if (e != hipSuccess) return hip_status(e, "moe_backward: gather x");
+  e = moe::launch_gather_rows(static_cast<const uint16_t *>(dy), H, b.perm_src, nullptr, k, N, b.offsets + E, false,
+                              b.dy_perm, nullptr, st);
+  if (e != hipSuccess) return hip_status(e, "moe_backward: gather dy");
+  // routed experts: rows [0, offsets[E]) in expert order (rows beyond are
+  // dropped assignments, outside every expert's range)
+  moe::BwdExpert &R = b.routed;
+  R.T = T;
+  R.k = k;
+  R.x = b.x_perm;
+  R.dy = b.dy_perm;
+  R.wgu = static_cast<const uint16_t *>(L->w_gate_up);
+  R.wd = static_cast<const uint16_t *>(L->w_down);
+  R.off = b.offsets;
+  R.gates = topk_gates;
+  R.perm_src = b.perm_src;
+  R.perm_pos = b.perm_pos;
+  R.dl = b.dl;
+  R.dwgu = dw_gate_up;
+  R.dwd = dw_down;
+  e = moe::launch_expert_backward(R, st);
+  if (e != hipSuccess) return hip_status(e, "moe_backward: routed experts");
+  e = moe::launch_router_backward(b.dl, b.x_perm, b.offsets, E, H, dw_router, dbias, st);
+  if (e != hipSuccess) return hip_status(e, "moe_backward: router");
+  const float *dx_shared = nullptr;
+  if (L->shared_inter > 0) {
+    moe::BwdExpert &S = b.shared;
+    S.T = T;
+    S.k = 1;
+    S.x = static_cast<const uint16_t *>(x);
+    S.dy = static_cast<const uint16_t *>(dy);
+    S.wgu = static_cast<const uint16_t *>(L->w_shared_gate_up);
+    S.wd = static_cast<const uint16_t *>(L->w_shared_down);
+    S.dwgu = dw_shared_gate_up;
+    S.dwd = dw_shared_down;
+    e = moe::launch_expert_backward(S, st);
+    if (e != hipSuccess) return hip_status(e, "moe_backward: shared expert");
+    dx_shared = S.dx_rows;
+  }
+  e = moe::launch_dx_backward(dx_shared, R.dx_rows, b.perm_pos, topk_ids, b.dl,
+                              static_cast<const uint16_t *>(L->w_router), T, k, H, dx, st);
+  return hip_status(e, "moe_backward: dx");
 }
 
 }  // extern "C"

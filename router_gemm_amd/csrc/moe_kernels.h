@@ -99,6 +99,49 @@ int num_compute_units();
 hipError_t launch_expert_ffn(const FfnGroup *g, int ngroups, int H, const FfnPlan &plan, int32_t *tiles_ws,
                              int site, hipStream_t st);
 
+// Tile list of a row-segmented grouped launch: bm-row entries over g's
+// experts (expert_gemm.hip).
+hipError_t launch_build_tiles(const FfnGroup &g, int bm, int max_tiles, TileEntry *tiles, int32_t *hdr,
+                              hipStream_t st);
+
+// ---- backward of the layer, bf16 experts (backward.hip)
+// One set of experts (the routed experts, or the shared expert as G = 1 with
+// off = NULL) whose rows are already in expert order.
+struct BwdExpert {
+  int H, I, G;
+  int64_t rows;              // N: rows in expert order
+  int64_t T;                 // tokens (routed: for the softmax backward)
+  int k;
+  const uint16_t *x;         // [N, H] bf16 input rows
+  const uint16_t *dy;        // [N, H] bf16 output gradient rows (ungated)
+  const uint16_t *wgu;       // [G, 2I, H]
+  const uint16_t *wd;        // [G, H, I]
+  const int32_t *off;        // [G+1] or NULL (G == 1, rows [0, N))
+  const float *gates;        // [T*k] gate of each assignment, or NULL (gate 1)
+  const int32_t *perm_src;   // [N] assignment of each row (with gates)
+  const int32_t *perm_pos;   // [T*k] row of each assignment (with dl)
+  float *z;                  // [N, 2I] scratch: recomputed pre-activations
+  float *u;                  // [N, I] scratch: dy W_down
+  uint16_t *hg;              // [N, I] scratch: gate * h, bf16
+  uint16_t *dz;              // [N, 2I] scratch: gradient of z, bf16
+  float *dg;                 // [N] gate gradients, or NULL
+  float *dl;                 // [N] logit gradients, or NULL
+  float *dx_rows;            // [N, H] out: input gradient of each row through the expert
+  float *dwgu;               // [G, 2I, H] out
+  float *dwd;                // [G, H, I] out
+  int32_t *tiles;            // tile-list workspace: kTileHdrWords + 2 * bwd_max_tiles(N, G) words
+  int max_tiles;
+};
+int bwd_max_tiles(int64_t rows, int G);
+hipError_t launch_expert_backward(const BwdExpert &X, hipStream_t st);
+// dW_r[e] = sum of dl[p] x_perm[p] over e's rows; dbias (NULL: skipped) = sum of dl[p].
+hipError_t launch_router_backward(const float *dl, const uint16_t *x_perm, const int32_t *off, int E, int H,
+                                  float *dwr, float *dbias, hipStream_t st);
+// dx[t] = dx_shared[t] (NULL: 0) + sum_j dx_rows[perm_pos[t k + j]] + sum_j dl W_r[ids[t k + j]].
+hipError_t launch_dx_backward(const float *dx_shared, const float *dx_rows, const int32_t *perm_pos,
+                              const int32_t *ids, const float *dl, const uint16_t *wr, int64_t T, int k, int H,
+                              float *dx, hipStream_t st);
+
 // ---- combine (combine.hip)
 // y[t] = shared[t] + sum over the token's assignments (fixed order) of g * y_perm[perm_pos]
 // tok_off/tok_list: per-token assignment lists (NULL: assignments t*k .. t*k+k-1).

@@ -104,6 +104,11 @@ CONFIGS = {
         router_std=1.0 / 64, dense=True,
         description="the model's dense SwiGLU FF layers (0-2 and 91): intermediate 13824, bf16, "
                     "8192 tokens, as one expert through moe_expert_ffn"),
+    "train_bf16": MoEConfig(
+        "train_bf16", T=8192, H=4096, E=352, k=8, I=1536, Is=1536, expert_dtype="bf16",
+        router_std=1.0 / 64,
+        description="training step of the Step-5 MoE layer in BF16 (forward + backward), one "
+                    "8192-token sequence, unbiased router on random inputs (near-balanced loads)"),
 }
 # Short aliases by position in the workload list.
 ALIASES = {"c0": "small_bf16", "c1": "decode_bf16", "c2": "decode_fp8",
@@ -261,6 +266,12 @@ def make_x(cfg: MoEConfig, device="cpu", T: Optional[int] = None) -> torch.Tenso
     """Token activations x ~ N(0,1), bf16 [T,H]."""
     T = cfg.T if T is None else T
     return _bf16_bits(_rng(cfg.seed, 1).standard_normal((T, cfg.H), dtype=np.float32)).to(device)
+
+
+def make_dy(cfg: MoEConfig, device="cpu", T: Optional[int] = None) -> torch.Tensor:
+    """Gradient of the layer output for the backward, dy ~ N(0,1), bf16 [T,H]."""
+    T = cfg.T if T is None else T
+    return _bf16_bits(_rng(cfg.seed, 8).standard_normal((T, cfg.H), dtype=np.float32)).to(device)
 
 
 def make_triples(cfg: MoEConfig):

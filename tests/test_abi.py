@@ -112,7 +112,7 @@ def test_permute_combine_ffn_refusals():
 def test_timing_sites_validate_without_gpu():
     lib = B.lib()
     assert lib.moe_timing_arm(-1, 4) == B.MOE_EINVAL
-    assert lib.moe_timing_arm(9, 4) == B.MOE_EINVAL
+    assert lib.moe_timing_arm(11, 4) == B.MOE_EINVAL          # MOE_SITE_COUNT
     assert lib.moe_timing_arm(4, 0) == B.MOE_EINVAL
     ms, n = C.c_double(1.0), C.c_int32(7)
     assert lib.moe_timing_read(5, C.byref(ms), C.byref(n)) == B.MOE_OK
@@ -131,3 +131,23 @@ def test_mxfp4_scale_refusals():
     L = layer(dtype=B.MOE_MXFP4_E2M1)
     r = lib.moe_permute(C.byref(L), FAKE, 64, FAKE, None, 512, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None)
     assert r == B.MOE_EINVAL and b"x_scale" in lib.moe_last_error()
+
+
+def test_backward_refusals_without_gpu():
+    """moe_backward: bf16 experts only, router and outputs required, its own
+    workspace size (moe_workspace_bytes does not cover it)."""
+    lib = B.lib()
+    L = layer(dtype=B.MOE_BF16)
+    args = lambda T=64, dx=FAKE, dsgu=FAKE, ws=FAKE, nb=1 << 40: (
+        C.byref(L), FAKE, T, FAKE, FAKE, FAKE, dx, FAKE, FAKE, dsgu, FAKE, FAKE, None, ws, nb, None)
+    need = lib.moe_backward_workspace_bytes(C.byref(L), 64)
+    assert need > lib.moe_workspace_bytes(C.byref(L), 64, 512)
+    assert lib.moe_backward(*args(nb=need - 1)) == B.MOE_EWORKSPACE
+    assert lib.moe_backward(*args(dx=None)) == B.MOE_EINVAL
+    assert lib.moe_backward(*args(dsgu=None)) == B.MOE_EINVAL and b"shared" in lib.moe_last_error()
+    assert lib.moe_backward(*args(T=0, ws=None, nb=0)) == B.MOE_OK        # no-op
+    L = layer(dtype=B.MOE_FP8_E4M3FN)
+    assert lib.moe_backward(*args()) == B.MOE_EUNSUPPORTED and b"bf16" in lib.moe_last_error()
+    L = layer(dtype=B.MOE_BF16, k=0)
+    assert lib.moe_backward(*args()) == B.MOE_EINVAL
+    assert lib.moe_backward_workspace_bytes(C.byref(L), 64) == 0
