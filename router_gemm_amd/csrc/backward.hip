@@ -26,9 +26,7 @@
 namespace moe {
 
 namespace {
-constexpr int BT = 128;          // output tile rows and columns
 constexpr int BK = 64;           // K step
-constexpr int TILE = BT * BK;    // bf16 elements of one staged operand tile
 constexpr int kGemmThreads = 256;
 }  // namespace
 
@@ -43,34 +41,41 @@ struct GemmArgs {
   float *c;            // fp32 output, C_g at c + g * cgstride, row pitch ldc
   int64_t ldc, cgstride;
   const int32_t *off;  // [G+1] segment offsets, or NULL: one group owning [0, rows) / [0, K)
-  int G, M, N, K;      // M: rows (row-segmented: all rows); K: reduction length (K-segmented: all of it)
-  int ntm, ntn;        // tiles along M (K-segmented) and N
-  const TileEntry *tiles;  // row-segmented: 128-row tile list and its header
+  int G, M, N, K;      // M: rows (row-grouped: all rows); K: reduction length (K-grouped: all of it)
+  int ntm, ntn;        // tiles along M (K-grouped) and N
+  const TileEntry *tiles;  // row-grouped: tile list (entries of the kernel's BM rows) and its header
   const int32_t *hdr;
 };
 
 // LDS position (in bf16 elements) of operand element (r, k) of a staged tile:
-// rows of 64 k, 16-byte units permuted per row so that both the staging
-// writes and the fragment reads spread over the banks.  N-layout tiles are
-// written 8 k of one row at a time, T-layout tiles 4 k of one row per lane
-// with 8 consecutive rows per lane, hence the two permutations.
+// rows of 64 k, the eight 16-byte units of a row permuted by an XOR of row
+// bits so that the staging writes and the fragment reads (16 consecutive rows
+// x 4 units per wave) each touch every bank equally.  N-layout tiles are
+// written one 16-byte unit per lane over 8 rows: unit ^= r % 8.  T-layout
+// tiles are written 2, 4 or 8 k of one row per lane, the lanes' rows 8 apart
+// (8 (lane % (ROWS/8)) + u, u alternating with the lane's parity): unit ^=
+// (r1 ^ r5, r4, r3), whose top bit varies inside any 16 consecutive rows (the
+// reads) and whose two top bits take every value over the lanes of one write.
 template <bool T>
 __device__ __forceinline__ int lds_pos(int r, int k) {
-  const int sw = T ? ((r >> 3) & 7) : (r & 7);
+  const int sw = T ? (((((r >> 1) ^ (r >> 5)) & 1) << 2) | (((r >> 4) & 1) << 1) | ((r >> 3) & 1)) : (r & 7);
   return r * BK + (((k >> 3) ^ sw) << 3) + (k & 7);
 }
 
-// Global loads of one operand's 128 x 64 tile into registers: 4 x 16 bytes
-// per thread.  N layout: chunk q = tid + 256 j holds row q / 8, k 8 (q % 8)
-// .. +7.  T layout: the thread's rows are 8 (tid % 16) .. +7 and its k are
-// 4 (tid / 16) + j.  Rows >= nr and k >= nk read as zero (rows come in whole
-// chunks: every row count and pitch here is a multiple of 8).
-template <bool T>
+// Global loads of one operand's ROWS x 64 tile into registers: ROWS / 32
+// chunks of 16 bytes per thread.  N layout: chunk q = tid + 256 j holds row
+// q / 8, k 8 (q % 8) .. +7.  T layout: the thread's rows are
+// 8 (tid % (ROWS/8)) .. +7 and its k are (ROWS/32) (tid / (ROWS/8)) + j.
+// Rows >= nr and k >= nk read as zero (rows come in whole chunks: every row
+// count and pitch here is a multiple of 8).
+template <bool T, int ROWS>
 __device__ __forceinline__ void tile_load(const uint16_t *base, int64_t rs, int64_t ks, int r0, int nr, int k0,
-                                          int nk, i32x4 (&v)[4]) {
+                                          int nk, i32x4 (&v)[ROWS / 32]) {
+  static_assert(ROWS == 64 || ROWS == 128 || ROWS == 256, "tiles are 64, 128 or 256 rows");
+  constexpr int RC = ROWS / 8, KPT = ROWS / 32;
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < KPT; ++j) {
     int r, k;
     int64_t o;
     if (!T) {
@@ -79,61 +84,87 @@ __device__ __forceinline__ void tile_load(const uint16_t *base, int64_t rs, int6
       k = k0 + ((q & 7) << 3);
       o = (int64_t)r * rs + k;
     } else {
-      r = r0 + ((tid & 15) << 3);
-      k = k0 + ((tid >> 4) << 2) + j;
+      r = r0 + (tid % RC) * 8;
+      k = k0 + (tid / RC) * KPT + j;
       o = (int64_t)k * ks + r;
     }
     v[j] = (r < nr && k < nk) ? load16(base + o) : i32x4{0, 0, 0, 0};
   }
 }
 
-template <bool T>
-__device__ __forceinline__ void tile_store(uint16_t *s, const i32x4 (&v)[4]) {
+// Element 2 h + odd (h constant, odd 0 or 1 per lane) of a 16-byte chunk of bf16.
+__device__ __forceinline__ uint32_t chunk_elem(const i32x4 &v, int h, int odd) {
+  return ((uint32_t)v[h] >> (16 * odd)) & 0xFFFFu;
+}
+
+template <bool T, int ROWS>
+__device__ __forceinline__ void tile_store(uint16_t *s, const i32x4 (&v)[ROWS / 32]) {
+  constexpr int RC = ROWS / 8, KPT = ROWS / 32;
   const int tid = threadIdx.x;
   if (!T) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < KPT; ++j) {
       const int q = tid + kGemmThreads * j;
       *reinterpret_cast<i32x4 *>(s + lds_pos<false>(q >> 3, (q & 7) << 3)) = v[j];
     }
   } else {
-    // transpose 4 k x 8 rows: row u of the thread gets k .. k+3 as 8 bytes
-    const int r = (tid & 15) << 3, k = (tid >> 4) << 2;
+    // transpose KPT k x 8 rows: row u of the thread gets its KPT k values;
+    // odd lanes take the rows in the order 1, 0, 3, 2, ... (see lds_pos)
+    const int rc = tid % RC, r = rc * 8, k = (tid / RC) * KPT, par = rc & 1;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int w = u >> 1;
-      uint32_t lo, hi;
-      if (u & 1) {
-        lo = ((uint32_t)v[0][w] >> 16) | ((uint32_t)v[1][w] & 0xFFFF0000u);
-        hi = ((uint32_t)v[2][w] >> 16) | ((uint32_t)v[3][w] & 0xFFFF0000u);
-      } else {
-        lo = ((uint32_t)v[0][w] & 0xFFFFu) | ((uint32_t)v[1][w] << 16);
-        hi = ((uint32_t)v[2][w] & 0xFFFFu) | ((uint32_t)v[3][w] << 16);
-      }
-      *reinterpret_cast<uint2 *>(s + lds_pos<true>(r + u, k)) = uint2{lo, hi};
+    for (int t = 0; t < 8; ++t) {
+      const int u = t ^ par, odd = (t & 1) ^ par;
+      uint32_t p[KPT / 2];
+#pragma unroll
+      for (int q = 0; q < KPT / 2; ++q)
+        p[q] = chunk_elem(v[2 * q], t >> 1, odd) | (chunk_elem(v[2 * q + 1], t >> 1, odd) << 16);
+      if constexpr (KPT == 2)
+        *reinterpret_cast<uint32_t *>(s + lds_pos<true>(r + u, k)) = p[0];
+      else if constexpr (KPT == 4)
+        *reinterpret_cast<uint2 *>(s + lds_pos<true>(r + u, k)) = uint2{p[0], p[1]};
+      else
+        *reinterpret_cast<i32x4 *>(s + lds_pos<true>(r + u, k)) =
+            i32x4{(int)p[0], (int)p[1], (int)p[2], (int)p[3]};
     }
   }
 }
 
-template <bool AT, bool BTL>
+// BM x BN output tile, four waves each computing 64 x 64: BM = 128, BN = 128
+// (2 x 2 waves) or BM = 256, BN = 64 (4 x 1 waves: row-grouped launches
+// whose groups hold up to 256 rows, so that each group's weight columns are
+// streamed from HBM once rather than once per 128-row tile).
+// NB = 2: two LDS stages (one barrier per K step); NB = 1: one stage and half
+// the LDS (two barriers per K step, more workgroups per CU: for the short
+// token ranges of the weight gradients).
+template <int BM, int BN, int NB, bool AT, bool BTL>
 __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sa[2][TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sb[2][TILE];
+  constexpr int WMW = BM / 64;  // waves along M
+  static_assert(BN == 64 * (4 / WMW), "four 64 x 64 waves");
+  // Staged operand tiles; K-grouped launches (weight gradients, both
+  // operands T-layout) reuse the space to stage half the output tile at a
+  // time, 64 rows of BN + 4 floats.
+  constexpr bool kStagedOut = AT && BTL;
+  constexpr int kOperandBytes = NB * (BM + BN) * BK * 2;
+  constexpr int kOutBytes = kStagedOut ? 64 * (BN + 4) * 4 : 0;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kOperandBytes > kOutBytes ? kOperandBytes : kOutBytes];
+  uint16_t(*sa)[BM * BK] = reinterpret_cast<uint16_t(*)[BM * BK]>(smem);
+  uint16_t(*sb)[BN * BK] = reinterpret_cast<uint16_t(*)[BN * BK]>(smem + NB * BM * BK * 2);
+  const int bid = blockIdx.x;
   const bool kseg = a.tiles == nullptr;
   int g, m0, mend, n0, kbeg, kend;
   if (kseg) {
     const int per = a.ntm * a.ntn;
-    g = blockIdx.x / per;
-    const int r = blockIdx.x - g * per;
-    m0 = (r / a.ntn) * BT;
-    n0 = (r % a.ntn) * BT;
+    g = bid / per;
+    const int r = bid - g * per;
+    m0 = (r / a.ntn) * BM;
+    n0 = (r % a.ntn) * BN;
     mend = a.M;
     kbeg = a.off ? a.off[g] : 0;
     kend = a.off ? a.off[g + 1] : a.K;
   } else {
-    const int tile = blockIdx.x / a.ntn;
+    const int tile = bid / a.ntn;
     if (tile >= a.hdr[0]) return;
-    n0 = (blockIdx.x - tile * a.ntn) * BT;
+    n0 = (bid - tile * a.ntn) * BN;
     const TileEntry te = a.tiles[tile];
     g = te.ge & 0xFFFFFF;
     const int rb = a.off ? a.off[g] : 0;
@@ -142,13 +173,13 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_kernel(GemmArgs a) 
     kbeg = 0;
     kend = a.K;
   }
-  // Row-segmented: A rows are global rows (gstride 0) and B is the group's
-  // weight; K-segmented: both operands are indexed by the global K (token)
+  // Row-grouped: A rows are global rows (gstride 0) and B is the group's
+  // weight; K-grouped: both operands are indexed by the global K (token)
   // index and only the output is per group.
   const uint16_t *abase = a.a.base + (int64_t)g * a.a.gstride;
   const uint16_t *bbase = a.b.base + (int64_t)g * a.b.gstride;
   const int lane = lane_id(), w = wave_id();
-  const int wm = (w & 1) * 64, wn = (w >> 1) * 64;
+  const int wm = (w % WMW) * 64, wn = (w / WMW) * 64;
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -156,55 +187,91 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_kernel(GemmArgs a) 
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = (int)cdiv(kend - kbeg, BK);
-  i32x4 va[4], vb[4];
+  i32x4 va[BM / 32], vb[BN / 32];
   if (nsteps > 0) {
-    tile_load<AT>(abase, a.a.rs, a.a.ks, m0, mend, kbeg, kend, va);
-    tile_load<BTL>(bbase, a.b.rs, a.b.ks, n0, a.N, kbeg, kend, vb);
-    tile_store<AT>(sa[0], va);
-    tile_store<BTL>(sb[0], vb);
+    tile_load<AT, BM>(abase, a.a.rs, a.a.ks, m0, mend, kbeg, kend, va);
+    tile_load<BTL, BN>(bbase, a.b.rs, a.b.ks, n0, a.N, kbeg, kend, vb);
+    tile_store<AT, BM>(sa[0], va);
+    tile_store<BTL, BN>(sb[0], vb);
     __syncthreads();
   }
   for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
+    const int buf = NB == 2 ? (s & 1) : 0;
     const bool more = s + 1 < nsteps;
     if (more) {
       const int k1 = kbeg + (s + 1) * BK;
-      tile_load<AT>(abase, a.a.rs, a.a.ks, m0, mend, k1, kend, va);
-      tile_load<BTL>(bbase, a.b.rs, a.b.ks, n0, a.N, k1, kend, vb);
+      tile_load<AT, BM>(abase, a.a.rs, a.a.ks, m0, mend, k1, kend, va);
+      tile_load<BTL, BN>(bbase, a.b.rs, a.b.ks, n0, a.N, k1, kend, vb);
     }
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
       bf16x8 fa[4], fb[4];
       const int kf = kk * 32 + 8 * (lane >> 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i)
         fa[i] = *reinterpret_cast<const bf16x8 *>(sa[buf] + lds_pos<AT>(wm + 16 * i + (lane & 15), kf));
-        fb[i] = *reinterpret_cast<const bf16x8 *>(sb[buf] + lds_pos<BTL>(wn + 16 * i + (lane & 15), kf));
-      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        fb[j] = *reinterpret_cast<const bf16x8 *>(sb[buf] + lds_pos<BTL>(wn + 16 * j + (lane & 15), kf));
+      // operands swapped: acc[i][j] holds the transposed 16 x 16 block, so
+      // each lane ends with 4 consecutive output columns of one row
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(fb[j], fa[i], acc[i][j]);
     }
+    if (NB == 1) __syncthreads();   // every wave is done with the stage before it is refilled
     if (more) {
-      tile_store<AT>(sa[buf ^ 1], va);
-      tile_store<BTL>(sb[buf ^ 1], vb);
+      tile_store<AT, BM>(sa[NB == 2 ? buf ^ 1 : 0], va);
+      tile_store<BTL, BN>(sb[NB == 2 ? buf ^ 1 : 0], vb);
     }
     __syncthreads();
   }
-  // lane holds C[4 (lane / 16) + r][lane % 16] of each 16 x 16 tile
+  // lane holds C[lane % 16][4 (lane / 16) + r] of each 16 x 16 block
   float *cbase = a.c + (int64_t)g * a.cgstride;
+  if constexpr (kStagedOut) {
+    // Weight gradients: each half of the tile (64 rows, the rows of two
+    // waves) goes through LDS so that every store instruction writes whole
+    // 512-byte rows; non-temporal, as nothing here reads them back.  The last
+    // barrier of the main loop has released the operand tiles.
+    constexpr int LDW = BN + 4;
+    float *stage = reinterpret_cast<float *>(smem);
+    const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int half = 0; half < 2; ++half) {
+      if ((w & 1) == half) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn + 16 * j + (lane & 15);
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm + 16 * i + 4 * (lane >> 4) + r;
-        if (m < mend && n < a.N) cbase[(int64_t)m * a.ldc + n] = acc[i][j][r];
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<f32x4 *>(stage + (16 * i + (lane & 15)) * LDW + wn + 16 * j + 4 * (lane >> 4)) =
+                acc[i][j];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = tid; q < 64 * BN / 4; q += kGemmThreads) {
+        const int row = q / (BN / 4), c4 = q % (BN / 4);
+        const int m = m0 + 64 * half + row, n = n0 + 4 * c4;
+        if (m < mend && n < a.N)
+          __builtin_nontemporal_store(*reinterpret_cast<const f32x4 *>(stage + row * LDW + 4 * c4),
+                                      reinterpret_cast<f32x4 *>(cbase + (int64_t)m * a.ldc + n));
+      }
+      __syncthreads();
+    }
+  } else {
+    // one 16-byte store per block (N is a multiple of 8)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + wm + 16 * i + (lane & 15);
+      if (m >= mend) continue;
+      float *crow = cbase + (int64_t)m * a.ldc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wn + 16 * j + 4 * (lane >> 4);
+        if (n < a.N) *reinterpret_cast<f32x4 *>(crow + n) = acc[i][j];
       }
     }
+  }
 }
 
 // ---------------------------------------------------------------- element-wise steps
@@ -325,14 +392,17 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float *__restrict__ d
 
 namespace {
 
-hipError_t launch_gemm(const GemmArgs &a, bool at, bool bt, unsigned blocks, hipStream_t st) {
-  if (blocks == 0) return hipSuccess;
+template <int BM, int BN>
+hipError_t launch_gemm(const GemmArgs &a, bool at, bool bt, int64_t nblocks, hipStream_t st) {
+  if (nblocks == 0) return hipSuccess;
+  if (nblocks > INT32_MAX) return hipErrorInvalidValue;
+  const unsigned blocks = (unsigned)nblocks;
   if (!at && !bt)
-    grouped_gemm_kernel<false, false><<<blocks, kGemmThreads, 0, st>>>(a);
+    grouped_gemm_kernel<BM, BN, 2, false, false><<<blocks, kGemmThreads, 0, st>>>(a);
   else if (!at && bt)
-    grouped_gemm_kernel<false, true><<<blocks, kGemmThreads, 0, st>>>(a);
-  else if (at && bt)
-    grouped_gemm_kernel<true, true><<<blocks, kGemmThreads, 0, st>>>(a);
+    grouped_gemm_kernel<BM, BN, 2, false, true><<<blocks, kGemmThreads, 0, st>>>(a);
+  else if (at && bt && BM == 128 && BN == 128)
+    grouped_gemm_kernel<128, 128, 1, true, true><<<blocks, kGemmThreads, 0, st>>>(a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -340,57 +410,74 @@ hipError_t launch_gemm(const GemmArgs &a, bool at, bool bt, unsigned blocks, hip
 
 bool op_t(const GemmOp &o) { return o.ks != 1; }
 
-// Row-segmented GEMM: rows of group g are [off[g], off[g+1]) (or [0, rows)
-// when off is NULL), walked through the 128-row tile list in tiles_ws;
-// C[row, n] = sum_k A(row, k) B_g(n, k).  A must be N-layout and K a
+// Row-grouped GEMM: rows of group g are [off[g], off[g+1]) (or [0, rows)
+// when off is NULL), walked through the tile list in tiles_ws (entries of bm
+// rows); C[row, n] = sum_k A(row, k) B_g(n, k).  A must be N-layout and K a
 // multiple of the K step.
 hipError_t gemm_rows(const GemmOp &A, const GemmOp &B, float *c, int64_t ldc, const int32_t *off, int G, int64_t rows,
-                     int N, int K, const int32_t *tiles_ws, int max_tiles, hipStream_t st) {
+                     int N, int K, const int32_t *tiles_ws, int bm, int max_tiles, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   if (op_t(A) || K % BK != 0) return hipErrorInvalidValue;
   const TileEntry *tiles = reinterpret_cast<const TileEntry *>(tiles_ws + kTileHdrWords);
-  GemmArgs a{A, B, c, ldc, 0, off, G, (int)rows, N, K, 0, (int)cdiv(N, BT), tiles, tiles_ws};
+  const int bn = bm == 256 ? 64 : 128;
+  GemmArgs a{A, B, c, ldc, 0, off, G, (int)rows, N, K, 0, (int)cdiv(N, bn), tiles, tiles_ws};
+  const int64_t blocks = (int64_t)max_tiles * a.ntn;
   timing_before(MOE_SITE_BWD_DGRAD, st);
-  const hipError_t e = launch_gemm(a, false, op_t(B), (unsigned)((int64_t)max_tiles * a.ntn), st);
+  const hipError_t e = bm == 256 ? launch_gemm<256, 64>(a, false, op_t(B), blocks, st)
+                                 : launch_gemm<128, 128>(a, false, op_t(B), blocks, st);
   timing_after(MOE_SITE_BWD_DGRAD, st);
   return e;
 }
 
-// K-segmented GEMM: C_g [M, N] = sum over k in group g's range of A(m, k) B(n, k),
+// K-grouped GEMM: C_g [M, N] = sum over k in group g's range of A(m, k) B(n, k),
 // for every group (a group with an empty range gets zeros).  Both operands
 // T-layout.
 hipError_t gemm_kseg(const GemmOp &A, const GemmOp &B, float *c, int64_t ldc, int64_t cgstride, const int32_t *off,
                      int G, int M, int N, int K, hipStream_t st) {
   if (!op_t(A) || !op_t(B)) return hipErrorInvalidValue;
-  GemmArgs a{A, B, c, ldc, cgstride, off, G, M, N, K, (int)cdiv(M, BT), (int)cdiv(N, BT), nullptr, nullptr};
+  GemmArgs a{A, B, c, ldc, cgstride, off, G, M, N, K, (int)cdiv(M, 128), (int)cdiv(N, 128), nullptr, nullptr};
   timing_before(MOE_SITE_BWD_WGRAD, st);
-  const hipError_t e = launch_gemm(a, true, true, (unsigned)((int64_t)G * a.ntm * a.ntn), st);
+  const hipError_t e = launch_gemm<128, 128>(a, true, true, (int64_t)G * a.ntm * a.ntn, st);
   timing_after(MOE_SITE_BWD_WGRAD, st);
   return e;
 }
 
+// Row tile height for a row-grouped launch.  Routed experts hold ~T k / E
+// rows each, so few that the GEMM is bound by streaming the expert's weights:
+// 256-row tiles (64 columns) read each weight column block once per expert
+// with up to 256 rows.  Otherwise (one group, or many rows per group)
+// 128 x 128 tiles.
+int row_tile(int64_t rows, int G) {
+  if (G <= 1) return 128;
+  return cdiv(rows, G) <= 256 ? 256 : 128;
+}
+int max_tiles_for(int64_t rows, int G, int bm) { return (int)(cdiv(rows, bm) + std::min<int64_t>(rows, G) + 1); }
+
 }  // namespace
 
-int bwd_max_tiles(int64_t rows, int G) { return (int)(cdiv(rows, BT) + std::min<int64_t>(rows, G) + 1); }
+int bwd_max_tiles(int64_t rows, int G) { return max_tiles_for(rows, G, 128); }
 
 hipError_t launch_expert_backward(const BwdExpert &X, hipStream_t st) {
   const int H = X.H, I = X.I, G = X.G;
   const int64_t N = X.rows;
   hipError_t e;
   if (N > 0) {
+    const int bm = row_tile(N, G);
+    const int mt = max_tiles_for(N, G, bm);
+    if (mt > X.max_tiles) return hipErrorInvalidValue;
     FfnGroup fg{};
     fg.off = X.off;
     fg.E = G;
     fg.nrows = (int32_t)N;
-    e = launch_build_tiles(fg, BT, X.max_tiles, reinterpret_cast<TileEntry *>(X.tiles + kTileHdrWords), X.tiles, st);
+    e = launch_build_tiles(fg, bm, mt, reinterpret_cast<TileEntry *>(X.tiles + kTileHdrWords), X.tiles, st);
     if (e != hipSuccess) return e;
     // z = x W_gu^T: B(n = j, k = h) = W_gu[g][j][h]
     e = gemm_rows(GemmOp{X.x, 0, H, 1}, GemmOp{X.wgu, (int64_t)2 * I * H, H, 1}, X.z, 2 * I, X.off, G, N, 2 * I, H,
-                  X.tiles, X.max_tiles, st);
+                  X.tiles, bm, mt, st);
     if (e != hipSuccess) return e;
     // u = dy W_d: B(n = i, k = c) = W_d[g][c][i]
-    e = gemm_rows(GemmOp{X.dy, 0, H, 1}, GemmOp{X.wd, (int64_t)H * I, 1, I}, X.u, I, X.off, G, N, I, H, X.tiles,
-                  X.max_tiles, st);
+    e = gemm_rows(GemmOp{X.dy, 0, H, 1}, GemmOp{X.wd, (int64_t)H * I, 1, I}, X.u, I, X.off, G, N, I, H, X.tiles, bm,
+                  mt, st);
     if (e != hipSuccess) return e;
     // rows past off[G] (assignments the sort dropped) belong to no expert
     const int32_t *kept = X.off ? X.off + G : nullptr;
@@ -399,7 +486,7 @@ hipError_t launch_expert_backward(const BwdExpert &X, hipStream_t st) {
     bwd_dz_kernel<<<(unsigned)N, 256, 0, st>>>(X.z, X.u, X.gates, X.perm_src, kept, N, I, X.dz);
     // dx rows = dz W_gu: B(n = h, k = j) = W_gu[g][j][h]
     e = gemm_rows(GemmOp{X.dz, 0, 2 * I, 1}, GemmOp{X.wgu, (int64_t)2 * I * H, 1, H}, X.dx_rows, H, X.off, G, N, H,
-                  2 * I, X.tiles, X.max_tiles, st);
+                  2 * I, X.tiles, bm, mt, st);
     if (e != hipSuccess) return e;
   }
   // dW_d[g] = dy^T hg over g's rows: A(m = c, k = p) = dy[p][c], B(n = i, k = p) = hg[p][i]

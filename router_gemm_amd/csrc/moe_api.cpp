@@ -525,6 +525,9 @@ moe_status moe_backward(const moe_layer *L, const void *x, int64_t T, const int3
     if (L->shared_inter > 0 && (!dw_shared_gate_up || !dw_shared_down))
       return fail(MOE_EINVAL, "shared expert gradients are NULL");
     if (!aligned16(x) || !aligned16(dy) || !aligned16(L->w_router)) return fail(MOE_EINVAL, "x, dy or w_router not 16-byte aligned");
+    if (!aligned16(dx) || !aligned16(dw_gate_up) || !aligned16(dw_down) || !aligned16(dw_router) ||
+        !aligned16(dw_shared_gate_up) || !aligned16(dw_shared_down))
+      return fail(MOE_EINVAL, "gradient outputs not 16-byte aligned");
     if ((s = check_expert_weights(L)) != MOE_OK) return s;
     if ((s = check_shared(L)) != MOE_OK) return s;
   }

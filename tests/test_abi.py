@@ -144,6 +144,7 @@ def test_backward_refusals_without_gpu():
     assert need > lib.moe_workspace_bytes(C.byref(L), 64, 512)
     assert lib.moe_backward(*args(nb=need - 1)) == B.MOE_EWORKSPACE
     assert lib.moe_backward(*args(dx=None)) == B.MOE_EINVAL
+    assert lib.moe_backward(*args(dx=FAKE + 4)) == B.MOE_EINVAL and b"aligned" in lib.moe_last_error()
     assert lib.moe_backward(*args(dsgu=None)) == B.MOE_EINVAL and b"shared" in lib.moe_last_error()
     assert lib.moe_backward(*args(T=0, ws=None, nb=0)) == B.MOE_OK        # no-op
     L = layer(dtype=B.MOE_FP8_E4M3FN)
