@@ -27,7 +27,6 @@ namespace moe {
 
 namespace {
 constexpr int BK = 64;           // K step
-constexpr int kGemmThreads = 256;
 }  // namespace
 
 // Operand element (r, k) of group g: base + g * gstride + r * rs + k * ks (bf16).
@@ -62,24 +61,27 @@ __device__ __forceinline__ int lds_pos(int r, int k) {
   return r * BK + (((k >> 3) ^ sw) << 3) + (k & 7);
 }
 
-// Global loads of one operand's ROWS x 64 tile into registers: ROWS / 32
-// chunks of 16 bytes per thread.  N layout: chunk q = tid + 256 j holds row
-// q / 8, k 8 (q % 8) .. +7.  T layout: the thread's rows are
-// 8 (tid % (ROWS/8)) .. +7 and its k are (ROWS/32) (tid / (ROWS/8)) + j.
+// Global loads of one operand's ROWS x 64 tile into registers by NT threads:
+// CPT = 8 ROWS / NT chunks of 16 bytes per thread.  N layout: chunk
+// q = tid + NT j holds row q / 8, k 8 (q % 8) .. +7.  T layout: the thread's
+// rows are 8 (tid % (ROWS/8)) .. +7 and its k are CPT (tid / (ROWS/8)) + j.
 // Rows >= nr and k >= nk read as zero (rows come in whole chunks: every row
-// count and pitch here is a multiple of 8).
-template <bool T, int ROWS>
-__device__ __forceinline__ void tile_load(const uint16_t *base, int64_t rs, int64_t ks, int r0, int nr, int k0,
-                                          int nk, i32x4 (&v)[ROWS / 32]) {
-  static_assert(ROWS == 64 || ROWS == 128 || ROWS == 256, "tiles are 64, 128 or 256 rows");
-  constexpr int RC = ROWS / 8, KPT = ROWS / 32;
+// count and pitch here is a multiple of 8): such a chunk is loaded from the
+// operand's base instead (no branch around the load) and bit j of the
+// returned mask, clear, makes tile_store write zeros for it.
+template <bool T, int ROWS, int NT>
+__device__ __forceinline__ uint32_t tile_load(const uint16_t *base, int64_t rs, int64_t ks, int r0, int nr, int k0,
+                                              int nk, i32x4 (&v)[8 * ROWS / NT]) {
+  constexpr int RC = ROWS / 8, KPT = 8 * ROWS / NT;
+  static_assert(KPT == 2 || KPT == 4 || KPT == 8, "2, 4 or 8 chunks per thread");
   const int tid = threadIdx.x;
+  uint32_t mask = 0;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     int r, k;
     int64_t o;
     if (!T) {
-      const int q = tid + kGemmThreads * j;
+      const int q = tid + NT * j;
       r = r0 + (q >> 3);
       k = k0 + ((q & 7) << 3);
       o = (int64_t)r * rs + k;
@@ -88,8 +90,11 @@ __device__ __forceinline__ void tile_load(const uint16_t *base, int64_t rs, int6
       k = k0 + (tid / RC) * KPT + j;
       o = (int64_t)k * ks + r;
     }
-    v[j] = (r < nr && k < nk) ? load16(base + o) : i32x4{0, 0, 0, 0};
+    const bool ok = r < nr && k < nk;
+    v[j] = load16(base + (ok ? o : 0));
+    mask |= (uint32_t)ok << j;
   }
+  return mask;
 }
 
 // Element 2 h + odd (h constant, odd 0 or 1 per lane) of a 16-byte chunk of bf16.
@@ -97,14 +102,17 @@ __device__ __forceinline__ uint32_t chunk_elem(const i32x4 &v, int h, int odd) {
   return ((uint32_t)v[h] >> (16 * odd)) & 0xFFFFu;
 }
 
-template <bool T, int ROWS>
-__device__ __forceinline__ void tile_store(uint16_t *s, const i32x4 (&v)[ROWS / 32]) {
-  constexpr int RC = ROWS / 8, KPT = ROWS / 32;
+template <bool T, int ROWS, int NT>
+__device__ __forceinline__ void tile_store(uint16_t *s, const i32x4 (&raw)[8 * ROWS / NT], uint32_t mask) {
+  constexpr int RC = ROWS / 8, KPT = 8 * ROWS / NT;
   const int tid = threadIdx.x;
+  i32x4 v[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) v[j] = ((mask >> j) & 1) ? raw[j] : i32x4{0, 0, 0, 0};
   if (!T) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const int q = tid + kGemmThreads * j;
+      const int q = tid + NT * j;
       *reinterpret_cast<i32x4 *>(s + lds_pos<false>(q >> 3, (q & 7) << 3)) = v[j];
     }
   } else {
@@ -129,17 +137,21 @@ __device__ __forceinline__ void tile_store(uint16_t *s, const i32x4 (&v)[ROWS / 
   }
 }
 
-// BM x BN output tile, four waves each computing 64 x 64: BM = 128, BN = 128
-// (2 x 2 waves) or BM = 256, BN = 64 (4 x 1 waves: row-grouped launches
-// whose groups hold up to 256 rows, so that each group's weight columns are
-// streamed from HBM once rather than once per 128-row tile).
+// BM x BN output tile, one 64 x 64 block per wave: BM = BN = 128 (2 x 2
+// waves), or BM = 256, BN = 128 (4 x 2 waves, 512 threads) for row-grouped
+// launches whose groups hold up to 256 rows, so that each group's weight
+// columns are streamed from HBM once rather than once per 128-row tile, and
+// each token row staged serves 128 weight columns.
 // NB = 2: two LDS stages (one barrier per K step); NB = 1: one stage and half
 // the LDS (two barriers per K step, more workgroups per CU: for the short
 // token ranges of the weight gradients).
+template <int BM, int BN>
+constexpr int gemm_threads() { return 64 * (BM / 64) * (BN / 64); }
+
 template <int BM, int BN, int NB, bool AT, bool BTL>
-__global__ __launch_bounds__(kGemmThreads) void grouped_gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__((64 * (BM / 64) * (BN / 64))) void grouped_gemm_kernel(GemmArgs a) {
+  constexpr int NT = gemm_threads<BM, BN>();
   constexpr int WMW = BM / 64;  // waves along M
-  static_assert(BN == 64 * (4 / WMW), "four 64 x 64 waves");
   // Staged operand tiles; K-grouped launches (weight gradients, both
   // operands T-layout) reuse the space to stage half the output tile at a
   // time, 64 rows of BN + 4 floats.
@@ -186,13 +198,18 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_kernel(GemmArgs a) 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // K step s is computed from LDS stage s % NB while the global loads of
+  // step s + 1 are in flight into registers; they move into LDS at the end
+  // of step s.  (Two steps of loads in flight gained nothing here and cost
+  // the weight-gradient launches a wave per SIMD.)
   const int nsteps = (int)cdiv(kend - kbeg, BK);
-  i32x4 va[BM / 32], vb[BN / 32];
+  i32x4 va[8 * BM / NT], vb[8 * BN / NT];
+  uint32_t ma = 0, mb = 0;
   if (nsteps > 0) {
-    tile_load<AT, BM>(abase, a.a.rs, a.a.ks, m0, mend, kbeg, kend, va);
-    tile_load<BTL, BN>(bbase, a.b.rs, a.b.ks, n0, a.N, kbeg, kend, vb);
-    tile_store<AT, BM>(sa[0], va);
-    tile_store<BTL, BN>(sb[0], vb);
+    ma = tile_load<AT, BM, NT>(abase, a.a.rs, a.a.ks, m0, mend, kbeg, kend, va);
+    mb = tile_load<BTL, BN, NT>(bbase, a.b.rs, a.b.ks, n0, a.N, kbeg, kend, vb);
+    tile_store<AT, BM, NT>(sa[0], va, ma);
+    tile_store<BTL, BN, NT>(sb[0], vb, mb);
     __syncthreads();
   }
   for (int s = 0; s < nsteps; ++s) {
@@ -200,8 +217,8 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_kernel(GemmArgs a) 
     const bool more = s + 1 < nsteps;
     if (more) {
       const int k1 = kbeg + (s + 1) * BK;
-      tile_load<AT, BM>(abase, a.a.rs, a.a.ks, m0, mend, k1, kend, va);
-      tile_load<BTL, BN>(bbase, a.b.rs, a.b.ks, n0, a.N, k1, kend, vb);
+      ma = tile_load<AT, BM, NT>(abase, a.a.rs, a.a.ks, m0, mend, k1, kend, va);
+      mb = tile_load<BTL, BN, NT>(bbase, a.b.rs, a.b.ks, n0, a.N, k1, kend, vb);
     }
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
@@ -222,8 +239,8 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_kernel(GemmArgs a) 
     }
     if (NB == 1) __syncthreads();   // every wave is done with the stage before it is refilled
     if (more) {
-      tile_store<AT, BM>(sa[NB == 2 ? buf ^ 1 : 0], va);
-      tile_store<BTL, BN>(sb[NB == 2 ? buf ^ 1 : 0], vb);
+      tile_store<AT, BM, NT>(sa[NB == 2 ? buf ^ 1 : 0], va, ma);
+      tile_store<BTL, BN, NT>(sb[NB == 2 ? buf ^ 1 : 0], vb, mb);
     }
     __syncthreads();
   }
@@ -249,7 +266,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_kernel(GemmArgs a) 
       }
       __syncthreads();
 #pragma unroll
-      for (int q = tid; q < 64 * BN / 4; q += kGemmThreads) {
+      for (int q = tid; q < 64 * BN / 4; q += NT) {
         const int row = q / (BN / 4), c4 = q % (BN / 4);
         const int m = m0 + 64 * half + row, n = n0 + 4 * c4;
         if (m < mend && n < a.N)
@@ -398,11 +415,11 @@ hipError_t launch_gemm(const GemmArgs &a, bool at, bool bt, int64_t nblocks, hip
   if (nblocks > INT32_MAX) return hipErrorInvalidValue;
   const unsigned blocks = (unsigned)nblocks;
   if (!at && !bt)
-    grouped_gemm_kernel<BM, BN, 2, false, false><<<blocks, kGemmThreads, 0, st>>>(a);
+    grouped_gemm_kernel<BM, BN, 2, false, false><<<blocks, gemm_threads<BM, BN>(), 0, st>>>(a);
   else if (!at && bt)
-    grouped_gemm_kernel<BM, BN, 2, false, true><<<blocks, kGemmThreads, 0, st>>>(a);
+    grouped_gemm_kernel<BM, BN, 2, false, true><<<blocks, gemm_threads<BM, BN>(), 0, st>>>(a);
   else if (at && bt && BM == 128 && BN == 128)
-    grouped_gemm_kernel<128, 128, 1, true, true><<<blocks, kGemmThreads, 0, st>>>(a);
+    grouped_gemm_kernel<128, 128, 1, true, true><<<blocks, gemm_threads<128, 128>(), 0, st>>>(a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -419,11 +436,11 @@ hipError_t gemm_rows(const GemmOp &A, const GemmOp &B, float *c, int64_t ldc, co
   if (rows == 0) return hipSuccess;
   if (op_t(A) || K % BK != 0) return hipErrorInvalidValue;
   const TileEntry *tiles = reinterpret_cast<const TileEntry *>(tiles_ws + kTileHdrWords);
-  const int bn = bm == 256 ? 64 : 128;
+  const int bn = 128;
   GemmArgs a{A, B, c, ldc, 0, off, G, (int)rows, N, K, 0, (int)cdiv(N, bn), tiles, tiles_ws};
   const int64_t blocks = (int64_t)max_tiles * a.ntn;
   timing_before(MOE_SITE_BWD_DGRAD, st);
-  const hipError_t e = bm == 256 ? launch_gemm<256, 64>(a, false, op_t(B), blocks, st)
+  const hipError_t e = bm == 256 ? launch_gemm<256, 128>(a, false, op_t(B), blocks, st)
                                  : launch_gemm<128, 128>(a, false, op_t(B), blocks, st);
   timing_after(MOE_SITE_BWD_DGRAD, st);
   return e;
@@ -444,9 +461,8 @@ hipError_t gemm_kseg(const GemmOp &A, const GemmOp &B, float *c, int64_t ldc, in
 
 // Row tile height for a row-grouped launch.  Routed experts hold ~T k / E
 // rows each, so few that the GEMM is bound by streaming the expert's weights:
-// 256-row tiles (64 columns) read each weight column block once per expert
-// with up to 256 rows.  Otherwise (one group, or many rows per group)
-// 128 x 128 tiles.
+// 256-row tiles read each weight column block once per expert with up to 256
+// rows.  Otherwise (one group, or many rows per group) 128-row tiles.
 int row_tile(int64_t rows, int G) {
   if (G <= 1) return 128;
   return cdiv(rows, G) <= 256 ? 256 : 128;
