@@ -299,8 +299,9 @@ def main():
 
 
 def bench_train(args, cfg, lt, x, dev):
-    """Training step of the layer: moe_forward then moe_backward (all weight,
-    router and input gradients) on one batch of tokens."""
+    """Training step of the layer: moe_forward_train (the forward, keeping the
+    expert pre-activations) then moe_backward (all weight, router and input
+    gradients) on one batch of tokens."""
     import numpy as np
     import torch
 
@@ -321,9 +322,11 @@ def bench_train(args, cfg, lt, x, dev):
                  dw_shared_gate_up=f32(2 * Is, H) if Is else None, dw_shared_down=f32(H, Is) if Is else None,
                  dw_router=f32(E, H), dbias=f32(E) if lt.router_bias is not None else None)
 
+    z_saved = torch.empty(B.moe_saved_z_floats(layer, T), dtype=torch.float32, device=dev)
+
     def step():
-        B.moe_forward(layer, x, T, y, topk_ids=ids, topk_gates=gts, ws=ws_f)
-        B.moe_backward(layer, x, T, ids, gts, dy, ws=ws_b, **grads)
+        B.moe_forward_train(layer, x, T, y, ids, gts, z_saved, ws=ws_f)
+        B.moe_backward(layer, x, T, ids, gts, dy, z_saved=z_saved, ws=ws_b, **grads)
 
     step()
     torch.cuda.synchronize()
@@ -354,9 +357,9 @@ def bench_train(args, cfg, lt, x, dev):
     # model flops of a training step: forward, plus twice the expert GEMM flops for the
     # data and weight gradients, plus the router's two gradient products
     model_flops = fwd_flops + 2.0 * 6 * ih + 2.0 * 2 * N * H
-    # the backward's grouped GEMM launches: recompute of z (2IH), dy W_down (IH), dz W_gate_up
-    # (2IH) per row = dgrad site; dW_down (IH) and dW_gate_up (2IH) per row = wgrad site
-    dgrad_flops, wgrad_flops = 2.0 * 5 * ih, 2.0 * 3 * ih
+    # the backward's grouped GEMM launches (the forward keeps z, so no recompute): dy W_down (IH)
+    # and dz W_gate_up (2IH) per row = dgrad site; dW_down (IH) and dW_gate_up (2IH) = wgrad site
+    dgrad_flops, wgrad_flops = 2.0 * 3 * ih, 2.0 * 3 * ih
     g_ms = {nm: ms / K for nm, (ms, n) in gemm.items()}
     g_launch = {nm: max(n // K, 1) for nm, (ms, n) in gemm.items()}
     gemm_ms = sum(g_ms.values())
@@ -366,7 +369,7 @@ def bench_train(args, cfg, lt, x, dev):
             "frac": round(achieved / peak, 4), "traffic": None,
             "traffic_note": "no counters taken on these kernel sources",
             "library_source_hash": library_source_hash(),
-            "kernel": "grouped bf16 GEMM of the backward (all its launches in a step: recompute, dgrad, wgrad)",
+            "kernel": "grouped bf16 GEMM of the backward (all its launches in a step: dgrad, wgrad)",
             "kernel_ms_per_step": round(gemm_ms, 4),
             "launches_per_step": sum(g_launch.values()),
             "algorithmic_flops_per_step": dgrad_flops + wgrad_flops,
@@ -391,7 +394,7 @@ def bench_train(args, cfg, lt, x, dev):
         "metric": METRIC, "value": round(T / t_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": cfg.name, "step": "moe_forward + moe_backward (all gradients)", "tokens": T,
+        "config": {"workload": cfg.name, "step": "moe_forward_train + moe_backward (all gradients)", "tokens": T,
                    "hidden": H, "experts": E, "top_k": k, "inter": I, "shared_inter": Is, "expert_dtype": "bf16",
                    "assignments": N, "active_experts": int((counts > 0).sum()),
                    "min_rows_per_expert": int(counts.min()), "max_rows_per_expert": int(counts.max()),

@@ -217,14 +217,17 @@ size_t moe_backward_workspace_bytes(const moe_layer *layer, int64_t T);
  *   each expert's SwiGLU FFN is differentiated with output gradient g_j dy
  *   (shared expert: dy); dW_router[e] += dl_j x, dbias[e] += dl_j,
  *   dx += dl_j W_router[e_j].
- * Recomputes the expert pre-activations from x (nothing is kept from the
- * forward but topk_ids and topk_gates).  GEMM inputs are bf16 (x, dy, the
+ * The expert pre-activations come from z_saved (moe_forward_train on the
+ * same x; its ids and gates) or, with z_saved NULL, are recomputed from x
+ * (then nothing is kept from the forward but topk_ids and topk_gates).
+ * GEMM inputs are bf16 (x, dy, the
  * weights, g * h and the gradient of the pre-activations, rounded to bf16),
  * accumulation fp32; per-row and per-token reductions in a fixed order.
  *   x            bf16 [T, H]  (the forward's input)
  *   topk_ids     int32 [T, k] (the forward's choice; an id outside [0, E) is skipped)
  *   topk_gates   f32 [T, k]   (the forward's gates: softmax over the chosen logits)
  *   dy           bf16 [T, H]  (gradient of the layer output)
+ *   z_saved      f32, layout of moe_forward_train, or NULL
  *   dx           f32 [T, H] out
  *   dw_gate_up   f32 [E, 2I, H] out;  dw_down f32 [E, H, I] out
  *   dw_shared_gate_up f32 [2Is, H] out, dw_shared_down f32 [H, Is] out (NULL if Is == 0)
@@ -234,10 +237,29 @@ size_t moe_backward_workspace_bytes(const moe_layer *layer, int64_t T);
  * and w_router are required.  T == 0 is a no-op (nothing written). */
 moe_status moe_backward(const moe_layer *layer, const void *x, int64_t T,
                         const int32_t *topk_ids, const float *topk_gates, const void *dy,
-                        float *dx, float *dw_gate_up, float *dw_down,
+                        const float *z_saved, float *dx, float *dw_gate_up, float *dw_down,
                         float *dw_shared_gate_up, float *dw_shared_down,
                         float *dw_router, float *dbias,
                         void *ws, size_t ws_bytes, void *stream);
+
+/* Floats of the pre-activation buffer moe_forward_train fills for up to T
+ * tokens: T*k*2I (routed rows) + T*2Is (shared expert).  0 on invalid
+ * arguments. */
+size_t moe_saved_z_floats(const moe_layer *layer, int64_t T);
+
+/* moe_forward for training (bf16 experts only): the same launches and the
+ * same outputs, and the gate/up GEMMs also write their fp32 pre-activations
+ * z = [a W_g^T | a W_u^T] (2I values per row; Megatron-style activation
+ * saving, so that moe_backward need not recompute them):
+ *   z_saved  f32 out, moe_saved_z_floats(layer, T) floats: rows 0..T*k-1 =
+ *            the routed assignments in expert order (the order of moe_permute
+ *            on topk_ids; rows of dropped assignments are left unwritten),
+ *            then T rows of the shared expert in token order ([T, 2Is]).
+ * topk_ids and topk_gates are required (moe_backward takes them). */
+moe_status moe_forward_train(const moe_layer *layer, const void *x, int64_t T,
+                             void *y, int32_t out_dtype,
+                             int32_t *topk_ids, float *topk_gates, float *z_saved,
+                             void *ws, size_t ws_bytes, void *stream);
 
 /* Static string naming a status. */
 const char *moe_status_string(moe_status s);

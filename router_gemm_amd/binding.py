@@ -45,7 +45,8 @@ class MoELayerC(C.Structure):
 
 
 EXPORTS = ["moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_forward", "moe_backward_workspace_bytes", "moe_backward", "moe_status_string",
+           "moe_forward", "moe_saved_z_floats", "moe_forward_train", "moe_backward_workspace_bytes",
+           "moe_backward", "moe_status_string",
            "moe_last_error", "moe_timing_arm", "moe_timing_read"]
 
 _lib = None
@@ -74,7 +75,11 @@ def lib() -> C.CDLL:
         L.moe_backward_workspace_bytes.restype = sz
         L.moe_backward_workspace_bytes.argtypes = [vp, i64]
         L.moe_backward.restype = C.c_int
-        L.moe_backward.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_backward.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_saved_z_floats.restype = sz
+        L.moe_saved_z_floats.argtypes = [vp, i64]
+        L.moe_forward_train.restype = C.c_int
+        L.moe_forward_train.argtypes = [vp, vp, i64, vp, i32, vp, vp, vp, vp, sz, vp]
         L.moe_status_string.restype = C.c_char_p
         L.moe_status_string.argtypes = [C.c_int]
         L.moe_last_error.restype = C.c_char_p
@@ -200,11 +205,24 @@ def backward_workspace(layer: Layer, T: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(moe_backward_workspace_bytes(layer, T), 256), dtype=torch.uint8, device=device)
 
 
+def moe_saved_z_floats(layer: Layer, T: int) -> int:
+    return int(lib().moe_saved_z_floats(layer.ref, T))
+
+
+def moe_forward_train(layer: Layer, x, T, y, topk_ids, topk_gates, z_saved, out_dtype=None, ws=None,
+                      stream=None):
+    w, nb = _ws(ws)
+    od = dtype_code(y) if out_dtype is None else out_dtype
+    _check(lib().moe_forward_train(layer.ref, _ptr(x), T, _ptr(y), od, _ptr(topk_ids), _ptr(topk_gates),
+                                   _ptr(z_saved), w, nb, _stream(stream)))
+
+
 def moe_backward(layer: Layer, x, T, topk_ids, topk_gates, dy, dx, dw_gate_up, dw_down,
-                 dw_shared_gate_up, dw_shared_down, dw_router, dbias=None, ws=None, stream=None):
+                 dw_shared_gate_up, dw_shared_down, dw_router, dbias=None, z_saved=None, ws=None,
+                 stream=None):
     w, nb = _ws(ws)
     _check(lib().moe_backward(layer.ref, _ptr(x), T, _ptr(topk_ids), _ptr(topk_gates), _ptr(dy),
-                              _ptr(dx), _ptr(dw_gate_up), _ptr(dw_down), _ptr(dw_shared_gate_up),
+                              _ptr(z_saved), _ptr(dx), _ptr(dw_gate_up), _ptr(dw_down), _ptr(dw_shared_gate_up),
                               _ptr(dw_shared_down), _ptr(dw_router), _ptr(dbias), w, nb,
                               _stream(stream)))
 

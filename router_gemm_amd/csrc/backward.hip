@@ -487,10 +487,12 @@ hipError_t launch_expert_backward(const BwdExpert &X, hipStream_t st) {
     fg.nrows = (int32_t)N;
     e = launch_build_tiles(fg, bm, mt, reinterpret_cast<TileEntry *>(X.tiles + kTileHdrWords), X.tiles, st);
     if (e != hipSuccess) return e;
-    // z = x W_gu^T: B(n = j, k = h) = W_gu[g][j][h]
-    e = gemm_rows(GemmOp{X.x, 0, H, 1}, GemmOp{X.wgu, (int64_t)2 * I * H, H, 1}, X.z, 2 * I, X.off, G, N, 2 * I, H,
-                  X.tiles, bm, mt, st);
-    if (e != hipSuccess) return e;
+    // z = x W_gu^T: B(n = j, k = h) = W_gu[g][j][h] (unless the forward kept it)
+    if (!X.z_given) {
+      e = gemm_rows(GemmOp{X.x, 0, H, 1}, GemmOp{X.wgu, (int64_t)2 * I * H, H, 1}, X.z, 2 * I, X.off, G, N, 2 * I, H,
+                    X.tiles, bm, mt, st);
+      if (e != hipSuccess) return e;
+    }
     // u = dy W_d: B(n = i, k = c) = W_d[g][c][i]
     e = gemm_rows(GemmOp{X.dy, 0, H, 1}, GemmOp{X.wd, (int64_t)H * I, 1, I}, X.u, I, X.off, G, N, I, H, X.tiles, bm,
                   mt, st);

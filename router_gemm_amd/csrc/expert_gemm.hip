@@ -448,6 +448,11 @@ __device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry 
         const uint32_t lo = f32_to_bf16(hv[i][m][0]) | (f32_to_bf16(hv[i][m][1]) << 16);
         const uint32_t hi = f32_to_bf16(hv[i][m][2]) | (f32_to_bf16(hv[i][m][3]) << 16);
         *reinterpret_cast<uint2 *>(G.h + ((int64_t)xrow[m] * I + col) * 2) = make_uint2(lo, hi);
+        if (G.z) {   // pre-activations kept for a backward
+          float *zr = G.z + (int64_t)xrow[m] * 2 * I + col;
+          *reinterpret_cast<f32x4 *>(zr) = ag[i][m];
+          *reinterpret_cast<f32x4 *>(zr + I) = au[i][m];
+        }
       }
     }
   } else {

@@ -325,6 +325,11 @@ __device__ __forceinline__ void tiled_item(const FfnGroup &G, const TileEntry &t
           const uint32_t lo = f32_to_bf16(hv[i][j][0]) | (f32_to_bf16(hv[i][j][1]) << 16);
           const uint32_t hi = f32_to_bf16(hv[i][j][2]) | (f32_to_bf16(hv[i][j][3]) << 16);
           *reinterpret_cast<uint2 *>(G.h + ((int64_t)(rbeg + tr) * I + col) * 2) = make_uint2(lo, hi);
+          if (G.z) {   // pre-activations kept for a backward
+            float *zr = G.z + (int64_t)(rbeg + tr) * 2 * I + col;
+            *reinterpret_cast<f32x4 *>(zr) = acc[i][j];
+            *reinterpret_cast<f32x4 *>(zr + I) = acc[i + 4][j];
+          }
         }
       }
     } else {

@@ -453,8 +453,9 @@ moe_status moe_combine(const moe_layer *L, const void *y_perm, int32_t y_dtype, 
                     "moe_combine");
 }
 
-moe_status moe_forward(const moe_layer *L, const void *x, int64_t T, void *y, int32_t out_dtype, int32_t *topk_ids,
-                       float *topk_gates, void *ws, size_t ws_bytes, void *stream) {
+namespace {
+moe_status forward_impl(const moe_layer *L, const void *x, int64_t T, void *y, int32_t out_dtype, int32_t *topk_ids,
+                        float *topk_gates, float *z_saved, void *ws, size_t ws_bytes, void *stream) {
   moe_status s;
   if ((s = check_layer_shape(L, true)) != MOE_OK) return s;
   if ((s = check_rows(T, T * (int64_t)L->top_k)) != MOE_OK) return s;
@@ -499,11 +500,38 @@ moe_status moe_forward(const moe_layer *L, const void *x, int64_t T, void *y, in
                                 is_fp8(L), f.x_perm, f.x_scale, st);
     if (e != hipSuccess) return hip_status(e, "moe_forward: gather");
   }
+  if (z_saved) {   // routed rows in expert order, then the shared expert's rows
+    R.z = z_saved;
+    if (f.ngroups == 2) f.groups[0].z = z_saved + (size_t)N * 2 * L->inter;
+  }
   e = moe::launch_expert_ffn(f.groups, f.ngroups, H, f.ffn.plan, f.ffn.tiles, MOE_SITE_GATE_UP, st);
   if (e != hipSuccess) return hip_status(e, "moe_forward: experts");
   e = moe::launch_combine(f.y_perm, false, f.perm_pos, nullptr, nullptr, L->top_k, gates, f.sh_out, out_f32, T, H, N, y,
                           out_f32, st);
   return hip_status(e, "moe_forward: combine");
+}
+}  // namespace
+
+moe_status moe_forward(const moe_layer *L, const void *x, int64_t T, void *y, int32_t out_dtype, int32_t *topk_ids,
+                       float *topk_gates, void *ws, size_t ws_bytes, void *stream) {
+  return forward_impl(L, x, T, y, out_dtype, topk_ids, topk_gates, nullptr, ws, ws_bytes, stream);
+}
+
+size_t moe_saved_z_floats(const moe_layer *L, int64_t T) {
+  if (check_layer_shape(L, true) != MOE_OK || check_rows(T, T * (int64_t)L->top_k) != MOE_OK) return 0;
+  return (size_t)T * L->top_k * 2 * L->inter + (size_t)T * 2 * L->shared_inter;
+}
+
+moe_status moe_forward_train(const moe_layer *L, const void *x, int64_t T, void *y, int32_t out_dtype,
+                             int32_t *topk_ids, float *topk_gates, float *z_saved, void *ws, size_t ws_bytes,
+                             void *stream) {
+  moe_status s;
+  if ((s = check_layer_shape(L, true)) != MOE_OK) return s;
+  if (L->expert_dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "moe_forward_train needs bf16 experts");
+  if (T > 0 && (!topk_ids || !topk_gates || !z_saved))
+    return fail(MOE_EINVAL, "moe_forward_train needs topk_ids, topk_gates and z_saved");
+  if (T > 0 && !aligned16(z_saved)) return fail(MOE_EINVAL, "z_saved not 16-byte aligned");
+  return forward_impl(L, x, T, y, out_dtype, topk_ids, topk_gates, z_saved, ws, ws_bytes, stream);
 }
 
 size_t moe_backward_workspace_bytes(const moe_layer *L, int64_t T) {
@@ -512,7 +540,8 @@ size_t moe_backward_workspace_bytes(const moe_layer *L, int64_t T) {
 }
 
 moe_status moe_backward(const moe_layer *L, const void *x, int64_t T, const int32_t *topk_ids,
-                        const float *topk_gates, const void *dy, float *dx, float *dw_gate_up, float *dw_down,
+                        const float *topk_gates, const void *dy, const float *z_saved, float *dx,
+                        float *dw_gate_up, float *dw_down,
                         float *dw_shared_gate_up, float *dw_shared_down, float *dw_router, float *dbias, void *ws,
                         size_t ws_bytes, void *stream) {
   moe_status s;
@@ -525,7 +554,7 @@ moe_status moe_backward(const moe_layer *L, const void *x, int64_t T, const int3
     if (L->shared_inter > 0 && (!dw_shared_gate_up || !dw_shared_down))
       return fail(MOE_EINVAL, "shared expert gradients are NULL");
     if (!aligned16(x) || !aligned16(dy) || !aligned16(L->w_router)) return fail(MOE_EINVAL, "x, dy or w_router not 16-byte aligned");
-    if (!aligned16(dx) || !aligned16(dw_gate_up) || !aligned16(dw_down) || !aligned16(dw_router) ||
+    if (!aligned16(dx) || !aligned16(dw_gate_up) || !aligned16(dw_down) || !aligned16(dw_router) || !aligned16(z_saved) ||
         !aligned16(dw_shared_gate_up) || !aligned16(dw_shared_down))
       return fail(MOE_EINVAL, "gradient outputs not 16-byte aligned");
     if ((s = check_expert_weights(L)) != MOE_OK) return s;
@@ -560,6 +589,10 @@ moe_status moe_backward(const moe_layer *L, const void *x, int64_t T, const int3
   R.perm_src = b.perm_src;
   R.perm_pos = b.perm_pos;
   R.dl = b.dl;
+  if (z_saved) {   // the forward's pre-activations: no recompute
+    R.z = const_cast<float *>(z_saved);
+    R.z_given = 1;
+  }
   R.dwgu = dw_gate_up;
   R.dwd = dw_down;
   e = moe::launch_expert_backward(R, st);
@@ -575,6 +608,10 @@ moe_status moe_backward(const moe_layer *L, const void *x, int64_t T, const int3
     S.dy = static_cast<const uint16_t *>(dy);
     S.wgu = static_cast<const uint16_t *>(L->w_shared_gate_up);
     S.wd = static_cast<const uint16_t *>(L->w_shared_down);
+    if (z_saved) {
+      S.z = const_cast<float *>(z_saved) + (size_t)N * 2 * L->inter;
+      S.z_given = 1;
+    }
     S.dwgu = dw_shared_gate_up;
     S.dwd = dw_shared_down;
     e = moe::launch_expert_backward(S, st);

@@ -65,6 +65,9 @@ struct FfnGroup {
   // xsrc[r] / xdiv of x (and xs), so the rows need not be gathered first.
   const int32_t *xsrc;
   int32_t xdiv;
+  // Optional (bf16 experts): [nrows, 2I] fp32, receives the gate/up
+  // pre-activations of each row (gate half, then up half) for a backward.
+  float *z;
 };
 constexpr int kMaxGroups = 2;
 // Tile list entry: group (0 or 1), expert of that group, first row (relative
@@ -120,7 +123,8 @@ struct BwdExpert {
   const float *gates;        // [T*k] gate of each assignment, or NULL (gate 1)
   const int32_t *perm_src;   // [N] assignment of each row (with gates)
   const int32_t *perm_pos;   // [T*k] row of each assignment (with dl)
-  float *z;                  // [N, 2I] scratch: recomputed pre-activations
+  float *z;                  // [N, 2I] pre-activations: recomputed here, or given (z_given)
+  int z_given;
   float *u;                  // [N, I] scratch: dy W_down
   uint16_t *hg;              // [N, I] scratch: gate * h, bf16
   uint16_t *dz;              // [N, 2I] scratch: gradient of z, bf16

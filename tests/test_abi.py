@@ -138,13 +138,14 @@ def test_backward_refusals_without_gpu():
     workspace size (moe_workspace_bytes does not cover it)."""
     lib = B.lib()
     L = layer(dtype=B.MOE_BF16)
-    args = lambda T=64, dx=FAKE, dsgu=FAKE, ws=FAKE, nb=1 << 40: (
-        C.byref(L), FAKE, T, FAKE, FAKE, FAKE, dx, FAKE, FAKE, dsgu, FAKE, FAKE, None, ws, nb, None)
+    args = lambda T=64, dx=FAKE, dsgu=FAKE, ws=FAKE, nb=1 << 40, z=None: (
+        C.byref(L), FAKE, T, FAKE, FAKE, FAKE, z, dx, FAKE, FAKE, dsgu, FAKE, FAKE, None, ws, nb, None)
     need = lib.moe_backward_workspace_bytes(C.byref(L), 64)
     assert need > lib.moe_workspace_bytes(C.byref(L), 64, 512)
     assert lib.moe_backward(*args(nb=need - 1)) == B.MOE_EWORKSPACE
     assert lib.moe_backward(*args(dx=None)) == B.MOE_EINVAL
     assert lib.moe_backward(*args(dx=FAKE + 4)) == B.MOE_EINVAL and b"aligned" in lib.moe_last_error()
+    assert lib.moe_backward(*args(z=FAKE + 8)) == B.MOE_EINVAL and b"aligned" in lib.moe_last_error()
     assert lib.moe_backward(*args(dsgu=None)) == B.MOE_EINVAL and b"shared" in lib.moe_last_error()
     assert lib.moe_backward(*args(T=0, ws=None, nb=0)) == B.MOE_OK        # no-op
     L = layer(dtype=B.MOE_FP8_E4M3FN)
@@ -152,3 +153,18 @@ def test_backward_refusals_without_gpu():
     L = layer(dtype=B.MOE_BF16, k=0)
     assert lib.moe_backward(*args()) == B.MOE_EINVAL
     assert lib.moe_backward_workspace_bytes(C.byref(L), 64) == 0
+
+
+def test_forward_train_refusals_without_gpu():
+    """moe_forward_train: bf16 experts, ids/gates/z_saved required; the saved
+    pre-activation buffer holds T*k*2I + T*2Is floats."""
+    lib = B.lib()
+    L = layer(dtype=B.MOE_BF16)
+    assert lib.moe_saved_z_floats(C.byref(L), 64) == 64 * 8 * 2 * 1536 + 64 * 2 * 1536
+    call = lambda ids=FAKE, z=FAKE: lib.moe_forward_train(C.byref(L), FAKE, 64, FAKE, B.MOE_BF16, ids, FAKE, z,
+                                                         FAKE, 1 << 40, None)
+    assert call(z=None) == B.MOE_EINVAL
+    assert call(ids=None) == B.MOE_EINVAL
+    assert call(z=FAKE + 4) == B.MOE_EINVAL and b"aligned" in lib.moe_last_error()
+    L = layer(dtype=B.MOE_FP8_E4M3FN)
+    assert call() == B.MOE_EUNSUPPORTED

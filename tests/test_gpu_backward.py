@@ -54,15 +54,29 @@ def _outputs(cfg, T, device):
                 dw_router=f(cfg.E, cfg.H), dbias=f(cfg.E))
 
 
-def run_backward(lt, x, dy, ids, gates, ws=None):
+def run_backward(lt, x, dy, ids, gates, ws=None, z_saved=None):
     cfg = lt.cfg
     layer = B.Layer.from_tensors(lt)
     T = x.shape[0]
     out = _outputs(cfg, T, x.device)
     ws = B.backward_workspace(layer, T, x.device) if ws is None else ws
-    B.moe_backward(layer, x, T, ids, gates, dy, ws=ws, **out)
+    B.moe_backward(layer, x, T, ids, gates, dy, z_saved=z_saved, ws=ws, **out)
     torch.cuda.synchronize()
     return out
+
+
+def run_forward_train(lt, x):
+    """moe_forward_train -> (y f32, ids, gates, z_saved)."""
+    cfg = lt.cfg
+    layer = B.Layer.from_tensors(lt)
+    T = x.shape[0]
+    y = torch.empty((T, cfg.H), dtype=torch.float32, device=x.device)
+    ids = torch.empty((T, cfg.k), dtype=torch.int32, device=x.device)
+    gates = torch.empty((T, cfg.k), dtype=torch.float32, device=x.device)
+    z = torch.full((B.moe_saved_z_floats(layer, T),), float("nan"), dtype=torch.float32, device=x.device)
+    B.moe_forward_train(layer, x, T, y, ids, gates, z, ws=B.workspace(layer, T, T * cfg.k, x.device))
+    torch.cuda.synchronize()
+    return y, ids, gates, z
 
 
 def _np(t):
@@ -73,12 +87,16 @@ def _cfg(base, **kw):
     return dataclasses.replace(W.get_config(base), **kw)
 
 
-def check_small(cfg):
+def check_small(cfg, saved=False):
     lt = W.make_layer(cfg, dev())
     x = W.make_x(cfg, dev())
     dy = W.make_dy(cfg, dev())
-    _, ids, gates = run_forward(lt, x)
-    out = {k: _np(v) for k, v in run_backward(lt, x, dy, ids, gates).items()}
+    y, ids, gates = run_forward(lt, x)
+    z = None
+    if saved:   # the training forward: same outputs, plus the pre-activations
+        y2, ids2, gates2, z = run_forward_train(lt, x)
+        assert torch.equal(y, y2) and torch.equal(ids, ids2) and torch.equal(gates, gates2)
+    out = {k: _np(v) for k, v in run_backward(lt, x, dy, ids, gates, z_saved=z).items()}
     OL = oracle_layer(lt)
     ref = oracle.backward(OL, W.bf16_bits(x), ids.cpu().numpy(), W.bf16_bits(dy))
     errs = {}
@@ -93,7 +111,8 @@ def check_small(cfg):
     if cfg.Is:
         errs["dw_shared_gate_up"] = _rel(out["dw_shared_gate_up"], ref["dw_shared_gate_up"])
         errs["dw_shared_down"] = _rel(out["dw_shared_down"], ref["dw_shared_down"])
-    _print(cfg.name, "T", cfg.T, "unused experts", int((~used).sum()), {k: f"{v:.2e}" for k, v in errs.items()})
+    _print(cfg.name, "saved z" if saved else "recomputed z", "T", cfg.T, "unused experts", int((~used).sum()),
+           {k: f"{v:.2e}" for k, v in errs.items()})
     for k, v in errs.items():
         assert v < TOL, (k, v)
     if cfg.k == 1:   # one chosen logit: the gate is 1 and the router gets no gradient
@@ -101,19 +120,28 @@ def check_small(cfg):
     return out
 
 
-def test_backward_small_full_parity():
-    check_small(W.get_config("small_bf16"))
+@pytest.mark.parametrize("saved", [False, True])
+def test_backward_small_full_parity(saved):
+    check_small(W.get_config("small_bf16"), saved)
 
 
-def test_backward_ragged_tiles_bias_and_unused_experts():
+@pytest.mark.parametrize("saved", [False, True])
+def test_backward_ragged_tiles_bias_and_unused_experts(saved):
     # H = 3 x 128, I = 2.5 column tiles, 200 tokens, Zipf-biased router (bias
     # gradient checked), 40 experts of which several get no token
     check_small(_cfg("small_bf16", name="bwd_ragged", T=200, H=384, E=40, k=3, I=320, Is=128,
-                             zipf_s=1.1, zipf_beta=0.6, router_std=1.0 / np.sqrt(384)))
+                     zipf_s=1.1, zipf_beta=0.6, router_std=1.0 / np.sqrt(384)), saved)
 
 
-def test_backward_k1_no_shared_expert_single_token_tiles():
-    check_small(_cfg("small_bf16", name="bwd_k1", T=37, E=64, k=1, Is=0))
+@pytest.mark.parametrize("saved", [False, True])
+def test_backward_k1_no_shared_expert_single_token_tiles(saved):
+    check_small(_cfg("small_bf16", name="bwd_k1", T=37, E=64, k=1, Is=0), saved)
+
+
+def test_forward_train_tiled_path_saves_pre_activations():
+    # 2048 tokens over 16 experts: the training forward takes the LDS-tiled
+    # expert kernels (rows read through the sort permutation)
+    check_small(_cfg("small_bf16", name="bwd_tiled", T=2048, E=16, k=2, I=256, Is=128), True)
 
 
 def test_backward_deterministic_and_zero_tokens():
@@ -137,16 +165,23 @@ def test_backward_deterministic_and_zero_tokens():
     assert torch.isnan(out["dx"]).all()
 
 
-def test_backward_training_workload_sampled():
-    """The training workload at full size: dx of sampled tokens, weight
-    gradients of the least and most loaded experts, softmax identities."""
+@pytest.mark.parametrize("saved", [True, False])
+def test_backward_training_workload_sampled(saved):
+    """The training workload at full size (moe_forward_train then moe_backward
+    with the saved pre-activations, the benchmark's step; and with the
+    recompute): dx of sampled tokens, weight gradients of the least and most
+    loaded experts, softmax identities."""
     cfg = W.get_config("train_bf16")
-    _print("case", cfg.name, "T", cfg.T)
+    _print("case", cfg.name, "T", cfg.T, "saved z" if saved else "recomputed z")
     lt = W.make_layer(cfg, dev())
     x = W.make_x(cfg, dev())
     dy = W.make_dy(cfg, dev())
-    _, ids, gates = run_forward(lt, x)
-    out = run_backward(lt, x, dy, ids, gates)
+    if saved:
+        _, ids, gates, z = run_forward_train(lt, x)
+    else:
+        (_, ids, gates), z = run_forward(lt, x), None
+    out = run_backward(lt, x, dy, ids, gates, z_saved=z)
+    del z
     for k, v in out.items():
         if v is not None:
             assert not torch.isnan(v).any(), k
