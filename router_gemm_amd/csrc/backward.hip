@@ -298,25 +298,44 @@ __device__ __forceinline__ float row_gate(const float *gates, const int32_t *per
   return gates ? gates[perm_src[p]] : 1.0f;
 }
 
-// One wave per row p: h = silu(z_gate) * z_up; hg[p] = g h (bf16, the down
-// layer's input as seen by dW_down); dg[p] = <u[p], h> with u = dy W_down, so
-// that dg is the gate's gradient <dy, FFN(x)> (lane partial sums, then the
-// wave tree: a fixed order).
-__global__ __launch_bounds__(256) void bwd_h_dg_kernel(const float *__restrict__ z, const float *__restrict__ u,
-                                                       const float *__restrict__ gates,
-                                                       const int32_t *__restrict__ perm_src,
-                                                       const int32_t *__restrict__ kept, int64_t N, int I,
-                                                       uint16_t *__restrict__ hg, float *__restrict__ dg) {
+// One wave per row p, 4 consecutive columns per lane at a time (I % 4 == 0):
+//   h = silu(z_gate) z_up;  hg[p] = g h (bf16, the down layer's input as seen
+//   by dW_down);  dg[p] = <u[p], h> with u = dy W_down, so that dg is the
+//   gate's gradient <dy, FFN(x)> (lane partial sums, then the wave tree: a
+//   fixed order);  with dh = g u, the SwiGLU backward
+//   dz_up = dh silu(z_gate),  dz_gate = dh z_up sigma(z_gate) (1 + z_gate (1 - sigma(z_gate))),
+//   stored bf16 as [gate half | up half], the layout of z.
+__global__ __launch_bounds__(256) void bwd_swiglu_kernel(const float *__restrict__ z, const float *__restrict__ u,
+                                                         const float *__restrict__ gates,
+                                                         const int32_t *__restrict__ perm_src,
+                                                         const int32_t *__restrict__ kept, int64_t N, int I,
+                                                         uint16_t *__restrict__ hg, uint16_t *__restrict__ dz,
+                                                         float *__restrict__ dg) {
   const int64_t p = (int64_t)blockIdx.x * 4 + wave_id();
   if (p >= (kept ? *kept : N)) return;
   const int lane = lane_id();
   const float g = row_gate(gates, perm_src, p);
   const float *zr = z + p * 2 * I, *ur = u + p * I;
+  uint16_t *hr = hg + p * I, *dr = dz + p * 2 * I;
   float acc = 0.f;
-  for (int i = lane; i < I; i += kWave) {
-    const float hv = swiglu(zr[i], zr[I + i]);
-    hg[p * I + i] = (uint16_t)f32_to_bf16(g * hv);
-    acc = __builtin_fmaf(ur[i], hv, acc);
+  for (int i = 4 * lane; i < I; i += 4 * kWave) {
+    const f32x4 zg = *reinterpret_cast<const f32x4 *>(zr + i);
+    const f32x4 zu = *reinterpret_cast<const f32x4 *>(zr + I + i);
+    const f32x4 uu = *reinterpret_cast<const f32x4 *>(ur + i);
+    uint32_t h16[4], g16[4], u16[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-zg[q]));
+      const float hv = zg[q] * sg * zu[q];
+      const float dh = g * uu[q];
+      acc = __builtin_fmaf(uu[q], hv, acc);
+      h16[q] = f32_to_bf16(g * hv);
+      u16[q] = f32_to_bf16(dh * zg[q] * sg);
+      g16[q] = f32_to_bf16(dh * zu[q] * sg * (1.0f + zg[q] * (1.0f - sg)));
+    }
+    *reinterpret_cast<uint2 *>(hr + i) = make_uint2(h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16));
+    *reinterpret_cast<uint2 *>(dr + i) = make_uint2(g16[0] | (g16[1] << 16), g16[2] | (g16[3] << 16));
+    *reinterpret_cast<uint2 *>(dr + I + i) = make_uint2(u16[0] | (u16[1] << 16), u16[2] | (u16[3] << 16));
   }
   acc = wave_sum(acc);
   if (dg && lane == 0) dg[p] = acc;
@@ -339,41 +358,27 @@ __global__ void bwd_dl_kernel(const float *__restrict__ dg, const float *__restr
   }
 }
 
-// One block per row p: with dh = g u, the SwiGLU backward
-//   dz_up = dh silu(z_gate),  dz_gate = dh z_up sigma(z_gate) (1 + z_gate (1 - sigma(z_gate)))
-// stored bf16 as [gate half | up half], the layout of z.
-__global__ __launch_bounds__(256) void bwd_dz_kernel(const float *__restrict__ z, const float *__restrict__ u,
-                                                     const float *__restrict__ gates,
-                                                     const int32_t *__restrict__ perm_src,
-                                                     const int32_t *__restrict__ kept, int64_t N, int I,
-                                                     uint16_t *__restrict__ dz) {
-  const int64_t p = blockIdx.x;
-  if (p >= (kept ? *kept : N)) return;
-  const float g = row_gate(gates, perm_src, p);
-  const float *zr = z + p * 2 * I, *ur = u + p * I;
-  uint16_t *dr = dz + p * 2 * I;
-  for (int i = threadIdx.x; i < I; i += blockDim.x) {
-    const float zg = zr[i], zu = zr[I + i];
-    const float dh = g * ur[i];
-    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-zg));
-    dr[I + i] = (uint16_t)f32_to_bf16(dh * zg * sg);
-    dr[i] = (uint16_t)f32_to_bf16(dh * zu * sg * (1.0f + zg * (1.0f - sg)));
-  }
-}
-
 // Router weight gradient: dW_r[e][h] = sum over e's rows p (in order) of
-// dl[p] x_perm[p][h]; dbias[e] = sum of dl[p].  Grid (E, ceil(H / 256)).
+// dl[p] x_perm[p][h], 8 consecutive h per thread (H % 8 == 0); dbias[e] =
+// sum of dl[p].  Grid (E, ceil(H / 2048)).
 __global__ __launch_bounds__(256) void bwd_router_w_kernel(const float *__restrict__ dl,
                                                            const uint16_t *__restrict__ x_perm,
                                                            const int32_t *__restrict__ off, int H,
                                                            float *__restrict__ dwr, float *__restrict__ dbias) {
   const int e = blockIdx.x;
-  const int h = blockIdx.y * 256 + threadIdx.x;
+  const int h = (blockIdx.y * 256 + threadIdx.x) * 8;
   const int p0 = off[e], p1 = off[e + 1];
   if (h < H) {
-    float acc = 0.f;
-    for (int p = p0; p < p1; ++p) acc = __builtin_fmaf(dl[p], bf16_to_f32(x_perm[(int64_t)p * H + h]), acc);
-    dwr[(int64_t)e * H + h] = acc;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int p = p0; p < p1; ++p) {
+      const float d = dl[p];
+      const i32x4 v = load16(x_perm + (int64_t)p * H + h);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(d, bf16_to_f32(((uint32_t)v[q >> 1] >> (16 * (q & 1))) & 0xFFFFu), acc[q]);
+    }
+    float *o = dwr + (int64_t)e * H + h;
+    *reinterpret_cast<f32x4 *>(o) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4 *>(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
   }
   if (dbias && blockIdx.y == 0 && threadIdx.x == 0) {
     float s = 0.f;
@@ -383,7 +388,8 @@ __global__ __launch_bounds__(256) void bwd_router_w_kernel(const float *__restri
 }
 
 // dx[t] = dx_shared[t] + sum_j dx_rows[row of (t, j)] + sum_j dl_j W_r[e_j],
-// fp32, in that order (slots in increasing j).  Grid (T, ceil(H / 256)).
+// fp32, in that order (slots in increasing j); 4 consecutive h per thread
+// (H % 4 == 0).  Grid (T, ceil(H / 1024)).
 __global__ __launch_bounds__(256) void bwd_dx_kernel(const float *__restrict__ dx_shared,
                                                      const float *__restrict__ dx_rows,
                                                      const int32_t *__restrict__ perm_pos,
@@ -391,18 +397,29 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float *__restrict__ d
                                                      const uint16_t *__restrict__ wr, int k, int H,
                                                      float *__restrict__ dx) {
   const int64_t t = blockIdx.x;
-  const int h = blockIdx.y * 256 + threadIdx.x;
+  const int h = (blockIdx.y * 256 + threadIdx.x) * 4;
   if (h >= H) return;
-  float acc = dx_shared ? dx_shared[t * H + h] : 0.f;
+  f32x4 acc = dx_shared ? *reinterpret_cast<const f32x4 *>(dx_shared + t * H + h) : f32x4{0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < k; ++j) {
     const int32_t p = perm_pos[t * k + j];
-    if (p >= 0) acc += dx_rows[(int64_t)p * H + h];
+    if (p >= 0) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(dx_rows + (int64_t)p * H + h);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] += v[q];
+    }
   }
   for (int j = 0; j < k; ++j) {
     const int32_t p = perm_pos[t * k + j];
-    if (p >= 0) acc = __builtin_fmaf(dl[p], bf16_to_f32(wr[(int64_t)ids[t * k + j] * H + h]), acc);
+    if (p >= 0) {
+      const float d = dl[p];
+      const uint2 w = *reinterpret_cast<const uint2 *>(wr + (int64_t)ids[t * k + j] * H + h);
+      acc[0] = __builtin_fmaf(d, bf16_to_f32(w.x & 0xFFFFu), acc[0]);
+      acc[1] = __builtin_fmaf(d, bf16_to_f32(w.x >> 16), acc[1]);
+      acc[2] = __builtin_fmaf(d, bf16_to_f32(w.y & 0xFFFFu), acc[2]);
+      acc[3] = __builtin_fmaf(d, bf16_to_f32(w.y >> 16), acc[3]);
+    }
   }
-  dx[t * H + h] = acc;
+  *reinterpret_cast<f32x4 *>(dx + t * H + h) = acc;
 }
 
 // ---------------------------------------------------------------- host side
@@ -499,9 +516,9 @@ hipError_t launch_expert_backward(const BwdExpert &X, hipStream_t st) {
     if (e != hipSuccess) return e;
     // rows past off[G] (assignments the sort dropped) belong to no expert
     const int32_t *kept = X.off ? X.off + G : nullptr;
-    bwd_h_dg_kernel<<<(unsigned)cdiv(N, 4), 256, 0, st>>>(X.z, X.u, X.gates, X.perm_src, kept, N, I, X.hg, X.dg);
+    bwd_swiglu_kernel<<<(unsigned)cdiv(N, 4), 256, 0, st>>>(X.z, X.u, X.gates, X.perm_src, kept, N, I, X.hg, X.dz,
+                                                            X.dg);
     if (X.dl) bwd_dl_kernel<<<(unsigned)cdiv(X.T, 256), 256, 0, st>>>(X.dg, X.gates, X.perm_pos, X.T, X.k, X.dl);
-    bwd_dz_kernel<<<(unsigned)N, 256, 0, st>>>(X.z, X.u, X.gates, X.perm_src, kept, N, I, X.dz);
     // dx rows = dz W_gu: B(n = h, k = j) = W_gu[g][j][h]
     e = gemm_rows(GemmOp{X.dz, 0, 2 * I, 1}, GemmOp{X.wgu, (int64_t)2 * I * H, 1, H}, X.dx_rows, H, X.off, G, N, H,
                   2 * I, X.tiles, bm, mt, st);
@@ -517,7 +534,7 @@ hipError_t launch_expert_backward(const BwdExpert &X, hipStream_t st) {
 
 hipError_t launch_router_backward(const float *dl, const uint16_t *x_perm, const int32_t *off, int E, int H,
                                   float *dwr, float *dbias, hipStream_t st) {
-  bwd_router_w_kernel<<<dim3((unsigned)E, (unsigned)cdiv(H, 256)), 256, 0, st>>>(dl, x_perm, off, H, dwr, dbias);
+  bwd_router_w_kernel<<<dim3((unsigned)E, (unsigned)cdiv(H, 2048)), 256, 0, st>>>(dl, x_perm, off, H, dwr, dbias);
   return hipGetLastError();
 }
 
@@ -525,7 +542,7 @@ hipError_t launch_dx_backward(const float *dx_shared, const float *dx_rows, cons
                               const int32_t *ids, const float *dl, const uint16_t *wr, int64_t T, int k, int H,
                               float *dx, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  bwd_dx_kernel<<<dim3((unsigned)T, (unsigned)cdiv(H, 256)), 256, 0, st>>>(dx_shared, dx_rows, perm_pos, ids, dl, wr,
+  bwd_dx_kernel<<<dim3((unsigned)T, (unsigned)cdiv(H, 1024)), 256, 0, st>>>(dx_shared, dx_rows, perm_pos, ids, dl, wr,
                                                                           k, H, dx);
   return hipGetLastError();
 }
