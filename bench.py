@@ -364,18 +364,42 @@ def bench_train(args, cfg, lt, x, dev):
     g_launch = {nm: max(n // K, 1) for nm, (ms, n) in gemm.items()}
     gemm_ms = sum(g_ms.values())
     peak = PEAK_TFLOPS["bf16"]
-    achieved = (dgrad_flops + wgrad_flops) / (gemm_ms / 1e3) / 1e12
-    roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": None,
-            "traffic_note": "no counters taken on these kernel sources",
-            "library_source_hash": library_source_hash(),
-            "kernel": "grouped bf16 GEMM of the backward (all its launches in a step: dgrad, wgrad)",
-            "kernel_ms_per_step": round(gemm_ms, 4),
-            "launches_per_step": sum(g_launch.values()),
-            "algorithmic_flops_per_step": dgrad_flops + wgrad_flops,
-            "per_site": {nm: {"ms_per_step": round(g_ms[nm], 4), "launches_per_step": g_launch[nm],
-                              "tflops": round(f / (g_ms[nm] / 1e3) / 1e12, 1) if g_ms[nm] > 0 else None}
-                         for nm, f in (("bwd_dgrad_gemm", dgrad_flops), ("bwd_wgrad_gemm", wgrad_flops))}}
+    # The dominant kernel is the weight-gradient GEMM (its site's launches: routed dW_down and
+    # dW_gate_up, the shared expert's two).  At ~186 rows per expert it does ~90 flops per byte
+    # it must move (the fp32 gradients it writes), below the MI355X ridge of 312: HBM-bound.
+    # Algorithmic bytes per step: the gradients written (fp32) + each operand row read once.
+    wgrad_bytes = (4 * 3 * I * H * E + 4 * 3 * Is * H) \
+        + N * (H + I) * 2 + N * (2 * I + H) * 2 \
+        + (T * (H + Is) * 2 + T * (2 * Is + H) * 2 if Is else 0)
+    w_ms = g_ms["bwd_wgrad_gemm"]
+    w_achieved = wgrad_bytes / (w_ms / 1e3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(w_achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(w_achieved / PEAK_HBM_GBS, 4)}
+    tr = TRAFFIC.get(cfg.name)
+    src_hash = library_source_hash()
+    if tr and tr["src_hash"] == src_hash:
+        roof["traffic"] = int((tr["fetch_kib"] * tr["fetch_scale"] + tr["write_kib"] * tr["write_scale"]) * 1024)
+        roof["traffic_per"] = "step (the site's launches)"
+    else:
+        roof["traffic"] = None
+        roof["traffic_note"] = ("no counters taken on these kernel sources" if not tr
+                                else "kernel sources changed since the counters were taken")
+    roof.update({
+        "library_source_hash": src_hash,
+        "kernel": "weight-gradient grouped bf16 GEMM (dW_gate_up, dW_down; routed and shared)",
+        "kernel_ms_per_step": round(w_ms, 4),
+        "launches_per_step": g_launch["bwd_wgrad_gemm"],
+        "avg_launch_us": round(1e3 * w_ms / g_launch["bwd_wgrad_gemm"], 2),
+        "algorithmic_bytes_per_step": int(wgrad_bytes),
+        "algorithmic_flops_per_step": wgrad_flops,
+        "tflops": round(wgrad_flops / (w_ms / 1e3) / 1e12, 1)})
+    gemms = {"bound": "mfma", "unit": "TFLOP/s", "peak": peak,
+             "all_launches_tflops": round((dgrad_flops + wgrad_flops) / (gemm_ms / 1e3) / 1e12, 1),
+             "all_launches_frac": round((dgrad_flops + wgrad_flops) / (gemm_ms / 1e3) / 1e12 / peak, 4),
+             "ms_per_step": round(gemm_ms, 4),
+             "per_site": {nm: {"ms_per_step": round(g_ms[nm], 4), "launches_per_step": g_launch[nm],
+                               "tflops": round(f / (g_ms[nm] / 1e3) / 1e12, 1) if g_ms[nm] > 0 else None}
+                          for nm, f in (("bwd_dgrad_gemm", dgrad_flops), ("bwd_wgrad_gemm", wgrad_flops))}}
 
     # per-kernel breakdown: a separate pass with every launch site timed
     sites = {0: "router_logits", 1: "router_topk", 2: "sort", 3: "gather", 4: "gate_up", 5: "down", 8: "combine",
@@ -402,6 +426,7 @@ def bench_train(args, cfg, lt, x, dev):
         "layer": {"model_tflops": round(model_flops / t_s / 1e12, 2), "mfma_util": round(model_flops / t_s / 1e12 / peak, 4),
                   "model_flops_per_step": model_flops, "wall_s": round(wall, 4)},
         "roofline": roof,
+        "backward_gemms": gemms,
         "breakdown_us_per_step": breakdown,
         "cpu_baseline": None,
     }
