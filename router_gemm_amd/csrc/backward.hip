@@ -7,15 +7,17 @@
 // expert, SwiGLU experts; "Full-Depth H100 Benchmark": the layer is trained
 // in BF16).
 //
-// Every GEMM of the backward is one grouped bf16 kernel, C_g = A_g B_g^T
-// over K, whose operands are each stored either K-contiguous ("N" layout:
-// element (r, k) at r*rs + k) or row-contiguous ("T" layout: at k*ks + r).
-// Groups are experts: either they own token rows (the M dimension: forward
-// recompute and data gradients) or a token range (the K dimension: weight
-// gradients).  128x128 output tiles, 64-wide K steps staged in LDS through
-// registers (the next step's global loads are in flight during the current
-// step's MFMAs), T-layout operands transposed on the way into LDS, fp32
-// accumulation and output.
+// The backward's GEMMs are grouped bf16 GEMMs C_g = A_g B_g^T over K in two
+// kernels.  grouped_gemm_kernel: groups (experts) own token rows (the data
+// gradients dy W_down and dz W_gate_up, and the recompute of the
+// pre-activations when the forward did not keep them); the token rows are
+// K-contiguous, the expert's weights are read along either axis of their
+// stored [out, in] layout ("N" layout: element (r, k) at r*rs + k; "T"
+// layout: at k*ks + r, transposed on its way into LDS).  Tiles are staged
+// through registers into two LDS stages.  wgrad_kernel: groups own a token
+// range (the weight gradients, sums over an expert's rows), both operands
+// row-contiguous; copied into LDS as stored and read with gfx950's
+// transposing LDS reads.  fp32 accumulation and output throughout.
 
 #include <algorithm>
 
@@ -142,49 +144,28 @@ __device__ __forceinline__ void tile_store(uint16_t *s, const i32x4 (&raw)[8 * R
 // launches whose groups hold up to 256 rows, so that each group's weight
 // columns are streamed from HBM once rather than once per 128-row tile, and
 // each token row staged serves 128 weight columns.
-// NB = 2: two LDS stages (one barrier per K step); NB = 1: one stage and half
-// the LDS (two barriers per K step, more workgroups per CU: for the short
-// token ranges of the weight gradients).
+// Two LDS stages, one barrier per K step.
 template <int BM, int BN>
 constexpr int gemm_threads() { return 64 * (BM / 64) * (BN / 64); }
 
-template <int BM, int BN, int NB, bool AT, bool BTL>
+template <int BM, int BN, bool BTL>
 __global__ __launch_bounds__((64 * (BM / 64) * (BN / 64))) void grouped_gemm_kernel(GemmArgs a) {
+  constexpr int NB = 2;
+  constexpr bool AT = false;
   constexpr int NT = gemm_threads<BM, BN>();
   constexpr int WMW = BM / 64;  // waves along M
-  // Staged operand tiles; K-grouped launches (weight gradients, both
-  // operands T-layout) reuse the space to stage half the output tile at a
-  // time, 64 rows of BN + 4 floats.
-  constexpr bool kStagedOut = AT && BTL;
-  constexpr int kOperandBytes = NB * (BM + BN) * BK * 2;
-  constexpr int kOutBytes = kStagedOut ? 64 * (BN + 4) * 4 : 0;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kOperandBytes > kOutBytes ? kOperandBytes : kOutBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NB * (BM + BN) * BK * 2];
   uint16_t(*sa)[BM * BK] = reinterpret_cast<uint16_t(*)[BM * BK]>(smem);
   uint16_t(*sb)[BN * BK] = reinterpret_cast<uint16_t(*)[BN * BK]>(smem + NB * BM * BK * 2);
   const int bid = blockIdx.x;
-  const bool kseg = a.tiles == nullptr;
-  int g, m0, mend, n0, kbeg, kend;
-  if (kseg) {
-    const int per = a.ntm * a.ntn;
-    g = bid / per;
-    const int r = bid - g * per;
-    m0 = (r / a.ntn) * BM;
-    n0 = (r % a.ntn) * BN;
-    mend = a.M;
-    kbeg = a.off ? a.off[g] : 0;
-    kend = a.off ? a.off[g + 1] : a.K;
-  } else {
-    const int tile = bid / a.ntn;
-    if (tile >= a.hdr[0]) return;
-    n0 = (bid - tile * a.ntn) * BN;
-    const TileEntry te = a.tiles[tile];
-    g = te.ge & 0xFFFFFF;
-    const int rb = a.off ? a.off[g] : 0;
-    m0 = rb + te.m0;
-    mend = a.off ? a.off[g + 1] : a.M;
-    kbeg = 0;
-    kend = a.K;
-  }
+  const int tile = bid / a.ntn;
+  if (tile >= a.hdr[0]) return;
+  const int n0 = (bid - tile * a.ntn) * BN;
+  const TileEntry te = a.tiles[tile];
+  const int g = te.ge & 0xFFFFFF;
+  const int m0 = (a.off ? a.off[g] : 0) + te.m0;
+  const int mend = a.off ? a.off[g + 1] : a.M;
+  const int kbeg = 0, kend = a.K;
   // Row-grouped: A rows are global rows (gstride 0) and B is the group's
   // weight; K-grouped: both operands are indexed by the global K (token)
   // index and only the output is per group.
@@ -213,7 +194,7 @@ __global__ __launch_bounds__((64 * (BM / 64) * (BN / 64))) void grouped_gemm_ker
     __syncthreads();
   }
   for (int s = 0; s < nsteps; ++s) {
-    const int buf = NB == 2 ? (s & 1) : 0;
+    const int buf = s & 1;
     const bool more = s + 1 < nsteps;
     if (more) {
       const int k1 = kbeg + (s + 1) * BK;
@@ -237,46 +218,16 @@ __global__ __launch_bounds__((64 * (BM / 64) * (BN / 64))) void grouped_gemm_ker
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(fb[j], fa[i], acc[i][j]);
     }
-    if (NB == 1) __syncthreads();   // every wave is done with the stage before it is refilled
     if (more) {
-      tile_store<AT, BM, NT>(sa[NB == 2 ? buf ^ 1 : 0], va, ma);
-      tile_store<BTL, BN, NT>(sb[NB == 2 ? buf ^ 1 : 0], vb, mb);
+      tile_store<AT, BM, NT>(sa[buf ^ 1], va, ma);
+      tile_store<BTL, BN, NT>(sb[buf ^ 1], vb, mb);
     }
     __syncthreads();
   }
-  // lane holds C[lane % 16][4 (lane / 16) + r] of each 16 x 16 block
+  // lane holds C[lane % 16][4 (lane / 16) + r] of each 16 x 16 block: one
+  // 16-byte store per block (N is a multiple of 8)
   float *cbase = a.c + (int64_t)g * a.cgstride;
-  if constexpr (kStagedOut) {
-    // Weight gradients: each half of the tile (64 rows, the rows of two
-    // waves) goes through LDS so that every store instruction writes whole
-    // 512-byte rows; non-temporal, as nothing here reads them back.  The last
-    // barrier of the main loop has released the operand tiles.
-    constexpr int LDW = BN + 4;
-    float *stage = reinterpret_cast<float *>(smem);
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if ((w & 1) == half) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<f32x4 *>(stage + (16 * i + (lane & 15)) * LDW + wn + 16 * j + 4 * (lane >> 4)) =
-                acc[i][j];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int q = tid; q < 64 * BN / 4; q += NT) {
-        const int row = q / (BN / 4), c4 = q % (BN / 4);
-        const int m = m0 + 64 * half + row, n = n0 + 4 * c4;
-        if (m < mend && n < a.N)
-          __builtin_nontemporal_store(*reinterpret_cast<const f32x4 *>(stage + row * LDW + 4 * c4),
-                                      reinterpret_cast<f32x4 *>(cbase + (int64_t)m * a.ldc + n));
-      }
-      __syncthreads();
-    }
-  } else {
-    // one 16-byte store per block (N is a multiple of 8)
+  {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = m0 + wm + 16 * i + (lane & 15);
@@ -288,6 +239,179 @@ __global__ __launch_bounds__((64 * (BM / 64) * (BN / 64))) void grouped_gemm_ker
         if (n < a.N) *reinterpret_cast<f32x4 *>(crow + n) = acc[i][j];
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------- weight-gradient GEMM
+
+// C_g [M, N] = sum over p in group g's token range of A[p][m] B[p][n]: both
+// operands are row-contiguous in m / n ("T" layout), the K (token) range is
+// short (an expert's rows).  The tiles go into LDS as stored -- [k][m] rows of
+// 128 bf16 -- by direct-to-LDS copies (a three-stage ring of 32-k steps, two
+// steps in flight), and the MFMA fragments (8 consecutive k of one m per
+// lane) come out of them with gfx950's transposing LDS read,
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element i of
+// the 4 x 16 block of 16-bit values whose rows the 16 lanes address (lane j
+// reads 4 consecutive m of row j / 4), i.e. 4 consecutive k of one m.  Two
+// such reads make one 16x16x32 operand.  128 x 128 output tiles, 4 waves of
+// 64 x 64, fp32 accumulation; the output goes out through LDS in whole
+// 512-byte rows, non-temporally.
+namespace {
+constexpr int WBK = 32;                  // K step
+constexpr int WROW = 256;                // bytes of one staged k row (128 bf16)
+constexpr int WTILE = WBK * WROW;        // 8 KB: one operand's tile of one step
+constexpr int WSTAGE = 2 * WTILE;        // A then B
+constexpr int WNSTAGE = 3;
+
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+
+// 32-byte segment permutation of staged k row r: segment s is stored at
+// s ^ wseg(r).  Over the 16 rows one transposing read touches (r = 8g + 4h +
+// t, g = 0..3, t = 0..3) it takes 8 values twice each, so the 64 lanes'
+// 8-byte pieces spread over all banks.
+__device__ __forceinline__ int wseg(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
+
+// Eight transposing reads (addresses a[0..7], byte offsets in LDS), waited for
+// inside the block.
+__device__ __forceinline__ void lds_read_tr8(const uint32_t (&a)[8], i32x2 (&r)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]));
+}
+}  // namespace
+
+__global__ __launch_bounds__(256) void wgrad_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[WNSTAGE * WSTAGE];
+  const int per = a.ntm * a.ntn;
+  const int g = blockIdx.x / per;
+  const int rt = blockIdx.x - g * per;
+  const int m0 = (rt / a.ntn) * 128, n0 = (rt % a.ntn) * 128;
+  const int kbeg = a.off ? a.off[g] : 0, kend = a.off ? a.off[g + 1] : a.K;
+  const int nsteps = (int)cdiv(kend - kbeg, WBK);
+  const int lane = lane_id(), w = wave_id();
+  const int wm = (w & 1) * 64, wn = (w >> 1) * 64;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)smem;
+
+  // Copies: operand tile rows 4q .. 4q+3 per instruction (q = w, w + 4), lane
+  // l -> row 4q + l / 16, 16-byte slot l % 16 of the row, which holds logical
+  // m = 16 (slot / 2 ^ wseg(row)) + 8 (slot % 2) (clamped inside the operand).
+  const int crow = lane >> 4;                       // + 4q
+  const int cm = 16 * (((lane & 15) >> 1) ^ wseg(4 * w + crow)) + 8 * (lane & 1);
+  const int am = min(m0 + cm, a.M - 8), bn = min(n0 + cm, a.N - 8);
+  auto issue = [&](int step) {
+    const int k0 = kbeg + step * WBK;
+    uint8_t *st = smem + (step % WNSTAGE) * WSTAGE;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int q = w + 4 * t;
+      const int64_t p = min(k0 + 4 * q + crow, kend - 1);
+      dma16(a.a.base + p * a.a.ks + am, st + q * 1024);
+      dma16(a.b.base + p * a.b.ks + bn, st + WTILE + q * 1024);
+    }
+  };
+  // Transposing reads: lane (g4 = lane / 16, j = lane % 16) reads k row
+  // 8 g4 + 4 h + j / 4 (h = half of its 8 k), 4 bf16 at m = mb + 4 (j % 4).
+  uint32_t ra[8], rb[8];   // per-stage-relative addresses: [2 i + h], [2 j + h]
+  {
+    const int g4 = lane >> 4, jj = lane & 15;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 8 * g4 + 4 * h + (jj >> 2);
+      const uint32_t rowb = (uint32_t)(r * WROW + 8 * (jj & 3));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ra[2 * i + h] = rowb + 32 * (((wm >> 4) + i) ^ wseg(r));
+        rb[2 * i + h] = WTILE + rowb + 32 * (((wn >> 4) + i) ^ wseg(r));
+      }
+    }
+  }
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (nsteps > 0) issue(0);
+  if (nsteps > 1) issue(1);
+  for (int s = 0; s < nsteps; ++s) {
+    // this wave's copies of step s have landed when at most those of step
+    // s + 1 (4 instructions) are still in flight; the barrier makes every
+    // wave's copies visible and frees the stage of step s - 1 for step s + 2
+    if (s + 1 < nsteps)
+      wait_vm<4>();
+    else
+      wait_vm<0>();
+    wg_barrier();
+    if (s + 2 < nsteps) issue(s + 2);
+    const uint32_t sb = lds0 + (uint32_t)((s % WNSTAGE) * WSTAGE);
+    uint32_t aa[8], ab[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      aa[q] = sb + ra[q];
+      ab[q] = sb + rb[q];
+    }
+    i32x2 fa2[8], fb2[8];
+    lds_read_tr8(aa, fa2);
+    lds_read_tr8(ab, fb2);
+    i32x4 fa[4], fb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fa[i] = i32x4{fa2[2 * i][0], fa2[2 * i][1], fa2[2 * i + 1][0], fa2[2 * i + 1][1]};
+      fb[i] = i32x4{fb2[2 * i][0], fb2[2 * i][1], fb2[2 * i + 1][0], fb2[2 * i + 1][1]};
+    }
+    const int k0 = kbeg + s * WBK;
+    if (k0 + WBK > kend) {
+      // last step: zero the A values of k >= kend (their copies repeated row kend - 1)
+      const int cnt = min(max(kend - (k0 + 8 * (lane >> 4)), 0), 8);   // valid k of this lane's 8
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t mk = (2 * q < cnt ? 0xFFFFu : 0u) | (2 * q + 1 < cnt ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i][q] = (int)((uint32_t)fa[i][q] & mk);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = mfma_bf16(__builtin_bit_cast(bf16x8, fb[j]), __builtin_bit_cast(bf16x8, fa[i]), acc[i][j]);
+  }
+  // lane holds C[lane % 16][4 (lane / 16) + r] of each 16 x 16 block; each
+  // half of the tile (64 rows, two waves) goes through LDS so that every
+  // store writes whole 512-byte rows
+  wg_barrier();
+  constexpr int LDW = 128 + 4;
+  float *stage = reinterpret_cast<float *>(smem);
+  float *cbase = a.c + (int64_t)g * a.cgstride;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if ((w & 1) == half) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<f32x4 *>(stage + (16 * i + (lane & 15)) * LDW + wn + 16 * j + 4 * (lane >> 4)) =
+              acc[i][j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = threadIdx.x; q < 64 * 32; q += 256) {
+      const int row = q >> 5, c4 = q & 31;
+      const int m = m0 + 64 * half + row, n = n0 + 4 * c4;
+      if (m < a.M && n < a.N)
+        __builtin_nontemporal_store(*reinterpret_cast<const f32x4 *>(stage + row * LDW + 4 * c4),
+                                    reinterpret_cast<f32x4 *>(cbase + (int64_t)m * a.ldc + n));
+    }
+    __syncthreads();
   }
 }
 
@@ -431,14 +555,11 @@ hipError_t launch_gemm(const GemmArgs &a, bool at, bool bt, int64_t nblocks, hip
   if (nblocks == 0) return hipSuccess;
   if (nblocks > INT32_MAX) return hipErrorInvalidValue;
   const unsigned blocks = (unsigned)nblocks;
-  if (!at && !bt)
-    grouped_gemm_kernel<BM, BN, 2, false, false><<<blocks, gemm_threads<BM, BN>(), 0, st>>>(a);
-  else if (!at && bt)
-    grouped_gemm_kernel<BM, BN, 2, false, true><<<blocks, gemm_threads<BM, BN>(), 0, st>>>(a);
-  else if (at && bt && BM == 128 && BN == 128)
-    grouped_gemm_kernel<128, 128, 1, true, true><<<blocks, gemm_threads<128, 128>(), 0, st>>>(a);
+  if (at) return hipErrorInvalidValue;
+  if (!bt)
+    grouped_gemm_kernel<BM, BN, false><<<blocks, gemm_threads<BM, BN>(), 0, st>>>(a);
   else
-    return hipErrorInvalidValue;
+    grouped_gemm_kernel<BM, BN, true><<<blocks, gemm_threads<BM, BN>(), 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -469,11 +590,15 @@ hipError_t gemm_rows(const GemmOp &A, const GemmOp &B, float *c, int64_t ldc, co
 hipError_t gemm_kseg(const GemmOp &A, const GemmOp &B, float *c, int64_t ldc, int64_t cgstride, const int32_t *off,
                      int G, int M, int N, int K, hipStream_t st) {
   if (!op_t(A) || !op_t(B)) return hipErrorInvalidValue;
+  if (M % 8 != 0 || N % 8 != 0) return hipErrorInvalidValue;
   GemmArgs a{A, B, c, ldc, cgstride, off, G, M, N, K, (int)cdiv(M, 128), (int)cdiv(N, 128), nullptr, nullptr};
+  const int64_t blocks = (int64_t)G * a.ntm * a.ntn;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
   timing_before(MOE_SITE_BWD_WGRAD, st);
-  const hipError_t e = launch_gemm<128, 128>(a, true, true, (int64_t)G * a.ntm * a.ntn, st);
+  wgrad_kernel<<<(unsigned)blocks, 256, 0, st>>>(a);
   timing_after(MOE_SITE_BWD_WGRAD, st);
-  return e;
+  return hipGetLastError();
 }
 
 // Row tile height for a row-grouped launch.  Routed experts hold ~T k / E
