@@ -8,16 +8,16 @@
 // in BF16).
 //
 // The backward's GEMMs are grouped bf16 GEMMs C_g = A_g B_g^T over K in two
-// kernels.  grouped_gemm_kernel: groups (experts) own token rows (the data
-// gradients dy W_down and dz W_gate_up, and the recompute of the
-// pre-activations when the forward did not keep them); the token rows are
+// kernels, both fed by direct-to-LDS copies (no operand passes through
+// registers on its way into LDS).  rows_kernel: groups (experts) own token
+// rows (the data gradients dy W_down and dz W_gate_up, and the recompute of
+// the pre-activations when the forward did not keep them); the token rows are
 // K-contiguous, the expert's weights are read along either axis of their
 // stored [out, in] layout ("N" layout: element (r, k) at r*rs + k; "T"
-// layout: at k*ks + r, transposed on its way into LDS).  Tiles are staged
-// through registers into two LDS stages.  wgrad_kernel: groups own a token
-// range (the weight gradients, sums over an expert's rows), both operands
-// row-contiguous; copied into LDS as stored and read with gfx950's
-// transposing LDS reads.  fp32 accumulation and output throughout.
+// layout: at k*ks + r).  wgrad_kernel: groups own a token range (the weight
+// gradients, sums over an expert's rows), both operands row-contiguous.
+// Row-contiguous tiles are staged as stored and read with gfx950's
+// transposing LDS read.  fp32 accumulation and output throughout.
 
 #include <algorithm>
 
@@ -26,10 +26,6 @@
 #include "moe_kernels.h"
 
 namespace moe {
-
-namespace {
-constexpr int BK = 64;           // K step
-}  // namespace
 
 // Operand element (r, k) of group g: base + g * gstride + r * rs + k * ks (bf16).
 struct GemmOp {
@@ -47,200 +43,6 @@ struct GemmArgs {
   const TileEntry *tiles;  // row-grouped: tile list (entries of the kernel's BM rows) and its header
   const int32_t *hdr;
 };
-
-// LDS position (in bf16 elements) of operand element (r, k) of a staged tile:
-// rows of 64 k, the eight 16-byte units of a row permuted by an XOR of row
-// bits so that the staging writes and the fragment reads (16 consecutive rows
-// x 4 units per wave) each touch every bank equally.  N-layout tiles are
-// written one 16-byte unit per lane over 8 rows: unit ^= r % 8.  T-layout
-// tiles are written 2, 4 or 8 k of one row per lane, the lanes' rows 8 apart
-// (8 (lane % (ROWS/8)) + u, u alternating with the lane's parity): unit ^=
-// (r1 ^ r5, r4, r3), whose top bit varies inside any 16 consecutive rows (the
-// reads) and whose two top bits take every value over the lanes of one write.
-template <bool T>
-__device__ __forceinline__ int lds_pos(int r, int k) {
-  const int sw = T ? (((((r >> 1) ^ (r >> 5)) & 1) << 2) | (((r >> 4) & 1) << 1) | ((r >> 3) & 1)) : (r & 7);
-  return r * BK + (((k >> 3) ^ sw) << 3) + (k & 7);
-}
-
-// Global loads of one operand's ROWS x 64 tile into registers by NT threads:
-// CPT = 8 ROWS / NT chunks of 16 bytes per thread.  N layout: chunk
-// q = tid + NT j holds row q / 8, k 8 (q % 8) .. +7.  T layout: the thread's
-// rows are 8 (tid % (ROWS/8)) .. +7 and its k are CPT (tid / (ROWS/8)) + j.
-// Rows >= nr and k >= nk read as zero (rows come in whole chunks: every row
-// count and pitch here is a multiple of 8): such a chunk is loaded from the
-// operand's base instead (no branch around the load) and bit j of the
-// returned mask, clear, makes tile_store write zeros for it.
-template <bool T, int ROWS, int NT>
-__device__ __forceinline__ uint32_t tile_load(const uint16_t *base, int64_t rs, int64_t ks, int r0, int nr, int k0,
-                                              int nk, i32x4 (&v)[8 * ROWS / NT]) {
-  constexpr int RC = ROWS / 8, KPT = 8 * ROWS / NT;
-  static_assert(KPT == 2 || KPT == 4 || KPT == 8, "2, 4 or 8 chunks per thread");
-  const int tid = threadIdx.x;
-  uint32_t mask = 0;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    int r, k;
-    int64_t o;
-    if (!T) {
-      const int q = tid + NT * j;
-      r = r0 + (q >> 3);
-      k = k0 + ((q & 7) << 3);
-      o = (int64_t)r * rs + k;
-    } else {
-      r = r0 + (tid % RC) * 8;
-      k = k0 + (tid / RC) * KPT + j;
-      o = (int64_t)k * ks + r;
-    }
-    const bool ok = r < nr && k < nk;
-    v[j] = load16(base + (ok ? o : 0));
-    mask |= (uint32_t)ok << j;
-  }
-  return mask;
-}
-
-// Element 2 h + odd (h constant, odd 0 or 1 per lane) of a 16-byte chunk of bf16.
-__device__ __forceinline__ uint32_t chunk_elem(const i32x4 &v, int h, int odd) {
-  return ((uint32_t)v[h] >> (16 * odd)) & 0xFFFFu;
-}
-
-template <bool T, int ROWS, int NT>
-__device__ __forceinline__ void tile_store(uint16_t *s, const i32x4 (&raw)[8 * ROWS / NT], uint32_t mask) {
-  constexpr int RC = ROWS / 8, KPT = 8 * ROWS / NT;
-  const int tid = threadIdx.x;
-  i32x4 v[KPT];
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) v[j] = ((mask >> j) & 1) ? raw[j] : i32x4{0, 0, 0, 0};
-  if (!T) {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int q = tid + NT * j;
-      *reinterpret_cast<i32x4 *>(s + lds_pos<false>(q >> 3, (q & 7) << 3)) = v[j];
-    }
-  } else {
-    // transpose KPT k x 8 rows: row u of the thread gets its KPT k values;
-    // odd lanes take the rows in the order 1, 0, 3, 2, ... (see lds_pos)
-    const int rc = tid % RC, r = rc * 8, k = (tid / RC) * KPT, par = rc & 1;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int u = t ^ par, odd = (t & 1) ^ par;
-      uint32_t p[KPT / 2];
-#pragma unroll
-      for (int q = 0; q < KPT / 2; ++q)
-        p[q] = chunk_elem(v[2 * q], t >> 1, odd) | (chunk_elem(v[2 * q + 1], t >> 1, odd) << 16);
-      if constexpr (KPT == 2)
-        *reinterpret_cast<uint32_t *>(s + lds_pos<true>(r + u, k)) = p[0];
-      else if constexpr (KPT == 4)
-        *reinterpret_cast<uint2 *>(s + lds_pos<true>(r + u, k)) = uint2{p[0], p[1]};
-      else
-        *reinterpret_cast<i32x4 *>(s + lds_pos<true>(r + u, k)) =
-            i32x4{(int)p[0], (int)p[1], (int)p[2], (int)p[3]};
-    }
-  }
-}
-
-// BM x BN output tile, one 64 x 64 block per wave: BM = BN = 128 (2 x 2
-// waves), or BM = 256, BN = 128 (4 x 2 waves, 512 threads) for row-grouped
-// launches whose groups hold up to 256 rows, so that each group's weight
-// columns are streamed from HBM once rather than once per 128-row tile, and
-// each token row staged serves 128 weight columns.
-// Two LDS stages, one barrier per K step.
-template <int BM, int BN>
-constexpr int gemm_threads() { return 64 * (BM / 64) * (BN / 64); }
-
-template <int BM, int BN, bool BTL>
-__global__ __launch_bounds__((64 * (BM / 64) * (BN / 64))) void grouped_gemm_kernel(GemmArgs a) {
-  constexpr int NB = 2;
-  constexpr bool AT = false;
-  constexpr int NT = gemm_threads<BM, BN>();
-  constexpr int WMW = BM / 64;  // waves along M
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NB * (BM + BN) * BK * 2];
-  uint16_t(*sa)[BM * BK] = reinterpret_cast<uint16_t(*)[BM * BK]>(smem);
-  uint16_t(*sb)[BN * BK] = reinterpret_cast<uint16_t(*)[BN * BK]>(smem + NB * BM * BK * 2);
-  const int bid = blockIdx.x;
-  const int tile = bid / a.ntn;
-  if (tile >= a.hdr[0]) return;
-  const int n0 = (bid - tile * a.ntn) * BN;
-  const TileEntry te = a.tiles[tile];
-  const int g = te.ge & 0xFFFFFF;
-  const int m0 = (a.off ? a.off[g] : 0) + te.m0;
-  const int mend = a.off ? a.off[g + 1] : a.M;
-  const int kbeg = 0, kend = a.K;
-  // Row-grouped: A rows are global rows (gstride 0) and B is the group's
-  // weight; K-grouped: both operands are indexed by the global K (token)
-  // index and only the output is per group.
-  const uint16_t *abase = a.a.base + (int64_t)g * a.a.gstride;
-  const uint16_t *bbase = a.b.base + (int64_t)g * a.b.gstride;
-  const int lane = lane_id(), w = wave_id();
-  const int wm = (w % WMW) * 64, wn = (w / WMW) * 64;
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // K step s is computed from LDS stage s % NB while the global loads of
-  // step s + 1 are in flight into registers; they move into LDS at the end
-  // of step s.  (Two steps of loads in flight gained nothing here and cost
-  // the weight-gradient launches a wave per SIMD.)
-  const int nsteps = (int)cdiv(kend - kbeg, BK);
-  i32x4 va[8 * BM / NT], vb[8 * BN / NT];
-  uint32_t ma = 0, mb = 0;
-  if (nsteps > 0) {
-    ma = tile_load<AT, BM, NT>(abase, a.a.rs, a.a.ks, m0, mend, kbeg, kend, va);
-    mb = tile_load<BTL, BN, NT>(bbase, a.b.rs, a.b.ks, n0, a.N, kbeg, kend, vb);
-    tile_store<AT, BM, NT>(sa[0], va, ma);
-    tile_store<BTL, BN, NT>(sb[0], vb, mb);
-    __syncthreads();
-  }
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    const bool more = s + 1 < nsteps;
-    if (more) {
-      const int k1 = kbeg + (s + 1) * BK;
-      ma = tile_load<AT, BM, NT>(abase, a.a.rs, a.a.ks, m0, mend, k1, kend, va);
-      mb = tile_load<BTL, BN, NT>(bbase, a.b.rs, a.b.ks, n0, a.N, k1, kend, vb);
-    }
-#pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      bf16x8 fa[4], fb[4];
-      const int kf = kk * 32 + 8 * (lane >> 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8 *>(sa[buf] + lds_pos<AT>(wm + 16 * i + (lane & 15), kf));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8 *>(sb[buf] + lds_pos<BTL>(wn + 16 * j + (lane & 15), kf));
-      // operands swapped: acc[i][j] holds the transposed 16 x 16 block, so
-      // each lane ends with 4 consecutive output columns of one row
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(fb[j], fa[i], acc[i][j]);
-    }
-    if (more) {
-      tile_store<AT, BM, NT>(sa[buf ^ 1], va, ma);
-      tile_store<BTL, BN, NT>(sb[buf ^ 1], vb, mb);
-    }
-    __syncthreads();
-  }
-  // lane holds C[lane % 16][4 (lane / 16) + r] of each 16 x 16 block: one
-  // 16-byte store per block (N is a multiple of 8)
-  float *cbase = a.c + (int64_t)g * a.cgstride;
-  {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wm + 16 * i + (lane & 15);
-      if (m >= mend) continue;
-      float *crow = cbase + (int64_t)m * a.ldc;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wn + 16 * j + 4 * (lane >> 4);
-        if (n < a.N) *reinterpret_cast<f32x4 *>(crow + n) = acc[i][j];
-      }
-    }
-  }
-}
 
 // ---------------------------------------------------------------- weight-gradient GEMM
 
@@ -415,6 +217,178 @@ __global__ __launch_bounds__(256) void wgrad_kernel(GemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- row-grouped GEMM, copy-staged
+
+// C[row, n] = sum_k A(row, k) B_g(n, k) for the rows of group g (rows
+// [off[g], off[g+1]), walked through a tile list of BM-row entries), with
+// both tiles copied into LDS by direct-to-LDS loads
+// (a three-stage ring of 32-k steps, two in flight): the token rows (K
+// contiguous) as 64-byte staged rows read with ds_read_b128, the weights
+// either the same way (N layout) or as [k][n] rows read with the transposing
+// ds_read_b64_tr_b16 (T layout), so no operand passes through registers on
+// its way into LDS.  BM x 128 tiles (BM = 256 or 128), one 64 x 64 block per
+// wave.
+namespace {
+constexpr int RBK = 32;
+constexpr int RNSTAGE = 3;
+constexpr int RBT = 128 * RBK * 2;       // bytes of the weight tile of one step
+
+// 16-byte unit u of staged 64-byte row r is stored at u ^ rsw(r): the 16 rows
+// x 4 units of one fragment read (and of one copy) cover every bank once.
+__device__ __forceinline__ int rsw(int r) { return (r >> 2) & 3; }
+
+__device__ __forceinline__ void lds_read4(const uint32_t (&a)[4], i32x4 (&r)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+}
+}  // namespace
+
+template <int BM, bool BTL>
+__global__ __launch_bounds__(2 * BM) void rows_kernel(GemmArgs a) {
+  constexpr int NW = BM / 32;                 // waves: BM / 64 along M x 2 along N
+  constexpr int WMW = BM / 64;
+  constexpr int RAT = BM * RBK * 2;           // bytes of the token tile of one step
+  constexpr int STAGE = RAT + RBT;
+  constexpr int BI = 8 / NW;                  // weight-tile copy instructions per wave
+  constexpr int PS = 2 + BI;                  // copy instructions per wave per stage
+  __shared__ __attribute__((aligned(16))) uint8_t smem[RNSTAGE * STAGE];
+  const int tile = blockIdx.x / a.ntn;
+  if (tile >= a.hdr[0]) return;
+  const int n0 = (blockIdx.x - tile * a.ntn) * 128;
+  const TileEntry te = a.tiles[tile];
+  const int g = te.ge & 0xFFFFFF;
+  const int m0 = (a.off ? a.off[g] : 0) + te.m0;
+  const int mend = a.off ? a.off[g + 1] : a.M;
+  const int nsteps = a.K / RBK;
+  const uint16_t *abase = a.a.base;
+  const uint16_t *bbase = a.b.base + (int64_t)g * a.b.gstride;
+  const int lane = lane_id(), w = wave_id();
+  const int wm = (w % WMW) * 64, wn = (w / WMW) * 64;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)smem;
+
+  // Token copies: instruction q (= w, w + NW) covers staged rows 16q .. 16q+15;
+  // lane l -> row 16q + l / 4, slot l % 4 = logical unit (l % 4) ^ rsw(row),
+  // i.e. k = 8 unit.  Rows past the group's end repeat its last row (their
+  // outputs are not stored).
+  int64_t aoff[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int r = 16 * (w + NW * t) + (lane >> 2);
+    aoff[t] = (int64_t)min(m0 + r, mend - 1) * a.a.rs + 8 * ((lane & 3) ^ rsw(r));
+  }
+  // Weight copies.  N layout: like the tokens, 128 rows (weight rows beyond N
+  // repeat row N - 1).  T layout: instruction q covers k rows 4q .. 4q+3 of
+  // 256 bytes, lane l -> k row 4q + l / 16, 16-byte slot l % 16 = logical
+  // column 16 ((slot / 2) ^ wseg(row)) + 8 (slot % 2) (clamped inside N).
+  int64_t boff[BI];
+#pragma unroll
+  for (int t = 0; t < BI; ++t) {
+    const int q = w + NW * t;
+    if constexpr (!BTL) {
+      const int r = 16 * q + (lane >> 2);
+      boff[t] = (int64_t)min(n0 + r, a.N - 1) * a.b.rs + 8 * ((lane & 3) ^ rsw(r));
+    } else {
+      const int r = 4 * q + (lane >> 4);
+      const int n = 16 * (((lane & 15) >> 1) ^ wseg(r)) + 8 * (lane & 1);
+      boff[t] = (int64_t)r * a.b.ks + min(n0 + n, a.N - 8);
+    }
+  }
+  auto issue = [&](int step) {
+    const int k0 = step * RBK;
+    uint8_t *st = smem + (step % RNSTAGE) * STAGE;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) dma16(abase + aoff[t] + k0, st + (w + NW * t) * 1024);
+#pragma unroll
+    for (int t = 0; t < BI; ++t)
+      dma16(bbase + boff[t] + (BTL ? (int64_t)k0 * a.b.ks : (int64_t)k0), st + RAT + (w + NW * t) * 1024);
+  };
+  // Fragment reads (stage-relative).  Tokens: row wm + 16 i + lane % 16,
+  // unit lane / 16.  Weights, N layout: row wn + 16 j + lane % 16; T layout:
+  // two transposing reads of k rows 8 (lane / 16) + 4 h + (lane % 16) / 4, 4
+  // values at column wn + 16 j + 4 (lane % 4).
+  uint32_t ra[4], rb[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wm + 16 * i + (lane & 15);
+    ra[i] = (uint32_t)(r * 64 + 16 * ((lane >> 4) ^ rsw(r)));
+  }
+  if constexpr (!BTL) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wn + 16 * j + (lane & 15);
+      rb[j] = (uint32_t)(RAT + r * 64 + 16 * ((lane >> 4) ^ rsw(r)));
+    }
+  } else {
+    const int g4 = lane >> 4, jj = lane & 15;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 8 * g4 + 4 * h + (jj >> 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        rb[2 * j + h] = (uint32_t)(RAT + r * WROW + 8 * (jj & 3) + 32 * (((wn >> 4) + j) ^ wseg(r)));
+    }
+  }
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue(0);
+  if (nsteps > 1) issue(1);
+  for (int s = 0; s < nsteps; ++s) {
+    if (s + 1 < nsteps)
+      wait_vm<PS>();
+    else
+      wait_vm<0>();
+    wg_barrier();
+    if (s + 2 < nsteps) issue(s + 2);
+    const uint32_t sb = lds0 + (uint32_t)((s % RNSTAGE) * STAGE);
+    uint32_t aa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) aa[i] = sb + ra[i];
+    i32x4 fa[4], fb[4];
+    lds_read4(aa, fa);
+    if constexpr (!BTL) {
+      uint32_t ab[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ab[j] = sb + rb[j];
+      lds_read4(ab, fb);
+    } else {
+      uint32_t ab[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) ab[q] = sb + rb[q];
+      i32x2 f2[8];
+      lds_read_tr8(ab, f2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[j] = i32x4{f2[2 * j][0], f2[2 * j][1], f2[2 * j + 1][0], f2[2 * j + 1][1]};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = mfma_bf16(__builtin_bit_cast(bf16x8, fb[j]), __builtin_bit_cast(bf16x8, fa[i]), acc[i][j]);
+  }
+  // lane holds C[lane % 16][4 (lane / 16) + r] of each 16 x 16 block
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + wm + 16 * i + (lane & 15);
+    if (m >= mend) continue;
+    float *crow = a.c + (int64_t)m * a.ldc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn + 16 * j + 4 * (lane >> 4);
+      if (n < a.N) *reinterpret_cast<f32x4 *>(crow + n) = acc[i][j];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- element-wise steps
 
 // Gate of row p: gates[perm_src[p]] (routed rows), 1 for the shared expert.
@@ -550,19 +524,6 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float *__restrict__ d
 
 namespace {
 
-template <int BM, int BN>
-hipError_t launch_gemm(const GemmArgs &a, bool at, bool bt, int64_t nblocks, hipStream_t st) {
-  if (nblocks == 0) return hipSuccess;
-  if (nblocks > INT32_MAX) return hipErrorInvalidValue;
-  const unsigned blocks = (unsigned)nblocks;
-  if (at) return hipErrorInvalidValue;
-  if (!bt)
-    grouped_gemm_kernel<BM, BN, false><<<blocks, gemm_threads<BM, BN>(), 0, st>>>(a);
-  else
-    grouped_gemm_kernel<BM, BN, true><<<blocks, gemm_threads<BM, BN>(), 0, st>>>(a);
-  return hipGetLastError();
-}
-
 bool op_t(const GemmOp &o) { return o.ks != 1; }
 
 // Row-grouped GEMM: rows of group g are [off[g], off[g+1]) (or [0, rows)
@@ -572,16 +533,22 @@ bool op_t(const GemmOp &o) { return o.ks != 1; }
 hipError_t gemm_rows(const GemmOp &A, const GemmOp &B, float *c, int64_t ldc, const int32_t *off, int G, int64_t rows,
                      int N, int K, const int32_t *tiles_ws, int bm, int max_tiles, hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  if (op_t(A) || K % BK != 0) return hipErrorInvalidValue;
+  if (op_t(A) || K % RBK != 0 || N % 8 != 0 || (op_t(B) && B.rs != 1)) return hipErrorInvalidValue;
   const TileEntry *tiles = reinterpret_cast<const TileEntry *>(tiles_ws + kTileHdrWords);
-  const int bn = 128;
-  GemmArgs a{A, B, c, ldc, 0, off, G, (int)rows, N, K, 0, (int)cdiv(N, bn), tiles, tiles_ws};
+  GemmArgs a{A, B, c, ldc, 0, off, G, (int)rows, N, K, 0, (int)cdiv(N, 128), tiles, tiles_ws};
   const int64_t blocks = (int64_t)max_tiles * a.ntn;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  const bool bt = op_t(B);
   timing_before(MOE_SITE_BWD_DGRAD, st);
-  const hipError_t e = bm == 256 ? launch_gemm<256, 128>(a, false, op_t(B), blocks, st)
-                                 : launch_gemm<128, 128>(a, false, op_t(B), blocks, st);
+  if (bm == 256) {
+    if (bt) rows_kernel<256, true><<<(unsigned)blocks, 512, 0, st>>>(a);
+    else rows_kernel<256, false><<<(unsigned)blocks, 512, 0, st>>>(a);
+  } else {
+    if (bt) rows_kernel<128, true><<<(unsigned)blocks, 256, 0, st>>>(a);
+    else rows_kernel<128, false><<<(unsigned)blocks, 256, 0, st>>>(a);
+  }
   timing_after(MOE_SITE_BWD_DGRAD, st);
-  return e;
+  return hipGetLastError();
 }
 
 // K-grouped GEMM: C_g [M, N] = sum over k in group g's range of A(m, k) B(n, k),
