@@ -230,7 +230,8 @@ __global__ __launch_bounds__(256) void wgrad_kernel(GemmArgs a) {
 // wave.
 namespace {
 constexpr int RBK = 32;
-constexpr int RNSTAGE = 3;
+constexpr int RBN256 = 256;   // columns of the 256-row tiles
+constexpr int RNS256 = 4;     // their LDS stages
 constexpr int RBT = 128 * RBK * 2;       // bytes of the weight tile of one step
 
 // 16-byte unit u of staged 64-byte row r is stored at u ^ rsw(r): the 16 rows
@@ -249,18 +250,20 @@ __device__ __forceinline__ void lds_read4(const uint32_t (&a)[4], i32x4 (&r)[4])
 }
 }  // namespace
 
-template <int BM, bool BTL>
-__global__ __launch_bounds__(2 * BM) void rows_kernel(GemmArgs a) {
-  constexpr int NW = BM / 32;                 // waves: BM / 64 along M x 2 along N
-  constexpr int WMW = BM / 64;
+template <int BM, int BN, int NSTG, bool BTL>
+__global__ __launch_bounds__((BM / 64) * (BN / 64) * 64) void rows_kernel(GemmArgs a) {
+  constexpr int NW = (BM / 64) * (BN / 64);   // waves, one 64 x 64 block each
+  constexpr int WMW = BM / 64;                // waves along M
   constexpr int RAT = BM * RBK * 2;           // bytes of the token tile of one step
-  constexpr int STAGE = RAT + RBT;
-  constexpr int BI = 8 / NW;                  // weight-tile copy instructions per wave
-  constexpr int PS = 2 + BI;                  // copy instructions per wave per stage
-  __shared__ __attribute__((aligned(16))) uint8_t smem[RNSTAGE * STAGE];
+  constexpr int STAGE = RAT + BN * RBK * 2;
+  constexpr int AI = BM / 16 / NW;            // token-tile copy instructions per wave
+  constexpr int BI = BN / 16 / NW;            // weight-tile copy instructions per wave
+  constexpr int PS = AI + BI;                 // copy instructions per wave per stage
+  static_assert(AI >= 1 && BI >= 1, "every wave copies");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NSTG * STAGE];
   const int tile = blockIdx.x / a.ntn;
   if (tile >= a.hdr[0]) return;
-  const int n0 = (blockIdx.x - tile * a.ntn) * 128;
+  const int n0 = (blockIdx.x - tile * a.ntn) * BN;
   const TileEntry te = a.tiles[tile];
   const int g = te.ge & 0xFFFFFF;
   const int m0 = (a.off ? a.off[g] : 0) + te.m0;
@@ -272,20 +275,22 @@ __global__ __launch_bounds__(2 * BM) void rows_kernel(GemmArgs a) {
   const int wm = (w % WMW) * 64, wn = (w / WMW) * 64;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)smem;
 
-  // Token copies: instruction q (= w, w + NW) covers staged rows 16q .. 16q+15;
+  // Token copies: instruction q (= w + NW t) covers staged rows 16q .. 16q+15;
   // lane l -> row 16q + l / 4, slot l % 4 = logical unit (l % 4) ^ rsw(row),
   // i.e. k = 8 unit.  Rows past the group's end repeat its last row (their
   // outputs are not stored).
-  int64_t aoff[2];
+  int64_t aoff[AI];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < AI; ++t) {
     const int r = 16 * (w + NW * t) + (lane >> 2);
     aoff[t] = (int64_t)min(m0 + r, mend - 1) * a.a.rs + 8 * ((lane & 3) ^ rsw(r));
   }
-  // Weight copies.  N layout: like the tokens, 128 rows (weight rows beyond N
-  // repeat row N - 1).  T layout: instruction q covers k rows 4q .. 4q+3 of
-  // 256 bytes, lane l -> k row 4q + l / 16, 16-byte slot l % 16 = logical
-  // column 16 ((slot / 2) ^ wseg(row)) + 8 (slot % 2) (clamped inside N).
+  // Weight copies.  N layout: like the tokens, BN rows (weight rows beyond N
+  // repeat row N - 1).  T layout: BN / 128 sub-tiles of 32 k rows x 128
+  // columns (256 bytes); instruction q covers k rows 4 (q % 8) .. +3 of
+  // sub-tile q / 8, lane l -> k row 4 (q % 8) + l / 16, 16-byte slot l % 16
+  // = logical column 128 (q / 8) + 16 ((slot / 2) ^ wseg(row)) + 8 (slot % 2)
+  // (clamped inside N).
   int64_t boff[BI];
 #pragma unroll
   for (int t = 0; t < BI; ++t) {
@@ -294,16 +299,16 @@ __global__ __launch_bounds__(2 * BM) void rows_kernel(GemmArgs a) {
       const int r = 16 * q + (lane >> 2);
       boff[t] = (int64_t)min(n0 + r, a.N - 1) * a.b.rs + 8 * ((lane & 3) ^ rsw(r));
     } else {
-      const int r = 4 * q + (lane >> 4);
-      const int n = 16 * (((lane & 15) >> 1) ^ wseg(r)) + 8 * (lane & 1);
+      const int r = 4 * (q & 7) + (lane >> 4);
+      const int n = 128 * (q >> 3) + 16 * (((lane & 15) >> 1) ^ wseg(r)) + 8 * (lane & 1);
       boff[t] = (int64_t)r * a.b.ks + min(n0 + n, a.N - 8);
     }
   }
   auto issue = [&](int step) {
     const int k0 = step * RBK;
-    uint8_t *st = smem + (step % RNSTAGE) * STAGE;
+    uint8_t *st = smem + (step % NSTG) * STAGE;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) dma16(abase + aoff[t] + k0, st + (w + NW * t) * 1024);
+    for (int t = 0; t < AI; ++t) dma16(abase + aoff[t] + k0, st + (w + NW * t) * 1024);
 #pragma unroll
     for (int t = 0; t < BI; ++t)
       dma16(bbase + boff[t] + (BTL ? (int64_t)k0 * a.b.ks : (int64_t)k0), st + RAT + (w + NW * t) * 1024);
@@ -331,7 +336,8 @@ __global__ __launch_bounds__(2 * BM) void rows_kernel(GemmArgs a) {
       const int r = 8 * g4 + 4 * h + (jj >> 2);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        rb[2 * j + h] = (uint32_t)(RAT + r * WROW + 8 * (jj & 3) + 32 * (((wn >> 4) + j) ^ wseg(r)));
+        rb[2 * j + h] = (uint32_t)(RAT + (wn >> 7) * RBT + r * WROW + 8 * (jj & 3) +
+                                   32 * ((((wn & 127) >> 4) + j) ^ wseg(r)));
     }
   }
   f32x4 acc[4][4];
@@ -340,16 +346,22 @@ __global__ __launch_bounds__(2 * BM) void rows_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  issue(0);
-  if (nsteps > 1) issue(1);
+  // NSTG - 1 steps of copies in flight: step s waits until at most the copies
+  // of steps s+1 .. s+NSTG-2 are outstanding
+#pragma unroll
+  for (int q = 0; q < NSTG - 1; ++q)
+    if (q < nsteps) issue(q);
   for (int s = 0; s < nsteps; ++s) {
-    if (s + 1 < nsteps)
+    const int ahead = min(nsteps - 1 - s, NSTG - 2);
+    if (ahead >= 2)
+      wait_vm<2 * PS>();
+    else if (ahead == 1)
       wait_vm<PS>();
     else
       wait_vm<0>();
     wg_barrier();
-    if (s + 2 < nsteps) issue(s + 2);
-    const uint32_t sb = lds0 + (uint32_t)((s % RNSTAGE) * STAGE);
+    if (s + NSTG - 1 < nsteps) issue(s + NSTG - 1);
+    const uint32_t sb = lds0 + (uint32_t)((s % NSTG) * STAGE);
     uint32_t aa[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) aa[i] = sb + ra[i];
@@ -535,17 +547,17 @@ hipError_t gemm_rows(const GemmOp &A, const GemmOp &B, float *c, int64_t ldc, co
   if (rows == 0) return hipSuccess;
   if (op_t(A) || K % RBK != 0 || N % 8 != 0 || (op_t(B) && B.rs != 1)) return hipErrorInvalidValue;
   const TileEntry *tiles = reinterpret_cast<const TileEntry *>(tiles_ws + kTileHdrWords);
-  GemmArgs a{A, B, c, ldc, 0, off, G, (int)rows, N, K, 0, (int)cdiv(N, 128), tiles, tiles_ws};
+  GemmArgs a{A, B, c, ldc, 0, off, G, (int)rows, N, K, 0, (int)cdiv(N, bm == 256 ? RBN256 : 128), tiles, tiles_ws};
   const int64_t blocks = (int64_t)max_tiles * a.ntn;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   const bool bt = op_t(B);
   timing_before(MOE_SITE_BWD_DGRAD, st);
   if (bm == 256) {
-    if (bt) rows_kernel<256, true><<<(unsigned)blocks, 512, 0, st>>>(a);
-    else rows_kernel<256, false><<<(unsigned)blocks, 512, 0, st>>>(a);
+    if (bt) rows_kernel<256, RBN256, RNS256, true><<<(unsigned)blocks, 4 * RBN256, 0, st>>>(a);
+    else rows_kernel<256, RBN256, RNS256, false><<<(unsigned)blocks, 4 * RBN256, 0, st>>>(a);
   } else {
-    if (bt) rows_kernel<128, true><<<(unsigned)blocks, 256, 0, st>>>(a);
-    else rows_kernel<128, false><<<(unsigned)blocks, 256, 0, st>>>(a);
+    if (bt) rows_kernel<128, 128, 3, true><<<(unsigned)blocks, 256, 0, st>>>(a);
+    else rows_kernel<128, 128, 3, false><<<(unsigned)blocks, 256, 0, st>>>(a);
   }
   timing_after(MOE_SITE_BWD_DGRAD, st);
   return hipGetLastError();
@@ -568,14 +580,11 @@ hipError_t gemm_kseg(const GemmOp &A, const GemmOp &B, float *c, int64_t ldc, in
   return hipGetLastError();
 }
 
-// Row tile height for a row-grouped launch.  Routed experts hold ~T k / E
-// rows each, so few that the GEMM is bound by streaming the expert's weights:
-// 256-row tiles read each weight column block once per expert with up to 256
-// rows.  Otherwise (one group, or many rows per group) 128-row tiles.
-int row_tile(int64_t rows, int G) {
-  if (G <= 1) return 128;
-  return cdiv(rows, G) <= 256 ? 256 : 128;
-}
+// Row tile height for a row-grouped launch: 256-row tiles (256 columns, a
+// four-stage copy ring; each group's weight column block is streamed once for
+// up to 256 rows) unless the groups hold so few rows on average that half a
+// 256-row tile would stay empty, then 128 x 128 tiles.
+int row_tile(int64_t rows, int G) { return cdiv(rows, G) >= 128 ? 256 : 128; }
 int max_tiles_for(int64_t rows, int G, int bm) { return (int)(cdiv(rows, bm) + std::min<int64_t>(rows, G) + 1); }
 
 }  // namespace
