@@ -62,8 +62,6 @@ namespace {
 constexpr int WBK = 32;                  // K step
 constexpr int WROW = 256;                // bytes of one staged k row (128 bf16)
 constexpr int WTILE = WBK * WROW;        // 8 KB: one operand's tile of one step
-constexpr int WSTAGE = 2 * WTILE;        // A then B
-constexpr int WNSTAGE = 3;
 
 typedef __attribute__((ext_vector_type(2))) int i32x2;
 
@@ -91,37 +89,59 @@ __device__ __forceinline__ void lds_read_tr8(const uint32_t (&a)[8], i32x2 (&r)[
 }
 }  // namespace
 
-__global__ __launch_bounds__(256) void wgrad_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[WNSTAGE * WSTAGE];
+// TB x TB output tiles (TB = 128: 4 waves, 3 stages; TB = 256: 16 waves, 4
+// stages), one 64 x 64 block per wave; each operand tile of a step is TB / 128
+// sub-tiles of 32 k rows x 128 columns.
+template <int TB, int NSTG>
+__global__ __launch_bounds__((TB / 64) * (TB / 64) * 64) void wgrad_kernel(GemmArgs a) {
+  constexpr int NW = (TB / 64) * (TB / 64);
+  constexpr int NT = 64 * NW;
+  constexpr int WMW = TB / 64;
+  constexpr int SUB = TB / 128;              // sub-tiles per operand tile
+  constexpr int OPT = SUB * WTILE;           // bytes of one operand tile of a step
+  constexpr int STG = 2 * OPT;
+  constexpr int CI = 8 * SUB / NW;           // copy instructions per wave per operand per stage
+  constexpr int PS = 2 * CI;
+  constexpr int LDW = TB + 4;                // floats per staged output row
+  static_assert(CI >= 1, "every wave copies");
+  static_assert(64 * LDW * 4 <= NSTG * STG, "output staging fits the ring");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NSTG * STG];
   const int per = a.ntm * a.ntn;
   const int g = blockIdx.x / per;
   const int rt = blockIdx.x - g * per;
-  const int m0 = (rt / a.ntn) * 128, n0 = (rt % a.ntn) * 128;
+  const int m0 = (rt / a.ntn) * TB, n0 = (rt % a.ntn) * TB;
   const int kbeg = a.off ? a.off[g] : 0, kend = a.off ? a.off[g + 1] : a.K;
   const int nsteps = (int)cdiv(kend - kbeg, WBK);
   const int lane = lane_id(), w = wave_id();
-  const int wm = (w & 1) * 64, wn = (w >> 1) * 64;
+  const int wm = (w % WMW) * 64, wn = (w / WMW) * 64;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)smem;
 
-  // Copies: operand tile rows 4q .. 4q+3 per instruction (q = w, w + 4), lane
-  // l -> row 4q + l / 16, 16-byte slot l % 16 of the row, which holds logical
-  // m = 16 (slot / 2 ^ wseg(row)) + 8 (slot % 2) (clamped inside the operand).
-  const int crow = lane >> 4;                       // + 4q
-  const int cm = 16 * (((lane & 15) >> 1) ^ wseg(4 * w + crow)) + 8 * (lane & 1);
-  const int am = min(m0 + cm, a.M - 8), bn = min(n0 + cm, a.N - 8);
+  // Copies: instruction q (= w + NW t) covers k rows 4 (q % 8) .. +3 of
+  // sub-tile q / 8; lane l -> k row 4 (q % 8) + l / 16, 16-byte slot l % 16
+  // of the row, which holds logical column 128 (q / 8) + 16 (slot / 2 ^
+  // wseg(row)) + 8 (slot % 2) (clamped inside the operand).
+  int am[CI], bn[CI], crow[CI];
+#pragma unroll
+  for (int t = 0; t < CI; ++t) {
+    const int q = w + NW * t;
+    crow[t] = 4 * (q & 7) + (lane >> 4);
+    const int c = 128 * (q >> 3) + 16 * (((lane & 15) >> 1) ^ wseg(crow[t])) + 8 * (lane & 1);
+    am[t] = min(m0 + c, a.M - 8);
+    bn[t] = min(n0 + c, a.N - 8);
+  }
   auto issue = [&](int step) {
     const int k0 = kbeg + step * WBK;
-    uint8_t *st = smem + (step % WNSTAGE) * WSTAGE;
+    uint8_t *st = smem + (step % NSTG) * STG;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int q = w + 4 * t;
-      const int64_t p = min(k0 + 4 * q + crow, kend - 1);
-      dma16(a.a.base + p * a.a.ks + am, st + q * 1024);
-      dma16(a.b.base + p * a.b.ks + bn, st + WTILE + q * 1024);
+    for (int t = 0; t < CI; ++t) {
+      const int q = w + NW * t;
+      const int64_t p = min(k0 + crow[t], kend - 1);
+      dma16(a.a.base + p * a.a.ks + am[t], st + q * 1024);
+      dma16(a.b.base + p * a.b.ks + bn[t], st + OPT + q * 1024);
     }
   };
   // Transposing reads: lane (g4 = lane / 16, j = lane % 16) reads k row
-  // 8 g4 + 4 h + j / 4 (h = half of its 8 k), 4 bf16 at m = mb + 4 (j % 4).
+  // 8 g4 + 4 h + j / 4 (h = half of its 8 k), 4 bf16 at column mb + 4 (j % 4).
   uint32_t ra[8], rb[8];   // per-stage-relative addresses: [2 i + h], [2 j + h]
   {
     const int g4 = lane >> 4, jj = lane & 15;
@@ -131,8 +151,8 @@ __global__ __launch_bounds__(256) void wgrad_kernel(GemmArgs a) {
       const uint32_t rowb = (uint32_t)(r * WROW + 8 * (jj & 3));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        ra[2 * i + h] = rowb + 32 * (((wm >> 4) + i) ^ wseg(r));
-        rb[2 * i + h] = WTILE + rowb + 32 * (((wn >> 4) + i) ^ wseg(r));
+        ra[2 * i + h] = (wm >> 7) * WTILE + rowb + 32 * ((((wm & 127) >> 4) + i) ^ wseg(r));
+        rb[2 * i + h] = OPT + (wn >> 7) * WTILE + rowb + 32 * ((((wn & 127) >> 4) + i) ^ wseg(r));
       }
     }
   }
@@ -142,19 +162,23 @@ __global__ __launch_bounds__(256) void wgrad_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (nsteps > 0) issue(0);
-  if (nsteps > 1) issue(1);
+  // NSTG - 1 steps of copies in flight: step s waits until at most the copies
+  // of steps s+1 .. s+NSTG-2 are outstanding; the barrier makes every wave's
+  // copies visible and frees the stage of step s - 1 for step s + NSTG - 1
+#pragma unroll
+  for (int q = 0; q < NSTG - 1; ++q)
+    if (q < nsteps) issue(q);
   for (int s = 0; s < nsteps; ++s) {
-    // this wave's copies of step s have landed when at most those of step
-    // s + 1 (4 instructions) are still in flight; the barrier makes every
-    // wave's copies visible and frees the stage of step s - 1 for step s + 2
-    if (s + 1 < nsteps)
-      wait_vm<4>();
+    const int ahead = min(nsteps - 1 - s, NSTG - 2);
+    if (ahead >= 2)
+      wait_vm<2 * PS>();
+    else if (ahead == 1)
+      wait_vm<PS>();
     else
       wait_vm<0>();
     wg_barrier();
-    if (s + 2 < nsteps) issue(s + 2);
-    const uint32_t sb = lds0 + (uint32_t)((s % WNSTAGE) * WSTAGE);
+    if (s + NSTG - 1 < nsteps) issue(s + NSTG - 1);
+    const uint32_t sb = lds0 + (uint32_t)((s % NSTG) * STG);
     uint32_t aa[8], ab[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -187,16 +211,15 @@ __global__ __launch_bounds__(256) void wgrad_kernel(GemmArgs a) {
       for (int j = 0; j < 4; ++j)
         acc[i][j] = mfma_bf16(__builtin_bit_cast(bf16x8, fb[j]), __builtin_bit_cast(bf16x8, fa[i]), acc[i][j]);
   }
-  // lane holds C[lane % 16][4 (lane / 16) + r] of each 16 x 16 block; each
-  // half of the tile (64 rows, two waves) goes through LDS so that every
-  // store writes whole 512-byte rows
+  // lane holds C[lane % 16][4 (lane / 16) + r] of each 16 x 16 block; the
+  // tile goes out 64 rows (one row of waves) at a time through LDS so that
+  // every store writes whole rows of TB floats
   wg_barrier();
-  constexpr int LDW = 128 + 4;
   float *stage = reinterpret_cast<float *>(smem);
   float *cbase = a.c + (int64_t)g * a.cgstride;
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    if ((w & 1) == half) {
+  for (int part = 0; part < WMW; ++part) {
+    if (w % WMW == part) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -206,9 +229,9 @@ __global__ __launch_bounds__(256) void wgrad_kernel(GemmArgs a) {
     }
     __syncthreads();
 #pragma unroll
-    for (int q = threadIdx.x; q < 64 * 32; q += 256) {
-      const int row = q >> 5, c4 = q & 31;
-      const int m = m0 + 64 * half + row, n = n0 + 4 * c4;
+    for (int q = threadIdx.x; q < 64 * TB / 4; q += NT) {
+      const int row = q / (TB / 4), c4 = q % (TB / 4);
+      const int m = m0 + 64 * part + row, n = n0 + 4 * c4;
       if (m < a.M && n < a.N)
         __builtin_nontemporal_store(*reinterpret_cast<const f32x4 *>(stage + row * LDW + 4 * c4),
                                     reinterpret_cast<f32x4 *>(cbase + (int64_t)m * a.ldc + n));
@@ -570,12 +593,20 @@ hipError_t gemm_kseg(const GemmOp &A, const GemmOp &B, float *c, int64_t ldc, in
                      int G, int M, int N, int K, hipStream_t st) {
   if (!op_t(A) || !op_t(B)) return hipErrorInvalidValue;
   if (M % 8 != 0 || N % 8 != 0) return hipErrorInvalidValue;
-  GemmArgs a{A, B, c, ldc, cgstride, off, G, M, N, K, (int)cdiv(M, 128), (int)cdiv(N, 128), nullptr, nullptr};
+  // 256 x 256 tiles when both dimensions fill them and there are enough of
+  // them to keep every CU busy twice over (the shared expert, one group with a
+  // long token range, has few), else 128 x 128
+  const int tb = (M >= 256 && N >= 256 && (int64_t)G * cdiv(M, 256) * cdiv(N, 256) >= 2 * num_compute_units()) ? 256
+                                                                                                          : 128;
+  GemmArgs a{A, B, c, ldc, cgstride, off, G, M, N, K, (int)cdiv(M, tb), (int)cdiv(N, tb), nullptr, nullptr};
   const int64_t blocks = (int64_t)G * a.ntm * a.ntn;
   if (blocks == 0) return hipSuccess;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   timing_before(MOE_SITE_BWD_WGRAD, st);
-  wgrad_kernel<<<(unsigned)blocks, 256, 0, st>>>(a);
+  if (tb == 256)
+    wgrad_kernel<256, 4><<<(unsigned)blocks, 1024, 0, st>>>(a);
+  else
+    wgrad_kernel<128, 3><<<(unsigned)blocks, 256, 0, st>>>(a);
   timing_after(MOE_SITE_BWD_WGRAD, st);
   return hipGetLastError();
 }
