@@ -48,24 +48,35 @@ def parse():
 # HBM traffic of the dominant kernel, from two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE,
 # KiB per dispatch) over this command, each scaled by what the same counter reads for a plain
 # 1 GiB device copy (bench.py --copy-calibration).  Valid only for the kernel sources they were
-# taken on: a different hash of the library sources reports null.
+# taken on: a different hash of the dominant kernel's sources (KERNEL_SOURCES) reports null.
 TRAFFIC = {
-    "decode_bf16": {"src_hash": "a87c18d4e41a8ac1", "fetch_kib": 3309815.9, "write_kib": 1884.8555, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_fp8": {"src_hash": "a87c18d4e41a8ac1", "fetch_kib": 1666956.0, "write_kib": 1191.5312, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_mxfp4": {"src_hash": "a87c18d4e41a8ac1", "fetch_kib": 1008328.0, "write_kib": 1199.4414, "fetch_scale": 2.0, "write_scale": 1.0},
-    "dense_ff_bf16": {"src_hash": "a87c18d4e41a8ac1", "fetch_kib": 1781697.4, "write_kib": 221184.0, "fetch_scale": 2.0, "write_scale": 1.0},
-    "prefill_fp8": {"src_hash": "a87c18d4e41a8ac1", "fetch_kib": 4420431.4, "write_kib": 140277.27, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_bf16": {"src_hash": "f7fe5ff773ec3dd2", "fetch_kib": 3308694.4, "write_kib": 1883.1193, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_fp8": {"src_hash": "f7fe5ff773ec3dd2", "fetch_kib": 1664782.2, "write_kib": 1184.9233, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_mxfp4": {"src_hash": "f7fe5ff773ec3dd2", "fetch_kib": 901014.14, "write_kib": 1183.3466, "fetch_scale": 2.0, "write_scale": 1.0},
+    "dense_ff_bf16": {"src_hash": "f7fe5ff773ec3dd2", "fetch_kib": 1779403.7, "write_kib": 221184.0, "fetch_scale": 2.0, "write_scale": 1.0},
+    "prefill_fp8": {"src_hash": "f7fe5ff773ec3dd2", "fetch_kib": 4419077.4, "write_kib": 140285.07, "fetch_scale": 2.0, "write_scale": 1.0},
+    "train_bf16": {"src_hash": "788118b9938d5ab5", "fetch_kib": 4393799.8, "write_kib": 26323206.0, "fetch_scale": 2.0, "write_scale": 1.0},
 }
 
 
-def library_source_hash():
+# Sources that decide what the dominant kernel of a workload does (its code,
+# the structures it reads, the launch plan): the forward's grouped gate/up
+# kernels, or the backward's weight-gradient kernel.
+KERNEL_SOURCES = {
+    "forward": ["expert_gemm.hip", "expert_gemm_tiled.hip", "expert_gemm_tiled_mx.hip", "moe_common.h",
+                "moe_kernels.h", "moe_api.cpp"],
+    "backward": ["backward.hip", "moe_common.h", "moe_kernels.h", "moe_api.cpp"],
+}
+
+
+def library_source_hash(family="forward"):
+    """Hash of the sources the family's dominant kernel is built from."""
     import hashlib
     d = os.path.join(ROOT, "router_gemm_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+    for f in sorted(KERNEL_SOURCES[family]):
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -243,7 +254,7 @@ def main():
         roof["traffic"] = None
         roof["traffic_note"] = ("no counters taken on these kernel sources" if not tr
                                 else "kernel sources changed since the counters were taken")
-    roof["library_source_hash"] = src_hash
+    roof["kernel_source_hash"] = src_hash
     roof["kernel"] = ("gate/up + SwiGLU of the dense FF layer (one expert)" if cfg.dense
                       else "grouped gate/up + SwiGLU (routed and shared experts)")
     roof["kernel_ms_per_step"] = round(gu_ms, 4)
@@ -376,7 +387,7 @@ def bench_train(args, cfg, lt, x, dev):
     roof = {"bound": "hbm", "achieved": round(w_achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(w_achieved / PEAK_HBM_GBS, 4)}
     tr = TRAFFIC.get(cfg.name)
-    src_hash = library_source_hash()
+    src_hash = library_source_hash("backward")
     if tr and tr["src_hash"] == src_hash:
         roof["traffic"] = int((tr["fetch_kib"] * tr["fetch_scale"] + tr["write_kib"] * tr["write_scale"]) * 1024)
         roof["traffic_per"] = "step (the site's launches)"
@@ -385,7 +396,7 @@ def bench_train(args, cfg, lt, x, dev):
         roof["traffic_note"] = ("no counters taken on these kernel sources" if not tr
                                 else "kernel sources changed since the counters were taken")
     roof.update({
-        "library_source_hash": src_hash,
+        "kernel_source_hash": src_hash,
         "kernel": "weight-gradient grouped bf16 GEMM (dW_gate_up, dW_down; routed and shared)",
         "kernel_ms_per_step": round(w_ms, 4),
         "launches_per_step": g_launch["bwd_wgrad_gemm"],
