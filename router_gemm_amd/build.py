@@ -26,6 +26,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.
 EXTRA = {
     "expert_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "expert_gemm_tiled.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "expert_gemm_tiled_mx.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

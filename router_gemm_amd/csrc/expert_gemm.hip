@@ -761,7 +761,9 @@ FfnPlan ffn_plan(const FfnGroup *g, int ngroups, int H) {
       mx_ok = mx_ok && tiled_mx_supported(g[i], H);
     }
   p.tiled = (all128 && H % 256 == 0 && mx_ok && g[0].nrows > 0 && avg >= 48.0) ? 1 : 0;
-  p.bm = p.tiled ? (any_mx ? 64 : 128) : 16 * p.mt;
+  // 256-row token tiles once the mean expert fills one (a weight tile then
+  // feeds all of an expert's rows from a single fetch)
+  p.bm = p.tiled ? (any_mx ? 64 : (avg >= 128.0 ? 256 : 128)) : 16 * p.mt;
   int64_t cap = 1;
   for (int i = 0; i < ngroups; ++i) cap += cdiv(g[i].nrows, p.bm) + std::min<int64_t>(g[i].nrows, g[i].E);
   p.max_tiles = (int)cap;
@@ -818,7 +820,7 @@ hipError_t launch_expert_ffn(const FfnGroup *g, int ngroups, int H, const FfnPla
       if (g[i].nrows == 0) continue;
       build_tiles_kernel<<<1, 1024, 0, st>>>(g[i], g[i], 1, g[i].mx ? 64 : 128, plan.max_tiles, tiles, hdr);
       const hipError_t e = g[i].mx ? launch_tiled_mx_ffn(g[i], H, tiles, hdr, num_compute_units(), site, st)
-                                   : launch_tiled_ffn(&g[i], 1, H, tiles, hdr, num_compute_units(), site, st);
+                                   : launch_tiled_ffn(&g[i], 1, H, tiles, hdr, num_compute_units(), 128, site, st);
       if (e != hipSuccess) return e;
     }
     return hipGetLastError();
@@ -826,7 +828,7 @@ hipError_t launch_expert_ffn(const FfnGroup *g, int ngroups, int H, const FfnPla
   build_tiles_kernel<<<1, 1024, 0, st>>>(a.g0, a.g1, ngroups, plan.bm, plan.max_tiles, tiles, hdr);
   if (plan.tiled) {
     if (H % 256 != 0) return hipErrorInvalidValue;
-    return launch_tiled_ffn(g, ngroups, H, tiles, hdr, num_compute_units(), site, st);
+    return launch_tiled_ffn(g, ngroups, H, tiles, hdr, num_compute_units(), plan.bm, site, st);
   }
   switch (plan.mt * 2 + (mx ? 1 : 0)) {
     case 2: run_stream<1, false>(a, plan, maxI, site, st); break;

@@ -386,11 +386,328 @@ __device__ __forceinline__ void tiled_item(const FfnGroup &G, const TileEntry &t
   __syncthreads();   // the next work item reuses the LDS ring and the reduction area
 }
 
+// ------------------------------------------------------------ wide tiles
+//
+// For experts with many rows (mean >= 128 per expert): a work item is 256
+// weight rows x 256 token rows and a workgroup is 8 waves, two per SIMD.  A
+// weight tile fetched once then feeds every row of most experts (instead of
+// being fetched again for each 128-row token tile), and a K chunk moves 64 KB
+// into LDS for twice the MFMAs of the 128-row item.  The LDS ring has two
+// stages (66 KB each): chunk kc+1 is copied while chunk kc is consumed.  A
+// wave owns 128 weight rows (wn) x 4 interleaved 16-row token slices
+// 16 (wm + 4 j); it reads its chunk's token fragments once and streams the 8
+// weight tiles' fragments through a double buffer, which keeps it within the
+// 256 registers a wave has at two waves per SIMD.
+
+namespace {
+constexpr int WBM = 256;                    // token rows per wide tile
+constexpr int WTHREADS = 512;
+constexpr int WTX = WBM * 128;              // token bytes per stage
+constexpr int WTSX = 2048;                  // token scales per stage (8 waves x 256 B)
+constexpr int WSTAGE = TW + WTX + WTSX;
+constexpr int WNSTAGE = 2;
+}  // namespace
+
+template <bool FP8, bool GATEUP>
+struct WideItem {
+  const FfnGroup &G;
+  int e, rbeg, rend, nvalid, I, K, KB, nchunk, col0, ntile, H;
+  int64_t rowb;
+  const uint8_t *wsrc, *asrc;
+  const float *ascale;
+  int lane, w, wn, wm;
+  uint32_t woff[4], xoff[4], soff;   // per-lane byte offsets of this lane's copies
+
+  __device__ WideItem(const FfnGroup &g, const TileEntry &te, int nt_, int H_) : G(g), ntile(nt_), H(H_) {
+    lane = threadIdx.x & 63;
+    w = uniform(threadIdx.x >> 6);
+    wn = w & 1;
+    wm = w >> 1;
+    e = te.ge & 0xFFFFFF;
+    rend = min(max(group_off(G, e + 1), 0), G.nrows);
+    rbeg = min(max(group_off(G, e), 0) + te.m0, rend);
+    nvalid = min(rend - rbeg, WBM);
+    I = G.I;
+    K = GATEUP ? H : I;
+    rowb = (int64_t)K * (FP8 ? 1 : 2);
+    nchunk = (int)(rowb / 128);
+    KB = K / 128;
+    col0 = GATEUP ? ntile * 128 : ntile * TBN;
+    wsrc = GATEUP ? G.wgu + (int64_t)e * 2 * I * rowb : G.wd + (int64_t)e * H * rowb;
+    const bool indirect = GATEUP && G.xsrc != nullptr;
+    asrc = (GATEUP ? G.x : G.h) + (indirect ? 0 : (int64_t)rbeg * rowb);
+    ascale = (GATEUP ? G.xs : G.hs) + (FP8 && !indirect ? (int64_t)rbeg * KB : 0);
+    const int sub = lane >> 3;   // row within an 8-row group
+    // copy instruction q = w + 8 t covers rows 8q .. 8q+7 of the weight and
+    // of the token tile (1 KB each)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r = 8 * (w + 8 * t) + sub;
+      const int c = (lane & 7) ^ swz_f(r);   // logical 16-byte column landing in this lane's slot
+      const int grow = GATEUP ? (r < 128 ? col0 + r : I + col0 + r - 128) : col0 + r;
+      woff[t] = (uint32_t)(grow * rowb + c * 16);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r = 8 * (w + 8 * t) + sub;
+      const int c = (lane & 7) ^ swz_f(r);
+      // rows past the end repeat a valid row; indirect rows come from x row xsrc[row] / xdiv
+      const int rr = min(r, nvalid - 1);
+      const int64_t src = indirect ? G.xsrc[rbeg + rr] / G.xdiv : rr;
+      xoff[t] = (uint32_t)(src * rowb + c * 16);
+    }
+    {
+      const int rr = min(32 * w + (lane & 31), nvalid - 1);
+      const int64_t src = indirect ? G.xsrc[rbeg + rr] / G.xdiv : rr;
+      soff = (uint32_t)(src * KB * 4);
+    }
+  }
+
+  // Direct-to-LDS copies of K chunk kc into stage buffer sb: 4 (weights) +
+  // 4 (tokens) [+ 1 (token scales, fp8)] instructions per wave.
+  __device__ __forceinline__ void issue(int kc, uint8_t *sb) const {
+    const uint8_t *wb = wsrc + (int64_t)kc * 128;
+    const uint8_t *xb = asrc + (int64_t)kc * 128;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dma16(wb + woff[t], sb + (w + 8 * t) * 1024);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dma16(xb + xoff[t], sb + TW + (w + 8 * t) * 1024);
+    if constexpr (FP8) dma4(reinterpret_cast<const uint8_t *>(ascale + kc) + soff, sb + TW + WTX + 256 * w);
+  }
+
+  struct AFrag {
+    i32x4 l, h;
+  };
+  template <int NJ>
+  struct BFrags {
+    i32x4 bl[NJ], bh[NJ];
+    float sx[NJ];
+    float sa, sb;
+  };
+
+  __device__ __forceinline__ int arow(int i) const {
+    return (GATEUP ? (i < 4 ? 64 * wn + 16 * i : 128 + 64 * wn + 16 * (i - 4)) : 128 * wn + 16 * i) + (lane & 15);
+  }
+
+  __device__ __forceinline__ void read_a(const uint8_t *sb, int i, AFrag &A) const {
+    const int ck = 2 * (lane >> 4);
+    A.l = *reinterpret_cast<const i32x4 *>(sb + swz(arow(i), ck));
+    A.h = *reinterpret_cast<const i32x4 *>(sb + swz(arow(i), ck + 1));
+  }
+
+  template <int NJ>
+  __device__ __forceinline__ void read_b(const uint8_t *sb, const float *wsc, int kc, BFrags<NJ> &F) const {
+    const int ck = 2 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int r = 16 * (wm + 4 * j) + (lane & 15);
+      F.bl[j] = *reinterpret_cast<const i32x4 *>(sb + TW + swz(r, ck));
+      F.bh[j] = *reinterpret_cast<const i32x4 *>(sb + TW + swz(r, ck + 1));
+      // token r's scale sits in wave (r / 32)'s slot, lane r % 32
+      if constexpr (FP8) F.sx[j] = *reinterpret_cast<const float *>(sb + TW + WTX + 256 * (r >> 5) + 4 * (r & 31));
+    }
+    if constexpr (FP8) {
+      F.sa = GATEUP ? wsc[kc] : wsc[wn * KB + kc];
+      F.sb = GATEUP ? wsc[KB + kc] : F.sa;
+    }
+  }
+
+  // The MFMAs of one K chunk from stage buffer sb: token fragments read once,
+  // weight tile i+1's fragments read while tile i's MFMAs run.
+  template <int NJ>
+  __device__ __forceinline__ void chunk(const uint8_t *sb, const float *wsc, int kc, f32x4 (&acc)[8][4]) const {
+    BFrags<NJ> F;
+    read_b<NJ>(sb, wsc, kc, F);
+    AFrag A[2];
+    read_a(sb, 0, A[0]);
+    if constexpr (FP8) {
+      // raw block products are folded into the accumulators one MFMA behind
+      float sc[2][NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        sc[0][j] = F.sa * F.sx[j];
+        sc[1][j] = F.sb * F.sx[j];
+      }
+      constexpr int NT = 8 * NJ;
+      f32x4 prev = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t <= NT; ++t) {
+        f32x4 cur = {0.f, 0.f, 0.f, 0.f};
+        if (t < NT) {
+          const int i = t / NJ, j = t % NJ;
+          if (j == 0 && i + 1 < 8) read_a(sb, i + 1, A[(i + 1) & 1]);
+          const AFrag &a = A[i & 1];
+          const i32x8 a8 = {a.l[0], a.l[1], a.l[2], a.l[3], a.h[0], a.h[1], a.h[2], a.h[3]};
+          const i32x8 b8 = {F.bl[j][0], F.bl[j][1], F.bl[j][2], F.bl[j][3],
+                            F.bh[j][0], F.bh[j][1], F.bh[j][2], F.bh[j][3]};
+          cur = mfma_fp8(a8, b8, f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+        if (t > 0) {
+          const int i = (t - 1) / NJ, j = (t - 1) % NJ;
+          const float s = sc[(GATEUP && i >= 4) ? 1 : 0][j];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(prev[r], s, acc[i][j][r]);
+        }
+        prev = cur;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i + 1 < 8) read_a(sb, i + 1, A[(i + 1) & 1]);
+        const AFrag &a = A[i & 1];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          acc[i][j] = mfma_bf16(__builtin_bit_cast(bf16x8, a.l), __builtin_bit_cast(bf16x8, F.bl[j]), acc[i][j]);
+          acc[i][j] = mfma_bf16(__builtin_bit_cast(bf16x8, a.h), __builtin_bit_cast(bf16x8, F.bh[j]), acc[i][j]);
+        }
+      }
+    }
+  }
+
+  // The item's weight-block scales, staged in LDS before the copy ring starts.
+  __device__ __forceinline__ void load_wscales(float *wsc) const {
+    if constexpr (FP8) {
+      const float *s0, *s1;
+      if (GATEUP) {
+        s0 = G.sgu + ((int64_t)e * (2 * I / 128) + col0 / 128) * KB;
+        s1 = G.sgu + ((int64_t)e * (2 * I / 128) + (I + col0) / 128) * KB;
+      } else {
+        s0 = G.sd + ((int64_t)e * (H / 128) + col0 / 128) * KB;
+        s1 = G.sd + ((int64_t)e * (H / 128) + (col0 + 128) / 128) * KB;
+      }
+      for (int i = threadIdx.x; i < 2 * KB; i += WTHREADS) wsc[i] = i < KB ? s0[i] : s1[i - KB];
+    }
+  }
+
+  // Step kc: wait for this wave's copies of chunk kc, sync the workgroup
+  // (every wave's copies have landed, and nobody reads chunk kc-1's buffer any
+  // more), refill that buffer with chunk kc+1, consume chunk kc.
+  template <int NJ>
+  __device__ __forceinline__ void mainloop(uint8_t *lds, const float *wsc, f32x4 (&acc)[8][4]) const {
+    issue(0, lds);
+    for (int kc = 0; kc < nchunk; ++kc) {
+      wait_vm_lgkm0<0>();
+      wg_barrier();
+      if (kc + 1 < nchunk) issue(kc + 1, lds + ((kc + 1) & 1) * WSTAGE);
+      chunk<NJ>(lds + (kc & 1) * WSTAGE, wsc, kc, acc);
+    }
+  }
+};
+
+template <bool FP8, bool GATEUP>
+__device__ __forceinline__ void wide_item(const FfnGroup &G, const TileEntry &te, int ntile, int H, uint8_t *lds,
+                                          float *red, float *wsc) {
+  WideItem<FP8, GATEUP> it(G, te, ntile, H);
+  it.load_wscales(wsc);
+  __syncthreads();
+  const int lane = it.lane, wn = it.wn, wm = it.wm;
+  // active 16-row token slices of this wave: slice j covers rows 16*(wm + 4j)
+  const int nact = uniform(it.nvalid <= 16 * wm ? 0 : min(4, (it.nvalid - 16 * wm + 63) / 64));
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  switch (nact) {
+    case 4: it.template mainloop<4>(lds, wsc, acc); break;
+    case 3: it.template mainloop<3>(lds, wsc, acc); break;
+    case 2: it.template mainloop<2>(lds, wsc, acc); break;
+    case 1: it.template mainloop<1>(lds, wsc, acc); break;
+    default: it.template mainloop<1>(lds, wsc, acc); break;   // keeps the barrier count equal across waves
+  }
+  const int rbeg = it.rbeg, nvalid = it.nvalid, I = it.I, col0 = it.col0;
+  int brow[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) brow[j] = 16 * (wm + 4 * j);
+
+  // ---- epilogue.  Lane holds rows 4*(lane/16)+r of weight tile i for token
+  // slice j, token row = rbeg + brow[j] + lane%16.
+  if constexpr (GATEUP) {
+    float hv[4][4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hv[i][j][r] = swiglu(acc[i][j][r], acc[i + 4][j][r]);
+    if constexpr (!FP8) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tr = brow[j] + (lane & 15);
+        if (tr >= nvalid) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int col = col0 + 64 * wn + 16 * i + 4 * (lane >> 4);
+          const uint32_t lo = f32_to_bf16(hv[i][j][0]) | (f32_to_bf16(hv[i][j][1]) << 16);
+          const uint32_t hi = f32_to_bf16(hv[i][j][2]) | (f32_to_bf16(hv[i][j][3]) << 16);
+          *reinterpret_cast<uint2 *>(G.h + ((int64_t)(rbeg + tr) * I + col) * 2) = make_uint2(lo, hi);
+          if (G.z) {   // pre-activations kept for a backward
+            float *zr = G.z + (int64_t)(rbeg + tr) * 2 * I + col;
+            *reinterpret_cast<f32x4 *>(zr) = acc[i][j];
+            *reinterpret_cast<f32x4 *>(zr + I) = acc[i + 4][j];
+          }
+        }
+      }
+    } else {
+      // amax over the tile's 128 h columns per token: lane (16 values), the 4
+      // lanes of the token (xor 16, 32), then the two weight-half waves (LDS).
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float am = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) am = __builtin_fmaxf(am, __builtin_fabsf(hv[i][j][r]));
+        am = __builtin_fmaxf(am, __shfl_xor(am, 16, kWave));
+        am = __builtin_fmaxf(am, __shfl_xor(am, 32, kWave));
+        if (lane < 16) red[wn * WBM + brow[j] + lane] = am;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tr = brow[j] + (lane & 15);
+        const float s = group_scale(__builtin_fmaxf(red[tr], red[WBM + tr]));
+        const float inv = __builtin_amdgcn_rcpf(s);
+        if (tr >= nvalid) continue;
+        const int64_t row = rbeg + tr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int col = col0 + 64 * wn + 16 * i + 4 * (lane >> 4);
+          *reinterpret_cast<uint32_t *>(G.h + row * I + col) =
+              f32x4_to_e4m3(hv[i][j][0] * inv, hv[i][j][1] * inv, hv[i][j][2] * inv, hv[i][j][3] * inv);
+        }
+        if (wn == 0 && lane < 16) G.hs[row * (I / 128) + ntile] = s;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tr = brow[j] + (lane & 15);
+      if (tr >= nvalid) continue;
+      const int64_t row = rbeg + tr;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int col = col0 + 128 * wn + 16 * i + 4 * (lane >> 4);
+        const int64_t o = row * H + col;
+        if (G.y_f32) {
+          *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(G.y) + o) = acc[i][j];
+        } else {
+          const uint32_t lo = f32_to_bf16(acc[i][j][0]) | (f32_to_bf16(acc[i][j][1]) << 16);
+          const uint32_t hi = f32_to_bf16(acc[i][j][2]) | (f32_to_bf16(acc[i][j][3]) << 16);
+          *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(G.y) + o) = make_uint2(lo, hi);
+        }
+      }
+    }
+  }
+  __syncthreads();   // the next work item reuses the LDS ring and the reduction area
+}
+
 // Work item L -> (tile-list slot, column tile).  The slots of one expert are
 // taken in bands of up to TBAND token tiles, and the items of a band are
 // ordered column-tile-major: the 32 workgroups of an XCD that start
 // consecutive items share about four weight tiles and eight token tiles,
 // instead of one token tile's twelve weight tiles.
+template <int BM>
 __device__ __forceinline__ void map_item(const TiledArgs &a, int L, int &slot, int &ntile) {
   const int s = L / a.nt;
   const TileEntry te = a.tiles[s];
@@ -398,8 +715,8 @@ __device__ __forceinline__ void map_item(const TiledArgs &a, int L, int &slot, i
   const int e = te.ge & 0xFFFFFF;
   const int r0 = min(max(group_off(G, e), 0), G.nrows);
   const int r1 = min(max(group_off(G, e + 1), r0), G.nrows);
-  const int t = te.m0 / TBM, p = t % TBAND;
-  const int band = min(TBAND, (r1 - r0 + TBM - 1) / TBM - (t - p));
+  const int t = te.m0 / BM, p = t % TBAND;
+  const int band = min(TBAND, (r1 - r0 + BM - 1) / BM - (t - p));
   const int s0 = s - p, q = L - a.nt * s0;
   slot = s0 + q % max(band, 1);
   ntile = q / max(band, 1);
@@ -427,7 +744,7 @@ __global__ __launch_bounds__(TTHREADS, 1) void tiled_ffn_kernel(TiledArgs a) {
   const int beg = range_start(xcd, n0, count, a.c0, a.c1), end = range_start(xcd + 1, n0, count, a.c0, a.c1);
   for (int L = beg + slot0; L < end; L += per) {
     int slot, ntile;
-    map_item(a, L, slot, ntile);
+    map_item<TBM>(a, L, slot, ntile);
     if (slot < nslots) {
       const TileEntry te = a.tiles[slot];
       const FfnGroup G = (te.ge >> 24) ? a.g1 : a.g0;
@@ -441,8 +758,35 @@ __global__ __launch_bounds__(TTHREADS, 1) void tiled_ffn_kernel(TiledArgs a) {
   }
 }
 
+template <bool GATEUP>
+__global__ __launch_bounds__(WTHREADS, 1) void wide_ffn_kernel(TiledArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  float *red = reinterpret_cast<float *>(lds + WNSTAGE * WSTAGE);
+  float *wsc = red + 2 * WBM;
+  const int nslots = a.hdr[0];
+  const int count = nslots * a.nt;
+  const int64_t n0 = (int64_t)min(a.hdr[1], nslots) * a.nt;
+  const int xcd = blockIdx.x & 7, per = gridDim.x >> 3, slot0 = blockIdx.x >> 3;
+  const int beg = range_start(xcd, n0, count, a.c0, a.c1), end = range_start(xcd + 1, n0, count, a.c0, a.c1);
+  for (int L = beg + slot0; L < end; L += per) {
+    int slot, ntile;
+    map_item<WBM>(a, L, slot, ntile);
+    if (slot < nslots) {
+      const TileEntry te = a.tiles[slot];
+      const FfnGroup G = (te.ge >> 24) ? a.g1 : a.g0;
+      if (!(GATEUP && ntile * 128 >= G.I)) {
+        if (G.fp8)
+          wide_item<true, GATEUP>(G, te, ntile, a.H, lds, red, wsc);
+        else
+          wide_item<false, GATEUP>(G, te, ntile, a.H, lds, red, wsc);
+      }
+    }
+  }
+}
+
 // LDS: the copy ring, the h-scale reduction area, the weight-scale staging (H, I <= 16384)
 size_t tiled_lds_bytes() { return NSTAGE * TSTAGE + 2 * TBM * sizeof(float) + 2 * 128 * sizeof(float); }
+size_t wide_lds_bytes() { return WNSTAGE * WSTAGE + 2 * WBM * sizeof(float) + 2 * 128 * sizeof(float); }
 
 int num_compute_units() {
   static int cached[64] = {};
@@ -457,36 +801,47 @@ int num_compute_units() {
 }
 
 hipError_t launch_tiled_ffn(const FfnGroup *g, int ngroups, int H, const void *tiles, int32_t *hdr, int num_cus,
-                            int site, hipStream_t st) {
+                            int bm, int site, hipStream_t st) {
+  if (bm != 128 && bm != WBM) return hipErrorInvalidValue;
+  const bool wide = bm == WBM;
   TiledArgs a{g[0], ngroups > 1 ? g[1] : g[0], static_cast<const TileEntry *>(tiles), hdr, H, 0, 0, 0};
   auto chunks = [](const FfnGroup &G, int K) { return std::max(1, K * (G.fp8 ? 1 : 2) / 128); };
   int maxI = 0;
   for (int i = 0; i < ngroups; ++i) maxI = std::max(maxI, (int)g[i].I);
   const unsigned grid = (unsigned)(std::max(num_cus, 8) / 8 * 8);
-  const size_t lds = tiled_lds_bytes();
+  const size_t lds = wide ? wide_lds_bytes() : tiled_lds_bytes();
   static bool attr_set[64] = {};
   int dev = 0;
   (void)hipGetDevice(&dev);
   if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-    hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void *>(&tiled_ffn_kernel<true>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void *>(&tiled_ffn_kernel<false>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e1 != hipSuccess) return e1;
-    if (e2 != hipSuccess) return e2;
+    const void *fns[4] = {reinterpret_cast<const void *>(&tiled_ffn_kernel<true>),
+                          reinterpret_cast<const void *>(&tiled_ffn_kernel<false>),
+                          reinterpret_cast<const void *>(&wide_ffn_kernel<true>),
+                          reinterpret_cast<const void *>(&wide_ffn_kernel<false>)};
+    const size_t need[4] = {tiled_lds_bytes(), tiled_lds_bytes(), wide_lds_bytes(), wide_lds_bytes()};
+    for (int i = 0; i < 4; ++i) {
+      const hipError_t e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)need[i]);
+      if (e != hipSuccess) return e;
+    }
     attr_set[dev] = true;
   }
   a.nt = maxI / 128;
   a.c0 = chunks(a.g0, H);
   a.c1 = chunks(a.g1, H);
   timing_before(site, st);
-  tiled_ffn_kernel<true><<<grid, TTHREADS, lds, st>>>(a);
+  if (wide)
+    wide_ffn_kernel<true><<<grid, WTHREADS, lds, st>>>(a);
+  else
+    tiled_ffn_kernel<true><<<grid, TTHREADS, lds, st>>>(a);
   timing_after(site, st);
   a.nt = H / TBN;
   a.c0 = chunks(a.g0, a.g0.I);
   a.c1 = chunks(a.g1, a.g1.I);
   timing_before(site + 1, st);
-  tiled_ffn_kernel<false><<<grid, TTHREADS, lds, st>>>(a);
+  if (wide)
+    wide_ffn_kernel<false><<<grid, WTHREADS, lds, st>>>(a);
+  else
+    tiled_ffn_kernel<false><<<grid, TTHREADS, lds, st>>>(a);
   timing_after(site + 1, st);
   return hipGetLastError();
 }

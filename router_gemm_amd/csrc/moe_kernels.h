@@ -77,7 +77,7 @@ struct TileEntry {
   int32_t m0;
 };
 struct FfnPlan {
-  int tiled;       // 1: LDS-tiled persistent kernels (128-row token tiles; 64 for MX FP4), 0: streaming
+  int tiled;       // 1: LDS-tiled persistent kernels (128- or 256-row token tiles; 64 for MX FP4), 0: streaming
   int mt;          // streaming: 16-row token subtiles per workgroup
   int gw;          // streaming: gate (and up) 16-row weight tiles per wave (2 -> 128 h columns)
   int bm;          // token rows per tile-list entry
@@ -88,9 +88,10 @@ struct FfnPlan {
 constexpr int kTileHdrWords = 64;
 FfnPlan ffn_plan(const FfnGroup *g, int ngroups, int H);
 size_t ffn_tiles_bytes(const FfnPlan &p);
-// LDS-tiled variant (expert_gemm_tiled.hip); tiles built with 128-row entries.
+// LDS-tiled variant (expert_gemm_tiled.hip); tiles built with bm-row entries,
+// bm = 128 (256 x 128 work items, 4 waves) or 256 (256 x 256, 8 waves).
 hipError_t launch_tiled_ffn(const FfnGroup *g, int ngroups, int H, const void *tiles, int32_t *hdr, int num_cus,
-                            int site, hipStream_t st);
+                            int bm, int site, hipStream_t st);
 // LDS-tiled variant for MX FP4 weights (expert_gemm_tiled_mx.hip): one group,
 // tiles built with 64-row entries; needs H and I multiples of 256.
 bool tiled_mx_supported(const FfnGroup &g, int H);

@@ -345,11 +345,21 @@ def test_forward_small_full_parity(name):
     _print(f"forward {name}: {st}")
 
 
-@pytest.mark.parametrize("name,over", [("c0", dict(T=517, I=128, Is=128)), ("small_fp8", dict(T=389))])
+@pytest.mark.parametrize("name,over", [
+    ("c0", dict(T=517, I=128, Is=128)),                     # 128-row token tiles (mean 65 rows)
+    ("small_fp8", dict(T=389)),                             # 128-row token tiles (mean 97 rows)
+    ("c0", dict(T=1500, I=256, Is=128)),                    # 256-row token tiles (mean 188 rows)
+    ("small_fp8", dict(T=777)),                             # 256-row token tiles (mean 194 rows)
+    ("small_fp8", dict(T=1100, zipf_s=1.1, zipf_beta=0.6)),  # 256-row tiles, skewed: 1..4 tiles per expert
+])
 def test_forward_tiled_path_reads_rows_through_permutation(name, over):
     """Enough rows per expert (mean >= 48) for the LDS-tiled kernels, which read
     the routed rows through the sort permutation (bf16 x directly, fp8 x
-    quantised once per token) instead of a gathered copy; ragged T."""
+    quantised once per token) instead of a gathered copy; ragged T.  From a
+    mean of 128 rows per expert the token tiles are 256 rows (eight-wave
+    workgroups); the skewed case has experts with a few rows (waves whose
+    token slices are all past the end) next to experts spanning several
+    tiles."""
     cfg = W.get_config(name, **over)
     assert cfg.N / cfg.E >= 48 and cfg.I % 128 == 0 and cfg.Is % 128 == 0
     lt = W.make_layer(cfg, dev())
