@@ -7,13 +7,17 @@ synthetic tokens already resident in HBM.  Prints one JSON line.
 
   python bench.py [--workload decode_bf16|decode_fp8|decode_mxfp4|prefill_fp8|ep8_share_fp8|dense_ff_bf16|
                               train_bf16|small_bf16]
-                  [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                  [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--weight-layout tile16|rows]
 
 The default workload is the bf16 decode layer (T=64 tokens, hidden 4096,
 352 experts, top-8, intermediate 1536, one shared expert).  The dominant
 kernel's roofline figure comes from HIP events recorded around that kernel
 inside the timed steps (moe_timing.h); the CPU baseline is the fp64 oracle
 on a bounded sample of the same workload, on the host's cores.
+
+The routed experts' bf16 and fp8 weights are repacked once, before the timed
+region, into the 16-row tile layout (moe_pack_weights; --weight-layout rows
+keeps them row-major); MX FP4 and training workloads use row-major weights.
 """
 from __future__ import annotations
 
@@ -39,6 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--weight-layout", choices=["tile16", "rows"], default="tile16",
+                    help="storage of the routed experts' bf16/fp8 weights (packed once before timing)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run plain 1 GiB device copies only (reference dispatches for the HBM byte counters)")
@@ -136,6 +142,10 @@ def main():
     fp8 = cfg.expert_dtype != "bf16"     # activations and h stored as e4m3 + 1x128 scales
     mx = cfg.expert_dtype == "mxfp4"
     layer = B.Layer.from_tensors(lt, top_k=cfg.k if not cfg.triples else 0)
+    weight_layout = "rows" if (mx or args.weight_layout == "rows") else "tile16"
+    if weight_layout == "tile16":
+        layer = layer.packed()   # a load-time repack, outside the timed region
+        torch.cuda.synchronize()
     N = cfg.N
     y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
@@ -294,7 +304,7 @@ def main():
         "config": {"workload": cfg.name, "tokens": T, "hidden": H, "experts": E, "top_k": cfg.k,
                    "inter": I, "shared_inter": Is, "expert_dtype": cfg.expert_dtype,
                    "assignments": N, "active_experts": active, "max_rows_per_expert": int(counts.max()),
-                   "parallelism": "1 GPU"},
+                   "weight_layout": weight_layout, "parallelism": "1 GPU"},
         "layer": {"algorithmic_bytes": int(layer_bytes), "hbm_GBps": round(layer_bytes / t_s / 1e9, 1),
                   "hbm_frac": round(layer_bytes / t_s / 1e9 / PEAK_HBM_GBS, 4),
                   "tflops": round((fl_routed + fl_bf16) / t_s / 1e12, 2),

@@ -85,6 +85,26 @@ typedef enum moe_status {
   MOE_EHIP = 4           /* a HIP launch failed; moe_last_error() has the detail */
 } moe_status;
 
+/* Storage layout of the routed experts' w_gate_up and w_down
+ * (moe_layer.weight_layout; bf16 and fp8 experts).
+ *   MOE_LAYOUT_ROWS    row-major, as described under moe_layer (the default)
+ *   MOE_LAYOUT_TILE16  the same bytes permuted inside each expert's matrix
+ *                      (written by moe_pack_weights).  For an expert's matrix
+ *                      of R rows x K bytes (R = 2I or H; K = H or I times the
+ *                      element size), tile (t, c) -- rows 16t..16t+15, bytes
+ *                      128c..128c+127 of each -- is 2048 contiguous bytes at
+ *                      offset (c*R/16 + t)*2048 (the tiles of one 128-byte K
+ *                      chunk are adjacent), and byte b of its row 16t+i sits
+ *                      at 1024*((b/16)%2) + 16*(i + 16*(b/32)) + b%16.  Each
+ *                      16-byte load of an MFMA operand fragment then reads one
+ *                      whole contiguous kilobyte per wave.
+ * MX FP4 experts and the shared expert's weights are always row-major;
+ * moe_forward_train and moe_backward take MOE_LAYOUT_ROWS only. */
+typedef enum moe_weight_layout {
+  MOE_LAYOUT_ROWS = 0,
+  MOE_LAYOUT_TILE16 = 1
+} moe_weight_layout;
+
 /* One MoE layer (host struct; the pointers in it are device pointers).
  *   hidden H, inter I (routed expert intermediate), num_experts E (experts
  *   held here: 352 for the whole layer, 44 for one of eight expert-parallel
@@ -101,6 +121,7 @@ typedef enum moe_status {
  *   s_down          fp8: f32 [E, H/128, I/128]; mxfp4: E8M0 bytes [E, H, I/32];
  *                   bf16: NULL
  *   w_shared_gate_up bf16 [2Is, H], w_shared_down bf16 [H, Is] (NULL if Is == 0)
+ *   weight_layout   moe_weight_layout of w_gate_up and w_down (0: row-major)
  * Weights are read-only; they are the layout of a linear layer's weight
  * ([out, in]; y = a W^T). */
 typedef struct moe_layer {
@@ -118,7 +139,23 @@ typedef struct moe_layer {
   const void *s_down;
   const void *w_shared_gate_up;
   const void *w_shared_down;
+  int32_t weight_layout;
 } moe_layer;
+
+/* Repack `count` row-major matrices of `rows` rows x `row_bytes` bytes each
+ * (stored one after the other) into the MOE_LAYOUT_TILE16 layout (a
+ * permutation of their bytes; the layout the expert GEMMs of "Step-5 minimal
+ * inference" -- the block-scaled FP8 expert GEMM -- read fastest).  For a
+ * layer's experts: w_gate_up with count = E, rows = 2I, row_bytes = H *
+ * element size; w_down with count = E, rows = H, row_bytes = I * element
+ * size (the fp8 scale tensors keep their layout).
+ *   src, dst   device memory, 16-byte aligned, not overlapping; dst receives
+ *              count*rows*row_bytes bytes.  Owned by the caller.
+ * MOE_EINVAL: NULL or misaligned pointers, count <= 0, rows <= 0 or
+ * rows % 16 != 0, row_bytes <= 0 or row_bytes % 128 != 0.  A load-time
+ * step: enqueued on `stream` like every other call. */
+moe_status moe_pack_weights(const void *src, void *dst, int64_t count, int64_t rows, int64_t row_bytes,
+                            void *stream);
 
 /* Workspace bytes that suffice for every call below except moe_backward on
  * this layer with up to T tokens and N assignments (N = T*k for routed

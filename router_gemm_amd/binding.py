@@ -24,6 +24,7 @@ MOE_MXFP4_E2M1 = 4
 EXPERT_DTYPE = {"bf16": MOE_BF16, "fp8": MOE_FP8_E4M3FN, "mxfp4": MOE_MXFP4_E2M1}
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
+MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE16 = 0, 1
 
 _DT = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}
 
@@ -41,12 +42,13 @@ class MoELayerC(C.Structure):
                 ("w_router", C.c_void_p), ("router_bias", C.c_void_p),
                 ("w_gate_up", C.c_void_p), ("s_gate_up", C.c_void_p),
                 ("w_down", C.c_void_p), ("s_down", C.c_void_p),
-                ("w_shared_gate_up", C.c_void_p), ("w_shared_down", C.c_void_p)]
+                ("w_shared_gate_up", C.c_void_p), ("w_shared_down", C.c_void_p),
+                ("weight_layout", C.c_int32)]
 
 
 EXPORTS = ["moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
            "moe_forward", "moe_saved_z_floats", "moe_forward_train", "moe_backward_workspace_bytes",
-           "moe_backward", "moe_status_string",
+           "moe_backward", "moe_pack_weights", "moe_status_string",
            "moe_last_error", "moe_timing_arm", "moe_timing_read"]
 
 _lib = None
@@ -80,6 +82,8 @@ def lib() -> C.CDLL:
         L.moe_saved_z_floats.argtypes = [vp, i64]
         L.moe_forward_train.restype = C.c_int
         L.moe_forward_train.argtypes = [vp, vp, i64, vp, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_pack_weights.restype = C.c_int
+        L.moe_pack_weights.argtypes = [vp, vp, i64, i64, i64, vp]
         L.moe_status_string.restype = C.c_char_p
         L.moe_status_string.argtypes = [C.c_int]
         L.moe_last_error.restype = C.c_char_p
@@ -120,12 +124,13 @@ class Layer:
 
     def __init__(self, hidden, inter, num_experts, top_k, expert_dtype, w_gate_up, w_down,
                  s_gate_up=None, s_down=None, w_router=None, router_bias=None,
-                 w_shared_gate_up=None, w_shared_down=None, shared_inter=0):
+                 w_shared_gate_up=None, w_shared_down=None, shared_inter=0, weight_layout=MOE_LAYOUT_ROWS):
         self.tensors = [w_gate_up, w_down, s_gate_up, s_down, w_router, router_bias,
                         w_shared_gate_up, w_shared_down]
         self.c = MoELayerC(hidden, inter, num_experts, top_k, shared_inter, expert_dtype,
                            _ptr(w_router), _ptr(router_bias), _ptr(w_gate_up), _ptr(s_gate_up),
-                           _ptr(w_down), _ptr(s_down), _ptr(w_shared_gate_up), _ptr(w_shared_down))
+                           _ptr(w_down), _ptr(s_down), _ptr(w_shared_gate_up), _ptr(w_shared_down),
+                           weight_layout)
 
     @property
     def ref(self):
@@ -139,6 +144,18 @@ class Layer:
                    EXPERT_DTYPE[cfg.expert_dtype], lt.w_gate_up, lt.w_down,
                    lt.s_gate_up, lt.s_down, lt.w_router, lt.router_bias,
                    lt.w_shared_gate_up, lt.w_shared_down, cfg.Is if lt.w_shared_gate_up is not None else 0)
+
+    def packed(self, stream=None) -> "Layer":
+        """The same layer with the routed experts' weights repacked into
+        MOE_LAYOUT_TILE16 (new device tensors; this layer is unchanged)."""
+        c = self.c
+        wgu, wd = self.tensors[0], self.tensors[1]
+        esz = 1 if c.expert_dtype == MOE_FP8_E4M3FN else 2
+        pgu = pack_weights(wgu, c.num_experts, 2 * c.inter, c.hidden * esz, stream)
+        pd = pack_weights(wd, c.num_experts, c.hidden, c.inter * esz, stream)
+        t = self.tensors
+        return Layer(c.hidden, c.inter, c.num_experts, c.top_k, c.expert_dtype, pgu, pd, t[2], t[3], t[4], t[5],
+                     t[6], t[7], c.shared_inter, MOE_LAYOUT_TILE16)
 
     @classmethod
     def shared_view(cls, lt) -> "Layer":
@@ -195,6 +212,20 @@ def moe_forward(layer: Layer, x, T, y, out_dtype=None, topk_ids=None, topk_gates
     od = dtype_code(y) if out_dtype is None else out_dtype
     _check(lib().moe_forward(layer.ref, _ptr(x), T, _ptr(y), od, _ptr(topk_ids), _ptr(topk_gates),
                              w, nb, _stream(stream)))
+
+
+def moe_pack_weights(src, dst, count: int, rows: int, row_bytes: int, stream=None):
+    _check(lib().moe_pack_weights(_ptr(src), _ptr(dst), count, rows, row_bytes, _stream(stream)))
+
+
+def pack_weights(w: torch.Tensor, count: int, rows: int, row_bytes: int, stream=None) -> torch.Tensor:
+    """A new tensor holding w (count row-major [rows, row_bytes]-byte
+    matrices) in the MOE_LAYOUT_TILE16 layout (same dtype and shape as w)."""
+    if w.numel() * w.element_size() != count * rows * row_bytes:
+        raise ValueError("pack_weights: count * rows * row_bytes does not match the tensor")
+    out = torch.empty_like(w)
+    moe_pack_weights(w, out, count, rows, row_bytes, stream)
+    return out
 
 
 def moe_backward_workspace_bytes(layer: Layer, T: int) -> int:

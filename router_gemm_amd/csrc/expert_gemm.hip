@@ -92,6 +92,12 @@ struct Frag {
 };
 
 __device__ __forceinline__ Frag load_frag(const uint8_t *p) { return Frag{load16(p), load16(p + 16)}; }
+// The fragment of a tile16 weight tile: two 1 KB loads of the wave (lane l at
+// 16 l and 1024 + 16 l), non-temporal: every weight line is read once.
+__device__ __forceinline__ Frag load_frag_t16(const uint8_t *p) {
+  return Frag{__builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(p)),
+              __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(p + 1024))};
+}
 
 __device__ __forceinline__ i32x8 frag_fp8(const Frag &f) {
   return i32x8{f.lo[0], f.lo[1], f.lo[2], f.lo[3], f.hi[0], f.hi[1], f.hi[2], f.hi[3]};
@@ -184,9 +190,10 @@ __device__ __forceinline__ void tile_rows(const FfnGroup &G, const TileEntry &te
 // Workgroup: 4 waves x (GW gate + GW up 16-row weight tiles) = 64*GW h
 // columns x 16*MT token rows.  Each wave streams its own weight rows straight
 // from HBM into MFMA operand registers (no reuse across waves, so no LDS).
-template <bool FP8, bool MX, int MT, int GW>
+template <bool FP8, bool MX, int MT, int GW, bool T16 = false>
 __device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry &te, int H) {
   static_assert(FP8 || !MX, "MX weights take e4m3 activations");
+  static_assert(!(MX && T16), "MX weights are row-major");
   constexpr int ESZ = FP8 ? 1 : 2;
   const int lane = lane_id(), w = wave_id();
   int rbeg, rend;
@@ -205,8 +212,13 @@ __device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry 
 #pragma unroll
   for (int i = 0; i < GW; ++i) {
     const int64_t rg = hc0 + 16 * i + (lane & 15), ru = I + rg;
-    wg[i] = wbase + rg * wrowb + koff;
-    wu[i] = wbase + ru * wrowb + koff;
+    if constexpr (T16) {   // lane l reads 16 l (and 1024 + 16 l) of each tile
+      wg[i] = wbase + ((int64_t)(hc0 + 16 * i) >> 4) * 2048 + 16 * lane;
+      wu[i] = wbase + ((int64_t)(I + hc0 + 16 * i) >> 4) * 2048 + 16 * lane;
+    } else {
+      wg[i] = wbase + rg * wrowb + koff;
+      wu[i] = wbase + ru * wrowb + koff;
+    }
     if constexpr (MX) {
       mg[i] = G.mgu + ((int64_t)e * 2 * I + rg) * (H / 32);
       mu[i] = G.mgu + ((int64_t)e * 2 * I + ru) * (H / 32);
@@ -408,8 +420,13 @@ __device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry 
       Frag fg[GW], fu[GW], fx[MT];
 #pragma unroll
       for (int i = 0; i < GW; ++i) {
-        fg[i] = load_frag(wg[i] + kb);
-        fu[i] = load_frag(wu[i] + kb);
+        if constexpr (T16) {   // chunk c of all 2I rows: c * 2I * 128 bytes in
+          fg[i] = load_frag_t16(wg[i] + (int64_t)c * 2 * I * 128);
+          fu[i] = load_frag_t16(wu[i] + (int64_t)c * 2 * I * 128);
+        } else {
+          fg[i] = load_frag(wg[i] + kb);
+          fu[i] = load_frag(wu[i] + kb);
+        }
       }
       float sx[MT];
 #pragma unroll
@@ -499,7 +516,17 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(StreamArgs a) {
   const FfnGroup G = pick_group(a.g0, a.g1, te.ge >> 24);
   if ((int)blockIdx.x * 64 * GW >= G.I) return;     // group narrower than the grid
   if (G.fp8) {
-    if constexpr (GW == 2) gate_up_body<true, MXK, MT, GW>(G, te, a.H);
+    if constexpr (GW == 2) {
+      if constexpr (!MXK) {
+        if (G.tile16) {
+          gate_up_body<true, false, MT, GW, true>(G, te, a.H);
+          return;
+        }
+      }
+      gate_up_body<true, MXK, MT, GW>(G, te, a.H);
+    }
+  } else if (G.tile16) {
+    gate_up_body<false, false, MT, GW, true>(G, te, a.H);
   } else {
     gate_up_body<false, false, MT, GW>(G, te, a.H);
   }
@@ -507,9 +534,10 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(StreamArgs a) {
 
 // ---------------------------------------------------------------- down (streaming)
 // Workgroup: 4 waves x NW 16-column output tiles = 64*NW columns, 16*MT rows.
-template <bool FP8, bool MX, int MT, int NW>
+template <bool FP8, bool MX, int MT, int NW, bool T16 = false>
 __device__ __forceinline__ void down_body(const FfnGroup &G, const TileEntry &te, int H) {
   static_assert(FP8 || !MX, "MX weights take e4m3 activations");
+  static_assert(!(MX && T16), "MX weights are row-major");
   constexpr int ESZ = FP8 ? 1 : 2;
   const int lane = lane_id(), w = wave_id();
   int rbeg, rend;
@@ -527,7 +555,10 @@ __device__ __forceinline__ void down_body(const FfnGroup &G, const TileEntry &te
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
     const int64_t r = c0 + 16 * i + (lane & 15);
-    wr[i] = wbase + r * wrowb + koff;
+    if constexpr (T16)
+      wr[i] = wbase + ((int64_t)(c0 + 16 * i) >> 4) * 2048 + 16 * lane;
+    else
+      wr[i] = wbase + r * wrowb + koff;
     if constexpr (MX) mr[i] = G.md + ((int64_t)e * H + r) * (I / 32);
   }
   const uint8_t *hr[MT];
@@ -690,7 +721,7 @@ __device__ __forceinline__ void down_body(const FfnGroup &G, const TileEntry &te
       float sw[NW], sh[MT];
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
-        fw[i] = load_frag(wr[i] + kb);
+        fw[i] = T16 ? load_frag_t16(wr[i] + (int64_t)c * H * 128) : load_frag(wr[i] + kb);   // H rows per chunk
         sw[i] = FP8 ? G.sd[((int64_t)e * (H / 128) + (c0 + 16 * i) / 128) * KB + c] : 0.f;
       }
 #pragma unroll
@@ -727,10 +758,19 @@ __global__ __launch_bounds__(256) void down_stream_kernel(StreamArgs a) {
   if ((int)blockIdx.y >= a.ntiles[0]) return;
   const TileEntry te = a.tiles[blockIdx.y];
   const FfnGroup G = pick_group(a.g0, a.g1, te.ge >> 24);
-  if (G.fp8)
+  if (G.fp8) {
+    if constexpr (!MXK) {
+      if (G.tile16) {
+        down_body<true, false, MT, NW, true>(G, te, a.H);
+        return;
+      }
+    }
     down_body<true, MXK, MT, NW>(G, te, a.H);
-  else
+  } else if (G.tile16) {
+    down_body<false, false, MT, NW, true>(G, te, a.H);
+  } else {
     down_body<false, false, MT, NW>(G, te, a.H);
+  }
 }
 
 // ---------------------------------------------------------------- host side

@@ -55,11 +55,12 @@ struct TiledArgs {
 
 // One work item: a 256 x 128 output tile (gate/up: 128 gate + the matching 128
 // up rows = 128 h columns; down: 256 output columns) of one expert.
-template <bool FP8, bool GATEUP>
+template <bool FP8, bool GATEUP, bool T16>
 struct TiledItem {
   // ---- set up by the constructor
   const FfnGroup &G;
   int e, rbeg, rend, nvalid, I, K, KB, nchunk, col0, ntile, H;
+  int64_t wrows;   // rows of the expert's weight matrix (2I or H)
   int64_t rowb;
   const uint8_t *wsrc, *asrc;
   const float *ascale;
@@ -82,6 +83,7 @@ struct TiledItem {
     KB = K / 128;
     col0 = GATEUP ? ntile * 128 : ntile * TBN;
     wsrc = GATEUP ? G.wgu + (int64_t)e * 2 * I * rowb : G.wd + (int64_t)e * H * rowb;
+    wrows = GATEUP ? 2 * (int64_t)I : (int64_t)H;
     const bool indirect = GATEUP && G.xsrc != nullptr;
     asrc = (GATEUP ? G.x : G.h) + (indirect ? 0 : (int64_t)rbeg * rowb);
     ascale = (GATEUP ? G.xs : G.hs) + (FP8 && !indirect ? (int64_t)rbeg * KB : 0);
@@ -91,7 +93,15 @@ struct TiledItem {
       const int r = 8 * (w + 4 * q) + sub;
       const int c = (lane & 7) ^ swz_f(r);   // logical 16-byte column landing in this lane's slot
       const int grow = GATEUP ? (r < 128 ? col0 + r : I + col0 + r - 128) : col0 + r;
-      woff[q] = (uint32_t)(grow * rowb + c * 16);
+      if constexpr (T16) {
+        // tile16 weights: instruction j = w + 4q copies half j % 2 of the
+        // item's 16-row tile j / 2 verbatim (LDS keeps the fragment-major tile)
+        const int j = w + 4 * q, rt = 16 * (j >> 1);
+        const int g0 = GATEUP ? (rt < 128 ? col0 + rt : I + col0 + rt - 128) : col0 + rt;
+        woff[q] = (uint32_t)(((int64_t)g0 >> 4) * 2048 + 1024 * (j & 1) + 16 * lane);
+      } else {
+        woff[q] = (uint32_t)(grow * rowb + c * 16);
+      }
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -112,7 +122,7 @@ struct TiledItem {
   // Issue the direct-to-LDS copies of K chunk kc into stage buffer sb:
   // 8 (weights) + 4 (tokens) [+ 1 (token scales, fp8)] instructions per wave.
   __device__ __forceinline__ void issue(int kc, uint8_t *sb) const {
-    const uint8_t *wb = wsrc + (int64_t)kc * 128;   // uniform bases, per-lane 32-bit offsets
+    const uint8_t *wb = wsrc + (int64_t)kc * (T16 ? 128 * wrows : 128);   // uniform bases, per-lane 32-bit offsets
     const uint8_t *xb = asrc + (int64_t)kc * 128;
 #pragma unroll
     for (int q = 0; q < 8; ++q) dma16(wb + woff[q], sb + (w + 4 * q) * 1024);
@@ -140,9 +150,15 @@ struct TiledItem {
   }
 
   __device__ __forceinline__ void read_a(const uint8_t *sb, int i, AFrags &A) const {
-    const int ck = 2 * (lane >> 4);
-    A.al[i] = *reinterpret_cast<const i32x4 *>(sb + swz(arow(i), ck));
-    A.ah[i] = *reinterpret_cast<const i32x4 *>(sb + swz(arow(i), ck + 1));
+    if constexpr (T16) {   // fragment-major tile (arow(i) - lane % 16) / 16: lane l at 16 l and 1024 + 16 l
+      const uint8_t *t = sb + 128 * (arow(i) - (lane & 15)) + 16 * lane;
+      A.al[i] = *reinterpret_cast<const i32x4 *>(t);
+      A.ah[i] = *reinterpret_cast<const i32x4 *>(t + 1024);
+    } else {
+      const int ck = 2 * (lane >> 4);
+      A.al[i] = *reinterpret_cast<const i32x4 *>(sb + swz(arow(i), ck));
+      A.ah[i] = *reinterpret_cast<const i32x4 *>(sb + swz(arow(i), ck + 1));
+    }
   }
 
   template <int NJ>
@@ -276,10 +292,10 @@ struct TiledItem {
   }
 };
 
-template <bool FP8, bool GATEUP>
+template <bool FP8, bool GATEUP, bool T16>
 __device__ __forceinline__ void tiled_item(const FfnGroup &G, const TileEntry &te, int ntile, int H, uint8_t *lds,
                                            float *red, float *wsc) {
-  TiledItem<FP8, GATEUP> it(G, te, ntile, H);
+  TiledItem<FP8, GATEUP, T16> it(G, te, ntile, H);
   it.load_wscales(wsc);
   __syncthreads();
   const int lane = it.lane, wn = it.wn, wm = it.wm;
@@ -408,10 +424,11 @@ constexpr int WSTAGE = TW + WTX + WTSX;
 constexpr int WNSTAGE = 2;
 }  // namespace
 
-template <bool FP8, bool GATEUP>
+template <bool FP8, bool GATEUP, bool T16>
 struct WideItem {
   const FfnGroup &G;
   int e, rbeg, rend, nvalid, I, K, KB, nchunk, col0, ntile, H;
+  int64_t wrows;   // rows of the expert's weight matrix (2I or H)
   int64_t rowb;
   const uint8_t *wsrc, *asrc;
   const float *ascale;
@@ -434,6 +451,7 @@ struct WideItem {
     KB = K / 128;
     col0 = GATEUP ? ntile * 128 : ntile * TBN;
     wsrc = GATEUP ? G.wgu + (int64_t)e * 2 * I * rowb : G.wd + (int64_t)e * H * rowb;
+    wrows = GATEUP ? 2 * (int64_t)I : (int64_t)H;
     const bool indirect = GATEUP && G.xsrc != nullptr;
     asrc = (GATEUP ? G.x : G.h) + (indirect ? 0 : (int64_t)rbeg * rowb);
     ascale = (GATEUP ? G.xs : G.hs) + (FP8 && !indirect ? (int64_t)rbeg * KB : 0);
@@ -445,7 +463,15 @@ struct WideItem {
       const int r = 8 * (w + 8 * t) + sub;
       const int c = (lane & 7) ^ swz_f(r);   // logical 16-byte column landing in this lane's slot
       const int grow = GATEUP ? (r < 128 ? col0 + r : I + col0 + r - 128) : col0 + r;
-      woff[t] = (uint32_t)(grow * rowb + c * 16);
+      if constexpr (T16) {
+        // tile16 weights: instruction j = w + 8t copies half j % 2 of the
+        // item's 16-row tile j / 2 verbatim (LDS keeps the fragment-major tile)
+        const int j = w + 8 * t, rt = 16 * (j >> 1);
+        const int g0 = GATEUP ? (rt < 128 ? col0 + rt : I + col0 + rt - 128) : col0 + rt;
+        woff[t] = (uint32_t)(((int64_t)g0 >> 4) * 2048 + 1024 * (j & 1) + 16 * lane);
+      } else {
+        woff[t] = (uint32_t)(grow * rowb + c * 16);
+      }
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -466,7 +492,7 @@ struct WideItem {
   // Direct-to-LDS copies of K chunk kc into stage buffer sb: 4 (weights) +
   // 4 (tokens) [+ 1 (token scales, fp8)] instructions per wave.
   __device__ __forceinline__ void issue(int kc, uint8_t *sb) const {
-    const uint8_t *wb = wsrc + (int64_t)kc * 128;
+    const uint8_t *wb = wsrc + (int64_t)kc * (T16 ? 128 * wrows : 128);
     const uint8_t *xb = asrc + (int64_t)kc * 128;
 #pragma unroll
     for (int t = 0; t < 4; ++t) dma16(wb + woff[t], sb + (w + 8 * t) * 1024);
@@ -490,9 +516,15 @@ struct WideItem {
   }
 
   __device__ __forceinline__ void read_a(const uint8_t *sb, int i, AFrag &A) const {
-    const int ck = 2 * (lane >> 4);
-    A.l = *reinterpret_cast<const i32x4 *>(sb + swz(arow(i), ck));
-    A.h = *reinterpret_cast<const i32x4 *>(sb + swz(arow(i), ck + 1));
+    if constexpr (T16) {   // fragment-major tile (arow(i) - lane % 16) / 16: lane l at 16 l and 1024 + 16 l
+      const uint8_t *t = sb + 128 * (arow(i) - (lane & 15)) + 16 * lane;
+      A.l = *reinterpret_cast<const i32x4 *>(t);
+      A.h = *reinterpret_cast<const i32x4 *>(t + 1024);
+    } else {
+      const int ck = 2 * (lane >> 4);
+      A.l = *reinterpret_cast<const i32x4 *>(sb + swz(arow(i), ck));
+      A.h = *reinterpret_cast<const i32x4 *>(sb + swz(arow(i), ck + 1));
+    }
   }
 
   template <int NJ>
@@ -594,10 +626,10 @@ struct WideItem {
   }
 };
 
-template <bool FP8, bool GATEUP>
+template <bool FP8, bool GATEUP, bool T16>
 __device__ __forceinline__ void wide_item(const FfnGroup &G, const TileEntry &te, int ntile, int H, uint8_t *lds,
                                           float *red, float *wsc) {
-  WideItem<FP8, GATEUP> it(G, te, ntile, H);
+  WideItem<FP8, GATEUP, T16> it(G, te, ntile, H);
   it.load_wscales(wsc);
   __syncthreads();
   const int lane = it.lane, wn = it.wn, wm = it.wm;
@@ -749,10 +781,16 @@ __global__ __launch_bounds__(TTHREADS, 1) void tiled_ffn_kernel(TiledArgs a) {
       const TileEntry te = a.tiles[slot];
       const FfnGroup G = (te.ge >> 24) ? a.g1 : a.g0;
       if (!(GATEUP && ntile * 128 >= G.I)) {
-        if (G.fp8)
-          tiled_item<true, GATEUP>(G, te, ntile, a.H, lds, red, wsc);
-        else
-          tiled_item<false, GATEUP>(G, te, ntile, a.H, lds, red, wsc);
+        if (G.fp8) {
+          if (G.tile16)
+            tiled_item<true, GATEUP, true>(G, te, ntile, a.H, lds, red, wsc);
+          else
+            tiled_item<true, GATEUP, false>(G, te, ntile, a.H, lds, red, wsc);
+        } else if (G.tile16) {
+          tiled_item<false, GATEUP, true>(G, te, ntile, a.H, lds, red, wsc);
+        } else {
+          tiled_item<false, GATEUP, false>(G, te, ntile, a.H, lds, red, wsc);
+        }
       }
     }
   }
@@ -775,10 +813,16 @@ __global__ __launch_bounds__(WTHREADS, 1) void wide_ffn_kernel(TiledArgs a) {
       const TileEntry te = a.tiles[slot];
       const FfnGroup G = (te.ge >> 24) ? a.g1 : a.g0;
       if (!(GATEUP && ntile * 128 >= G.I)) {
-        if (G.fp8)
-          wide_item<true, GATEUP>(G, te, ntile, a.H, lds, red, wsc);
-        else
-          wide_item<false, GATEUP>(G, te, ntile, a.H, lds, red, wsc);
+        if (G.fp8) {
+          if (G.tile16)
+            wide_item<true, GATEUP, true>(G, te, ntile, a.H, lds, red, wsc);
+          else
+            wide_item<true, GATEUP, false>(G, te, ntile, a.H, lds, red, wsc);
+        } else if (G.tile16) {
+          wide_item<false, GATEUP, true>(G, te, ntile, a.H, lds, red, wsc);
+        } else {
+          wide_item<false, GATEUP, false>(G, te, ntile, a.H, lds, red, wsc);
+        }
       }
     }
   }

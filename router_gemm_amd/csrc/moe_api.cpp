@@ -85,6 +85,10 @@ moe_status check_layer_shape(const moe_layer *L, bool need_router) {
   if (need_router && (L->top_k < 1 || L->top_k > kMaxK || L->top_k > L->num_experts))
     return fail(MOE_EINVAL, "top_k %d outside [1, min(E=%d, %d)]", L->top_k, L->num_experts, kMaxK);
   if (L->top_k < 0 || L->top_k > kMaxK) return fail(MOE_EINVAL, "top_k %d outside [0, %d]", L->top_k, kMaxK);
+  if (L->weight_layout != MOE_LAYOUT_ROWS && L->weight_layout != MOE_LAYOUT_TILE16)
+    return fail(MOE_EINVAL, "weight_layout %d is not MOE_LAYOUT_ROWS or MOE_LAYOUT_TILE16", L->weight_layout);
+  if (L->weight_layout == MOE_LAYOUT_TILE16 && is_mx(L))
+    return fail(MOE_EUNSUPPORTED, "mxfp4 experts take row-major weights only");
   return MOE_OK;
 }
 
@@ -180,6 +184,7 @@ moe::FfnGroup routed_group(const moe_layer *L, const void *x_perm, const float *
   g.fp8 = is_fp8(L) ? 1 : 0;
   g.mx = is_mx(L) ? 1 : 0;
   g.y_f32 = y_f32 ? 1 : 0;
+  g.tile16 = L->weight_layout == MOE_LAYOUT_TILE16 ? 1 : 0;
   return g;
 }
 
@@ -528,6 +533,8 @@ moe_status moe_forward_train(const moe_layer *L, const void *x, int64_t T, void 
   moe_status s;
   if ((s = check_layer_shape(L, true)) != MOE_OK) return s;
   if (L->expert_dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "moe_forward_train needs bf16 experts");
+  if (L->weight_layout != MOE_LAYOUT_ROWS)
+    return fail(MOE_EUNSUPPORTED, "moe_forward_train takes row-major expert weights");
   if (T > 0 && (!topk_ids || !topk_gates || !z_saved))
     return fail(MOE_EINVAL, "moe_forward_train needs topk_ids, topk_gates and z_saved");
   if (T > 0 && !aligned16(z_saved)) return fail(MOE_EINVAL, "z_saved not 16-byte aligned");
@@ -547,6 +554,8 @@ moe_status moe_backward(const moe_layer *L, const void *x, int64_t T, const int3
   moe_status s;
   if ((s = check_layer_shape(L, true)) != MOE_OK) return s;
   if (L->expert_dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "moe_backward needs bf16 experts");
+  if (L->weight_layout != MOE_LAYOUT_ROWS)
+    return fail(MOE_EUNSUPPORTED, "moe_backward takes row-major expert weights");
   if ((s = check_rows(T, T * (int64_t)L->top_k)) != MOE_OK) return s;
   if (T > 0) {
     if (!x || !dy || !topk_ids || !topk_gates || !L->w_router) return fail(MOE_EINVAL, "NULL backward input");
@@ -621,6 +630,25 @@ moe_status moe_backward(const moe_layer *L, const void *x, int64_t T, const int3
   e = moe::launch_dx_backward(dx_shared, R.dx_rows, b.perm_pos, topk_ids, b.dl,
                               static_cast<const uint16_t *>(L->w_router), T, k, H, dx, st);
   return hip_status(e, "moe_backward: dx");
+}
+
+moe_status moe_pack_weights(const void *src, void *dst, int64_t count, int64_t rows, int64_t row_bytes,
+                            void *stream) {
+  if (!src || !dst) return fail(MOE_EINVAL, "moe_pack_weights: NULL pointer");
+  if (!aligned16(src) || !aligned16(dst)) return fail(MOE_EINVAL, "moe_pack_weights: pointers not 16-byte aligned");
+  if (count <= 0 || rows <= 0 || rows % 16 != 0 || row_bytes <= 0 || row_bytes % 128 != 0)
+    return fail(MOE_EINVAL,
+                "moe_pack_weights: count %lld must be positive, rows %lld a positive multiple of 16 and row_bytes "
+                "%lld of 128", (long long)count, (long long)rows, (long long)row_bytes);
+  if (rows > (int64_t)1 << 40 || row_bytes > (int64_t)1 << 40 || count > ((int64_t)1 << 62) / (rows * row_bytes))
+    return fail(MOE_EINVAL, "moe_pack_weights: size too large");
+  const uint8_t *a = static_cast<const uint8_t *>(src);
+  const uint8_t *b = static_cast<const uint8_t *>(dst);
+  const int64_t n = count * rows * row_bytes;
+  if (a < b + n && b < a + n) return fail(MOE_EINVAL, "moe_pack_weights: src and dst overlap");
+  return hip_status(
+      moe::launch_pack_tile16(a, static_cast<uint8_t *>(dst), count, rows, row_bytes, (hipStream_t)stream),
+      "moe_pack_weights");
 }
 
 }  // extern "C"

@@ -68,6 +68,14 @@ struct FfnGroup {
   // Optional (bf16 experts): [nrows, 2I] fp32, receives the gate/up
   // pre-activations of each row (gate half, then up half) for a backward.
   float *z;
+  // wgu and wd in the 16-row tile layout (bf16 and fp8 weights): in each
+  // expert's [R, K] matrix the 16 x 128-byte tile (t, c) -- rows 16t..16t+15,
+  // bytes 128c..128c+127 -- is 2048 contiguous bytes at (c * R/16 + t) * 2048
+  // (the tiles of one K chunk are adjacent); byte b of its row i sits at
+  // 1024 ((b / 16) % 2) + 16 (i + 16 (b / 32)) + b % 16, so that each of the
+  // two 16-byte loads of an MFMA fragment (lane l = row + 16 k-group) reads
+  // 1 KB of contiguous memory.
+  int32_t tile16;
 };
 constexpr int kMaxGroups = 2;
 // Tile list entry: group (0 or 1), expert of that group, first row (relative
@@ -105,6 +113,10 @@ hipError_t launch_expert_ffn(const FfnGroup *g, int ngroups, int H, const FfnPla
 
 // Tile list of a row-segmented grouped launch: bm-row entries over g's
 // experts (expert_gemm.hip).
+// Repack count row-major [rows, row_bytes] matrices into the tile16 layout
+// (layout.hip); rows % 16 == 0, row_bytes % 128 == 0.
+hipError_t launch_pack_tile16(const uint8_t *src, uint8_t *dst, int64_t count, int64_t rows, int64_t row_bytes,
+                              hipStream_t st);
 hipError_t launch_build_tiles(const FfnGroup &g, int bm, int max_tiles, TileEntry *tiles, int32_t *hdr,
                               hipStream_t st);
 

@@ -168,3 +168,36 @@ def test_forward_train_refusals_without_gpu():
     assert call(z=FAKE + 4) == B.MOE_EINVAL and b"aligned" in lib.moe_last_error()
     L = layer(dtype=B.MOE_FP8_E4M3FN)
     assert call() == B.MOE_EUNSUPPORTED
+
+
+def test_weight_layout_and_pack_refusals_without_gpu():
+    """weight_layout is 0 or 1, tile16 is refused for MX weights and for the
+    training calls; moe_pack_weights validates pointers and sizes first."""
+    lib = B.lib()
+
+    def with_layout(v, **kw):
+        L = layer(**kw)
+        L.weight_layout = v
+        return L
+
+    assert route(with_layout(B.MOE_LAYOUT_TILE16), T=0) == B.MOE_OK
+    assert route(with_layout(B.MOE_LAYOUT_TILE16, dtype=B.MOE_BF16), T=0) == B.MOE_OK
+    assert route(with_layout(2), T=0) == B.MOE_EINVAL
+    assert route(with_layout(-1), T=0) == B.MOE_EINVAL
+    assert route(with_layout(B.MOE_LAYOUT_TILE16, dtype=B.MOE_MXFP4_E2M1), T=0) == B.MOE_EUNSUPPORTED
+    L = with_layout(B.MOE_LAYOUT_TILE16, dtype=B.MOE_BF16)
+    r = lib.moe_backward(C.byref(L), FAKE, 64, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                         FAKE, 1 << 40, None)
+    assert r == B.MOE_EUNSUPPORTED and b"row-major" in lib.moe_last_error()
+    r = lib.moe_forward_train(C.byref(L), FAKE, 64, FAKE, B.MOE_BF16, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert r == B.MOE_EUNSUPPORTED and b"row-major" in lib.moe_last_error()
+    pack = lambda src=FAKE, dst=FAKE + (1 << 24), n=1, rows=16, rb=128: lib.moe_pack_weights(src, dst, n, rows, rb,
+                                                                                              None)
+    assert pack(src=None) == B.MOE_EINVAL
+    assert pack(dst=None) == B.MOE_EINVAL
+    assert pack(src=FAKE + 8) == B.MOE_EINVAL and b"aligned" in lib.moe_last_error()
+    for n, rows, rb in ((1, 15, 128), (1, 0, 128), (1, -16, 128), (1, 16, 64), (1, 16, 0), (1, 32, 200), (0, 16, 128),
+                        (-1, 16, 128), (1 << 40, 1 << 20, 1 << 20)):
+        assert pack(n=n, rows=rows, rb=rb) == B.MOE_EINVAL, (n, rows, rb)
+    assert pack(dst=FAKE + 1024) == B.MOE_EINVAL and b"overlap" in lib.moe_last_error()
+    assert pack(n=2, dst=FAKE + 2048) == B.MOE_EINVAL and b"overlap" in lib.moe_last_error()
