@@ -56,22 +56,22 @@ def parse():
 # 1 GiB device copy (bench.py --copy-calibration).  Valid only for the kernel sources they were
 # taken on: a different hash of the dominant kernel's sources (KERNEL_SOURCES) reports null.
 TRAFFIC = {
-    "decode_bf16": {"src_hash": "f7fe5ff773ec3dd2", "fetch_kib": 3308694.4, "write_kib": 1883.1193, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_fp8": {"src_hash": "f7fe5ff773ec3dd2", "fetch_kib": 1664782.2, "write_kib": 1184.9233, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_mxfp4": {"src_hash": "f7fe5ff773ec3dd2", "fetch_kib": 901014.14, "write_kib": 1183.3466, "fetch_scale": 2.0, "write_scale": 1.0},
-    "dense_ff_bf16": {"src_hash": "f7fe5ff773ec3dd2", "fetch_kib": 1779403.7, "write_kib": 221184.0, "fetch_scale": 2.0, "write_scale": 1.0},
-    "prefill_fp8": {"src_hash": "f7fe5ff773ec3dd2", "fetch_kib": 4419077.4, "write_kib": 140285.07, "fetch_scale": 2.0, "write_scale": 1.0},
-    "train_bf16": {"src_hash": "788118b9938d5ab5", "fetch_kib": 4393799.8, "write_kib": 26323206.0, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_bf16": {"src_hash": "a1fbeaa3c19f4726", "fetch_kib": 3274962.9, "write_kib": 1737.8608, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_fp8": {"src_hash": "a1fbeaa3c19f4726", "fetch_kib": 1651566.0, "write_kib": 1142.9403, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_mxfp4": {"src_hash": "a1fbeaa3c19f4726", "fetch_kib": 902069.74, "write_kib": 1183.429, "fetch_scale": 2.0, "write_scale": 1.0},
+    "dense_ff_bf16": {"src_hash": "a1fbeaa3c19f4726", "fetch_kib": 1360433.8, "write_kib": 223773.8, "fetch_scale": 2.0, "write_scale": 1.0},
+    "prefill_fp8": {"src_hash": "a1fbeaa3c19f4726", "fetch_kib": 3328990.5, "write_kib": 139244.69, "fetch_scale": 2.0, "write_scale": 1.0},
+    "train_bf16": {"src_hash": "2a9aad1ca9d35755", "fetch_kib": 4398337.5, "write_kib": 26398060.0, "fetch_scale": 2.0, "write_scale": 1.0},
 }
 
 
 # Sources that decide what the dominant kernel of a workload does (its code,
 # the structures it reads, the launch plan): the forward's grouped gate/up
 # kernels, or the backward's weight-gradient kernel.
-KERNEL_SOURCES = {
-    "forward": ["expert_gemm.hip", "expert_gemm_tiled.hip", "expert_gemm_tiled_mx.hip", "moe_common.h",
-                "moe_kernels.h", "moe_api.cpp"],
-    "backward": ["backward.hip", "moe_common.h", "moe_kernels.h", "moe_api.cpp"],
+KERNEL_SOURCES = {   # relative to router_gemm_amd/csrc (build.py holds the compiler flags)
+    "forward": ["expert_gemm.hip", "expert_gemm_tiled.hip", "expert_gemm_tiled_mx.hip", "layout.hip", "moe_common.h",
+                "moe_kernels.h", "moe_api.cpp", "../build.py"],
+    "backward": ["backward.hip", "moe_common.h", "moe_kernels.h", "moe_api.cpp", "../build.py"],
 }
 
 
@@ -307,7 +307,7 @@ def main():
                    "weight_layout": weight_layout, "parallelism": "1 GPU"},
         "layer": {"algorithmic_bytes": int(layer_bytes), "hbm_GBps": round(layer_bytes / t_s / 1e9, 1),
                   "hbm_frac": round(layer_bytes / t_s / 1e9 / PEAK_HBM_GBS, 4),
-                  "tflops": round((fl_routed + fl_bf16) / t_s / 1e12, 2),
+                  "tflops": round((fl_routed_fp8 + fl_bf16) / t_s / 1e12, 2),
                   "mfma_util_blended": round(mfma_util, 4), "wall_s": round(wall, 4)},
         "roofline": roof,
         "breakdown_us_per_step": breakdown,
