@@ -78,6 +78,44 @@ def test_packed_forward_equals_row_major(name, over):
     assert torch.equal(y0, y1), float((y0 - y1).abs().max())
 
 
+@pytest.mark.parametrize("name,over", [("small_bf16", {}), ("small_fp8", dict(T=777))])
+def test_packed_forward_bf16_output(name, over):
+    """bf16 output (the rounding of the combine's fp32 sums) is the same too."""
+    cfg = dataclasses.replace(W.get_config(name), **over)
+    lt = W.make_layer(cfg, dev())
+    x = W.make_x(cfg, dev())
+    layer = B.Layer.from_tensors(lt)
+    out = []
+    for L in (layer, layer.packed()):
+        y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev())
+        B.moe_forward(L, x, cfg.T, y, ws=B.workspace(L, cfg.T, cfg.N, dev()))
+        torch.cuda.synchronize()
+        out.append(y)
+    assert torch.equal(out[0], out[1])
+
+
+def test_packed_pre_routed_expert_ffn():
+    """moe_expert_ffn on pre-routed rows of many experts (the expert-parallel
+    share's call): 44 fp8 experts, 3000 rows with Zipf-like loads."""
+    cfg = dataclasses.replace(W.get_config("small_fp8"), E=44, k=0)
+    lt = W.make_layer(cfg, dev())
+    rng = np.random.default_rng(9)
+    counts = np.maximum(1, (3000 / np.arange(1, 45) ** 1.1 / np.sum(1 / np.arange(1, 45) ** 1.1))).astype(int)
+    N = int(counts.sum())
+    off = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(dev())
+    xq = torch.from_numpy(rng.integers(0, 0x7f, (N, cfg.H), dtype=np.uint8)).to(dev())   # finite e4m3 codes
+    xs = torch.from_numpy(rng.uniform(0.5, 2.0, (N, cfg.H // 128)).astype(np.float32)).to(dev())
+    layer = B.Layer.from_tensors(lt, top_k=0)
+    out = []
+    for L in (layer, layer.packed()):
+        y = torch.empty((N, cfg.H), dtype=torch.float32, device=dev())
+        B.moe_expert_ffn(L, off, xq, xs, N, y, ws=B.workspace(L, N, N, dev()))
+        torch.cuda.synchronize()
+        out.append(y)
+    assert torch.isfinite(out[0]).all()
+    assert torch.equal(out[0], out[1])
+
+
 def test_packed_expert_ffn_one_expert():
     """moe_expert_ffn on a one-expert layer (the dense FF layer's call): 300
     rows over a 2560-wide intermediate, bf16."""
