@@ -56,12 +56,12 @@ def parse():
 # 1 GiB device copy (bench.py --copy-calibration).  Valid only for the kernel sources they were
 # taken on: a different hash of the dominant kernel's sources (KERNEL_SOURCES) reports null.
 TRAFFIC = {
-    "decode_bf16": {"src_hash": "359693ec67ca2285", "fetch_kib": 3274962.9, "write_kib": 1737.8608, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_fp8": {"src_hash": "359693ec67ca2285", "fetch_kib": 1651566.0, "write_kib": 1142.9403, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_mxfp4": {"src_hash": "359693ec67ca2285", "fetch_kib": 902069.74, "write_kib": 1183.429, "fetch_scale": 2.0, "write_scale": 1.0},
-    "dense_ff_bf16": {"src_hash": "359693ec67ca2285", "fetch_kib": 1360433.8, "write_kib": 223773.8, "fetch_scale": 2.0, "write_scale": 1.0},
-    "prefill_fp8": {"src_hash": "359693ec67ca2285", "fetch_kib": 3328990.5, "write_kib": 139244.69, "fetch_scale": 2.0, "write_scale": 1.0},
-    "train_bf16": {"src_hash": "4f96340a864f115c", "fetch_kib": 4398337.5, "write_kib": 26398060.0, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_bf16": {"src_hash": "a207159d7d8c0496", "fetch_kib": 3274981.4, "write_kib": 1738.7557, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_fp8": {"src_hash": "a207159d7d8c0496", "fetch_kib": 1651565.1, "write_kib": 1143.0369, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_mxfp4": {"src_hash": "a207159d7d8c0496", "fetch_kib": 901931.72, "write_kib": 1184.2812, "fetch_scale": 2.0, "write_scale": 1.0},
+    "dense_ff_bf16": {"src_hash": "a207159d7d8c0496", "fetch_kib": 1360456.4, "write_kib": 223783.5, "fetch_scale": 2.0, "write_scale": 1.0},
+    "prefill_fp8": {"src_hash": "a207159d7d8c0496", "fetch_kib": 3332139.3, "write_kib": 139351.34, "fetch_scale": 2.0, "write_scale": 1.0},
+    "train_bf16": {"src_hash": "4f96340a864f115c", "fetch_kib": 4397870.4, "write_kib": 26396252.0, "fetch_scale": 2.0, "write_scale": 1.0},
 }
 
 

@@ -297,34 +297,15 @@ struct TiledItem {
   }
 };
 
-template <bool FP8, bool GATEUP, bool T16>
-__device__ __forceinline__ void tiled_item(const FfnGroup &G, const TileEntry &te, int ntile, int H, uint8_t *lds,
-                                           float *red, float *wsc) {
-  TiledItem<FP8, GATEUP, T16> it(G, te, ntile, H);
-  it.load_wscales(wsc);
-  __syncthreads();
-  const int lane = it.lane, wn = it.wn, wm = it.wm;
-  // active 16-row token slices of this wave: slice j covers rows 16*(wm + 2j)
-  const int nact = uniform(it.nvalid <= 16 * wm ? 0 : min(4, (it.nvalid - 16 * wm + 31) / 32));
-  f32x4 acc[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  switch (nact) {
-    case 4: it.template mainloop<4>(lds, wsc, acc); break;
-    case 3: it.template mainloop<3>(lds, wsc, acc); break;
-    case 2: it.template mainloop<2>(lds, wsc, acc); break;
-    case 1: it.template mainloop<1>(lds, wsc, acc); break;
-    default: it.template mainloop<1>(lds, wsc, acc); break;   // keeps the barrier count equal across waves
-  }
-  const int rbeg = it.rbeg, nvalid = it.nvalid, I = it.I, col0 = it.col0;
-  int brow[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) brow[j] = 16 * (wm + 2 * j);
-
-  // ---- epilogue.  Lane holds rows 4*(lane/16)+r of weight tile i for token
-  // slice j, token row = rbeg + brow[j] + lane%16.
+// Epilogue of a work item: lane holds rows 4*(lane/16)+r of weight tile i for
+// token slice j (token row rbeg + brow[j] + lane%16).  gate/up: SwiGLU, then h
+// as bf16 (and the pre-activations when asked) or as e4m3 with one scale per
+// token per 128 columns (amax over the two weight-half waves through `red`,
+// 2 x BM floats); down: the output rows.
+template <bool FP8, bool GATEUP, int BM>
+__device__ __forceinline__ void store_item(const FfnGroup &G, const f32x4 (&acc)[8][4], const int (&brow)[4],
+                                           int lane, int wn, int rbeg, int nvalid, int I, int col0, int ntile,
+                                           int H, float *red) {
   if constexpr (GATEUP) {
     float hv[4][4][4];
 #pragma unroll
@@ -332,9 +313,7 @@ __device__ __forceinline__ void tiled_item(const FfnGroup &G, const TileEntry &t
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          hv[i][j][r] = swiglu(acc[i][j][r], acc[i + 4][j][r]);
-        }
+        for (int r = 0; r < 4; ++r) hv[i][j][r] = swiglu(acc[i][j][r], acc[i + 4][j][r]);
     if constexpr (!FP8) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -365,13 +344,13 @@ __device__ __forceinline__ void tiled_item(const FfnGroup &G, const TileEntry &t
           for (int r = 0; r < 4; ++r) am = __builtin_fmaxf(am, __builtin_fabsf(hv[i][j][r]));
         am = __builtin_fmaxf(am, __shfl_xor(am, 16, kWave));
         am = __builtin_fmaxf(am, __shfl_xor(am, 32, kWave));
-        if (lane < 16) red[wn * TBM + brow[j] + lane] = am;
+        if (lane < 16) red[wn * BM + brow[j] + lane] = am;
       }
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int tr = brow[j] + (lane & 15);
-        const float s = group_scale(__builtin_fmaxf(red[tr], red[TBM + tr]));
+        const float s = group_scale(__builtin_fmaxf(red[tr], red[BM + tr]));
         const float inv = __builtin_amdgcn_rcpf(s);
         if (tr >= nvalid) continue;
         const int64_t row = rbeg + tr;
@@ -404,6 +383,35 @@ __device__ __forceinline__ void tiled_item(const FfnGroup &G, const TileEntry &t
       }
     }
   }
+}
+
+template <bool FP8, bool GATEUP, bool T16>
+__device__ __forceinline__ void tiled_item(const FfnGroup &G, const TileEntry &te, int ntile, int H, uint8_t *lds,
+                                           float *red, float *wsc) {
+  TiledItem<FP8, GATEUP, T16> it(G, te, ntile, H);
+  it.load_wscales(wsc);
+  __syncthreads();
+  const int lane = it.lane, wn = it.wn, wm = it.wm;
+  // active 16-row token slices of this wave: slice j covers rows 16*(wm + 2j)
+  const int nact = uniform(it.nvalid <= 16 * wm ? 0 : min(4, (it.nvalid - 16 * wm + 31) / 32));
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  switch (nact) {
+    case 4: it.template mainloop<4>(lds, wsc, acc); break;
+    case 3: it.template mainloop<3>(lds, wsc, acc); break;
+    case 2: it.template mainloop<2>(lds, wsc, acc); break;
+    case 1: it.template mainloop<1>(lds, wsc, acc); break;
+    default: it.template mainloop<1>(lds, wsc, acc); break;   // keeps the barrier count equal across waves
+  }
+  const int rbeg = it.rbeg, nvalid = it.nvalid, I = it.I, col0 = it.col0;
+  int brow[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) brow[j] = 16 * (wm + 2 * j);
+
+  store_item<FP8, GATEUP, TBM>(G, acc, brow, lane, wn, rbeg, nvalid, I, col0, ntile, H, red);
   __syncthreads();   // the next work item reuses the LDS ring and the reduction area
 }
 
@@ -657,85 +665,7 @@ __device__ __forceinline__ void wide_item(const FfnGroup &G, const TileEntry &te
 #pragma unroll
   for (int j = 0; j < 4; ++j) brow[j] = 16 * (wm + 4 * j);
 
-  // ---- epilogue.  Lane holds rows 4*(lane/16)+r of weight tile i for token
-  // slice j, token row = rbeg + brow[j] + lane%16.
-  if constexpr (GATEUP) {
-    float hv[4][4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hv[i][j][r] = swiglu(acc[i][j][r], acc[i + 4][j][r]);
-    if constexpr (!FP8) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tr = brow[j] + (lane & 15);
-        if (tr >= nvalid) continue;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int col = col0 + 64 * wn + 16 * i + 4 * (lane >> 4);
-          const uint32_t lo = f32_to_bf16(hv[i][j][0]) | (f32_to_bf16(hv[i][j][1]) << 16);
-          const uint32_t hi = f32_to_bf16(hv[i][j][2]) | (f32_to_bf16(hv[i][j][3]) << 16);
-          *reinterpret_cast<uint2 *>(G.h + ((int64_t)(rbeg + tr) * I + col) * 2) = make_uint2(lo, hi);
-          if (G.z) {   // pre-activations kept for a backward
-            float *zr = G.z + (int64_t)(rbeg + tr) * 2 * I + col;
-            *reinterpret_cast<f32x4 *>(zr) = acc[i][j];
-            *reinterpret_cast<f32x4 *>(zr + I) = acc[i + 4][j];
-          }
-        }
-      }
-    } else {
-      // amax over the tile's 128 h columns per token: lane (16 values), the 4
-      // lanes of the token (xor 16, 32), then the two weight-half waves (LDS).
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float am = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) am = __builtin_fmaxf(am, __builtin_fabsf(hv[i][j][r]));
-        am = __builtin_fmaxf(am, __shfl_xor(am, 16, kWave));
-        am = __builtin_fmaxf(am, __shfl_xor(am, 32, kWave));
-        if (lane < 16) red[wn * WBM + brow[j] + lane] = am;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tr = brow[j] + (lane & 15);
-        const float s = group_scale(__builtin_fmaxf(red[tr], red[WBM + tr]));
-        const float inv = __builtin_amdgcn_rcpf(s);
-        if (tr >= nvalid) continue;
-        const int64_t row = rbeg + tr;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int col = col0 + 64 * wn + 16 * i + 4 * (lane >> 4);
-          *reinterpret_cast<uint32_t *>(G.h + row * I + col) =
-              f32x4_to_e4m3(hv[i][j][0] * inv, hv[i][j][1] * inv, hv[i][j][2] * inv, hv[i][j][3] * inv);
-        }
-        if (wn == 0 && lane < 16) G.hs[row * (I / 128) + ntile] = s;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tr = brow[j] + (lane & 15);
-      if (tr >= nvalid) continue;
-      const int64_t row = rbeg + tr;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int col = col0 + 128 * wn + 16 * i + 4 * (lane >> 4);
-        const int64_t o = row * H + col;
-        if (G.y_f32) {
-          *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(G.y) + o) = acc[i][j];
-        } else {
-          const uint32_t lo = f32_to_bf16(acc[i][j][0]) | (f32_to_bf16(acc[i][j][1]) << 16);
-          const uint32_t hi = f32_to_bf16(acc[i][j][2]) | (f32_to_bf16(acc[i][j][3]) << 16);
-          *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(G.y) + o) = make_uint2(lo, hi);
-        }
-      }
-    }
-  }
+  store_item<FP8, GATEUP, WBM>(G, acc, brow, lane, wn, rbeg, nvalid, I, col0, ntile, H, red);
   __syncthreads();   // the next work item reuses the LDS ring and the reduction area
 }
 
