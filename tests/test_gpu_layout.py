@@ -59,6 +59,9 @@ CASES = [
     ("small_bf16", {}),                                   # streaming, bf16, two gate tiles per wave
     ("small_bf16", dict(I=192, Is=64)),                   # streaming, bf16, I % 128 != 0: one gate tile per wave
     ("small_fp8", {}),                                    # streaming, fp8
+    ("small_bf16", dict(T=1)),                            # one token
+    ("small_fp8", dict(T=1, E=4, k=1)),                   # one token, one expert per token
+    ("small_bf16", dict(I=64, Is=64)),                    # the narrowest bf16 experts (one 64-column tile)
     ("small_bf16", dict(T=517, I=128, Is=128)),           # LDS-tiled, 128-row token tiles
     ("small_fp8", dict(T=389)),                           # LDS-tiled, 128-row token tiles, fp8
     ("small_bf16", dict(T=1500, I=256, Is=128)),          # LDS-tiled, 256-row token tiles
