@@ -61,6 +61,7 @@ TRAFFIC = {
     "decode_mxfp4": {"src_hash": "a207159d7d8c0496", "fetch_kib": 901931.72, "write_kib": 1184.2812, "fetch_scale": 2.0, "write_scale": 1.0},
     "dense_ff_bf16": {"src_hash": "a207159d7d8c0496", "fetch_kib": 1360456.4, "write_kib": 223783.5, "fetch_scale": 2.0, "write_scale": 1.0},
     "prefill_fp8": {"src_hash": "a207159d7d8c0496", "fetch_kib": 3332139.3, "write_kib": 139351.34, "fetch_scale": 2.0, "write_scale": 1.0},
+    "ep8_share_fp8": {"src_hash": "a207159d7d8c0496", "fetch_kib": 377384.14, "write_kib": 40499.205, "fetch_scale": 2.0, "write_scale": 1.0},
     "train_bf16": {"src_hash": "4f96340a864f115c", "fetch_kib": 4397870.4, "write_kib": 26396252.0, "fetch_scale": 2.0, "write_scale": 1.0},
 }
 
