@@ -16,8 +16,9 @@
  *
  * Conventions for every call
  *   - Pointers are DEVICE pointers unless stated otherwise; tensors are
- *     row-major and contiguous, 16-byte aligned.  `stream` is a hipStream_t
- *     passed as void* (NULL = the null stream).
+ *     row-major and contiguous, 16-byte aligned (the routed experts' weights
+ *     may instead be in the tile16 layout: moe_weight_layout below).
+ *     `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *   - The caller owns every buffer (inputs, outputs, workspace).  The library
  *     allocates and frees nothing and keeps no device state between calls.
  *     Calls on distinct streams with distinct workspaces may run concurrently.
