@@ -169,8 +169,13 @@ static void token_logits(const oref_layer *L, const uint16_t *xr, double *l) {
   }
 }
 
+/* The value a logit is ranked by: a NaN logit ranks as -infinity (below every
+ * number; among equal values the lower expert index comes first). */
+static inline double rank_value(double v) { return isnan(v) ? -INFINITY : v; }
+
 /* k largest of l[0..E) ordered by (value desc, index asc); then slots sorted
- * by ascending expert id.  Returns the gap l_(k) - l_(k+1). */
+ * by ascending expert id.  Returns the gap l_(k) - l_(k+1) (0 when the two
+ * are equal, infinities included). */
 static double select_topk(const double *l, int E, int k, int32_t *ids) {
   char *taken = (char *)calloc((size_t)E, 1);
   double kth = 0.0;
@@ -178,16 +183,16 @@ static double select_topk(const double *l, int E, int k, int32_t *ids) {
     int best = -1;
     for (int e = 0; e < E; ++e) {
       if (taken[e]) continue;
-      if (best < 0 || l[e] > l[best]) best = e;   /* strict: lower index keeps ties */
+      if (best < 0 || rank_value(l[e]) > rank_value(l[best])) best = e;   /* strict: lower index keeps ties */
     }
     taken[best] = 1;
     ids[j] = best;
-    kth = l[best];
+    kth = rank_value(l[best]);
   }
   double next = -INFINITY;
   int have_next = 0;
   for (int e = 0; e < E; ++e)
-    if (!taken[e] && (!have_next || l[e] > next)) { next = l[e]; have_next = 1; }
+    if (!taken[e] && (!have_next || rank_value(l[e]) > next)) { next = rank_value(l[e]); have_next = 1; }
   free(taken);
   /* insertion sort of the k chosen ids, ascending */
   for (int a = 1; a < k; ++a) {
@@ -196,16 +201,25 @@ static double select_topk(const double *l, int E, int k, int32_t *ids) {
     while (b >= 0 && ids[b] > v) { ids[b + 1] = ids[b]; --b; }
     ids[b + 1] = v;
   }
-  return have_next ? kth - next : INFINITY;
+  if (!have_next) return INFINITY;
+  return kth == next ? 0.0 : kth - next;   /* equal values, infinite ones too: a tie */
 }
 
-/* softmax over the chosen logits == full softmax renormalised over them */
+/* softmax over the chosen logits == full softmax renormalised over them.
+ * Logits are taken at their rank value (NaN as -infinity); a logit equal to
+ * the largest chosen one weighs exp(0) = 1, which extends the formula to
+ * infinite logits: k chosen -infinity logits (a token whose logits are all
+ * NaN) share the gate equally, 1/k each. */
 static void softmax_chosen(const double *l, const int32_t *ids, int k, double *g) {
   double mx = -INFINITY;
-  for (int j = 0; j < k; ++j) if (l[ids[j]] > mx) mx = l[ids[j]];
+  for (int j = 0; j < k; ++j) if (rank_value(l[ids[j]]) > mx) mx = rank_value(l[ids[j]]);
   double den = 0.0;
-  for (int j = 0; j < k; ++j) den += exp(l[ids[j]] - mx);
-  for (int j = 0; j < k; ++j) g[j] = exp(l[ids[j]] - mx) / den;
+  for (int j = 0; j < k; ++j) {
+    const double v = rank_value(l[ids[j]]);
+    g[j] = v == mx ? 1.0 : exp(v - mx);
+    den += g[j];
+  }
+  for (int j = 0; j < k; ++j) g[j] /= den;
 }
 
 static inline int64_t tok_of(const int64_t *list, int64_t i) { return list ? list[i] : i; }

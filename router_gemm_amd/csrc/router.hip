@@ -153,7 +153,8 @@ __global__ __launch_bounds__(256, 1) void router_logits_tiled_kernel(
 
 // One wave per token: logits = sum of the S partials (in order s = 0..S-1)
 // + bias; k rounds of a wave-wide arg-max under the order (value desc, index
-// asc); slots sorted by expert id; gates = exp(l - l_max) / sum, fp32.
+// asc), a NaN logit ranking as -infinity; slots sorted by expert id; gates =
+// exp(l - l_max) / sum, fp32.
 template <int NJ>
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const float *__restrict__ partial, int S, const float *__restrict__ bias, int T, int E, int k,
@@ -187,6 +188,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     if (e < E) {
       if (bias) v[j] += bias[e];
       if (logits_out) logits_out[(int64_t)t * E + e] = v[j];
+      if (v[j] != v[j]) v[j] = -__builtin_huge_valf();   // a NaN logit ranks as -infinity
     }
   }
   uint32_t taken = 0;
@@ -224,8 +226,10 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     const int ej = __shfl(my_e, j, kWave);
     rank += (ej < my_e) ? 1 : 0;
   }
+  // a chosen logit equal to the largest weighs exp(0) = 1 (so k chosen
+  // -infinity logits, a token whose logits are all NaN, get 1/k each)
   const float vmax = __shfl(my_v, 0, kWave);
-  const float ex = lane < k ? expf(my_v - vmax) : 0.f;
+  const float ex = lane < k ? (my_v == vmax ? 1.0f : expf(my_v - vmax)) : 0.f;
   const float den = __shfl(wave_sum(ex), 0, kWave);
   if (lane < k) {
     ids[(int64_t)t * k + rank] = my_e;

@@ -137,3 +137,45 @@ def test_prefill_zipf_bias_skews_loads(orc):
     ratio = cnt.max() / cnt.mean()
     assert 8.5 < ratio < 11.5, ratio
     assert (cnt > 0).sum() == cfg.E
+
+
+def test_nan_logits_rank_below_every_number(orc):
+    """A NaN logit ranks as -infinity: experts whose bias is NaN are chosen only
+    when fewer than k others are left, lowest index first; a token whose
+    logits are all NaN (a NaN in x) gets experts 0..k-1 with gates 1/k (the k
+    chosen values are equal, so the softmax over them is uniform); a +inf
+    logit takes gate 1.  The oracle's logits output keeps the NaN values."""
+    rng = np.random.default_rng(31)
+    E, k, H = 12, 4, 64
+    bias = np.zeros(E, dtype=np.float32)
+    bias[[0, 3, 7]] = np.nan
+    L = _tiny_layer(orc, E=E, k=k, H=H, bias=bias)
+    x = _bf16(rng.standard_normal((6, H)))
+    x[5, 9] = 0x7FC0                                  # bf16 NaN: every logit of token 5 is NaN
+    ids, gates, gap, logits = orc.route(L, x, want_logits=True)
+    assert np.isnan(logits[:, [0, 3, 7]]).all() and np.isnan(logits[5]).all()
+    finite = np.setdiff1d(np.arange(E), [0, 3, 7])
+    for t in range(5):
+        lt = logits[t, finite]
+        want = np.sort(finite[np.argsort(-lt, kind="stable")[:k]])
+        np.testing.assert_array_equal(ids[t], want)
+        np.testing.assert_allclose(gates[t], softmax(logits[t, want]), rtol=1e-13)
+    np.testing.assert_array_equal(ids[5], np.arange(k))
+    np.testing.assert_array_equal(gates[5], np.full(k, 1.0 / k))
+    assert gap[5] == 0.0                               # the k-th and (k+1)-th values are equal (-inf)
+    # only 2 numbers left for k = 4: the two finite logits, then the two lowest NaN experts
+    bias2 = np.full(E, np.nan, dtype=np.float32)
+    bias2[[5, 10]] = 0.0
+    L2 = _tiny_layer(orc, E=E, k=k, H=H, bias=bias2)
+    ids2, gates2, _, lg2 = orc.route(L2, x[:5], want_logits=True)
+    np.testing.assert_array_equal(ids2, np.tile([0, 1, 5, 10], (5, 1)))
+    for t in range(5):   # the NaN experts weigh exp(-inf) = 0
+        np.testing.assert_allclose(gates2[t], [0, 0, *softmax(lg2[t, [5, 10]])], rtol=1e-13)
+    # a +inf logit: chosen, gate 1
+    bias3 = np.zeros(E, dtype=np.float32)
+    bias3[6] = np.inf
+    L3 = _tiny_layer(orc, E=E, k=k, H=H, bias=bias3)
+    ids3, gates3, _, _ = orc.route(L3, x[:5], want_logits=True)
+    for t in range(5):
+        assert 6 in ids3[t]
+        np.testing.assert_array_equal(gates3[t], (ids3[t] == 6).astype(np.float64))
