@@ -79,8 +79,8 @@ typedef enum moe_status {
   MOE_EINVAL = 1,        /* NULL pointer where one is required, bad size or dimension,
                             k outside [1, min(E, 32)], misaligned pointer */
   MOE_EUNSUPPORTED = 2,  /* valid but not built: H % 128 != 0; bf16 experts with I % 64 != 0;
-                            fp8 or mxfp4 experts with I % 128 != 0; E > 1024; H, I or the
-                            shared expert's I > 16384;
+                            fp8 or mxfp4 experts with I % 128 != 0; a shared expert with
+                            Is % 64 != 0; E > 1024; H, I or Is > 16384;
                             unsupported dtype combination */
   MOE_EWORKSPACE = 3,    /* ws_bytes smaller than the call needs */
   MOE_EHIP = 4           /* a HIP launch failed; moe_last_error() has the detail */
@@ -217,6 +217,10 @@ moe_status moe_expert_ffn(const moe_layer *layer, const int32_t *expert_offsets,
 /* Weighted un-permute and combine, adding the shared-expert output:
  *   y[t] = shared[t] + sum_{i: token(i) = t} gates[i] * y_perm[perm_pos[i]]
  * in fp32, shared first, then increasing i; rounded once to out_dtype.
+ * ("Step-5-Preview", "Model Architecture": the routed experts' outputs are
+ * weighted by the router and the one shared expert's output is added;
+ * "Step-5 minimal inference", "Long-output stability": partial results are
+ * added in a fixed order with FP32 accumulation.)
  *   y_perm       [N, H] (y_dtype MOE_BF16 or MOE_F32)
  *   perm_pos     int32 [N]  (-1: assignment skipped)
  *   assign_token int32 [N] or NULL (NULL: token(i) = i / k)
@@ -232,7 +236,11 @@ moe_status moe_combine(const moe_layer *layer, const void *y_perm, int32_t y_dty
                        void *ws, size_t ws_bytes, void *stream);
 
 /* The whole layer: route -> permute -> routed expert FFN -> shared expert
- * FFN -> combine, all on `stream`.
+ * FFN -> combine, all on `stream` ("Step-5-Preview", "Model Architecture":
+ * top-8 of 352 routed experts plus one shared expert, intermediate 1,536;
+ * "Step-5 minimal inference", introduction: block-scaled FP8 expert GEMMs).
+ * The shared expert rides in the routed experts' launches, or runs in a
+ * launch of its own when Is % 128 != 0 while I % 128 == 0.
  *   x          bf16 [T, H]
  *   y          [T, H] out (MOE_BF16 or MOE_F32)
  *   topk_ids   int32 [T, k] out or NULL;  topk_gates f32 [T, k] out or NULL */

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y
   } else {
     i32x4 r;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) r[q] = (int)(f32_to_bf16(acc[2 * q]) | (f32_to_bf16(acc[2 * q + 1]) << 16));
+    for (int q = 0; q < 4; ++q) r[q] = (int)(pack_bf16x2(acc[2 * q], acc[2 * q + 1]));
     store16(reinterpret_cast<uint16_t *>(y) + t * H + c, r);
   }
 }

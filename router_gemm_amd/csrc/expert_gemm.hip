@@ -469,8 +469,8 @@ __device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry 
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         if (!xv[m]) continue;
-        const uint32_t lo = f32_to_bf16(hv[i][m][0]) | (f32_to_bf16(hv[i][m][1]) << 16);
-        const uint32_t hi = f32_to_bf16(hv[i][m][2]) | (f32_to_bf16(hv[i][m][3]) << 16);
+        const uint32_t lo = pack_bf16x2(hv[i][m][0], hv[i][m][1]);
+        const uint32_t hi = pack_bf16x2(hv[i][m][2], hv[i][m][3]);
         *reinterpret_cast<uint2 *>(G.h + ((int64_t)xrow[m] * I + col) * 2) = make_uint2(lo, hi);
         if (G.z) {   // pre-activations kept for a backward
           float *zr = G.z + (int64_t)xrow[m] * 2 * I + col;
@@ -501,12 +501,11 @@ __device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry 
       const float am = __builtin_fmaxf(__builtin_fmaxf(red[0][tl], red[1][tl]),
                                        __builtin_fmaxf(red[2][tl], red[3][tl]));
       const float s = group_scale(am);
-      const float inv = __builtin_amdgcn_rcpf(s);
       if (!xv[m]) continue;
 #pragma unroll
       for (int i = 0; i < GW; ++i) {
         const int col = hc0 + 16 * i + 4 * (lane >> 4);
-        const uint32_t q = f32x4_to_e4m3(hv[i][m][0] * inv, hv[i][m][1] * inv, hv[i][m][2] * inv, hv[i][m][3] * inv);
+        const uint32_t q = quant4_e4m3(hv[i][m][0], hv[i][m][1], hv[i][m][2], hv[i][m][3], s);
         *reinterpret_cast<uint32_t *>(G.h + (int64_t)xrow[m] * I + col) = q;
       }
       if (w == 0 && lane < 16) G.hs[(int64_t)xrow[m] * (I / 128) + blockIdx.x] = s;
@@ -752,8 +751,8 @@ __device__ __forceinline__ void down_body(const FfnGroup &G, const TileEntry &te
       if (G.y_f32) {
         *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(G.y) + o) = acc[i][m];
       } else {
-        const uint32_t lo = f32_to_bf16(acc[i][m][0]) | (f32_to_bf16(acc[i][m][1]) << 16);
-        const uint32_t hi = f32_to_bf16(acc[i][m][2]) | (f32_to_bf16(acc[i][m][3]) << 16);
+        const uint32_t lo = pack_bf16x2(acc[i][m][0], acc[i][m][1]);
+        const uint32_t hi = pack_bf16x2(acc[i][m][2], acc[i][m][3]);
         *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(G.y) + o) = make_uint2(lo, hi);
       }
     }

@@ -322,8 +322,8 @@ __device__ __forceinline__ void store_item(const FfnGroup &G, const f32x4 (&acc)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int col = col0 + 64 * wn + 16 * i + 4 * (lane >> 4);
-          const uint32_t lo = f32_to_bf16(hv[i][j][0]) | (f32_to_bf16(hv[i][j][1]) << 16);
-          const uint32_t hi = f32_to_bf16(hv[i][j][2]) | (f32_to_bf16(hv[i][j][3]) << 16);
+          const uint32_t lo = pack_bf16x2(hv[i][j][0], hv[i][j][1]);
+          const uint32_t hi = pack_bf16x2(hv[i][j][2], hv[i][j][3]);
           *reinterpret_cast<uint2 *>(G.h + ((int64_t)(rbeg + tr) * I + col) * 2) = make_uint2(lo, hi);
           if (G.z) {   // pre-activations kept for a backward
             float *zr = G.z + (int64_t)(rbeg + tr) * 2 * I + col;
@@ -351,14 +351,13 @@ __device__ __forceinline__ void store_item(const FfnGroup &G, const f32x4 (&acc)
       for (int j = 0; j < 4; ++j) {
         const int tr = brow[j] + (lane & 15);
         const float s = group_scale(__builtin_fmaxf(red[tr], red[BM + tr]));
-        const float inv = __builtin_amdgcn_rcpf(s);
         if (tr >= nvalid) continue;
         const int64_t row = rbeg + tr;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int col = col0 + 64 * wn + 16 * i + 4 * (lane >> 4);
           *reinterpret_cast<uint32_t *>(G.h + row * I + col) =
-              f32x4_to_e4m3(hv[i][j][0] * inv, hv[i][j][1] * inv, hv[i][j][2] * inv, hv[i][j][3] * inv);
+              quant4_e4m3(hv[i][j][0], hv[i][j][1], hv[i][j][2], hv[i][j][3], s);
         }
         if (wn == 0 && lane < 16) G.hs[row * (I / 128) + ntile] = s;
       }
@@ -376,8 +375,8 @@ __device__ __forceinline__ void store_item(const FfnGroup &G, const f32x4 (&acc)
         if (G.y_f32) {
           *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(G.y) + o) = acc[i][j];
         } else {
-          const uint32_t lo = f32_to_bf16(acc[i][j][0]) | (f32_to_bf16(acc[i][j][1]) << 16);
-          const uint32_t hi = f32_to_bf16(acc[i][j][2]) | (f32_to_bf16(acc[i][j][3]) << 16);
+          const uint32_t lo = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+          const uint32_t hi = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
           *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(G.y) + o) = make_uint2(lo, hi);
         }
       }
@@ -447,6 +446,11 @@ struct WideItem {
   const float *ascale;
   int lane, w, wn, wm;
   uint32_t woff[4], xoff[4], soff;   // per-lane byte offsets of this lane's copies
+  // LDS read offsets inside a stage: token slice 0's two 16-byte fragment
+  // halves and its scale (slice j adds 8192 j / 512 j: its rows are
+  // 16 (wm + 4 j) + lane % 16, whose swizzle lane % 8 does not depend on j),
+  // and the weight fragment of tile 0 (tile16 copies).
+  uint32_t rb_l, rb_h, rb_s, ra;
 
   __device__ WideItem(const FfnGroup &g, const TileEntry &te, int nt_, int H_) : G(g), ntile(nt_), H(H_) {
     lane = threadIdx.x & 63;
@@ -500,17 +504,30 @@ struct WideItem {
       const int64_t src = indirect ? G.xsrc[rbeg + rr] / G.xdiv : rr;
       soff = (uint32_t)(src * KB * 4);
     }
+    {
+      const int r0 = 16 * wm + (lane & 15), ck = 2 * (lane >> 4);
+      rb_l = (uint32_t)(TW + swz(r0, ck));
+      rb_h = (uint32_t)(TW + swz(r0, ck + 1));
+      rb_s = (uint32_t)(TW + WTX + 256 * (r0 >> 5) + 4 * (r0 & 31));
+      ra = (uint32_t)(128 * (arow(0) - (lane & 15)) + 16 * lane);
+    }
   }
 
   // Direct-to-LDS copies of K chunk kc into stage buffer sb: 4 (weights) +
-  // 4 (tokens) [+ 1 (token scales, fp8)] instructions per wave.
+  // up to 4 (tokens) [+ 1 (token scales, fp8)] instructions per wave.  A
+  // token copy whose 8 rows all lie past the item's last row is skipped: the
+  // stale LDS rows it leaves only feed MFMA output columns of padding rows,
+  // which are never stored (an output column depends on its own token only).
+  // The waits count nothing but "all of this wave's copies", so a wave may
+  // issue fewer than the others.
   __device__ __forceinline__ void issue(int kc, uint8_t *sb) const {
     const uint8_t *wb = wsrc + (int64_t)kc * (T16 ? 128 * wrows : 128);
     const uint8_t *xb = asrc + (int64_t)kc * 128;
 #pragma unroll
     for (int t = 0; t < 4; ++t) dma16(wb + woff[t], sb + (w + 8 * t) * 1024);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) dma16(xb + xoff[t], sb + TW + (w + 8 * t) * 1024);
+    for (int t = 0; t < 4; ++t)
+      if (8 * (w + 8 * t) < nvalid) dma16(xb + xoff[t], sb + TW + (w + 8 * t) * 1024);
     if constexpr (FP8) dma4(reinterpret_cast<const uint8_t *>(ascale + kc) + soff, sb + TW + WTX + 256 * w);
   }
 
@@ -559,8 +576,74 @@ struct WideItem {
 
   // The MFMAs of one K chunk from stage buffer sb: token fragments read once,
   // weight tile i+1's fragments read while tile i's MFMAs run.
+  // Weight tile i's fragment (tile16 copies: the tile's two kilobytes at
+  // 2048 (arow(i) - lane % 16) / 16 = ra + tile offset).
+  __device__ __forceinline__ void read_a16(const uint8_t *sb, int i, AFrag &A) const {
+    const int dt = GATEUP ? (i < 4 ? 16 * i : 128 + 16 * (i - 4)) : 16 * i;   // arow(i) - arow(0)
+    const uint8_t *t = sb + ra + 128 * dt;
+    A.l = *reinterpret_cast<const i32x4 *>(t);
+    A.h = *reinterpret_cast<const i32x4 *>(t + 1024);
+  }
+
+  // fp8 chunk with tile16 weights.  The first MFMA's operands (weight tile 0,
+  // token slice 0, their scales) are read before the other slices, so a wave
+  // starts as soon as they land; each block product is folded into its
+  // accumulators two MFMAs later, when it is ready (no hazard stalls).
+  template <int NJ>
+  __device__ __forceinline__ void chunk_fp8_t16(const uint8_t *sb, const float *wsc, int kc,
+                                                f32x4 (&acc)[8][4]) const {
+    i32x4 bl[NJ], bh[NJ];
+    float sx[NJ];
+    AFrag A[2];
+    read_a16(sb, 0, A[0]);
+    bl[0] = *reinterpret_cast<const i32x4 *>(sb + rb_l);
+    bh[0] = *reinterpret_cast<const i32x4 *>(sb + rb_h);
+    sx[0] = *reinterpret_cast<const float *>(sb + rb_s);
+    const float sa = GATEUP ? wsc[kc] : wsc[wn * KB + kc];
+    const float sbw = GATEUP ? wsc[KB + kc] : sa;
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int NT = 8 * NJ;
+    f32x4 p1 = {0.f, 0.f, 0.f, 0.f}, p2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NT + 2; ++t) {
+      f32x4 cur = {0.f, 0.f, 0.f, 0.f};
+      if (t < NT) {
+        const int i = t / NJ, j = t % NJ;
+        const AFrag &a = A[i & 1];
+        const i32x8 a8 = {a.l[0], a.l[1], a.l[2], a.l[3], a.h[0], a.h[1], a.h[2], a.h[3]};
+        const i32x8 b8 = {bl[j][0], bl[j][1], bl[j][2], bl[j][3], bh[j][0], bh[j][1], bh[j][2], bh[j][3]};
+        cur = mfma_fp8(a8, b8, f32x4{0.f, 0.f, 0.f, 0.f});
+        if (t == 0) {   // the other token slices, while the first MFMA runs
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int jj = 1; jj < NJ; ++jj) {
+            bl[jj] = *reinterpret_cast<const i32x4 *>(sb + rb_l + 8192 * jj);
+            bh[jj] = *reinterpret_cast<const i32x4 *>(sb + rb_h + 8192 * jj);
+            sx[jj] = *reinterpret_cast<const float *>(sb + rb_s + 512 * jj);
+          }
+        }
+        if (j == 0 && i + 1 < 8) read_a16(sb, i + 1, A[(i + 1) & 1]);
+      }
+      if (t >= 2) {
+        const int i = (t - 2) / NJ, j = (t - 2) % NJ;
+        const float sc = ((GATEUP && i >= 4) ? sbw : sa) * sx[j];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p2[r], sc, acc[i][j][r]);
+      }
+      p2 = p1;
+      p1 = cur;
+      // keep this order: the scheduler would otherwise hoist every scale
+      // product to the top and wait there for all fragment reads
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
   template <int NJ>
   __device__ __forceinline__ void chunk(const uint8_t *sb, const float *wsc, int kc, f32x4 (&acc)[8][4]) const {
+    if constexpr (FP8 && T16) {
+      chunk_fp8_t16<NJ>(sb, wsc, kc, acc);
+      return;
+    }
     BFrags<NJ> F;
     read_b<NJ>(sb, wsc, kc, F);
     AFrag A[2];

@@ -291,14 +291,13 @@ __device__ __forceinline__ void mx_item(const FfnGroup &G, const TileEntry &te, 
     for (int j = 0; j < 2; ++j) {
       const int tr = brow[j] + (lane & 15);
       const float s = group_scale(__builtin_fmaxf(red[tr], red[XBM + tr]));
-      const float inv = __builtin_amdgcn_rcpf(s);
       if (tr >= nvalid) continue;
       const int64_t row = rbeg + tr;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int col = col0 + 64 * wn + 16 * i + 4 * (lane >> 4);
         *reinterpret_cast<uint32_t *>(G.h + row * I + col) =
-            f32x4_to_e4m3(hv[i][j][0] * inv, hv[i][j][1] * inv, hv[i][j][2] * inv, hv[i][j][3] * inv);
+            quant4_e4m3(hv[i][j][0], hv[i][j][1], hv[i][j][2], hv[i][j][3], s);
       }
       if (wn == 0 && lane < 16) G.hs[row * (I / 128) + ntile] = s;
     }
@@ -315,8 +314,8 @@ __device__ __forceinline__ void mx_item(const FfnGroup &G, const TileEntry &te, 
         if (G.y_f32) {
           *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(G.y) + o) = acc[i][j];
         } else {
-          const uint32_t lo = f32_to_bf16(acc[i][j][0]) | (f32_to_bf16(acc[i][j][1]) << 16);
-          const uint32_t hi = f32_to_bf16(acc[i][j][2]) | (f32_to_bf16(acc[i][j][3]) << 16);
+          const uint32_t lo = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+          const uint32_t hi = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
           *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(G.y) + o) = make_uint2(lo, hi);
         }
       }

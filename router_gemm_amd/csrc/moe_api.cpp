@@ -224,6 +224,12 @@ struct ForwardWs {
   FfnWs ffn;                       // routed (+ shared) experts in one launch
   moe::FfnGroup groups[moe::kMaxGroups];
   int ngroups;
+  // A shared expert whose width is not a multiple of 128 next to routed
+  // experts whose width is: its own launch (streaming kernels), so that the
+  // routed experts keep the 128-column kernels (LDS-tiled, or fp8).
+  bool shared_apart;
+  FfnWs ffn_sh;
+  moe::FfnGroup sh_group;
   uint16_t *y_perm;
   void *sh_out;
 };
@@ -242,16 +248,21 @@ ForwardWs carve_forward(Carve &c, const moe_layer *L, const void *x, int64_t T, 
   f.x_scale = is_fp8(L) ? c.take<float>((size_t)N * (H / 128) + 1) : nullptr;
   f.y_perm = c.take<uint16_t>((size_t)N * H + 8);
   f.ngroups = 0;
+  f.shared_apart = L->shared_inter > 0 && L->shared_inter % 128 != 0 && L->inter % 128 == 0;
   if (L->shared_inter > 0) {
     f.sh_out = c.take<uint8_t>((size_t)T * H * (out_f32 ? 4 : 2) + 16);
     // the shared expert's tiles go first in the list: they carry twice the bytes
     // (bf16); no offsets array: one expert holding all T rows
-    f.groups[f.ngroups++] = shared_group(L, x, nullptr, T, f.sh_out, out_f32);
+    if (!f.shared_apart) f.groups[f.ngroups++] = shared_group(L, x, nullptr, T, f.sh_out, out_f32);
   } else {
     f.sh_out = nullptr;
   }
   f.groups[f.ngroups++] = routed_group(L, f.x_perm, f.x_scale, f.offsets, N, f.y_perm, false);
   f.ffn = carve_ffn(c, f.groups, f.ngroups, H);
+  if (f.shared_apart) {
+    f.sh_group = shared_group(L, x, nullptr, T, f.sh_out, out_f32);
+    f.ffn_sh = carve_ffn(c, &f.sh_group, 1, H);
+  }
   return f;
 }
 
@@ -508,9 +519,14 @@ moe_status forward_impl(const moe_layer *L, const void *x, int64_t T, void *y, i
   if (z_saved) {   // routed rows in expert order, then the shared expert's rows
     R.z = z_saved;
     if (f.ngroups == 2) f.groups[0].z = z_saved + (size_t)N * 2 * L->inter;
+    if (f.shared_apart) f.sh_group.z = z_saved + (size_t)N * 2 * L->inter;
   }
   e = moe::launch_expert_ffn(f.groups, f.ngroups, H, f.ffn.plan, f.ffn.tiles, MOE_SITE_GATE_UP, st);
   if (e != hipSuccess) return hip_status(e, "moe_forward: experts");
+  if (f.shared_apart) {
+    e = moe::launch_expert_ffn(&f.sh_group, 1, H, f.ffn_sh.plan, f.ffn_sh.tiles, MOE_SITE_GATE_UP, st);
+    if (e != hipSuccess) return hip_status(e, "moe_forward: shared expert");
+  }
   e = moe::launch_combine(f.y_perm, false, f.perm_pos, nullptr, nullptr, L->top_k, gates, f.sh_out, out_f32, T, H, N, y,
                           out_f32, st);
   return hip_status(e, "moe_forward: combine");

@@ -23,12 +23,18 @@ constexpr float kFp8Max = 448.0f;  // largest finite OCP E4M3FN value
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
-// binary32 -> bf16, round to nearest even (NaN kept quiet).
+// binary32 -> bf16, round to nearest even (NaN stays NaN): gfx950's
+// conversion instruction (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Two binary32 values -> two bf16 codes (a in the low 16 bits), one packed
+// conversion instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Two binary32 values -> two E4M3FN codes in the low 16 bits.  The hardware
@@ -43,6 +49,13 @@ __device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b) {
 // Four binary32 values -> four E4M3FN codes packed little-endian.
 __device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, float d) {
   return f32x2_to_e4m3(a, b) | (f32x2_to_e4m3(c, d) << 16);
+}
+
+// Four values of a 1x128 group -> four E4M3FN codes: code = RNE(v / s) with
+// an IEEE binary32 division (not a multiply by a reciprocal, whose last bit
+// can move a quotient across an e4m3 rounding boundary), saturating.
+__device__ __forceinline__ uint32_t quant4_e4m3(float a, float b, float c, float d, float s) {
+  return f32x4_to_e4m3(__fdiv_rn(a, s), __fdiv_rn(b, s), __fdiv_rn(c, s), __fdiv_rn(d, s));
 }
 
 // Scale of a 1x128 group: amax / 448 with an IEEE binary32 division; 1 for an

@@ -177,9 +177,9 @@ def test_backward_training_workload_sampled(saved):
     x = W.make_x(cfg, dev())
     dy = W.make_dy(cfg, dev())
     if saved:
-        _, ids, gates, z = run_forward_train(lt, x)
+        y, ids, gates, z = run_forward_train(lt, x)
     else:
-        (_, ids, gates), z = run_forward(lt, x), None
+        (y, ids, gates), z = run_forward(lt, x), None
     out = run_backward(lt, x, dy, ids, gates, z_saved=z)
     del z
     for k, v in out.items():
@@ -188,6 +188,16 @@ def test_backward_training_workload_sampled(saved):
     OL = oracle_layer(lt)
     xb, dyb, idn = W.bf16_bits(x), W.bf16_bits(dy), ids.cpu().numpy()
     tl = np.array([0, 1, cfg.T // 2 + 3, cfg.T - 1])
+    # the training forward's own output (moe_forward_train, or moe_forward for
+    # the recompute case) on the sampled tokens plus two of the most loaded
+    # expert's tokens, against the oracle with the same ids
+    hot = np.bincount(idn.ravel(), minlength=cfg.E).argmax()
+    tly = np.unique(np.concatenate([tl, np.nonzero((idn == hot).any(1))[0][:2]]))
+    y_ref = oracle.forward_with_ids(OL, xb, idn[tly], token_list=tly)
+    e_y = rel_err_rows(_np(y)[tly], y_ref)
+    _print(cfg.name, "forward y max rel err", f"{e_y.max():.2e}", "over", len(tly), "tokens")
+    assert e_y.max() < TOL
+    assert e_y.max() < 2e-3              # regression bar (observed 6.9e-4)
     ref = oracle.backward(OL, xb, idn, dyb, token_list=tl, weights=False)
     e_dx = rel_err_rows(out["dx"][torch.from_numpy(tl).to(dev())].cpu().numpy(), ref["dx"])
     load = np.bincount(idn.ravel(), minlength=cfg.E)

@@ -13,7 +13,7 @@ from router_gemm_amd import binding as B
 from router_gemm_amd import workloads as W
 
 from conftest import gpu_available
-from gpu_util import TOL, check_forward, check_ids, dev, oracle_layer, rel_err_rows, run_forward, to_np
+from gpu_util import REG, TOL, check_forward, check_ids, dev, oracle_layer, rel_err_rows, run_forward, to_np
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
@@ -24,7 +24,7 @@ def test_decode_full_parity(name):
     print(f"[{cfg.name}] building layer", flush=True)
     lt = W.make_layer(cfg, dev())
     x = W.make_x(cfg, dev())
-    st = check_forward(lt, x)
+    st = check_forward(lt, x, reg=REG[cfg.name])
     print(f"[{cfg.name}] {st}", flush=True)
 
 
@@ -34,8 +34,14 @@ def test_prefill_routing_grouping_and_sampled_outputs():
     lt = W.make_layer(cfg, dev())
     x = W.make_x(cfg, dev())
     OL = oracle_layer(lt)
-    sample = np.random.default_rng(0).choice(cfg.T, 24, replace=False)
-    st = check_forward(lt, x, OL=OL, sample=sample)
+    # 24 seeded tokens plus 4 routed to the most loaded expert (its rows span
+    # several 256-row token tiles, the last one partly filled)
+    ids_all, _, _, _ = oracle.route(OL, W.bf16_bits(x))
+    hot = np.bincount(ids_all.ravel(), minlength=cfg.E).argmax()
+    hot_tokens = np.nonzero((ids_all == hot).any(1))[0]
+    sample = np.unique(np.concatenate([np.random.default_rng(0).choice(cfg.T, 24, replace=False),
+                                       hot_tokens[[0, 1, -2, -1]]]))
+    st = check_forward(lt, x, OL=OL, sample=sample, reg=REG[cfg.name])
     print(f"[prefill_fp8] {st}", flush=True)
     # grouping of the GPU's own ids, bit-exact, plus every fp8 byte of x_perm
     _, ids, _ = run_forward(lt, x)
@@ -76,7 +82,7 @@ def test_prefill_mxfp4_sampled_outputs():
     hot = np.bincount(ids_all.ravel(), minlength=cfg.E).argmax()
     hot_tokens = np.nonzero((ids_all == hot).any(1))[0][:4]
     sample = np.concatenate([np.random.default_rng(2).choice(cfg.T, 20, replace=False), hot_tokens])
-    st = check_forward(lt, x, OL=OL, sample=np.unique(sample))
+    st = check_forward(lt, x, OL=OL, sample=np.unique(sample), reg=REG[cfg.name])
     print(f"[prefill_mxfp4] {st}", flush=True)
 
 
@@ -117,3 +123,33 @@ def test_ep_share_primitives_with_triples():
     err = rel_err_rows(to_np(y)[sample], y_ref)
     print(f"[ep8_share_fp8] max rel err {err.max():.3e} over {len(sample)} tokens", flush=True)
     assert err.max() < TOL["fp8"]
+    assert err.max() < 7.5e-3            # regression bar (observed 2.5e-3)
+
+
+@pytest.mark.parametrize("layout", ["tile16", "rows"])
+def test_dense_ff_full_shape_sampled(layout):
+    """The model's dense FF layers at their full shape (intermediate 13,824 as
+    one expert holding all 8,192 tokens, H = 4,096: 108 column tiles of the
+    256 x 256 items, the benchmark's launch) through moe_expert_ffn: 8 rows
+    spread over the token tiles, including the first and last rows of tiles,
+    against the oracle."""
+    cfg = W.get_config("dense_ff_bf16")
+    print(f"[dense_ff_bf16 {layout}] building layer", flush=True)
+    lt = W.make_layer(cfg, dev())
+    x = W.make_x(cfg, dev())
+    layer = B.Layer.from_tensors(lt)
+    if layout == "tile16":
+        layer = layer.packed()
+    d = dev()
+    off = torch.tensor([0, cfg.T], dtype=torch.int32, device=d)
+    y = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=d)
+    B.moe_expert_ffn(layer, off, x, None, cfg.T, y, ws=B.workspace(layer, cfg.T, cfg.T, d))
+    torch.cuda.synchronize()
+    OL = oracle_layer(lt)
+    xb = W.bf16_bits(x)
+    rows = np.array([0, 1, 255, 256, 4097, 6000, 8190, 8191])
+    y_ref = np.stack([oracle.expert_row(OL, 0, xb[r])[0] for r in rows])
+    err = rel_err_rows(to_np(y)[rows], y_ref)
+    print(f"[dense_ff_bf16 {layout}] max rel err {err.max():.3e} over {len(rows)} rows", flush=True)
+    assert err.max() < TOL["bf16"]
+    assert err.max() < 5e-5              # regression bar (observed 1.5e-5: bf16 h, no fp8 step)

@@ -14,7 +14,7 @@ from router_gemm_amd import binding as B
 from router_gemm_amd import workloads as W
 
 from conftest import gpu_available
-from gpu_util import TOL, check_forward, check_ids, dev, oracle_layer, rel_err_rows, run_forward, to_np
+from gpu_util import REG, TOL, check_forward, check_ids, dev, oracle_layer, rel_err_rows, run_forward, to_np
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
@@ -96,6 +96,32 @@ def test_route_exact_ties_lowest_index():
     # all-equal logits: x = 0 -> every logit 0 -> experts 0..k-1, gates 1/k
     ids0, g0 = _route_with(wr.to(dev()), torch.zeros((3, H), dtype=torch.bfloat16, device=dev()), k)
     assert (ids0 == np.arange(k)).all() and np.allclose(g0, 1.0 / k, atol=1e-7)
+
+
+@pytest.mark.parametrize("T", [40, 2100])     # split-K logits kernel; LDS-tiled logits kernel
+def test_route_nan_logits_rank_lowest(T):
+    """NaN logits rank as -infinity, as in the oracle: experts with a NaN bias
+    are never chosen while k others are left; a token with a NaN in x (every
+    logit NaN) gets experts 0..k-1 with gates 1/k; the same with only two
+    finite logits (the two, then the lowest NaN experts, gate 0); the logits
+    output keeps the NaN values."""
+    E, H, k = 40, 256, 4
+    g = torch.Generator(device="cpu").manual_seed(6)
+    wr = (torch.randn(E, H, generator=g) / 16).to(torch.bfloat16)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    x[3, 17] = float("nan")
+    for nan_experts in ([1, 8, 33], [e for e in range(E) if e not in (12, 30)]):
+        bias = np.zeros(E, dtype=np.float32)
+        bias[nan_experts] = np.nan
+        ids, gates = _route_with(wr.to(dev()), x.to(dev()), k, bias=torch.from_numpy(bias).to(dev()))
+        OL = oracle.Layer(H, 64, E, k, "bf16", W.bf16_bits(wr), np.zeros((E, 128, H), np.uint16),
+                          np.zeros((E, H, 64), np.uint16), router_bias=bias)
+        ids_ref, g_ref, gap, l_ref = oracle.route(OL, W.bf16_bits(x), want_logits=True)
+        same = check_ids(ids, ids_ref, gap)
+        assert np.abs(gates[same] - g_ref[same]).max() < 2e-6
+        np.testing.assert_array_equal(ids[3], np.arange(k))
+        np.testing.assert_array_equal(gates[3], np.full(k, 0.25, dtype=np.float32))
+        assert not np.isin(ids[np.arange(T) != 3], nan_experts).any() if len(nan_experts) < E - k else True
 
 
 def test_route_k_equals_E_and_k1():
@@ -334,6 +360,41 @@ def test_combine_of_permute_is_identity():
         assert torch.equal(y.float(), x.float() * k)
 
 
+def test_combine_rounds_to_bf16_nearest_even():
+    """One assignment per token with gate 1 and no shared expert: y = bf16(y_perm)
+    (the single rounding of the combine).  Every bf16 store of the layer uses the
+    same conversion; here it meets exact midpoints (ties to even both ways),
+    values just either side of them, zeros, the largest finite values,
+    overflow to infinity and fp32 subnormals, checked bit for bit against torch's
+    round-to-nearest-even conversion on the CPU."""
+    rng = np.random.default_rng(21)
+    H = 512
+    hi = rng.integers(0, 1 << 16, size=4096, dtype=np.uint32)
+    hi = hi[((hi >> 7) & 0xFF) != 0xFF]                       # finite bf16 upper halves
+    lo = np.concatenate([np.full(hi.size // 4, 0x8000), np.full(hi.size // 4, 0x7FFF),
+                         np.full(hi.size // 4, 0x8001), rng.integers(0, 1 << 16, size=hi.size - 3 * (hi.size // 4))])
+    bits = (hi << 16) | lo.astype(np.uint32)
+    special = np.array([0x00000000, 0x80000000, 0x7F7FFFFF, 0xFF7FFFFF, 0x7F7F8000, 0x7F7F7FFF,
+                        0x00000001, 0x80008000, 0x00018000, 0x007FFFFF, 0x00800000], dtype=np.uint32)
+    bits = np.concatenate([special, bits])
+    T = -(-bits.size // H)
+    bits = np.resize(bits, T * H)
+    vals = bits.view(np.float32).reshape(T, H)
+    d = dev()
+    layer = B.Layer(H, 128, 8, 1, B.MOE_BF16, None, None)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=d)
+    pos = torch.arange(T, dtype=torch.int32, device=d)
+    B.moe_combine(layer, torch.from_numpy(vals).to(d), B.MOE_F32, pos, None, torch.ones(T, device=d), T,
+                  None, 0, T, y, B.MOE_BF16, ws=B.workspace(layer, T, T, d))
+    torch.cuda.synchronize()
+    # the sum starts from +0 (no shared expert), so -0 comes out as +0
+    want = torch.from_numpy(vals + np.float32(0)).to(torch.bfloat16).view(torch.int16).numpy()
+    got = y.cpu().view(torch.int16).numpy()
+    bad = np.nonzero(got != want)
+    assert bad[0].size == 0, f"{bad[0].size} mismatches, e.g. fp32 {bits.reshape(T, H)[bad][:4]} -> " \
+                             f"{got[bad][:4].view(np.uint16)} (want {want[bad][:4].view(np.uint16)})"
+
+
 # ------------------------------------------------------------------ whole layer
 
 @pytest.mark.parametrize("name", ["c0", "small_fp8"])
@@ -341,7 +402,7 @@ def test_forward_small_full_parity(name):
     cfg = W.get_config(name)
     lt = W.make_layer(cfg, dev())
     x = W.make_x(cfg, dev())
-    st = check_forward(lt, x)
+    st = check_forward(lt, x, reg=REG[cfg.name])
     _print(f"forward {name}: {st}")
 
 
@@ -366,6 +427,23 @@ def test_forward_tiled_path_reads_rows_through_permutation(name, over):
     x = W.make_x(cfg, dev())
     st = check_forward(lt, x)
     _print(f"forward tiled {name} {over}: {st}")
+
+
+@pytest.mark.parametrize("name,over", [
+    ("small_fp8", dict(Is=192)),                            # fp8 routed experts, streaming kernels
+    ("small_fp8", dict(T=777, Is=192)),                     # fp8 routed experts, 256-row tiles
+    ("c0", dict(T=1500, I=256, Is=192)),                    # bf16 routed experts, 256-row tiles
+])
+def test_forward_shared_width_not_multiple_of_128(name, over):
+    """A shared expert whose width is a multiple of 64 but not of 128 next to
+    routed experts whose width is: the shared expert gets a launch of its own
+    (streaming kernels, 64-column tiles) and the routed experts keep theirs
+    (fp8 needs 128-column tiles; bf16 keeps the LDS-tiled kernels)."""
+    cfg = W.get_config(name, **over)
+    lt = W.make_layer(cfg, dev())
+    x = W.make_x(cfg, dev())
+    st = check_forward(lt, x)
+    _print(f"forward shared width {cfg.Is} {name} {over}: {st}")
 
 
 def test_forward_ragged_and_single_token():
