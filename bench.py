@@ -5,15 +5,20 @@ One step = one pass of the whole layer (router, grouping, routed expert
 gate/up + SwiGLU and down, shared expert, combine) over one batch of
 synthetic tokens already resident in HBM.  Prints one JSON line.
 
-  python bench.py [--workload decode_bf16|decode_fp8|decode_mxfp4|prefill_fp8|ep8_share_fp8|dense_ff_bf16|
-                              train_bf16|small_bf16]
-                  [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--weight-layout tile16|rows]
+  python bench.py [--workload prefill_fp8|decode_fp8|decode_bf16|decode_mxfp4|prefill_mxfp4|ep8_share_fp8|
+                              dense_ff_bf16|train_bf16|small_bf16]
+                  [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-decode]
+                  [--weight-layout tile16|rows]
 
-The default workload is the bf16 decode layer (T=64 tokens, hidden 4096,
-352 experts, top-8, intermediate 1536, one shared expert).  The dominant
-kernel's roofline figure comes from HIP events recorded around that kernel
-inside the timed steps (moe_timing.h); the CPU baseline is the fp64 oracle
-on a bounded sample of the same workload, on the host's cores.
+The default workload is the FP8 prefill layer (T=8192 tokens, hidden 4096,
+352 experts, top-8 with the Zipf-skewed router, intermediate 1536, one bf16
+shared expert), scored by MFMA utilisation; the same run then times the FP8
+decode layer (T=64, the same expert weights, unbiased router) in a timed
+region of its own, scored by HBM bandwidth, and reports it as the nested
+object "decode_fp8" (--no-decode leaves it out).  The dominant kernel's
+roofline figure comes from HIP events recorded around that kernel inside the
+timed steps (moe_timing.h); the CPU baseline is the fp64 oracle on a bounded
+sample of the same workload, on the host's cores.
 
 The routed experts' bf16 and fp8 weights are repacked once, before the timed
 region, into the 16-row tile layout (moe_pack_weights; --weight-layout rows
@@ -22,6 +27,7 @@ keeps them row-major); MX FP4 and training workloads use row-major weights.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -41,7 +47,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode_bf16")
+    ap.add_argument("--workload", default="prefill_fp8")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="prefill_fp8 only: leave out the FP8 decode layer timed in the same run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--weight-layout", choices=["tile16", "rows"], default="tile16",
                     help="storage of the routed experts' bf16/fp8 weights (packed once before timing)")
@@ -150,14 +158,40 @@ def main():
     if cfg.name.startswith("train"):
         bench_train(args, cfg, lt, x, dev)
         return
-    T, H, E, I, Is = cfg.T, cfg.H, cfg.E, cfg.I, cfg.Is
-    fp8 = cfg.expert_dtype != "bf16"     # activations and h stored as e4m3 + 1x128 scales
     mx = cfg.expert_dtype == "mxfp4"
     layer = B.Layer.from_tensors(lt, top_k=cfg.k if not cfg.triples else 0)
     weight_layout = "rows" if (mx or args.weight_layout == "rows") else "tile16"
     if weight_layout == "tile16":
         layer = layer.packed()   # a load-time repack, outside the timed region
         torch.cuda.synchronize()
+    out = measure(args, cfg, lt, layer, x, weight_layout, dev)
+    if cfg.name == "prefill_fp8" and not args.no_decode:
+        # the decode layer of the same model: the same expert, shared-expert and
+        # router weights (same seed and shapes), no router bias, T = 64
+        dcfg = W.get_config("decode_fp8")
+        assert (dcfg.E, dcfg.H, dcfg.I, dcfg.Is, dcfg.expert_dtype, dcfg.seed, dcfg.router_std) == \
+               (cfg.E, cfg.H, cfg.I, cfg.Is, cfg.expert_dtype, cfg.seed, cfg.router_std)
+        print(f"[bench] timing {dcfg.name} (same expert weights)", file=sys.stderr, flush=True)
+        dlt = dataclasses.replace(lt, cfg=dcfg, router_bias=None)
+        d = measure(args, dcfg, dlt, layer.with_router_bias(None), W.make_x(dcfg, dev), weight_layout, dev)
+        for key in ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "data", "warmup"):
+            d.pop(key, None)
+        out["decode_fp8"] = d
+    print(json.dumps(out), flush=True)
+
+
+def measure(args, cfg, lt, layer, x, weight_layout, dev):
+    """Time K steps of one workload's layer (inputs resident in HBM) and return
+    the JSON object of the bench line."""
+    import numpy as np
+    import torch
+
+    from router_gemm_amd import binding as B
+    from router_gemm_amd import workloads as W
+
+    T, H, E, I, Is = cfg.T, cfg.H, cfg.E, cfg.I, cfg.Is
+    fp8 = cfg.expert_dtype != "bf16"     # activations and h stored as e4m3 + 1x128 scales
+    mx = cfg.expert_dtype == "mxfp4"
     N = cfg.N
     y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
@@ -328,7 +362,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, lt, x, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+    return out
 
 
 def bench_train(args, cfg, lt, x, dev):
@@ -468,6 +502,19 @@ def bench_train(args, cfg, lt, x, dev):
     print(json.dumps(out), flush=True)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (the first "model name" line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline_train(cfg, lt, x, dy, target_s):
     """The fp64 oracle's forward and backward (input gradient only: its weight
     gradients would be 53 GB of fp64 at this shape) on a sample of tokens."""
@@ -494,7 +541,8 @@ def cpu_baseline_train(cfg, lt, x, dy, target_s):
         el = time.perf_counter() - t0
         if el >= target_s or done >= 8 * n:
             break
-    return {"value": round(done / el, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+    return {"value": round(done / el, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "cpu": cpu_model(),
+            "kind": "oracle",
             "sample": f"{n} of the {cfg.T} tokens of {cfg.name} (seeded choice): forward of the layer, then "
                       f"the backward's input gradient (no weight gradients), {done // n} pass(es) in {el:.1f} s; "
                       f"the sample's routing is done once beforehand, untimed"}
@@ -532,7 +580,8 @@ def cpu_baseline(cfg, lt, x, target_s):
         el = time.perf_counter() - t0
         if el >= target_s or done >= 16 * n:
             break
-    return {"value": round(done / el, 2), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+    return {"value": round(done / el, 2), "unit": "tokens/s", "cores": oracle.num_threads(), "cpu": cpu_model(),
+            "kind": "oracle",
             "fp64_gflops": round(pass_flops * (done // n) / el / 1e9, 2),
             "sample": f"{n} of the {cfg.T} tokens of {cfg.name} (seeded choice), full layer per token, "
                       f"{done // n} pass(es) in {el:.1f} s"}

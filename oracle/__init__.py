@@ -24,19 +24,27 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
 SRC_PATH = os.path.join(_HERE, "moe_oracle.c")
+# MOE_ORACLE_SANITIZE=1 selects the AddressSanitizer + UBSan build (CPU tests
+# only; the process must preload gcc's libasan, see tests/run_sanitized.py).
+SANITIZE = os.environ.get("MOE_ORACLE_SANITIZE", "") == "1"
+LIB_PATH = os.path.join(_HERE, "libmoe_oracle_san.so" if SANITIZE else "libmoe_oracle.so")
 
 _i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
 
 
-def build() -> str:
-    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
-           "-Wall", "-Wpointer-arith", SRC_PATH, "-o", LIB_PATH + ".tmp", "-lm"]
+def build(sanitize: bool = SANITIZE) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction); with
+    `sanitize`, the AddressSanitizer + UBSan build (-O1, aborts on the first
+    report) next to the plain one."""
+    out = os.path.join(_HERE, "libmoe_oracle_san.so" if sanitize else "libmoe_oracle.so")
+    opt = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=undefined"] if sanitize else ["-O2"]
+    cmd = ["gcc", *opt, "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+           "-Wall", "-Wpointer-arith", SRC_PATH, "-o", out + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(LIB_PATH + ".tmp", LIB_PATH)
-    return LIB_PATH
+    os.replace(out + ".tmp", out)
+    return out
 
 
 class _Layer(C.Structure):

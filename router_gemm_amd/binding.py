@@ -14,7 +14,12 @@ from typing import Optional
 
 import torch
 
-from .build import LIB
+from .build import LIB, LIB_SAN
+
+# MOE_SANITIZED_HOST=1: load the build whose host code carries AddressSanitizer
+# and UBSan (CPU tests of the argument validation only; tests/run_sanitized.py)
+if os.environ.get("MOE_SANITIZED_HOST", "") == "1":
+    LIB = LIB_SAN
 
 MOE_BF16 = 1
 MOE_FP8_E4M3FN = 2
@@ -156,6 +161,12 @@ class Layer:
         t = self.tensors
         return Layer(c.hidden, c.inter, c.num_experts, c.top_k, c.expert_dtype, pgu, pd, t[2], t[3], t[4], t[5],
                      t[6], t[7], c.shared_inter, MOE_LAYOUT_TILE16)
+
+    def with_router_bias(self, router_bias: Optional[torch.Tensor]) -> "Layer":
+        """The same layer (same weight tensors and layout) with another router bias."""
+        c, t = self.c, self.tensors
+        return Layer(c.hidden, c.inter, c.num_experts, c.top_k, c.expert_dtype, t[0], t[1], t[2], t[3], t[4],
+                     router_bias, t[6], t[7], c.shared_inter, c.weight_layout)
 
     @classmethod
     def shared_view(cls, lt) -> "Layer":
