@@ -249,6 +249,25 @@ moe_status moe_forward(const moe_layer *layer, const void *x, int64_t T,
                        int32_t *topk_ids, float *topk_gates,
                        void *ws, size_t ws_bytes, void *stream);
 
+/* moe_forward without a workspace argument, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): its scratch memory is a device array the library owns,
+ * MOE_NOALLOC_SCRATCH_BYTES on each GPU it runs on, held until the process
+ * ends.  It allocates and frees nothing.  Same arguments, kernels and outputs
+ * as moe_forward (bit for bit).
+ *   MOE_EWORKSPACE  the call needs more scratch than the array holds (what
+ *                   moe_forward would need; for the Step-5 layer: T above 359
+ *                   tokens with bf16 experts, above 469 with fp8 or mxfp4
+ *                   experts); checked on the host before the device is touched.
+ * Other errors as moe_forward.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time
+ * on the same GPU (two streams, two threads) race and must be serialised by
+ * the caller.  Nothing in the array needs to be cleared between calls. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_forward_noalloc(const moe_layer *layer, const void *x, int64_t T,
+                               void *y, int32_t out_dtype,
+                               int32_t *topk_ids, float *topk_gates, void *stream);
+
 /* Workspace bytes moe_backward needs for up to T tokens (moe_workspace_bytes
  * does not cover moe_backward).  Host-only; 0 on invalid arguments. */
 size_t moe_backward_workspace_bytes(const moe_layer *layer, int64_t T);

@@ -52,7 +52,7 @@ class MoELayerC(C.Structure):
 
 
 EXPORTS = ["moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_forward", "moe_saved_z_floats", "moe_forward_train", "moe_backward_workspace_bytes",
+           "moe_forward", "moe_forward_noalloc", "moe_saved_z_floats", "moe_forward_train", "moe_backward_workspace_bytes",
            "moe_backward", "moe_pack_weights", "moe_status_string",
            "moe_last_error", "moe_timing_arm", "moe_timing_read"]
 
@@ -79,6 +79,8 @@ def lib() -> C.CDLL:
         L.moe_combine.argtypes = [vp, vp, i32, vp, vp, vp, i64, vp, i32, i64, vp, i32, vp, sz, vp]
         L.moe_forward.restype = C.c_int
         L.moe_forward.argtypes = [vp, vp, i64, vp, i32, vp, vp, vp, sz, vp]
+        L.moe_forward_noalloc.restype = C.c_int
+        L.moe_forward_noalloc.argtypes = [vp, vp, i64, vp, i32, vp, vp, vp]
         L.moe_backward_workspace_bytes.restype = sz
         L.moe_backward_workspace_bytes.argtypes = [vp, i64]
         L.moe_backward.restype = C.c_int
@@ -223,6 +225,15 @@ def moe_forward(layer: Layer, x, T, y, out_dtype=None, topk_ids=None, topk_gates
     od = dtype_code(y) if out_dtype is None else out_dtype
     _check(lib().moe_forward(layer.ref, _ptr(x), T, _ptr(y), od, _ptr(topk_ids), _ptr(topk_gates),
                              w, nb, _stream(stream)))
+
+
+def moe_forward_noalloc(layer: Layer, x, T, y, out_dtype=None, topk_ids=None, topk_gates=None, stream=None):
+    od = dtype_code(y) if out_dtype is None else out_dtype
+    _check(lib().moe_forward_noalloc(layer.ref, _ptr(x), T, _ptr(y), od, _ptr(topk_ids), _ptr(topk_gates),
+                                     _stream(stream)))
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20   # include/moe.h
 
 
 def moe_pack_weights(src, dst, count: int, rows: int, row_bytes: int, stream=None):

@@ -538,6 +538,24 @@ moe_status moe_forward(const moe_layer *L, const void *x, int64_t T, void *y, in
   return forward_impl(L, x, T, y, out_dtype, topk_ids, topk_gates, nullptr, ws, ws_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace moe {
+// For the variant of moe_forward whose scratch memory is the library's static
+// device array (scratch.hip).
+size_t forward_ws_bytes(const moe_layer *L, int64_t T) {
+  if (check_layer_shape(L, true) != MOE_OK || check_rows(T, T * (int64_t)L->top_k) != MOE_OK) return 0;
+  return need_forward(L, T);
+}
+moe_status forward_with_ws(const moe_layer *L, const void *x, int64_t T, void *y, int32_t out_dtype,
+                           int32_t *topk_ids, float *topk_gates, void *ws, size_t ws_bytes, void *stream) {
+  return forward_impl(L, x, T, y, out_dtype, topk_ids, topk_gates, nullptr, ws, ws_bytes, stream);
+}
+moe_status api_error(moe_status s, const char *msg) { return fail(s, "%s", msg); }
+}  // namespace moe
+
+extern "C" {
+
 size_t moe_saved_z_floats(const moe_layer *L, int64_t T) {
   if (check_layer_shape(L, true) != MOE_OK || check_rows(T, T * (int64_t)L->top_k) != MOE_OK) return 0;
   return (size_t)T * L->top_k * 2 * L->inter + (size_t)T * 2 * L->shared_inter;

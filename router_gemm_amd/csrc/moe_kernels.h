@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/moe.h"
+
 namespace moe {
 
 constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -158,6 +160,15 @@ hipError_t launch_router_backward(const float *dl, const uint16_t *x_perm, const
 hipError_t launch_dx_backward(const float *dx_shared, const float *dx_rows, const int32_t *perm_pos,
                               const int32_t *ids, const float *dl, const uint16_t *wr, int64_t T, int k, int H,
                               float *dx, hipStream_t st);
+
+// ---- the C ABI's forward on a given scratch buffer (moe_api.cpp)
+// Workspace bytes moe_forward needs for T tokens (0 on invalid arguments).
+size_t forward_ws_bytes(const moe_layer *L, int64_t T);
+// moe_forward with its scratch memory at ws (ws_bytes usable).
+moe_status forward_with_ws(const moe_layer *L, const void *x, int64_t T, void *y, int32_t out_dtype,
+                           int32_t *topk_ids, float *topk_gates, void *ws, size_t ws_bytes, void *stream);
+// Record `msg` as moe_last_error() and return s.
+moe_status api_error(moe_status s, const char *msg);
 
 // ---- combine (combine.hip)
 // y[t] = shared[t] + sum over the token's assignments (fixed order) of g * y_perm[perm_pos]
