@@ -346,7 +346,10 @@ __device__ __forceinline__ void store_item(const FfnGroup &G, const f32x4 (&acc)
         am = __builtin_fmaxf(am, __shfl_xor(am, 32, kWave));
         if (lane < 16) red[wn * BM + brow[j] + lane] = am;
       }
-      __syncthreads();
+      // LDS-only barrier: a __syncthreads would also wait for the next work
+      // item's copies, which are in flight during this epilogue
+      wait_lgkm0();
+      wg_barrier();
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int tr = brow[j] + (lane & 15);
@@ -362,7 +365,7 @@ __device__ __forceinline__ void store_item(const FfnGroup &G, const f32x4 (&acc)
         if (wn == 0 && lane < 16) G.hs[row * (I / 128) + ntile] = s;
       }
     }
-  } else {
+  } else if (G.y_f32) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int tr = brow[j] + (lane & 15);
@@ -371,13 +374,32 @@ __device__ __forceinline__ void store_item(const FfnGroup &G, const f32x4 (&acc)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int col = col0 + 128 * wn + 16 * i + 4 * (lane >> 4);
-        const int64_t o = row * H + col;
-        if (G.y_f32) {
-          *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(G.y) + o) = acc[i][j];
-        } else {
-          const uint32_t lo = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
-          const uint32_t hi = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-          *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(G.y) + o) = make_uint2(lo, hi);
+        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(G.y) + row * H + col) = acc[i][j];
+      }
+    }
+  } else {
+    // bf16 rows, 16 bytes per lane: lane (t, q = lane / 16) holds columns
+    // 16 i + 4 q .. +3 of tiles i and i+1 (i even); lanes q and q ^ 1 swap
+    // halves so that an even q ends up with columns 16 i + 4 q .. +7 of tile i
+    // and an odd q with 16 (i+1) + 4 (q-1) .. +7 of tile i+1.
+    const int q = lane >> 4;
+    const bool even = (q & 1) == 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tr = brow[j] + (lane & 15);
+      const int64_t row = rbeg + tr;
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const uint32_t a0 = pack_bf16x2(acc[i][j][0], acc[i][j][1]), a1 = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+        const uint32_t b0 = pack_bf16x2(acc[i + 1][j][0], acc[i + 1][j][1]),
+                       b1 = pack_bf16x2(acc[i + 1][j][2], acc[i + 1][j][3]);
+        // every lane takes part in the swap, stored or not
+        const uint32_t r0 = (uint32_t)__shfl_xor((int)(even ? b0 : a0), 16, kWave);
+        const uint32_t r1 = (uint32_t)__shfl_xor((int)(even ? b1 : a1), 16, kWave);
+        if (tr < nvalid) {
+          const int col = col0 + 128 * wn + (even ? 16 * i + 4 * q : 16 * (i + 1) + 4 * (q - 1));
+          const i32x4 v = even ? i32x4{(int)a0, (int)a1, (int)r0, (int)r1} : i32x4{(int)r0, (int)r1, (int)b0, (int)b1};
+          store16(reinterpret_cast<uint16_t *>(G.y) + row * H + col, v);
         }
       }
     }
@@ -709,25 +731,59 @@ struct WideItem {
 
   // Step kc: wait for this wave's copies of chunk kc, sync the workgroup
   // (every wave's copies have landed, and nobody reads chunk kc-1's buffer any
-  // more), refill that buffer with chunk kc+1, consume chunk kc.
+  // more), refill that buffer with chunk kc+1, consume chunk kc.  Chunk 0 was
+  // issued into stage `par` before the call (by the previous work item, or
+  // before the first); chunk kc sits in stage (par + kc) % 2.
   template <int NJ>
-  __device__ __forceinline__ void mainloop(uint8_t *lds, const float *wsc, f32x4 (&acc)[8][4]) const {
-    issue(0, lds);
+  __device__ __forceinline__ void mainloop(uint8_t *lds, int par, const float *wsc, f32x4 (&acc)[8][4]) const {
     for (int kc = 0; kc < nchunk; ++kc) {
       wait_vm_lgkm0<0>();
       wg_barrier();
-      if (kc + 1 < nchunk) issue(kc + 1, lds + ((kc + 1) & 1) * WSTAGE);
-      chunk<NJ>(lds + (kc & 1) * WSTAGE, wsc, kc, acc);
+      if (kc + 1 < nchunk) issue(kc + 1, lds + ((par + kc + 1) & 1) * WSTAGE);
+      chunk<NJ>(lds + ((par + kc) & 1) * WSTAGE, wsc, kc, acc);
     }
   }
 };
 
+// A resolved work item of the wide kernel.
+struct WideWork {
+  TileEntry te;
+  int ntile;
+  int valid;
+};
+
+// Start work item w: stage its weight-block scales in wscb and issue its
+// chunk 0 into stage buffer sb.
 template <bool FP8, bool GATEUP, bool T16>
-__device__ __forceinline__ void wide_item(const FfnGroup &G, const TileEntry &te, int ntile, int H, uint8_t *lds,
-                                          float *red, float *wsc) {
-  WideItem<FP8, GATEUP, T16> it(G, te, ntile, H);
-  it.load_wscales(wsc);
-  __syncthreads();
+__device__ __forceinline__ void wide_begin_t(const FfnGroup &G, const WideWork &w, int H, uint8_t *sb, float *wscb) {
+  WideItem<FP8, GATEUP, T16> it(G, w.te, w.ntile, H);
+  it.load_wscales(wscb);
+  it.issue(0, sb);
+}
+template <bool GATEUP>
+__device__ __forceinline__ void wide_begin(const TiledArgs &a, const WideWork &w, uint8_t *sb, float *wscb) {
+  const FfnGroup &G = (w.te.ge >> 24) ? a.g1 : a.g0;
+  if (G.fp8) {
+    if (G.tile16)
+      wide_begin_t<true, GATEUP, true>(G, w, a.H, sb, wscb);
+    else
+      wide_begin_t<true, GATEUP, false>(G, w, a.H, sb, wscb);
+  } else if (G.tile16) {
+    wide_begin_t<false, GATEUP, true>(G, w, a.H, sb, wscb);
+  } else {
+    wide_begin_t<false, GATEUP, false>(G, w, a.H, sb, wscb);
+  }
+}
+
+// One work item whose chunk 0 (stage par) and weight scales (wscb[0]) were
+// issued beforehand.  After its last chunk's MFMAs it starts the next item
+// (chunk 0 into the other stage... the stage its chunk nchunk-2 used, which
+// every wave is done with; scales into wscb[1]), so that those copies are in
+// flight during this item's epilogue.  Returns the next item's chunk-0 stage.
+template <bool FP8, bool GATEUP, bool T16>
+__device__ __forceinline__ int wide_item(const TiledArgs &a, const FfnGroup &G, const WideWork &cur,
+                                         const WideWork &next, int par, uint8_t *lds, float *red, float *const wscb[2]) {
+  WideItem<FP8, GATEUP, T16> it(G, cur.te, cur.ntile, a.H);
   const int lane = it.lane, wn = it.wn, wm = it.wm;
   // active 16-row token slices of this wave: slice j covers rows 16*(wm + 4j)
   const int nact = uniform(it.nvalid <= 16 * wm ? 0 : min(4, (it.nvalid - 16 * wm + 63) / 64));
@@ -737,19 +793,27 @@ __device__ __forceinline__ void wide_item(const FfnGroup &G, const TileEntry &te
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   switch (nact) {
-    case 4: it.template mainloop<4>(lds, wsc, acc); break;
-    case 3: it.template mainloop<3>(lds, wsc, acc); break;
-    case 2: it.template mainloop<2>(lds, wsc, acc); break;
-    case 1: it.template mainloop<1>(lds, wsc, acc); break;
-    default: it.template mainloop<1>(lds, wsc, acc); break;   // keeps the barrier count equal across waves
+    case 4: it.template mainloop<4>(lds, par, wscb[0], acc); break;
+    case 3: it.template mainloop<3>(lds, par, wscb[0], acc); break;
+    case 2: it.template mainloop<2>(lds, par, wscb[0], acc); break;
+    case 1: it.template mainloop<1>(lds, par, wscb[0], acc); break;
+    default: it.template mainloop<1>(lds, par, wscb[0], acc); break;   // keeps the barrier count equal across waves
   }
+  const int npar = (par + it.nchunk) & 1;
+  if (next.valid) wide_begin<GATEUP>(a, next, lds + npar * WSTAGE, wscb[1]);
   const int rbeg = it.rbeg, nvalid = it.nvalid, I = it.I, col0 = it.col0;
   int brow[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) brow[j] = 16 * (wm + 4 * j);
 
-  store_item<FP8, GATEUP, WBM>(G, acc, brow, lane, wn, rbeg, nvalid, I, col0, ntile, H, red);
-  __syncthreads();   // the next work item reuses the LDS ring and the reduction area
+  store_item<FP8, GATEUP, WBM>(G, acc, brow, lane, wn, rbeg, nvalid, I, col0, cur.ntile,
+                               a.H, red);
+  // the next item's first step waits for its copies and syncs the workgroup
+  // before anything reads LDS; the reduction area is free once every wave is
+  // past this barrier (LDS only: the copies in flight are not waited for)
+  wait_lgkm0();
+  wg_barrier();
+  return npar;
 }
 
 // Work item L -> (tile-list slot, column tile).  The slots of one expert are
@@ -814,41 +878,66 @@ __global__ __launch_bounds__(TTHREADS, 1) void tiled_ffn_kernel(TiledArgs a) {
   }
 }
 
+// The first work item at or after L (stepping by `per`) that exists: a
+// tile-list slot that is filled and, for gate/up, a column tile inside its
+// group's width.  L is advanced to it (end: none).
+template <bool GATEUP>
+__device__ __forceinline__ WideWork wide_find(const TiledArgs &a, int &L, int end, int per, int nslots) {
+  WideWork w{{0, 0}, 0, 0};
+  for (; L < end; L += per) {
+    int slot, ntile;
+    map_item<WBM>(a, L, slot, ntile);
+    if (slot >= nslots) continue;
+    const TileEntry te = a.tiles[slot];
+    const FfnGroup &G = (te.ge >> 24) ? a.g1 : a.g0;
+    if (GATEUP && ntile * 128 >= G.I) continue;
+    w.te = te;
+    w.ntile = ntile;
+    w.valid = 1;
+    break;
+  }
+  return w;
+}
+
 template <bool GATEUP>
 __global__ __launch_bounds__(WTHREADS, 1) void wide_ffn_kernel(TiledArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   float *red = reinterpret_cast<float *>(lds + WNSTAGE * WSTAGE);
-  float *wsc = red + 2 * WBM;
+  float *wscs = red + 2 * WBM;   // two weight-scale buffers (current item, next item), 256 floats each
   const int nslots = a.hdr[0];
   const int count = nslots * a.nt;
   const int64_t n0 = (int64_t)min(a.hdr[1], nslots) * a.nt;
   const int xcd = blockIdx.x & 7, per = gridDim.x >> 3, slot0 = blockIdx.x >> 3;
   const int beg = range_start(xcd, n0, count, a.c0, a.c1), end = range_start(xcd + 1, n0, count, a.c0, a.c1);
-  for (int L = beg + slot0; L < end; L += per) {
-    int slot, ntile;
-    map_item<WBM>(a, L, slot, ntile);
-    if (slot < nslots) {
-      const TileEntry te = a.tiles[slot];
-      const FfnGroup G = (te.ge >> 24) ? a.g1 : a.g0;
-      if (!(GATEUP && ntile * 128 >= G.I)) {
-        if (G.fp8) {
-          if (G.tile16)
-            wide_item<true, GATEUP, true>(G, te, ntile, a.H, lds, red, wsc);
-          else
-            wide_item<true, GATEUP, false>(G, te, ntile, a.H, lds, red, wsc);
-        } else if (G.tile16) {
-          wide_item<false, GATEUP, true>(G, te, ntile, a.H, lds, red, wsc);
-        } else {
-          wide_item<false, GATEUP, false>(G, te, ntile, a.H, lds, red, wsc);
-        }
-      }
+  int L = beg + slot0;
+  WideWork cur = wide_find<GATEUP>(a, L, end, per, nslots);
+  if (!cur.valid) return;
+  int par = 0, wb = 0;
+  wide_begin<GATEUP>(a, cur, lds, wscs);
+  while (cur.valid) {
+    L += per;
+    const WideWork next = wide_find<GATEUP>(a, L, end, per, nslots);
+    float *const wscb[2] = {wscs + 256 * wb, wscs + 256 * (wb ^ 1)};
+    const FfnGroup &G = (cur.te.ge >> 24) ? a.g1 : a.g0;
+    if (G.fp8) {
+      if (G.tile16)
+        par = wide_item<true, GATEUP, true>(a, G, cur, next, par, lds, red, wscb);
+      else
+        par = wide_item<true, GATEUP, false>(a, G, cur, next, par, lds, red, wscb);
+    } else if (G.tile16) {
+      par = wide_item<false, GATEUP, true>(a, G, cur, next, par, lds, red, wscb);
+    } else {
+      par = wide_item<false, GATEUP, false>(a, G, cur, next, par, lds, red, wscb);
     }
+    wb ^= 1;
+    cur = next;
   }
 }
 
-// LDS: the copy ring, the h-scale reduction area, the weight-scale staging (H, I <= 16384)
+// LDS: the copy ring, the h-scale reduction area, the weight-scale staging (H, I <= 16384;
+// the wide kernel keeps two buffers, the current item's and the next one's)
 size_t tiled_lds_bytes() { return NSTAGE * TSTAGE + 2 * TBM * sizeof(float) + 2 * 128 * sizeof(float); }
-size_t wide_lds_bytes() { return WNSTAGE * WSTAGE + 2 * WBM * sizeof(float) + 2 * 128 * sizeof(float); }
+size_t wide_lds_bytes() { return WNSTAGE * WSTAGE + 2 * WBM * sizeof(float) + 2 * 2 * 128 * sizeof(float); }
 
 int num_compute_units() {
   static int cached[64] = {};

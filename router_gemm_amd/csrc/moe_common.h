@@ -138,6 +138,9 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
+// s_waitcnt lgkmcnt(0) only (LDS and scalar-memory operations complete).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
+
 // Workgroup barrier without a memory fence (the direct-to-LDS copies are
 // waited for explicitly with vmcnt); the empty asm keeps the compiler from
 // moving LDS accesses across it.
