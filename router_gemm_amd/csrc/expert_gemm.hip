@@ -840,7 +840,7 @@ static void run_stream(const StreamArgs &a, const FfnPlan &plan, int maxI, int s
 }
 
 hipError_t launch_expert_ffn(const FfnGroup *g, int ngroups, int H, const FfnPlan &plan, int32_t *tiles_ws,
-                             int site, hipStream_t st) {
+                             int site, hipStream_t st, bool tiles_ready) {
   if (ngroups < 1 || ngroups > kMaxGroups) return hipErrorInvalidValue;
   int64_t rows = 0;
   int maxI = 0;
@@ -871,7 +871,7 @@ hipError_t launch_expert_ffn(const FfnGroup *g, int ngroups, int H, const FfnPla
     }
     return hipGetLastError();
   }
-  build_tiles_kernel<<<1, 1024, 0, st>>>(a.g0, a.g1, ngroups, plan.bm, plan.max_tiles, tiles, hdr);
+  if (!tiles_ready) build_tiles_kernel<<<1, 1024, 0, st>>>(a.g0, a.g1, ngroups, plan.bm, plan.max_tiles, tiles, hdr);
   if (plan.tiled) {
     if (H % 256 != 0) return hipErrorInvalidValue;
     return launch_tiled_ffn(g, ngroups, H, tiles, hdr, num_compute_units(), plan.bm, site, st);

@@ -496,32 +496,43 @@ moe_status forward_impl(const moe_layer *L, const void *x, int64_t T, void *y, i
   e = moe::launch_router(static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(L->w_router), L->router_bias,
                          T, E, H, L->top_k, f.route.partial, f.route.S, ids, gates, nullptr, st);
   if (e != hipSuccess) return hip_status(e, "moe_forward: route");
-  e = moe::launch_counting_sort(ids, nullptr, 0, N, E, f.offsets, f.perm_src, f.perm_pos, f.sort, st);
-  if (e != hipSuccess) return hip_status(e, "moe_forward: sort");
-  // LDS-tiled expert kernels read the routed rows through the sort permutation
-  // (x quantised once per token for fp8 experts) instead of a gathered copy;
-  // their per-lane row offsets are 32-bit.
   moe::FfnGroup &R = f.groups[f.ngroups - 1];
-  if (f.ffn.plan.tiled && T * H * (int64_t)esz(L) < (int64_t(1) << 31)) {
-    R.xsrc = f.perm_src;
-    R.xdiv = L->top_k;
-    if (is_fp8(L)) {
-      e = moe::launch_quantize_rows(static_cast<const uint16_t *>(x), H, T, f.x_perm, f.x_scale, st);
-      if (e != hipSuccess) return hip_status(e, "moe_forward: quantise");
-    } else {
-      R.x = static_cast<const uint8_t *>(x);
-    }
+  bool tiles_ready = false;
+  if (!f.ffn.plan.tiled && moe::permute_small_ok(N, E)) {
+    // a decode-sized call: sort, tables, tile list and row gather in one launch
+    moe::SmallTiles tl{reinterpret_cast<moe::TileEntry *>(f.ffn.tiles + moe::kTileHdrWords), f.ffn.tiles,
+                       f.ffn.plan.bm, f.ffn.plan.max_tiles, f.ngroups == 2 ? 1 : 0, (int)T};
+    e = moe::launch_permute_small(ids, N, E, L->top_k, static_cast<const uint16_t *>(x), H, is_fp8(L), f.offsets,
+                                  f.perm_src, f.perm_pos, f.x_perm, f.x_scale, tl, st);
+    if (e != hipSuccess) return hip_status(e, "moe_forward: grouping");
+    tiles_ready = true;
   } else {
-    e = moe::launch_gather_rows(static_cast<const uint16_t *>(x), H, f.perm_src, nullptr, L->top_k, N, f.offsets + E,
-                                is_fp8(L), f.x_perm, f.x_scale, st);
-    if (e != hipSuccess) return hip_status(e, "moe_forward: gather");
+    e = moe::launch_counting_sort(ids, nullptr, 0, N, E, f.offsets, f.perm_src, f.perm_pos, f.sort, st);
+    if (e != hipSuccess) return hip_status(e, "moe_forward: sort");
+    // LDS-tiled expert kernels read the routed rows through the sort permutation
+    // (x quantised once per token for fp8 experts) instead of a gathered copy;
+    // their per-lane row offsets are 32-bit.
+    if (f.ffn.plan.tiled && T * H * (int64_t)esz(L) < (int64_t(1) << 31)) {
+      R.xsrc = f.perm_src;
+      R.xdiv = L->top_k;
+      if (is_fp8(L)) {
+        e = moe::launch_quantize_rows(static_cast<const uint16_t *>(x), H, T, f.x_perm, f.x_scale, st);
+        if (e != hipSuccess) return hip_status(e, "moe_forward: quantise");
+      } else {
+        R.x = static_cast<const uint8_t *>(x);
+      }
+    } else {
+      e = moe::launch_gather_rows(static_cast<const uint16_t *>(x), H, f.perm_src, nullptr, L->top_k, N, f.offsets + E,
+                                  is_fp8(L), f.x_perm, f.x_scale, st);
+      if (e != hipSuccess) return hip_status(e, "moe_forward: gather");
+    }
   }
   if (z_saved) {   // routed rows in expert order, then the shared expert's rows
     R.z = z_saved;
     if (f.ngroups == 2) f.groups[0].z = z_saved + (size_t)N * 2 * L->inter;
     if (f.shared_apart) f.sh_group.z = z_saved + (size_t)N * 2 * L->inter;
   }
-  e = moe::launch_expert_ffn(f.groups, f.ngroups, H, f.ffn.plan, f.ffn.tiles, MOE_SITE_GATE_UP, st);
+  e = moe::launch_expert_ffn(f.groups, f.ngroups, H, f.ffn.plan, f.ffn.tiles, MOE_SITE_GATE_UP, st, tiles_ready);
   if (e != hipSuccess) return hip_status(e, "moe_forward: experts");
   if (f.shared_apart) {
     e = moe::launch_expert_ffn(&f.sh_group, 1, H, f.ffn_sh.plan, f.ffn_sh.tiles, MOE_SITE_GATE_UP, st);

@@ -110,8 +110,9 @@ hipError_t launch_tiled_mx_ffn(const FfnGroup &g, int H, const void *tiles, int3
 // Compute units of the current device (cached per device).
 int num_compute_units();
 // site: timing site of the gate/up launch (the down launch uses site + 1).
+// tiles_ready: the tile list in tiles_ws was written beforehand (launch_permute_small).
 hipError_t launch_expert_ffn(const FfnGroup *g, int ngroups, int H, const FfnPlan &plan, int32_t *tiles_ws,
-                             int site, hipStream_t st);
+                             int site, hipStream_t st, bool tiles_ready = false);
 
 // Tile list of a row-segmented grouped launch: bm-row entries over g's
 // experts (expert_gemm.hip).
@@ -121,6 +122,23 @@ hipError_t launch_pack_tile16(const uint8_t *src, uint8_t *dst, int64_t count, i
                               hipStream_t st);
 hipError_t launch_build_tiles(const FfnGroup &g, int bm, int max_tiles, TileEntry *tiles, int32_t *hdr,
                               hipStream_t st);
+
+// Tile list written by the one-launch grouping below: bm-row entries; with
+// lead_group, group 0 is one expert of lead_rows rows (the shared expert) and
+// the sorted experts are group 1.  tiles == NULL: no list.
+struct SmallTiles {
+  TileEntry *tiles;
+  int32_t *hdr;
+  int bm, max_tiles, lead_group, lead_rows;
+};
+// The sort of the N = T*k routed assignments (token i / k) into nbins
+// experts, its tables, the tile list and the (fp8: quantised) row gather of
+// x, in one launch, for N <= 512 and nbins <= 4096 (permute_small_ok):
+// the results of launch_counting_sort + launch_gather_rows + the tile list.
+bool permute_small_ok(int64_t N, int64_t nbins);
+hipError_t launch_permute_small(const int32_t *keys, int64_t N, int64_t nbins, int k, const uint16_t *x, int64_t H,
+                                bool fp8, int32_t *offsets, int32_t *perm_src, int32_t *perm_pos, void *x_perm,
+                                float *x_scale, const SmallTiles &tl, hipStream_t st);
 
 // ---- backward of the layer, bf16 experts (backward.hip)
 // One set of experts (the routed experts, or the shared expert as G = 1 with

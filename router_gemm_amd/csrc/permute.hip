@@ -330,6 +330,182 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_one_chunk_kernel(
   }
 }
 
+// ---------------------------------------------------------------- small grouping, one launch
+
+// Everything between the router and the expert GEMMs for a decode-sized call
+// (N <= 512 assignments, one sort chunk), in one launch: each workgroup
+// sorts the N keys in LDS (the same total order, so every workgroup obtains
+// the same result), workgroup 0 writes the offsets, both permutation tables
+// and the expert GEMMs' tile list, and every wave gathers (and, fp8,
+// quantises) one row of x_perm.  Sorted position p holds the p-th assignment
+// in (expert, index) order, which is row p of the expert order, so a wave
+// needs no table to find its row's source.  Kernel boundaries cost several
+// microseconds each on this GPU; this replaces three launches.
+template <bool FP8>
+__global__ __launch_bounds__(SORT_THREADS) void permute_small_kernel(
+    const int32_t *__restrict__ keys, int64_t N, int nbins, int k, const uint16_t *__restrict__ x, int H,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ perm_src, int32_t *__restrict__ perm_pos,
+    void *__restrict__ x_perm, float *__restrict__ x_scale, SmallTiles tl) {
+  __shared__ uint64_t sk[CH];
+  __shared__ int32_t start[CH];
+  __shared__ int32_t off[ONE_CHUNK_BINS + 1];
+  __shared__ int32_t part[SORT_THREADS];
+  const int tid = threadIdx.x;
+  for (int b = tid; b <= nbins; b += SORT_THREADS) off[b] = 0;
+  sort_chunk_lds(keys, nullptr, 0, N, nbins, 0, sk, start);
+  const int nreal = (int)N;
+  for (int j = tid; j < nreal; j += SORT_THREADS) {
+    const uint32_t key = (uint32_t)(sk[j] >> 32);
+    const bool last = (j == nreal - 1) || ((uint32_t)(sk[j + 1] >> 32) != key);
+    if (last) off[key] = j - start[j] + 1;   // count of the bin (the dropped bin nbins included)
+  }
+  __syncthreads();
+  const int per = (nbins + SORT_THREADS - 1) / SORT_THREADS;
+  const int b0 = min(tid * per, nbins), b1 = min(b0 + per, nbins);
+  if (blockIdx.x == 0) {
+    // exclusive scan of the bin counts -> offsets (thread t owns bins [b0, b1))
+    int32_t sum = 0;
+    for (int b = b0; b < b1; ++b) sum += off[b];
+    part[tid] = sum;
+    __syncthreads();
+    for (int o = 1; o < SORT_THREADS; o <<= 1) {
+      const int32_t add = tid >= o ? part[tid - o] : 0;
+      __syncthreads();
+      part[tid] += add;
+      __syncthreads();
+    }
+    const int32_t total = part[SORT_THREADS - 1];
+    int32_t run = part[tid] - sum;
+    for (int b = b0; b < b1; ++b) {
+      const int32_t c = off[b];
+      offsets[b] = run;
+      off[b] = run;
+      run += c;
+    }
+    if (tid == 0) offsets[nbins] = total;
+    __syncthreads();
+    for (int j = tid; j < nreal; j += SORT_THREADS) {
+      const uint64_t v = sk[j];
+      const int32_t key = (int32_t)(v >> 32);
+      const int32_t i = (int32_t)(uint32_t)v;
+      if (key >= nbins) {
+        perm_pos[i] = -1;
+        continue;
+      }
+      perm_src[j] = i;   // j = off[key] + (j - start[j])
+      perm_pos[i] = j;
+    }
+    if (tl.tiles) {
+      // tile list: the preceding group's ceil(nrows0 / bm) entries (one
+      // expert holding rows 0..nrows0-1), then ceil(n_e / bm) per expert e
+      __syncthreads();
+      const int base0 = tl.lead_group ? (tl.lead_rows + tl.bm - 1) / tl.bm : 0;
+      int32_t cnt = 0;
+      for (int b = b0; b < b1; ++b) {
+        const int32_t n = (b + 1 < nbins ? off[b + 1] : total) - off[b];
+        cnt += (n + tl.bm - 1) / tl.bm;
+      }
+      part[tid] = cnt;
+      __syncthreads();
+      for (int o = 1; o < SORT_THREADS; o <<= 1) {
+        const int32_t add = tid >= o ? part[tid - o] : 0;
+        __syncthreads();
+        part[tid] += add;
+        __syncthreads();
+      }
+      const int g = tl.lead_group ? 1 : 0;
+      int32_t slot = base0 + part[tid] - cnt;
+      for (int b = b0; b < b1; ++b) {
+        const int32_t n = (b + 1 < nbins ? off[b + 1] : total) - off[b];
+        for (int m0 = 0; m0 < n; m0 += tl.bm, ++slot)
+          if (slot < tl.max_tiles) tl.tiles[slot] = TileEntry{(g << 24) | b, m0};
+      }
+      for (int j = tid; j < base0; j += SORT_THREADS)
+        if (j < tl.max_tiles) tl.tiles[j] = TileEntry{0, j * tl.bm};
+      if (tid == 0) {
+        tl.hdr[0] = min(base0 + part[SORT_THREADS - 1], tl.max_tiles);
+        tl.hdr[1] = min(base0, tl.max_tiles);
+      }
+    }
+  }
+  __syncthreads();
+  // n_valid: assignments with an expert in range (they sort first)
+  __shared__ int32_t nvalid_s;
+  if (tid == 0) {
+    int lo = 0, hi = nreal;   // first sorted position whose key is the dropped bin
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((int)(sk[mid] >> 32) >= nbins) hi = mid; else lo = mid + 1;
+    }
+    nvalid_s = lo;
+  }
+  __syncthreads();
+  const int64_t p = (int64_t)blockIdx.x * (SORT_THREADS / kWave) + wave_id();
+  if (p >= nvalid_s) return;
+  const int lane = lane_id();
+  const int64_t t = (int64_t)(uint32_t)sk[p] / k;
+  const uint16_t *src = x + t * H;
+  constexpr int BATCH = 4;
+  if constexpr (!FP8) {
+    uint16_t *dst = reinterpret_cast<uint16_t *>(x_perm) + p * H;
+    for (int c0 = lane * 8; c0 < H; c0 += 512 * BATCH) {
+      i32x4 raw[BATCH];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u)
+        if (c0 + 512 * u < H) raw[u] = load16(src + c0 + 512 * u);
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u)
+        if (c0 + 512 * u < H) store16(dst + c0 + 512 * u, raw[u]);
+    }
+  } else {
+    uint8_t *dst = reinterpret_cast<uint8_t *>(x_perm) + p * H;
+    for (int c0 = lane * 8; c0 < H; c0 += 512 * BATCH) {
+      i32x4 rawb[BATCH];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u)
+        if (c0 + 512 * u < H) rawb[u] = load16(src + c0 + 512 * u);
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int c = c0 + 512 * u;
+        if (c >= H) break;
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t wv = (uint32_t)rawb[u][q];
+          v[2 * q] = bf16_to_f32(wv & 0xFFFFu);
+          v[2 * q + 1] = bf16_to_f32(wv >> 16);
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[q]));
+        amax = wave_xor_max(amax, 16);
+        const float sc = group_scale(amax);
+        *reinterpret_cast<uint2 *>(dst + c) =
+            make_uint2(quant4_e4m3(v[0], v[1], v[2], v[3], sc), quant4_e4m3(v[4], v[5], v[6], v[7], sc));
+        if ((lane & 15) == 0) x_scale[p * (H / 128) + c / 128] = sc;
+      }
+    }
+  }
+}
+
+bool permute_small_ok(int64_t N, int64_t nbins) { return N >= 1 && N <= CH && nbins <= ONE_CHUNK_BINS; }
+
+hipError_t launch_permute_small(const int32_t *keys, int64_t N, int64_t nbins, int k, const uint16_t *x, int64_t H,
+                                bool fp8, int32_t *offsets, int32_t *perm_src, int32_t *perm_pos, void *x_perm,
+                                float *x_scale, const SmallTiles &tl, hipStream_t st) {
+  if (!permute_small_ok(N, nbins)) return hipErrorInvalidValue;
+  const unsigned g = (unsigned)cdiv(N, SORT_THREADS / kWave);
+  timing_before(2, st);
+  if (fp8)
+    permute_small_kernel<true><<<g, SORT_THREADS, 0, st>>>(keys, N, (int)nbins, k, x, (int)H, offsets, perm_src,
+                                                           perm_pos, x_perm, x_scale, tl);
+  else
+    permute_small_kernel<false><<<g, SORT_THREADS, 0, st>>>(keys, N, (int)nbins, k, x, (int)H, offsets, perm_src,
+                                                            perm_pos, x_perm, x_scale, tl);
+  timing_after(2, st);
+  return hipGetLastError();
+}
+
 hipError_t launch_counting_sort(const int32_t *keys, const int32_t *aux, int64_t aux_bound, int64_t N,
                                 int64_t nbins, int32_t *offsets, int32_t *perm_src, int32_t *perm_pos,
                                 int32_t *ws, hipStream_t st) {
