@@ -205,25 +205,14 @@ def measure(args, cfg, lt, layer, x, weight_layout, dev):
 
         counts = np.array([T])
     elif cfg.triples:
+        # one rank's expert-parallel share: the pre-routed triples through
+        # moe_forward_routed (grouping, routed + shared expert launches, combine)
         tok, exp, gate = W.make_triples(cfg)
         tok_g, exp_g, gate_g = (torch.from_numpy(a).to(dev) for a in (tok, exp, gate))
-        shared = B.Layer.shared_view(lt)
-        ws = torch.empty(max(B.moe_workspace_bytes(layer, T, N), B.moe_workspace_bytes(shared, T, T)),
-                         dtype=torch.uint8, device=dev)
-        off = torch.empty(E + 1, dtype=torch.int32, device=dev)
-        src = torch.empty(N, dtype=torch.int32, device=dev)
-        pos = torch.empty(N, dtype=torch.int32, device=dev)
-        xp = torch.empty((N, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
-        xs = torch.empty((N, H // 128), dtype=torch.float32, device=dev) if fp8 else None
-        yp = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
-        s_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-        sh_off = torch.tensor([0, T], dtype=torch.int32, device=dev)
+        ws = B.workspace(layer, T, N, dev)
 
         def step():
-            B.moe_permute(layer, x, T, exp_g, tok_g, N, off, src, pos, xp, xs, ws=ws)
-            B.moe_expert_ffn(layer, off, xp, xs, N, yp, ws=ws)
-            B.moe_expert_ffn(shared, sh_off, x, None, T, s_out, ws=ws)
-            B.moe_combine(layer, yp, B.MOE_BF16, pos, tok_g, gate_g, N, s_out, B.MOE_BF16, T, y, B.MOE_BF16, ws=ws)
+            B.moe_forward_routed(layer, x, T, exp_g, tok_g, gate_g, N, y, ws=ws)
 
         counts = np.bincount(exp, minlength=E)
     else:
@@ -279,9 +268,9 @@ def measure(args, cfg, lt, layer, x, weight_layout, dev):
         fl_routed_fp8 = fl_routed
     t_s = ms_per_step / 1e3
     mfma_util = (fl_routed_fp8 / (PEAK_TFLOPS["fp8"] * 1e12) + fl_bf16 / (PEAK_TFLOPS["bf16"] * 1e12)) / t_s
-    # gate/up launch(es) of one step: the routed experts' [gate; up] weights (+ scales), their
-    # input rows and h output, plus the shared expert's (same launch inside moe_forward; a second
-    # moe_expert_ffn launch at the same timing site for the pre-routed workload)
+    # gate/up launch of one step: the routed experts' [gate; up] weights (+ scales), their
+    # input rows and h output, plus the shared expert's (same launch inside moe_forward and
+    # moe_forward_routed)
     gu_bytes = active * w_gu_b + N * H * esz + N * I * esz + ((N * H // 128 + N * I // 128) * 4 if fp8 else 0)
     if Is > 0:
         gu_bytes += 2 * Is * H * 2 + T * H * 2 + T * Is * 2

@@ -249,6 +249,27 @@ moe_status moe_forward(const moe_layer *layer, const void *x, int64_t T,
                        int32_t *topk_ids, float *topk_gates,
                        void *ws, size_t ws_bytes, void *stream);
 
+/* The layer on pre-routed assignments: one expert-parallel rank's share of
+ * the layer ("Step-5 minimal inference", introduction and "Contents": TP=EP=8
+ * places 44 of the 352 experts on each rank), whose (token, expert, gate)
+ * triples come from elsewhere.
+ *   y[t] = shared(x[t]) + sum_{i: assign_token[i] = t} gates[i] * FFN_{assign_expert[i]}(x[t])
+ * in fp32 (shared first, then increasing i), rounded once to out_dtype: the
+ * result of moe_permute, moe_expert_ffn (routed experts, and the shared
+ * expert as its one-expert layer), moe_combine, with the shared expert's
+ * work inside the routed experts' launches (one gate/up and one down launch).
+ *   x             bf16 [T, H]
+ *   assign_expert int32 [N]: local expert of assignment i; assign_token int32 [N]:
+ *                 its token; an assignment with either out of range is dropped
+ *   gates         f32 [N], taken as given (no renormalisation)
+ *   y             [T, H] out (MOE_BF16 or MOE_F32); a token with no assignment
+ *                 gets the shared expert's output (or 0)
+ * top_k and w_router are not used (top_k may be 0).  T == 0 is a no-op. */
+moe_status moe_forward_routed(const moe_layer *layer, const void *x, int64_t T,
+                              const int32_t *assign_expert, const int32_t *assign_token, const float *gates,
+                              int64_t N, void *y, int32_t out_dtype,
+                              void *ws, size_t ws_bytes, void *stream);
+
 /* moe_forward without a workspace argument, for callers that cannot allocate
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation): its scratch memory is a device array the library owns,

@@ -52,7 +52,7 @@ class MoELayerC(C.Structure):
 
 
 EXPORTS = ["moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_forward", "moe_forward_noalloc", "moe_saved_z_floats", "moe_forward_train", "moe_backward_workspace_bytes",
+           "moe_forward", "moe_forward_routed", "moe_forward_noalloc", "moe_saved_z_floats", "moe_forward_train", "moe_backward_workspace_bytes",
            "moe_backward", "moe_pack_weights", "moe_status_string",
            "moe_last_error", "moe_timing_arm", "moe_timing_read"]
 
@@ -79,6 +79,8 @@ def lib() -> C.CDLL:
         L.moe_combine.argtypes = [vp, vp, i32, vp, vp, vp, i64, vp, i32, i64, vp, i32, vp, sz, vp]
         L.moe_forward.restype = C.c_int
         L.moe_forward.argtypes = [vp, vp, i64, vp, i32, vp, vp, vp, sz, vp]
+        L.moe_forward_routed.restype = C.c_int
+        L.moe_forward_routed.argtypes = [vp, vp, i64, vp, vp, vp, i64, vp, i32, vp, sz, vp]
         L.moe_forward_noalloc.restype = C.c_int
         L.moe_forward_noalloc.argtypes = [vp, vp, i64, vp, i32, vp, vp, vp]
         L.moe_backward_workspace_bytes.restype = sz
@@ -225,6 +227,14 @@ def moe_forward(layer: Layer, x, T, y, out_dtype=None, topk_ids=None, topk_gates
     od = dtype_code(y) if out_dtype is None else out_dtype
     _check(lib().moe_forward(layer.ref, _ptr(x), T, _ptr(y), od, _ptr(topk_ids), _ptr(topk_gates),
                              w, nb, _stream(stream)))
+
+
+def moe_forward_routed(layer: Layer, x, T, assign_expert, assign_token, gates, N, y, out_dtype=None, ws=None,
+                       stream=None):
+    w, nb = _ws(ws)
+    od = dtype_code(y) if out_dtype is None else out_dtype
+    _check(lib().moe_forward_routed(layer.ref, _ptr(x), T, _ptr(assign_expert), _ptr(assign_token), _ptr(gates), N,
+                                    _ptr(y), od, w, nb, _stream(stream)))
 
 
 def moe_forward_noalloc(layer: Layer, x, T, y, out_dtype=None, topk_ids=None, topk_gates=None, stream=None):

@@ -266,6 +266,50 @@ ForwardWs carve_forward(Carve &c, const moe_layer *L, const void *x, int64_t T, 
   return f;
 }
 
+// Forward for pre-routed assignments: the grouping, the gathered (and, fp8,
+// quantised) rows, routed + shared expert FFN, and the per-token grouping of
+// the combine.
+struct RoutedWs {
+  int32_t *offsets, *perm_src, *perm_pos, *sort;
+  uint8_t *x_perm;
+  float *x_scale;
+  FfnWs ffn;
+  moe::FfnGroup groups[moe::kMaxGroups];
+  int ngroups;
+  bool shared_apart;
+  FfnWs ffn_sh;
+  moe::FfnGroup sh_group;
+  uint16_t *y_perm;
+  void *sh_out;
+  CombineWs comb;
+};
+RoutedWs carve_routed(Carve &c, const moe_layer *L, const void *x, int64_t T, int64_t N, bool out_f32) {
+  RoutedWs f;
+  const int H = L->hidden, E = L->num_experts;
+  f.offsets = c.take<int32_t>((size_t)E + 1);
+  f.perm_src = c.take<int32_t>((size_t)N + 1);
+  f.perm_pos = c.take<int32_t>((size_t)N + 1);
+  f.sort = carve_sort(c, N, E);
+  f.x_perm = c.take<uint8_t>((size_t)N * H * esz(L) + 16);
+  f.x_scale = is_fp8(L) ? c.take<float>((size_t)N * (H / 128) + 1) : nullptr;
+  f.y_perm = c.take<uint16_t>((size_t)N * H + 8);
+  f.ngroups = 0;
+  f.shared_apart = L->shared_inter > 0 && L->shared_inter % 128 != 0 && L->inter % 128 == 0;
+  f.sh_out = nullptr;
+  if (L->shared_inter > 0) {
+    f.sh_out = c.take<uint8_t>((size_t)T * H * (out_f32 ? 4 : 2) + 16);
+    if (!f.shared_apart) f.groups[f.ngroups++] = shared_group(L, x, nullptr, T, f.sh_out, out_f32);
+  }
+  f.groups[f.ngroups++] = routed_group(L, f.x_perm, f.x_scale, f.offsets, N, f.y_perm, false);
+  f.ffn = carve_ffn(c, f.groups, f.ngroups, H);
+  if (f.shared_apart) {
+    f.sh_group = shared_group(L, x, nullptr, T, f.sh_out, out_f32);
+    f.ffn_sh = carve_ffn(c, &f.sh_group, 1, H);
+  }
+  f.comb = carve_combine(c, T, N);
+  return f;
+}
+
 // Backward: the sort, rows gathered into expert order, and each expert set's
 // scratch (routed experts; shared expert).
 struct BackwardWs {
@@ -329,6 +373,11 @@ size_t need_forward(const moe_layer *L, int64_t T) {
   carve_forward(c, L, nullptr, T, true);
   return c.used;
 }
+size_t need_routed(const moe_layer *L, int64_t T, int64_t N) {
+  Carve c(nullptr);
+  carve_routed(c, L, nullptr, T, N, true);
+  return c.used;
+}
 
 }  // namespace
 
@@ -354,6 +403,7 @@ size_t moe_workspace_bytes(const moe_layer *L, int64_t T, int64_t N) {
   upd(need_permute(L, N));
   upd(need_ffn(L, N));
   upd(need_combine(T, N, true));
+  upd(need_routed(L, T, N));
   if (L->top_k >= 1) {
     upd(need_route(L, T));
     upd(need_forward(L, T));
@@ -547,6 +597,50 @@ moe_status forward_impl(const moe_layer *L, const void *x, int64_t T, void *y, i
 moe_status moe_forward(const moe_layer *L, const void *x, int64_t T, void *y, int32_t out_dtype, int32_t *topk_ids,
                        float *topk_gates, void *ws, size_t ws_bytes, void *stream) {
   return forward_impl(L, x, T, y, out_dtype, topk_ids, topk_gates, nullptr, ws, ws_bytes, stream);
+}
+
+moe_status moe_forward_routed(const moe_layer *L, const void *x, int64_t T, const int32_t *assign_expert,
+                              const int32_t *assign_token, const float *gates, int64_t N, void *y, int32_t out_dtype,
+                              void *ws, size_t ws_bytes, void *stream) {
+  moe_status s;
+  if ((s = check_layer_shape(L, false)) != MOE_OK) return s;
+  if ((s = check_rows(T, N)) != MOE_OK) return s;
+  if (!out_dtype_ok(out_dtype)) return fail(MOE_EUNSUPPORTED, "out_dtype %d is not MOE_BF16 or MOE_F32", out_dtype);
+  if (T > 0) {
+    if (!x || !y) return fail(MOE_EINVAL, "NULL forward argument");
+    if (!aligned16(x) || !aligned16(y)) return fail(MOE_EINVAL, "x or y not 16-byte aligned");
+    if ((s = check_shared(L)) != MOE_OK) return s;
+  }
+  if (N > 0) {
+    if (!assign_expert || !assign_token || !gates) return fail(MOE_EINVAL, "NULL assignment argument");
+    if ((s = check_expert_weights(L)) != MOE_OK) return s;
+  }
+  if (T == 0) return MOE_OK;   // no token: every assignment is out of range, nothing to write
+  if ((s = check_ws(ws, ws_bytes, need_routed(L, T, N))) != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const bool out_f32 = out_dtype == MOE_F32;
+  const int H = L->hidden, E = L->num_experts;
+  Carve c(ws);
+  RoutedWs f = carve_routed(c, L, x, T, N, out_f32);
+  hipError_t e = moe::launch_counting_sort(assign_expert, assign_token, T, N, E, f.offsets, f.perm_src, f.perm_pos,
+                                           f.sort, st);
+  if (e != hipSuccess) return hip_status(e, "moe_forward_routed: sort");
+  e = moe::launch_gather_rows(static_cast<const uint16_t *>(x), H, f.perm_src, assign_token, 1, N, f.offsets + E,
+                              is_fp8(L), f.x_perm, f.x_scale, st);
+  if (e != hipSuccess) return hip_status(e, "moe_forward_routed: gather");
+  // routed and shared expert in the same launches
+  e = moe::launch_expert_ffn(f.groups, f.ngroups, H, f.ffn.plan, f.ffn.tiles, MOE_SITE_GATE_UP, st);
+  if (e != hipSuccess) return hip_status(e, "moe_forward_routed: experts");
+  if (f.shared_apart) {
+    e = moe::launch_expert_ffn(&f.sh_group, 1, H, f.ffn_sh.plan, f.ffn_sh.tiles, MOE_SITE_GATE_UP, st);
+    if (e != hipSuccess) return hip_status(e, "moe_forward_routed: shared expert");
+  }
+  e = moe::launch_counting_sort(assign_token, nullptr, 0, N, T, f.comb.tok_off, f.comb.tok_list, nullptr,
+                                f.comb.sort, st);
+  if (e != hipSuccess) return hip_status(e, "moe_forward_routed: token sort");
+  e = moe::launch_combine(f.y_perm, false, f.perm_pos, f.comb.tok_off, f.comb.tok_list, 0, gates, f.sh_out, out_f32, T,
+                          H, N, y, out_f32, st);
+  return hip_status(e, "moe_forward_routed: combine");
 }
 
 }  // extern "C"

@@ -28,7 +28,15 @@ constexpr int SORT_THREADS = 256;
 constexpr int SCAN_BLOCK = 256;         // bins per workgroup of the multi-workgroup scan
 constexpr int64_t SINGLE_SCAN_BINS = 4096;
 
+// The chunk table of the stable sort has (N / 512) * (nbins + 1) words: past
+// kTableWords (many bins, e.g. one per token of a long pre-routed batch) the
+// sort takes an O(N + nbins) path instead (sort_wide_bins below).
+constexpr int64_t kTableWords = int64_t(4) << 20;
+static bool sort_uses_table(int64_t N, int64_t nbins) { return cdiv(N, CH) * (nbins + 1) <= kTableWords; }
+
 size_t sort_ws_words(int64_t N, int64_t nbins) {
+  if (!sort_uses_table(N, nbins))   // bin cursors [nbins+1], the unordered list [N], scan block totals
+    return (size_t)((nbins + 1) + N + cdiv(nbins, SCAN_BLOCK) + 1);
   const int64_t nchunk = cdiv(N, CH);
   // chunk counts [nchunk][nbins+1], sorted keys/indices/ranks [nchunk*CH] x 3,
   // per-block totals of the multi-workgroup scan
@@ -330,6 +338,100 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_one_chunk_kernel(
   }
 }
 
+// ---------------------------------------------------------------- many bins: O(N + nbins)
+
+// Stable counting sort for many bins without the [chunk][bin] table:
+// (1) zero the bin counters, (2) count each bin with integer atomics (the
+// totals do not depend on the order of the additions), (3) exclusive scan
+// (the scan kernels above on a one-chunk table), (4) place every element at
+// its bin's cursor with an atomic increment (an order that varies from run to
+// run), (5) one wave per bin restores increasing element index: the final
+// slot of element v is its bin's offset plus the number of elements of the
+// bin smaller than v.  Outputs are those of the chunked sort, bit for bit.
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t *__restrict__ p, int64_t n, int32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__device__ __forceinline__ bool key_valid(const int32_t *keys, const int32_t *aux, int64_t aux_bound, int nbins,
+                                          int64_t i, int32_t &key) {
+  key = keys[i];
+  bool ok = key >= 0 && key < nbins;
+  if (aux) {
+    const int32_t a = aux[i];
+    ok = ok && a >= 0 && a < aux_bound;
+  }
+  return ok;
+}
+
+__global__ __launch_bounds__(256) void count_bins_kernel(const int32_t *__restrict__ keys, const int32_t *__restrict__ aux,
+                                                         int64_t aux_bound, int64_t N, int nbins,
+                                                         int32_t *__restrict__ cnt) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int32_t key;
+  if (i < N && key_valid(keys, aux, aux_bound, nbins, i, key)) atomicAdd(&cnt[key], 1);
+}
+
+__global__ __launch_bounds__(256) void place_bins_kernel(const int32_t *__restrict__ keys, const int32_t *__restrict__ aux,
+                                                         int64_t aux_bound, int64_t N, int nbins,
+                                                         int32_t *__restrict__ cursor, int32_t *__restrict__ unordered,
+                                                         int32_t *__restrict__ perm_pos) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= N) return;
+  int32_t key;
+  if (key_valid(keys, aux, aux_bound, nbins, i, key)) {
+    unordered[atomicAdd(&cursor[key], 1)] = (int32_t)i;
+  } else if (perm_pos) {
+    perm_pos[i] = -1;
+  }
+}
+
+// One wave per bin: rank of each element among the bin's elements.
+__global__ __launch_bounds__(256) void order_bins_kernel(const int32_t *__restrict__ offsets, int nbins,
+                                                         const int32_t *__restrict__ unordered,
+                                                         int32_t *__restrict__ perm_src, int32_t *__restrict__ perm_pos) {
+  const int64_t b = (int64_t)blockIdx.x * 4 + wave_id();
+  if (b >= nbins) return;
+  const int lane = lane_id();
+  const int32_t o0 = offsets[b], n = offsets[b + 1] - o0;
+  for (int q0 = 0; q0 < n; q0 += kWave) {
+    const bool mine = q0 + lane < n;
+    const int32_t v = mine ? unordered[o0 + q0 + lane] : 0;
+    int32_t rank = 0;
+    for (int r0 = 0; r0 < n; r0 += kWave) {
+      const int32_t u = r0 + lane < n ? unordered[o0 + r0 + lane] : 0x7FFFFFFF;
+      for (int l = 0; l < kWave && r0 + l < n; ++l) rank += __shfl(u, l, kWave) < v ? 1 : 0;
+    }
+    if (mine) {
+      if (perm_src) perm_src[o0 + rank] = v;
+      if (perm_pos) perm_pos[v] = o0 + rank;
+    }
+  }
+}
+
+static hipError_t sort_wide_bins(const int32_t *keys, const int32_t *aux, int64_t aux_bound, int64_t N, int64_t nbins,
+                                 int32_t *offsets, int32_t *perm_src, int32_t *perm_pos, int32_t *ws, hipStream_t st) {
+  int32_t *cc = ws;                       // [1][nbins+1]: counts, then cursors
+  int32_t *unordered = cc + nbins + 1;    // [N]
+  int32_t *bsum = unordered + N;
+  fill_i32_kernel<<<(unsigned)cdiv(nbins + 1, 256), 256, 0, st>>>(cc, nbins + 1, 0);
+  if (N > 0) count_bins_kernel<<<(unsigned)cdiv(N, 256), 256, 0, st>>>(keys, aux, aux_bound, N, (int)nbins, cc);
+  if (nbins <= SINGLE_SCAN_BINS) {
+    scan_counts_kernel<<<1, 1024, 0, st>>>(cc, 1, (int)nbins, offsets);
+  } else {
+    const unsigned nb = (unsigned)cdiv(nbins, SCAN_BLOCK);
+    scan_bins_pass1<<<nb, SCAN_BLOCK, 0, st>>>(cc, 1, (int)nbins, offsets, bsum);
+    scan_bins_pass2<<<1, 1024, 0, st>>>(bsum, (int)nb, (int)nbins, offsets);
+    scan_bins_pass3<<<nb, SCAN_BLOCK, 0, st>>>(cc, 1, (int)nbins, offsets, bsum);
+  }
+  if (N > 0) {
+    place_bins_kernel<<<(unsigned)cdiv(N, 256), 256, 0, st>>>(keys, aux, aux_bound, N, (int)nbins, cc, unordered,
+                                                              perm_pos);
+    order_bins_kernel<<<(unsigned)cdiv(nbins, 4), 256, 0, st>>>(offsets, (int)nbins, unordered, perm_src, perm_pos);
+  }
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- small grouping, one launch
 
 // Everything between the router and the expert GEMMs for a decode-sized call
@@ -515,6 +617,11 @@ hipError_t launch_counting_sort(const int32_t *keys, const int32_t *aux, int64_t
   int32_t *s_idx = s_key + nchunk * CH;
   int32_t *s_rank = s_idx + nchunk * CH;
   timing_before(2, st);
+  if (!sort_uses_table(N, nbins)) {
+    const hipError_t e = sort_wide_bins(keys, aux, aux_bound, N, nbins, offsets, perm_src, perm_pos, ws, st);
+    timing_after(2, st);
+    return e;
+  }
   if (N <= CH && nbins <= ONE_CHUNK_BINS) {
     sort_one_chunk_kernel<<<1, SORT_THREADS, 0, st>>>(keys, aux, aux_bound, N, (int)nbins, offsets, perm_src,
                                                      perm_pos);

@@ -201,3 +201,19 @@ def test_weight_layout_and_pack_refusals_without_gpu():
         assert pack(n=n, rows=rows, rb=rb) == B.MOE_EINVAL, (n, rows, rb)
     assert pack(dst=FAKE + 1024) == B.MOE_EINVAL and b"overlap" in lib.moe_last_error()
     assert pack(n=2, dst=FAKE + 2048) == B.MOE_EINVAL and b"overlap" in lib.moe_last_error()
+
+
+def test_forward_routed_refusals():
+    lib = B.lib()
+    L = layer()
+    f = lambda L=L, T=16, N=20, x=FAKE, ae=FAKE, at=FAKE, g=FAKE, y=FAKE, od=B.MOE_BF16, ws=FAKE, nb=1 << 40: \
+        lib.moe_forward_routed(C.byref(L), x, T, ae, at, g, N, y, od, ws, nb, None)
+    assert f(x=None) == B.MOE_EINVAL
+    assert f(ae=None) == B.MOE_EINVAL and f(at=None) == B.MOE_EINVAL and f(g=None) == B.MOE_EINVAL
+    assert f(od=7) == B.MOE_EUNSUPPORTED
+    assert f(T=-1) == B.MOE_EINVAL
+    assert f(nb=16) == B.MOE_EWORKSPACE
+    assert f(x=FAKE + 4) == B.MOE_EINVAL                     # misaligned
+    assert f(T=0, x=None, y=None) == B.MOE_OK                # no-op
+    bad = layer(H=100)
+    assert f(L=bad) == B.MOE_EUNSUPPORTED

@@ -153,3 +153,33 @@ def test_dense_ff_full_shape_sampled(layout):
     print(f"[dense_ff_bf16 {layout}] max rel err {err.max():.3e} over {len(rows)} rows", flush=True)
     assert err.max() < TOL["bf16"]
     assert err.max() < 5e-5              # regression bar (observed 1.5e-5: bf16 h, no fp8 step)
+
+
+def test_ep_share_forward_routed():
+    """The same EP-8 share through moe_forward_routed (the shared expert inside
+    the routed experts' launches): sampled tokens against the oracle, the
+    hottest tokens and tokens without a local assignment included."""
+    cfg = W.get_config("c4")
+    print("[ep8_share_fp8 routed] building layer", flush=True)
+    lt = W.make_layer(cfg, dev())
+    x = W.make_x(cfg, dev())
+    tok, exp, gate = W.make_triples(cfg)
+    d = dev()
+    T, N, H = cfg.T, cfg.N, cfg.H
+    for packed in (False, True):
+        layer = B.Layer.from_tensors(lt, top_k=0)
+        if packed:
+            layer = layer.packed()
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=d)
+        tok_g, exp_g, gate_g = (torch.from_numpy(a).to(d) for a in (tok, exp, gate))
+        B.moe_forward_routed(layer, x, T, exp_g, tok_g, gate_g, N, y, ws=B.workspace(layer, T, N, d))
+        torch.cuda.synchronize()
+        OL = oracle_layer(lt)
+        rng = np.random.default_rng(3)
+        hot = np.bincount(tok, minlength=T)
+        sample = np.concatenate([rng.choice(T, 16, replace=False), np.argsort(-hot)[:4], np.nonzero(hot == 0)[0][:2]])
+        y_ref = oracle.forward_triples(OL, W.bf16_bits(x), tok, exp, gate, token_list=sample)
+        err = rel_err_rows(to_np(y)[sample], y_ref)
+        print(f"[ep8_share_fp8 routed, {'tile16' if packed else 'rows'}] max rel err {err.max():.3e}", flush=True)
+        assert err.max() < TOL["fp8"]
+        assert err.max() < 7.5e-3            # regression bar

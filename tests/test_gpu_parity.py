@@ -514,3 +514,76 @@ def test_combine_many_tokens_uses_multiblock_scan():
     torch.cuda.synchronize()
     y_ref = oracle.combine(yp.astype(np.float64), pos, gates, T, tok=tok)
     assert rel_err_rows(to_np(y), y_ref).max() < 1e-6
+
+
+def test_combine_per_token_grouping_without_chunk_table():
+    """Many tokens and assignments (T = 40000, N = 60000: the stable sort's
+    chunk table would pass 4M words), so the per-token grouping takes the
+    O(N + T) path (atomic counts and placement, then a per-token rank pass):
+    sums against the oracle, bit-identical repeats, and the summation order
+    (increasing assignment index) on triples whose fp32 sum depends on it."""
+    rng = np.random.default_rng(23)
+    T, H, N = 40000, 128, 60000
+    d = dev()
+    yp = rng.standard_normal((N, H)).astype(np.float32)
+    pos = rng.permutation(N).astype(np.int32)
+    tok = rng.integers(0, T, size=N).astype(np.int32)
+    tok[rng.choice(N, 9, replace=False)] = -3          # dropped
+    gates = rng.random(N).astype(np.float32)
+    # order probes: token t0 has exactly three assignments, i0 < i1 < i2 with
+    # rows +2^25, 1, -2^25 and gates 1: in index order (2^25 + 1) - 2^25 = 0,
+    # while -2^25 or 1 placed before 2^25 leaves 1
+    probes = rng.choice(T, 50, replace=False)
+    tok[np.isin(tok, probes)] = rng.choice(np.setdiff1d(np.arange(T), probes), int(np.isin(tok, probes).sum()))
+    for t0 in probes:
+        idx = np.sort(rng.choice(np.nonzero(~np.isin(tok, probes))[0], 3, replace=False))
+        tok[idx] = t0
+        for v, i in zip((2.0 ** 25, 1.0, -(2.0 ** 25)), idx):
+            yp[pos[i]] = v
+            gates[i] = 1.0
+    layer = B.Layer(H, 128, 8, 0, B.MOE_BF16, None, None)
+    args = (torch.from_numpy(yp).to(d), B.MOE_F32, torch.from_numpy(pos).to(d), torch.from_numpy(tok).to(d),
+            torch.from_numpy(gates).to(d), N, None, 0, T)
+    outs = []
+    for _ in range(2):
+        y = torch.empty((T, H), dtype=torch.float32, device=d)
+        B.moe_combine(layer, *args, y, B.MOE_F32, ws=B.workspace(layer, T, N, d))
+        torch.cuda.synchronize()
+        outs.append(y)
+    assert torch.equal(outs[0], outs[1])
+    y = outs[0].cpu().numpy()
+    assert (y[probes] == 0).all(), "assignments of a token were not summed in increasing index order"
+    keep = ~np.isin(np.arange(T), probes)
+    y_ref = oracle.combine(yp.astype(np.float64), pos, gates, T, tok=tok)
+    assert rel_err_rows(y[keep], y_ref[keep]).max() < 1e-6
+
+
+@pytest.mark.parametrize("name,over,N", [("small_fp8", dict(T=300), 700), ("small_fp8", dict(T=300, Is=192), 700),
+                                         ("c0", dict(T=150), 333), ("small_fp8", dict(T=2000), 6000)])
+def test_forward_routed_matches_oracle(name, over, N):
+    """moe_forward_routed on seeded pre-routed triples (some dropped: expert or
+    token out of range; some tokens without an assignment) against the oracle
+    on every token; small (streaming kernels) and large (LDS-tiled) shares,
+    and a shared expert of a width that gets its own launch."""
+    cfg = W.get_config(name, **over)
+    lt = W.make_layer(cfg, dev())
+    x = W.make_x(cfg, dev())
+    rng = np.random.default_rng(N)
+    T, E = cfg.T, cfg.E
+    tok = rng.integers(0, T, size=N).astype(np.int32)
+    exp = rng.integers(0, E, size=N).astype(np.int32)
+    gate = rng.random(N).astype(np.float32)
+    exp[rng.choice(N, 5, replace=False)] = E + 2
+    tok[rng.choice(N, 5, replace=False)] = -1
+    tok[np.isin(tok, [3, 7])] = 0               # tokens 3 and 7 get only the shared expert
+    d = dev()
+    layer = B.Layer.from_tensors(lt, top_k=0)
+    y = torch.empty((T, cfg.H), dtype=torch.float32, device=d)
+    B.moe_forward_routed(layer, x, T, torch.from_numpy(exp).to(d), torch.from_numpy(tok).to(d),
+                         torch.from_numpy(gate).to(d), N, y, ws=B.workspace(layer, T, N, d))
+    torch.cuda.synchronize()
+    OL = oracle_layer(lt)
+    y_ref = oracle.forward_triples(OL, W.bf16_bits(x), tok, exp, gate)
+    err = rel_err_rows(to_np(y), y_ref)
+    _print(f"forward_routed {name} {over} N={N}: max rel err {err.max():.3e}")
+    assert err.max() < TOL[cfg.expert_dtype]
