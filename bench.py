@@ -64,13 +64,15 @@ def parse():
 # 1 GiB device copy (bench.py --copy-calibration).  Valid only for the kernel sources they were
 # taken on: a different hash of the dominant kernel's sources (KERNEL_SOURCES) reports null.
 TRAFFIC = {
-    "decode_bf16": {"src_hash": "a207159d7d8c0496", "fetch_kib": 3274981.4, "write_kib": 1738.7557, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_fp8": {"src_hash": "a207159d7d8c0496", "fetch_kib": 1651565.1, "write_kib": 1143.0369, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_mxfp4": {"src_hash": "a207159d7d8c0496", "fetch_kib": 901931.72, "write_kib": 1184.2812, "fetch_scale": 2.0, "write_scale": 1.0},
-    "dense_ff_bf16": {"src_hash": "a207159d7d8c0496", "fetch_kib": 1360456.4, "write_kib": 223783.5, "fetch_scale": 2.0, "write_scale": 1.0},
-    "prefill_fp8": {"src_hash": "a207159d7d8c0496", "fetch_kib": 3332139.3, "write_kib": 139351.34, "fetch_scale": 2.0, "write_scale": 1.0},
-    "ep8_share_fp8": {"src_hash": "a207159d7d8c0496", "fetch_kib": 377384.14, "write_kib": 40499.205, "fetch_scale": 2.0, "write_scale": 1.0},
-    "train_bf16": {"src_hash": "4f96340a864f115c", "fetch_kib": 4397870.4, "write_kib": 26396252.0, "fetch_scale": 2.0, "write_scale": 1.0},
+    "prefill_fp8": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 3279064.55, "write_kib": 136931.61, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_fp8": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 1651577.25, "write_kib": 1142.84, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_bf16": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 3274984.22, "write_kib": 1738.03, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_mxfp4": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 901304.02, "write_kib": 1184.88, "fetch_scale": 2.0, "write_scale": 1.0},
+    "prefill_mxfp4": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 854758.88, "write_kib": 66423.19, "fetch_scale": 2.0, "write_scale": 1.0},
+    "ep8_share_fp8": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 853764.47, "write_kib": 77136.86, "fetch_scale": 2.0, "write_scale": 1.0},
+    "dense_ff_bf16": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 1360289.88, "write_kib": 221708.33, "fetch_scale": 2.0, "write_scale": 1.0},
+    # per step: the four weight-gradient launches (routed dW_down, dW_gate_up; the shared expert's two)
+    "train_bf16": {"src_hash": "c4be7805626206ce", "fetch_kib": 4398878.92, "write_kib": 26400004.28, "fetch_scale": 2.0, "write_scale": 1.0},
 }
 
 
