@@ -133,7 +133,7 @@ struct SmallTiles {
 };
 // The sort of the N = T*k routed assignments (token i / k) into nbins
 // experts, its tables, the tile list and the (fp8: quantised) row gather of
-// x, in one launch, for N <= 512 and nbins <= 4096 (permute_small_ok):
+// x, in one launch, for N <= 512 and nbins <= 1024 (permute_small_ok):
 // the results of launch_counting_sort + launch_gather_rows + the tile list.
 bool permute_small_ok(int64_t N, int64_t nbins);
 hipError_t launch_permute_small(const int32_t *keys, int64_t N, int64_t nbins, int k, const uint16_t *x, int64_t H,

@@ -434,118 +434,175 @@ static hipError_t sort_wide_bins(const int32_t *keys, const int32_t *aux, int64_
 
 // ---------------------------------------------------------------- small grouping, one launch
 
+// Stable counting sort of N <= 512 keys over nbins <= 1024 bins inside one
+// workgroup of 256 threads, with a handful of barriers instead of a sorting
+// network.  Element i lies in chunk c = i / 64, the 64 lanes of one wave
+// (wave w holds chunks w and w + 4).  Inside a chunk the lanes with the same
+// key are found with one ballot per key bit (the lanes that agree with this
+// lane on every bit); the lowest of them writes the chunk's count of that
+// key, and a lane's rank among them is the number of them below it.  A pass
+// over the bins turns the [chunk][bin] counts into bases (a prefix over the
+// chunks, then an exclusive scan of the bin totals), and element i lands at
+// base[c][key] + its rank in the chunk: increasing index inside every bin,
+// the unique stable order.  Keys outside [0, nbins) are dropped.  Counts are
+// plain stores, one per (chunk, key), so every result is reproducible.
+constexpr int SMALL_SORT_BINS = 1024;
+constexpr int SMALL_CHUNKS = CH / kWave;
+static_assert(SMALL_CHUNKS == 2 * (SORT_THREADS / kWave), "two chunks per wave");
+struct SmallSortLds {
+  int32_t cnt[SMALL_CHUNKS * SMALL_SORT_BINS];   // [chunk][bin]: counts, then bases
+  int32_t off[SMALL_SORT_BINS + 1];              // bin offsets; off[nbins] = number of valid keys
+  int32_t src[CH];                               // src[p] = element at sorted position p
+  int32_t wsum[SORT_THREADS / kWave];            // per-wave totals of a block scan
+};
+
+// Exclusive scan of one value per thread over the workgroup (thread order);
+// *total = the sum of all.  Every thread of the workgroup must call it.
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *wsum, int32_t *total) {
+  const int lane = lane_id(), w = wave_id();
+  int32_t inc = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int32_t u = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += u;
+  }
+  if (lane == kWave - 1) wsum[w] = inc;
+  __syncthreads();
+  int32_t base = 0, tot = 0;
+#pragma unroll
+  for (int q = 0; q < SORT_THREADS / kWave; ++q) {
+    const int32_t s = wsum[q];
+    if (q < w) base += s;
+    tot += s;
+  }
+  *total = tot;
+  __syncthreads();   // wsum is free again
+  return base + inc - v;
+}
+
+// Sorts keys[0..N) into L (off, src); pos[q] = sorted position of element
+// threadIdx.x + 256 q, or -1 (dropped or past N).  Returns the number of valid keys.
+__device__ __forceinline__ int small_sort_lds(const int32_t *__restrict__ keys, int N, int nbins, SmallSortLds &L,
+                                              int32_t pos[2]) {
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  for (int b = tid; b < SMALL_CHUNKS * nbins; b += SORT_THREADS) L.cnt[b] = 0;
+  int32_t key[2];
+  bool valid[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int i = tid + SORT_THREADS * q;
+    key[q] = i < N ? keys[i] : -1;
+    valid[q] = key[q] >= 0 && key[q] < nbins;
+    if (!valid[q]) key[q] = nbins;   // every dropped or padding lane shares the id nbins (never counted)
+  }
+  __syncthreads();
+  const int nbits = 32 - __builtin_clz((unsigned)nbins);   // ids 0..nbins
+  const uint64_t below = (1ull << lane) - 1;
+  int32_t rank[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    uint64_t same = ~0ull;
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (key[q] >> b) & 1;
+      const uint64_t ones = __builtin_amdgcn_ballot_w64(bit);
+      same &= bit ? ones : ~ones;
+    }
+    rank[q] = __builtin_popcountll(same & below);
+    if (valid[q] && rank[q] == 0) L.cnt[(w + 4 * q) * nbins + key[q]] = __builtin_popcountll(same);
+  }
+  __syncthreads();
+  // thread t owns bins [b0, b1): prefix over the chunks, then the bin totals' scan
+  const int per = (nbins + SORT_THREADS - 1) / SORT_THREADS;
+  const int b0 = min(tid * per, nbins), b1 = min(b0 + per, nbins);
+  int32_t sum = 0;
+  for (int b = b0; b < b1; ++b) {
+    int32_t run = 0;
+#pragma unroll
+    for (int c = 0; c < SMALL_CHUNKS; ++c) {
+      const int32_t n = L.cnt[c * nbins + b];
+      L.cnt[c * nbins + b] = run;
+      run += n;
+    }
+    L.off[b] = run;
+    sum += run;
+  }
+  int32_t total;
+  int32_t base = block_exclusive_scan(sum, L.wsum, &total);
+  for (int b = b0; b < b1; ++b) {
+    const int32_t n = L.off[b];
+    L.off[b] = base;
+#pragma unroll
+    for (int c = 0; c < SMALL_CHUNKS; ++c) L.cnt[c * nbins + b] += base;
+    base += n;
+  }
+  if (tid == 0) L.off[nbins] = total;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    pos[q] = -1;
+    if (valid[q]) {
+      pos[q] = L.cnt[(w + 4 * q) * nbins + key[q]] + rank[q];
+      L.src[pos[q]] = tid + SORT_THREADS * q;
+    }
+  }
+  __syncthreads();
+  return total;
+}
+
 // Everything between the router and the expert GEMMs for a decode-sized call
-// (N <= 512 assignments, one sort chunk), in one launch: each workgroup
-// sorts the N keys in LDS (the same total order, so every workgroup obtains
-// the same result), workgroup 0 writes the offsets, both permutation tables
-// and the expert GEMMs' tile list, and every wave gathers (and, fp8,
-// quantises) one row of x_perm.  Sorted position p holds the p-th assignment
-// in (expert, index) order, which is row p of the expert order, so a wave
-// needs no table to find its row's source.  Kernel boundaries cost several
-// microseconds each on this GPU; this replaces three launches.
+// (N <= 512 assignments, nbins <= 1024), in one launch: each workgroup sorts
+// the N keys in LDS (the same stable order in every workgroup), workgroup 0
+// writes the offsets, both permutation tables and the expert GEMMs' tile
+// list, and every wave gathers (and, fp8, quantises) one row of x_perm.
+// Kernel boundaries cost several microseconds each on this GPU; this replaces
+// three launches.
 template <bool FP8>
 __global__ __launch_bounds__(SORT_THREADS) void permute_small_kernel(
     const int32_t *__restrict__ keys, int64_t N, int nbins, int k, const uint16_t *__restrict__ x, int H,
     int32_t *__restrict__ offsets, int32_t *__restrict__ perm_src, int32_t *__restrict__ perm_pos,
     void *__restrict__ x_perm, float *__restrict__ x_scale, SmallTiles tl) {
-  __shared__ uint64_t sk[CH];
-  __shared__ int32_t start[CH];
-  __shared__ int32_t off[ONE_CHUNK_BINS + 1];
-  __shared__ int32_t part[SORT_THREADS];
+  __shared__ SmallSortLds L;
   const int tid = threadIdx.x;
-  for (int b = tid; b <= nbins; b += SORT_THREADS) off[b] = 0;
-  sort_chunk_lds(keys, nullptr, 0, N, nbins, 0, sk, start);
-  const int nreal = (int)N;
-  for (int j = tid; j < nreal; j += SORT_THREADS) {
-    const uint32_t key = (uint32_t)(sk[j] >> 32);
-    const bool last = (j == nreal - 1) || ((uint32_t)(sk[j + 1] >> 32) != key);
-    if (last) off[key] = j - start[j] + 1;   // count of the bin (the dropped bin nbins included)
-  }
-  __syncthreads();
-  const int per = (nbins + SORT_THREADS - 1) / SORT_THREADS;
-  const int b0 = min(tid * per, nbins), b1 = min(b0 + per, nbins);
+  int32_t pos[2];
+  const int nvalid = small_sort_lds(keys, (int)N, nbins, L, pos);
   if (blockIdx.x == 0) {
-    // exclusive scan of the bin counts -> offsets (thread t owns bins [b0, b1))
-    int32_t sum = 0;
-    for (int b = b0; b < b1; ++b) sum += off[b];
-    part[tid] = sum;
-    __syncthreads();
-    for (int o = 1; o < SORT_THREADS; o <<= 1) {
-      const int32_t add = tid >= o ? part[tid - o] : 0;
-      __syncthreads();
-      part[tid] += add;
-      __syncthreads();
-    }
-    const int32_t total = part[SORT_THREADS - 1];
-    int32_t run = part[tid] - sum;
-    for (int b = b0; b < b1; ++b) {
-      const int32_t c = off[b];
-      offsets[b] = run;
-      off[b] = run;
-      run += c;
-    }
-    if (tid == 0) offsets[nbins] = total;
-    __syncthreads();
-    for (int j = tid; j < nreal; j += SORT_THREADS) {
-      const uint64_t v = sk[j];
-      const int32_t key = (int32_t)(v >> 32);
-      const int32_t i = (int32_t)(uint32_t)v;
-      if (key >= nbins) {
-        perm_pos[i] = -1;
-        continue;
+    for (int b = tid; b <= nbins; b += SORT_THREADS) offsets[b] = L.off[b];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int i = tid + SORT_THREADS * q;
+      if (i < N) {
+        perm_pos[i] = pos[q];
+        if (pos[q] >= 0) perm_src[pos[q]] = i;
       }
-      perm_src[j] = i;   // j = off[key] + (j - start[j])
-      perm_pos[i] = j;
     }
     if (tl.tiles) {
       // tile list: the preceding group's ceil(nrows0 / bm) entries (one
       // expert holding rows 0..nrows0-1), then ceil(n_e / bm) per expert e
-      __syncthreads();
       const int base0 = tl.lead_group ? (tl.lead_rows + tl.bm - 1) / tl.bm : 0;
+      const int per = (nbins + SORT_THREADS - 1) / SORT_THREADS;
+      const int b0 = min(tid * per, nbins), b1 = min(b0 + per, nbins);
       int32_t cnt = 0;
-      for (int b = b0; b < b1; ++b) {
-        const int32_t n = (b + 1 < nbins ? off[b + 1] : total) - off[b];
-        cnt += (n + tl.bm - 1) / tl.bm;
-      }
-      part[tid] = cnt;
-      __syncthreads();
-      for (int o = 1; o < SORT_THREADS; o <<= 1) {
-        const int32_t add = tid >= o ? part[tid - o] : 0;
-        __syncthreads();
-        part[tid] += add;
-        __syncthreads();
-      }
+      for (int b = b0; b < b1; ++b) cnt += (L.off[b + 1] - L.off[b] + tl.bm - 1) / tl.bm;
+      int32_t ntile;
+      int32_t slot = base0 + block_exclusive_scan(cnt, L.wsum, &ntile);
       const int g = tl.lead_group ? 1 : 0;
-      int32_t slot = base0 + part[tid] - cnt;
       for (int b = b0; b < b1; ++b) {
-        const int32_t n = (b + 1 < nbins ? off[b + 1] : total) - off[b];
+        const int32_t n = L.off[b + 1] - L.off[b];
         for (int m0 = 0; m0 < n; m0 += tl.bm, ++slot)
           if (slot < tl.max_tiles) tl.tiles[slot] = TileEntry{(g << 24) | b, m0};
       }
       for (int j = tid; j < base0; j += SORT_THREADS)
         if (j < tl.max_tiles) tl.tiles[j] = TileEntry{0, j * tl.bm};
       if (tid == 0) {
-        tl.hdr[0] = min(base0 + part[SORT_THREADS - 1], tl.max_tiles);
+        tl.hdr[0] = min(base0 + ntile, tl.max_tiles);
         tl.hdr[1] = min(base0, tl.max_tiles);
       }
     }
   }
-  __syncthreads();
-  // n_valid: assignments with an expert in range (they sort first)
-  __shared__ int32_t nvalid_s;
-  if (tid == 0) {
-    int lo = 0, hi = nreal;   // first sorted position whose key is the dropped bin
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if ((int)(sk[mid] >> 32) >= nbins) hi = mid; else lo = mid + 1;
-    }
-    nvalid_s = lo;
-  }
-  __syncthreads();
   const int64_t p = (int64_t)blockIdx.x * (SORT_THREADS / kWave) + wave_id();
-  if (p >= nvalid_s) return;
+  if (p >= nvalid) return;
   const int lane = lane_id();
-  const int64_t t = (int64_t)(uint32_t)sk[p] / k;
+  const int64_t t = (int64_t)L.src[p] / k;
   const uint16_t *src = x + t * H;
   constexpr int BATCH = 4;
   if constexpr (!FP8) {
@@ -590,7 +647,7 @@ __global__ __launch_bounds__(SORT_THREADS) void permute_small_kernel(
   }
 }
 
-bool permute_small_ok(int64_t N, int64_t nbins) { return N >= 1 && N <= CH && nbins <= ONE_CHUNK_BINS; }
+bool permute_small_ok(int64_t N, int64_t nbins) { return N >= 1 && N <= CH && nbins >= 1 && nbins <= SMALL_SORT_BINS; }
 
 hipError_t launch_permute_small(const int32_t *keys, int64_t N, int64_t nbins, int k, const uint16_t *x, int64_t H,
                                 bool fp8, int32_t *offsets, int32_t *perm_src, int32_t *perm_pos, void *x_perm,

@@ -26,26 +26,33 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
   const bool tvalid = trow < T;
   const uint16_t *xp = x + (int64_t)(tvalid ? trow : 0) * H + kbeg;
   const uint16_t *wp[4];
-  bool ev[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int er = e0 + 16 * j + (lane & 15);
-    ev[j] = er < E;
-    wp[j] = wr + (int64_t)(ev[j] ? er : 0) * H + kbeg;
+    wp[j] = wr + (int64_t)(er < E ? er : 0) * H + kbeg;
   }
   f32x4 acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const i32x4 zero = {0, 0, 0, 0};
-#pragma unroll 4
-  for (int k = 0; k < kchunk; k += 32) {
-    const i32x4 a = tvalid ? load16(xp + k) : zero;
-    i32x4 b[4];
+  // batches of 8 K-steps: all 40 loads of a batch are issued before its
+  // MFMAs.  Rows past T and experts past E read a valid row (their outputs
+  // are not stored), and steps past the chunk re-read its last step (their
+  // MFMAs are skipped), so every load is unconditional and in bounds.
+  for (int k0 = 0; k0 < kchunk; k0 += 256) {
+    i32x4 a[8], b[8][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = ev[j] ? load16(wp[j] + k) : zero;
+    for (int u = 0; u < 8; ++u) {
+      const int kk = min(k0 + 32 * u, kchunk - 32);
+      a[u] = load16(xp + kk);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[j] = mfma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b[j]), acc[j]);
+      for (int j = 0; j < 4; ++j) b[u][j] = load16(wp[j] + kk);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (k0 + 32 * u < kchunk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[j] = mfma_bf16(__builtin_bit_cast(bf16x8, a[u]), __builtin_bit_cast(bf16x8, b[u][j]), acc[j]);
   }
   // lane holds D[token 4*(lane/16)+r][expert lane%16] of each tile
 #pragma unroll
@@ -151,10 +158,43 @@ __global__ __launch_bounds__(256, 1) void router_logits_tiled_kernel(
     }
 }
 
+// Order-preserving map of a float (NaN excluded) to uint32: a larger float has
+// a larger key, and 0 lies below every key (-infinity maps to 0x007FFFFF).
+// Callers pass -0 as +0 so that the two zeros tie.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __builtin_bit_cast(float, (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// Largest key over the wave, in every lane: max over each 16-lane row with
+// DPP moves (quad exchanges of 1 and 2, row rotations by 4 and 8), then over
+// the four rows' results read from lanes 0, 16, 32 and 48.  All 64 lanes must
+// be active.
+__device__ __forceinline__ uint32_t wave_max_key(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false));   // row_ror:4
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false));   // row_ror:8
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
 // One wave per token: logits = sum of the S partials (in order s = 0..S-1)
 // + bias; k rounds of a wave-wide arg-max under the order (value desc, index
 // asc), a NaN logit ranking as -infinity; slots sorted by expert id; gates =
-// exp(l - l_max) / sum, fp32.
+// exp(l - l_max) / sum, fp32, the sum taken over the winners in the order
+// they were chosen.
+//
+// Lane l holds experts [l*NJ, l*NJ + NJ), so among lanes holding the largest
+// key the lowest lane holds the lowest expert index (and inside a lane the
+// first of equal keys is kept): a round is a DPP max of the lanes' best keys,
+// a ballot of the lanes that hold it and the lowest of them, with no
+// cross-lane shuffles.  Every winner's id and value are wave-uniform, so the
+// slot ranks and the softmax denominator are kept up to date round by round.
 template <int NJ>
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const float *__restrict__ partial, int S, const float *__restrict__ bias, int T, int E, int k,
@@ -162,78 +202,74 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
   const int lane = lane_id();
   const int t = blockIdx.x * 4 + wave_id();
   if (t >= T) return;
+  const int e0 = lane * NJ;
   float v[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) v[j] = 0.f;
-  // partial sums added in split order s = 0..S-1 (S <= 8); every split's
-  // values are loaded before the first add, so the loads overlap
-  float pv[8][NJ];
+  // partial sums added in split order; the loads of a batch of splits are
+  // issued before the first add, so their latencies overlap
+  constexpr int SB = NJ <= 8 ? 16 : 4;
+  for (int s0 = 0; s0 < S; s0 += SB) {
+    float pv[SB][NJ];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const float *p = partial + ((int64_t)(s < S ? s : 0) * T + t) * E;
+    for (int s = 0; s < SB; ++s) {
+      const float *p = partial + ((int64_t)(s0 + s < S ? s0 + s : 0) * T + t) * E + e0;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int e = lane + 64 * j;
-      pv[s][j] = (s < S && e < E) ? p[e] : 0.f;
+      for (int j = 0; j < NJ; ++j) pv[s][j] = (s0 + s < S && e0 + j < E) ? p[j] : 0.f;
     }
+#pragma unroll
+    for (int s = 0; s < SB; ++s)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        if (s0 + s < S) v[j] += pv[s][j];
   }
-#pragma unroll
-  for (int s = 0; s < 8; ++s)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      if (s < S) v[j] += pv[s][j];
+  uint32_t key[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int e = lane + 64 * j;
+    const int e = e0 + j;
+    key[j] = 0;
     if (e < E) {
       if (bias) v[j] += bias[e];
       if (logits_out) logits_out[(int64_t)t * E + e] = v[j];
-      if (v[j] != v[j]) v[j] = -__builtin_huge_valf();   // a NaN logit ranks as -infinity
+      const float r = v[j] != v[j] ? -__builtin_huge_valf() : v[j] + 0.0f;   // NaN -> -infinity, -0 -> +0
+      key[j] = order_key(r);
     }
   }
-  uint32_t taken = 0;
-  float my_v = 0.f;
-  int my_e = 0;
+  float my_v = 0.f, vmax = 0.f, den = 0.f;
+  int my_e = 0, my_rank = 0;
   for (int it = 0; it < k; ++it) {
-    float bv = -__builtin_huge_valf();
-    int be = 0x7FFFFFFF;
+    uint32_t bk = 0;
+    int bj = 0;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int e = lane + 64 * j;
-      if (e < E && !((taken >> j) & 1u) && (v[j] > bv || (v[j] == bv && e < be))) {
-        bv = v[j];
-        be = e;
+    for (int j = 0; j < NJ; ++j)
+      if (key[j] > bk) {
+        bk = key[j];
+        bj = j;
       }
-    }
+    const uint32_t m = wave_max_key(bk);
+    const int wl = __builtin_ctzll(__builtin_amdgcn_ballot_w64(bk == m));
+    const int ew = __builtin_amdgcn_readlane(e0 + bj, wl);
+    const float vw = key_value(m);
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oe = __shfl_xor(be, o, kWave);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if (be < E && (be & 63) == lane) taken |= 1u << (be >> 6);
+    for (int j = 0; j < NJ; ++j)
+      if (lane == wl && j == bj) key[j] = 0;   // taken
+    // earlier winners (lanes < it) against the new one
+    const int below = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < it && my_e < ew));
+    if (lane < it && ew < my_e) ++my_rank;
     if (lane == it) {
-      my_v = bv;
-      my_e = be;
+      my_v = vw;
+      my_e = ew;
+      my_rank = below;
     }
+    // a chosen logit equal to the largest weighs exp(0) = 1 (so k chosen
+    // -infinity logits, a token whose logits are all NaN, get 1/k each)
+    if (it == 0) vmax = vw;
+    den += vw == vmax ? 1.0f : expf(vw - vmax);
   }
-  // slot of the j-th winner = number of winners with a smaller expert id
-  int rank = 0;
-  for (int j = 0; j < k; ++j) {
-    const int ej = __shfl(my_e, j, kWave);
-    rank += (ej < my_e) ? 1 : 0;
-  }
-  // a chosen logit equal to the largest weighs exp(0) = 1 (so k chosen
-  // -infinity logits, a token whose logits are all NaN, get 1/k each)
-  const float vmax = __shfl(my_v, 0, kWave);
-  const float ex = lane < k ? (my_v == vmax ? 1.0f : expf(my_v - vmax)) : 0.f;
-  const float den = __shfl(wave_sum(ex), 0, kWave);
   if (lane < k) {
-    ids[(int64_t)t * k + rank] = my_e;
-    gates[(int64_t)t * k + rank] = __fdiv_rn(ex, den);
+    const float ex = my_v == vmax ? 1.0f : expf(my_v - vmax);
+    ids[(int64_t)t * k + my_rank] = my_e;
+    gates[(int64_t)t * k + my_rank] = __fdiv_rn(ex, den);
   }
 }
 
@@ -245,9 +281,9 @@ int router_ksplit(int64_t T, int E, int H) {
   if (router_tiled(T, H)) return 1;
   const int64_t tiles = cdiv(E, 64) * cdiv(T, 64);
   int S = 1;
-  // split K (at most 8 ways) until there are enough workgroups, keeping chunks
-  // of >= 256 that are multiples of 32
-  while (S < 8 && tiles * S < 256 && H % (2 * S) == 0 && (H / (2 * S)) % 32 == 0 && H / (2 * S) >= 256) S *= 2;
+  // split K (at most 16 ways) until there are enough workgroups, keeping
+  // chunks of >= 256 that are multiples of 32
+  while (S < 16 && tiles * S < 256 && H % (2 * S) == 0 && (H / (2 * S)) % 32 == 0 && H / (2 * S) >= 256) S *= 2;
   return S;
 }
 

@@ -63,6 +63,38 @@ def test_route_many_tokens_tiled_path():
     assert np.abs(gates.cpu().numpy()[same] - g_ref[same]).max() < 2e-6
 
 
+@pytest.mark.parametrize("T,H,E,k", [
+    (50, 640, 100, 6),      # 2-way K split, 320-wide chunks: a batch of 8 K-steps, then one of 2
+    (33, 384, 77, 3),       # no split, a 384-wide chunk: 8 K-steps, then 4
+    (16, 4096, 1000, 32),   # 16 experts per lane, k = 32, a 16-way split (four batches of split loads)
+    (70, 4096, 1024, 8),    # the largest expert count, an 8-way split
+])
+def test_route_split_chunk_tails_and_wide_experts(T, H, E, k):
+    """The split-K logits kernel on chunks that are not a multiple of its
+    8-step batches, and the top-k kernel with 16 experts per lane: ids, gates
+    and logits of every token against the oracle."""
+    g = torch.Generator(device="cpu").manual_seed(7)
+    wr = (torch.randn(E, H, generator=g) / H ** 0.5).to(torch.bfloat16)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    I = 64   # the expert weights are never read by the router
+    layer = B.Layer(H, I, E, k, B.MOE_BF16, torch.zeros((E, 2 * I, H), dtype=torch.bfloat16, device=dev()),
+                    torch.zeros((E, H, I), dtype=torch.bfloat16, device=dev()), w_router=wr.to(dev()))
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev())
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev())
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev())
+    B.moe_route(layer, x.to(dev()), T, ids, gates, logits, ws=B.workspace(layer, T, T * k, dev()))
+    torch.cuda.synchronize()
+    OL = oracle.Layer(H, I, E, k, "bf16", W.bf16_bits(wr), np.zeros((E, 2 * I, H), np.uint16),
+                      np.zeros((E, H, I), np.uint16))
+    ids_ref, g_ref, gap, l_ref = oracle.route(OL, W.bf16_bits(x), want_logits=True)
+    same = check_ids(ids.cpu().numpy(), ids_ref, gap)
+    np.testing.assert_allclose(logits.cpu().numpy(), l_ref, rtol=0, atol=2e-5)
+    assert np.abs(gates.cpu().numpy()[same] - g_ref[same]).max() < 2e-6
+    # slots in ascending expert id, no repeats
+    ids_np = ids.cpu().numpy()
+    assert (np.diff(ids_np, axis=1) > 0).all()
+
+
 def _route_with(wr, x, k, bias=None):
     E, H = wr.shape
     I = 64
