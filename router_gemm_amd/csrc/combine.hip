@@ -10,41 +10,131 @@
 
 namespace moe {
 
-__device__ __forceinline__ void load8(const void *base, bool f32, int64_t idx, float v[8]) {
-  if (f32) {
-    const f32x4 *p = reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(base) + idx);
-    const f32x4 a = p[0], b = p[1];
-    v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
-    v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+// 8 consecutive values of an fp32 or bf16 row: the raw load and its
+// conversion are separate steps, so that several loads can be in flight
+// before the first conversion waits for its data.
+struct Raw8 {
+  i32x4 a, b;
+};
+template <bool F32>
+__device__ __forceinline__ Raw8 raw8(const void *base, int64_t idx) {
+  Raw8 r;
+  if constexpr (F32) {
+    const i32x4 *p = reinterpret_cast<const i32x4 *>(reinterpret_cast<const float *>(base) + idx);
+    r.a = p[0];
+    r.b = p[1];
   } else {
-    const i32x4 r = load16(reinterpret_cast<const uint16_t *>(base) + idx);
+    r.a = load16(reinterpret_cast<const uint16_t *>(base) + idx);
+  }
+  return r;
+}
+template <bool F32>
+__device__ __forceinline__ void cvt8(const Raw8 &r, float v[8]) {
+  if constexpr (F32) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      v[2 * q] = bf16_to_f32((uint32_t)r[q] & 0xFFFFu);
-      v[2 * q + 1] = bf16_to_f32((uint32_t)r[q] >> 16);
+      // each element goes through a scalar first: hipcc drops the index of a
+      // vector element used directly as __builtin_bit_cast's operand
+      const int32_t lo = r.a[q], hi = r.b[q];
+      v[q] = __builtin_bit_cast(float, lo);
+      v[4 + q] = __builtin_bit_cast(float, hi);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = bf16_to_f32((uint32_t)r.a[q] & 0xFFFFu);
+      v[2 * q + 1] = bf16_to_f32((uint32_t)r.a[q] >> 16);
     }
   }
 }
+template <bool F32>
+__device__ __forceinline__ void load8(const void *base, int64_t idx, float v[8]) {
+  cvt8<F32>(raw8<F32>(base, idx), v);
+}
 
 // Grid: one workgroup (256 threads) per (token, 2048-column block); each
-// thread owns 8 consecutive columns.  The token's assignments are taken in
-// batches of up to 32: their rows and gates are staged in LDS, then every
-// thread issues its row loads 8 at a time before summing them in order, so
-// the memory latency is paid once per 8 rows rather than twice per row.
+// thread owns 8 consecutive columns.
+//
+// Assignments t*k .. t*k+k-1 (the router's layout, k <= 8): the rows and
+// gates are the same for the whole workgroup, so they come through scalar
+// loads with no staging, and the shared row and all k expert rows are loaded
+// before the first add: one memory latency per workgroup after the row
+// indices.  Otherwise (a token list, or k > 8) the token's assignments are
+// taken in batches of up to 32 staged in LDS, and every thread issues its row
+// loads 8 at a time before summing them in order.
 constexpr int kCombBatch = 32;
 
-__global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y_perm, int yp_f32,
+__device__ __forceinline__ void store8(void *y, bool f32, int64_t idx, const float acc[8]) {
+  if (f32) {
+    f32x4 *o = reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(y) + idx);
+    o[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    o[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  } else {
+    i32x4 r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = (int)(pack_bf16x2(acc[2 * q], acc[2 * q + 1]));
+    store16(reinterpret_cast<uint16_t *>(y) + idx, r);
+  }
+}
+
+// YF32 / SF32: y_perm / the shared rows are fp32 (else bf16).
+template <bool YF32, bool SF32>
+__global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y_perm,
                                                       const int32_t *__restrict__ perm_pos,
                                                       const int32_t *__restrict__ tok_off,
                                                       const int32_t *__restrict__ tok_list, int k,
                                                       const float *__restrict__ gates,
-                                                      const void *__restrict__ shared, int sh_f32, int64_t H, int64_t nrows,
+                                                      const void *__restrict__ shared, int64_t H, int64_t nrows,
                                                       void *__restrict__ y, int out_f32) {
   __shared__ int32_t srow[kCombBatch];
   __shared__ float sgate[kCombBatch];
   const int64_t t = blockIdx.x;
   const int64_t c = (int64_t)blockIdx.y * 2048 + (int64_t)threadIdx.x * 8;
   const bool active = c < H;
+  float acc[8];
+  if (!tok_off && k <= 8) {
+    // slots past k re-read slot k-1 (in bounds, left out below), so the 16
+    // loads are unconditional and go out together
+    int32_t pr[8];
+    float g[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = t * k + min(u, k - 1);
+      pr[u] = perm_pos[i];
+      g[u] = gates[i];
+    }
+    // both sets in registers before the row loads (which need the rows
+    // anyway): keeps the compiler from sinking each gate load into its slot's
+    // branch, where the loads would wait one after another
+#pragma unroll
+    for (int u = 0; u < 8; ++u) asm volatile("" ::"s"(pr[u]), "s"(g[u]));
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u >= k || pr[u] < 0 || pr[u] >= nrows) pr[u] = -1;   // -1: assignment skipped
+    if (!active) return;
+    // a skipped slot reads row 0 (none when nrows == 0) and is left out of the sum
+    Raw8 rs, rv[8];
+    if (shared) rs = raw8<SF32>(shared, t * H + c);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u < k && nrows > 0) rv[u] = raw8<YF32>(y_perm, (int64_t)(pr[u] >= 0 ? pr[u] : 0) * H + c);
+    if (shared) {
+      cvt8<SF32>(rs, acc);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (u >= k || pr[u] < 0) continue;
+      float v[8];
+      cvt8<YF32>(rv[u], v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(g[u], v[q], acc[q]);
+    }
+    store8(y, out_f32 != 0, t * H + c, acc);
+    return;
+  }
   int jbeg, jend;
   if (tok_off) {
     jbeg = tok_off[t];
@@ -53,9 +143,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y
     jbeg = (int)(t * k);
     jend = jbeg + k;
   }
-  float acc[8];
   if (shared && active) {
-    load8(shared, sh_f32 != 0, t * H + c, acc);
+    load8<SF32>(shared, t * H + c, acc);
   } else {
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = 0.f;
@@ -77,7 +166,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y
         for (int u = 0; u < 8; ++u) {
           pr[u] = q0 + u < n ? srow[q0 + u] : -1;
           // a skipped slot reads row 0 and is left out of the sum below
-          load8(y_perm, yp_f32 != 0, (int64_t)(pr[u] >= 0 ? pr[u] : 0) * H + c, v[u]);
+          load8<YF32>(y_perm, (int64_t)(pr[u] >= 0 ? pr[u] : 0) * H + c, v[u]);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -90,17 +179,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y
     }
     __syncthreads();
   }
-  if (!active) return;
-  if (out_f32) {
-    f32x4 *o = reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(y) + t * H + c);
-    o[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
-    o[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
-  } else {
-    i32x4 r;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) r[q] = (int)(pack_bf16x2(acc[2 * q], acc[2 * q + 1]));
-    store16(reinterpret_cast<uint16_t *>(y) + t * H + c, r);
-  }
+  if (active) store8(y, out_f32 != 0, t * H + c, acc);
 }
 
 hipError_t launch_combine(const void *y_perm, bool yp_f32, const int32_t *perm_pos, const int32_t *tok_off,
@@ -109,8 +188,15 @@ hipError_t launch_combine(const void *y_perm, bool yp_f32, const int32_t *perm_p
   if (T == 0) return hipSuccess;
   timing_before(8, st);
   const dim3 grid((unsigned)T, (unsigned)cdiv(H, 2048));
-  combine_kernel<<<grid, 256, 0, st>>>(y_perm, yp_f32 ? 1 : 0, perm_pos, tok_off, tok_list, k, gates,
-                                              shared, sh_f32 ? 1 : 0, H, nrows, y, out_f32 ? 1 : 0);
+  const int of = out_f32 ? 1 : 0;
+#define MOE_COMBINE(Y, S) \
+  combine_kernel<Y, S><<<grid, 256, 0, st>>>(y_perm, perm_pos, tok_off, tok_list, k, gates, shared, H, nrows, y, of)
+  if (yp_f32) {
+    if (sh_f32) MOE_COMBINE(true, true); else MOE_COMBINE(true, false);
+  } else {
+    if (sh_f32) MOE_COMBINE(false, true); else MOE_COMBINE(false, false);
+  }
+#undef MOE_COMBINE
   timing_after(8, st);
   return hipGetLastError();
 }
