@@ -64,13 +64,13 @@ def parse():
 # 1 GiB device copy (bench.py --copy-calibration).  Valid only for the kernel sources they were
 # taken on: a different hash of the dominant kernel's sources (KERNEL_SOURCES) reports null.
 TRAFFIC = {
-    "prefill_fp8": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 3279064.55, "write_kib": 136931.61, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_fp8": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 1651577.25, "write_kib": 1142.84, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_bf16": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 3274984.22, "write_kib": 1738.03, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_mxfp4": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 901304.02, "write_kib": 1184.88, "fetch_scale": 2.0, "write_scale": 1.0},
-    "prefill_mxfp4": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 854758.88, "write_kib": 66423.19, "fetch_scale": 2.0, "write_scale": 1.0},
-    "ep8_share_fp8": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 853764.47, "write_kib": 77136.86, "fetch_scale": 2.0, "write_scale": 1.0},
-    "dense_ff_bf16": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 1360289.88, "write_kib": 221708.33, "fetch_scale": 2.0, "write_scale": 1.0},
+    "prefill_fp8": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 3264844.23, "write_kib": 136346.65, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_fp8": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 1651580.12, "write_kib": 1142.52, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_bf16": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 3274986.5, "write_kib": 1737.97, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_mxfp4": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 900890.4, "write_kib": 1185.24, "fetch_scale": 2.0, "write_scale": 1.0},
+    "prefill_mxfp4": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 853982.57, "write_kib": 66450.92, "fetch_scale": 2.0, "write_scale": 1.0},
+    "ep8_share_fp8": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 850576.62, "write_kib": 77144.12, "fetch_scale": 2.0, "write_scale": 1.0},
+    "dense_ff_bf16": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 1360257.05, "write_kib": 221707.84, "fetch_scale": 2.0, "write_scale": 1.0},
     # per step: the four weight-gradient launches (routed dW_down, dW_gate_up; the shared expert's two)
     "train_bf16": {"src_hash": "c4be7805626206ce", "fetch_kib": 4398878.92, "write_kib": 26400004.28, "fetch_scale": 2.0, "write_scale": 1.0},
 }

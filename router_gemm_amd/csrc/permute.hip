@@ -34,13 +34,37 @@ constexpr int64_t SINGLE_SCAN_BINS = 4096;
 constexpr int64_t kTableWords = int64_t(4) << 20;
 static bool sort_uses_table(int64_t N, int64_t nbins) { return cdiv(N, CH) * (nbins + 1) <= kTableWords; }
 
+// Exclusive scan of one value per thread over the workgroup (thread order);
+// *total = the sum of all.  Every thread of the workgroup must call it.
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *wsum, int32_t *total) {
+  const int lane = lane_id(), w = wave_id();
+  int32_t inc = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int32_t u = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += u;
+  }
+  if (lane == kWave - 1) wsum[w] = inc;
+  __syncthreads();
+  int32_t base = 0, tot = 0;
+#pragma unroll
+  for (int q = 0; q < SORT_THREADS / kWave; ++q) {
+    const int32_t s = wsum[q];
+    if (q < w) base += s;
+    tot += s;
+  }
+  *total = tot;
+  __syncthreads();   // wsum is free again
+  return base + inc - v;
+}
+
 size_t sort_ws_words(int64_t N, int64_t nbins) {
   if (!sort_uses_table(N, nbins))   // bin cursors [nbins+1], the unordered list [N], scan block totals
     return (size_t)((nbins + 1) + N + cdiv(nbins, SCAN_BLOCK) + 1);
   const int64_t nchunk = cdiv(N, CH);
   // chunk counts [nchunk][nbins+1], sorted keys/indices/ranks [nchunk*CH] x 3,
-  // per-block totals of the multi-workgroup scan
-  return (size_t)(nchunk * (nbins + 1) + 3 * nchunk * CH + cdiv(nbins, SCAN_BLOCK) + 1);
+  // per-block totals of the multi-workgroup scan, bin totals [nbins+1]
+  return (size_t)(nchunk * (nbins + 1) + 3 * nchunk * CH + cdiv(nbins, SCAN_BLOCK) + 1 + nbins + 1);
 }
 
 // Sort chunk `chunk` of the keys in LDS: sk[j] = (bin << 32 | i) ascending
@@ -281,6 +305,76 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *__restrict_
   if (perm_pos) perm_pos[i] = pos;
 }
 
+// Up to 4096 bins: (2) one workgroup per bin scans its column of the chunk
+// table (every load of a thread issued before the first add, one block scan)
+// in place and writes the bin's total to tot[b]; (3) the scatter's
+// workgroups each scan the totals in LDS (workgroup 0 publishes them as
+// offsets) and place every element at offset[key] + cc[chunk][key] + rank.
+// Same results as the single-workgroup scan, with the columns scanned in
+// parallel instead of 1024 threads walking 128-entry columns in turn.
+constexpr int COL_PER = 16;   // chunks per thread and pass of the column scan
+__global__ __launch_bounds__(SORT_THREADS) void scan_columns_kernel(int32_t *__restrict__ cc, int nchunk, int nbins,
+                                                                    int32_t *__restrict__ tot) {
+  __shared__ int32_t wsum[SORT_THREADS / kWave];
+  const int b = blockIdx.x;
+  const int64_t ld = nbins + 1;
+  const int per = min(COL_PER, (nchunk + SORT_THREADS - 1) / SORT_THREADS);
+  int32_t carry = 0;
+  for (int base = 0; base < nchunk; base += SORT_THREADS * per) {
+    const int c0 = base + threadIdx.x * per;
+    int32_t v[COL_PER];
+#pragma unroll
+    for (int u = 0; u < COL_PER; ++u) v[u] = (u < per && c0 + u < nchunk) ? cc[(int64_t)(c0 + u) * ld + b] : 0;
+    int32_t sum = 0;
+#pragma unroll
+    for (int u = 0; u < COL_PER; ++u) sum += v[u];
+    int32_t total;
+    int32_t run = carry + block_exclusive_scan(sum, wsum, &total);
+#pragma unroll
+    for (int u = 0; u < COL_PER; ++u) {
+      if (u < per && c0 + u < nchunk) cc[(int64_t)(c0 + u) * ld + b] = run;
+      run += v[u];
+    }
+    carry += total;
+  }
+  if (threadIdx.x == 0) tot[b] = carry;
+}
+
+__global__ __launch_bounds__(SORT_THREADS) void scatter_scan_kernel(
+    const int32_t *__restrict__ cc, int nbins, int64_t N, const int32_t *__restrict__ s_key,
+    const int32_t *__restrict__ s_idx, const int32_t *__restrict__ s_rank, const int32_t *__restrict__ tot,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ perm_src, int32_t *__restrict__ perm_pos) {
+  __shared__ int32_t off[SINGLE_SCAN_BINS + 1];
+  __shared__ int32_t wsum[SORT_THREADS / kWave];
+  const int tid = threadIdx.x;
+  const int per = (nbins + SORT_THREADS - 1) / SORT_THREADS;
+  const int b0 = min(tid * per, nbins), b1 = min(b0 + per, nbins);
+  int32_t sum = 0;
+  for (int b = b0; b < b1; ++b) sum += tot[b];
+  int32_t total;
+  int32_t run = block_exclusive_scan(sum, wsum, &total);
+  for (int b = b0; b < b1; ++b) {
+    off[b] = run;
+    run += tot[b];
+  }
+  if (tid == 0) off[nbins] = total;
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int b = tid; b <= nbins; b += SORT_THREADS) offsets[b] = off[b];
+  const int64_t j = (int64_t)blockIdx.x * SORT_THREADS + tid;
+  if (j >= N) return;
+  const int32_t key = s_key[j];
+  const int32_t i = s_idx[j];
+  if (key >= nbins) {
+    if (perm_pos) perm_pos[i] = -1;
+    return;
+  }
+  const int64_t c = j / CH;
+  const int32_t pos = off[key] + cc[c * (nbins + 1) + key] + s_rank[j];
+  if (perm_src) perm_src[pos] = i;
+  if (perm_pos) perm_pos[i] = pos;
+}
+
 // The whole sort in one workgroup when every key fits one chunk (N <= 512,
 // e.g. a decode step) and the bins fit LDS: chunk sort, bin counts, their
 // exclusive scan and the scatter, with the same results as the general path.
@@ -456,30 +550,6 @@ struct SmallSortLds {
   int32_t wsum[SORT_THREADS / kWave];            // per-wave totals of a block scan
 };
 
-// Exclusive scan of one value per thread over the workgroup (thread order);
-// *total = the sum of all.  Every thread of the workgroup must call it.
-__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *wsum, int32_t *total) {
-  const int lane = lane_id(), w = wave_id();
-  int32_t inc = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int32_t u = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += u;
-  }
-  if (lane == kWave - 1) wsum[w] = inc;
-  __syncthreads();
-  int32_t base = 0, tot = 0;
-#pragma unroll
-  for (int q = 0; q < SORT_THREADS / kWave; ++q) {
-    const int32_t s = wsum[q];
-    if (q < w) base += s;
-    tot += s;
-  }
-  *total = tot;
-  __syncthreads();   // wsum is free again
-  return base + inc - v;
-}
-
 // Sorts keys[0..N) into L (off, src); pos[q] = sorted position of element
 // threadIdx.x + 256 q, or -1 (dropped or past N).  Returns the number of valid keys.
 __device__ __forceinline__ int small_sort_lds(const int32_t *__restrict__ keys, int N, int nbins, SmallSortLds &L,
@@ -604,7 +674,7 @@ __global__ __launch_bounds__(SORT_THREADS) void permute_small_kernel(
   const int lane = lane_id();
   const int64_t t = (int64_t)L.src[p] / k;
   const uint16_t *src = x + t * H;
-  constexpr int BATCH = 4;
+  constexpr int BATCH = 8;   // a whole row of up to 4096 values per batch of loads
   if constexpr (!FP8) {
     uint16_t *dst = reinterpret_cast<uint16_t *>(x_perm) + p * H;
     for (int c0 = lane * 8; c0 < H; c0 += 512 * BATCH) {
@@ -689,7 +759,16 @@ hipError_t launch_counting_sort(const int32_t *keys, const int32_t *aux, int64_t
     sort_chunks_kernel<<<(unsigned)nchunk, SORT_THREADS, 0, st>>>(keys, aux, aux_bound, N, (int)nbins, cc,
                                                                   s_key, s_idx, s_rank);
   if (nbins <= SINGLE_SCAN_BINS) {
-    scan_counts_kernel<<<1, 1024, 0, st>>>(cc, (int)nchunk, (int)nbins, offsets);
+    int32_t *tot = s_rank + nchunk * CH + cdiv(nbins, SCAN_BLOCK) + 1;
+    if (N > 0) {
+      scan_columns_kernel<<<(unsigned)nbins, SORT_THREADS, 0, st>>>(cc, (int)nchunk, (int)nbins, tot);
+      scatter_scan_kernel<<<(unsigned)cdiv(N, SORT_THREADS), SORT_THREADS, 0, st>>>(
+          cc, (int)nbins, N, s_key, s_idx, s_rank, tot, offsets, perm_src, perm_pos);
+    } else {
+      scan_counts_kernel<<<1, 1024, 0, st>>>(cc, (int)nchunk, (int)nbins, offsets);   // all offsets 0
+    }
+    timing_after(2, st);
+    return hipGetLastError();
   } else {
     int32_t *bsum = s_rank + nchunk * CH;
     const unsigned nb = (unsigned)cdiv(nbins, SCAN_BLOCK);
@@ -722,9 +801,9 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t *__rest
   const int64_t i = perm_src ? perm_src[p] : p;   // no permutation: quantise rows in place order
   const int64_t t = tok ? tok[i] : i / k;
   const uint16_t *src = x + t * H;
-  // row segments of 512 values (8 per lane), four at a time: the loads of a
-  // batch are issued before any of them is used
-  constexpr int BATCH = 4;
+  // row segments of 512 values (8 per lane), eight at a time (a whole row of
+  // up to 4096 values): the loads of a batch are issued before any is used
+  constexpr int BATCH = 8;
   if constexpr (!FP8) {
     uint16_t *dst = reinterpret_cast<uint16_t *>(x_perm) + p * H;
     for (int c0 = lane * 8; c0 < H; c0 += 512 * BATCH) {

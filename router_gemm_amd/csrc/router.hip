@@ -66,80 +66,85 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
   }
 }
 
-// Router logits for many tokens: LDS-tiled, one pass over K (S = 1).
-// Workgroup tile 64 tokens x 192 experts; per 64-wide K chunk (128 bytes of
-// bf16) the 256 rows (64 token rows, 192 router-weight rows) are copied
-// straight into LDS (a ring of three 32 KB stages, two in flight), so a token
-// row fetched once feeds 192 experts and a weight row feeds 64 tokens.  Wave w
-// owns all 64 tokens x experts [48w, 48w+48): 4 x 3 MFMA tiles of 16x16.
-// Rows past T or E repeat a valid row and are not stored.
+// Router logits for many tokens: LDS-tiled, K split S ways into partials.
+// Workgroup tile 128 tokens x 192 experts over chunks [s*cps, s*cps + cps) of
+// K; per 64-wide K chunk (128 bytes of bf16) the 320 rows (128 token rows,
+// 192 router-weight rows) are copied straight into LDS (a ring of three 40 KB
+// stages, two in flight), so a token row fetched once feeds 192 experts and a
+// weight row feeds 128 tokens: the copies, which bound this kernel, move
+// T*E*H*2*(1/192 + 1/128) bytes in all.  Eight waves, two per SIMD: wave w
+// owns tokens [64*(w/4), +64) x experts [48*(w%4), +48) as 4 x 3 MFMA tiles
+// of 16x16.  Rows past T or E repeat a valid row and are not stored.
 namespace {
-constexpr int RT_M = 64, RT_N = 192, RT_ROWS = RT_M + RT_N;
+constexpr int RT_M = 128, RT_N = 192, RT_ROWS = RT_M + RT_N;
 constexpr int RT_STAGE = RT_ROWS * 128, RT_NSTAGE = 3;
+constexpr int RT_Q = RT_ROWS / 64;   // copies per lane per chunk (8 waves x 8 rows each)
+static_assert(RT_M % 64 == 0 && RT_ROWS % 64 == 0, "copy rows come in groups of 64");
 }  // namespace
 
-__global__ __launch_bounds__(256, 1) void router_logits_tiled_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, float *__restrict__ logits, int T, int E,
-    int H) {
+__global__ __launch_bounds__(512, 1) void router_logits_tiled_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, float *__restrict__ partial, int T, int E,
+    int H, int cps) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = lane_id(), w = uniform(wave_id());
-  const int t0 = blockIdx.y * RT_M, e0 = blockIdx.x * RT_N;
+  const int t0 = blockIdx.y * RT_M, e0 = blockIdx.x * RT_N, s = blockIdx.z;
   const int64_t rowb = (int64_t)H * 2;
-  const int nchunk = (int)(rowb / 128);
-  // this lane's 8 copies per chunk: LDS row r = 8 * (w + 4q) + lane / 8
-  uint32_t off[8];
+  const int kc0 = s * cps;
+  const int nchunk = max(0, min(cps, (int)(rowb / 128) - kc0));
+  // this lane's RT_Q copies per chunk: LDS row r = 8 * (w + 8q) + lane / 8
+  uint32_t off[RT_Q];
   const uint8_t *src[2] = {reinterpret_cast<const uint8_t *>(x), reinterpret_cast<const uint8_t *>(wr)};
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int r = 8 * (w + 4 * q) + (lane >> 3);
+  for (int q = 0; q < RT_Q; ++q) {
+    const int r = 8 * (w + 8 * q) + (lane >> 3);
     const int c = (lane & 7) ^ swz_f(r);
     const int grow = r < RT_M ? min(t0 + r, T - 1) : min(e0 + r - RT_M, E - 1);
     off[q] = (uint32_t)(grow * rowb + c * 16);
   }
-  // q < 2: token rows (r < 64), q >= 2: weight rows
+  // q < RT_M / 32: token rows, the rest: weight rows
   auto issue = [&](int kc, uint8_t *sb) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) dma16(src[q < 2 ? 0 : 1] + (int64_t)kc * 128 + off[q], sb + (w + 4 * q) * 1024);
+    for (int q = 0; q < RT_Q; ++q)
+      dma16(src[q < RT_M / 64 ? 0 : 1] + (int64_t)(kc0 + kc) * 128 + off[q], sb + (w + 8 * q) * 1024);
   };
+  const int wm = w >> 2, wn = w & 3;
   f32x4 acc[4][3];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 3; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  issue(0, lds);
+  if (nchunk > 0) issue(0, lds);
   if (nchunk > 1) issue(1, lds + RT_STAGE);
   for (int kc = 0; kc < nchunk; ++kc) {
     if (kc + 2 < nchunk) issue(kc + 2, lds + ((kc + 2) % RT_NSTAGE) * RT_STAGE);
     // chunk kc landed: the copies of kc+1 and kc+2 may still be in flight
     if (kc + 2 < nchunk)
-      wait_vm<16>();
+      wait_vm<2 * RT_Q>();
     else if (kc + 1 < nchunk)
-      wait_vm<8>();
+      wait_vm<RT_Q>();
     else
       wait_vm<0>();
     wg_barrier();
     const uint8_t *sb = lds + (kc % RT_NSTAGE) * RT_STAGE;
     const int ck = 2 * (lane >> 4);
-    i32x4 a[4][2], b[3][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * i + (lane & 15);
-      a[i][0] = *reinterpret_cast<const i32x4 *>(sb + swz(r, ck));
-      a[i][1] = *reinterpret_cast<const i32x4 *>(sb + swz(r, ck + 1));
-    }
+    i32x4 b[3][2];
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      const int r = RT_M + 48 * w + 16 * j + (lane & 15);
+      const int r = RT_M + 48 * wn + 16 * j + (lane & 15);
       b[j][0] = *reinterpret_cast<const i32x4 *>(sb + swz(r, ck));
       b[j][1] = *reinterpret_cast<const i32x4 *>(sb + swz(r, ck + 1));
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const int r = 64 * wm + 16 * i + (lane & 15);
+      const i32x4 a0 = *reinterpret_cast<const i32x4 *>(sb + swz(r, ck));
+      const i32x4 a1 = *reinterpret_cast<const i32x4 *>(sb + swz(r, ck + 1));
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
-        acc[i][j] = mfma_bf16(__builtin_bit_cast(bf16x8, a[i][0]), __builtin_bit_cast(bf16x8, b[j][0]), acc[i][j]);
-        acc[i][j] = mfma_bf16(__builtin_bit_cast(bf16x8, a[i][1]), __builtin_bit_cast(bf16x8, b[j][1]), acc[i][j]);
+        acc[i][j] = mfma_bf16(__builtin_bit_cast(bf16x8, a0), __builtin_bit_cast(bf16x8, b[j][0]), acc[i][j]);
+        acc[i][j] = mfma_bf16(__builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, b[j][1]), acc[i][j]);
       }
+    }
     // every wave is done reading this stage before it is refilled (kc + 3)
     wait_vm_lgkm0<63>();
     wg_barrier();
@@ -149,11 +154,11 @@ __global__ __launch_bounds__(256, 1) void router_logits_tiled_kernel(
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      const int e = e0 + 48 * w + 16 * j + (lane & 15);
+      const int e = e0 + 48 * wn + 16 * j + (lane & 15);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = t0 + 16 * i + 4 * (lane >> 4) + r;
-        if (t < T && e < E) logits[(int64_t)t * E + e] = acc[i][j][r];
+        const int t = t0 + 64 * wm + 16 * i + 4 * (lane >> 4) + r;
+        if (t < T && e < E) partial[((int64_t)s * T + t) * E + e] = acc[i][j][r];
       }
     }
 }
@@ -277,8 +282,17 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
 // (per-lane copy offsets are 32-bit: the token rows must span < 2 GiB)
 static bool router_tiled(int64_t T, int H) { return T >= 2048 && H % 64 == 0 && T * H * 2 < (int64_t(1) << 31); }
 
+// The tiled kernel's split: enough workgroups for every CU (K chunks of 64
+// kept at 8 or more per split).
+static int tiled_split(int64_t T, int E, int H) {
+  const int64_t tiles = cdiv(E, RT_N) * cdiv(T, RT_M);
+  int S = 1;
+  while (S < 16 && tiles * S < 256 && (H / 64) / (2 * S) >= 8) S *= 2;
+  return S;
+}
+
 int router_ksplit(int64_t T, int E, int H) {
-  if (router_tiled(T, H)) return 1;
+  if (router_tiled(T, H)) return tiled_split(T, E, H);
   const int64_t tiles = cdiv(E, 64) * cdiv(T, 64);
   int S = 1;
   // split K (at most 16 ways) until there are enough workgroups, keeping
@@ -292,7 +306,7 @@ hipError_t launch_router(const uint16_t *x, const uint16_t *wr, const float *bia
                          float *logits, hipStream_t st) {
   if (T == 0) return hipSuccess;
   timing_before(0, st);
-  if (router_tiled(T, H) && S == 1) {
+  if (router_tiled(T, H) && S == tiled_split(T, E, H)) {
     const size_t lds = (size_t)RT_NSTAGE * RT_STAGE;
     static bool attr_set[64] = {};
     int dev = 0;
@@ -303,8 +317,9 @@ hipError_t launch_router(const uint16_t *x, const uint16_t *wr, const float *bia
       if (e != hipSuccess) return e;
       attr_set[dev] = true;
     }
-    dim3 gt((unsigned)cdiv(E, RT_N), (unsigned)cdiv(T, RT_M));
-    router_logits_tiled_kernel<<<gt, 256, lds, st>>>(x, wr, partial, (int)T, E, H);
+    const int cps = (int)cdiv(H / 64, S);
+    dim3 gt((unsigned)cdiv(E, RT_N), (unsigned)cdiv(T, RT_M), (unsigned)S);
+    router_logits_tiled_kernel<<<gt, 512, lds, st>>>(x, wr, partial, (int)T, E, H, cps);
   } else {
     dim3 g1((unsigned)cdiv(E, 64), (unsigned)cdiv(T, 64), (unsigned)S);
     router_logits_kernel<<<g1, 256, 0, st>>>(x, wr, partial, (int)T, E, H, H / S);

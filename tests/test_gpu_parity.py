@@ -45,8 +45,9 @@ def test_route_matches_oracle(name):
 
 def test_route_many_tokens_tiled_path():
     """T >= 2048 takes the LDS-tiled logits kernel: ragged T (not a multiple of
-    the 64-token tile) and E = 352 (not a multiple of the 192-expert tile);
-    every token's ids, gates and logits against the oracle."""
+    the 128-token tile) and E = 352 (not a multiple of the 192-expert tile),
+    one K split at this hidden size; every token's ids, gates and logits
+    against the oracle."""
     cfg = W.get_config("c0", T=2085, E=352, k=8, I=64, Is=0)
     lt = W.make_layer(cfg, dev())
     x = W.make_x(cfg, dev())
@@ -107,6 +108,31 @@ def _route_with(wr, x, k, bias=None):
     B.moe_route(layer, x, T, ids, gates, ws=B.workspace(layer, T, T * k, dev()))
     torch.cuda.synchronize()
     return ids.cpu().numpy(), gates.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,H,E", [(4096, 4096, 352), (2500, 8192, 200)])
+def test_route_tiled_split_k(T, H, E):
+    """Many tokens at a long hidden size: the LDS-tiled logits kernel with its
+    K split into partials (4 and 8 ways here; ragged T and E), summed in order
+    by the top-k kernel: ids, gates and logits of every token."""
+    k = 8
+    g = torch.Generator(device="cpu").manual_seed(8)
+    wr = (torch.randn(E, H, generator=g) / H ** 0.5).to(torch.bfloat16)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    I = 64   # the expert weights are never read by the router
+    layer = B.Layer(H, I, E, k, B.MOE_BF16, torch.zeros((E, 2 * I, H), dtype=torch.bfloat16, device=dev()),
+                    torch.zeros((E, H, I), dtype=torch.bfloat16, device=dev()), w_router=wr.to(dev()))
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev())
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev())
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev())
+    B.moe_route(layer, x.to(dev()), T, ids, gates, logits, ws=B.workspace(layer, T, T * k, dev()))
+    torch.cuda.synchronize()
+    OL = oracle.Layer(H, I, E, k, "bf16", W.bf16_bits(wr), np.zeros((E, 2 * I, H), np.uint16),
+                      np.zeros((E, H, I), np.uint16))
+    ids_ref, g_ref, gap, l_ref = oracle.route(OL, W.bf16_bits(x), want_logits=True)
+    same = check_ids(ids.cpu().numpy(), ids_ref, gap)
+    np.testing.assert_allclose(logits.cpu().numpy(), l_ref, rtol=0, atol=2e-5)
+    assert np.abs(gates.cpu().numpy()[same] - g_ref[same]).max() < 2e-6
 
 
 def test_route_exact_ties_lowest_index():
