@@ -183,3 +183,31 @@ def test_ep_share_forward_routed():
         print(f"[ep8_share_fp8 routed, {'tile16' if packed else 'rows'}] max rel err {err.max():.3e}", flush=True)
         assert err.max() < TOL["fp8"]
         assert err.max() < 7.5e-3            # regression bar
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_forward_bitwise_repeatable_full_size(name):
+    """20 forwards of the decode (T=64) and prefill (T=8192) FP8 layers in the
+    benchmark's launch configuration (tile16 weights), the workspace refilled
+    with a different byte pattern before each: outputs, ids and gates equal
+    bit for bit every time (no atomics, fixed summation orders)."""
+    cfg = W.get_config(name)
+    print(f"[{cfg.name}] building layer", flush=True)
+    lt = W.make_layer(cfg, dev())
+    x = W.make_x(cfg, dev())
+    layer = B.Layer.from_tensors(lt).packed()
+    T, d = cfg.T, dev()
+    ws = B.workspace(layer, T, cfg.N, d)
+    ref = None
+    for rep in range(20):
+        ws.fill_(rep * 37 % 256)
+        y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=d)
+        ids = torch.empty((T, cfg.k), dtype=torch.int32, device=d)
+        gates = torch.empty((T, cfg.k), dtype=torch.float32, device=d)
+        B.moe_forward(layer, x, T, y, out_dtype=B.MOE_BF16, topk_ids=ids, topk_gates=gates, ws=ws)
+        torch.cuda.synchronize()
+        if ref is None:
+            ref = (y, ids, gates)
+        else:
+            assert torch.equal(y, ref[0]) and torch.equal(ids, ref[1]) and torch.equal(gates, ref[2]), rep
+    print(f"[{cfg.name}] 20 forwards bitwise equal", flush=True)
