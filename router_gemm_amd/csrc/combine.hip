@@ -55,13 +55,13 @@ __device__ __forceinline__ void load8(const void *base, int64_t idx, float v[8])
 // Grid: one workgroup (256 threads) per (token, 2048-column block); each
 // thread owns 8 consecutive columns.
 //
-// Assignments t*k .. t*k+k-1 (the router's layout, k <= 8): the rows and
+// Assignments t*k .. t*k+k-1 (the router's layout, 1 <= k <= 8): the rows and
 // gates are the same for the whole workgroup, so they come through scalar
 // loads with no staging, and the shared row and all k expert rows are loaded
 // before the first add: one memory latency per workgroup after the row
-// indices.  Otherwise (a token list, or k > 8) the token's assignments are
-// taken in batches of up to 32 staged in LDS, and every thread issues its row
-// loads 8 at a time before summing them in order.
+// indices.  Otherwise (a token list, or k outside 1..8) the token's
+// assignments are taken in batches of up to 32 staged in LDS, and every
+// thread issues its row loads 8 at a time before summing them in order.
 constexpr int kCombBatch = 32;
 
 __device__ __forceinline__ void store8(void *y, bool f32, int64_t idx, const float acc[8]) {
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y
   const int64_t c = (int64_t)blockIdx.y * 2048 + (int64_t)threadIdx.x * 8;
   const bool active = c < H;
   float acc[8];
-  if (!tok_off && k <= 8) {
+  if (!tok_off && k >= 1 && k <= 8) {
     // slots past k re-read slot k-1 (in bounds, left out below), so the 16
     // loads are unconditional and go out together
     int32_t pr[8];
