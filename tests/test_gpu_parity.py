@@ -362,6 +362,36 @@ def test_combine_matches_oracle(tokens, ydt, sdt, odt):
     assert err.max() < (1e-6 if odt == torch.float32 else 2 ** -8)
 
 
+@pytest.mark.parametrize("k,ydt,odt", [(1, torch.float32, torch.float32), (3, torch.bfloat16, torch.bfloat16),
+                                       (8, torch.bfloat16, torch.float32), (8, torch.float32, torch.bfloat16)])
+def test_combine_router_layout_edges(k, ydt, odt):
+    """The router's layout (slot u of token t at t*k + u) at k = 1, 3 and 8:
+    a second 2048-column block only partly covered (H = 2176), skipped slots
+    (perm_pos -1 and positions at or past the N rows), a shared expert, every
+    combination of fp32 / bf16 rows and outputs."""
+    rng = np.random.default_rng(17 + k)
+    T, H = 37, 2176
+    N = T * k
+    d = dev()
+    yp = torch.from_numpy(rng.standard_normal((N, H)).astype(np.float32)).to(ydt)
+    pos = rng.permutation(N).astype(np.int32)
+    skip = rng.choice(N, min(6, N), replace=False)
+    pos[skip[:3]] = -1
+    pos[skip[3:]] = N + np.arange(len(skip) - 3, dtype=np.int32)   # past the last row
+    gates = rng.random(N).astype(np.float32)
+    sh = rng.standard_normal((T, H)).astype(np.float32)
+    layer = B.Layer(H, 128, 8, k, B.MOE_BF16, None, None)
+    y = torch.empty((T, H), dtype=odt, device=d)
+    B.moe_combine(layer, yp.to(d), B.dtype_code(yp), torch.from_numpy(pos).to(d), None,
+                  torch.from_numpy(gates).to(d), N, torch.from_numpy(sh).to(d), B.MOE_F32, T, y,
+                  B.dtype_code(y), ws=B.workspace(layer, T, N, d))
+    torch.cuda.synchronize()
+    pos_ref = np.where(pos >= N, -1, pos).astype(np.int32)
+    y_ref = oracle.combine(to_np(yp), pos_ref, gates, T, k=k, tok=None, shared=sh)
+    err = rel_err_rows(to_np(y), y_ref)
+    assert err.max() < (1e-6 if odt == torch.float32 else 2 ** -8)
+
+
 @pytest.mark.parametrize("tokens", [True, False])
 def test_combine_long_assignment_lists_and_partial_column_block(tokens):
     """Tokens with 70, 33, 32, 9 and 0 assignments (several 32-slot batches,
