@@ -520,6 +520,15 @@ moe_status moe_combine(const moe_layer *L, const void *y_perm, int32_t y_dtype, 
 }
 
 namespace {
+// The expert GEMMs' tile list, for the sort to write from its own offsets (the
+// shared expert's group first when it rides in the routed launches); none for
+// tiled MX layers, whose groups get lists of their own.
+moe::SmallTiles sort_tiles(const moe_layer *L, const FfnWs &ffn, int ngroups, int64_t T) {
+  if (ffn.plan.tiled && is_mx(L)) return moe::SmallTiles{};
+  return moe::SmallTiles{reinterpret_cast<moe::TileEntry *>(ffn.tiles + moe::kTileHdrWords), ffn.tiles, ffn.plan.bm,
+                         ffn.plan.max_tiles, ngroups == 2 ? 1 : 0, (int)T};
+}
+
 moe_status forward_impl(const moe_layer *L, const void *x, int64_t T, void *y, int32_t out_dtype, int32_t *topk_ids,
                         float *topk_gates, float *z_saved, void *ws, size_t ws_bytes, void *stream) {
   moe_status s;
@@ -557,7 +566,8 @@ moe_status forward_impl(const moe_layer *L, const void *x, int64_t T, void *y, i
     if (e != hipSuccess) return hip_status(e, "moe_forward: grouping");
     tiles_ready = true;
   } else {
-    e = moe::launch_counting_sort(ids, nullptr, 0, N, E, f.offsets, f.perm_src, f.perm_pos, f.sort, st);
+    e = moe::launch_counting_sort_tiles(ids, nullptr, 0, N, E, f.offsets, f.perm_src, f.perm_pos, f.sort,
+                                        sort_tiles(L, f.ffn, f.ngroups, T), &tiles_ready, st);
     if (e != hipSuccess) return hip_status(e, "moe_forward: sort");
     // LDS-tiled expert kernels read the routed rows through the sort permutation
     // (x quantised once per token for fp8 experts) instead of a gathered copy;
@@ -622,14 +632,16 @@ moe_status moe_forward_routed(const moe_layer *L, const void *x, int64_t T, cons
   const int H = L->hidden, E = L->num_experts;
   Carve c(ws);
   RoutedWs f = carve_routed(c, L, x, T, N, out_f32);
-  hipError_t e = moe::launch_counting_sort(assign_expert, assign_token, T, N, E, f.offsets, f.perm_src, f.perm_pos,
-                                           f.sort, st);
+  bool tiles_ready = false;
+  hipError_t e = moe::launch_counting_sort_tiles(assign_expert, assign_token, T, N, E, f.offsets, f.perm_src,
+                                                 f.perm_pos, f.sort, sort_tiles(L, f.ffn, f.ngroups, T), &tiles_ready,
+                                                 st);
   if (e != hipSuccess) return hip_status(e, "moe_forward_routed: sort");
   e = moe::launch_gather_rows(static_cast<const uint16_t *>(x), H, f.perm_src, assign_token, 1, N, f.offsets + E,
                               is_fp8(L), f.x_perm, f.x_scale, st);
   if (e != hipSuccess) return hip_status(e, "moe_forward_routed: gather");
   // routed and shared expert in the same launches
-  e = moe::launch_expert_ffn(f.groups, f.ngroups, H, f.ffn.plan, f.ffn.tiles, MOE_SITE_GATE_UP, st);
+  e = moe::launch_expert_ffn(f.groups, f.ngroups, H, f.ffn.plan, f.ffn.tiles, MOE_SITE_GATE_UP, st, tiles_ready);
   if (e != hipSuccess) return hip_status(e, "moe_forward_routed: experts");
   if (f.shared_apart) {
     e = moe::launch_expert_ffn(&f.sh_group, 1, H, f.ffn_sh.plan, f.ffn_sh.tiles, MOE_SITE_GATE_UP, st);

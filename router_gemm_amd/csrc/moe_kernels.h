@@ -136,6 +136,12 @@ struct SmallTiles {
 // x, in one launch, for N <= 512 and nbins <= 1024 (permute_small_ok):
 // the results of launch_counting_sort + launch_gather_rows + the tile list.
 bool permute_small_ok(int64_t N, int64_t nbins);
+// launch_counting_sort, and where its launches allow (the chunk table with
+// up to 4096 bins) the expert GEMMs' tile list from the same offsets, as
+// build_tiles_kernel would write it: *tiles_done says whether it was written.
+hipError_t launch_counting_sort_tiles(const int32_t *keys, const int32_t *aux, int64_t aux_bound, int64_t N,
+                                      int64_t nbins, int32_t *offsets, int32_t *perm_src, int32_t *perm_pos,
+                                      int32_t *ws, const SmallTiles &tl, bool *tiles_done, hipStream_t st);
 hipError_t launch_permute_small(const int32_t *keys, int64_t N, int64_t nbins, int k, const uint16_t *x, int64_t H,
                                 bool fp8, int32_t *offsets, int32_t *perm_src, int32_t *perm_pos, void *x_perm,
                                 float *x_scale, const SmallTiles &tl, hipStream_t st);

@@ -58,6 +58,34 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *wsum
   return base + inc - v;
 }
 
+// The expert GEMMs' tile list from the bin offsets off[0..nbins] (in LDS):
+// the preceding group's ceil(lead_rows / bm) entries (one expert holding rows
+// 0..lead_rows-1), then ceil(n_e / bm) per expert e, and the header (entry
+// count, lead entry count): the list build_tiles_kernel writes.  Every thread
+// of the workgroup must call it.
+__device__ void write_tile_list(const int32_t *off, int nbins, const SmallTiles &tl, int32_t *wsum) {
+  const int tid = threadIdx.x;
+  const int base0 = tl.lead_group ? (tl.lead_rows + tl.bm - 1) / tl.bm : 0;
+  const int per = (nbins + SORT_THREADS - 1) / SORT_THREADS;
+  const int b0 = min(tid * per, nbins), b1 = min(b0 + per, nbins);
+  int32_t cnt = 0;
+  for (int b = b0; b < b1; ++b) cnt += (off[b + 1] - off[b] + tl.bm - 1) / tl.bm;
+  int32_t ntile;
+  int32_t slot = base0 + block_exclusive_scan(cnt, wsum, &ntile);
+  const int g = tl.lead_group ? 1 : 0;
+  for (int b = b0; b < b1; ++b) {
+    const int32_t n = off[b + 1] - off[b];
+    for (int m0 = 0; m0 < n; m0 += tl.bm, ++slot)
+      if (slot < tl.max_tiles) tl.tiles[slot] = TileEntry{(g << 24) | b, m0};
+  }
+  for (int j = tid; j < base0; j += SORT_THREADS)
+    if (j < tl.max_tiles) tl.tiles[j] = TileEntry{0, j * tl.bm};
+  if (tid == 0) {
+    tl.hdr[0] = min(base0 + ntile, tl.max_tiles);
+    tl.hdr[1] = min(base0, tl.max_tiles);
+  }
+}
+
 size_t sort_ws_words(int64_t N, int64_t nbins) {
   if (!sort_uses_table(N, nbins))   // bin cursors [nbins+1], the unordered list [N], scan block totals
     return (size_t)((nbins + 1) + N + cdiv(nbins, SCAN_BLOCK) + 1);
@@ -343,7 +371,7 @@ __global__ __launch_bounds__(SORT_THREADS) void scan_columns_kernel(int32_t *__r
 __global__ __launch_bounds__(SORT_THREADS) void scatter_scan_kernel(
     const int32_t *__restrict__ cc, int nbins, int64_t N, const int32_t *__restrict__ s_key,
     const int32_t *__restrict__ s_idx, const int32_t *__restrict__ s_rank, const int32_t *__restrict__ tot,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ perm_src, int32_t *__restrict__ perm_pos) {
+    int32_t *__restrict__ offsets, int32_t *__restrict__ perm_src, int32_t *__restrict__ perm_pos, SmallTiles tl) {
   __shared__ int32_t off[SINGLE_SCAN_BINS + 1];
   __shared__ int32_t wsum[SORT_THREADS / kWave];
   const int tid = threadIdx.x;
@@ -359,8 +387,10 @@ __global__ __launch_bounds__(SORT_THREADS) void scatter_scan_kernel(
   }
   if (tid == 0) off[nbins] = total;
   __syncthreads();
-  if (blockIdx.x == 0)
+  if (blockIdx.x == 0) {
     for (int b = tid; b <= nbins; b += SORT_THREADS) offsets[b] = off[b];
+    if (tl.tiles) write_tile_list(off, nbins, tl, wsum);   // the expert GEMMs' tile list
+  }
   const int64_t j = (int64_t)blockIdx.x * SORT_THREADS + tid;
   if (j >= N) return;
   const int32_t key = s_key[j];
@@ -645,29 +675,7 @@ __global__ __launch_bounds__(SORT_THREADS) void permute_small_kernel(
         if (pos[q] >= 0) perm_src[pos[q]] = i;
       }
     }
-    if (tl.tiles) {
-      // tile list: the preceding group's ceil(nrows0 / bm) entries (one
-      // expert holding rows 0..nrows0-1), then ceil(n_e / bm) per expert e
-      const int base0 = tl.lead_group ? (tl.lead_rows + tl.bm - 1) / tl.bm : 0;
-      const int per = (nbins + SORT_THREADS - 1) / SORT_THREADS;
-      const int b0 = min(tid * per, nbins), b1 = min(b0 + per, nbins);
-      int32_t cnt = 0;
-      for (int b = b0; b < b1; ++b) cnt += (L.off[b + 1] - L.off[b] + tl.bm - 1) / tl.bm;
-      int32_t ntile;
-      int32_t slot = base0 + block_exclusive_scan(cnt, L.wsum, &ntile);
-      const int g = tl.lead_group ? 1 : 0;
-      for (int b = b0; b < b1; ++b) {
-        const int32_t n = L.off[b + 1] - L.off[b];
-        for (int m0 = 0; m0 < n; m0 += tl.bm, ++slot)
-          if (slot < tl.max_tiles) tl.tiles[slot] = TileEntry{(g << 24) | b, m0};
-      }
-      for (int j = tid; j < base0; j += SORT_THREADS)
-        if (j < tl.max_tiles) tl.tiles[j] = TileEntry{0, j * tl.bm};
-      if (tid == 0) {
-        tl.hdr[0] = min(base0 + ntile, tl.max_tiles);
-        tl.hdr[1] = min(base0, tl.max_tiles);
-      }
-    }
+    if (tl.tiles) write_tile_list(L.off, nbins, tl, L.wsum);
   }
   const int64_t p = (int64_t)blockIdx.x * (SORT_THREADS / kWave) + wave_id();
   if (p >= nvalid) return;
@@ -735,9 +743,10 @@ hipError_t launch_permute_small(const int32_t *keys, int64_t N, int64_t nbins, i
   return hipGetLastError();
 }
 
-hipError_t launch_counting_sort(const int32_t *keys, const int32_t *aux, int64_t aux_bound, int64_t N,
+static hipError_t counting_sort(const int32_t *keys, const int32_t *aux, int64_t aux_bound, int64_t N,
                                 int64_t nbins, int32_t *offsets, int32_t *perm_src, int32_t *perm_pos,
-                                int32_t *ws, hipStream_t st) {
+                                int32_t *ws, const SmallTiles &tl, bool *tiles_done, hipStream_t st) {
+  if (tiles_done) *tiles_done = false;
   const int64_t nchunk = cdiv(N, CH);
   int32_t *cc = ws;
   int32_t *s_key = cc + nchunk * (nbins + 1);
@@ -763,7 +772,8 @@ hipError_t launch_counting_sort(const int32_t *keys, const int32_t *aux, int64_t
     if (N > 0) {
       scan_columns_kernel<<<(unsigned)nbins, SORT_THREADS, 0, st>>>(cc, (int)nchunk, (int)nbins, tot);
       scatter_scan_kernel<<<(unsigned)cdiv(N, SORT_THREADS), SORT_THREADS, 0, st>>>(
-          cc, (int)nbins, N, s_key, s_idx, s_rank, tot, offsets, perm_src, perm_pos);
+          cc, (int)nbins, N, s_key, s_idx, s_rank, tot, offsets, perm_src, perm_pos, tl);
+      if (tiles_done && tl.tiles) *tiles_done = true;
     } else {
       scan_counts_kernel<<<1, 1024, 0, st>>>(cc, (int)nchunk, (int)nbins, offsets);   // all offsets 0
     }
@@ -781,6 +791,18 @@ hipError_t launch_counting_sort(const int32_t *keys, const int32_t *aux, int64_t
                                                           perm_pos);
   timing_after(2, st);
   return hipGetLastError();
+}
+
+hipError_t launch_counting_sort(const int32_t *keys, const int32_t *aux, int64_t aux_bound, int64_t N,
+                                int64_t nbins, int32_t *offsets, int32_t *perm_src, int32_t *perm_pos,
+                                int32_t *ws, hipStream_t st) {
+  return counting_sort(keys, aux, aux_bound, N, nbins, offsets, perm_src, perm_pos, ws, SmallTiles{}, nullptr, st);
+}
+
+hipError_t launch_counting_sort_tiles(const int32_t *keys, const int32_t *aux, int64_t aux_bound, int64_t N,
+                                      int64_t nbins, int32_t *offsets, int32_t *perm_src, int32_t *perm_pos,
+                                      int32_t *ws, const SmallTiles &tl, bool *tiles_done, hipStream_t st) {
+  return counting_sort(keys, aux, aux_bound, N, nbins, offsets, perm_src, perm_pos, ws, tl, tiles_done, st);
 }
 
 // ---------------------------------------------------------------- gather
