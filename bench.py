@@ -64,15 +64,15 @@ def parse():
 # 1 GiB device copy (bench.py --copy-calibration).  Valid only for the kernel sources they were
 # taken on: a different hash of the dominant kernel's sources (KERNEL_SOURCES) reports null.
 TRAFFIC = {
-    "prefill_fp8": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 3264844.23, "write_kib": 136346.65, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_fp8": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 1651580.12, "write_kib": 1142.52, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_bf16": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 3274986.5, "write_kib": 1737.97, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_mxfp4": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 900890.4, "write_kib": 1185.24, "fetch_scale": 2.0, "write_scale": 1.0},
-    "prefill_mxfp4": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 853982.57, "write_kib": 66450.92, "fetch_scale": 2.0, "write_scale": 1.0},
-    "ep8_share_fp8": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 850576.62, "write_kib": 77144.12, "fetch_scale": 2.0, "write_scale": 1.0},
-    "dense_ff_bf16": {"src_hash": "6f729d7ae5c73258", "fetch_kib": 1360257.05, "write_kib": 221707.84, "fetch_scale": 2.0, "write_scale": 1.0},
+    "prefill_fp8": {"src_hash": "dd536528522c1788", "fetch_kib": 3285737.82, "write_kib": 136893.6, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_fp8": {"src_hash": "dd536528522c1788", "fetch_kib": 1651581.38, "write_kib": 1142.28, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_bf16": {"src_hash": "dd536528522c1788", "fetch_kib": 3274989.97, "write_kib": 1737.75, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_mxfp4": {"src_hash": "dd536528522c1788", "fetch_kib": 900978.58, "write_kib": 1186.91, "fetch_scale": 2.0, "write_scale": 1.0},
+    "prefill_mxfp4": {"src_hash": "dd536528522c1788", "fetch_kib": 855450.69, "write_kib": 66411.11, "fetch_scale": 2.0, "write_scale": 1.0},
+    "ep8_share_fp8": {"src_hash": "dd536528522c1788", "fetch_kib": 852428.2, "write_kib": 77116.44, "fetch_scale": 2.0, "write_scale": 1.0},
+    "dense_ff_bf16": {"src_hash": "dd536528522c1788", "fetch_kib": 1360259.51, "write_kib": 221708.33, "fetch_scale": 2.0, "write_scale": 1.0},
     # per step: the four weight-gradient launches (routed dW_down, dW_gate_up; the shared expert's two)
-    "train_bf16": {"src_hash": "c4be7805626206ce", "fetch_kib": 4398878.92, "write_kib": 26400004.28, "fetch_scale": 2.0, "write_scale": 1.0},
+    "train_bf16": {"src_hash": "43d48f110e50a49b", "fetch_kib": 4397478.32, "write_kib": 26404451.44, "fetch_scale": 2.0, "write_scale": 1.0},
 }
 
 
