@@ -543,6 +543,19 @@ def test_forward_ragged_and_single_token():
         check_forward(lt, x, OL=OL)
 
 
+@pytest.mark.parametrize("name,T", [("small_fp8", 40), ("small_fp8", 100), ("c0", 43)])
+def test_forward_top_k_above_8(name, T):
+    """k = 12 of 32 experts: the combine's batched path (more than 8 slots a
+    token); 480 assignments (the one-launch grouping), 516 and 1200 (the
+    chunk-table sort, which also writes the tile list, then the gather);
+    ragged T, fp8 and bf16 experts."""
+    cfg = W.get_config(name, E=32, k=12, T=T)
+    lt = W.make_layer(cfg, dev())
+    x = W.make_x(cfg, dev())
+    st = check_forward(lt, x)
+    _print(f"forward k=12 {name} T={T}: {st}")
+
+
 def test_forward_bf16_output_and_k1_E1():
     cfg = W.get_config("c0", E=1, k=1)
     lt = W.make_layer(cfg, dev())
