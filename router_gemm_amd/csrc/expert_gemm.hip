@@ -808,8 +808,9 @@ FfnPlan ffn_plan(const FfnGroup *g, int ngroups, int H) {
     }
   p.tiled = (all128 && H % 256 == 0 && mx_ok && g[0].nrows > 0 && avg >= 48.0) ? 1 : 0;
   // 256-row token tiles once the mean expert fills one (a weight tile then
-  // feeds all of an expert's rows from a single fetch)
-  p.bm = p.tiled ? (any_mx ? 64 : (avg >= 128.0 ? 256 : 128)) : 16 * p.mt;
+  // feeds all of an expert's rows from a single fetch); below that, MX tiles
+  // are 64 rows
+  p.bm = p.tiled ? (avg >= 128.0 ? 256 : (any_mx ? 64 : 128)) : 16 * p.mt;
   int64_t cap = 1;
   for (int i = 0; i < ngroups; ++i) cap += cdiv(g[i].nrows, p.bm) + std::min<int64_t>(g[i].nrows, g[i].E);
   p.max_tiles = (int)cap;
@@ -859,6 +860,11 @@ hipError_t launch_expert_ffn(const FfnGroup *g, int ngroups, int H, const FfnPla
   int32_t *hdr = tiles_ws;
   TileEntry *tiles = reinterpret_cast<TileEntry *>(tiles_ws + kTileHdrWords);
   StreamArgs a{g[0], ngroups > 1 ? g[1] : g[0], tiles, hdr, H};
+  if (plan.tiled && mx && plan.bm == 256) {
+    // MX and bf16 groups together, 256-row tiles
+    if (!tiles_ready) build_tiles_kernel<<<1, 1024, 0, st>>>(a.g0, a.g1, ngroups, plan.bm, plan.max_tiles, tiles, hdr);
+    return launch_wide_mx_ffn(g, ngroups, H, tiles, hdr, num_compute_units(), site, st);
+  }
   if (plan.tiled && mx) {
     // MX tiles are 64 token rows, the other groups' 128: each group gets its
     // own tile list and launches, one after the other on the stream.

@@ -443,7 +443,7 @@ __device__ __forceinline__ void tiled_item(const FfnGroup &G, const TileEntry &t
 // weight tile fetched once then feeds every row of most experts (instead of
 // being fetched again for each 128-row token tile), and a K chunk moves 64 KB
 // into LDS for twice the MFMAs of the 128-row item.  The LDS ring has two
-// stages (66 KB each): chunk kc+1 is copied while chunk kc is consumed.  A
+// stages (65 KB each): chunk kc+1 is copied while chunk kc is consumed.  A
 // wave owns 128 weight rows (wn) x 4 interleaved 16-row token slices
 // 16 (wm + 4 j); it reads its chunk's token fragments once and streams the 8
 // weight tiles' fragments through a double buffer, which keeps it within the
@@ -453,7 +453,7 @@ namespace {
 constexpr int WBM = 256;                    // token rows per wide tile
 constexpr int WTHREADS = 512;
 constexpr int WTX = WBM * 128;              // token bytes per stage
-constexpr int WTSX = 2048;                  // token scales per stage (8 waves x 256 B)
+constexpr int WTSX = 4 * WBM;               // token scales per stage (4 bytes per token row)
 constexpr int WSTAGE = TW + WTX + WTSX;
 constexpr int WNSTAGE = 2;
 }  // namespace
@@ -466,8 +466,9 @@ struct WideItem {
   int64_t rowb;
   const uint8_t *wsrc, *asrc;
   const float *ascale;
+  __amdgpu_buffer_rsrc_t rw, rx, rsx;   // copy sources: weights, token rows, token scales
   int lane, w, wn, wm;
-  uint32_t woff[4], xoff[4], soff;   // per-lane byte offsets of this lane's copies
+  uint32_t woff[4], xoff[4], xoff2[4], soff;   // per-lane byte offsets of this lane's copies
   // LDS read offsets inside a stage: token slice 0's two 16-byte fragment
   // halves and its scale (slice j adds 8192 j / 512 j: its rows are
   // 16 (wm + 4 j) + lane % 16, whose swizzle lane % 8 does not depend on j),
@@ -495,62 +496,81 @@ struct WideItem {
     asrc = (GATEUP ? G.x : G.h) + (indirect ? 0 : (int64_t)rbeg * rowb);
     ascale = (GATEUP ? G.xs : G.hs) + (FP8 && !indirect ? (int64_t)rbeg * KB : 0);
     const int sub = lane >> 3;   // row within an 8-row group
-    // copy instruction q = w + 8 t covers rows 8q .. 8q+7 of the weight and
-    // of the token tile (1 KB each)
+    // Copy instruction q = w + 8t covers rows 8q .. 8q+7 of the weight and of
+    // the token tile (1 KB each); waves 0-3 issue q and q + 4 (rows 32 further
+    // on: the same swizzle, weight offsets 32 rows further, token rows looked
+    // up again), and the token scales of rows 64w .. 64w+63.
+    if (w < 4) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int r = 8 * (w + 8 * t) + sub;
-      const int c = (lane & 7) ^ swz_f(r);   // logical 16-byte column landing in this lane's slot
-      const int grow = GATEUP ? (r < 128 ? col0 + r : I + col0 + r - 128) : col0 + r;
-      if constexpr (T16) {
-        // tile16 weights: instruction j = w + 8t copies half j % 2 of the
-        // item's 16-row tile j / 2 verbatim (LDS keeps the fragment-major tile)
-        const int j = w + 8 * t, rt = 16 * (j >> 1);
-        const int g0 = GATEUP ? (rt < 128 ? col0 + rt : I + col0 + rt - 128) : col0 + rt;
-        woff[t] = (uint32_t)(((int64_t)g0 >> 4) * 2048 + 1024 * (j & 1) + 16 * lane);
-      } else {
-        woff[t] = (uint32_t)(grow * rowb + c * 16);
+      for (int t = 0; t < 4; ++t) {
+        const int r = 8 * (w + 8 * t) + sub;
+        const int c = (lane & 7) ^ swz_f(r);   // logical 16-byte column landing in this lane's slot
+        const int grow = GATEUP ? (r < 128 ? col0 + r : I + col0 + r - 128) : col0 + r;
+        if constexpr (T16) {
+          // tile16 weights: instruction j = w + 8t copies half j % 2 of the
+          // item's 16-row tile j / 2 verbatim (LDS keeps the fragment-major tile)
+          const int j = w + 8 * t, rt = 16 * (j >> 1);
+          const int g0 = GATEUP ? (rt < 128 ? col0 + rt : I + col0 + rt - 128) : col0 + rt;
+          woff[t] = (uint32_t)(((int64_t)g0 >> 4) * 2048 + 1024 * (j & 1) + 16 * lane);
+        } else {
+          woff[t] = (uint32_t)(grow * rowb + c * 16);
+        }
       }
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int r = 8 * (w + 8 * t) + sub;
-      const int c = (lane & 7) ^ swz_f(r);
       // rows past the end repeat a valid row; indirect rows come from x row xsrc[row] / xdiv
-      const int rr = min(r, nvalid - 1);
-      const int64_t src = indirect ? G.xsrc[rbeg + rr] / G.xdiv : rr;
-      xoff[t] = (uint32_t)(src * rowb + c * 16);
+      auto xrow = [&](int r) -> int64_t {
+        const int rr = min(r, nvalid - 1);
+        return indirect ? G.xsrc[rbeg + rr] / G.xdiv : rr;
+      };
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int r = 8 * (w + 8 * t) + sub, r2 = r + 32;
+        xoff[t] = (uint32_t)(xrow(r) * rowb + ((lane & 7) ^ swz_f(r)) * 16);
+        xoff2[t] = (uint32_t)(xrow(r2) * rowb + ((lane & 7) ^ swz_f(r2)) * 16);
+      }
+      soff = (uint32_t)(xrow(64 * w + lane) * KB * 4);
     }
+    // buffer sizes: the expert's weight matrix, the item's token rows and
+    // scales (indirect rows: any row of x, whose offsets stay below 2^31)
     {
-      const int rr = min(32 * w + (lane & 31), nvalid - 1);
-      const int64_t src = indirect ? G.xsrc[rbeg + rr] / G.xdiv : rr;
-      soff = (uint32_t)(src * KB * 4);
+      const uint32_t kAny = 0x7FFFFFFF;
+      rw = buf_rsrc(wsrc, (uint32_t)(wrows * rowb));
+      rx = buf_rsrc(asrc, indirect ? kAny : (uint32_t)(nvalid * rowb));
+      rsx = buf_rsrc(ascale, indirect ? kAny : (uint32_t)(nvalid * KB * 4));
     }
     {
       const int r0 = 16 * wm + (lane & 15), ck = 2 * (lane >> 4);
       rb_l = (uint32_t)(TW + swz(r0, ck));
       rb_h = (uint32_t)(TW + swz(r0, ck + 1));
-      rb_s = (uint32_t)(TW + WTX + 256 * (r0 >> 5) + 4 * (r0 & 31));
+      rb_s = (uint32_t)(TW + WTX + 4 * r0);
       ra = (uint32_t)(128 * (arow(0) - (lane & 15)) + 16 * lane);
     }
   }
 
-  // Direct-to-LDS copies of K chunk kc into stage buffer sb: 4 (weights) +
-  // up to 4 (tokens) [+ 1 (token scales, fp8)] instructions per wave.  A
-  // token copy whose 8 rows all lie past the item's last row is skipped: the
+  // Direct-to-LDS copies of K chunk kc into stage buffer sb.  Waves 0-3 issue
+  // every copy: their own (instruction q = w + 8t) and those of the wave that
+  // shares their SIMD (q + 4, rows 32 further on), 8 (weights) + up to 8
+  // (tokens) [+ 1 (token scales, fp8)] instructions; waves 4-7 issue none and
+  // go straight to their MFMAs, so that while one wave of a SIMD waits for the
+  // copy path to take its instructions the other keeps the matrix core busy.
+  // A token copy whose 8 rows all lie past the item's last row is skipped: the
   // stale LDS rows it leaves only feed MFMA output columns of padding rows,
   // which are never stored (an output column depends on its own token only).
-  // The waits count nothing but "all of this wave's copies", so a wave may
-  // issue fewer than the others.
+  // The waits count nothing but "all of this wave's copies".
   __device__ __forceinline__ void issue(int kc, uint8_t *sb) const {
-    const uint8_t *wb = wsrc + (int64_t)kc * (T16 ? 128 * wrows : 128);
-    const uint8_t *xb = asrc + (int64_t)kc * 128;
+    if (w >= 4) return;
+    const uint32_t wk = (uint32_t)kc * (T16 ? 128 * (uint32_t)wrows : 128);
+    const uint32_t w2 = wk + (T16 ? 4096u : 32u * (uint32_t)rowb);   // the partner's weight rows, 32 further on
 #pragma unroll
-    for (int t = 0; t < 4; ++t) dma16(wb + woff[t], sb + (w + 8 * t) * 1024);
+    for (int t = 0; t < 4; ++t) {
+      bdma16(rw, woff[t], wk, sb + (w + 8 * t) * 1024);
+      bdma16(rw, woff[t], w2, sb + (w + 4 + 8 * t) * 1024);
+    }
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      if (8 * (w + 8 * t) < nvalid) dma16(xb + xoff[t], sb + TW + (w + 8 * t) * 1024);
-    if constexpr (FP8) dma4(reinterpret_cast<const uint8_t *>(ascale + kc) + soff, sb + TW + WTX + 256 * w);
+    for (int t = 0; t < 4; ++t) {
+      if (8 * (w + 8 * t) < nvalid) bdma16(rx, xoff[t], 128 * kc, sb + TW + (w + 8 * t) * 1024);
+      if (8 * (w + 4 + 8 * t) < nvalid) bdma16(rx, xoff2[t], 128 * kc, sb + TW + (w + 4 + 8 * t) * 1024);
+    }
+    if constexpr (FP8) bdma4(rsx, soff, 4 * kc, sb + TW + WTX + 256 * w);
   }
 
   struct AFrag {
@@ -588,7 +608,7 @@ struct WideItem {
       F.bl[j] = *reinterpret_cast<const i32x4 *>(sb + TW + swz(r, ck));
       F.bh[j] = *reinterpret_cast<const i32x4 *>(sb + TW + swz(r, ck + 1));
       // token r's scale sits in wave (r / 32)'s slot, lane r % 32
-      if constexpr (FP8) F.sx[j] = *reinterpret_cast<const float *>(sb + TW + WTX + 256 * (r >> 5) + 4 * (r & 31));
+      if constexpr (FP8) F.sx[j] = *reinterpret_cast<const float *>(sb + TW + WTX + 4 * r);
     }
     if constexpr (FP8) {
       F.sa = GATEUP ? wsc[kc] : wsc[wn * KB + kc];
@@ -641,7 +661,7 @@ struct WideItem {
           for (int jj = 1; jj < NJ; ++jj) {
             bl[jj] = *reinterpret_cast<const i32x4 *>(sb + rb_l + 8192 * jj);
             bh[jj] = *reinterpret_cast<const i32x4 *>(sb + rb_h + 8192 * jj);
-            sx[jj] = *reinterpret_cast<const float *>(sb + rb_s + 512 * jj);
+            sx[jj] = *reinterpret_cast<const float *>(sb + rb_s + 256 * jj);
           }
         }
         if (j == 0 && i + 1 < 8) read_a16(sb, i + 1, A[(i + 1) & 1]);
@@ -934,10 +954,321 @@ __global__ __launch_bounds__(WTHREADS, 1) void wide_ffn_kernel(TiledArgs a) {
   }
 }
 
+// ------------------------------------------------------ wide tiles, MX FP4
+//
+// The wide item for MX FP4 weights (E2M1 codes two to a byte, one E8M0 scale
+// per 32 inputs of a row; e4m3 tokens with fp32 1x128 group scales): the same
+// 256 weight rows x 256 token rows, 8 waves and wave layout as the fp8/bf16
+// wide item, and the same epilogue.  A K chunk of 128 inputs is 64 bytes of
+// codes per weight row, so a stage is 16 KB of codes + 32 KB of token rows
+// + 1 KB of token scales + 1 KB of E8M0 words (50 KB) and the ring holds
+// three stages: chunks kc+1 and kc+2 are in flight while chunk kc is consumed.
+//   - codes: instruction t of wave w copies the item's 16-row tile w + 8t with
+//     lane l taking row l%16, bytes 16(l/16)..+15 of the chunk, so that a tile
+//     lands fragment-major and each lane later reads its A operand at 16 l;
+//   - token rows as in the wide item (8 rows x 128 bytes per instruction,
+//     XOR-swizzled 16-byte columns); the B operand takes columns l/16 and
+//     4 + l/16 of the row (the instruction's input order);
+//   - one scale word per token row (waves 0-3) and per weight row (waves 4-7);
+//     a lane's E8M0 byte (its row, 32-input block l/16) is the scaled MFMA's A
+//     scale, the token scale multiplies the block product, which is folded into
+//     the accumulators two MFMAs later.
+// The next item's chunks 0 and 1 are issued right after an item's last step
+// (the two stages its chunks nchunk-3 and nchunk-2 used), so the ring keeps
+// running across items; the shared expert's bf16 items, when they ride in the
+// launch, run the bf16 wide item on the first two 65 KB of the same LDS.
+
+namespace {
+constexpr int MXC = TBN * 64;             // code bytes per stage
+constexpr int MXTOK = MXC;                // token rows (WTX bytes)
+constexpr int MXTS = MXTOK + WTX;         // token scale words, 4 bytes per token row
+constexpr int MXWS = MXTS + 4 * WBM;      // E8M0 words, 4 bytes per weight row
+constexpr int MXSTAGE = MXWS + 4 * TBN;
+constexpr int MXNSTAGE = 3;
+static_assert(MXNSTAGE * MXSTAGE >= WNSTAGE * WSTAGE, "the bf16 items' ring must fit in the MX ring");
+}  // namespace
+
+template <bool GATEUP>
+struct WideMxItem {
+  const FfnGroup &G;
+  int e, rbeg, rend, nvalid, I, K, nchunk, col0, ntile, H, nissue;
+  const uint8_t *wsrc, *ssrc, *asrc;
+  const float *ascale;
+  __amdgpu_buffer_rsrc_t rw, rx, rsc;   // copy sources: codes, token rows, this wave's scale words
+  int lane, w, wn, wm;
+  uint32_t woff[2], xoff[4], soff;   // per-lane byte offsets of this lane's copies
+  // LDS read offsets inside a stage: token slice 0's two fragment halves and
+  // its scale word (slice j adds 8192 j / 256 j), weight tile 0's fragment and
+  // its E8M0 byte (tile i adds 64 dt / 4 dt, dt = its first row - tile 0's).
+  uint32_t rb_l, rb_h, rb_s, ra, rs;
+
+  __device__ WideMxItem(const FfnGroup &g, const TileEntry &te, int nt_, int H_) : G(g), ntile(nt_), H(H_) {
+    lane = threadIdx.x & 63;
+    w = uniform(threadIdx.x >> 6);
+    wn = w & 1;
+    wm = w >> 1;
+    const int g4 = lane >> 4;
+    e = te.ge & 0xFFFFFF;
+    rend = min(max(group_off(G, e + 1), 0), G.nrows);
+    rbeg = min(max(group_off(G, e), 0) + te.m0, rend);
+    nvalid = min(rend - rbeg, WBM);
+    I = G.I;
+    K = GATEUP ? H : I;
+    nchunk = K / 128;
+    col0 = GATEUP ? ntile * 128 : ntile * TBN;
+    const int64_t wrows = GATEUP ? 2 * (int64_t)I : (int64_t)H;
+    const int wrowb = K / 2, srowb = K / 32;
+    wsrc = (GATEUP ? G.wgu : G.wd) + (int64_t)e * wrows * wrowb;
+    ssrc = (GATEUP ? G.mgu : G.md) + (int64_t)e * wrows * srowb;
+    const bool indirect = GATEUP && G.xsrc != nullptr;
+    asrc = (GATEUP ? G.x : G.h) + (indirect ? 0 : (int64_t)rbeg * K);
+    ascale = (GATEUP ? G.xs : G.hs) + (indirect ? 0 : (int64_t)rbeg * nchunk);
+    auto wrow = [&](int r) { return GATEUP ? (r < 128 ? col0 + r : I + col0 + r - 128) : col0 + r; };
+    // rows past the end repeat a valid row; indirect rows come from x row xsrc[row] / xdiv
+    auto xrow = [&](int r) -> int64_t {
+      const int rr = min(r, nvalid - 1);
+      return indirect ? G.xsrc[rbeg + rr] / G.xdiv : rr;
+    };
+#pragma unroll
+    for (int t = 0; t < 2; ++t) woff[t] = (uint32_t)(wrow(16 * (w + 8 * t) + (lane & 15)) * wrowb + 16 * g4);
+    nissue = 3;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r = 8 * (w + 8 * t) + (lane >> 3);
+      const int c = (lane & 7) ^ swz_f(r);
+      xoff[t] = (uint32_t)(xrow(r) * K + c * 16);
+      if (8 * (w + 8 * t) < nvalid) ++nissue;
+    }
+    soff = w < 4 ? (uint32_t)(xrow(64 * w + lane) * nchunk * 4) : (uint32_t)(wrow(64 * (w - 4) + lane) * srowb);
+    // buffer sizes: the expert's code and scale matrices, the item's token rows
+    // (indirect rows: any row of x, whose offsets the caller keeps below 2^31)
+    const uint32_t kAny = 0x7FFFFFFF;
+    rw = buf_rsrc(wsrc, (uint32_t)(wrows * wrowb));
+    rx = buf_rsrc(asrc, indirect ? kAny : (uint32_t)(nvalid * K));
+    rsc = w < 4 ? buf_rsrc(ascale, indirect ? kAny : (uint32_t)(nvalid * nchunk * 4))
+                : buf_rsrc(ssrc, (uint32_t)(wrows * srowb));
+    const int r0 = 16 * wm + (lane & 15);
+    rb_l = (uint32_t)(MXTOK + swz(r0, g4));
+    rb_h = (uint32_t)(MXTOK + swz(r0, 4 + g4));
+    rb_s = (uint32_t)(MXTS + 4 * r0);
+    const int a0 = GATEUP ? 64 * wn : 128 * wn;   // first weight row of tile 0
+    ra = (uint32_t)(64 * a0 + 16 * lane);
+    rs = (uint32_t)(MXWS + 4 * (a0 + (lane & 15)) + g4);
+  }
+
+  // Direct-to-LDS copies of K chunk kc into stage buffer sb: 2 (codes) + up to
+  // 4 (tokens) + 1 (scale words) instructions per wave, nissue in all; copy q
+  // of the seven.  A token copy whose 8 rows all lie past the item's last row
+  // is skipped (those LDS rows only feed output columns of padding rows, which
+  // are never stored).
+  static constexpr int NCOPY = 7;
+  __device__ __forceinline__ void issue_one(int q, int kc, uint8_t *sb) const {
+    if (q < 2) {
+      bdma16(rw, woff[q], 64 * kc, sb + (w + 8 * q) * 1024);
+    } else if (q < 6) {
+      const int t = q - 2;
+      if (8 * (w + 8 * t) < nvalid) bdma16(rx, xoff[t], 128 * kc, sb + MXTOK + (w + 8 * t) * 1024);
+    } else {
+      bdma4(rsc, soff, 4 * kc, sb + (w < 4 ? MXTS + 256 * w : MXWS + 256 * (w - 4)));
+    }
+  }
+  __device__ __forceinline__ void issue(int kc, uint8_t *sb) const {
+#pragma unroll
+    for (int q = 0; q < NCOPY; ++q) issue_one(q, kc, sb);
+  }
+
+  // Wait until this wave's copies of the chunk about to be consumed have
+  // landed (those of the chunk after it may still be in flight).
+  __device__ __forceinline__ void wait_one_behind() const {
+    switch (nissue) {
+      case 7: wait_vm_lgkm0<7>(); break;
+      case 6: wait_vm_lgkm0<6>(); break;
+      case 5: wait_vm_lgkm0<5>(); break;
+      case 4: wait_vm_lgkm0<4>(); break;
+      default: wait_vm_lgkm0<3>(); break;
+    }
+  }
+
+  __device__ __forceinline__ static int tile_dt(int i) { return GATEUP ? (i < 4 ? 16 * i : 128 + 16 * (i - 4)) : 16 * i; }
+
+  // The MFMAs of one K chunk: token fragments read once (slice 0 first, the
+  // others while the first MFMA runs), weight tile i+1's fragment and scale
+  // byte read while tile i's MFMAs run.
+  template <int NJ>
+  __device__ __forceinline__ void chunk(const uint8_t *sb, f32x4 (&acc)[8][4]) const {
+    i32x4 bl[NJ], bh[NJ];
+    float sx[NJ];
+    i32x4 A[2];
+    int sa[2];
+    A[0] = *reinterpret_cast<const i32x4 *>(sb + ra);
+    sa[0] = sb[rs];
+    bl[0] = *reinterpret_cast<const i32x4 *>(sb + rb_l);
+    bh[0] = *reinterpret_cast<const i32x4 *>(sb + rb_h);
+    sx[0] = *reinterpret_cast<const float *>(sb + rb_s);
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int NT = 8 * NJ;
+    f32x4 p1 = {0.f, 0.f, 0.f, 0.f}, p2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NT + 2; ++t) {
+      f32x4 cur = {0.f, 0.f, 0.f, 0.f};
+      if (t < NT) {
+        const int i = t / NJ, j = t % NJ;
+        cur = mfma_mx(A[i & 1], bl[j], bh[j], sa[i & 1]);
+        if (t == 0) {
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int jj = 1; jj < NJ; ++jj) {
+            bl[jj] = *reinterpret_cast<const i32x4 *>(sb + rb_l + 8192 * jj);
+            bh[jj] = *reinterpret_cast<const i32x4 *>(sb + rb_h + 8192 * jj);
+            sx[jj] = *reinterpret_cast<const float *>(sb + rb_s + 256 * jj);
+          }
+        }
+        if (j == 0 && i + 1 < 8) {
+          A[(i + 1) & 1] = *reinterpret_cast<const i32x4 *>(sb + ra + 64 * tile_dt(i + 1));
+          sa[(i + 1) & 1] = sb[rs + 4 * tile_dt(i + 1)];
+        }
+      }
+
+      if (t >= 2) {
+        const int i = (t - 2) / NJ, j = (t - 2) % NJ;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p2[r], sx[j], acc[i][j][r]);
+      }
+      p2 = p1;
+      p1 = cur;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Step kc: wait for this wave's copies of chunk kc, sync the workgroup
+  // (every wave's copies have landed, and nobody reads chunk kc-1's buffer any
+  // more), consume chunk kc and refill that buffer with chunk kc+2: waves 0-3
+  // issue their copies before their MFMAs, waves 4-7 (the other wave on each
+  // SIMD) after them, so that while one wave of a SIMD waits for the copy path
+  // to take its instructions the other keeps the matrix core busy.  Chunks 0
+  // and 1 were issued into stages par and par+1 (mod 3) before the call; chunk
+  // kc sits in stage (par + kc) % 3.  The first step also waits for chunk 1
+  // (and for the previous item's output stores, issued after it).
+  template <int NJ>
+  __device__ __forceinline__ void mainloop(uint8_t *lds, int par, f32x4 (&acc)[8][4]) const {
+    int sc = par, sn = par == 0 ? 2 : par - 1;   // stages of chunk kc and of chunk kc+2
+    const bool late = w >= 4;
+    for (int kc = 0; kc < nchunk; ++kc) {
+      // waves 4-7: chunk kc+1 into the stage chunk kc-2 used (free since the
+      // last barrier), after their MFMAs of chunk kc-1
+      if (late && kc >= 1 && kc + 1 < nchunk) issue(kc + 1, lds + (sn == 0 ? 2 : sn - 1) * MXSTAGE);
+      if (kc == 0 || kc + 1 == nchunk)
+        wait_vm_lgkm0<0>();
+      else
+        wait_one_behind();
+      wg_barrier();
+      // waves 0-3: chunk kc+2 into the stage chunk kc-1 used, before their MFMAs
+      if (!late && kc + 2 < nchunk) issue(kc + 2, lds + sn * MXSTAGE);
+      chunk<NJ>(lds + sc * MXSTAGE, acc);
+      sc = sc == 2 ? 0 : sc + 1;
+      sn = sn == 2 ? 0 : sn + 1;
+    }
+  }
+};
+
+// Issue work item w's chunks 0 and 1 into stages par and par+1 (mod 3).
+template <bool GATEUP>
+__device__ __forceinline__ void wide_mx_begin(const TiledArgs &a, const WideWork &w, uint8_t *lds, int par) {
+  const FfnGroup &G = (w.te.ge >> 24) ? a.g1 : a.g0;
+  WideMxItem<GATEUP> it(G, w.te, w.ntile, a.H);
+  it.issue(0, lds + par * MXSTAGE);
+  if (it.nchunk > 1) it.issue(1, lds + (par == 2 ? 0 : par + 1) * MXSTAGE);
+}
+
+// One MX work item whose chunks 0 and 1 were issued beforehand.  After its
+// last step it starts the next item (if `next` is an MX item) in the two
+// stages after its last chunk's, so that those copies are in flight during
+// this item's epilogue.  Returns the next item's first stage.
+template <bool GATEUP>
+__device__ __forceinline__ int wide_mx_item(const TiledArgs &a, const FfnGroup &G, const WideWork &cur,
+                                            const WideWork &next, int par, uint8_t *lds, float *red) {
+  WideMxItem<GATEUP> it(G, cur.te, cur.ntile, a.H);
+  const int lane = it.lane, wn = it.wn, wm = it.wm;
+  // active 16-row token slices of this wave: slice j covers rows 16*(wm + 4j)
+  const int nact = uniform(it.nvalid <= 16 * wm ? 0 : min(4, (it.nvalid - 16 * wm + 63) / 64));
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  switch (nact) {
+    case 4: it.template mainloop<4>(lds, par, acc); break;
+    case 3: it.template mainloop<3>(lds, par, acc); break;
+    case 2: it.template mainloop<2>(lds, par, acc); break;
+    case 1: it.template mainloop<1>(lds, par, acc); break;
+    default: it.template mainloop<1>(lds, par, acc); break;   // keeps the barrier count equal across waves
+  }
+  const int npar = (par + it.nchunk) % MXNSTAGE;
+  if (next.valid) wide_mx_begin<GATEUP>(a, next, lds, npar);
+  const int rbeg = it.rbeg, nvalid = it.nvalid, I = it.I, col0 = it.col0;
+  int brow[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) brow[j] = 16 * (wm + 4 * j);
+  store_item<true, GATEUP, WBM>(G, acc, brow, lane, wn, rbeg, nvalid, I, col0, cur.ntile, a.H, red);
+  // the next item's first step waits for its copies and syncs the workgroup
+  // before anything reads LDS; the reduction area is free once every wave is
+  // past this barrier
+  wait_lgkm0();
+  wg_barrier();
+  return npar;
+}
+
+// A bf16 item of the shared expert inside the MX launch (the bf16 wide item;
+// bf16 items stage no weight scales).
+template <bool GATEUP>
+__device__ __forceinline__ int wide_bf16_item(const TiledArgs &a, const FfnGroup &G, const WideWork &cur,
+                                              const WideWork &next, int par, uint8_t *lds, float *red) {
+  float *const wscb[2] = {red, red};
+  return G.tile16 ? wide_item<false, GATEUP, true>(a, G, cur, next, par, lds, red, wscb)
+                  : wide_item<false, GATEUP, false>(a, G, cur, next, par, lds, red, wscb);
+}
+
+// MX routed experts (and a bf16 shared expert) with 256-row token tiles.  Each
+// workgroup's items of one kind follow each other with their copies
+// overlapped; where the kind changes the ring starts over at stage 0.
+template <bool GATEUP>
+__global__ __launch_bounds__(WTHREADS, 1) void wide_mx_kernel(TiledArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  float *red = reinterpret_cast<float *>(lds + MXNSTAGE * MXSTAGE);
+  const int nslots = a.hdr[0];
+  const int count = nslots * a.nt;
+  const int64_t n0 = (int64_t)min(a.hdr[1], nslots) * a.nt;
+  const int xcd = blockIdx.x & 7, per = gridDim.x >> 3, slot0 = blockIdx.x >> 3;
+  const int beg = range_start(xcd, n0, count, a.c0, a.c1), end = range_start(xcd + 1, n0, count, a.c0, a.c1);
+  int L = beg + slot0;
+  WideWork cur = wide_find<GATEUP>(a, L, end, per, nslots);
+  bool begun = false;
+  int par = 0;
+  while (cur.valid) {
+    L += per;
+    const WideWork next = wide_find<GATEUP>(a, L, end, per, nslots);
+    const FfnGroup &G = (cur.te.ge >> 24) ? a.g1 : a.g0;
+    const bool mx = G.mx != 0;
+    const bool same = next.valid && (((next.te.ge >> 24) ? a.g1 : a.g0).mx != 0) == mx;
+    const WideWork nx = same ? next : WideWork{{0, 0}, 0, 0};
+    if (!begun) {
+      par = 0;
+      if (mx)
+        wide_mx_begin<GATEUP>(a, cur, lds, 0);
+      else
+        wide_begin<GATEUP>(a, cur, lds, red);
+    }
+    par = mx ? wide_mx_item<GATEUP>(a, G, cur, nx, par, lds, red) : wide_bf16_item<GATEUP>(a, G, cur, nx, par, lds, red);
+    begun = same;
+    cur = next;
+  }
+}
+
 // LDS: the copy ring, the h-scale reduction area, the weight-scale staging (H, I <= 16384;
 // the wide kernel keeps two buffers, the current item's and the next one's)
 size_t tiled_lds_bytes() { return NSTAGE * TSTAGE + 2 * TBM * sizeof(float) + 2 * 128 * sizeof(float); }
 size_t wide_lds_bytes() { return WNSTAGE * WSTAGE + 2 * WBM * sizeof(float) + 2 * 2 * 128 * sizeof(float); }
+size_t wide_mx_lds_bytes() { return MXNSTAGE * MXSTAGE + 2 * WBM * sizeof(float); }
 
 int num_compute_units() {
   static int cached[64] = {};
@@ -993,6 +1324,49 @@ hipError_t launch_tiled_ffn(const FfnGroup *g, int ngroups, int H, const void *t
     wide_ffn_kernel<false><<<grid, WTHREADS, lds, st>>>(a);
   else
     tiled_ffn_kernel<false><<<grid, TTHREADS, lds, st>>>(a);
+  timing_after(site + 1, st);
+  return hipGetLastError();
+}
+
+
+hipError_t launch_wide_mx_ffn(const FfnGroup *g, int ngroups, int H, const void *tiles, int32_t *hdr, int num_cus,
+                              int site, hipStream_t st) {
+  if (ngroups < 1 || ngroups > 2) return hipErrorInvalidValue;
+  for (int i = 0; i < ngroups; ++i) {
+    if (g[i].mx ? !tiled_mx_supported(g[i], H) : (g[i].fp8 || g[i].I % 128 != 0)) return hipErrorInvalidValue;
+  }
+  if (H % 256 != 0) return hipErrorInvalidValue;
+  TiledArgs a{g[0], ngroups > 1 ? g[1] : g[0], static_cast<const TileEntry *>(tiles), hdr, H, 0, 0, 0};
+  // relative cost of one item for the XCD split: K chunks x the chunk's cost
+  // (an MX stage is 50 KB of copies, a bf16 stage 65 KB with more LDS reads)
+  auto cost = [](const FfnGroup &G, int K) { return G.mx ? 3 * std::max(1, K / 128) : 4 * std::max(1, K * 2 / 128); };
+  int maxI = 0;
+  for (int i = 0; i < ngroups; ++i) maxI = std::max(maxI, (int)g[i].I);
+  const unsigned grid = (unsigned)(std::max(num_cus, 8) / 8 * 8);
+  const size_t lds = wide_mx_lds_bytes();
+  static bool attr_set[64] = {};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (dev >= 0 && dev < 64 && !attr_set[dev]) {
+    const void *fns[2] = {reinterpret_cast<const void *>(&wide_mx_kernel<true>),
+                          reinterpret_cast<const void *>(&wide_mx_kernel<false>)};
+    for (int i = 0; i < 2; ++i) {
+      const hipError_t e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    attr_set[dev] = true;
+  }
+  a.nt = maxI / 128;
+  a.c0 = cost(a.g0, H);
+  a.c1 = cost(a.g1, H);
+  timing_before(site, st);
+  wide_mx_kernel<true><<<grid, WTHREADS, lds, st>>>(a);
+  timing_after(site, st);
+  a.nt = H / TBN;
+  a.c0 = cost(a.g0, a.g0.I);
+  a.c1 = cost(a.g1, a.g1.I);
+  timing_before(site + 1, st);
+  wide_mx_kernel<false><<<grid, WTHREADS, lds, st>>>(a);
   timing_after(site + 1, st);
   return hipGetLastError();
 }

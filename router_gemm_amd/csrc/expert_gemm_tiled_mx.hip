@@ -52,13 +52,6 @@ struct MxTiledArgs {
 };
 }  // namespace
 
-// acc += (E2M1 A with per-lane E8M0 scale sa) * (E4M3 B), returned unscaled.
-__device__ __forceinline__ f32x4 mfma_mx(const i32x4 &a, const i32x4 &blo, const i32x4 &bhi, int sa) {
-  const i32x8 a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
-  const i32x8 b8 = {blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, f32x4{0.f, 0.f, 0.f, 0.f}, 4, 0, 0, sa, 0, 127);
-}
-
 template <bool GATEUP>
 struct MxItem {
   const FfnGroup &G;

@@ -522,9 +522,9 @@ moe_status moe_combine(const moe_layer *L, const void *y_perm, int32_t y_dtype, 
 namespace {
 // The expert GEMMs' tile list, for the sort to write from its own offsets (the
 // shared expert's group first when it rides in the routed launches); none for
-// tiled MX layers, whose groups get lists of their own.
+// MX layers on 64-row tiles, whose groups get lists of their own.
 moe::SmallTiles sort_tiles(const moe_layer *L, const FfnWs &ffn, int ngroups, int64_t T) {
-  if (ffn.plan.tiled && is_mx(L)) return moe::SmallTiles{};
+  if (ffn.plan.tiled && is_mx(L) && ffn.plan.bm != 256) return moe::SmallTiles{};
   return moe::SmallTiles{reinterpret_cast<moe::TileEntry *>(ffn.tiles + moe::kTileHdrWords), ffn.tiles, ffn.plan.bm,
                          ffn.plan.max_tiles, ngroups == 2 ? 1 : 0, (int)T};
 }

@@ -84,6 +84,16 @@ __device__ __forceinline__ f32x4 mfma_fp8(const i32x8 &a, const i32x8 &b, const 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// (16x16, f32) = A(16x128 E2M1, per-lane E8M0 scale sa) * B(128x16 e4m3),
+// returned unscaled by the B side (its scale byte is 127, i.e. 1).  Lane l of A
+// supplies row l%16 and inputs 32(l/16)..+31 (16 bytes, the stored packing);
+// of B, column l%16 and inputs 16(l/16)..+15 (blo) and 64+16(l/16)..+15 (bhi).
+__device__ __forceinline__ f32x4 mfma_mx(const i32x4 &a, const i32x4 &blo, const i32x4 &bhi, int sa) {
+  const i32x8 a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  const i32x8 b8 = {blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, f32x4{0.f, 0.f, 0.f, 0.f}, 4, 0, 0, sa, 0, 127);
+}
+
 // ---------------------------------------------------------------- waves
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
@@ -122,6 +132,20 @@ __device__ __forceinline__ void dma16_stream(const void *g, uint8_t *lds_base) {
 // Copy 4 bytes per lane to LDS at base + 4 * lane.
 __device__ __forceinline__ void dma4(const void *g, uint8_t *lds_base) {
   __builtin_amdgcn_global_load_lds((gbl_void *)g, (lds_void *)lds_base, 4, 0, 0);
+}
+
+// The same copies through a buffer resource: base address and size in four
+// SGPRs, a per-lane 32-bit byte offset (voff) and a wave-uniform one (soff),
+// so that a copy inside a loop needs one VGPR and no 64-bit address.  Word 3
+// is the gfx9 descriptor with a 32-bit data format (a zero format reads 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_base, 16, (int)voff, (int)soff, 0, 0);
+}
+__device__ __forceinline__ void bdma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_base, 4, (int)voff, (int)soff, 0, 0);
 }
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0], [15:14]).

@@ -87,7 +87,7 @@ struct TileEntry {
   int32_t m0;
 };
 struct FfnPlan {
-  int tiled;       // 1: LDS-tiled persistent kernels (128- or 256-row token tiles; 64 for MX FP4), 0: streaming
+  int tiled;       // 1: LDS-tiled persistent kernels (128- or 256-row token tiles; MX FP4: 64 or 256), 0: streaming
   int mt;          // streaming: 16-row token subtiles per workgroup
   int gw;          // streaming: gate (and up) 16-row weight tiles per wave (2 -> 128 h columns)
   int bm;          // token rows per tile-list entry
@@ -107,6 +107,11 @@ hipError_t launch_tiled_ffn(const FfnGroup *g, int ngroups, int H, const void *t
 bool tiled_mx_supported(const FfnGroup &g, int H);
 hipError_t launch_tiled_mx_ffn(const FfnGroup &g, int H, const void *tiles, int32_t *hdr, int num_cus, int site,
                                hipStream_t st);
+// 256 x 256 items for MX FP4 weights (expert_gemm_tiled.hip): the MX group
+// and optionally a bf16 group (the shared expert) in one launch, tiles built
+// with 256-row entries; H and the MX group's I multiples of 256.
+hipError_t launch_wide_mx_ffn(const FfnGroup *g, int ngroups, int H, const void *tiles, int32_t *hdr, int num_cus,
+                              int site, hipStream_t st);
 // Compute units of the current device (cached per device).
 int num_compute_units();
 // site: timing site of the gate/up launch (the down launch uses site + 1).

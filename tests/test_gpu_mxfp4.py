@@ -40,9 +40,14 @@ def _grouped_e4m3_rows(E, N, H, rng, empty_frac=0.3):
     (1, 100, 512, 1536, torch.float32),     # one expert, the routed width (tiled: 100 rows)
     (32, 150, 768, 640, torch.float32),     # 16-row tiles: 6 gate/up chunks (pipelined steps + a lone last step), 5 down chunks
     (8, 200, 1024, 512, torch.bfloat16),    # 32-row tiles: 8 and 4 chunks
-    # LDS-tiled MX kernels (>= 48 rows per expert, H and I multiples of 256):
-    (6, 1500, 1024, 768, torch.bfloat16),   # several 64-row token tiles per expert; 4 and 3 (odd) stages
-    (3, 700, 512, 256, torch.float32),      # 2 and 1 stages; ragged last token tile
+    # LDS-tiled MX kernels, 64-row token tiles (48..127 rows per expert, H and I multiples of 256):
+    (16, 1100, 512, 256, torch.bfloat16),   # ~69 rows: 2 and 1 stages; ragged last token tiles
+    (12, 1000, 1024, 768, torch.float32),   # ~83: 4 and 3 (odd) stages
+    # 256 x 256 MX items (128 or more rows per expert), three-stage ring of 128-input chunks:
+    (6, 1500, 1024, 768, torch.bfloat16),   # several 256-row token tiles per expert; 8 and 6 chunks
+    (3, 700, 512, 256, torch.float32),      # 4 and 2 chunks (the down items' two chunks are both issued ahead)
+    (2, 1300, 768, 512, torch.bfloat16),    # ~650 rows: bands of token tiles; 6 and 4 chunks, 3 down column tiles
+    (1, 300, 512, 1536, torch.float32),     # one expert, the routed width: 12 gate/up column tiles, 12 down chunks
 ])
 def test_mx_expert_ffn_matches_oracle(E, N, H, I, ydt):
     rng = np.random.default_rng(E * N + H)
@@ -62,7 +67,10 @@ def test_mx_expert_ffn_matches_oracle(E, N, H, I, ydt):
     assert err.max() < TOL["mxfp4"]
 
 
-@pytest.mark.parametrize("T", [136, 1, 17, 389])
+# 136, 1, 17: streaming kernels; 389: 64-row MX tiles and the shared expert's
+# own tiled launch; 600 and 1100: 256 x 256 MX items with the bf16 shared
+# expert's items in the same launches
+@pytest.mark.parametrize("T", [136, 1, 17, 389, 600, 1100])
 def test_mx_forward_matches_oracle(T):
     cfg = W.get_config("small_mxfp4", T=T)
     _print(f"[mx forward T={T}]")
@@ -78,6 +86,30 @@ def test_mx_forward_bf16_output_without_shared_expert():
     x = W.make_x(cfg, dev())
     st = check_forward(lt, x, out_dtype=torch.bfloat16)
     _print(f"[mx forward bf16 out, no shared] {st}")
+
+
+@pytest.mark.parametrize("over", [dict(T=1100), dict(T=1100, Is=0), dict(T=900, zipf_s=1.1, zipf_beta=0.6)])
+def test_mx_wide_forward_bitwise_repeatable(over):
+    """The 256 x 256 MX items: the same output bits on every call, whatever
+    the workspace held before (no order-dependent sums; every padding row and
+    stale LDS byte stays out of the stored results), and within tolerance of
+    the oracle."""
+    cfg = W.get_config("small_mxfp4", **over)
+    _print(f"[mx wide repeat {over}]")
+    lt = W.make_layer(cfg, dev())
+    x = W.make_x(cfg, dev())
+    check_forward(lt, x)
+    layer = B.Layer.from_tensors(lt)
+    ws = B.workspace(layer, cfg.T, cfg.N, dev())
+    outs = []
+    for rep in range(5):
+        ws.fill_(rep * 53 % 256)
+        y = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=dev())
+        B.moe_forward(layer, x, cfg.T, y, ws=ws)
+        torch.cuda.synchronize()
+        outs.append(y)
+    for y in outs[1:]:
+        assert torch.equal(y, outs[0])
 
 
 def test_mx_weights_are_read_as_stored():
