@@ -64,15 +64,15 @@ def parse():
 # 1 GiB device copy (bench.py --copy-calibration).  Valid only for the kernel sources they were
 # taken on: a different hash of the dominant kernel's sources (KERNEL_SOURCES) reports null.
 TRAFFIC = {
-    "prefill_fp8": {"src_hash": "dd536528522c1788", "fetch_kib": 3285737.82, "write_kib": 136893.6, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_fp8": {"src_hash": "dd536528522c1788", "fetch_kib": 1651581.38, "write_kib": 1142.28, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_bf16": {"src_hash": "dd536528522c1788", "fetch_kib": 3274989.97, "write_kib": 1737.75, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_mxfp4": {"src_hash": "dd536528522c1788", "fetch_kib": 900978.58, "write_kib": 1186.91, "fetch_scale": 2.0, "write_scale": 1.0},
-    "prefill_mxfp4": {"src_hash": "dd536528522c1788", "fetch_kib": 855450.69, "write_kib": 66411.11, "fetch_scale": 2.0, "write_scale": 1.0},
-    "ep8_share_fp8": {"src_hash": "dd536528522c1788", "fetch_kib": 852428.2, "write_kib": 77116.44, "fetch_scale": 2.0, "write_scale": 1.0},
-    "dense_ff_bf16": {"src_hash": "dd536528522c1788", "fetch_kib": 1360259.51, "write_kib": 221708.33, "fetch_scale": 2.0, "write_scale": 1.0},
+    "prefill_fp8": {"src_hash": "8e107ac2906496f8", "fetch_kib": 3097365.46, "write_kib": 134001.85, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_fp8": {"src_hash": "8e107ac2906496f8", "fetch_kib": 1651580.41, "write_kib": 1142.31, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_bf16": {"src_hash": "8e107ac2906496f8", "fetch_kib": 3274978.3, "write_kib": 1737.57, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_mxfp4": {"src_hash": "8e107ac2906496f8", "fetch_kib": 901174.0, "write_kib": 1185.47, "fetch_scale": 2.0, "write_scale": 1.0},
+    "prefill_mxfp4": {"src_hash": "8e107ac2906496f8", "fetch_kib": 2184216.05, "write_kib": 137567.91, "fetch_scale": 2.0, "write_scale": 1.0},
+    "ep8_share_fp8": {"src_hash": "8e107ac2906496f8", "fetch_kib": 845621.63, "write_kib": 76793.13, "fetch_scale": 2.0, "write_scale": 1.0},
+    "dense_ff_bf16": {"src_hash": "8e107ac2906496f8", "fetch_kib": 1360304.1, "write_kib": 221350.27, "fetch_scale": 2.0, "write_scale": 1.0},
     # per step: the four weight-gradient launches (routed dW_down, dW_gate_up; the shared expert's two)
-    "train_bf16": {"src_hash": "43d48f110e50a49b", "fetch_kib": 4397478.32, "write_kib": 26404451.44, "fetch_scale": 2.0, "write_scale": 1.0},
+    "train_bf16": {"src_hash": "51e2e1bdd29a60c1", "fetch_kib": 4391215.36, "write_kib": 26326419.96, "fetch_scale": 2.0, "write_scale": 1.0},
 }
 
 
