@@ -111,12 +111,8 @@ CONFIGS = {
                     "8192-token sequence, unbiased router on random inputs (near-balanced loads)"),
 }
 # Short aliases by position in the workload list.
-ALIASES = {"c0": "small_bf16", "c1": "decode_bf16", "c2": "decode_fp8",
-           "c3": "prefill_fp8", "c4": "ep8_share_fp8"}
-
-
 def get_config(name: str, **overrides) -> MoEConfig:
-    cfg = CONFIGS[ALIASES.get(name, name)]
+    cfg = CONFIGS[name]
     return dataclasses.replace(cfg, **overrides) if overrides else cfg
 
 

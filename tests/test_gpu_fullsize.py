@@ -18,7 +18,7 @@ from gpu_util import REG, TOL, check_forward, check_ids, dev, oracle_layer, rel_
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "decode_mxfp4"])
+@pytest.mark.parametrize("name", ["decode_bf16", "decode_fp8", "decode_mxfp4"])
 def test_decode_full_parity(name):
     cfg = W.get_config(name)
     print(f"[{cfg.name}] building layer", flush=True)
@@ -29,7 +29,7 @@ def test_decode_full_parity(name):
 
 
 def test_prefill_routing_grouping_and_sampled_outputs():
-    cfg = W.get_config("c3")
+    cfg = W.get_config("prefill_fp8")
     print("[prefill_fp8] building layer", flush=True)
     lt = W.make_layer(cfg, dev())
     x = W.make_x(cfg, dev())
@@ -87,7 +87,7 @@ def test_prefill_mxfp4_sampled_outputs():
 
 
 def test_ep_share_primitives_with_triples():
-    cfg = W.get_config("c4")
+    cfg = W.get_config("ep8_share_fp8")
     print("[ep8_share_fp8] building layer", flush=True)
     lt = W.make_layer(cfg, dev())
     x = W.make_x(cfg, dev())
@@ -159,7 +159,7 @@ def test_ep_share_forward_routed():
     """The same EP-8 share through moe_forward_routed (the shared expert inside
     the routed experts' launches): sampled tokens against the oracle, the
     hottest tokens and tokens without a local assignment included."""
-    cfg = W.get_config("c4")
+    cfg = W.get_config("ep8_share_fp8")
     print("[ep8_share_fp8 routed] building layer", flush=True)
     lt = W.make_layer(cfg, dev())
     x = W.make_x(cfg, dev())
@@ -185,7 +185,7 @@ def test_ep_share_forward_routed():
         assert err.max() < 7.5e-3            # regression bar
 
 
-@pytest.mark.parametrize("name", ["c2", "c3"])
+@pytest.mark.parametrize("name", ["decode_fp8", "prefill_fp8"])
 def test_forward_bitwise_repeatable_full_size(name):
     """20 forwards of the decode (T=64) and prefill (T=8192) FP8 layers in the
     benchmark's launch configuration (tile16 weights), the workspace refilled

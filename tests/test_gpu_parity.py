@@ -25,7 +25,7 @@ def _print(*a):
 
 # ------------------------------------------------------------------ router
 
-@pytest.mark.parametrize("name", ["c0", "small_fp8"])
+@pytest.mark.parametrize("name", ["small_bf16", "small_fp8"])
 def test_route_matches_oracle(name):
     cfg = W.get_config(name)
     lt = W.make_layer(cfg, dev())
@@ -48,7 +48,7 @@ def test_route_many_tokens_tiled_path():
     the 128-token tile) and E = 352 (not a multiple of the 192-expert tile),
     one K split at this hidden size; every token's ids, gates and logits
     against the oracle."""
-    cfg = W.get_config("c0", T=2085, E=352, k=8, I=64, Is=0)
+    cfg = W.get_config("small_bf16", T=2085, E=352, k=8, I=64, Is=0)
     lt = W.make_layer(cfg, dev())
     x = W.make_x(cfg, dev())
     layer = B.Layer.from_tensors(lt)
@@ -183,7 +183,7 @@ def test_route_nan_logits_rank_lowest(T):
 
 
 def test_route_k_equals_E_and_k1():
-    cfg = W.get_config("c0", k=32, T=37)
+    cfg = W.get_config("small_bf16", k=32, T=37)
     lt = W.make_layer(cfg, dev())
     x = W.make_x(cfg, dev())
     OL = oracle_layer(lt)
@@ -192,7 +192,7 @@ def test_route_k_equals_E_and_k1():
     _, g_ref, _, _ = oracle.route(OL, W.bf16_bits(x))
     assert np.abs(gates - g_ref).max() < 2e-6
     ids1, g1 = _route_with(lt.w_router, x, 1)
-    OL1 = oracle_layer(W.make_layer(W.get_config("c0", k=1), "cpu"))
+    OL1 = oracle_layer(W.make_layer(W.get_config("small_bf16", k=1), "cpu"))
     ids1_ref, _, gap1, _ = oracle.route(OL1, W.bf16_bits(x))
     check_ids(ids1, ids1_ref, gap1)
     assert (g1 == 1.0).all()
@@ -315,7 +315,7 @@ def test_expert_ffn_matches_oracle(fp8, E, N, H, I, ydt):
 
 
 def test_shared_expert_view_matches_oracle():
-    cfg = W.get_config("c0")
+    cfg = W.get_config("small_bf16")
     lt = W.make_layer(cfg, dev())
     x = W.make_x(cfg, dev())
     layer = B.Layer.shared_view(lt)
@@ -485,7 +485,7 @@ def test_combine_rounds_to_bf16_nearest_even():
 
 # ------------------------------------------------------------------ whole layer
 
-@pytest.mark.parametrize("name", ["c0", "small_fp8"])
+@pytest.mark.parametrize("name", ["small_bf16", "small_fp8"])
 def test_forward_small_full_parity(name):
     cfg = W.get_config(name)
     lt = W.make_layer(cfg, dev())
@@ -495,9 +495,9 @@ def test_forward_small_full_parity(name):
 
 
 @pytest.mark.parametrize("name,over", [
-    ("c0", dict(T=517, I=128, Is=128)),                     # 128-row token tiles (mean 65 rows)
+    ("small_bf16", dict(T=517, I=128, Is=128)),                     # 128-row token tiles (mean 65 rows)
     ("small_fp8", dict(T=389)),                             # 128-row token tiles (mean 97 rows)
-    ("c0", dict(T=1500, I=256, Is=128)),                    # 256-row token tiles (mean 188 rows)
+    ("small_bf16", dict(T=1500, I=256, Is=128)),                    # 256-row token tiles (mean 188 rows)
     ("small_fp8", dict(T=777)),                             # 256-row token tiles (mean 194 rows)
     ("small_fp8", dict(T=1100, zipf_s=1.1, zipf_beta=0.6)),  # 256-row tiles, skewed: 1..4 tiles per expert
 ])
@@ -520,7 +520,7 @@ def test_forward_tiled_path_reads_rows_through_permutation(name, over):
 @pytest.mark.parametrize("name,over", [
     ("small_fp8", dict(Is=192)),                            # fp8 routed experts, streaming kernels
     ("small_fp8", dict(T=777, Is=192)),                     # fp8 routed experts, 256-row tiles
-    ("c0", dict(T=1500, I=256, Is=192)),                    # bf16 routed experts, 256-row tiles
+    ("small_bf16", dict(T=1500, I=256, Is=192)),                    # bf16 routed experts, 256-row tiles
 ])
 def test_forward_shared_width_not_multiple_of_128(name, over):
     """A shared expert whose width is a multiple of 64 but not of 128 next to
@@ -543,7 +543,7 @@ def test_forward_ragged_and_single_token():
         check_forward(lt, x, OL=OL)
 
 
-@pytest.mark.parametrize("name,T", [("small_fp8", 40), ("small_fp8", 100), ("c0", 43)])
+@pytest.mark.parametrize("name,T", [("small_fp8", 40), ("small_fp8", 100), ("small_bf16", 43)])
 def test_forward_top_k_above_8(name, T):
     """k = 12 of 32 experts: the combine's batched path (more than 8 slots a
     token); 480 assignments (the one-launch grouping), 516 and 1200 (the
@@ -557,14 +557,14 @@ def test_forward_top_k_above_8(name, T):
 
 
 def test_forward_bf16_output_and_k1_E1():
-    cfg = W.get_config("c0", E=1, k=1)
+    cfg = W.get_config("small_bf16", E=1, k=1)
     lt = W.make_layer(cfg, dev())
     x = W.make_x(cfg, dev())
     check_forward(lt, x, out_dtype=torch.bfloat16)
 
 
 def test_forward_zero_tokens():
-    cfg = W.get_config("c0")
+    cfg = W.get_config("small_bf16")
     lt = W.make_layer(cfg, dev())
     layer = B.Layer.from_tensors(lt)
     y = torch.empty((0, cfg.H), dtype=torch.float32, device=dev())
@@ -660,7 +660,7 @@ def test_combine_per_token_grouping_without_chunk_table():
 
 
 @pytest.mark.parametrize("name,over,N", [("small_fp8", dict(T=300), 700), ("small_fp8", dict(T=300, Is=192), 700),
-                                         ("c0", dict(T=150), 333), ("small_fp8", dict(T=2000), 6000)])
+                                         ("small_bf16", dict(T=150), 333), ("small_fp8", dict(T=2000), 6000)])
 def test_forward_routed_matches_oracle(name, over, N):
     """moe_forward_routed on seeded pre-routed triples (some dropped: expert or
     token out of range; some tokens without an assignment) against the oracle

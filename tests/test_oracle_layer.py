@@ -15,7 +15,7 @@ from router_gemm_amd import workloads as W
 
 @pytest.fixture(scope="module")
 def small(orc):
-    cfg = W.get_config("c0")
+    cfg = W.get_config("small_bf16")
     lt = W.make_layer(cfg)
     h = W.host_layer_arrays(lt)
     L = orc.Layer(cfg.H, cfg.I, cfg.E, cfg.k, False, h["w_router"], h["w_gate_up"], h["w_down"],

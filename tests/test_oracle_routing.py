@@ -123,7 +123,7 @@ def test_gates_for_ids_consistent(orc):
 
 def test_prefill_zipf_bias_skews_loads(orc):
     """The prefill workload's router bias gives the hottest expert ~10x the mean load."""
-    cfg = W.get_config("c3")
+    cfg = W.get_config("prefill_fp8")
     lt_r = W._bf16_bits(W._rng(cfg.seed, 2).standard_normal((cfg.E, cfg.H), dtype=np.float32)
                         * np.float32(cfg.router_std))
     bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)

@@ -57,10 +57,10 @@ def _run_both(lt, x, out_dtype):
 @pytest.mark.gpu
 @pytest.mark.skipif(not gpu_available(), reason="needs a GPU")
 @pytest.mark.parametrize("name,Ts,out_dtype", [
-    ("c2", (64, 17), torch.bfloat16),          # the decode layer: 352 fp8 experts, streaming kernels
-    ("c1", (64, 5), torch.float32),            # bf16 experts
+    ("decode_fp8", (64, 17), torch.bfloat16),          # the decode layer: 352 fp8 experts, streaming kernels
+    ("decode_bf16", (64, 5), torch.float32),            # bf16 experts
     ("small_fp8", (300, 200), torch.float32),  # LDS-tiled kernels (mean rows >= 48), then streaming
-    ("c0", (128, 31), torch.bfloat16),
+    ("small_bf16", (128, 31), torch.bfloat16),
 ])
 def test_noalloc_matches_moe_forward_on_consecutive_calls(name, Ts, out_dtype):
     cfg = W.get_config(name)
