@@ -200,7 +200,7 @@ __device__ __forceinline__ uint32_t wave_max_key(uint32_t v) {
 // a ballot of the lanes that hold it and the lowest of them, with no
 // cross-lane shuffles.  Every winner's id and value are wave-uniform, so the
 // slot ranks and the softmax denominator are kept up to date round by round.
-template <int NJ>
+template <int NJ, int SB>
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const float *__restrict__ partial, int S, const float *__restrict__ bias, int T, int E, int k,
     int32_t *__restrict__ ids, float *__restrict__ gates, float *__restrict__ logits_out) {
@@ -211,9 +211,9 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
   float v[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) v[j] = 0.f;
-  // partial sums added in split order; the loads of a batch of splits are
-  // issued before the first add, so their latencies overlap
-  constexpr int SB = NJ <= 8 ? 16 : 4;
+  // partial sums added in split order; the loads of a batch of SB splits are
+  // issued before the first add, so their latencies overlap (SB no larger
+  // than the split count needs: the batch's registers set the occupancy)
   for (int s0 = 0; s0 < S; s0 += SB) {
     float pv[SB][NJ];
 #pragma unroll
@@ -328,9 +328,13 @@ hipError_t launch_router(const uint16_t *x, const uint16_t *wr, const float *bia
   const unsigned g2 = (unsigned)cdiv(T, 4);
   const int nj = (int)cdiv(E, 64);
   timing_before(1, st);
-#define MOE_TOPK_CASE(NJ)                                                                      \
-  case NJ:                                                                                     \
-    router_topk_kernel<NJ><<<g2, 256, 0, st>>>(partial, S, bias, (int)T, E, k, ids, gates, logits); \
+#define MOE_TOPK_CASE(NJ)                                                                                  \
+  case NJ:                                                                                                 \
+    if (S <= 2)                                                                                            \
+      router_topk_kernel<NJ, 2><<<g2, 256, 0, st>>>(partial, S, bias, (int)T, E, k, ids, gates, logits);   \
+    else                                                                                                   \
+      router_topk_kernel<NJ, (NJ <= 8 ? 16 : 4)><<<g2, 256, 0, st>>>(partial, S, bias, (int)T, E, k, ids, \
+                                                                    gates, logits);                        \
     break;
   switch (nj) {
     MOE_TOPK_CASE(1) MOE_TOPK_CASE(2) MOE_TOPK_CASE(3) MOE_TOPK_CASE(4)
