@@ -806,7 +806,12 @@ FfnPlan ffn_plan(const FfnGroup *g, int ngroups, int H) {
       any_mx = true;
       mx_ok = mx_ok && tiled_mx_supported(g[i], H);
     }
-  p.tiled = (all128 && H % 256 == 0 && mx_ok && g[0].nrows > 0 && avg >= 48.0) ? 1 : 0;
+  // (measured crossover on the Step-5 layer, one MI355X: with 10 or more
+  // rows per expert on average the tiled kernels are faster, by 8% at 11.6
+  // rows and 30% at 46.5 for fp8 and bf16 experts; MX FP4 from 12 rows, where
+  // the two tie; below that the streaming kernels win, by up to 12% at 8.7)
+  const double tiled_min = any_mx ? 12.0 : 10.0;
+  p.tiled = (all128 && H % 256 == 0 && mx_ok && g[0].nrows > 0 && avg >= tiled_min) ? 1 : 0;
   // 256-row token tiles once the mean expert fills one (a weight tile then
   // feeds all of an expert's rows from a single fetch); below that, MX tiles
   // are 64 rows

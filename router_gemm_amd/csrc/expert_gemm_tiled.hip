@@ -1,7 +1,7 @@
 // expert_gemm_tiled.hip -- the grouped expert GEMMs for experts with many
 // rows (prefill): LDS-tiled, double-buffered, persistent and XCD-aware.  Two
 // work-item shapes share the design below: 256 weight rows x 128 token rows
-// on 4 waves (tiled_ffn_kernel, experts with 48..127 rows on average) and
+// on 4 waves (tiled_ffn_kernel, experts with 10..127 rows on average) and
 // 256 x 256 on 8 waves (wide_ffn_kernel, 128 rows or more; see "wide tiles"
 // further down).  Weights come row-major or as tile16 tiles (FfnGroup::tile16),
 // which are copied into LDS verbatim and read in fragment order.
