@@ -812,10 +812,14 @@ FfnPlan ffn_plan(const FfnGroup *g, int ngroups, int H) {
   // the two tie; below that the streaming kernels win, by up to 12% at 8.7)
   const double tiled_min = any_mx ? 12.0 : 10.0;
   p.tiled = (all128 && H % 256 == 0 && mx_ok && g[0].nrows > 0 && avg >= tiled_min) ? 1 : 0;
-  // 256-row token tiles once the mean expert fills one (a weight tile then
-  // feeds all of an expert's rows from a single fetch); below that, MX tiles
-  // are 64 rows
-  p.bm = p.tiled ? (avg >= 128.0 ? 256 : (any_mx ? 64 : 128)) : 16 * p.mt;
+  // 256-row token tiles (a weight tile then feeds all of an expert's rows
+  // from a single fetch) from 128 rows per expert with bf16 weights, from 96
+  // with fp8 and from 48 with MX FP4, whose 64-row tiles below that fetch
+  // each weight tile once per 64 rows (measured on the Step-5 layer: at 70
+  // rows per expert the wide MX kernel is 25% faster, at 116 the wide fp8
+  // one 9%; wide bf16 items lose below 128); below, 128-row tiles (MX: 64)
+  const double wide_min = any_mx ? 48.0 : (g[big].fp8 ? 96.0 : 128.0);
+  p.bm = p.tiled ? (avg >= wide_min ? 256 : (any_mx ? 64 : 128)) : 16 * p.mt;
   int64_t cap = 1;
   for (int i = 0; i < ngroups; ++i) cap += cdiv(g[i].nrows, p.bm) + std::min<int64_t>(g[i].nrows, g[i].E);
   p.max_tiles = (int)cap;

@@ -87,11 +87,13 @@ def test_prefill_mxfp4_sampled_outputs():
 
 
 @pytest.mark.parametrize("name,T,packed", [("decode_fp8", 512, True), ("decode_fp8", 2048, False),
-                                           ("decode_bf16", 512, True), ("decode_mxfp4", 768, False)])
+                                           ("decode_fp8", 5120, True), ("decode_bf16", 512, True),
+                                           ("decode_mxfp4", 768, False), ("decode_mxfp4", 3072, False)])
 def test_mid_batch_tiled_path_sampled(name, T, packed):
     """Batches of a few hundred to a few thousand tokens at the full layer
-    shape: 10 to 48 rows per expert on average, where the 128-row tiled
-    kernels run with most token tiles far from full.  Routing of every token
+    shape: 10 to 116 rows per expert on average, where the 128-row (MX:
+    64-row) tiled kernels and, from 96 (MX: 48) rows, the 256-row wide kernels
+    run with most token tiles far from full.  Routing of every token
     against the oracle; outputs on 12 seeded tokens plus tokens of the least
     and the most loaded expert."""
     cfg = W.get_config(name, T=T)
