@@ -2,7 +2,7 @@
 // rows (prefill): LDS-tiled, double-buffered, persistent and XCD-aware.  Two
 // work-item shapes share the design below: 256 weight rows x 128 token rows
 // on 4 waves (tiled_ffn_kernel, experts with 10..127 rows on average) and
-// 256 x 256 on 8 waves (wide_ffn_kernel, 128 rows or more; see "wide tiles"
+// 256 x 256 on 8 waves (wide_ffn_kernel, 128 rows or more, 96 with fp8 weights; see "wide tiles"
 // further down).  Weights come row-major or as tile16 tiles (FfnGroup::tile16),
 // which are copied into LDS verbatim and read in fragment order.
 //
@@ -438,7 +438,8 @@ __device__ __forceinline__ void tiled_item(const FfnGroup &G, const TileEntry &t
 
 // ------------------------------------------------------------ wide tiles
 //
-// For experts with many rows (mean >= 128 per expert): a work item is 256
+// For experts with many rows (mean >= 128 per expert, 96 with fp8 weights, 48
+// with MX FP4 in the MX variant below): a work item is 256
 // weight rows x 256 token rows and a workgroup is 8 waves, two per SIMD.  A
 // weight tile fetched once then feeds every row of most experts (instead of
 // being fetched again for each 128-row token tile), and a K chunk moves 64 KB
