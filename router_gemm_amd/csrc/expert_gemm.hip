@@ -184,6 +184,9 @@ struct StreamArgs {
   const TileEntry *tiles;
   const int32_t *ntiles;
   int H;
+  int ssplit;      // > 1: group sgroup's gate/up K split this many ways (blockIdx.z), partial sums to spart
+  int sgroup;
+  float *spart;    // [ssplit][16][2 I] fp32 (I of group sgroup)
 };
 
 // Rows [rbeg, rend) of the tile, clamped to the group's row count.
@@ -197,8 +200,13 @@ __device__ __forceinline__ void tile_rows(const FfnGroup &G, const TileEntry &te
 // Workgroup: 4 waves x (GW gate + GW up 16-row weight tiles) = 64*GW h
 // columns x 16*MT token rows.  Each wave streams its own weight rows straight
 // from HBM into MFMA operand registers (no reuse across waves, so no LDS).
-template <bool FP8, bool MX, int MT, int GW, bool T16 = false>
-__device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry &te, int H) {
+// SPLIT (bf16, one 16-row tile, row-major weights): chunks
+// [nchunk z / S, nchunk (z+1) / S) only, and the raw gate and up sums go to
+// spart[z][row][2I] instead of through the epilogue.
+template <bool FP8, bool MX, int MT, int GW, bool T16 = false, bool SPLIT = false>
+__device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry &te, int H, int z = 0, int S = 1,
+                                             float *spart = nullptr) {
+  static_assert(!SPLIT || (!FP8 && MT == 1), "the K split is for bf16 groups with 16-row tiles");
   static_assert(FP8 || !MX, "MX weights take e4m3 activations");
   static_assert(!(MX && T16), "MX weights are row-major");
   constexpr int ESZ = FP8 ? 1 : 2;
@@ -460,16 +468,18 @@ __device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry 
           au[i][m] = chunk_mma<FP8>(s.fu[i], s.fx[m], au[i][m], s.swu * s.sx[m]);
         }
     };
+    const int c_lo = SPLIT ? (int)((int64_t)nchunk * z / S) : 0;         // non-empty: nchunk >= S
+    const int c_hi = SPLIT ? (int)((int64_t)nchunk * (z + 1) / S) : nchunk;
     Step s0, s1;
-    load_step(s0, 0);
-    int c = 0;
-    for (; c + 2 < nchunk; c += 2) {
+    load_step(s0, c_lo);
+    int c = c_lo;
+    for (; c + 2 < c_hi; c += 2) {
       load_step(s1, c + 1);
       mma_step(s0);
       load_step(s0, c + 2);
       mma_step(s1);
     }
-    if (c + 1 < nchunk) {
+    if (c + 1 < c_hi) {
       load_step(s1, c + 1);
       mma_step(s0);
       mma_step(s1);
@@ -508,6 +518,17 @@ __device__ __forceinline__ void gate_up_body(const FfnGroup &G, const TileEntry 
     }
   }
 
+  if constexpr (SPLIT) {   // raw sums of this K range; rows of the one tile
+#pragma unroll
+    for (int i = 0; i < GW; ++i) {
+      const int col = hc0 + 16 * i + 4 * (lane >> 4);
+      if (!xv[0]) continue;
+      float *p = spart + ((int64_t)z * 16 + (xrow[0] - rbeg)) * 2 * I + col;
+      *reinterpret_cast<f32x4 *>(p) = ag[i][0];
+      *reinterpret_cast<f32x4 *>(p + I) = au[i][0];
+    }
+    return;
+  }
   // Epilogue: lane holds columns hc0 + 16i + 4*(lane/16) + r of token row xrow[m].
   float hv[GW][MT][4];
 #pragma unroll
@@ -576,6 +597,13 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(StreamArgs a) {
   const TileEntry te = a.tiles[blockIdx.y];
   const FfnGroup G = pick_group(a.g0, a.g1, te.ge >> 24);
   if ((int)blockIdx.x * 64 * GW >= G.I) return;     // group narrower than the grid
+  if constexpr (MT == 1 && GW == 2) {
+    if (a.ssplit > 1 && (te.ge >> 24) == a.sgroup) {   // the split group's one tile: a K range per blockIdx.z
+      gate_up_body<false, false, 1, 2, false, true>(G, te, a.H, (int)blockIdx.z, a.ssplit, a.spart);
+      return;
+    }
+  }
+  if (blockIdx.z > 0) return;                       // the other tiles run once
   if (G.fp8) {
     if constexpr (GW == 2) {
       if constexpr (!MXK) {
@@ -919,21 +947,74 @@ FfnPlan ffn_plan(const FfnGroup *g, int ngroups, int H) {
   int64_t cap = 1;
   for (int i = 0; i < ngroups; ++i) cap += cdiv(g[i].nrows, p.bm) + std::min<int64_t>(g[i].nrows, g[i].E);
   p.max_tiles = (int)cap;
+  // A few tokens: the shared expert's gate/up (one bf16 expert, one 16-row
+  // tile) would leave each of its workgroups 512 H bytes of weights to stream
+  // alone (2 MB at H = 4096; measured: without it the Step-5 layer at T = 1
+  // takes 62 instead of 107 us), so its K is split four ways.  Measured on the
+  // Step-5 layer: with fp8 experts 17, 13 and 12% faster at T = 1, 2, 4 (4%
+  // slower at 8), with MX FP4 21, 21, 22 and 6% at T = 1, 2, 4, 8; with bf16
+  // experts no gain (their own 2 MB workgroups set the launch), so no split.
+  p.ssplit = 1;
+  p.sgroup = 0;
+  p.spart_floats = 0;
+  if (!p.tiled && p.mt == 1 && p.gw == 2 && ngroups == 2 && H >= 1024) {
+    for (int i = 0; i < 2; ++i) {
+      const FfnGroup &s = g[i];
+      const FfnGroup &r = g[1 - i];
+      const int rows_max = r.mx ? 8 : (r.fp8 ? 4 : 0);
+      if (s.E == 1 && !s.fp8 && !s.mx && !s.tile16 && s.z == nullptr && s.nrows > 0 && s.nrows <= rows_max &&
+          r.E > 1) {
+        p.ssplit = 4;
+        p.sgroup = i;
+        p.spart_floats = (int64_t)p.ssplit * 16 * 2 * s.I;
+        break;
+      }
+    }
+  }
   (void)rows;
   (void)experts;
   return p;
 }
 
 size_t ffn_tiles_bytes(const FfnPlan &p) {
-  return align_up(sizeof(TileEntry) * (size_t)p.max_tiles + kTileHdrWords * sizeof(int32_t), 256);
+  return align_up(sizeof(TileEntry) * (size_t)p.max_tiles + kTileHdrWords * sizeof(int32_t), 256) +
+         align_up(sizeof(float) * (size_t)p.spart_floats, 256);
+}
+
+// The split partial sums sit after the tile list in the same workspace.
+static float *split_partials(int32_t *tiles_ws, const FfnPlan &p) {
+  if (p.ssplit <= 1) return nullptr;
+  return reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(tiles_ws) +
+                                   align_up(sizeof(TileEntry) * (size_t)p.max_tiles + kTileHdrWords * sizeof(int32_t), 256));
+}
+
+// The split group's h: the ssplit partial sums of each pre-activation added
+// in split order (z = 0 first), SwiGLU, rounded to bf16 as in the epilogue.
+__global__ __launch_bounds__(256) void split_finish_kernel(FfnGroup G, const float *__restrict__ spart, int S) {
+  const int I = G.I;
+  const int64_t total = (int64_t)G.nrows * I;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int r = (int)(i / I), c = (int)(i % I);
+    float g = 0.f, u = 0.f;
+    for (int z = 0; z < S; ++z) {
+      const float *p = spart + ((int64_t)z * 16 + r) * 2 * I;
+      g += p[c];
+      u += p[I + c];
+    }
+    reinterpret_cast<uint16_t *>(G.h)[(int64_t)r * I + c] = (uint16_t)f32_to_bf16(swiglu(g, u));
+  }
 }
 
 template <int MT, bool MXK>
 static void run_stream(const StreamArgs &a, const FfnPlan &plan, int maxI, int site, hipStream_t st) {
   timing_before(site, st);
   if (plan.gw == 2) {
-    dim3 g1((unsigned)cdiv(maxI, 128), (unsigned)plan.max_tiles);
+    dim3 g1((unsigned)cdiv(maxI, 128), (unsigned)plan.max_tiles, (unsigned)(MT == 1 ? a.ssplit : 1));
     gate_up_stream_kernel<MT, 2, MXK><<<g1, 256, 0, st>>>(a);
+    if (MT == 1 && a.ssplit > 1) {
+      const FfnGroup &gs = a.sgroup ? a.g1 : a.g0;
+      split_finish_kernel<<<(unsigned)cdiv((int64_t)gs.nrows * gs.I, 256), 256, 0, st>>>(gs, a.spart, a.ssplit);
+    }
   } else {
     dim3 g1((unsigned)cdiv(maxI, 64), (unsigned)plan.max_tiles);
     gate_up_stream_kernel<MT, 1, false><<<g1, 256, 0, st>>>(a);
@@ -964,7 +1045,7 @@ hipError_t launch_expert_ffn(const FfnGroup *g, int ngroups, int H, const FfnPla
   if (rows == 0) return hipSuccess;
   int32_t *hdr = tiles_ws;
   TileEntry *tiles = reinterpret_cast<TileEntry *>(tiles_ws + kTileHdrWords);
-  StreamArgs a{g[0], ngroups > 1 ? g[1] : g[0], tiles, hdr, H};
+  StreamArgs a{g[0], ngroups > 1 ? g[1] : g[0], tiles, hdr, H, plan.ssplit, plan.sgroup, split_partials(tiles_ws, plan)};
   if (plan.tiled && mx && plan.bm == 256) {
     // MX and bf16 groups together, 256-row tiles
     if (!tiles_ready) build_tiles_kernel<<<1, 1024, 0, st>>>(a.g0, a.g1, ngroups, plan.bm, plan.max_tiles, tiles, hdr);

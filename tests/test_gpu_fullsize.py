@@ -86,6 +86,20 @@ def test_prefill_mxfp4_sampled_outputs():
     print(f"[prefill_mxfp4] {st}", flush=True)
 
 
+@pytest.mark.parametrize("name,T", [("decode_fp8", 1), ("decode_fp8", 3), ("decode_fp8", 5),
+                                    ("decode_bf16", 2), ("decode_mxfp4", 5), ("decode_mxfp4", 8)])
+def test_small_batch_full_parity(name, T):
+    """A few tokens at the full layer shape: with fp8 experts up to 4 tokens
+    and MX FP4 up to 8 the shared expert's gate/up K is split four ways and
+    its partial sums are added in order by a finishing pass (T = 5 with fp8
+    and the bf16 layer run unsplit).  Every token against the oracle."""
+    cfg = W.get_config(name, T=T)
+    lt = W.make_layer(cfg, dev())
+    x = W.make_x(cfg, dev())
+    st = check_forward(lt, x, reg=REG[name])
+    print(f"[{name} T={T}] {st}", flush=True)
+
+
 @pytest.mark.parametrize("name,T,packed", [("decode_fp8", 512, True), ("decode_fp8", 2048, False),
                                            ("decode_fp8", 5120, True), ("decode_bf16", 512, True),
                                            ("decode_mxfp4", 768, False), ("decode_mxfp4", 3072, False)])
