@@ -64,13 +64,13 @@ def parse():
 # 1 GiB device copy (bench.py --copy-calibration).  Valid only for the kernel sources they were
 # taken on: a different hash of the dominant kernel's sources (KERNEL_SOURCES) reports null.
 TRAFFIC = {
-    "prefill_fp8": {"src_hash": "25dd2b7ad9a7299f", "fetch_kib": 3120263.95, "write_kib": 134151.16, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_fp8": {"src_hash": "25dd2b7ad9a7299f", "fetch_kib": 1651585.25, "write_kib": 1141.86, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_bf16": {"src_hash": "25dd2b7ad9a7299f", "fetch_kib": 3274922.17, "write_kib": 1732.05, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_mxfp4": {"src_hash": "25dd2b7ad9a7299f", "fetch_kib": 900843.74, "write_kib": 1179.8, "fetch_scale": 2.0, "write_scale": 1.0},
-    "prefill_mxfp4": {"src_hash": "25dd2b7ad9a7299f", "fetch_kib": 2198786.4, "write_kib": 137784.15, "fetch_scale": 2.0, "write_scale": 1.0},
-    "ep8_share_fp8": {"src_hash": "25dd2b7ad9a7299f", "fetch_kib": 851503.85, "write_kib": 76808.12, "fetch_scale": 2.0, "write_scale": 1.0},
-    "dense_ff_bf16": {"src_hash": "25dd2b7ad9a7299f", "fetch_kib": 1360332.79, "write_kib": 221369.12, "fetch_scale": 2.0, "write_scale": 1.0},
+    "prefill_fp8": {"src_hash": "dfdd1489a7d27ffe", "fetch_kib": 3106610.77, "write_kib": 134214.32, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_fp8": {"src_hash": "dfdd1489a7d27ffe", "fetch_kib": 1651543.98, "write_kib": 1140.02, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_bf16": {"src_hash": "dfdd1489a7d27ffe", "fetch_kib": 3274902.55, "write_kib": 1730.53, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_mxfp4": {"src_hash": "dfdd1489a7d27ffe", "fetch_kib": 898050.6, "write_kib": 1180.68, "fetch_scale": 2.0, "write_scale": 1.0},
+    "prefill_mxfp4": {"src_hash": "dfdd1489a7d27ffe", "fetch_kib": 2190012.05, "write_kib": 137694.99, "fetch_scale": 2.0, "write_scale": 1.0},
+    "ep8_share_fp8": {"src_hash": "dfdd1489a7d27ffe", "fetch_kib": 849880.47, "write_kib": 76833.68, "fetch_scale": 2.0, "write_scale": 1.0},
+    "dense_ff_bf16": {"src_hash": "dfdd1489a7d27ffe", "fetch_kib": 1360301.04, "write_kib": 221362.96, "fetch_scale": 2.0, "write_scale": 1.0},
     # per step: the four weight-gradient launches (routed dW_down, dW_gate_up; the shared expert's two)
     "train_bf16": {"src_hash": "51e2e1bdd29a60c1", "fetch_kib": 4391215.36, "write_kib": 26326419.96, "fetch_scale": 2.0, "write_scale": 1.0},
 }
