@@ -72,7 +72,7 @@ TRAFFIC = {
     "ep8_share_fp8": {"src_hash": "dfdd1489a7d27ffe", "fetch_kib": 849880.47, "write_kib": 76833.68, "fetch_scale": 2.0, "write_scale": 1.0},
     "dense_ff_bf16": {"src_hash": "dfdd1489a7d27ffe", "fetch_kib": 1360301.04, "write_kib": 221362.96, "fetch_scale": 2.0, "write_scale": 1.0},
     # per step: the four weight-gradient launches (routed dW_down, dW_gate_up; the shared expert's two)
-    "train_bf16": {"src_hash": "51e2e1bdd29a60c1", "fetch_kib": 4391215.36, "write_kib": 26326419.96, "fetch_scale": 2.0, "write_scale": 1.0},
+    "train_bf16": {"src_hash": "de929ec2da51e8d2", "fetch_kib": 4392258.36, "write_kib": 26326024.52, "fetch_scale": 2.0, "write_scale": 1.0},
 }
 
 
