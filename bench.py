@@ -64,13 +64,13 @@ def parse():
 # 1 GiB device copy (bench.py --copy-calibration).  Valid only for the kernel sources they were
 # taken on: a different hash of the dominant kernel's sources (KERNEL_SOURCES) reports null.
 TRAFFIC = {
-    "prefill_fp8": {"src_hash": "dfdd1489a7d27ffe", "fetch_kib": 3106610.77, "write_kib": 134214.32, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_fp8": {"src_hash": "dfdd1489a7d27ffe", "fetch_kib": 1651543.98, "write_kib": 1140.02, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_bf16": {"src_hash": "dfdd1489a7d27ffe", "fetch_kib": 3274902.55, "write_kib": 1730.53, "fetch_scale": 2.0, "write_scale": 1.0},
-    "decode_mxfp4": {"src_hash": "dfdd1489a7d27ffe", "fetch_kib": 898050.6, "write_kib": 1180.68, "fetch_scale": 2.0, "write_scale": 1.0},
-    "prefill_mxfp4": {"src_hash": "dfdd1489a7d27ffe", "fetch_kib": 2190012.05, "write_kib": 137694.99, "fetch_scale": 2.0, "write_scale": 1.0},
-    "ep8_share_fp8": {"src_hash": "dfdd1489a7d27ffe", "fetch_kib": 849880.47, "write_kib": 76833.68, "fetch_scale": 2.0, "write_scale": 1.0},
-    "dense_ff_bf16": {"src_hash": "dfdd1489a7d27ffe", "fetch_kib": 1360301.04, "write_kib": 221362.96, "fetch_scale": 2.0, "write_scale": 1.0},
+    "prefill_fp8": {"src_hash": "34ea98c4f774e2f2", "fetch_kib": 3132184.61, "write_kib": 134275.79, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_fp8": {"src_hash": "34ea98c4f774e2f2", "fetch_kib": 1651545.47, "write_kib": 1141.0, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_bf16": {"src_hash": "34ea98c4f774e2f2", "fetch_kib": 3274900.49, "write_kib": 1730.61, "fetch_scale": 2.0, "write_scale": 1.0},
+    "decode_mxfp4": {"src_hash": "34ea98c4f774e2f2", "fetch_kib": 898080.84, "write_kib": 1180.38, "fetch_scale": 2.0, "write_scale": 1.0},
+    "prefill_mxfp4": {"src_hash": "34ea98c4f774e2f2", "fetch_kib": 2199479.88, "write_kib": 137705.2, "fetch_scale": 2.0, "write_scale": 1.0},
+    "ep8_share_fp8": {"src_hash": "34ea98c4f774e2f2", "fetch_kib": 847462.41, "write_kib": 76832.77, "fetch_scale": 2.0, "write_scale": 1.0},
+    "dense_ff_bf16": {"src_hash": "34ea98c4f774e2f2", "fetch_kib": 1360378.88, "write_kib": 221362.7, "fetch_scale": 2.0, "write_scale": 1.0},
     # per step: the four weight-gradient launches (routed dW_down, dW_gate_up; the shared expert's two)
     "train_bf16": {"src_hash": "de929ec2da51e8d2", "fetch_kib": 4392258.36, "write_kib": 26326024.52, "fetch_scale": 2.0, "write_scale": 1.0},
 }

@@ -186,7 +186,7 @@ struct StreamArgs {
   int H;
   int ssplit;      // > 1: group sgroup's gate/up K split this many ways (blockIdx.z), partial sums to spart
   int sgroup;
-  float *spart;    // [ssplit][16][2 I] fp32 (I of group sgroup)
+  float *spart;    // [ssplit][16][2 I] fp32 (I of group sgroup); needs nchunk >= ssplit (the plan asks H >= 1024)
 };
 
 // Rows [rbeg, rend) of the tile, clamped to the group's row count.
@@ -954,6 +954,7 @@ FfnPlan ffn_plan(const FfnGroup *g, int ngroups, int H) {
   // Step-5 layer: with fp8 experts 17, 13 and 12% faster at T = 1, 2, 4 (4%
   // slower at 8), with MX FP4 21, 21, 22 and 6% at T = 1, 2, 4, 8; with bf16
   // experts no gain (their own 2 MB workgroups set the launch), so no split.
+  // Eight ways for one or two tokens, four above.
   p.ssplit = 1;
   p.sgroup = 0;
   p.spart_floats = 0;
@@ -964,7 +965,7 @@ FfnPlan ffn_plan(const FfnGroup *g, int ngroups, int H) {
       const int rows_max = r.mx ? 8 : (r.fp8 ? 4 : 0);
       if (s.E == 1 && !s.fp8 && !s.mx && !s.tile16 && s.z == nullptr && s.nrows > 0 && s.nrows <= rows_max &&
           r.E > 1) {
-        p.ssplit = 4;
+        p.ssplit = s.nrows <= 2 ? 8 : 4;   // 8: 5-7% faster than 4 at T = 1, 2; 2-3% slower at 4, 8
         p.sgroup = i;
         p.spart_floats = (int64_t)p.ssplit * 16 * 2 * s.I;
         break;

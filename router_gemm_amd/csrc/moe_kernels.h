@@ -92,7 +92,7 @@ struct FfnPlan {
   int gw;          // streaming: gate (and up) 16-row weight tiles per wave (2 -> 128 h columns)
   int bm;          // token rows per tile-list entry
   int max_tiles;   // capacity of the tile list
-  // streaming, few tokens: K split this many ways for the one-expert bf16
+  // streaming, few tokens: K split this many ways (4 or 8) for the one-expert bf16
   // group sgroup (the shared expert), whose fp32 partial sums (spart_floats,
   // after the tile list in the same workspace) a finishing pass adds in order
   int ssplit;
