@@ -58,8 +58,9 @@ def _run_both(lt, x, out_dtype):
 @pytest.mark.skipif(not gpu_available(), reason="needs a GPU")
 @pytest.mark.parametrize("name,Ts,out_dtype", [
     ("decode_fp8", (64, 17), torch.bfloat16),          # the decode layer: 352 fp8 experts, streaming kernels
+    ("decode_fp8", (4, 1), torch.bfloat16),            # the shared expert's K split 4, then 8 ways
     ("decode_bf16", (64, 5), torch.float32),            # bf16 experts
-    ("small_fp8", (300, 200), torch.float32),  # LDS-tiled kernels (mean rows >= 48), then streaming
+    ("small_fp8", (300, 30), torch.float32),   # LDS-tiled kernels (mean 75 rows), then streaming (7.5)
     ("small_bf16", (128, 31), torch.bfloat16),
 ])
 def test_noalloc_matches_moe_forward_on_consecutive_calls(name, Ts, out_dtype):
